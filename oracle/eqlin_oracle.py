@@ -1,0 +1,203 @@
+"""fp64 CPU oracle for the p4 group-circulant (EQ-)linear layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only the test suite, the smoke check and the benchmark's
+CPU-baseline leg use it.  It shares no code, table or helper with the HIP
+library; both sides receive the same arrays from a seeded generator that holds
+none of the layer's arithmetic.
+
+Source: "Technical summary: Flash EQ-Linear" (gist.science, arXiv 2607.21271),
+sections "Key insight", "Algorithmic approach" (items 1-3), "Specialisation for
+the p4 rotation group" and "Main contributions" (item 2).
+
+What the layer computes (plain definition, no Fourier tricks)
+-------------------------------------------------------------
+The page ("Key insight") states that the EQ-Linear weight is group-circulant:
+it is built by cyclically shifting and replicating a learnable parameter set,
+so the layer is a circular convolution along the group axis combined with a
+linear map along the channel axis.  With group size T, C = C'*T input and
+D = D'*T output channels, channel index = group_channel*T + group_element
+(group element fastest), and learnable w[d', c', u] (u = 0..T-1):
+
+    W[d'T + t, c'T + s] = w[d', c', (t - s) mod T]
+    Y = X W^T,   i.e.   Y[n, d'T+t] = sum_{c', s} w[d', c', (t-s) mod T] X[n, c'T+s]
+
+The page only says "cyclically shifting"; the orientation (t - s) is a
+reading (the opposite orientation conjugates the weight spectrum and is the
+transpose pass used for dX below).  The Fourier algorithm the page describes is
+exact (DFT invertibility + convolution theorem, "Main contributions" item 2),
+so the oracle is the plain definition above, not the Fourier algorithm.
+
+Backward pass (plain calculus on the same definition):
+    dX = dY W                      (transposed group-circulant)
+    dw[d', c', u] = sum_n sum_t dY[n, d'T+t] X[n, c'T + (t-u) mod T]
+
+Every routine here is T-generic and runs in float64 with NumPy.  The only
+library primitive used as a step is a dense matrix product.
+
+The group spectrum routine (``group_spectrum``) is the plain DFT definition
+F[k] = sum_u z[u] exp(-2 pi i k u / T) along the group axis, used to check the
+prepared weight planes ("Algorithmic approach" item 1, conjugate symmetry in
+item 2, p4 specialisation).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "dense_expand",
+    "forward_direct",
+    "backward_direct",
+    "dx_direct",
+    "dw_direct",
+    "group_spectrum",
+    "kept_p4_planes",
+    "forward_rows",
+    "dw_entries",
+]
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def _split_groups(A: np.ndarray, T: int) -> np.ndarray:
+    """[rows][G*T] -> [rows][G][T] (group element fastest)."""
+    rows, width = A.shape
+    if width % T:
+        raise ValueError(f"width {width} is not a multiple of T={T}")
+    return A.reshape(rows, width // T, T)
+
+
+def dense_expand(w) -> np.ndarray:
+    """Dense D x C weight of the group-circulant layer ("Key insight").
+
+    W[d'T + t, c'T + s] = w[d', c', (t - s) mod T], built entry by entry from
+    the definition with explicit index arithmetic.
+    """
+    w = _f64(w)
+    Dp, Cp, T = w.shape
+    W = np.empty((Dp * T, Cp * T), dtype=np.float64)
+    for t in range(T):
+        for s in range(T):
+            W[t::T, s::T] = w[:, :, (t - s) % T]
+    return W
+
+
+def forward_direct(X, w) -> np.ndarray:
+    """Y = X W^T by the direct circular-convolution formula ("Key insight").
+
+    Y3[n, d', t] = sum_u sum_c' w[d', c', u] * X3[n, c', (t - u) mod T]
+    (u = t - s).  For each shift u this is one dense contraction over c'
+    against the group-rolled input X3[..., (t-u) mod T] = roll(X3, u)[..., t].
+    """
+    X = _f64(X)
+    w = _f64(w)
+    Dp, Cp, T = w.shape
+    N = X.shape[0]
+    X3 = _split_groups(X, T)
+    if X3.shape[1] != Cp:
+        raise ValueError("X width does not match w")
+    Y3 = np.zeros((N, Dp, T), dtype=np.float64)
+    for u in range(T):
+        Xs = np.roll(X3, u, axis=2)            # Xs[n, c', t] = X3[n, c', (t-u) mod T]
+        # [N*T, C'] @ [C', D'] -> [N, T, D']
+        prod = Xs.transpose(0, 2, 1).reshape(N * T, Cp) @ w[:, :, u].T
+        Y3 += prod.reshape(N, T, Dp).transpose(0, 2, 1)
+    return Y3.reshape(N, Dp * T)
+
+
+def dx_direct(dY, w) -> np.ndarray:
+    """dX = dY W (transposed group-circulant), by the direct formula.
+
+    dX3[n, c', s] = sum_u sum_d' w[d', c', u] * dY3[n, d', (s + u) mod T]
+    """
+    dY = _f64(dY)
+    w = _f64(w)
+    Dp, Cp, T = w.shape
+    N = dY.shape[0]
+    G3 = _split_groups(dY, T)
+    if G3.shape[1] != Dp:
+        raise ValueError("dY width does not match w")
+    dX3 = np.zeros((N, Cp, T), dtype=np.float64)
+    for u in range(T):
+        Gs = np.roll(G3, -u, axis=2)           # Gs[n, d', s] = G3[n, d', (s+u) mod T]
+        prod = Gs.transpose(0, 2, 1).reshape(N * T, Dp) @ w[:, :, u]
+        dX3 += prod.reshape(N, T, Cp).transpose(0, 2, 1)
+    return dX3.reshape(N, Cp * T)
+
+
+def dw_direct(dY, X, T: int = 4) -> np.ndarray:
+    """Gradient with respect to the learnable circulant vectors w.
+
+    dw[d', c', u] = sum_n sum_t dY3[n, d', t] * X3[n, c', (t - u) mod T],
+    i.e. the dense gradient dY^T X summed along each circulant diagonal.
+    """
+    dY = _f64(dY)
+    X = _f64(X)
+    G3 = _split_groups(dY, T)
+    X3 = _split_groups(X, T)
+    N, Dp, _ = G3.shape
+    Cp = X3.shape[1]
+    dw = np.empty((Dp, Cp, T), dtype=np.float64)
+    Gm = G3.transpose(1, 0, 2).reshape(Dp, N * T)         # [D', (n,t)]
+    for u in range(T):
+        Xs = np.roll(X3, u, axis=2)                        # Xs[n, c', t] = X3[n, c', (t-u)]
+        Xm = Xs.transpose(0, 2, 1).reshape(N * T, Cp)      # [(n,t), C']
+        dw[:, :, u] = Gm @ Xm
+    return dw
+
+
+def backward_direct(dY, X, w):
+    """(dX, dw) of the layer for upstream gradient dY, autograd-free."""
+    w = _f64(w)
+    return dx_direct(dY, w), dw_direct(dY, X, w.shape[2])
+
+
+def group_spectrum(z) -> np.ndarray:
+    """DFT along the last (group) axis by its definition, complex128.
+
+    F[..., k] = sum_u z[..., u] * exp(-2 pi i k u / T)
+    ("Algorithmic approach" item 1: the group convolution becomes a pointwise
+    product per frequency).
+    """
+    z = _f64(z)
+    T = z.shape[-1]
+    k = np.arange(T).reshape(T, 1)
+    u = np.arange(T).reshape(1, T)
+    F = np.exp(-2j * np.pi * k * u / T)                   # F[k, u]
+    return z.astype(np.complex128) @ F.T
+
+
+def kept_p4_planes(w) -> np.ndarray:
+    """The non-redundant real planes of the p4 (T=4) weight spectrum.
+
+    Real input gives a conjugate-symmetric spectrum ("Algorithmic approach"
+    item 2), F[3] = conj(F[1]); F[0] and F[2] are real.  Returns, per
+    (d', c'), the four reals (Re F0, Re F2, Re F1, Im F1), shape [D'][C'][4].
+    """
+    w = _f64(w)
+    if w.shape[-1] != 4:
+        raise ValueError("p4 planes need T = 4")
+    F = group_spectrum(w)
+    return np.stack([F[..., 0].real, F[..., 2].real, F[..., 1].real, F[..., 1].imag], axis=-1)
+
+
+def forward_rows(X, w, rows) -> np.ndarray:
+    """Selected output rows of forward_direct, for spot checks of huge shapes."""
+    X = _f64(X)
+    rows = np.asarray(rows, dtype=np.int64)
+    return forward_direct(X[rows], w)
+
+
+def dw_entries(dY, X, idx, T: int = 4) -> np.ndarray:
+    """Selected dw[d', c', :] vectors (idx = [(d', c'), ...]) by the definition."""
+    G3 = _split_groups(_f64(dY), T)
+    X3 = _split_groups(_f64(X), T)
+    out = np.empty((len(idx), T), dtype=np.float64)
+    for i, (d, c) in enumerate(idx):
+        g = G3[:, d, :]                                    # [N, T]
+        x = X3[:, c, :]                                    # [N, T]
+        for u in range(T):
+            out[i, u] = float(np.sum(g * np.roll(x, u, axis=1)))
+    return out
