@@ -1,0 +1,280 @@
+"""Benchmark of the p4 group-circulant linear layer on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+for every layer of the workload, prepare the weight spectra, run the forward
+(Y = X W^T), and the backward (dX = dY W, then dw).  Inputs live in HBM before
+the timed region starts; R rotating buffer sets (more than the 256 MB
+Infinity Cache) keep consecutive steps from being served by the cache.
+
+The reported metric is the forward dense-equivalent throughput
+2*N*D*C / t_forward (the same N x D x C dense GEMM counts 2NDC FLOPs), summed
+over the workload's layers, with t_forward the forward kernel time measured by
+HIP events on the launch stream inside the timed steps.  The fraction of the
+MFMA peak counts the FLOPs the kernel executes: six real products of
+N x D/4 x C/4, i.e. 0.75 NDC.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dtype f32|f16]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "EQ-Linear fwd dense-equiv TFLOP/s (2NDC) + % MFMA peak, p4 ViT-B/H shapes"
+PEAK_TFLOPS = {"f32": 157.3, "f16": 2500.0}      # MI355X dense MFMA peaks
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="vitb_attn")
+    p.add_argument("--dtype", default=None)
+    p.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0 = enough to exceed 600 MB)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--forward-only", action="store_true",
+                   help="time only the forward (for profiling the forward kernel); not a valid bench line")
+    p.add_argument("--copy-calibration-mb", type=int, default=0,
+                   help="also run one plain device copy of this many MB (counter calibration)")
+    return p.parse_args()
+
+
+def dense_weight(torch, w):
+    """Dense D x C weight of the circulant blocks for the dense-GEMM comparator."""
+    Dp, Cp, T = w.shape
+    t = torch.arange(T, device=w.device)
+    idx = (t.view(T, 1) - t.view(1, T)) % T                  # idx[t, s] = (t - s) mod T
+    return w[:, :, idx].permute(0, 2, 1, 3).reshape(Dp * T, Cp * T).contiguous()
+
+
+def cpu_baseline(layers, budget_s=12.0):
+    """Time the fp64 oracle forward on the host cores (reported baseline only)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    flops = 0.0
+    elapsed = 0.0
+    samples = []
+    t_start = time.perf_counter()
+    while time.perf_counter() - t_start < budget_s:
+        for (L, X, w, _) in layers:
+            n = min(L.N, 2048)
+            t0 = time.perf_counter()
+            oracle.forward_direct(X[:n], w)
+            dt = time.perf_counter() - t0
+            elapsed += dt
+            flops += 2.0 * n * L.C * L.D
+            samples.append(f"{L.name}:{n}x{L.C}->{L.D}")
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 oracle forward_direct on the first rows of each layer "
+                      f"({', '.join(sorted(set(samples)))}), repeated for {elapsed:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    from group_circulant_linear_amd import eqlin
+    from group_circulant_linear_amd.inputs import WORKLOADS, make_layer_inputs
+
+    wl = WORKLOADS[args.workload]
+    dt = args.dtype or wl.dtypes[0]
+    tdt = torch.float32 if dt == "f32" else torch.float16
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    eqlin.load_library()
+
+    # ---- inputs (host, seeded) -> HBM, rotating sets
+    layers = []
+    for li, L in enumerate(wl.layers):
+        X, w, dY = make_layer_inputs(L.N, L.C, L.D, dt, seed=0, layer=li)
+        layers.append((L, X, w, dY))
+    set_bytes = 0
+    for (L, X, w, dY) in layers:
+        es = X.itemsize
+        set_bytes += es * L.N * (2 * L.C + 2 * L.D) + eqlin.eqlin_backward_workspace_bytes(L.N, L.C, L.D, tdt)
+    nsets = args.sets or max(2, int(np.ceil(600e6 / set_bytes)))
+
+    sets = []
+    for r in range(nsets):
+        S = []
+        for (L, X, w, dY) in layers:
+            tX = torch.from_numpy(X).to(dev)
+            tw = torch.from_numpy(w).to(dev)
+            tdY = torch.from_numpy(dY).to(dev)
+            Wbuf = torch.empty(eqlin.eqlin_prepared_weight_bytes(L.C, L.D, tdt), dtype=torch.uint8, device=dev)
+            Y = torch.empty((L.N, L.D), dtype=tdt, device=dev)
+            dX = torch.empty((L.N, L.C), dtype=tdt, device=dev)
+            dw = torch.empty((L.D // 4, L.C // 4, 4), dtype=torch.float32, device=dev)
+            ws = torch.empty(max(1, eqlin.eqlin_backward_workspace_bytes(L.N, L.C, L.D, tdt)), dtype=torch.uint8,
+                             device=dev)
+            S.append(dict(L=L, X=tX, w=tw, dY=tdY, Wbuf=Wbuf, Y=Y, dX=dX, dw=dw, ws=ws))
+        sets.append(S)
+    torch.cuda.synchronize()
+
+    phases = ("prepare", "forward", "dx", "dw")
+
+    def step(i, events=None):
+        S = sets[i % nsets]
+        for li, b in enumerate(S):
+            ev = events[li] if events is not None else None
+            if ev is not None:
+                ev["prepare"][0].record()
+            Wh = eqlin.eqlin_prepare_weights(b["w"], out=b["Wbuf"])
+            if ev is not None:
+                ev["prepare"][1].record()
+                ev["forward"][0].record()
+            eqlin.eqlin_forward(b["X"], Wh, out=b["Y"])
+            if ev is not None:
+                ev["forward"][1].record()
+            if args.forward_only:
+                continue
+            if ev is not None:
+                ev["dx"][0].record()
+            eqlin.eqlin_backward_dx(b["dY"], Wh, out=b["dX"])
+            if ev is not None:
+                ev["dx"][1].record()
+                ev["dw"][0].record()
+            eqlin.eqlin_backward_dw(b["dY"], b["X"], workspace=b["ws"], out=b["dw"])
+            if ev is not None:
+                ev["dw"][1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"# warmup done ({args.warmup} steps, {nsets} buffer sets)", file=sys.stderr, flush=True)
+
+    K = args.steps
+    evs = [[{p: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for p in phases}
+            for _ in layers] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+
+    ph_us = {p: [0.0] * len(layers) for p in phases}
+    for i in range(K):
+        for li in range(len(layers)):
+            for p in phases:
+                if args.forward_only and p in ("dx", "dw"):
+                    continue
+                a, b = evs[i][li][p]
+                ph_us[p][li] += a.elapsed_time(b) * 1e3 / K
+
+    fwd_flops = sum(2.0 * L.N * L.C * L.D for (L, _, _, _) in layers)
+    fwd_us = sum(ph_us["forward"])
+    value = fwd_flops / (fwd_us * 1e-6) / 1e12
+    exec_flops = 0.75 * sum(L.N * L.C * L.D for (L, _, _, _) in layers)
+
+    # roofline of the forward kernel (one launch per layer; summed over layers)
+    achieved = exec_flops / (fwd_us * 1e-6) / 1e12
+    peak = PEAK_TFLOPS[dt]
+    roofline = {"bound": "mfma", "kernel": "fwd_kernel", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+
+    per_layer = []
+    for li, (L, _, _, _) in enumerate(layers):
+        nd = L.N * L.C * L.D
+        es = 4 if dt == "f32" else 2
+        d = {"layer": L.name, "N": L.N, "C": L.C, "D": L.D}
+        for p in phases:
+            d[f"{p}_us"] = round(ph_us[p][li], 2)
+        d["fwd_tflops_dense_equiv"] = round(2 * nd / (ph_us["forward"][li] * 1e-6) / 1e12, 2)
+        d["fwd_mfma_frac"] = round(0.75 * nd / (ph_us["forward"][li] * 1e-6) / 1e12 / peak, 4)
+        d["fwd_hbm_gbs_algorithmic"] = round(
+            (es * L.N * (L.C + L.D) + es * L.C * L.D / 4) / (ph_us["forward"][li] * 1e-6) / 1e9, 1)
+        if not args.forward_only:
+            d["dx_mfma_frac"] = round(0.75 * nd / (ph_us["dx"][li] * 1e-6) / 1e12 / peak, 4)
+            d["dw_mfma_frac"] = round(0.75 * nd / (ph_us["dw"][li] * 1e-6) / 1e12 / peak, 4)
+        per_layer.append(d)
+
+    # dense GEMM comparator: F.linear on the pre-expanded weight, same dtype, same stream
+    dense = None
+    if not args.no_dense:
+        F = torch.nn.functional
+        tot_f, tot_b = 0.0, 0.0
+        for li, (L, X, w, dY) in enumerate(layers):
+            b = sets[0][li]
+            Wd = dense_weight(torch, b["w"])
+            Xs = [sets[r][li]["X"] for r in range(nsets)]
+            dYs = [sets[r][li]["dY"] for r in range(nsets)]
+            Yd = torch.empty((L.N, L.D), dtype=tdt, device=dev)
+            dXd = torch.empty((L.N, L.C), dtype=tdt, device=dev)
+            dWd = torch.empty((L.D, L.C), dtype=tdt, device=dev)
+            for i in range(3):
+                torch.matmul(Xs[i % nsets], Wd.t(), out=Yd)
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            reps = max(10, K)
+            torch.cuda.synchronize()
+            e0.record()
+            for i in range(reps):
+                torch.matmul(Xs[i % nsets], Wd.t(), out=Yd)
+            e1.record()
+            for i in range(reps):
+                torch.matmul(dYs[i % nsets], Wd, out=dXd)
+                torch.matmul(dYs[i % nsets].t(), Xs[i % nsets], out=dWd)
+            e2.record()
+            torch.cuda.synchronize()
+            tot_f += e0.elapsed_time(e1) * 1e3 / reps
+            tot_b += e1.elapsed_time(e2) * 1e3 / reps
+            del Wd
+        eq_b = sum(ph_us["dx"]) + sum(ph_us["dw"])
+        dense = {"fwd_us": round(tot_f, 2), "fwd_tflops": round(fwd_flops / (tot_f * 1e-6) / 1e12, 2),
+                 "fwd_speedup": round(tot_f / fwd_us, 3), "bwd_us": round(tot_b, 2),
+                 "bwd_speedup": (round(tot_b / eq_b, 3) if not args.forward_only else None),
+                 "what": "torch.matmul (hipBLASLt) on the pre-expanded dense weight, same dtype"}
+
+    if args.copy_calibration_mb:
+        nb = args.copy_calibration_mb * (1 << 20)
+        src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(layers)
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description, "dtype": dt,
+                   "layers": [{"name": L.name, "N": L.N, "C": L.C, "D": L.D} for (L, _, _, _) in layers],
+                   "T": 4, "step": ("prepare+forward" if args.forward_only else "prepare+forward+dX+dw"),
+                   "buffer_sets": nsets},
+        "fwd_mfma_frac": round(achieved / peak, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "dense_gemm": dense,
+        "per_layer": per_layer,
+    }
+    if args.forward_only:
+        out["note"] = "forward-only profiling run, not a bench line"
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

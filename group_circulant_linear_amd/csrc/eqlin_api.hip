@@ -1,0 +1,192 @@
+// C ABI of the p4 group-circulant linear layer: argument validation, tile
+// choice and kernel launches.  The contract of every entry point is stated in
+// include/eqlin.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "eqlin.h"
+#include "eqlin_kernels.h"
+
+namespace {
+
+constexpr int kNumCu = 256;  // MI355X compute units (8 XCDs x 32)
+thread_local int g_last_hip_error = 0;
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int elem_bytes(int dtype) { return dtype == EQLIN_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape / dtype checks common to every entry point.
+int check_shape(int64_t N, int C, int D, int T, int dtype) {
+  if (dtype != EQLIN_F32 && dtype != EQLIN_F16) return EQLIN_EINVAL;
+  if (T != 4) return EQLIN_ENOTSUP;
+  if (N < 0 || C <= 0 || D <= 0 || (C % 4) != 0 || (D % 4) != 0) return EQLIN_EINVAL;
+  if (dtype == EQLIN_F16 && (((C / 4) % 2) != 0 || ((D / 4) % 2) != 0)) return EQLIN_ENOTSUP;
+  return EQLIN_OK;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return EQLIN_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return EQLIN_EHIP;
+}
+
+size_t plane_bytes(int C, int D, int dtype) {
+  return static_cast<size_t>(C / 4) * static_cast<size_t>(D / 4) * 4u * static_cast<size_t>(elem_bytes(dtype));
+}
+
+size_t transpose_offset(int C, int D, int dtype) { return (plane_bytes(C, D, dtype) + 255u) & ~size_t(255); }
+
+// Forward tile choice: the largest workgroup tile that still gives every CU
+// at least one workgroup; EQLIN_FWD_TILE (11, 12, 21, 22) overrides.
+int choose_fwd_tile(int dtype, int64_t nrows, int mg) {
+  if (const char* env = getenv("EQLIN_FWD_TILE")) {
+    const int t = atoi(env);
+    if (t == 11 || t == 12 || t == 21 || t == 22) return t;
+  }
+  auto tiles = [&](int fm, int fn) { return cdiv(nrows, 64 * fm) * cdiv(mg, 64 * fn); };
+  if (dtype == EQLIN_F32) return tiles(2, 1) >= kNumCu ? 21 : 11;
+  if (tiles(2, 2) >= kNumCu) return 22;
+  if (tiles(2, 1) >= kNumCu) return 21;
+  return 11;
+}
+
+// Row splits of the dw reduction: enough workgroups to cover the chip twice,
+// each split a whole number of pipeline stages.
+struct DwPlan {
+  int64_t rows_per_split;
+  int nsplit;
+};
+
+DwPlan plan_dw(int64_t N, int C, int D, int dtype) {
+  DwPlan p{0, 0};
+  if (N <= 0) return p;
+  const int64_t tiles = cdiv(D / 4, 64) * cdiv(C / 4, 64);
+  const int64_t stage = eqlin::dw_rows_per_stage(dtype);
+  int64_t want = cdiv(2 * kNumCu, tiles);
+  const int64_t max_split = cdiv(N, stage);
+  if (want > max_split) want = max_split;
+  if (want < 1) want = 1;
+  p.rows_per_split = cdiv(cdiv(N, want), stage) * stage;
+  p.nsplit = static_cast<int>(cdiv(N, p.rows_per_split));
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int eqlin_version(void) { return 100; }
+
+const char* eqlin_status_str(int status) {
+  switch (status) {
+    case EQLIN_OK: return "ok";
+    case EQLIN_EINVAL: return "invalid argument";
+    case EQLIN_ENOTSUP: return "unsupported configuration (T must be 4; f16 needs even group counts)";
+    case EQLIN_EALIGN: return "data pointer not 16-byte aligned";
+    case EQLIN_EWORKSPACE: return "workspace or prepared-weight buffer too small";
+    case EQLIN_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int eqlin_last_hip_error(void) { return g_last_hip_error; }
+
+size_t eqlin_prepared_weight_bytes(int C, int D, int T, int dtype) {
+  if (check_shape(0, C, D, T, dtype) != EQLIN_OK) return 0;
+  return transpose_offset(C, D, dtype) + plane_bytes(C, D, dtype);
+}
+
+size_t eqlin_prepared_transpose_offset(int C, int D, int T, int dtype) {
+  if (check_shape(0, C, D, T, dtype) != EQLIN_OK) return 0;
+  return transpose_offset(C, D, dtype);
+}
+
+int eqlin_prepare_weights(const void* w, int C, int D, int T, int dtype, void* W_hat, size_t W_hat_bytes,
+                          void* stream) {
+  int st = check_shape(0, C, D, T, dtype);
+  if (st != EQLIN_OK) return st;
+  if (!w || !W_hat) return EQLIN_EINVAL;
+  if (!aligned16(w) || !aligned16(W_hat)) return EQLIN_EALIGN;
+  if (W_hat_bytes < eqlin_prepared_weight_bytes(C, D, T, dtype)) return EQLIN_EWORKSPACE;
+  char* base = static_cast<char*>(W_hat);
+  return hip_status(eqlin::launch_prepare(dtype, w, base, base + transpose_offset(C, D, dtype), D / 4, C / 4,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int eqlin_forward(const void* X, int64_t N, int C, int D, int T, const void* W_hat, void* Y, int dtype,
+                  void* stream) {
+  int st = check_shape(N, C, D, T, dtype);
+  if (st != EQLIN_OK) return st;
+  if (N == 0) return EQLIN_OK;
+  if (!X || !W_hat || !Y) return EQLIN_EINVAL;
+  if (!aligned16(X) || !aligned16(W_hat) || !aligned16(Y)) return EQLIN_EALIGN;
+  const int tile = choose_fwd_tile(dtype, N, D / 4);
+  return hip_status(
+      eqlin::launch_forward(dtype, tile, X, W_hat, Y, N, C / 4, D / 4, static_cast<hipStream_t>(stream)));
+}
+
+size_t eqlin_backward_workspace_bytes(int64_t N, int C, int D, int T, int dtype) {
+  if (check_shape(N, C, D, T, dtype) != EQLIN_OK) return 0;
+  const DwPlan p = plan_dw(N, C, D, dtype);
+  return static_cast<size_t>(p.nsplit) * 4u * static_cast<size_t>(C / 4) * static_cast<size_t>(D / 4) *
+         sizeof(float);
+}
+
+int eqlin_backward_dx(const void* dY, int64_t N, int C, int D, int T, const void* W_hat, void* dX, int dtype,
+                      void* stream) {
+  int st = check_shape(N, C, D, T, dtype);
+  if (st != EQLIN_OK) return st;
+  if (N == 0) return EQLIN_OK;
+  if (!dY || !W_hat || !dX) return EQLIN_EINVAL;
+  if (!aligned16(dY) || !aligned16(W_hat) || !aligned16(dX)) return EQLIN_EALIGN;
+  // dX = dY W: the forward kernel with the transposed, conjugated planes
+  // (input groups D', output groups C').
+  const char* wb = static_cast<const char*>(W_hat) + transpose_offset(C, D, dtype);
+  const int tile = choose_fwd_tile(dtype, N, C / 4);
+  return hip_status(
+      eqlin::launch_forward(dtype, tile, dY, wb, dX, N, D / 4, C / 4, static_cast<hipStream_t>(stream)));
+}
+
+int eqlin_backward_dw(const void* dY, const void* X, int64_t N, int C, int D, int T, float* dw, void* workspace,
+                      size_t workspace_bytes, int dtype, void* stream) {
+  int st = check_shape(N, C, D, T, dtype);
+  if (st != EQLIN_OK) return st;
+  if (!dw) return EQLIN_EINVAL;
+  if (N > 0 && (!dY || !X || !workspace)) return EQLIN_EINVAL;
+  if (!aligned16(dw)) return EQLIN_EALIGN;
+  if (N > 0 && (!aligned16(dY) || !aligned16(X) || !aligned16(workspace))) return EQLIN_EALIGN;
+  if (workspace_bytes < eqlin_backward_workspace_bytes(N, C, D, T, dtype)) return EQLIN_EWORKSPACE;
+  const DwPlan p = plan_dw(N, C, D, dtype);
+  return hip_status(eqlin::launch_dw(dtype, dY, X, static_cast<float*>(workspace), dw, N, D / 4, C / 4,
+                                     p.rows_per_split, p.nsplit, static_cast<hipStream_t>(stream)));
+}
+
+int eqlin_backward(const void* dY, const void* X, int64_t N, int C, int D, int T, const void* W_hat, void* dX,
+                   float* dw, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  int st = check_shape(N, C, D, T, dtype);
+  if (st != EQLIN_OK) return st;
+  if (!dX && !dw) return EQLIN_EINVAL;
+  // validate both halves before launching either
+  if (dX && N > 0) {
+    if (!dY || !W_hat) return EQLIN_EINVAL;
+    if (!aligned16(dY) || !aligned16(W_hat) || !aligned16(dX)) return EQLIN_EALIGN;
+  }
+  if (dw) {
+    if (N > 0 && (!dY || !X || !workspace)) return EQLIN_EINVAL;
+    if (!aligned16(dw)) return EQLIN_EALIGN;
+    if (N > 0 && (!aligned16(dY) || !aligned16(X) || !aligned16(workspace))) return EQLIN_EALIGN;
+    if (workspace_bytes < eqlin_backward_workspace_bytes(N, C, D, T, dtype)) return EQLIN_EWORKSPACE;
+  }
+  if (dX) {
+    st = eqlin_backward_dx(dY, N, C, D, T, W_hat, dX, dtype, stream);
+    if (st != EQLIN_OK) return st;
+  }
+  if (dw) return eqlin_backward_dw(dY, X, N, C, D, T, dw, workspace, workspace_bytes, dtype, stream);
+  return EQLIN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,241 @@
+"""Thin Python binding of libeqlin.so (argument marshalling only).
+
+Every step of the layer runs in the HIP library; this module checks tensor
+shapes, dtypes, devices and contiguity, allocates outputs with PyTorch (device
+memory plumbing) and passes raw pointers plus torch's current HIP stream to the
+C ABI declared in include/eqlin.h.  There is no fallback: if the library is not
+built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import NamedTuple, Optional
+
+import torch
+
+from .build import LIB, INCLUDE
+
+T_P4 = 4
+EQLIN_F32, EQLIN_F16 = 0, 1
+STATUS = {0: "EQLIN_OK", 1: "EQLIN_EINVAL", 2: "EQLIN_ENOTSUP", 3: "EQLIN_EALIGN",
+          4: "EQLIN_EWORKSPACE", 5: "EQLIN_EHIP"}
+_DTYPES = {torch.float32: EQLIN_F32, torch.float16: EQLIN_F16}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class EqlinError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+def header_symbols() -> list:
+    """Names of every function include/eqlin.h declares."""
+    with open(os.path.join(INCLUDE, "eqlin.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(eqlin_\w+)\s*\(", text)))
+
+
+def load_library(path: str = LIB) -> ctypes.CDLL:
+    """Load libeqlin.so and declare the C signatures (raises if not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run __graft_entry__.build() "
+                           "or python -m group_circulant_linear_amd.build")
+    lib = ctypes.CDLL(path)
+    c_int, c_i64, c_sz, c_vp, c_fp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p
+    sigs = {
+        "eqlin_version": (c_int, []),
+        "eqlin_status_str": (ctypes.c_char_p, [c_int]),
+        "eqlin_last_hip_error": (c_int, []),
+        "eqlin_prepared_weight_bytes": (c_sz, [c_int, c_int, c_int, c_int]),
+        "eqlin_prepared_transpose_offset": (c_sz, [c_int, c_int, c_int, c_int]),
+        "eqlin_prepare_weights": (c_int, [c_vp, c_int, c_int, c_int, c_int, c_vp, c_sz, c_vp]),
+        "eqlin_forward": (c_int, [c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_int, c_vp]),
+        "eqlin_backward_workspace_bytes": (c_sz, [c_i64, c_int, c_int, c_int, c_int]),
+        "eqlin_backward": (c_int, [c_vp, c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_fp, c_vp, c_sz,
+                                   c_int, c_vp]),
+        "eqlin_backward_dx": (c_int, [c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_int, c_vp]),
+        "eqlin_backward_dw": (c_int, [c_vp, c_vp, c_i64, c_int, c_int, c_int, c_fp, c_vp, c_sz, c_int, c_vp]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        lib = load_library()
+        msg = lib.eqlin_status_str(status).decode()
+        if status == 5:
+            msg += f", hipError {lib.eqlin_last_hip_error()}"
+        raise EqlinError(fn, status, msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or float16")
+    return _DTYPES[t.dtype]
+
+
+def _need_cuda(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+class Prepared(NamedTuple):
+    """Prepared weight spectra (opaque byte buffer) and the layer they belong to."""
+    buf: torch.Tensor
+    C: int
+    D: int
+    dtype: torch.dtype
+
+
+def eqlin_prepared_weight_bytes(C: int, D: int, dtype: torch.dtype) -> int:
+    return int(load_library().eqlin_prepared_weight_bytes(C, D, T_P4, _DTYPES[dtype]))
+
+
+def eqlin_prepared_transpose_offset(C: int, D: int, dtype: torch.dtype) -> int:
+    return int(load_library().eqlin_prepared_transpose_offset(C, D, T_P4, _DTYPES[dtype]))
+
+
+def eqlin_prepare_weights(w: torch.Tensor, out: Optional[torch.Tensor] = None) -> Prepared:
+    """w [D'][C'][4] -> prepared spectra for eqlin_forward / eqlin_backward."""
+    lib = load_library()
+    _need_cuda(w, "w")
+    dt = _dtype_code(w)
+    if w.dim() != 3 or w.shape[2] != T_P4:
+        raise ValueError(f"w must have shape [D/4, C/4, 4], got {tuple(w.shape)}")
+    D, C = 4 * w.shape[0], 4 * w.shape[1]
+    nbytes = int(lib.eqlin_prepared_weight_bytes(C, D, T_P4, dt))
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    _need_cuda(out, "out")
+    _check("eqlin_prepare_weights",
+           lib.eqlin_prepare_weights(_ptr(w), C, D, T_P4, dt, _ptr(out), out.numel() * out.element_size(),
+                                     _stream(w)))
+    return Prepared(out, C, D, w.dtype)
+
+
+def eqlin_forward(X: torch.Tensor, W_hat: Prepared, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X W^T for the group-circulant W, X [N][C] -> Y [N][D]."""
+    lib = load_library()
+    _need_cuda(X, "X")
+    dt = _dtype_code(X)
+    if X.dtype != W_hat.dtype:
+        raise TypeError("X and the prepared weights differ in dtype")
+    if X.dim() != 2 or X.shape[1] != W_hat.C:
+        raise ValueError(f"X must have shape [N, {W_hat.C}], got {tuple(X.shape)}")
+    N = X.shape[0]
+    if out is None:
+        out = torch.empty((N, W_hat.D), dtype=X.dtype, device=X.device)
+    _need_cuda(out, "out")
+    if tuple(out.shape) != (N, W_hat.D) or out.dtype != X.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    _check("eqlin_forward", lib.eqlin_forward(_ptr(X), N, W_hat.C, W_hat.D, T_P4, _ptr(W_hat.buf), _ptr(out),
+                                              dt, _stream(X)))
+    return out
+
+
+def eqlin_backward_workspace_bytes(N: int, C: int, D: int, dtype: torch.dtype) -> int:
+    return int(load_library().eqlin_backward_workspace_bytes(N, C, D, T_P4, _DTYPES[dtype]))
+
+
+def eqlin_backward(dY: torch.Tensor, X: Optional[torch.Tensor], W_hat: Prepared, need_dx: bool = True,
+                   need_dw: bool = True, workspace: Optional[torch.Tensor] = None,
+                   dX_out: Optional[torch.Tensor] = None, dw_out: Optional[torch.Tensor] = None):
+    """(dX [N][C] or None, dw [D/4][C/4][4] float32 or None) for upstream gradient dY [N][D]."""
+    lib = load_library()
+    _need_cuda(dY, "dY")
+    dt = _dtype_code(dY)
+    if dY.dtype != W_hat.dtype:
+        raise TypeError("dY and the prepared weights differ in dtype")
+    C, D = W_hat.C, W_hat.D
+    if dY.dim() != 2 or dY.shape[1] != D:
+        raise ValueError(f"dY must have shape [N, {D}], got {tuple(dY.shape)}")
+    N = dY.shape[0]
+    if not (need_dx or need_dw):
+        raise ValueError("nothing to compute")
+    dX = dw = None
+    if need_dx:
+        dX = dX_out if dX_out is not None else torch.empty((N, C), dtype=dY.dtype, device=dY.device)
+        _need_cuda(dX, "dX")
+    ws_bytes = 0
+    if need_dw:
+        if X is None:
+            raise ValueError("dw needs X")
+        _need_cuda(X, "X")
+        if X.dtype != dY.dtype or tuple(X.shape) != (N, C):
+            raise ValueError(f"X must be [N, {C}] of dtype {dY.dtype}")
+        dw = dw_out if dw_out is not None else torch.empty((D // 4, C // 4, 4), dtype=torch.float32,
+                                                           device=dY.device)
+        _need_cuda(dw, "dw")
+        ws_bytes = int(lib.eqlin_backward_workspace_bytes(N, C, D, T_P4, dt))
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dY.device)
+        _need_cuda(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check("eqlin_backward",
+           lib.eqlin_backward(_ptr(dY), _ptr(X) if need_dw else None, N, C, D, T_P4, _ptr(W_hat.buf),
+                              _ptr(dX), _ptr(dw), _ptr(workspace) if need_dw else None, ws_bytes, dt,
+                              _stream(dY)))
+    return dX, dw
+
+
+def eqlin_backward_dx(dY: torch.Tensor, W_hat: Prepared, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dX = dY W, dY [N][D] -> dX [N][C]."""
+    lib = load_library()
+    _need_cuda(dY, "dY")
+    dt = _dtype_code(dY)
+    C, D = W_hat.C, W_hat.D
+    if dY.dtype != W_hat.dtype or dY.dim() != 2 or dY.shape[1] != D:
+        raise ValueError(f"dY must be [N, {D}] of dtype {W_hat.dtype}")
+    N = dY.shape[0]
+    if out is None:
+        out = torch.empty((N, C), dtype=dY.dtype, device=dY.device)
+    _need_cuda(out, "out")
+    _check("eqlin_backward_dx", lib.eqlin_backward_dx(_ptr(dY), N, C, D, T_P4, _ptr(W_hat.buf), _ptr(out), dt,
+                                                      _stream(dY)))
+    return out
+
+
+def eqlin_backward_dw(dY: torch.Tensor, X: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dw [D/4][C/4][4] (float32) from dY [N][D] and X [N][C]."""
+    lib = load_library()
+    _need_cuda(dY, "dY")
+    _need_cuda(X, "X")
+    dt = _dtype_code(dY)
+    if X.dtype != dY.dtype or X.dim() != 2 or dY.dim() != 2 or X.shape[0] != dY.shape[0]:
+        raise ValueError("dY [N, D] and X [N, C] must share N and dtype")
+    N, C, D = X.shape[0], X.shape[1], dY.shape[1]
+    if out is None:
+        out = torch.empty((D // 4, C // 4, 4), dtype=torch.float32, device=dY.device)
+    _need_cuda(out, "out")
+    ws_bytes = int(lib.eqlin_backward_workspace_bytes(N, C, D, T_P4, dt))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dY.device)
+    _need_cuda(workspace, "workspace")
+    _check("eqlin_backward_dw",
+           lib.eqlin_backward_dw(_ptr(dY), _ptr(X), N, C, D, T_P4, _ptr(out), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), dt, _stream(dY)))
+    return out

@@ -1,0 +1,147 @@
+/*
+ * eqlin.h -- C ABI of the MI355X (gfx950) p4 group-circulant linear layer
+ * ("Flash EQ-Linear").
+ *
+ * The layer (Flash EQ-Linear technical summary, gist.science 2607.21271,
+ * section "Key insight"): the dense weight W (D x C) is made of
+ * (D/4) x (C/4) blocks, block (d', c') being the 4 x 4 circulant of a
+ * learnable vector w[d', c', 0..3]:
+ *
+ *     W[4d' + t, 4c' + s] = w[d', c', (t - s) mod 4]
+ *     Y = X W^T,  Y[n, 4d' + t] = sum_{c', s} w[d', c', (t - s) mod 4] X[n, 4c' + s]
+ *
+ * It is computed exactly through the group DFT ("Algorithmic approach",
+ * items 1-2; "Specialisation for the p4 rotation group"): only the
+ * non-redundant frequencies f0, f2 (real) and f1 (complex) of the real
+ * signals are formed, with add/sub-only transforms, and the contraction
+ * becomes six real per-frequency matrix products instead of sixteen.
+ *
+ * Conventions shared by every entry point
+ *   - T is the group size and must be 4 (the summary's method is specialised
+ *     to the p4 rotation group, "Limitations"); any other T -> EQLIN_ENOTSUP.
+ *   - C, D are the full channel widths, positive multiples of 4; C' = C/4 and
+ *     D' = D/4 are the group-channel counts.  The channel index is
+ *     group_channel * 4 + group_element (group element fastest).
+ *   - All matrices are row-major and contiguous:
+ *       X, dX  [N][C]      Y, dY  [N][D]      w  [D'][C'][4]     dw [D'][C'][4]
+ *   - dtype EQLIN_F32: X, Y, dY, dX, w in float32, arithmetic in float32.
+ *     dtype EQLIN_F16: X, Y, dY, dX, w stored as IEEE binary16; the group
+ *     transforms run in float32, the Fourier operands are rounded once
+ *     (nearest-even) to binary16 for the matrix cores, products accumulate in
+ *     float32, and outputs are rounded nearest-even to binary16.  dw is float32
+ *     for both dtypes.  With EQLIN_F16, C' and D' must be even
+ *     (otherwise EQLIN_ENOTSUP).
+ *   - Every data pointer is a DEVICE pointer on the current HIP device, owned
+ *     by the caller, 16-byte aligned (else EQLIN_EALIGN).  The library never
+ *     allocates, frees or retains memory and keeps no mutable global state;
+ *     calls are thread-safe.  Outputs must not alias inputs.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on it and returns without synchronising.
+ *   - All arguments are validated before any kernel is enqueued: on any error
+ *     nothing is launched and no output is touched.  A launch failure reported
+ *     by the HIP runtime returns EQLIN_EHIP (see eqlin_last_hip_error()).
+ *   - N == 0 is a valid empty batch: forward and dX enqueue nothing, dw is
+ *     written as zeros.
+ */
+#ifndef EQLIN_H
+#define EQLIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage dtypes. */
+enum { EQLIN_F32 = 0, EQLIN_F16 = 1 };
+
+/* Status codes returned by every int-returning entry point. */
+enum {
+  EQLIN_OK = 0,
+  EQLIN_EINVAL = 1,     /* bad size, negative N, null required pointer, unknown dtype */
+  EQLIN_ENOTSUP = 2,    /* T != 4, or an odd group count with EQLIN_F16 */
+  EQLIN_EALIGN = 3,     /* a data pointer is not 16-byte aligned */
+  EQLIN_EWORKSPACE = 4, /* workspace / prepared-weight buffer too small */
+  EQLIN_EHIP = 5        /* the HIP runtime reported an error for a launch */
+};
+
+/* Library ABI version (major * 100 + minor). */
+int eqlin_version(void);
+
+/* Static string for a status code ("unknown status" for others). */
+const char* eqlin_status_str(int status);
+
+/* hipError_t value that produced the calling thread's last EQLIN_EHIP (0 if none). */
+int eqlin_last_hip_error(void);
+
+/*
+ * Size in bytes of the prepared-weight buffer W_hat for a layer, or 0 if the
+ * arguments are invalid.
+ *
+ * W_hat layout (element = the storage dtype, es = 4 or 2 bytes):
+ *   offset 0:            forward planes  Wf[D'][C'][4] = (F0, F2, Re F1, Im F1)
+ *   offset eqlin_prepared_transpose_offset(): transpose planes
+ *                        Wb[C'][D'][4] = (F0, F2, Re F1, -Im F1)
+ * where F_k[d', c'] = sum_u w[d', c', u] exp(-2 pi i k u / 4) is the group DFT
+ * of each circulant vector ("Algorithmic approach", item 1), F3 = conj(F1)
+ * being redundant for real w (item 2).  Wb is the spectrum of the transposed,
+ * group-reversed weight used by the dX pass (a conjugate, so the sign of Im F1
+ * flips).
+ */
+size_t eqlin_prepared_weight_bytes(int C, int D, int T, int dtype);
+size_t eqlin_prepared_transpose_offset(int C, int D, int T, int dtype);
+
+/*
+ * a1: group DFT of the weights.  w [D'][C'][4] (device, storage dtype) ->
+ * W_hat (device, W_hat_bytes >= eqlin_prepared_weight_bytes, else
+ * EQLIN_EWORKSPACE).  Run it once per weight version; the forward and
+ * backward calls consume W_hat read-only.  The transform uses adds and
+ * subtracts only ("Specialisation for the p4 rotation group").
+ */
+int eqlin_prepare_weights(const void* w, int C, int D, int T, int dtype,
+                          void* W_hat, size_t W_hat_bytes, void* stream);
+
+/*
+ * a2-a4: Y = X W^T.  X [N][C], Y [N][D] (device, storage dtype), W_hat from
+ * eqlin_prepare_weights for the same (C, D, dtype).  One fused kernel: group
+ * DFT of X tiles into on-chip Fourier planes, the six real per-frequency
+ * products on the matrix cores, inverse DFT (scales 1/4 and 1/2) in registers
+ * and a single store of Y; no intermediate global-memory writes
+ * ("Implementation" section).
+ */
+int eqlin_forward(const void* X, int64_t N, int C, int D, int T,
+                  const void* W_hat, void* Y, int dtype, void* stream);
+
+/* Workspace bytes eqlin_backward / eqlin_backward_dw need for this shape. */
+size_t eqlin_backward_workspace_bytes(int64_t N, int C, int D, int T, int dtype);
+
+/*
+ * a5 + a6: backward pass for upstream gradient dY [N][D].
+ *   dX [N][C] = dY W   (transposed group-circulant; skipped if dX == NULL)
+ *   dw [D'][C'][4] (float32) = d<dY, Y>/dw
+ *      = sum_n sum_t dY[n, 4d'+t] X[n, 4c' + (t-u) mod 4]   (skipped if dw == NULL)
+ * dw is formed per frequency as sum_n G_k conj(Xhat_k) (G = group DFT of dY),
+ * reduced over row splits in a fixed order (deterministic) and inverse
+ * transformed along u.  `workspace` (device, >= eqlin_backward_workspace_bytes)
+ * holds the per-split partial spectra; it may be NULL only when dw == NULL.
+ * X may be NULL when dw == NULL.
+ */
+int eqlin_backward(const void* dY, const void* X, int64_t N, int C, int D, int T,
+                   const void* W_hat, void* dX, float* dw,
+                   void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/* a5 alone: dX = dY W.  Same contract as eqlin_backward with dw == NULL. */
+int eqlin_backward_dx(const void* dY, int64_t N, int C, int D, int T,
+                      const void* W_hat, void* dX, int dtype, void* stream);
+
+/* a6 alone: dw only.  Same contract as eqlin_backward with dX == NULL. */
+int eqlin_backward_dw(const void* dY, const void* X, int64_t N, int C, int D, int T,
+                      float* dw, void* workspace, size_t workspace_bytes,
+                      int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EQLIN_H */

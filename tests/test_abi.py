@@ -1,0 +1,98 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments before any kernel launch (no GPU needed:
+every call here fails validation, so nothing is enqueued)."""
+import ctypes
+
+import pytest
+
+from group_circulant_linear_amd import eqlin
+
+OK, EINVAL, ENOTSUP, EALIGN, EWORKSPACE = 0, 1, 2, 3, 4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return eqlin.load_library()
+
+
+def test_exports_every_header_symbol(lib):
+    names = eqlin.header_symbols()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.eqlin_version() >= 100
+    for s in range(6):
+        assert lib.eqlin_status_str(s)
+    assert lib.eqlin_status_str(99) == b"unknown status"
+    assert lib.eqlin_last_hip_error() == 0
+
+
+def test_size_queries(lib):
+    # fp32: D'*C'*4 floats per plane set, transposed copy at a 256 B boundary
+    assert lib.eqlin_prepared_transpose_offset(768, 768, 4, 0) == 192 * 192 * 16
+    assert lib.eqlin_prepared_weight_bytes(768, 768, 4, 0) == 2 * 192 * 192 * 16
+    assert lib.eqlin_prepared_weight_bytes(768, 3072, 4, 1) == 2 * 192 * 768 * 8
+    off = lib.eqlin_prepared_transpose_offset(4, 4, 4, 0)
+    assert off == 256 and lib.eqlin_prepared_weight_bytes(4, 4, 4, 0) == 256 + 16
+    assert lib.eqlin_prepared_weight_bytes(768, 768, 3, 0) == 0
+    assert lib.eqlin_prepared_weight_bytes(770, 768, 4, 0) == 0
+    assert lib.eqlin_prepared_weight_bytes(12, 16, 4, 1) == 0      # odd C' with f16
+    assert lib.eqlin_backward_workspace_bytes(0, 768, 768, 4, 0) == 0
+    ws = lib.eqlin_backward_workspace_bytes(12608, 768, 768, 4, 0)
+    assert ws > 0 and ws % (4 * 192 * 192 * 4) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)        # aligned, never dereferenced (validation fails first)
+MISALIGNED = ctypes.c_void_p(0x1004)
+
+
+def test_forward_validation(lib):
+    f = lib.eqlin_forward
+    assert f(FAKE, 8, 32, 32, 3, FAKE, FAKE, 0, None) == ENOTSUP
+    assert f(FAKE, 8, 30, 32, 4, FAKE, FAKE, 0, None) == EINVAL
+    assert f(FAKE, 8, 32, 0, 4, FAKE, FAKE, 0, None) == EINVAL
+    assert f(FAKE, -1, 32, 32, 4, FAKE, FAKE, 0, None) == EINVAL
+    assert f(FAKE, 8, 32, 32, 4, FAKE, FAKE, 7, None) == EINVAL
+    assert f(None, 8, 32, 32, 4, FAKE, FAKE, 0, None) == EINVAL
+    assert f(FAKE, 8, 32, 32, 4, None, FAKE, 0, None) == EINVAL
+    assert f(MISALIGNED, 8, 32, 32, 4, FAKE, FAKE, 0, None) == EALIGN
+    assert f(FAKE, 8, 32, 32, 4, FAKE, MISALIGNED, 0, None) == EALIGN
+    assert f(FAKE, 8, 20, 32, 4, FAKE, FAKE, 1, None) == ENOTSUP   # C'=5 odd with f16
+    assert f(None, 0, 32, 32, 4, None, None, 0, None) == OK        # empty batch: nothing enqueued
+
+
+def test_prepare_validation(lib):
+    p = lib.eqlin_prepare_weights
+    need = lib.eqlin_prepared_weight_bytes(32, 32, 4, 0)
+    assert p(FAKE, 32, 32, 4, 0, FAKE, need - 1, None) == EWORKSPACE
+    assert p(None, 32, 32, 4, 0, FAKE, need, None) == EINVAL
+    assert p(MISALIGNED, 32, 32, 4, 0, FAKE, need, None) == EALIGN
+    assert p(FAKE, 32, 32, 5, 0, FAKE, need, None) == ENOTSUP
+
+
+def test_backward_validation(lib):
+    b = lib.eqlin_backward
+    ws = lib.eqlin_backward_workspace_bytes(64, 32, 32, 4, 0)
+    assert b(FAKE, FAKE, 64, 32, 32, 4, FAKE, None, None, FAKE, ws, 0, None) == EINVAL   # nothing requested
+    assert b(FAKE, FAKE, 64, 32, 32, 4, FAKE, FAKE, FAKE, FAKE, ws - 1, 0, None) == EWORKSPACE
+    assert b(FAKE, None, 64, 32, 32, 4, FAKE, None, FAKE, FAKE, ws, 0, None) == EINVAL   # dw without X
+    assert b(FAKE, FAKE, 64, 32, 32, 4, FAKE, FAKE, FAKE, None, ws, 0, None) == EINVAL   # dw without workspace
+    assert b(FAKE, FAKE, 64, 32, 32, 4, None, FAKE, None, None, 0, 0, None) == EINVAL    # dX without W_hat
+    assert b(FAKE, FAKE, 64, 32, 32, 4, FAKE, MISALIGNED, FAKE, FAKE, ws, 0, None) == EALIGN
+    assert b(FAKE, FAKE, 64, 32, 32, 2, FAKE, FAKE, FAKE, FAKE, ws, 0, None) == ENOTSUP
+    d = lib.eqlin_backward_dw
+    assert d(FAKE, FAKE, 64, 32, 32, 4, None, FAKE, ws, 0, None) == EINVAL
+    assert d(FAKE, FAKE, 64, 32, 32, 4, FAKE, FAKE, 0, 0, None) == EWORKSPACE
+    x = lib.eqlin_backward_dx
+    assert x(FAKE, 64, 32, 32, 4, FAKE, None, 0, None) == EINVAL
+    assert x(None, 0, 32, 32, 4, None, None, 0, None) == OK
+
+
+def test_python_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    w = torch.zeros(8, 8, 4)
+    with pytest.raises(ValueError):
+        eqlin.eqlin_prepare_weights(w)

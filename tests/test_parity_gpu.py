@@ -1,0 +1,228 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Metric: max|gpu - ref| / max|ref| over the compared outputs.  Bars: 1e-5 for
+fp32, 3e-3 for f16 storage with fp32 accumulation.  Small shapes span several
+tiles plus ragged row / column / k tails and are compared element by element;
+the full-size workloads are compared whole where the oracle takes seconds
+(ViT-B attention forward and backward) and on sampled rows otherwise.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from group_circulant_linear_amd.inputs import WORKLOADS, make_layer_inputs
+
+torch = pytest.importorskip("torch")
+eq = pytest.importorskip("group_circulant_linear_amd.eqlin")
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 3e-3}
+DEV = "cuda"
+
+
+def rel_err(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    return float(np.max(np.abs(got - ref)) / max(float(np.max(np.abs(ref))), 1e-300))
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.double().cpu().numpy()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# --------------------------------------------------------------------- a1
+
+@pytest.mark.parametrize("dt,Dp,Cp", [("f32", 5, 3), ("f32", 192, 192), ("f16", 6, 4), ("f16", 768, 192)])
+def test_prepared_planes_match_group_spectrum(dt, Dp, Cp):
+    say(f"prepare {dt} D'={Dp} C'={Cp}")
+    _, w, _ = make_layer_inputs(4, 4 * Cp, 4 * Dp, dt, seed=1, with_dy=False)
+    Wh = eq.eqlin_prepare_weights(dev(w))
+    tdt = torch.float32 if dt == "f32" else torch.float16
+    buf = Wh.buf
+    esz = 4 if dt == "f32" else 2
+    nplane = Dp * Cp * 4
+    off = eq.eqlin_prepared_transpose_offset(4 * Cp, 4 * Dp, tdt)
+    wf = host(buf[: nplane * esz].view(tdt)).reshape(Dp, Cp, 4)
+    wb = host(buf[off: off + nplane * esz].view(tdt)).reshape(Cp, Dp, 4)
+    ref = oracle.kept_p4_planes(w.astype(np.float64))
+    tol = 1e-6 if dt == "f32" else 1e-3
+    assert rel_err(wf, ref) < tol
+    conj = ref.copy()
+    conj[..., 3] = -conj[..., 3]
+    assert rel_err(wb, conj.transpose(1, 0, 2)) < tol
+
+
+# ----------------------------------------------------------------- forward
+
+SMALL_SHAPES = {
+    "f32": [(64, 32, 32), (1, 4, 4), (131, 12, 20), (1000, 160, 96), (257, 64 * 4 + 4 * 20, 4 * 70),
+            (333, 4 * 200, 4 * 130)],
+    "f16": [(64, 32, 32), (1, 8, 8), (131, 8 * 3, 8 * 5), (1000, 8 * 20, 8 * 12), (257, 4 * 34, 4 * 70),
+            (333, 4 * 200, 4 * 130)],
+}
+
+
+def _forward_case(dt, N, C, D, seed=0):
+    X, w, _ = make_layer_inputs(N, C, D, dt, seed=seed, with_dy=False)
+    Wh = eq.eqlin_prepare_weights(dev(w))
+    Y = eq.eqlin_forward(dev(X), Wh)
+    return X, w, host(Y)
+
+
+@pytest.mark.parametrize("tile", ["auto", "11", "12", "21", "22"])
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_forward_small_shapes_all_tiles(dt, tile, monkeypatch):
+    if tile != "auto":
+        monkeypatch.setenv("EQLIN_FWD_TILE", tile)
+    for (N, C, D) in SMALL_SHAPES[dt]:
+        say(f"forward {dt} tile={tile} N={N} C={C} D={D}")
+        X, w, Y = _forward_case(dt, N, C, D)
+        err = rel_err(Y, oracle.forward_direct(X, w))
+        assert err <= TOL[dt], (N, C, D, err)
+
+
+def _sample_rows(N, rng, k=96):
+    rows = set(range(8)) | set(range(N - 8, N))
+    rows |= set(rng.choice(N, size=k, replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name,dt", [("tiny", "f32"), ("vitb_attn", "f32"), ("vitb_mlp", "f16"),
+                                     ("vith_mlp", "f32"), ("vith_mlp", "f16")])
+def test_forward_workloads(name, dt):
+    wl = WORKLOADS[name]
+    for li, L in enumerate(wl.layers):
+        say(f"forward workload {name} {L.name} {dt} N={L.N} C={L.C} D={L.D}")
+        X, w, _ = make_layer_inputs(L.N, L.C, L.D, dt, seed=0, layer=li, with_dy=False)
+        Wh = eq.eqlin_prepare_weights(dev(w))
+        Y = host(eq.eqlin_forward(dev(X), Wh))
+        if L.N * L.C * L.D <= 12608 * 768 * 768:
+            err = rel_err(Y, oracle.forward_direct(X, w))
+        else:
+            rows = _sample_rows(L.N, np.random.default_rng(li))
+            err = rel_err(Y[rows], oracle.forward_rows(X, w, rows))
+        say(f"  rel err {err:.3e}")
+        assert err <= TOL[dt]
+
+
+# ---------------------------------------------------------------- backward
+
+BWD_SHAPES = {
+    "f32": [(64, 32, 32), (1, 4, 4), (77, 12, 20), (1000, 160, 96), (3001, 4 * 70, 4 * 130)],
+    "f16": [(64, 32, 32), (1, 8, 8), (77, 8 * 3, 8 * 5), (1000, 8 * 20, 8 * 12), (3001, 4 * 70, 4 * 130)],
+}
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_backward_small_shapes(dt):
+    for (N, C, D) in BWD_SHAPES[dt]:
+        say(f"backward {dt} N={N} C={C} D={D}")
+        X, w, dY = make_layer_inputs(N, C, D, dt, seed=2)
+        Wh = eq.eqlin_prepare_weights(dev(w))
+        dX, dw = eq.eqlin_backward(dev(dY), dev(X), Wh)
+        dXr, dwr = oracle.backward_direct(dY, X, w)
+        e1, e2 = rel_err(host(dX), dXr), rel_err(host(dw), dwr)
+        assert e1 <= TOL[dt], ("dX", N, C, D, e1)
+        assert e2 <= TOL[dt], ("dw", N, C, D, e2)
+
+
+@pytest.mark.parametrize("dt", ["f16", "f32"])
+def test_backward_workload_vitb(dt):
+    L = WORKLOADS["vitb_attn_bwd"].layers[0]
+    say(f"backward workload vitb_attn_bwd {dt} N={L.N} C={L.C} D={L.D}")
+    X, w, dY = make_layer_inputs(L.N, L.C, L.D, dt, seed=0)
+    Wh = eq.eqlin_prepare_weights(dev(w))
+    dX, dw = eq.eqlin_backward(dev(dY), dev(X), Wh)
+    e1 = rel_err(host(dX), oracle.dx_direct(dY, w))
+    e2 = rel_err(host(dw), oracle.dw_direct(dY, X))
+    say(f"  dX rel err {e1:.3e}  dw rel err {e2:.3e}")
+    assert e1 <= TOL[dt] and e2 <= TOL[dt]
+
+
+def test_backward_separate_entry_points_agree():
+    X, w, dY = make_layer_inputs(500, 64, 96, "f32", seed=4)
+    Wh = eq.eqlin_prepare_weights(dev(w))
+    dX, dw = eq.eqlin_backward(dev(dY), dev(X), Wh)
+    dX2 = eq.eqlin_backward_dx(dev(dY), Wh)
+    dw2 = eq.eqlin_backward_dw(dev(dY), dev(X))
+    assert torch.equal(dX, dX2) and torch.equal(dw, dw2)
+
+
+# -------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_empty_batch(dt):
+    tdt = torch.float32 if dt == "f32" else torch.float16
+    _, w, _ = make_layer_inputs(1, 32, 48, dt, seed=5, with_dy=False)
+    Wh = eq.eqlin_prepare_weights(dev(w))
+    X = torch.empty((0, 32), dtype=tdt, device=DEV)
+    dY = torch.empty((0, 48), dtype=tdt, device=DEV)
+    assert eq.eqlin_forward(X, Wh).shape == (0, 48)
+    dw = torch.full((12, 8, 4), float("nan"), device=DEV)
+    dX, dw = eq.eqlin_backward(dY, X, Wh, dw_out=dw)
+    torch.cuda.synchronize()
+    assert dX.shape == (0, 32)
+    assert torch.count_nonzero(dw).item() == 0
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_determinism(dt):
+    X, w, dY = make_layer_inputs(2000, 256, 384, dt, seed=6)
+    Wh = eq.eqlin_prepare_weights(dev(w))
+    tX, tdY = dev(X), dev(dY)
+    Y1 = eq.eqlin_forward(tX, Wh).clone()
+    Y2 = eq.eqlin_forward(tX, Wh)
+    dX1, dw1 = eq.eqlin_backward(tdY, tX, Wh)
+    dX2, dw2 = eq.eqlin_backward(tdY, tX, Wh)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2) and torch.equal(dX1, dX2) and torch.equal(dw1, dw2)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_row_isolation(dt):
+    # a NaN in row r of X may only reach row r of Y (checks tail masking and row mapping)
+    N, C, D = 300, 128, 160
+    X, w, _ = make_layer_inputs(N, C, D, dt, seed=7, with_dy=False)
+    Wh = eq.eqlin_prepare_weights(dev(w))
+    Y0 = host(eq.eqlin_forward(dev(X), Wh))
+    Xn = X.copy()
+    for r in (0, 131, N - 1):
+        Xn[r, 5] = np.nan
+    Y1 = host(eq.eqlin_forward(dev(Xn), Wh))
+    bad = np.isnan(Y1).any(axis=1)
+    assert set(np.nonzero(bad)[0].tolist()) == {0, 131, N - 1}
+    assert np.array_equal(Y1[~bad], Y0[~bad])
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_group_shift_equivariance(dt):
+    N, C, D = 512, 256, 192
+    X, w, _ = make_layer_inputs(N, C, D, dt, seed=8, with_dy=False)
+    Xr = np.roll(X.reshape(N, C // 4, 4), 1, axis=2).reshape(N, C)
+    Wh = eq.eqlin_prepare_weights(dev(w))
+    Y = host(eq.eqlin_forward(dev(X), Wh)).reshape(N, D // 4, 4)
+    Yr = host(eq.eqlin_forward(dev(Xr), Wh)).reshape(N, D // 4, 4)
+    assert rel_err(Yr, np.roll(Y, 1, axis=2)) <= TOL[dt]
+
+
+def test_non_default_stream():
+    X, w, dY = make_layer_inputs(700, 96, 64, "f32", seed=9)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        tX, tw, tdY = dev(X), dev(w), dev(dY)
+        Wh = eq.eqlin_prepare_weights(tw)
+        Y = eq.eqlin_forward(tX, Wh)
+        dX, dw = eq.eqlin_backward(tdY, tX, Wh)
+    s.synchronize()
+    assert rel_err(host(Y), oracle.forward_direct(X, w)) <= 1e-5
+    dXr, dwr = oracle.backward_direct(dY, X, w)
+    assert rel_err(host(dX), dXr) <= 1e-5 and rel_err(host(dw), dwr) <= 1e-5
