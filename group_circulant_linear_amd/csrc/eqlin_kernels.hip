@@ -183,20 +183,30 @@ template <int FM, int FN>
 struct Core<float, FM, FN> {
   __device__ __forceinline__ static void mma(f32x16 (&acc)[4][FM][FN], const u32x4 (&a)[4][FM],
                                              const u32x4 (&b)[4][FN]) {
+    // bit-cast whole vectors, then index (a bit-cast of one vector element
+    // would reinterpret the vector's first element)
+    f32x4 af[4][FM], bf[4][FN];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) af[p][fm] = __builtin_bit_cast(f32x4, a[p][fm]);
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) bf[p][fn] = __builtin_bit_cast(f32x4, b[p][fn]);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
-        const float a0 = __builtin_bit_cast(float, a[0][fm][j]);
-        const float a2 = __builtin_bit_cast(float, a[1][fm][j]);
-        const float ar = __builtin_bit_cast(float, a[2][fm][j]);
-        const float ai = __builtin_bit_cast(float, a[3][fm][j]);
+        const float a0 = af[0][fm][j];
+        const float a2 = af[1][fm][j];
+        const float ar = af[2][fm][j];
+        const float ai = af[3][fm][j];
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-          const float b0 = __builtin_bit_cast(float, b[0][fn][j]);
-          const float b2 = __builtin_bit_cast(float, b[1][fn][j]);
-          const float br = __builtin_bit_cast(float, b[2][fn][j]);
-          const float bi = __builtin_bit_cast(float, b[3][fn][j]);
+          const float b0 = bf[0][fn][j];
+          const float b2 = bf[1][fn][j];
+          const float br = bf[2][fn][j];
+          const float bi = bf[3][fn][j];
           acc[0][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][fm][fn], 0, 0, 0);
           acc[2][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(ar, br, acc[2][fm][fn], 0, 0, 0);
           acc[1][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a2, b2, acc[1][fm][fn], 0, 0, 0);
