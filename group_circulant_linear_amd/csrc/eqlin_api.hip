@@ -34,28 +34,68 @@ int hip_status(hipError_t e) {
   return EQLIN_EHIP;
 }
 
-size_t plane_bytes(int C, int D, int dtype) {
-  return static_cast<size_t>(C / 4) * static_cast<size_t>(D / 4) * 4u * static_cast<size_t>(elem_bytes(dtype));
+// Prepared planes of one direction: rows x ceil(groups / SG) stage blocks of
+// 256 bytes (4 planes x 64 bytes).
+size_t plane_set_bytes(int rows, int groups, int dtype) {
+  const int sg = eqlin::stage_groups(dtype);
+  return static_cast<size_t>(rows) * static_cast<size_t>(cdiv(groups, sg)) * 256u;
 }
 
-size_t transpose_offset(int C, int D, int dtype) { return (plane_bytes(C, D, dtype) + 255u) & ~size_t(255); }
+size_t transpose_offset(int C, int D, int dtype) {
+  return (plane_set_bytes(D / 4, C / 4, dtype) + 255u) & ~size_t(255);
+}
 
-// Forward tile choice: the largest workgroup tile that still gives every CU
-// at least one workgroup; EQLIN_FWD_TILE (11, 12, 21, 22) overrides.
+// Buffer loads use 32-bit byte offsets inside one workgroup tile.
+constexpr int64_t kMaxTileBytes = int64_t(1) << 30;
+
+bool fwd_offsets_fit(int in_width, int out_groups, int dtype) {
+  const int64_t row_bytes = int64_t(in_width) * elem_bytes(dtype);
+  const int64_t wrow_bytes = cdiv(in_width / 4, eqlin::stage_groups(dtype)) * 256;
+  (void)out_groups;
+  return 256 * row_bytes < kMaxTileBytes && 256 * wrow_bytes < kMaxTileBytes;
+}
+
+struct TileShape {
+  int code, bm, bn, lds_kb;
+};
+// forward tile candidates (code = FM FN WM WN)
+constexpr TileShape kF32Tiles[] = {{1122, 64, 64, 80},  {1121, 64, 32, 60}, {1112, 32, 64, 60},
+                                   {2122, 128, 64, 120}, {1222, 64, 128, 120}, {1141, 128, 32, 100},
+                                   {2121, 128, 32, 100}};
+constexpr TileShape kF16Tiles[] = {{2222, 128, 128, 160}, {2122, 128, 64, 120}, {1222, 64, 128, 120},
+                                   {1122, 64, 64, 80},    {2121, 128, 32, 100}};
+
+// Forward tile choice: estimated time ~ (rounds of workgroups per CU) x
+// (tile area), i.e. minimise ceil(tiles / (CUs * resident)) * BM * BN, preferring
+// larger tiles on ties (less operand re-reading).  EQLIN_FWD_TILE overrides.
 int choose_fwd_tile(int dtype, int64_t nrows, int mg) {
   if (const char* env = getenv("EQLIN_FWD_TILE")) {
     const int t = atoi(env);
-    if (t == 11 || t == 12 || t == 21 || t == 22) return t;
+    if (eqlin::fwd_tile_known(t)) return t;
   }
-  auto tiles = [&](int fm, int fn) { return cdiv(nrows, 64 * fm) * cdiv(mg, 64 * fn); };
-  if (dtype == EQLIN_F32) return tiles(2, 1) >= kNumCu ? 21 : 11;
-  if (tiles(2, 2) >= kNumCu) return 22;
-  if (tiles(2, 1) >= kNumCu) return 21;
-  return 11;
+  const TileShape* tiles = dtype == EQLIN_F32 ? kF32Tiles : kF16Tiles;
+  const int ntiles = dtype == EQLIN_F32 ? int(sizeof(kF32Tiles) / sizeof(TileShape))
+                                        : int(sizeof(kF16Tiles) / sizeof(TileShape));
+  int best = tiles[0].code;
+  double best_cost = 1e300;
+  for (int i = 0; i < ntiles; ++i) {
+    const TileShape& t = tiles[i];
+    const int64_t n = cdiv(nrows, t.bm) * cdiv(mg, t.bn);
+    const int resident = 160 / t.lds_kb;
+    const int64_t slots = int64_t(kNumCu) * (resident > 0 ? resident : 1);
+    const double rounds = double(cdiv(n, slots)) * slots / kNumCu;  // per-CU workgroup count
+    const double cost = rounds * t.bm * t.bn * (1.0 + 0.02 * (128.0 / t.bm + 128.0 / t.bn));
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = t.code;
+    }
+  }
+  return best;
 }
 
 // Row splits of the dw reduction: enough workgroups to cover the chip twice,
-// each split a whole number of pipeline stages.
+// each split a whole number of pipeline stages, and small enough for 32-bit
+// offsets inside a split.
 struct DwPlan {
   int64_t rows_per_split;
   int nsplit;
@@ -66,11 +106,14 @@ DwPlan plan_dw(int64_t N, int C, int D, int dtype) {
   if (N <= 0) return p;
   const int64_t tiles = cdiv(D / 4, 64) * cdiv(C / 4, 64);
   const int64_t stage = eqlin::dw_rows_per_stage(dtype);
+  const int64_t row_bytes = int64_t(C > D ? C : D) * elem_bytes(dtype);
   int64_t want = cdiv(2 * kNumCu, tiles);
   const int64_t max_split = cdiv(N, stage);
   if (want > max_split) want = max_split;
   if (want < 1) want = 1;
   p.rows_per_split = cdiv(cdiv(N, want), stage) * stage;
+  const int64_t cap = (kMaxTileBytes / row_bytes) / stage * stage;
+  if (p.rows_per_split > cap) p.rows_per_split = cap > stage ? cap : stage;
   p.nsplit = static_cast<int>(cdiv(N, p.rows_per_split));
   return p;
 }
@@ -97,7 +140,7 @@ int eqlin_last_hip_error(void) { return g_last_hip_error; }
 
 size_t eqlin_prepared_weight_bytes(int C, int D, int T, int dtype) {
   if (check_shape(0, C, D, T, dtype) != EQLIN_OK) return 0;
-  return transpose_offset(C, D, dtype) + plane_bytes(C, D, dtype);
+  return transpose_offset(C, D, dtype) + plane_set_bytes(C / 4, D / 4, dtype);
 }
 
 size_t eqlin_prepared_transpose_offset(int C, int D, int T, int dtype) {
@@ -124,6 +167,7 @@ int eqlin_forward(const void* X, int64_t N, int C, int D, int T, const void* W_h
   if (N == 0) return EQLIN_OK;
   if (!X || !W_hat || !Y) return EQLIN_EINVAL;
   if (!aligned16(X) || !aligned16(W_hat) || !aligned16(Y)) return EQLIN_EALIGN;
+  if (!fwd_offsets_fit(C, D / 4, dtype)) return EQLIN_ENOTSUP;
   const int tile = choose_fwd_tile(dtype, N, D / 4);
   return hip_status(
       eqlin::launch_forward(dtype, tile, X, W_hat, Y, N, C / 4, D / 4, static_cast<hipStream_t>(stream)));
@@ -143,6 +187,7 @@ int eqlin_backward_dx(const void* dY, int64_t N, int C, int D, int T, const void
   if (N == 0) return EQLIN_OK;
   if (!dY || !W_hat || !dX) return EQLIN_EINVAL;
   if (!aligned16(dY) || !aligned16(W_hat) || !aligned16(dX)) return EQLIN_EALIGN;
+  if (!fwd_offsets_fit(D, C / 4, dtype)) return EQLIN_ENOTSUP;
   // dX = dY W: the forward kernel with the transposed, conjugated planes
   // (input groups D', output groups C').
   const char* wb = static_cast<const char*>(W_hat) + transpose_offset(C, D, dtype);
@@ -174,6 +219,7 @@ int eqlin_backward(const void* dY, const void* X, int64_t N, int C, int D, int T
   if (dX && N > 0) {
     if (!dY || !W_hat) return EQLIN_EINVAL;
     if (!aligned16(dY) || !aligned16(W_hat) || !aligned16(dX)) return EQLIN_EALIGN;
+    if (!fwd_offsets_fit(D, C / 4, dtype)) return EQLIN_ENOTSUP;
   }
   if (dw) {
     if (N > 0 && (!dY || !X || !workspace)) return EQLIN_EINVAL;

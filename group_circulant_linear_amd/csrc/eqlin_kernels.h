@@ -5,12 +5,16 @@
 
 namespace eqlin {
 
-// tile codes: 10 * FM + FN, workgroup tile (64 FM rows) x (64 FN output groups)
+// Forward tile codes: four digits FM FN WM WN.  A workgroup has WM x WN waves;
+// each wave owns FM x FN fragments of 32 x 32 per accumulator plane, so the
+// workgroup tile is (32 FM WM) rows x (32 FN WN) output groups.
+bool fwd_tile_known(int tile);
 hipError_t launch_forward(int dtype, int tile, const void* in, const void* wp, void* out, int64_t nrows,
                           int kg, int mg, hipStream_t s);
 hipError_t launch_dw(int dtype, const void* dy, const void* x, float* ws, float* dw, int64_t nrows, int mg,
                      int ng, int64_t rows_per_split, int nsplit, hipStream_t s);
 hipError_t launch_prepare(int dtype, const void* w, void* wf, void* wb, int mg, int ng, hipStream_t s);
-int dw_rows_per_stage(int dtype);
+int stage_groups(int dtype);       // group channels per pipeline stage (16 fp32, 32 f16)
+int dw_rows_per_stage(int dtype);  // rows per dw pipeline stage (16 fp32, 32 f16)
 
 }  // namespace eqlin

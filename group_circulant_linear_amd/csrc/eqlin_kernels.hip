@@ -78,6 +78,18 @@ __device__ __forceinline__ void idft4(float f0, float f2, float f1r, float f1i, 
 }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Buffer resource over [base, base + bytes): raw buffer loads at offsets past
+// the range return zeros.  Ranges are clamped below 2^31 so that kOob is
+// always out of range.
+constexpr uint32_t kOob = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes > 0x7ffffff0ull ? 0x7ffffff0u : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // Blocks are dispatched round-robin over the 8 XCDs.  Renumber so that
@@ -269,24 +281,31 @@ __device__ __forceinline__ void mma_chunk(f32x16 (&acc)[4][FM][FN], const char* 
 //
 // out[n][4m + t] = IDFT_t( sum_k Ahat[n][k] (*) Bhat[m][k] )
 // A = in [nrows][4 kg] (raw groups, transformed on the fly),
-// B = prepared spectra wp [mg][kg][4], out [nrows][4 mg].
-// Stage = 64 bytes per plane row (16 fp32 or 32 f16 groups along k).
-// Thread t loads, for rows t/4 (+64 per pass), the 16 B pieces q + 4j
-// (q = t % 4, j = 0..3) of the stage window: coalesced global reads, and the
-// four pieces land in the contiguous LDS slots [16q, 16q+16) of each plane
-// (a fixed permutation of k inside the stage, identical for A and B).
-template <typename E, int FM, int FN>
-__global__ void __launch_bounds__(kThreads)
+// B = prepared spectra in stage blocks (see prepare_kernel), out [nrows][4 mg].
+// A stage covers 64 bytes of every plane row: SG = 16 fp32 or 32 f16 groups
+// along k.  Thread t owns row t / 4 (+ NT/4 per pass) and 16-byte slot block
+// q = t % 4 of that row: it loads the pieces q + 4j (j = 0..3) of the stage
+// window (coalesced), transforms them and writes the contiguous LDS block q
+// of each plane; the prepared weights are stored in that same slot order, so
+// their 16-byte pieces are copied to LDS unchanged.  Global loads are buffer
+// loads: addresses past the end of the tile's range (rows >= nrows) or
+// flagged out of range (groups >= kg) return zeros without branches.
+// LDS is double-buffered: one barrier per stage, and the loads of stage s+2
+// are in flight while stage s is multiplied.
+template <typename E, int FM, int FN, int WM, int WN>
+__global__ void __launch_bounds__(64 * WM * WN)
 fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ out,
            int64_t nrows, int kg, int mg, int tiles_n) {
-  constexpr int BM = 64 * FM, BN = 64 * FN;
+  constexpr int NT = 64 * WM * WN;
+  constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
   constexpr int GP = Traits<E>::kGroupsPerPiece;
   constexpr int SG = 16 * GP;              // groups per stage
-  constexpr int STRIDE = 80;               // 64 B + 16 B pad
+  constexpr int STRIDE = 80;               // 64 B plane row + 16 B pad
   constexpr int A_PLANE = BM * STRIDE, B_PLANE = BN * STRIDE;
-  __shared__ __attribute__((aligned(16))) char lds[4 * (A_PLANE + B_PLANE)];
-  char* a_lds = lds;
-  char* b_lds = lds + 4 * A_PLANE;
+  constexpr int BUF = 4 * (A_PLANE + B_PLANE);
+  constexpr int RPP = NT / 4;              // tile rows covered per load pass
+  constexpr int PA = (BM + RPP - 1) / RPP, PB = (BN + RPP - 1) / RPP;
+  __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -294,47 +313,52 @@ fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ o
   const int tn = (int)(lid % tiles_n);
   const int64_t row0 = tm * BM;
   const int col0 = tn * BN;
-
-  const int64_t in_ld = 4 * (int64_t)kg;    // elements per input row
-  const int q = tid & 3, rl = tid >> 2;
   const int ksteps = (kg + SG - 1) / SG;
 
-  // stage register buffers
-  u32x4 ra[FM][4], rb[FN][4];
-  auto load_stage = [&](int ks) {
+  const uint32_t row_bytes = (uint32_t)kg * 4u * (uint32_t)sizeof(E);
+  const __amdgpu_buffer_rsrc_t a_src =
+      make_rsrc(in + row0 * 4 * (int64_t)kg, (uint64_t)(nrows - row0) * row_bytes);
+  const __amdgpu_buffer_rsrc_t b_src =
+      make_rsrc(wp + (int64_t)col0 * ksteps * SG * 4, (uint64_t)(mg - col0) * (uint64_t)ksteps * 256u);
+
+  const int q = tid & 3, rl = tid >> 2;
+  u32x4 ra[PA][4], rb[PB][4];
+  auto load = [&](int ks) {
 #pragma unroll
-    for (int ps = 0; ps < FM; ++ps) {
-      const int64_t row = row0 + ps * 64 + rl;
+    for (int ps = 0; ps < PA; ++ps) {
+      const uint32_t r = (uint32_t)(ps * RPP + rl);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int g = ks * SG + (q + 4 * j) * GP;
-        ra[ps][j] = (row < nrows && g < kg) ? ld16(in + row * in_ld + 4 * (int64_t)g) : u32x4{0, 0, 0, 0};
+        const uint32_t off = g < kg ? r * row_bytes + (uint32_t)g * 4u * (uint32_t)sizeof(E) : kOob;
+        ra[ps][j] = bload16(a_src, off);
       }
     }
 #pragma unroll
-    for (int ps = 0; ps < FN; ++ps) {
-      const int m = col0 + ps * 64 + rl;
+    for (int ps = 0; ps < PB; ++ps) {
+      const uint32_t m = (uint32_t)(ps * RPP + rl);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int g = ks * SG + (q + 4 * j) * GP;
-        rb[ps][j] = (m < mg && g < kg) ? ld16(wp + ((int64_t)m * kg + g) * 4) : u32x4{0, 0, 0, 0};
-      }
+      for (int p = 0; p < 4; ++p) rb[ps][p] = bload16(b_src, (m * (uint32_t)ksteps + (uint32_t)ks) * 256u + p * 64 + q * 16);
     }
   };
-  auto store_stage = [&]() {
+  auto store = [&](char* buf) {
 #pragma unroll
-    for (int ps = 0; ps < FM; ++ps) {
-      u32x4 pl[4];
-      pieces_to_planes<E, true, false>(ra[ps], pl);
+    for (int ps = 0; ps < PA; ++ps) {
+      const int r = ps * RPP + rl;
+      if (BM % RPP == 0 || r < BM) {
+        u32x4 pl[4];
+        pieces_to_planes<E, true, false>(ra[ps], pl);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) st16(a_lds + p * A_PLANE + (ps * 64 + rl) * STRIDE + q * 16, pl[p]);
+        for (int p = 0; p < 4; ++p) st16(buf + p * A_PLANE + r * STRIDE + q * 16, pl[p]);
+      }
     }
 #pragma unroll
-    for (int ps = 0; ps < FN; ++ps) {
-      u32x4 pl[4];
-      pieces_to_planes<E, false, false>(rb[ps], pl);
+    for (int ps = 0; ps < PB; ++ps) {
+      const int m = ps * RPP + rl;
+      if (BN % RPP == 0 || m < BN) {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) st16(b_lds + p * B_PLANE + (ps * 64 + rl) * STRIDE + q * 16, pl[p]);
+        for (int p = 0; p < 4; ++p) st16(buf + 4 * A_PLANE + p * B_PLANE + m * STRIDE + q * 16, rb[ps][p]);
+      }
     }
   };
 
@@ -346,18 +370,23 @@ fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ o
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) acc[p][fm][fn] = f32x16{};
 
-  const int wr = wave >> 1, wc = wave & 1;
+  const int wr = wave / WN, wc = wave % WN;
   const int li = lane & 31, lh = lane >> 5;
-  const char* a_frag = a_lds + (wr * 32 * FM + li) * STRIDE + lh * 16;
-  const char* b_frag = b_lds + (wc * 32 * FN + li) * STRIDE + lh * 16;
+  const int a_frag = (wr * 32 * FM + li) * STRIDE + lh * 16;
+  const int b_frag = 4 * A_PLANE + (wc * 32 * FN + li) * STRIDE + lh * 16;
 
-  load_stage(0);
+  load(0);
+  store(lds);
+  if (ksteps > 1) load(1);
+  __syncthreads();
   for (int ks = 0; ks < ksteps; ++ks) {
-    store_stage();
-    __syncthreads();
-    if (ks + 1 < ksteps) load_stage(ks + 1);
-    mma_chunk<E, FM, FN>(acc, a_frag, A_PLANE, b_frag, B_PLANE, STRIDE, 0);
-    mma_chunk<E, FM, FN>(acc, a_frag, A_PLANE, b_frag, B_PLANE, STRIDE, 1);
+    char* cur = lds + (ks & 1) * BUF;
+    mma_chunk<E, FM, FN>(acc, cur + a_frag, A_PLANE, cur + b_frag, B_PLANE, STRIDE, 0);
+    mma_chunk<E, FM, FN>(acc, cur + a_frag, A_PLANE, cur + b_frag, B_PLANE, STRIDE, 1);
+    if (ks + 1 < ksteps) {
+      store(lds + ((ks + 1) & 1) * BUF);
+      if (ks + 2 < ksteps) load(ks + 2);
+    }
     __syncthreads();
   }
 
@@ -393,23 +422,24 @@ fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ o
 // over the rows of one split; the four planes are written to
 // ws[split][plane][mg][ng] (float32).  Tiles 64 x 64, one 32 x 32 fragment
 // per wave and plane.  The k axis is the row axis: thread (piece column pc,
-// row block rq) loads KV consecutive rows of one 16 B piece, so every LDS
-// write is one 16 B vector of KV consecutive rows of one plane.
+// row block rq) loads 4 consecutive rows of one 16 B piece (1 fp32 or 2 f16
+// groups), transforms them and writes, per group and plane, the 4 rows as one
+// contiguous LDS vector (16 B fp32, 8 B f16).  A stage is 64 bytes of every
+// plane row (16 fp32 / 32 f16 rows); LDS is double-buffered as in fwd_kernel.
 template <typename E>
 __global__ void __launch_bounds__(kThreads)
 dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __restrict__ ws,
                   int64_t nrows, int mg, int ng, int64_t rows_per_split, int tiles_m, int tiles_n) {
   constexpr int GP = Traits<E>::kGroupsPerPiece;
-  constexpr int KV = Traits<E>::kValsPerSlot;      // rows per thread (one 16 B slot)
+  constexpr int KV = 4;                            // rows per thread per stage
   constexpr int PR = 64 / GP;                      // pieces per tile row (64 groups)
   constexpr int RB = kThreads / PR;                // row blocks per stage
-  constexpr int SR = RB * KV;                      // rows per stage: 16 (fp32) / 64 (f16)
-  constexpr int NCH = SR * (int)sizeof(E) / 32;    // 32-byte chunks per plane row
-  constexpr int STRIDE = SR * (int)sizeof(E) + 16;
+  constexpr int SR = RB * KV;                      // rows per stage: 16 (fp32) / 32 (f16)
+  constexpr int STRIDE = 80;
   constexpr int PLANE = 64 * STRIDE;
-  __shared__ __attribute__((aligned(16))) char lds[8 * PLANE];
-  char* a_lds = lds;
-  char* b_lds = lds + 4 * PLANE;
+  constexpr int BUF = 8 * PLANE;
+  static_assert(SR * (int)sizeof(E) == 64, "one stage is 64 bytes per plane row");
+  __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ntiles = tiles_m * tiles_n;
@@ -419,38 +449,47 @@ dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __re
   const int m0 = (tile / tiles_n) * 64, n0 = (tile % tiles_n) * 64;
   const int64_t rbeg = split * rows_per_split;
   const int64_t rend = (rbeg + rows_per_split < nrows) ? rbeg + rows_per_split : nrows;
+  const int nstages = (int)((rend - rbeg + SR - 1) / SR);
+
+  const uint32_t a_row = (uint32_t)mg * 4u * (uint32_t)sizeof(E);
+  const uint32_t b_row = (uint32_t)ng * 4u * (uint32_t)sizeof(E);
+  const __amdgpu_buffer_rsrc_t a_src = make_rsrc(dy + rbeg * 4 * (int64_t)mg, (uint64_t)(rend - rbeg) * a_row);
+  const __amdgpu_buffer_rsrc_t b_src = make_rsrc(x + rbeg * 4 * (int64_t)ng, (uint64_t)(rend - rbeg) * b_row);
 
   const int pc = tid % PR, rq = tid / PR;
-  const int64_t a_ld = 4 * (int64_t)mg, b_ld = 4 * (int64_t)ng;
   const int ga = m0 + pc * GP, gb = n0 + pc * GP;
+  const bool a_ok = ga < mg, b_ok = gb < ng;
+  const uint32_t a_col = (uint32_t)ga * 4u * (uint32_t)sizeof(E);
+  const uint32_t b_col = (uint32_t)gb * 4u * (uint32_t)sizeof(E);
 
-  u32x4 ra[KV / 4][4], rb[KV / 4][4];
-  auto load_stage = [&](int64_t r0) {
+  u32x4 ra[KV], rb[KV];
+  auto load = [&](int st) {
 #pragma unroll
     for (int v = 0; v < KV; ++v) {
-      const int64_t row = r0 + rq * KV + v;
-      const bool ok = row < rend;
-      ra[v / 4][v % 4] = (ok && ga < mg) ? ld16(dy + row * a_ld + 4 * (int64_t)ga) : u32x4{0, 0, 0, 0};
-      rb[v / 4][v % 4] = (ok && gb < ng) ? ld16(x + row * b_ld + 4 * (int64_t)gb) : u32x4{0, 0, 0, 0};
+      const uint32_t row = (uint32_t)(st * SR + rq * KV + v);
+      ra[v] = bload16(a_src, a_ok ? row * a_row + a_col : kOob);
+      rb[v] = bload16(b_src, b_ok ? row * b_row + b_col : kOob);
     }
   };
-  auto store_stage = [&]() {
+  auto store = [&](char* buf) {
+    char* a_lds = buf;
+    char* b_lds = buf + 4 * PLANE;
     if constexpr (sizeof(E) == 4) {
       u32x4 pa[4], pb[4];
-      pieces_to_planes<float, true, false>(ra[0], pa);
-      pieces_to_planes<float, true, true>(rb[0], pb);
+      pieces_to_planes<float, true, false>(ra, pa);
+      pieces_to_planes<float, true, true>(rb, pb);
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         st16(a_lds + p * PLANE + pc * STRIDE + rq * 16, pa[p]);
         st16(b_lds + p * PLANE + pc * STRIDE + rq * 16, pb[p]);
       }
     } else {
-      // 8 rows x 2 groups per operand: transform, then gather per (group, plane)
-      _Float16 ha[2][4][8], hb[2][4][8];
+      // 4 rows x 2 groups per operand: transform, gather 4 rows per (group, plane)
+      f16x4 ha[2][4], hb[2][4];
 #pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const f16x8 xa = __builtin_bit_cast(f16x8, ra[v / 4][v % 4]);
-        const f16x8 xb = __builtin_bit_cast(f16x8, rb[v / 4][v % 4]);
+      for (int v = 0; v < KV; ++v) {
+        const f16x8 xa = __builtin_bit_cast(f16x8, ra[v]);
+        const f16x8 xb = __builtin_bit_cast(f16x8, rb[v]);
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           float f[4], g[4];
@@ -470,14 +509,10 @@ dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __re
       for (int e = 0; e < 2; ++e) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          f16x8 oa, ob;
-#pragma unroll
-          for (int v = 0; v < 8; ++v) {
-            oa[v] = ha[e][p][v];
-            ob[v] = hb[e][p][v];
-          }
-          st16(a_lds + p * PLANE + (pc * 2 + e) * STRIDE + rq * 16, __builtin_bit_cast(u32x4, oa));
-          st16(b_lds + p * PLANE + (pc * 2 + e) * STRIDE + rq * 16, __builtin_bit_cast(u32x4, ob));
+          *reinterpret_cast<u32x2*>(a_lds + p * PLANE + (pc * 2 + e) * STRIDE + rq * 8) =
+              __builtin_bit_cast(u32x2, ha[e][p]);
+          *reinterpret_cast<u32x2*>(b_lds + p * PLANE + (pc * 2 + e) * STRIDE + rq * 8) =
+              __builtin_bit_cast(u32x2, hb[e][p]);
         }
       }
     }
@@ -489,16 +524,23 @@ dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __re
 
   const int wr = wave >> 1, wc = wave & 1;
   const int li = lane & 31, lh = lane >> 5;
-  const char* a_frag = a_lds + (wr * 32 + li) * STRIDE + lh * 16;
-  const char* b_frag = b_lds + (wc * 32 + li) * STRIDE + lh * 16;
+  const int a_frag = (wr * 32 + li) * STRIDE + lh * 16;
+  const int b_frag = 4 * PLANE + (wc * 32 + li) * STRIDE + lh * 16;
 
-  if (rbeg < rend) load_stage(rbeg);
-  for (int64_t r0 = rbeg; r0 < rend; r0 += SR) {
-    store_stage();
+  if (nstages > 0) {
+    load(0);
+    store(lds);
+    if (nstages > 1) load(1);
     __syncthreads();
-    if (r0 + SR < rend) load_stage(r0 + SR);
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) mma_chunk<E, 1, 1>(acc, a_frag, PLANE, b_frag, PLANE, STRIDE, c);
+  }
+  for (int st = 0; st < nstages; ++st) {
+    char* cur = lds + (st & 1) * BUF;
+    mma_chunk<E, 1, 1>(acc, cur + a_frag, PLANE, cur + b_frag, PLANE, STRIDE, 0);
+    mma_chunk<E, 1, 1>(acc, cur + a_frag, PLANE, cur + b_frag, PLANE, STRIDE, 1);
+    if (st + 1 < nstages) {
+      store(lds + ((st + 1) & 1) * BUF);
+      if (st + 2 < nstages) load(st + 2);
+    }
     __syncthreads();
   }
 
@@ -535,26 +577,43 @@ dw_finalize_kernel(const float* __restrict__ ws, float* __restrict__ dw, int mg,
 
 // ============================================================ prepare
 //
-// w[m][n][0..3] -> wf[m][n] = (F0, F2, Re F1, Im F1) and the transposed,
-// conjugated wb[n][m] = (F0, F2, Re F1, -Im F1) used by the dX pass.
+// Weight spectra in the stage-block layout read by fwd_kernel:
+//   dst[row][ks][plane][s]   (SG = 16 fp32 / 32 f16 slots per 64-byte block)
+// where slot s of stage ks holds group channel ks * SG + slot_group(s) (the
+// slot order fwd_kernel's loaders produce for the transformed input) and
+// groups past the end are zero.
+//   forward planes:   row = d', groups = c',  (F0, F2, Re F1,  Im F1) of w[d'][c']
+//   transpose planes: row = c', groups = d',  (F0, F2, Re F1, -Im F1) of w[d'][c']
+// The second set is the spectrum of the transposed, group-reversed weight
+// (a conjugate), used by the dX pass.
 template <typename E>
+__host__ __device__ constexpr int slot_group(int s) {
+  return sizeof(E) == 4 ? (s >> 2) + 4 * (s & 3) : 2 * ((s >> 3) + 4 * ((s >> 1) & 3)) + (s & 1);
+}
+
+template <typename E, bool kTranspose>
 __global__ void __launch_bounds__(kThreads)
-prepare_kernel(const E* __restrict__ w, E* __restrict__ wf, E* __restrict__ wb, int mg, int ng) {
+prepare_kernel(const E* __restrict__ w, E* __restrict__ dst, int mg, int ng) {
+  constexpr int SG = 16 * Traits<E>::kGroupsPerPiece;
+  const int rows = kTranspose ? ng : mg;
+  const int kgr = kTranspose ? mg : ng;
+  const int nks = (kgr + SG - 1) / SG;
   const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= (int64_t)mg * ng) return;
-  const int m = (int)(idx / ng), n = (int)(idx % ng);
-  float z[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) z[u] = (float)w[idx * 4 + u];
-  float f[4];
-  dft4(z[0], z[1], z[2], z[3], f[0], f[1], f[2], f[3]);
-  E* pf = wf + idx * 4;
-  E* pb = wb + ((int64_t)n * mg + m) * 4;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    pf[p] = (E)f[p];
-    pb[p] = (E)(p == 3 ? -f[p] : f[p]);
+  if (idx >= (int64_t)rows * nks * SG) return;
+  const int s = (int)(idx % SG);
+  const int64_t t = idx / SG;
+  const int ks = (int)(t % nks);
+  const int64_t row = t / nks;
+  const int g = ks * SG + slot_group<E>(s);
+  float f[4] = {0.f, 0.f, 0.f, 0.f};
+  if (g < kgr) {
+    const E* src = kTranspose ? w + ((int64_t)g * ng + row) * 4 : w + (row * ng + g) * 4;
+    dft4((float)src[0], (float)src[1], (float)src[2], (float)src[3], f[0], f[1], f[2], f[3]);
+    if (kTranspose) f[3] = -f[3];
   }
+  E* o = dst + (row * nks + ks) * 4 * SG + s;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) o[p * SG] = (E)f[p];
 }
 
 // ============================================================ launchers
@@ -563,43 +622,48 @@ namespace {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 }  // namespace
 
-template <typename E, int FM, int FN>
-hipError_t launch_fwd_t(const E* in, const E* wp, E* out, int64_t nrows, int kg, int mg, hipStream_t s) {
-  const int64_t tiles_m = cdiv(nrows, 64 * FM);
-  const int tiles_n = (int)cdiv(mg, 64 * FN);
+template <typename E, int FM, int FN, int WM, int WN>
+hipError_t launch_fwd_t(const void* in, const void* wp, void* out, int64_t nrows, int kg, int mg, hipStream_t s) {
+  constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
+  const int64_t tiles_m = cdiv(nrows, BM);
+  const int tiles_n = (int)cdiv(mg, BN);
   const int64_t grid = tiles_m * tiles_n;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_kernel<E, FM, FN>), dim3((unsigned)grid), dim3(kThreads), 0, s, in, wp, out, nrows,
-                     kg, mg, tiles_n);
+  hipLaunchKernelGGL((fwd_kernel<E, FM, FN, WM, WN>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, s,
+                     static_cast<const E*>(in), static_cast<const E*>(wp), static_cast<E*>(out), nrows, kg, mg,
+                     tiles_n);
   return hipGetLastError();
+}
+
+#define EQLIN_FWD_TILES(X) \
+  X(1122) X(1121) X(1112) X(2122) X(1222) X(1141) X(2222) X(2121)
+
+bool fwd_tile_known(int tile) {
+  switch (tile) {
+#define EQLIN_CASE(T) case T:
+    EQLIN_FWD_TILES(EQLIN_CASE)
+#undef EQLIN_CASE
+    return true;
+    default: return false;
+  }
 }
 
 hipError_t launch_forward(int dtype, int tile, const void* in, const void* wp, void* out, int64_t nrows,
                           int kg, int mg, hipStream_t s) {
-  if (dtype == 0) {
-    const float* i = static_cast<const float*>(in);
-    const float* w = static_cast<const float*>(wp);
-    float* o = static_cast<float*>(out);
-    switch (tile) {
-      case 11: return launch_fwd_t<float, 1, 1>(i, w, o, nrows, kg, mg, s);
-      case 12: return launch_fwd_t<float, 1, 2>(i, w, o, nrows, kg, mg, s);
-      case 22: return launch_fwd_t<float, 2, 2>(i, w, o, nrows, kg, mg, s);
-      default: return launch_fwd_t<float, 2, 1>(i, w, o, nrows, kg, mg, s);
-    }
-  }
-  const _Float16* i = static_cast<const _Float16*>(in);
-  const _Float16* w = static_cast<const _Float16*>(wp);
-  _Float16* o = static_cast<_Float16*>(out);
+#define EQLIN_CASE(T)                                                                                  \
+  case T:                                                                                              \
+    return dtype == 0 ? launch_fwd_t<float, T / 1000, (T / 100) % 10, (T / 10) % 10, T % 10>(in, wp, out, nrows, kg, mg, s) \
+                      : launch_fwd_t<_Float16, T / 1000, (T / 100) % 10, (T / 10) % 10, T % 10>(in, wp, out, nrows, kg, mg, s);
   switch (tile) {
-    case 11: return launch_fwd_t<_Float16, 1, 1>(i, w, o, nrows, kg, mg, s);
-    case 21: return launch_fwd_t<_Float16, 2, 1>(i, w, o, nrows, kg, mg, s);
-    case 12: return launch_fwd_t<_Float16, 1, 2>(i, w, o, nrows, kg, mg, s);
-    default: return launch_fwd_t<_Float16, 2, 2>(i, w, o, nrows, kg, mg, s);
+    EQLIN_FWD_TILES(EQLIN_CASE)
+    default: return hipErrorInvalidValue;
   }
+#undef EQLIN_CASE
 }
 
-int dw_rows_per_stage(int dtype) { return dtype == 0 ? 16 : 64; }
+int stage_groups(int dtype) { return dtype == 0 ? 16 : 32; }
+int dw_rows_per_stage(int dtype) { return dtype == 0 ? 16 : 32; }
 
 hipError_t launch_dw(int dtype, const void* dy, const void* x, float* ws, float* dw, int64_t nrows, int mg,
                      int ng, int64_t rows_per_split, int nsplit, hipStream_t s) {
@@ -625,14 +689,18 @@ hipError_t launch_dw(int dtype, const void* dy, const void* x, float* ws, float*
 }
 
 hipError_t launch_prepare(int dtype, const void* w, void* wf, void* wb, int mg, int ng, hipStream_t s) {
-  const int64_t grid = cdiv((int64_t)mg * ng, kThreads);
+  const int sg = stage_groups(dtype);
+  const int64_t nf = (int64_t)mg * cdiv(ng, sg) * sg, nb = (int64_t)ng * cdiv(mg, sg) * sg;
   if (dtype == 0) {
-    hipLaunchKernelGGL((prepare_kernel<float>), dim3((unsigned)grid), dim3(kThreads), 0, s,
-                       static_cast<const float*>(w), static_cast<float*>(wf), static_cast<float*>(wb), mg, ng);
+    hipLaunchKernelGGL((prepare_kernel<float, false>), dim3((unsigned)cdiv(nf, kThreads)), dim3(kThreads), 0, s,
+                       static_cast<const float*>(w), static_cast<float*>(wf), mg, ng);
+    hipLaunchKernelGGL((prepare_kernel<float, true>), dim3((unsigned)cdiv(nb, kThreads)), dim3(kThreads), 0, s,
+                       static_cast<const float*>(w), static_cast<float*>(wb), mg, ng);
   } else {
-    hipLaunchKernelGGL((prepare_kernel<_Float16>), dim3((unsigned)grid), dim3(kThreads), 0, s,
-                       static_cast<const _Float16*>(w), static_cast<_Float16*>(wf), static_cast<_Float16*>(wb),
-                       mg, ng);
+    hipLaunchKernelGGL((prepare_kernel<_Float16, false>), dim3((unsigned)cdiv(nf, kThreads)), dim3(kThreads), 0,
+                       s, static_cast<const _Float16*>(w), static_cast<_Float16*>(wf), mg, ng);
+    hipLaunchKernelGGL((prepare_kernel<_Float16, true>), dim3((unsigned)cdiv(nb, kThreads)), dim3(kThreads), 0,
+                       s, static_cast<const _Float16*>(w), static_cast<_Float16*>(wb), mg, ng);
   }
   return hipGetLastError();
 }

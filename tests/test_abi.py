@@ -31,12 +31,15 @@ def test_version_and_status_strings(lib):
 
 
 def test_size_queries(lib):
-    # fp32: D'*C'*4 floats per plane set, transposed copy at a 256 B boundary
-    assert lib.eqlin_prepared_transpose_offset(768, 768, 4, 0) == 192 * 192 * 16
-    assert lib.eqlin_prepared_weight_bytes(768, 768, 4, 0) == 2 * 192 * 192 * 16
-    assert lib.eqlin_prepared_weight_bytes(768, 3072, 4, 1) == 2 * 192 * 768 * 8
+    # rows x ceil(groups / S) stage blocks of 256 bytes (S = 16 fp32, 32 f16),
+    # forward set then the transposed set at a 256 B boundary
+    assert lib.eqlin_prepared_transpose_offset(768, 768, 4, 0) == 192 * 12 * 256
+    assert lib.eqlin_prepared_weight_bytes(768, 768, 4, 0) == 2 * 192 * 12 * 256
+    assert lib.eqlin_prepared_weight_bytes(768, 3072, 4, 1) == 768 * 6 * 256 + 192 * 24 * 256
     off = lib.eqlin_prepared_transpose_offset(4, 4, 4, 0)
-    assert off == 256 and lib.eqlin_prepared_weight_bytes(4, 4, 4, 0) == 256 + 16
+    assert off == 256 and lib.eqlin_prepared_weight_bytes(4, 4, 4, 0) == 512
+    # 20 input groups -> 2 stage blocks per forward row (zero padded)
+    assert lib.eqlin_prepared_transpose_offset(80, 12, 4, 0) == 3 * 2 * 256
     assert lib.eqlin_prepared_weight_bytes(768, 768, 3, 0) == 0
     assert lib.eqlin_prepared_weight_bytes(770, 768, 4, 0) == 0
     assert lib.eqlin_prepared_weight_bytes(12, 16, 4, 1) == 0      # odd C' with f16

@@ -41,18 +41,40 @@ def say(*a):
 
 # --------------------------------------------------------------------- a1
 
-@pytest.mark.parametrize("dt,Dp,Cp", [("f32", 5, 3), ("f32", 192, 192), ("f16", 6, 4), ("f16", 768, 192)])
+def slot_group(s, dt):
+    """Group channel held by slot s of a 64-byte stage block (header's layout)."""
+    if dt == "f32":
+        return (s >> 2) + 4 * (s & 3)
+    return 2 * ((s >> 3) + 4 * ((s >> 1) & 3)) + (s & 1)
+
+
+def decode_planes(flat, rows, groups, dt):
+    """[rows][ceil(groups/S)][4][S] stage blocks -> [rows][groups][4]; checks zero padding."""
+    S = 16 if dt == "f32" else 32
+    nks = -(-groups // S)
+    blk = flat[: rows * nks * 4 * S].reshape(rows, nks, 4, S)
+    out = np.zeros((rows, groups, 4))
+    for ks in range(nks):
+        for s in range(S):
+            g = ks * S + slot_group(s, dt)
+            if g < groups:
+                out[:, g, :] = blk[:, ks, :, s]
+            else:
+                assert np.all(blk[:, ks, :, s] == 0)
+    return out
+
+
+@pytest.mark.parametrize("dt,Dp,Cp", [("f32", 5, 3), ("f32", 20, 36), ("f32", 192, 192), ("f16", 6, 4),
+                                       ("f16", 40, 70), ("f16", 768, 192)])
 def test_prepared_planes_match_group_spectrum(dt, Dp, Cp):
     say(f"prepare {dt} D'={Dp} C'={Cp}")
     _, w, _ = make_layer_inputs(4, 4 * Cp, 4 * Dp, dt, seed=1, with_dy=False)
     Wh = eq.eqlin_prepare_weights(dev(w))
     tdt = torch.float32 if dt == "f32" else torch.float16
     buf = Wh.buf
-    esz = 4 if dt == "f32" else 2
-    nplane = Dp * Cp * 4
     off = eq.eqlin_prepared_transpose_offset(4 * Cp, 4 * Dp, tdt)
-    wf = host(buf[: nplane * esz].view(tdt)).reshape(Dp, Cp, 4)
-    wb = host(buf[off: off + nplane * esz].view(tdt)).reshape(Cp, Dp, 4)
+    wf = decode_planes(host(buf[:off].view(tdt)), Dp, Cp, dt)
+    wb = decode_planes(host(buf[off:].view(tdt)), Cp, Dp, dt)
     ref = oracle.kept_p4_planes(w.astype(np.float64))
     tol = 1e-6 if dt == "f32" else 1e-3
     assert rel_err(wf, ref) < tol
@@ -78,7 +100,7 @@ def _forward_case(dt, N, C, D, seed=0):
     return X, w, host(Y)
 
 
-@pytest.mark.parametrize("tile", ["auto", "11", "12", "21", "22"])
+@pytest.mark.parametrize("tile", ["auto", "1122", "1121", "1112", "2122", "1222", "1141", "2222", "2121"])
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 def test_forward_small_shapes_all_tiles(dt, tile, monkeypatch):
     if tile != "auto":
