@@ -223,17 +223,19 @@ def main():
             dXd = torch.empty((L.N, L.C), dtype=tdt, device=dev)
             dWd = torch.empty((L.D, L.C), dtype=tdt, device=dev)
             for i in range(3):
-                torch.matmul(Xs[i % nsets], Wd.t(), out=Yd)
+                torch.mm(Xs[i % nsets], Wd.t(), out=Yd)
+                torch.mm(dYs[i % nsets], Wd, out=dXd)
+                torch.mm(dYs[i % nsets].t(), Xs[i % nsets], out=dWd)
             e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
             reps = max(10, K)
             torch.cuda.synchronize()
             e0.record()
             for i in range(reps):
-                torch.matmul(Xs[i % nsets], Wd.t(), out=Yd)
+                torch.mm(Xs[i % nsets], Wd.t(), out=Yd)
             e1.record()
             for i in range(reps):
-                torch.matmul(dYs[i % nsets], Wd, out=dXd)
-                torch.matmul(dYs[i % nsets].t(), Xs[i % nsets], out=dWd)
+                torch.mm(dYs[i % nsets], Wd, out=dXd)
+                torch.mm(dYs[i % nsets].t(), Xs[i % nsets], out=dWd)
             e2.record()
             torch.cuda.synchronize()
             tot_f += e0.elapsed_time(e1) * 1e3 / reps

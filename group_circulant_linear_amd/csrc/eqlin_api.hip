@@ -56,18 +56,17 @@ bool fwd_offsets_fit(int in_width, int out_groups, int dtype) {
 }
 
 struct TileShape {
-  int code, bm, bn, lds_kb;
+  int code, bm, bn;
+  double eff;  // measured fraction of the MFMA peak on large shapes (MI355X)
 };
-// forward tile candidates (code = FM FN WM WN)
-constexpr TileShape kF32Tiles[] = {{1122, 64, 64, 80},  {1121, 64, 32, 60}, {1112, 32, 64, 60},
-                                   {2122, 128, 64, 120}, {1222, 64, 128, 120}, {1141, 128, 32, 100},
-                                   {2121, 128, 32, 100}};
-constexpr TileShape kF16Tiles[] = {{2222, 128, 128, 160}, {2122, 128, 64, 120}, {1222, 64, 128, 120},
-                                   {1122, 64, 64, 80},    {2121, 128, 32, 100}};
+// Forward tile candidates (code = FM FN WM WN) with their measured efficiency
+// on the ViT-B / ViT-H layer shapes.
+constexpr TileShape kF32Tiles[] = {{1122, 64, 64, 0.64}, {1112, 32, 64, 0.52}, {1121, 64, 32, 0.50}};
+constexpr TileShape kF16Tiles[] = {{2124, 128, 128, 0.21}, {1122, 64, 64, 0.18}, {1112, 32, 64, 0.13}};
 
-// Forward tile choice: estimated time ~ (rounds of workgroups per CU) x
-// (tile area), i.e. minimise ceil(tiles / (CUs * resident)) * BM * BN, preferring
-// larger tiles on ties (less operand re-reading).  EQLIN_FWD_TILE overrides.
+// Forward tile choice: workgroups are spread round-robin over the CUs, so a
+// CU's work is ceil(tiles / CUs) tiles; minimise that work divided by the
+// tile's efficiency.  EQLIN_FWD_TILE overrides (any compiled tile code).
 int choose_fwd_tile(int dtype, int64_t nrows, int mg) {
   if (const char* env = getenv("EQLIN_FWD_TILE")) {
     const int t = atoi(env);
@@ -81,11 +80,8 @@ int choose_fwd_tile(int dtype, int64_t nrows, int mg) {
   for (int i = 0; i < ntiles; ++i) {
     const TileShape& t = tiles[i];
     const int64_t n = cdiv(nrows, t.bm) * cdiv(mg, t.bn);
-    const int resident = 160 / t.lds_kb;
-    const int64_t slots = int64_t(kNumCu) * (resident > 0 ? resident : 1);
-    const double rounds = double(cdiv(n, slots)) * slots / kNumCu;  // per-CU workgroup count
-    const double cost = rounds * t.bm * t.bn * (1.0 + 0.02 * (128.0 / t.bm + 128.0 / t.bn));
-    if (cost < best_cost) {
+    const double cost = double(cdiv(n, kNumCu)) * t.bm * t.bn / t.eff;
+    if (cost < best_cost * 0.97) {  // keep the earlier (larger) tile unless clearly better
       best_cost = cost;
       best = t.code;
     }
@@ -104,10 +100,11 @@ struct DwPlan {
 DwPlan plan_dw(int64_t N, int C, int D, int dtype) {
   DwPlan p{0, 0};
   if (N <= 0) return p;
+  // two 64 x 64 workgroups fit one CU (LDS); use at most that many in total
   const int64_t tiles = cdiv(D / 4, 64) * cdiv(C / 4, 64);
   const int64_t stage = eqlin::dw_rows_per_stage(dtype);
   const int64_t row_bytes = int64_t(C > D ? C : D) * elem_bytes(dtype);
-  int64_t want = cdiv(2 * kNumCu, tiles);
+  int64_t want = (2 * kNumCu) / tiles;
   const int64_t max_split = cdiv(N, stage);
   if (want > max_split) want = max_split;
   if (want < 1) want = 1;

@@ -558,21 +558,38 @@ dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __re
 }
 
 // Sum the split partials in split order (deterministic), inverse group DFT
-// along u, write dw[m][n][0..3] (float32).  nsplit == 0 writes zeros.
+// along u, write dw[m][n][0..3] (float32).  Thread (plane p, entry e) of a
+// 256-thread block sums plane p of one of 64 consecutive entries; the four
+// plane sums meet in LDS and one thread per entry applies the inverse DFT.
+// nsplit == 0 writes zeros.
 __global__ void __launch_bounds__(kThreads)
 dw_finalize_kernel(const float* __restrict__ ws, float* __restrict__ dw, int mg, int ng, int nsplit) {
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  __shared__ float part[4][64];
   const int64_t plane = (int64_t)mg * ng;
-  if (idx >= plane) return;
-  float f[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < nsplit; ++s) {
-    const float* src = ws + (int64_t)s * 4 * plane + idx;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) f[p] += src[p * plane];
+  const int e = threadIdx.x & 63, p = threadIdx.x >> 6;
+  const int64_t idx = (int64_t)blockIdx.x * 64 + e;
+  float acc = 0.f;
+  if (idx < plane) {
+    const float* src = ws + p * plane + idx;
+    const int64_t step = 4 * plane;
+    int s = 0;
+    for (; s + 4 <= nsplit; s += 4) {
+      const float v0 = src[(s + 0) * step], v1 = src[(s + 1) * step];
+      const float v2 = src[(s + 2) * step], v3 = src[(s + 3) * step];
+      acc += v0;
+      acc += v1;
+      acc += v2;
+      acc += v3;
+    }
+    for (; s < nsplit; ++s) acc += src[s * step];
   }
-  float y[4];
-  idft4(f[0], f[1], f[2], f[3], y);
-  st16(dw + idx * 4, __builtin_bit_cast(u32x4, f32x4{y[0], y[1], y[2], y[3]}));
+  part[p][e] = acc;
+  __syncthreads();
+  if (p == 0 && idx < plane) {
+    float y[4];
+    idft4(part[0][e], part[1][e], part[2][e], part[3][e], y);
+    st16(dw + idx * 4, __builtin_bit_cast(u32x4, f32x4{y[0], y[1], y[2], y[3]}));
+  }
 }
 
 // ============================================================ prepare
@@ -637,7 +654,7 @@ hipError_t launch_fwd_t(const void* in, const void* wp, void* out, int64_t nrows
 }
 
 #define EQLIN_FWD_TILES(X) \
-  X(1122) X(1121) X(1112) X(2122) X(1222) X(1141) X(2222) X(2121)
+  X(1122) X(1121) X(1112) X(2122) X(1222) X(1141) X(2222) X(2121) X(1124) X(2124) X(1142)
 
 bool fwd_tile_known(int tile) {
   switch (tile) {
@@ -683,7 +700,7 @@ hipError_t launch_dw(int dtype, const void* dy, const void* x, float* ws, float*
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t fgrid = cdiv((int64_t)mg * ng, kThreads);
+  const int64_t fgrid = cdiv((int64_t)mg * ng, 64);
   hipLaunchKernelGGL(dw_finalize_kernel, dim3((unsigned)fgrid), dim3(kThreads), 0, s, ws, dw, mg, ng, nsplit);
   return hipGetLastError();
 }
