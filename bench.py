@@ -51,6 +51,25 @@ def parse():
     return p.parse_args()
 
 
+def profiled_traffic(workload, dt, kernel_name):
+    """HBM bytes per launch of `kernel_name` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is no
+    summary for this workload or the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{dt}.json")
+    src = os.path.join(ROOT, "group_circulant_linear_amd", "csrc", "eqlin_kernels.hip")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+        with open(src, "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != d["source_sha256"]:
+                return None
+        rows = [r for k, v in d["kernels"].items() if k.startswith(kernel_name) for r in v]
+        return max(r["bytes"] for r in rows) if rows else None
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def dense_weight(torch, w):
     """Dense D x C weight of the circulant blocks for the dense-GEMM comparator."""
     Dp, Cp, T = w.shape
@@ -190,8 +209,14 @@ def main():
     # roofline of the forward kernel (one launch per layer; summed over layers)
     achieved = exec_flops / (fwd_us * 1e-6) / 1e12
     peak = PEAK_TFLOPS[dt]
-    roofline = {"bound": "mfma", "kernel": "fwd_kernel", "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+    es_b = 4 if dt == "f32" else 2
+    alg_bytes = sum(es_b * L.N * (L.C + L.D) + es_b * L.C * L.D / 4 for (L, _, _, _) in layers)
+    traffic = profiled_traffic(wl.name, dt, "eqlin::fwd_kernel") if len(layers) == 1 else None
+    roofline = {"bound": "mfma", "kernel": "eqlin::fwd_kernel", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": (round(traffic) if traffic else None),
+                "traffic_algorithmic": round(alg_bytes), "traffic_unit": "bytes per launch",
+                "flops_per_launch": exec_flops}
 
     per_layer = []
     for li, (L, _, _, _) in enumerate(layers):
