@@ -24,14 +24,15 @@
 //   out_plane[m][n] = sum_k A_plane[m][k] (*) B_plane[n][k]
 // where (*) is: f0*f0, f2*f2 and the complex product on (Re f1, Im f1).
 // Both operands are staged per pipeline stage into LDS as four planes
-// [plane][row][k] with k contiguous (16 B padding per row keeps the 16-byte
-// LDS reads of 32 consecutive rows on distinct banks).  Every lane reads 16
-// bytes per plane per 32x32 fragment: 4 fp32 k-values (four 32x32x2 f32
+// [plane][row][k] with k contiguous in 64-byte rows whose four 16-byte slots
+// are XOR-swizzled (see swz_slot).  Every lane reads 16 bytes per plane per
+// 32x32 fragment: 4 fp32 k-values (four 32x32x2 f32
 // MFMAs) or 8 f16 k-values (one 32x32x16 f16 MFMA).  A workgroup has four
 // 64-wide waves in a 2 x 2 arrangement; each wave owns FM x FN fragments of
 // 32 x 32 for each of the four accumulator planes (f0, f2, Re f1, Im f1).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "eqlin_kernels.h"
 
@@ -46,6 +47,12 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kNumXcd = 8;
+// LDS plane rows are 64 bytes (four 16-byte slots) with no padding; the slot
+// index is XOR-swizzled with bits 2-3 of the row, which keeps both the
+// 4-lanes-per-row stores and the 32-rows-per-wave fragment reads free of bank
+// conflicts on gfx950 (checked with the LDS bank-conflict counter).
+constexpr int kRowBytes = 64;
+__device__ __forceinline__ int swz_slot(int row, int slot) { return slot ^ ((row >> 2) & 3); }
 
 template <typename E> struct Traits;
 template <> struct Traits<float> {
@@ -259,22 +266,47 @@ struct Core<_Float16, FM, FN> {
   }
 };
 
-// Reads this lane's operand slots of chunk `c` from the LDS planes and runs
-// the complex core.  Plane p of A starts at a_lds + p * a_plane; row r at
-// r * stride; the lane reads 16 B at byte c * 32 + half * 16 of rows
-// (wave_row + 32 fm + lane % 32).
+// Reads this lane's 16-byte operand slot of one chunk from every LDS plane
+// and runs the complex core.  a_lds / b_lds point at the lane's slot in plane
+// 0 of its first fragment row; plane p is p * a_plane further, fragment fm
+// 32 rows further.
 template <typename E, int FM, int FN>
 __device__ __forceinline__ void mma_chunk(f32x16 (&acc)[4][FM][FN], const char* a_lds, int a_plane,
-                                          const char* b_lds, int b_plane, int stride, int c) {
+                                          const char* b_lds, int b_plane, int stride) {
   u32x4 a[4][FM], b[4][FN];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) a[p][fm] = ld16(a_lds + p * a_plane + fm * 32 * stride + c * 32);
+    for (int fm = 0; fm < FM; ++fm) a[p][fm] = ld16(a_lds + p * a_plane + fm * 32 * stride);
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) b[p][fn] = ld16(b_lds + p * b_plane + fn * 32 * stride + c * 32);
+    for (int fn = 0; fn < FN; ++fn) b[p][fn] = ld16(b_lds + p * b_plane + fn * 32 * stride);
   }
   Core<E, FM, FN>::mma(acc, a, b);
+}
+
+// Instruction interleaving for one pipeline stage of fwd_kernel: spread the
+// operand reads of the second chunk, the global loads two stages ahead, and
+// the next stage's transform and LDS writes between the MFMAs, so that one
+// wave keeps its matrix core busy while it prepares the next stage.
+// Masks: 0x008 MFMA, 0x100 DS read, 0x200 DS write, 0x020 VMEM read, 0x002 VALU.
+template <typename E, int FM, int FN, int PA, int PB>
+__device__ __forceinline__ void interleave_schedule() {
+  constexpr int kMfma = (sizeof(E) == 4 ? 4 : 1) * 6 * FM * FN * 2;
+  constexpr int kDsRead = 2 * 4 * (FM + FN);
+  constexpr int kVmem = 4 * (PA + PB);
+  constexpr int kDsWrite = 4 * (PA + PB);
+  constexpr int kHalf = kDsRead / 2;
+  __builtin_amdgcn_sched_group_barrier(0x100, kHalf, 0);
+#pragma unroll
+  for (int i = 0; i < kMfma; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i < kHalf) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (i >= kMfma / 4 && i < kMfma / 4 + kVmem) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    if (i >= kMfma / 2) {
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      if ((i - kMfma / 2) % ((kMfma / 2 + kDsWrite - 1) / kDsWrite) == 0) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    }
+  }
 }
 
 // ============================================================ forward / dX
@@ -292,7 +324,7 @@ __device__ __forceinline__ void mma_chunk(f32x16 (&acc)[4][FM][FN], const char* 
 // flagged out of range (groups >= kg) return zeros without branches.
 // LDS is double-buffered: one barrier per stage, and the loads of stage s+2
 // are in flight while stage s is multiplied.
-template <typename E, int FM, int FN, int WM, int WN>
+template <typename E, int FM, int FN, int WM, int WN, int SCHED>
 __global__ void __launch_bounds__(64 * WM * WN)
 fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ out,
            int64_t nrows, int kg, int mg, int tiles_n) {
@@ -300,7 +332,7 @@ fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ o
   constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
   constexpr int GP = Traits<E>::kGroupsPerPiece;
   constexpr int SG = 16 * GP;              // groups per stage
-  constexpr int STRIDE = 80;               // 64 B plane row + 16 B pad
+  constexpr int STRIDE = kRowBytes;
   constexpr int A_PLANE = BM * STRIDE, B_PLANE = BN * STRIDE;
   constexpr int BUF = 4 * (A_PLANE + B_PLANE);
   constexpr int RPP = NT / 4;              // tile rows covered per load pass
@@ -309,10 +341,8 @@ fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ o
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int64_t tm = lid / tiles_n;
-  const int tn = (int)(lid % tiles_n);
-  const int64_t row0 = tm * BM;
-  const int col0 = tn * BN;
+  const int64_t row0 = (lid / tiles_n) * BM;
+  const int col0 = (int)(lid % tiles_n) * BN;
   const int ksteps = (kg + SG - 1) / SG;
 
   const uint32_t row_bytes = (uint32_t)kg * 4u * (uint32_t)sizeof(E);
@@ -338,7 +368,8 @@ fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ o
     for (int ps = 0; ps < PB; ++ps) {
       const uint32_t m = (uint32_t)(ps * RPP + rl);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) rb[ps][p] = bload16(b_src, (m * (uint32_t)ksteps + (uint32_t)ks) * 256u + p * 64 + q * 16);
+      for (int p = 0; p < 4; ++p)
+        rb[ps][p] = bload16(b_src, ks < ksteps ? (m * (uint32_t)ksteps + (uint32_t)ks) * 256u + p * 64 + q * 16 : kOob);
     }
   };
   auto store = [&](char* buf) {
@@ -349,7 +380,7 @@ fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ o
         u32x4 pl[4];
         pieces_to_planes<E, true, false>(ra[ps], pl);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) st16(buf + p * A_PLANE + r * STRIDE + q * 16, pl[p]);
+        for (int p = 0; p < 4; ++p) st16(buf + p * A_PLANE + r * STRIDE + swz_slot(r, q) * 16, pl[p]);
       }
     }
 #pragma unroll
@@ -357,7 +388,7 @@ fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ o
       const int m = ps * RPP + rl;
       if (BN % RPP == 0 || m < BN) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) st16(buf + 4 * A_PLANE + p * B_PLANE + m * STRIDE + q * 16, rb[ps][p]);
+        for (int p = 0; p < 4; ++p) st16(buf + 4 * A_PLANE + p * B_PLANE + m * STRIDE + swz_slot(m, q) * 16, rb[ps][p]);
       }
     }
   };
@@ -372,21 +403,27 @@ fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ o
 
   const int wr = wave / WN, wc = wave % WN;
   const int li = lane & 31, lh = lane >> 5;
-  const int a_frag = (wr * 32 * FM + li) * STRIDE + lh * 16;
-  const int b_frag = 4 * A_PLANE + (wc * 32 * FN + li) * STRIDE + lh * 16;
+  // fragment rows differ from li by multiples of 32, so the swizzle of every
+  // row this lane reads is that of li
+  const int a_frag = (wr * 32 * FM + li) * STRIDE;
+  const int b_frag = 4 * A_PLANE + (wc * 32 * FN + li) * STRIDE;
+  const int c0 = swz_slot(li, lh) * 16, c1 = swz_slot(li, 2 + lh) * 16;
 
   load(0);
   store(lds);
-  if (ksteps > 1) load(1);
+  load(1);
   __syncthreads();
+  // Branch-free steady state: past the last stage the loads read zeros (out
+  // of range) and the store fills the idle buffer, so one basic block holds
+  // the MFMAs, the next stage's transform / LDS writes and the loads two
+  // stages ahead, and the scheduler can interleave them.
   for (int ks = 0; ks < ksteps; ++ks) {
     char* cur = lds + (ks & 1) * BUF;
-    mma_chunk<E, FM, FN>(acc, cur + a_frag, A_PLANE, cur + b_frag, B_PLANE, STRIDE, 0);
-    mma_chunk<E, FM, FN>(acc, cur + a_frag, A_PLANE, cur + b_frag, B_PLANE, STRIDE, 1);
-    if (ks + 1 < ksteps) {
-      store(lds + ((ks + 1) & 1) * BUF);
-      if (ks + 2 < ksteps) load(ks + 2);
-    }
+    mma_chunk<E, FM, FN>(acc, cur + a_frag + c0, A_PLANE, cur + b_frag + c0, B_PLANE, STRIDE);
+    mma_chunk<E, FM, FN>(acc, cur + a_frag + c1, A_PLANE, cur + b_frag + c1, B_PLANE, STRIDE);
+    store(lds + ((ks + 1) & 1) * BUF);
+    load(ks + 2);
+    if constexpr (SCHED == 1) interleave_schedule<E, FM, FN, PA, PB>();
     __syncthreads();
   }
 
@@ -435,7 +472,7 @@ dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __re
   constexpr int PR = 64 / GP;                      // pieces per tile row (64 groups)
   constexpr int RB = kThreads / PR;                // row blocks per stage
   constexpr int SR = RB * KV;                      // rows per stage: 16 (fp32) / 32 (f16)
-  constexpr int STRIDE = 80;
+  constexpr int STRIDE = kRowBytes;
   constexpr int PLANE = 64 * STRIDE;
   constexpr int BUF = 8 * PLANE;
   static_assert(SR * (int)sizeof(E) == 64, "one stage is 64 bytes per plane row");
@@ -480,8 +517,8 @@ dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __re
       pieces_to_planes<float, true, true>(rb, pb);
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        st16(a_lds + p * PLANE + pc * STRIDE + rq * 16, pa[p]);
-        st16(b_lds + p * PLANE + pc * STRIDE + rq * 16, pb[p]);
+        st16(a_lds + p * PLANE + pc * STRIDE + swz_slot(pc, rq) * 16, pa[p]);
+        st16(b_lds + p * PLANE + pc * STRIDE + swz_slot(pc, rq) * 16, pb[p]);
       }
     } else {
       // 4 rows x 2 groups per operand: transform, gather 4 rows per (group, plane)
@@ -509,10 +546,10 @@ dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __re
       for (int e = 0; e < 2; ++e) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          *reinterpret_cast<u32x2*>(a_lds + p * PLANE + (pc * 2 + e) * STRIDE + rq * 8) =
-              __builtin_bit_cast(u32x2, ha[e][p]);
-          *reinterpret_cast<u32x2*>(b_lds + p * PLANE + (pc * 2 + e) * STRIDE + rq * 8) =
-              __builtin_bit_cast(u32x2, hb[e][p]);
+          const int row = pc * 2 + e;
+          const int off = row * STRIDE + swz_slot(row, rq >> 1) * 16 + (rq & 1) * 8;
+          *reinterpret_cast<u32x2*>(a_lds + p * PLANE + off) = __builtin_bit_cast(u32x2, ha[e][p]);
+          *reinterpret_cast<u32x2*>(b_lds + p * PLANE + off) = __builtin_bit_cast(u32x2, hb[e][p]);
         }
       }
     }
@@ -524,8 +561,9 @@ dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __re
 
   const int wr = wave >> 1, wc = wave & 1;
   const int li = lane & 31, lh = lane >> 5;
-  const int a_frag = (wr * 32 + li) * STRIDE + lh * 16;
-  const int b_frag = 4 * PLANE + (wc * 32 + li) * STRIDE + lh * 16;
+  const int a_frag = (wr * 32 + li) * STRIDE;
+  const int b_frag = 4 * PLANE + (wc * 32 + li) * STRIDE;
+  const int c0 = swz_slot(li, lh) * 16, c1 = swz_slot(li, 2 + lh) * 16;
 
   if (nstages > 0) {
     load(0);
@@ -535,8 +573,8 @@ dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __re
   }
   for (int st = 0; st < nstages; ++st) {
     char* cur = lds + (st & 1) * BUF;
-    mma_chunk<E, 1, 1>(acc, cur + a_frag, PLANE, cur + b_frag, PLANE, STRIDE, 0);
-    mma_chunk<E, 1, 1>(acc, cur + a_frag, PLANE, cur + b_frag, PLANE, STRIDE, 1);
+    mma_chunk<E, 1, 1>(acc, cur + a_frag + c0, PLANE, cur + b_frag + c0, PLANE, STRIDE);
+    mma_chunk<E, 1, 1>(acc, cur + a_frag + c1, PLANE, cur + b_frag + c1, PLANE, STRIDE);
     if (st + 1 < nstages) {
       store(lds + ((st + 1) & 1) * BUF);
       if (st + 2 < nstages) load(st + 2);
@@ -639,18 +677,28 @@ namespace {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 }  // namespace
 
-template <typename E, int FM, int FN, int WM, int WN>
-hipError_t launch_fwd_t(const void* in, const void* wp, void* out, int64_t nrows, int kg, int mg, hipStream_t s) {
+template <typename E, int FM, int FN, int WM, int WN, int SCHED>
+hipError_t launch_fwd_s(const void* in, const void* wp, void* out, int64_t nrows, int kg, int mg, hipStream_t s) {
   constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
   const int64_t tiles_m = cdiv(nrows, BM);
   const int tiles_n = (int)cdiv(mg, BN);
   const int64_t grid = tiles_m * tiles_n;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_kernel<E, FM, FN, WM, WN>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, s,
+  hipLaunchKernelGGL((fwd_kernel<E, FM, FN, WM, WN, SCHED>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, s,
                      static_cast<const E*>(in), static_cast<const E*>(wp), static_cast<E*>(out), nrows, kg, mg,
                      tiles_n);
   return hipGetLastError();
+}
+
+template <typename E, int FM, int FN, int WM, int WN>
+hipError_t launch_fwd_t(const void* in, const void* wp, void* out, int64_t nrows, int kg, int mg, hipStream_t s) {
+  static const int sched = [] {
+    const char* e = getenv("EQLIN_SCHED");
+    return e ? atoi(e) : 1;
+  }();
+  return sched == 1 ? launch_fwd_s<E, FM, FN, WM, WN, 1>(in, wp, out, nrows, kg, mg, s)
+                    : launch_fwd_s<E, FM, FN, WM, WN, 0>(in, wp, out, nrows, kg, mg, s);
 }
 
 #define EQLIN_FWD_TILES(X) \
