@@ -149,7 +149,7 @@ def main():
         sets.append(S)
     torch.cuda.synchronize()
 
-    phases = ("prepare", "forward", "dx", "dw")
+    phases = ("prepare", "forward", "backward")
 
     def step(i, events=None):
         S = sets[i % nsets]
@@ -167,14 +167,10 @@ def main():
             if args.forward_only:
                 continue
             if ev is not None:
-                ev["dx"][0].record()
-            eqlin.eqlin_backward_dx(b["dY"], Wh, out=b["dX"])
+                ev["backward"][0].record()
+            eqlin.eqlin_backward(b["dY"], b["X"], Wh, workspace=b["ws"], dX_out=b["dX"], dw_out=b["dw"])
             if ev is not None:
-                ev["dx"][1].record()
-                ev["dw"][0].record()
-            eqlin.eqlin_backward_dw(b["dY"], b["X"], workspace=b["ws"], out=b["dw"])
-            if ev is not None:
-                ev["dw"][1].record()
+                ev["backward"][1].record()
 
     for i in range(args.warmup):
         step(i)
@@ -196,7 +192,7 @@ def main():
     for i in range(K):
         for li in range(len(layers)):
             for p in phases:
-                if args.forward_only and p in ("dx", "dw"):
+                if args.forward_only and p == "backward":
                     continue
                 a, b = evs[i][li][p]
                 ph_us[p][li] += a.elapsed_time(b) * 1e3 / K
@@ -230,8 +226,8 @@ def main():
         d["fwd_hbm_gbs_algorithmic"] = round(
             (es * L.N * (L.C + L.D) + es * L.C * L.D / 4) / (ph_us["forward"][li] * 1e-6) / 1e9, 1)
         if not args.forward_only:
-            d["dx_mfma_frac"] = round(0.75 * nd / (ph_us["dx"][li] * 1e-6) / 1e12 / peak, 4)
-            d["dw_mfma_frac"] = round(0.75 * nd / (ph_us["dw"][li] * 1e-6) / 1e12 / peak, 4)
+            d["bwd_tflops_dense_equiv"] = round(4 * nd / (ph_us["backward"][li] * 1e-6) / 1e12, 2)
+            d["bwd_mfma_frac"] = round(1.5 * nd / (ph_us["backward"][li] * 1e-6) / 1e12 / peak, 4)
         per_layer.append(d)
 
     # dense GEMM comparator: F.linear on the pre-expanded weight, same dtype, same stream
@@ -266,7 +262,7 @@ def main():
             tot_f += e0.elapsed_time(e1) * 1e3 / reps
             tot_b += e1.elapsed_time(e2) * 1e3 / reps
             del Wd
-        eq_b = sum(ph_us["dx"]) + sum(ph_us["dw"])
+        eq_b = sum(ph_us["backward"])
         dense = {"fwd_us": round(tot_f, 2), "fwd_tflops": round(fwd_flops / (tot_f * 1e-6) / 1e12, 2),
                  "fwd_speedup": round(tot_f / fwd_us, 3), "bwd_us": round(tot_b, 2),
                  "bwd_speedup": (round(tot_b / eq_b, 3) if not args.forward_only else None),

@@ -89,6 +89,16 @@ int choose_fwd_tile(int dtype, int64_t nrows, int mg) {
   return best;
 }
 
+// eqlin_backward with both outputs runs dX and the dw partials in one launch
+// unless EQLIN_BWD_FUSED=0.
+bool use_fused_backward() {
+  static const bool fused = [] {
+    const char* e = getenv("EQLIN_BWD_FUSED");
+    return !(e && atoi(e) == 0);
+  }();
+  return fused;
+}
+
 // Row splits of the dw reduction: enough workgroups to cover the chip twice,
 // each split a whole number of pipeline stages, and small enough for 32-bit
 // offsets inside a split.
@@ -223,6 +233,13 @@ int eqlin_backward(const void* dY, const void* X, int64_t N, int C, int D, int T
     if (!aligned16(dw)) return EQLIN_EALIGN;
     if (N > 0 && (!aligned16(dY) || !aligned16(X) || !aligned16(workspace))) return EQLIN_EALIGN;
     if (workspace_bytes < eqlin_backward_workspace_bytes(N, C, D, T, dtype)) return EQLIN_EWORKSPACE;
+  }
+  if (dX && dw && N > 0 && use_fused_backward()) {
+    // one launch for dX and the dw partials (they share dY), then the finalize
+    const DwPlan p = plan_dw(N, C, D, dtype);
+    const char* wb = static_cast<const char*>(W_hat) + transpose_offset(C, D, dtype);
+    return hip_status(eqlin::launch_bwd_fused(dtype, dY, X, wb, dX, static_cast<float*>(workspace), dw, N, D / 4,
+                                              C / 4, p.rows_per_split, p.nsplit, static_cast<hipStream_t>(stream)));
   }
   if (dX) {
     st = eqlin_backward_dx(dY, N, C, D, T, W_hat, dX, dtype, stream);

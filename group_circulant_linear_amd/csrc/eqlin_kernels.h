@@ -13,6 +13,11 @@ hipError_t launch_forward(int dtype, int tile, const void* in, const void* wp, v
                           int kg, int mg, hipStream_t s);
 hipError_t launch_dw(int dtype, const void* dy, const void* x, float* ws, float* dw, int64_t nrows, int mg,
                      int ng, int64_t rows_per_split, int nsplit, hipStream_t s);
+// dX (forward structure on the transpose spectra wb, tile 1122) and the dw
+// split partials in one launch, then the dw finalize.  nrows > 0.
+hipError_t launch_bwd_fused(int dtype, const void* dy, const void* x, const void* wb, void* dx, float* ws,
+                            float* dw, int64_t nrows, int dg, int cg, int64_t rows_per_split, int nsplit,
+                            hipStream_t s);
 hipError_t launch_prepare(int dtype, const void* w, void* wf, void* wb, int mg, int ng, hipStream_t s);
 int stage_groups(int dtype);       // group channels per pipeline stage (16 fp32, 32 f16)
 int dw_rows_per_stage(int dtype);  // rows per dw pipeline stage (16 fp32, 32 f16)

@@ -324,10 +324,16 @@ __device__ __forceinline__ void interleave_schedule() {
 // flagged out of range (groups >= kg) return zeros without branches.
 // LDS is double-buffered: one barrier per stage, and the loads of stage s+2
 // are in flight while stage s is multiplied.
+template <typename E, int FM, int FN, int WM, int WN>
+constexpr int fwd_lds_bytes() {
+  return 2 * 4 * (32 * FM * WM + 32 * FN * WN) * kRowBytes;
+}
+
+// One forward (or dX) tile: workgroup-level logical tile id `lid`.
 template <typename E, int FM, int FN, int WM, int WN, int SCHED>
-__global__ void __launch_bounds__(64 * WM * WN)
-fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ out,
-           int64_t nrows, int kg, int mg, int tiles_n) {
+__device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __restrict__ in,
+                                         const E* __restrict__ wp, E* __restrict__ out, int64_t nrows, int kg,
+                                         int mg, int tiles_n) {
   constexpr int NT = 64 * WM * WN;
   constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
   constexpr int GP = Traits<E>::kGroupsPerPiece;
@@ -337,10 +343,9 @@ fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ o
   constexpr int BUF = 4 * (A_PLANE + B_PLANE);
   constexpr int RPP = NT / 4;              // tile rows covered per load pass
   constexpr int PA = (BM + RPP - 1) / RPP, PB = (BN + RPP - 1) / RPP;
-  __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
+  static_assert(2 * BUF == fwd_lds_bytes<E, FM, FN, WM, WN>(), "LDS size");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
   const int64_t row0 = (lid / tiles_n) * BM;
   const int col0 = (int)(lid % tiles_n) * BN;
   const int ksteps = (kg + SG - 1) / SG;
@@ -453,6 +458,15 @@ fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ o
   }
 }
 
+template <typename E, int FM, int FN, int WM, int WN, int SCHED>
+__global__ void __launch_bounds__(64 * WM * WN)
+fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ out,
+           int64_t nrows, int kg, int mg, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) char lds[fwd_lds_bytes<E, FM, FN, WM, WN>()];
+  fwd_tile<E, FM, FN, WM, WN, SCHED>(lds, xcd_logical_id(blockIdx.x, gridDim.x), in, wp, out, nrows, kg, mg,
+                                     tiles_n);
+}
+
 // ============================================================ dw partials
 //
 // P_k[m][n] = sum_rows G_k[row][m] conj(Xhat_k[row][n])   (m = d', n = c')
@@ -463,10 +477,12 @@ fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ o
 // groups), transforms them and writes, per group and plane, the 4 rows as one
 // contiguous LDS vector (16 B fp32, 8 B f16).  A stage is 64 bytes of every
 // plane row (16 fp32 / 32 f16 rows); LDS is double-buffered as in fwd_kernel.
+constexpr int kDwLdsBytes = 2 * 8 * 64 * kRowBytes;
+
 template <typename E>
-__global__ void __launch_bounds__(kThreads)
-dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __restrict__ ws,
-                  int64_t nrows, int mg, int ng, int64_t rows_per_split, int tiles_m, int tiles_n) {
+__device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restrict__ dy, const E* __restrict__ x,
+                                        float* __restrict__ ws, int64_t nrows, int mg, int ng,
+                                        int64_t rows_per_split, int tiles_m, int tiles_n) {
   constexpr int GP = Traits<E>::kGroupsPerPiece;
   constexpr int KV = 4;                            // rows per thread per stage
   constexpr int PR = 64 / GP;                      // pieces per tile row (64 groups)
@@ -476,11 +492,10 @@ dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __re
   constexpr int PLANE = 64 * STRIDE;
   constexpr int BUF = 8 * PLANE;
   static_assert(SR * (int)sizeof(E) == 64, "one stage is 64 bytes per plane row");
-  __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
+  static_assert(2 * BUF == kDwLdsBytes, "LDS size");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ntiles = tiles_m * tiles_n;
-  const int64_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
   const int64_t split = lid / ntiles;
   const int tile = (int)(lid % ntiles);
   const int m0 = (tile / tiles_n) * 64, n0 = (tile % tiles_n) * 64;
@@ -592,6 +607,38 @@ dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __re
 #pragma unroll
       for (int p = 0; p < 4; ++p) dst[p * plane_elems + (int64_t)m * ng + n] = acc[p][0][0][r];
     }
+  }
+}
+
+template <typename E>
+__global__ void __launch_bounds__(kThreads)
+dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __restrict__ ws,
+                  int64_t nrows, int mg, int ng, int64_t rows_per_split, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) char lds[kDwLdsBytes];
+  dw_tile<E>(lds, xcd_logical_id(blockIdx.x, gridDim.x), dy, x, ws, nrows, mg, ng, rows_per_split, tiles_m,
+             tiles_n);
+}
+
+// Backward in one launch: the first ndw_pad workgroups are dw split partials,
+// the rest are dX tiles (the forward structure on the transpose spectra).
+// Both roles read dY; running them in one grid lets the dispatcher fill the
+// tail of one role with work of the other.  ndw_pad is a multiple of 8, so
+// each role keeps its own XCD-aware numbering.
+template <typename E, int SCHED>
+__global__ void __launch_bounds__(kThreads)
+bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E* __restrict__ wb,
+                 E* __restrict__ dx, float* __restrict__ ws, int64_t nrows, int dg, int cg,
+                 int64_t rows_per_split, int dw_tiles_m, int dw_tiles_n, int64_t ndw, int64_t ndw_pad,
+                 int dx_tiles_n) {
+  constexpr int kLds = fwd_lds_bytes<E, 1, 1, 2, 2>() > kDwLdsBytes ? fwd_lds_bytes<E, 1, 1, 2, 2>() : kDwLdsBytes;
+  __shared__ __attribute__((aligned(16))) char lds[kLds];
+  const int64_t b = blockIdx.x;
+  if (b < ndw_pad) {
+    const int64_t lid = xcd_logical_id(b, ndw_pad);
+    if (lid < ndw) dw_tile<E>(lds, lid, dy, x, ws, nrows, dg, cg, rows_per_split, dw_tiles_m, dw_tiles_n);
+  } else {
+    const int64_t nb = gridDim.x - ndw_pad;
+    fwd_tile<E, 1, 1, 2, 2, SCHED>(lds, xcd_logical_id(b - ndw_pad, nb), dy, wb, dx, nrows, dg, cg, dx_tiles_n);
   }
 }
 
@@ -750,6 +797,36 @@ hipError_t launch_dw(int dtype, const void* dy, const void* x, float* ws, float*
   }
   const int64_t fgrid = cdiv((int64_t)mg * ng, 64);
   hipLaunchKernelGGL(dw_finalize_kernel, dim3((unsigned)fgrid), dim3(kThreads), 0, s, ws, dw, mg, ng, nsplit);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_fused(int dtype, const void* dy, const void* x, const void* wb, void* dx, float* ws,
+                            float* dw, int64_t nrows, int dg, int cg, int64_t rows_per_split, int nsplit,
+                            hipStream_t s) {
+  const int dw_tiles_m = (int)cdiv(dg, 64), dw_tiles_n = (int)cdiv(cg, 64);
+  const int64_t ndw = (int64_t)dw_tiles_m * dw_tiles_n * nsplit;
+  const int64_t ndw_pad = cdiv(ndw, 8) * 8;
+  const int dx_tiles_n = (int)cdiv(cg, 64);
+  const int64_t ndx = cdiv(nrows, 64) * dx_tiles_n;
+  const int64_t grid = ndw_pad + ndx;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (grid > 0) {
+    if (dtype == 0) {
+      hipLaunchKernelGGL((bwd_fused_kernel<float, 1>), dim3((unsigned)grid), dim3(kThreads), 0, s,
+                         static_cast<const float*>(dy), static_cast<const float*>(x),
+                         static_cast<const float*>(wb), static_cast<float*>(dx), ws, nrows, dg, cg,
+                         rows_per_split, dw_tiles_m, dw_tiles_n, ndw, ndw_pad, dx_tiles_n);
+    } else {
+      hipLaunchKernelGGL((bwd_fused_kernel<_Float16, 1>), dim3((unsigned)grid), dim3(kThreads), 0, s,
+                         static_cast<const _Float16*>(dy), static_cast<const _Float16*>(x),
+                         static_cast<const _Float16*>(wb), static_cast<_Float16*>(dx), ws, nrows, dg, cg,
+                         rows_per_split, dw_tiles_m, dw_tiles_n, ndw, ndw_pad, dx_tiles_n);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t fgrid = cdiv((int64_t)dg * cg, 64);
+  hipLaunchKernelGGL(dw_finalize_kernel, dim3((unsigned)fgrid), dim3(kThreads), 0, s, ws, dw, dg, cg, nsplit);
   return hipGetLastError();
 }
 
