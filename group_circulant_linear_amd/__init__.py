@@ -19,6 +19,12 @@ _BINDING = {
 def __getattr__(name):
     if name in _BINDING:
         return getattr(importlib.import_module(".eqlin", __name__), name)
-    if name in ("eqlin", "inputs", "build"):
+    if name in ("FlashEQLinear", "EQLinearFunction", "convert_state_dict"):
+        return getattr(importlib.import_module(".module", __name__), name)
+    if name in ("eqlin", "inputs", "build", "module"):
         return importlib.import_module("." + name, __name__)
     raise AttributeError(name)
+
+
+def __dir__():
+    return sorted(list(_BINDING) + ["eqlin", "inputs", "build", "module", "FlashEQLinear", "EQLinearFunction"])

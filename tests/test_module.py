@@ -1,0 +1,97 @@
+"""FlashEQLinear: the plug-and-play module over the C ABI (GPU), and its host-side
+pieces (CPU): construction, state-dict conversion, dense view, no CPU fallback."""
+import numpy as np
+import pytest
+
+import oracle
+from group_circulant_linear_amd.inputs import make_layer_inputs
+
+torch = pytest.importorskip("torch")
+from group_circulant_linear_amd.module import FlashEQLinear, convert_state_dict  # noqa: E402
+
+
+def test_dense_view_matches_oracle_expansion():
+    m = FlashEQLinear(24, 40)
+    W = m.dense_weight().detach().double().numpy()
+    assert np.array_equal(W, oracle.dense_expand(m.w.detach().double().numpy()))
+
+
+def test_from_naive_copies_parameters_and_rejects_other_groups():
+    w = torch.randn(5, 3, 4)
+    m = FlashEQLinear.from_naive(w)
+    assert (m.in_features, m.out_features) == (12, 20)
+    assert torch.equal(m.w.detach(), w)
+    with pytest.raises(ValueError):
+        FlashEQLinear.from_naive(torch.randn(5, 3, 8))
+    with pytest.raises(ValueError):
+        FlashEQLinear(10, 8)
+
+
+def test_convert_state_dict_renames_only_keys():
+    sd = {"blocks.0.mlp.fc1.weight_vec": torch.ones(2, 2, 4), "blocks.0.norm.weight": torch.ones(3)}
+    out = convert_state_dict(sd, {"weight_vec": "w"})
+    assert set(out) == {"blocks.0.mlp.fc1.w", "blocks.0.norm.weight"}
+    assert out["blocks.0.mlp.fc1.w"] is sd["blocks.0.mlp.fc1.weight_vec"]
+
+
+def test_no_cpu_fallback():
+    m = FlashEQLinear(16, 16)
+    with pytest.raises(ValueError):
+        m(torch.randn(3, 16))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dt,tol", [("f32", 1e-5), ("f16", 3e-3)])
+def test_module_forward_backward_matches_oracle(dt, tol):
+    B, S, C, D = 3, 197, 96, 160
+    X, w, dY = make_layer_inputs(B * S, C, D, dt, seed=11)
+    m = FlashEQLinear.from_naive(torch.from_numpy(w).cuda())
+    Xt = torch.from_numpy(X).cuda().reshape(B, S, C).requires_grad_(True)
+    Y = m(Xt)
+    assert Y.shape == (B, S, D)
+    Y.backward(torch.from_numpy(dY).cuda().reshape(B, S, D))
+    torch.cuda.synchronize()
+    Yr = oracle.forward_direct(X, w)
+    dXr, dwr = oracle.backward_direct(dY, X, w)
+
+    def rel(a, b):
+        return float(np.max(np.abs(a - b)) / np.max(np.abs(b)))
+    assert rel(Y.detach().double().cpu().numpy().reshape(-1, D), Yr) <= tol
+    assert rel(Xt.grad.double().cpu().numpy().reshape(-1, C), dXr) <= tol
+    # the parameter gradient is cast to the parameter dtype; f16 adds one rounding
+    assert rel(m.w.grad.double().cpu().numpy(), dwr) <= tol
+
+
+@pytest.mark.gpu
+def test_spectra_cache_follows_weight_updates():
+    X, w, _ = make_layer_inputs(300, 64, 64, "f32", seed=12, with_dy=False)
+    m = FlashEQLinear.from_naive(torch.from_numpy(w).cuda())
+    Xt = torch.from_numpy(X).cuda()
+    Y1 = m(Xt).detach().clone()
+    p1 = m._cache.prepared
+    Y1b = m(Xt)
+    assert m._cache.prepared is p1            # reused: same weight version
+    assert torch.equal(Y1, Y1b)
+    with torch.no_grad():
+        m.w.mul_(2.0)                         # in-place update bumps the version
+    Y2 = m(Xt)
+    assert m._cache.prepared is not p1
+    torch.cuda.synchronize()
+    assert torch.allclose(Y2, 2 * Y1, rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.gpu
+def test_sgd_step_through_module():
+    torch.manual_seed(0)
+    m = FlashEQLinear(128, 64).cuda()
+    opt = torch.optim.SGD(m.parameters(), lr=0.1)
+    X = torch.randn(512, 128, device="cuda")
+    target = torch.randn(512, 64, device="cuda")
+    losses = []
+    for _ in range(5):
+        opt.zero_grad()
+        loss = torch.nn.functional.mse_loss(m(X), target)
+        loss.backward()
+        opt.step()
+        losses.append(loss.item())
+    assert losses[-1] < losses[0]
