@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--forward-only", action="store_true",
                    help="time only the forward (for profiling the forward kernel); not a valid bench line")
+    p.add_argument("--mlp-block", action="store_true",
+                   help="time the EQ-MLP block fc1(+bias, GELU) -> fc2(+bias) of a two-layer workload with the "
+                        "fused epilogue, next to the dense torch block; prints its own JSON line")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="also run one plain device copy of this many MB (counter calibration)")
     return p.parse_args()
@@ -104,11 +107,75 @@ def cpu_baseline(layers, budget_s=12.0):
                       f"({', '.join(sorted(set(samples)))}), repeated for {elapsed:.1f} s"}
 
 
+def mlp_block(args):
+    """EQ-MLP block timing: fc1 (+bias, GELU fused) then fc2 (+bias fused)."""
+    import torch
+    from group_circulant_linear_amd import eqlin
+    from group_circulant_linear_amd.inputs import WORKLOADS, make_layer_inputs
+
+    wl = WORKLOADS[args.workload]
+    if len(wl.layers) != 2:
+        raise SystemExit("--mlp-block needs a two-layer workload (vitb_mlp, vith_mlp)")
+    dt = args.dtype or wl.dtypes[0]
+    tdt = torch.float32 if dt == "f32" else torch.float16
+    dev = torch.device("cuda:0")
+    L1, L2 = wl.layers
+    X, w1, _ = make_layer_inputs(L1.N, L1.C, L1.D, dt, seed=0, layer=0, with_dy=False)
+    _, w2, _ = make_layer_inputs(8, L2.C, L2.D, dt, seed=0, layer=1, with_dy=False)
+    rng = np.random.default_rng(1)
+    nsets = 3
+    Xs = [torch.from_numpy(X).to(dev) for _ in range(nsets)]
+    tw1, tw2 = torch.from_numpy(w1).to(dev), torch.from_numpy(w2).to(dev)
+    b1 = torch.from_numpy(rng.standard_normal(L1.D // 4).astype(X.dtype)).to(dev)
+    b2 = torch.from_numpy(rng.standard_normal(L2.D // 4).astype(X.dtype)).to(dev)
+    W1, W2 = eqlin.eqlin_prepare_weights(tw1), eqlin.eqlin_prepare_weights(tw2)
+    Hs = [torch.empty((L1.N, L1.D), dtype=tdt, device=dev) for _ in range(nsets)]
+    Ys = [torch.empty((L1.N, L2.D), dtype=tdt, device=dev) for _ in range(nsets)]
+
+    def eq_block(i):
+        eqlin.eqlin_forward_ex(Xs[i % nsets], W1, b1, "gelu", out=Hs[i % nsets])
+        eqlin.eqlin_forward_ex(Hs[i % nsets], W2, b2, "none", out=Ys[i % nsets])
+
+    D1, D2 = dense_weight(torch, tw1), dense_weight(torch, tw2)
+    db1, db2 = b1.repeat_interleave(4), b2.repeat_interleave(4)
+    F = torch.nn.functional
+
+    def dense_block(i):
+        h = F.gelu(F.linear(Xs[i % nsets], D1, db1))
+        return F.linear(h, D2, db2)
+
+    def timeit(fn, reps):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    eq_us = timeit(eq_block, args.steps)
+    dense_us = timeit(dense_block, args.steps)
+    flops = 2.0 * L1.N * (L1.C * L1.D + L2.C * L2.D)
+    print(json.dumps({"mode": "mlp_block", "workload": wl.name, "dtype": dt,
+                      "block": f"fc1 {L1.C}->{L1.D} +bias+GELU, fc2 {L2.C}->{L2.D} +bias, N={L1.N}",
+                      "eq_us": round(eq_us, 2), "dense_us": round(dense_us, 2),
+                      "speedup": round(dense_us / eq_us, 3),
+                      "eq_tflops_dense_equiv": round(flops / (eq_us * 1e-6) / 1e12, 2),
+                      "dense_what": "torch F.linear + F.gelu + F.linear on the pre-expanded dense weights"}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.mlp_block:
+        mlp_block(args)
+        return
 
     import torch
     from group_circulant_linear_amd import eqlin

@@ -176,8 +176,23 @@ int eqlin_forward(const void* X, int64_t N, int C, int D, int T, const void* W_h
   if (!aligned16(X) || !aligned16(W_hat) || !aligned16(Y)) return EQLIN_EALIGN;
   if (!fwd_offsets_fit(C, D / 4, dtype)) return EQLIN_ENOTSUP;
   const int tile = choose_fwd_tile(dtype, N, D / 4);
-  return hip_status(
-      eqlin::launch_forward(dtype, tile, X, W_hat, Y, N, C / 4, D / 4, static_cast<hipStream_t>(stream)));
+  return hip_status(eqlin::launch_forward(dtype, tile, X, W_hat, Y, N, C / 4, D / 4, nullptr, 0,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int eqlin_forward_ex(const void* X, int64_t N, int C, int D, int T, const void* W_hat, const void* bias, int act,
+                     void* Y, int dtype, void* stream) {
+  int st = check_shape(N, C, D, T, dtype);
+  if (st != EQLIN_OK) return st;
+  if (act != EQLIN_ACT_NONE && act != EQLIN_ACT_GELU) return EQLIN_EINVAL;
+  if (N == 0) return EQLIN_OK;
+  if (!X || !W_hat || !Y) return EQLIN_EINVAL;
+  if (!aligned16(X) || !aligned16(W_hat) || !aligned16(Y)) return EQLIN_EALIGN;
+  if (bias && (reinterpret_cast<uintptr_t>(bias) % elem_bytes(dtype)) != 0) return EQLIN_EALIGN;
+  if (!fwd_offsets_fit(C, D / 4, dtype)) return EQLIN_ENOTSUP;
+  const int tile = choose_fwd_tile(dtype, N, D / 4);
+  return hip_status(eqlin::launch_forward(dtype, tile, X, W_hat, Y, N, C / 4, D / 4, bias, act,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 size_t eqlin_backward_workspace_bytes(int64_t N, int C, int D, int T, int dtype) {
@@ -199,8 +214,8 @@ int eqlin_backward_dx(const void* dY, int64_t N, int C, int D, int T, const void
   // (input groups D', output groups C').
   const char* wb = static_cast<const char*>(W_hat) + transpose_offset(C, D, dtype);
   const int tile = choose_fwd_tile(dtype, N, C / 4);
-  return hip_status(
-      eqlin::launch_forward(dtype, tile, dY, wb, dX, N, D / 4, C / 4, static_cast<hipStream_t>(stream)));
+  return hip_status(eqlin::launch_forward(dtype, tile, dY, wb, dX, N, D / 4, C / 4, nullptr, 0,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 int eqlin_backward_dw(const void* dY, const void* X, int64_t N, int C, int D, int T, float* dw, void* workspace,

@@ -9,8 +9,9 @@ namespace eqlin {
 // each wave owns FM x FN fragments of 32 x 32 per accumulator plane, so the
 // workgroup tile is (32 FM WM) rows x (32 FN WN) output groups.
 bool fwd_tile_known(int tile);
+// bias: nullable, one storage-dtype value per output group; act: 0 none, 1 GELU (erf)
 hipError_t launch_forward(int dtype, int tile, const void* in, const void* wp, void* out, int64_t nrows,
-                          int kg, int mg, hipStream_t s);
+                          int kg, int mg, const void* bias, int act, hipStream_t s);
 hipError_t launch_dw(int dtype, const void* dy, const void* x, float* ws, float* dw, int64_t nrows, int mg,
                      int ng, int64_t rows_per_split, int nsplit, hipStream_t s);
 // dX (forward structure on the transpose spectra wb, tile 1122) and the dw

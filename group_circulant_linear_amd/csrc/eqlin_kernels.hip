@@ -84,6 +84,22 @@ __device__ __forceinline__ void idft4(float f0, float f2, float f1r, float f1i, 
   y[3] = d + i;
 }
 
+// erf(z) by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26: for z >= 0, erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5)
+// exp(-z^2) with t = 1 / (1 + p z); |error| <= 1.5e-7.  Odd extension for
+// z < 0.  exp(-z^2) uses the hardware base-2 exponential.
+__device__ __forceinline__ float erf_as7126(float z) {
+  const float a = fabsf(z);
+  const float t = __frcp_rn(1.0f + 0.3275911f * a);
+  const float poly = t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+  const float e = __builtin_amdgcn_exp2f(-a * a * 1.4426950408889634f);
+  const float r = 1.0f - poly * e;
+  return copysignf(r, z);
+}
+
+// GELU(x) = x * Phi(x) = x/2 * (1 + erf(x / sqrt(2)))
+__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erf_as7126(x * 0.70710678118654752f)); }
+
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 // Buffer resource over [base, base + bytes): raw buffer loads at offsets past
@@ -333,7 +349,7 @@ constexpr int fwd_lds_bytes() {
 template <typename E, int FM, int FN, int WM, int WN, int SCHED>
 __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __restrict__ in,
                                          const E* __restrict__ wp, E* __restrict__ out, int64_t nrows, int kg,
-                                         int mg, int tiles_n) {
+                                         int mg, int tiles_n, const E* __restrict__ bias, int act) {
   constexpr int NT = 64 * WM * WN;
   constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
   constexpr int GP = Traits<E>::kGroupsPerPiece;
@@ -432,19 +448,29 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
     __syncthreads();
   }
 
-  // epilogue: inverse group DFT in registers, one vector store per (row, group)
+  // epilogue: inverse group DFT in registers, optional group-invariant bias
+  // and GELU, one vector store per (row, group)
   const int64_t out_ld = 4 * (int64_t)mg;
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
       const int m = col0 + wc * 32 * FN + fn * 32 + li;
+      const float bm = (bias != nullptr && m < mg) ? (float)bias[m] : 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t row = row0 + wr * 32 * FM + fm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
         if (row < nrows && m < mg) {
           float y[4];
           idft4(acc[0][fm][fn][r], acc[1][fm][fn][r], acc[2][fm][fn][r], acc[3][fm][fn][r], y);
+          if (bias != nullptr) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) y[t] += bm;
+          }
+          if (act == 1) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) y[t] = gelu_erf(y[t]);
+          }
           E* dst = out + row * out_ld + 4 * (int64_t)m;
           if constexpr (sizeof(E) == 4) {
             st16(dst, __builtin_bit_cast(u32x4, f32x4{y[0], y[1], y[2], y[3]}));
@@ -461,10 +487,10 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
 template <typename E, int FM, int FN, int WM, int WN, int SCHED>
 __global__ void __launch_bounds__(64 * WM * WN)
 fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ out,
-           int64_t nrows, int kg, int mg, int tiles_n) {
+           int64_t nrows, int kg, int mg, int tiles_n, const E* __restrict__ bias, int act) {
   __shared__ __attribute__((aligned(16))) char lds[fwd_lds_bytes<E, FM, FN, WM, WN>()];
   fwd_tile<E, FM, FN, WM, WN, SCHED>(lds, xcd_logical_id(blockIdx.x, gridDim.x), in, wp, out, nrows, kg, mg,
-                                     tiles_n);
+                                     tiles_n, bias, act);
 }
 
 // ============================================================ dw partials
@@ -638,7 +664,8 @@ bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E* __r
     if (lid < ndw) dw_tile<E>(lds, lid, dy, x, ws, nrows, dg, cg, rows_per_split, dw_tiles_m, dw_tiles_n);
   } else {
     const int64_t nb = gridDim.x - ndw_pad;
-    fwd_tile<E, 1, 1, 2, 2, SCHED>(lds, xcd_logical_id(b - ndw_pad, nb), dy, wb, dx, nrows, dg, cg, dx_tiles_n);
+    fwd_tile<E, 1, 1, 2, 2, SCHED>(lds, xcd_logical_id(b - ndw_pad, nb), dy, wb, dx, nrows, dg, cg, dx_tiles_n,
+                                   nullptr, 0);
   }
 }
 
@@ -725,7 +752,8 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 }  // namespace
 
 template <typename E, int FM, int FN, int WM, int WN, int SCHED>
-hipError_t launch_fwd_s(const void* in, const void* wp, void* out, int64_t nrows, int kg, int mg, hipStream_t s) {
+hipError_t launch_fwd_s(const void* in, const void* wp, void* out, int64_t nrows, int kg, int mg,
+                        const void* bias, int act, hipStream_t s) {
   constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
   const int64_t tiles_m = cdiv(nrows, BM);
   const int tiles_n = (int)cdiv(mg, BN);
@@ -734,18 +762,19 @@ hipError_t launch_fwd_s(const void* in, const void* wp, void* out, int64_t nrows
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fwd_kernel<E, FM, FN, WM, WN, SCHED>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, s,
                      static_cast<const E*>(in), static_cast<const E*>(wp), static_cast<E*>(out), nrows, kg, mg,
-                     tiles_n);
+                     tiles_n, static_cast<const E*>(bias), act);
   return hipGetLastError();
 }
 
 template <typename E, int FM, int FN, int WM, int WN>
-hipError_t launch_fwd_t(const void* in, const void* wp, void* out, int64_t nrows, int kg, int mg, hipStream_t s) {
+hipError_t launch_fwd_t(const void* in, const void* wp, void* out, int64_t nrows, int kg, int mg, const void* bias,
+                        int act, hipStream_t s) {
   static const int sched = [] {
     const char* e = getenv("EQLIN_SCHED");
     return e ? atoi(e) : 1;
   }();
-  return sched == 1 ? launch_fwd_s<E, FM, FN, WM, WN, 1>(in, wp, out, nrows, kg, mg, s)
-                    : launch_fwd_s<E, FM, FN, WM, WN, 0>(in, wp, out, nrows, kg, mg, s);
+  return sched == 1 ? launch_fwd_s<E, FM, FN, WM, WN, 1>(in, wp, out, nrows, kg, mg, bias, act, s)
+                    : launch_fwd_s<E, FM, FN, WM, WN, 0>(in, wp, out, nrows, kg, mg, bias, act, s);
 }
 
 #define EQLIN_FWD_TILES(X) \
@@ -762,11 +791,11 @@ bool fwd_tile_known(int tile) {
 }
 
 hipError_t launch_forward(int dtype, int tile, const void* in, const void* wp, void* out, int64_t nrows,
-                          int kg, int mg, hipStream_t s) {
+                          int kg, int mg, const void* bias, int act, hipStream_t s) {
 #define EQLIN_CASE(T)                                                                                  \
   case T:                                                                                              \
-    return dtype == 0 ? launch_fwd_t<float, T / 1000, (T / 100) % 10, (T / 10) % 10, T % 10>(in, wp, out, nrows, kg, mg, s) \
-                      : launch_fwd_t<_Float16, T / 1000, (T / 100) % 10, (T / 10) % 10, T % 10>(in, wp, out, nrows, kg, mg, s);
+    return dtype == 0 ? launch_fwd_t<float, T / 1000, (T / 100) % 10, (T / 10) % 10, T % 10>(in, wp, out, nrows, kg, mg, bias, act, s) \
+                      : launch_fwd_t<_Float16, T / 1000, (T / 100) % 10, (T / 10) % 10, T % 10>(in, wp, out, nrows, kg, mg, bias, act, s);
   switch (tile) {
     EQLIN_FWD_TILES(EQLIN_CASE)
     default: return hipErrorInvalidValue;

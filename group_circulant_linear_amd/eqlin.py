@@ -58,6 +58,7 @@ def load_library(path: str = LIB) -> ctypes.CDLL:
         "eqlin_prepared_transpose_offset": (c_sz, [c_int, c_int, c_int, c_int]),
         "eqlin_prepare_weights": (c_int, [c_vp, c_int, c_int, c_int, c_int, c_vp, c_sz, c_vp]),
         "eqlin_forward": (c_int, [c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_int, c_vp]),
+        "eqlin_forward_ex": (c_int, [c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_int, c_vp, c_int, c_vp]),
         "eqlin_backward_workspace_bytes": (c_sz, [c_i64, c_int, c_int, c_int, c_int]),
         "eqlin_backward": (c_int, [c_vp, c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_fp, c_vp, c_sz,
                                    c_int, c_vp]),
@@ -153,6 +154,34 @@ def eqlin_forward(X: torch.Tensor, W_hat: Prepared, out: Optional[torch.Tensor] 
         raise ValueError("out has the wrong shape or dtype")
     _check("eqlin_forward", lib.eqlin_forward(_ptr(X), N, W_hat.C, W_hat.D, T_P4, _ptr(W_hat.buf), _ptr(out),
                                               dt, _stream(X)))
+    return out
+
+
+ACT = {"none": 0, "gelu": 1}
+
+
+def eqlin_forward_ex(X: torch.Tensor, W_hat: Prepared, bias: Optional[torch.Tensor] = None, act: str = "none",
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = act(X W^T + b) in one kernel; bias [D/4] (group-invariant, storage dtype) or None."""
+    lib = load_library()
+    _need_cuda(X, "X")
+    dt = _dtype_code(X)
+    if X.dtype != W_hat.dtype:
+        raise TypeError("X and the prepared weights differ in dtype")
+    if X.dim() != 2 or X.shape[1] != W_hat.C:
+        raise ValueError(f"X must have shape [N, {W_hat.C}], got {tuple(X.shape)}")
+    if act not in ACT:
+        raise ValueError(f"act must be one of {sorted(ACT)}")
+    if bias is not None:
+        _need_cuda(bias, "bias")
+        if bias.dtype != X.dtype or tuple(bias.shape) != (W_hat.D // 4,):
+            raise ValueError(f"bias must be [{W_hat.D // 4}] of dtype {X.dtype}")
+    N = X.shape[0]
+    if out is None:
+        out = torch.empty((N, W_hat.D), dtype=X.dtype, device=X.device)
+    _need_cuda(out, "out")
+    _check("eqlin_forward_ex", lib.eqlin_forward_ex(_ptr(X), N, W_hat.C, W_hat.D, T_P4, _ptr(W_hat.buf),
+                                                    _ptr(bias), ACT[act], _ptr(out), dt, _stream(X)))
     return out
 
 

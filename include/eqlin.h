@@ -24,7 +24,8 @@
  *     group_channel * 4 + group_element (group element fastest).
  *   - All matrices are row-major and contiguous:
  *       X, dX  [N][C]      Y, dY  [N][D]      w  [D'][C'][4]     dw [D'][C'][4]
- *   - dtype EQLIN_F32: X, Y, dY, dX, w in float32, arithmetic in float32.
+ *   - dtype EQLIN_F32: X, Y, dY, dX, w in float32, arithmetic in float32
+ *     (true fp32 matrix-core products).
  *     dtype EQLIN_F16: X, Y, dY, dX, w stored as IEEE binary16; the group
  *     transforms run in float32, the Fourier operands are rounded once
  *     (nearest-even) to binary16 for the matrix cores, products accumulate in
@@ -79,15 +80,22 @@ int eqlin_last_hip_error(void);
  * Size in bytes of the prepared-weight buffer W_hat for a layer, or 0 if the
  * arguments are invalid.
  *
- * W_hat layout (element = the storage dtype, es = 4 or 2 bytes):
- *   offset 0:            forward planes  Wf[D'][C'][4] = (F0, F2, Re F1, Im F1)
- *   offset eqlin_prepared_transpose_offset(): transpose planes
- *                        Wb[C'][D'][4] = (F0, F2, Re F1, -Im F1)
- * where F_k[d', c'] = sum_u w[d', c', u] exp(-2 pi i k u / 4) is the group DFT
- * of each circulant vector ("Algorithmic approach", item 1), F3 = conj(F1)
- * being redundant for real w (item 2).  Wb is the spectrum of the transposed,
- * group-reversed weight used by the dX pass (a conjugate, so the sign of Im F1
- * flips).
+ * W_hat layout (element = the storage dtype; S = 16 for EQLIN_F32, 32 for
+ * EQLIN_F16 group channels per 64-byte block):
+ *   offset 0: forward set  [D'][ceil(C'/S)][4 planes][S]
+ *   offset eqlin_prepared_transpose_offset() (a multiple of 256):
+ *             transpose set [C'][ceil(D'/S)][4 planes][S]
+ * Planes of the forward set are (F0, F2, Re F1, Im F1) of w[d'][c'], where
+ * F_k = sum_u w[d', c', u] exp(-2 pi i k u / 4) is the group DFT of each
+ * circulant vector ("Algorithmic approach", item 1; F3 = conj(F1) is
+ * redundant for real w, item 2).  The transpose set holds
+ * (F0, F2, Re F1, -Im F1): the spectrum of the transposed, group-reversed
+ * weight (a conjugate) used by the dX pass.  Within block ks of a row, slot s
+ * holds group channel ks*S + g(s) with
+ *   g(s) = (s >> 2) + 4 (s & 3)                              (EQLIN_F32)
+ *   g(s) = 2 ((s >> 3) + 4 ((s >> 1) & 3)) + (s & 1)          (EQLIN_F16)
+ * (the order in which the forward kernel's loaders deposit the transformed
+ * input on chip), and slots past the last group channel hold zeros.
  */
 size_t eqlin_prepared_weight_bytes(int C, int D, int T, int dtype);
 size_t eqlin_prepared_transpose_offset(int C, int D, int T, int dtype);
@@ -112,6 +120,24 @@ int eqlin_prepare_weights(const void* w, int C, int D, int T, int dtype,
  */
 int eqlin_forward(const void* X, int64_t N, int C, int D, int T,
                   const void* W_hat, void* Y, int dtype, void* stream);
+
+/* Epilogue activations for eqlin_forward_ex. */
+enum { EQLIN_ACT_NONE = 0, EQLIN_ACT_GELU = 1 };
+
+/*
+ * Forward with a fused epilogue: Y = act(X W^T + b).
+ *   bias: NULL or a device pointer to D' = D/4 values in the storage dtype
+ *         (element-aligned).  The bias is group-invariant: b[d'] is added to
+ *         all four outputs 4d'+0..3 of output group d', which keeps the layer
+ *         equivariant (the summary is silent on bias; this is the reading).
+ *   act:  EQLIN_ACT_NONE or EQLIN_ACT_GELU (GELU(z) = z/2 (1 + erf(z/sqrt 2)),
+ *         pointwise, so it commutes with the group shift), else EQLIN_EINVAL.
+ * The bias add and the activation run in float32 in the register epilogue
+ * of the same kernel, before the single rounding to the storage dtype.
+ * Forward only (inference); everything else as eqlin_forward.
+ */
+int eqlin_forward_ex(const void* X, int64_t N, int C, int D, int T, const void* W_hat,
+                     const void* bias, int act, void* Y, int dtype, void* stream);
 
 /* Workspace bytes eqlin_backward / eqlin_backward_dw need for this shape. */
 size_t eqlin_backward_workspace_bytes(int64_t N, int C, int D, int T, int dtype);

@@ -45,6 +45,8 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
+    "forward_bias_act",
+    "gelu_erf",
     "dense_expand",
     "forward_direct",
     "backward_direct",
@@ -201,3 +203,26 @@ def dw_entries(dY, X, idx, T: int = 4) -> np.ndarray:
         for u in range(T):
             out[i, u] = float(np.sum(g * np.roll(x, u, axis=1)))
     return out
+
+
+def gelu_erf(z) -> np.ndarray:
+    """GELU by its definition z * Phi(z) = z/2 * (1 + erf(z / sqrt 2)), float64."""
+    from math import erf, sqrt
+    z = _f64(z)
+    verf = np.vectorize(erf, otypes=[np.float64])
+    return 0.5 * z * (1.0 + verf(z / sqrt(2.0)))
+
+
+def forward_bias_act(X, w, bias=None, act: str = "none") -> np.ndarray:
+    """act(X W^T + b) with a group-invariant bias b[d'] added to the T outputs of
+    output group d' (reading: the summary is silent on bias; a bias shared by the
+    group elements keeps the layer equivariant) and an optional GELU."""
+    Y = forward_direct(X, w)
+    T = _f64(w).shape[2]
+    if bias is not None:
+        Y = Y + np.repeat(_f64(bias), T)[None, :]
+    if act == "gelu":
+        Y = gelu_erf(Y)
+    elif act != "none":
+        raise ValueError(act)
+    return Y

@@ -99,3 +99,11 @@ def test_python_binding_rejects_cpu_tensors():
     w = torch.zeros(8, 8, 4)
     with pytest.raises(ValueError):
         eqlin.eqlin_prepare_weights(w)
+
+
+def test_forward_ex_validation(lib):
+    f = lib.eqlin_forward_ex
+    assert f(FAKE, 8, 32, 32, 4, FAKE, None, 2, FAKE, 0, None) == EINVAL        # unknown activation
+    assert f(FAKE, 8, 32, 32, 4, FAKE, ctypes.c_void_p(0x1001), 1, FAKE, 0, None) == EALIGN  # misaligned fp32 bias
+    assert f(FAKE, 8, 32, 32, 3, FAKE, None, 1, FAKE, 0, None) == ENOTSUP
+    assert f(None, 0, 32, 32, 4, None, None, 1, None, 0, None) == OK            # empty batch

@@ -346,3 +346,30 @@ def test_pins_catch_planted_mistakes():
 
     assert _rel(wrong_orientation(X, w), ref) > 1e-3
     assert _rel(dropped_shift(X, w), ref) > 1e-3
+
+
+# ------------------------------------------------- fused epilogue (bias, GELU)
+
+def test_gelu_matches_torch_and_closed_forms():
+    torch = pytest.importorskip("torch")
+    z = np.linspace(-8, 8, 1001)
+    ref = torch.nn.functional.gelu(torch.tensor(z, dtype=torch.float64)).numpy()
+    assert np.max(np.abs(oracle.gelu_erf(z) - ref)) < 1e-15
+    assert oracle.gelu_erf(np.array([0.0]))[0] == 0.0
+    # GELU(z) - GELU(-z) = z (Phi(z) + Phi(-z) = 1)
+    assert np.max(np.abs(oracle.gelu_erf(z) - oracle.gelu_erf(-z) - z)) < 1e-14
+
+
+def test_bias_act_forward_is_equivariant_and_reduces_to_forward():
+    X = _rand((7, 24), 40)
+    w = _rand((5, 6, 4), 41)
+    b = _rand(5, 42)
+    assert np.array_equal(oracle.forward_bias_act(X, w), oracle.forward_direct(X, w))
+    Y = oracle.forward_bias_act(X, w, b, "gelu").reshape(7, 5, 4)
+    Xr = np.roll(X.reshape(7, 6, 4), 1, axis=2).reshape(7, 24)
+    Yr = oracle.forward_bias_act(Xr, w, b, "gelu").reshape(7, 5, 4)
+    assert _rel(Yr, np.roll(Y, 1, axis=2)) < 1e-14
+    # the bias is one value per output group, the same for all four elements
+    Z = oracle.forward_bias_act(X, w, b) - oracle.forward_direct(X, w)
+    assert np.allclose(Z.reshape(7, 5, 4), b[None, :, None], rtol=0, atol=1e-14)
+
