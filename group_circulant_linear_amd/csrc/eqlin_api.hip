@@ -59,10 +59,10 @@ struct TileShape {
   int code, bm, bn;
   double eff;  // measured fraction of the MFMA peak on large shapes (MI355X)
 };
-// Forward tile candidates (code = FM FN WM WN) with their measured efficiency
+// Forward tile candidates (code = FM FN WM WN NBUF) with their measured efficiency
 // on the ViT-B / ViT-H layer shapes.
-constexpr TileShape kF32Tiles[] = {{1122, 64, 64, 0.64}, {1112, 32, 64, 0.52}, {1121, 64, 32, 0.50}};
-constexpr TileShape kF16Tiles[] = {{2124, 128, 128, 0.21}, {1122, 64, 64, 0.18}, {1112, 32, 64, 0.13}};
+constexpr TileShape kF32Tiles[] = {{11221, 64, 64, 0.70}, {11222, 64, 64, 0.63}, {11122, 32, 64, 0.52}};
+constexpr TileShape kF16Tiles[] = {{21242, 128, 128, 0.24}, {11221, 64, 64, 0.20}, {11122, 32, 64, 0.13}};
 
 // Forward tile choice: workgroups are spread round-robin over the CUs, so a
 // CU's work is ceil(tiles / CUs) tiles; minimise that work divided by the
@@ -110,7 +110,7 @@ struct DwPlan {
 DwPlan plan_dw(int64_t N, int C, int D, int dtype) {
   DwPlan p{0, 0};
   if (N <= 0) return p;
-  // two 64 x 64 workgroups fit one CU (LDS); use at most that many in total
+  // a few 64 x 64 workgroups fit one CU; use at most two per CU in total
   const int64_t tiles = cdiv(D / 4, 64) * cdiv(C / 4, 64);
   const int64_t stage = eqlin::dw_rows_per_stage(dtype);
   const int64_t row_bytes = int64_t(C > D ? C : D) * elem_bytes(dtype);

@@ -47,6 +47,17 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kNumXcd = 8;
+#ifndef EQLIN_DW_BUFS
+#define EQLIN_DW_BUFS 1
+#endif
+#ifndef EQLIN_BWD_FWD_BUFS
+#define EQLIN_BWD_FWD_BUFS 1
+#endif
+// LDS stage buffers of the dw partial tiles and of the dX tiles inside the
+// fused backward (1: smaller LDS, more resident workgroups per CU).
+constexpr int kDwBufs = EQLIN_DW_BUFS;
+constexpr int kBwdFwdBufs = EQLIN_BWD_FWD_BUFS;
+
 // LDS plane rows are 64 bytes (four 16-byte slots) with no padding; the slot
 // index is XOR-swizzled with bits 2-3 of the row, which keeps both the
 // 4-lanes-per-row stores and the 32-rows-per-wave fragment reads free of bank
@@ -340,13 +351,15 @@ __device__ __forceinline__ void interleave_schedule() {
 // flagged out of range (groups >= kg) return zeros without branches.
 // LDS is double-buffered: one barrier per stage, and the loads of stage s+2
 // are in flight while stage s is multiplied.
-template <typename E, int FM, int FN, int WM, int WN>
+template <typename E, int FM, int FN, int WM, int WN, int NBUF>
 constexpr int fwd_lds_bytes() {
-  return 2 * 4 * (32 * FM * WM + 32 * FN * WN) * kRowBytes;
+  return NBUF * 4 * (32 * FM * WM + 32 * FN * WN) * kRowBytes;
 }
 
-// One forward (or dX) tile: workgroup-level logical tile id `lid`.
-template <typename E, int FM, int FN, int WM, int WN, int SCHED>
+// One forward (or dX) tile: workgroup-level logical tile id `lid`.  NBUF = 2
+// double-buffers the LDS stages (one barrier per stage); NBUF = 1 halves the
+// LDS footprint (two barriers per stage) so that more workgroups fit a CU.
+template <typename E, int FM, int FN, int WM, int WN, int NBUF, int SCHED>
 __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __restrict__ in,
                                          const E* __restrict__ wp, E* __restrict__ out, int64_t nrows, int kg,
                                          int mg, int tiles_n, const E* __restrict__ bias, int act) {
@@ -359,7 +372,7 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
   constexpr int BUF = 4 * (A_PLANE + B_PLANE);
   constexpr int RPP = NT / 4;              // tile rows covered per load pass
   constexpr int PA = (BM + RPP - 1) / RPP, PB = (BN + RPP - 1) / RPP;
-  static_assert(2 * BUF == fwd_lds_bytes<E, FM, FN, WM, WN>(), "LDS size");
+  static_assert(NBUF * BUF == fwd_lds_bytes<E, FM, FN, WM, WN, NBUF>(), "LDS size");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row0 = (lid / tiles_n) * BM;
@@ -435,16 +448,17 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
   load(1);
   __syncthreads();
   // Branch-free steady state: past the last stage the loads read zeros (out
-  // of range) and the store fills the idle buffer, so one basic block holds
+  // of range) and the store fills an idle buffer, so one basic block holds
   // the MFMAs, the next stage's transform / LDS writes and the loads two
   // stages ahead, and the scheduler can interleave them.
   for (int ks = 0; ks < ksteps; ++ks) {
-    char* cur = lds + (ks & 1) * BUF;
+    char* cur = lds + (NBUF == 2 ? (ks & 1) * BUF : 0);
     mma_chunk<E, FM, FN>(acc, cur + a_frag + c0, A_PLANE, cur + b_frag + c0, B_PLANE, STRIDE);
     mma_chunk<E, FM, FN>(acc, cur + a_frag + c1, A_PLANE, cur + b_frag + c1, B_PLANE, STRIDE);
-    store(lds + ((ks + 1) & 1) * BUF);
+    if constexpr (NBUF == 1) __syncthreads();   // every wave is done reading the only buffer
+    store(lds + (NBUF == 2 ? ((ks + 1) & 1) * BUF : 0));
     load(ks + 2);
-    if constexpr (SCHED == 1) interleave_schedule<E, FM, FN, PA, PB>();
+    if constexpr (SCHED == 1 && NBUF == 2) interleave_schedule<E, FM, FN, PA, PB>();
     __syncthreads();
   }
 
@@ -484,12 +498,13 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
   }
 }
 
-template <typename E, int FM, int FN, int WM, int WN, int SCHED>
-__global__ void __launch_bounds__(64 * WM * WN)
+// Two waves per SIMD (256 registers per lane) unless a wave holds 4+ fragments.
+template <typename E, int FM, int FN, int WM, int WN, int NBUF, int SCHED>
+__global__ void __launch_bounds__(64 * WM * WN, FM * FN >= 4 ? 1 : 2)
 fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ out,
            int64_t nrows, int kg, int mg, int tiles_n, const E* __restrict__ bias, int act) {
-  __shared__ __attribute__((aligned(16))) char lds[fwd_lds_bytes<E, FM, FN, WM, WN>()];
-  fwd_tile<E, FM, FN, WM, WN, SCHED>(lds, xcd_logical_id(blockIdx.x, gridDim.x), in, wp, out, nrows, kg, mg,
+  __shared__ __attribute__((aligned(16))) char lds[fwd_lds_bytes<E, FM, FN, WM, WN, NBUF>()];
+  fwd_tile<E, FM, FN, WM, WN, NBUF, SCHED>(lds, xcd_logical_id(blockIdx.x, gridDim.x), in, wp, out, nrows, kg, mg,
                                      tiles_n, bias, act);
 }
 
@@ -503,9 +518,12 @@ fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ o
 // groups), transforms them and writes, per group and plane, the 4 rows as one
 // contiguous LDS vector (16 B fp32, 8 B f16).  A stage is 64 bytes of every
 // plane row (16 fp32 / 32 f16 rows); LDS is double-buffered as in fwd_kernel.
-constexpr int kDwLdsBytes = 2 * 8 * 64 * kRowBytes;
+template <int NBUF>
+constexpr int dw_lds_bytes() {
+  return NBUF * 8 * 64 * kRowBytes;
+}
 
-template <typename E>
+template <typename E, int NBUF>
 __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restrict__ dy, const E* __restrict__ x,
                                         float* __restrict__ ws, int64_t nrows, int mg, int ng,
                                         int64_t rows_per_split, int tiles_m, int tiles_n) {
@@ -518,7 +536,7 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
   constexpr int PLANE = 64 * STRIDE;
   constexpr int BUF = 8 * PLANE;
   static_assert(SR * (int)sizeof(E) == 64, "one stage is 64 bytes per plane row");
-  static_assert(2 * BUF == kDwLdsBytes, "LDS size");
+  static_assert(NBUF * BUF == dw_lds_bytes<NBUF>(), "LDS size");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ntiles = tiles_m * tiles_n;
@@ -613,11 +631,12 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
     __syncthreads();
   }
   for (int st = 0; st < nstages; ++st) {
-    char* cur = lds + (st & 1) * BUF;
+    char* cur = lds + (NBUF == 2 ? (st & 1) * BUF : 0);
     mma_chunk<E, 1, 1>(acc, cur + a_frag + c0, PLANE, cur + b_frag + c0, PLANE, STRIDE);
     mma_chunk<E, 1, 1>(acc, cur + a_frag + c1, PLANE, cur + b_frag + c1, PLANE, STRIDE);
     if (st + 1 < nstages) {
-      store(lds + ((st + 1) & 1) * BUF);
+      if constexpr (NBUF == 1) __syncthreads();   // every wave is done reading the only buffer
+      store(lds + (NBUF == 2 ? ((st + 1) & 1) * BUF : 0));
       if (st + 2 < nstages) load(st + 2);
     }
     __syncthreads();
@@ -637,11 +656,11 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
 }
 
 template <typename E>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads, 2)
 dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __restrict__ ws,
                   int64_t nrows, int mg, int ng, int64_t rows_per_split, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) char lds[kDwLdsBytes];
-  dw_tile<E>(lds, xcd_logical_id(blockIdx.x, gridDim.x), dy, x, ws, nrows, mg, ng, rows_per_split, tiles_m,
+  __shared__ __attribute__((aligned(16))) char lds[dw_lds_bytes<kDwBufs>()];
+  dw_tile<E, kDwBufs>(lds, xcd_logical_id(blockIdx.x, gridDim.x), dy, x, ws, nrows, mg, ng, rows_per_split, tiles_m,
              tiles_n);
 }
 
@@ -651,20 +670,22 @@ dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __re
 // tail of one role with work of the other.  ndw_pad is a multiple of 8, so
 // each role keeps its own XCD-aware numbering.
 template <typename E, int SCHED>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads, 2)
 bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E* __restrict__ wb,
                  E* __restrict__ dx, float* __restrict__ ws, int64_t nrows, int dg, int cg,
                  int64_t rows_per_split, int dw_tiles_m, int dw_tiles_n, int64_t ndw, int64_t ndw_pad,
                  int dx_tiles_n) {
-  constexpr int kLds = fwd_lds_bytes<E, 1, 1, 2, 2>() > kDwLdsBytes ? fwd_lds_bytes<E, 1, 1, 2, 2>() : kDwLdsBytes;
+  constexpr int kLds = fwd_lds_bytes<E, 1, 1, 2, 2, kBwdFwdBufs>() > dw_lds_bytes<kDwBufs>()
+                           ? fwd_lds_bytes<E, 1, 1, 2, 2, kBwdFwdBufs>()
+                           : dw_lds_bytes<kDwBufs>();
   __shared__ __attribute__((aligned(16))) char lds[kLds];
   const int64_t b = blockIdx.x;
   if (b < ndw_pad) {
     const int64_t lid = xcd_logical_id(b, ndw_pad);
-    if (lid < ndw) dw_tile<E>(lds, lid, dy, x, ws, nrows, dg, cg, rows_per_split, dw_tiles_m, dw_tiles_n);
+    if (lid < ndw) dw_tile<E, kDwBufs>(lds, lid, dy, x, ws, nrows, dg, cg, rows_per_split, dw_tiles_m, dw_tiles_n);
   } else {
     const int64_t nb = gridDim.x - ndw_pad;
-    fwd_tile<E, 1, 1, 2, 2, SCHED>(lds, xcd_logical_id(b - ndw_pad, nb), dy, wb, dx, nrows, dg, cg, dx_tiles_n,
+    fwd_tile<E, 1, 1, 2, 2, kBwdFwdBufs, SCHED>(lds, xcd_logical_id(b - ndw_pad, nb), dy, wb, dx, nrows, dg, cg, dx_tiles_n,
                                    nullptr, 0);
   }
 }
@@ -751,7 +772,7 @@ namespace {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 }  // namespace
 
-template <typename E, int FM, int FN, int WM, int WN, int SCHED>
+template <typename E, int FM, int FN, int WM, int WN, int NBUF, int SCHED>
 hipError_t launch_fwd_s(const void* in, const void* wp, void* out, int64_t nrows, int kg, int mg,
                         const void* bias, int act, hipStream_t s) {
   constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
@@ -760,25 +781,26 @@ hipError_t launch_fwd_s(const void* in, const void* wp, void* out, int64_t nrows
   const int64_t grid = tiles_m * tiles_n;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_kernel<E, FM, FN, WM, WN, SCHED>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, s,
+  hipLaunchKernelGGL((fwd_kernel<E, FM, FN, WM, WN, NBUF, SCHED>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, s,
                      static_cast<const E*>(in), static_cast<const E*>(wp), static_cast<E*>(out), nrows, kg, mg,
                      tiles_n, static_cast<const E*>(bias), act);
   return hipGetLastError();
 }
 
-template <typename E, int FM, int FN, int WM, int WN>
+template <typename E, int FM, int FN, int WM, int WN, int NBUF>
 hipError_t launch_fwd_t(const void* in, const void* wp, void* out, int64_t nrows, int kg, int mg, const void* bias,
                         int act, hipStream_t s) {
   static const int sched = [] {
     const char* e = getenv("EQLIN_SCHED");
     return e ? atoi(e) : 1;
   }();
-  return sched == 1 ? launch_fwd_s<E, FM, FN, WM, WN, 1>(in, wp, out, nrows, kg, mg, bias, act, s)
-                    : launch_fwd_s<E, FM, FN, WM, WN, 0>(in, wp, out, nrows, kg, mg, bias, act, s);
+  return sched == 1 ? launch_fwd_s<E, FM, FN, WM, WN, NBUF, 1>(in, wp, out, nrows, kg, mg, bias, act, s)
+                    : launch_fwd_s<E, FM, FN, WM, WN, NBUF, 0>(in, wp, out, nrows, kg, mg, bias, act, s);
 }
 
+// compiled forward tiles, code = FM FN WM WN NBUF (decimal digits)
 #define EQLIN_FWD_TILES(X) \
-  X(1122) X(1121) X(1112) X(2122) X(1222) X(1141) X(2222) X(2121) X(1124) X(2124) X(1142)
+  X(11222) X(11122) X(11212) X(21222) X(12222) X(22222) X(21242) X(11241) X(21221) X(12221) X(11221)
 
 bool fwd_tile_known(int tile) {
   switch (tile) {
@@ -794,8 +816,11 @@ hipError_t launch_forward(int dtype, int tile, const void* in, const void* wp, v
                           int kg, int mg, const void* bias, int act, hipStream_t s) {
 #define EQLIN_CASE(T)                                                                                  \
   case T:                                                                                              \
-    return dtype == 0 ? launch_fwd_t<float, T / 1000, (T / 100) % 10, (T / 10) % 10, T % 10>(in, wp, out, nrows, kg, mg, bias, act, s) \
-                      : launch_fwd_t<_Float16, T / 1000, (T / 100) % 10, (T / 10) % 10, T % 10>(in, wp, out, nrows, kg, mg, bias, act, s);
+    return dtype == 0                                                                                      \
+               ? launch_fwd_t<float, T / 10000, (T / 1000) % 10, (T / 100) % 10, (T / 10) % 10, T % 10>(     \
+                     in, wp, out, nrows, kg, mg, bias, act, s)                                                \
+               : launch_fwd_t<_Float16, T / 10000, (T / 1000) % 10, (T / 100) % 10, (T / 10) % 10, T % 10>(  \
+                     in, wp, out, nrows, kg, mg, bias, act, s);
   switch (tile) {
     EQLIN_FWD_TILES(EQLIN_CASE)
     default: return hipErrorInvalidValue;

@@ -100,7 +100,8 @@ def _forward_case(dt, N, C, D, seed=0):
     return X, w, host(Y)
 
 
-@pytest.mark.parametrize("tile", ["auto", "1122", "1121", "1112", "2122", "1222", "1141", "2222", "2121"])
+@pytest.mark.parametrize("tile", ["auto", "11222", "11122", "11212", "21222", "12222", "22222", "21242",
+                                  "11241", "21221", "12221", "11221"])
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 def test_forward_small_shapes_all_tiles(dt, tile, monkeypatch):
     if tile != "auto":
