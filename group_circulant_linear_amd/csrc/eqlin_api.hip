@@ -59,10 +59,10 @@ struct TileShape {
   int code, bm, bn;
   double eff;  // measured fraction of the MFMA peak on large shapes (MI355X)
 };
-// Forward tile candidates (code = FM FN WM WN NBUF) with their measured efficiency
+// Forward tile candidates (code = FM FN WM WN NBUF PF) with their measured efficiency
 // on the ViT-B / ViT-H layer shapes.
-constexpr TileShape kF32Tiles[] = {{11221, 64, 64, 0.70}, {11222, 64, 64, 0.63}, {11122, 32, 64, 0.52}};
-constexpr TileShape kF16Tiles[] = {{21242, 128, 128, 0.24}, {11221, 64, 64, 0.20}, {11122, 32, 64, 0.13}};
+constexpr TileShape kF32Tiles[] = {{112211, 64, 64, 0.70}, {112221, 64, 64, 0.63}, {111221, 32, 64, 0.52}};
+constexpr TileShape kF16Tiles[] = {{212421, 128, 128, 0.24}, {112211, 64, 64, 0.20}, {111221, 32, 64, 0.13}};
 
 // Forward tile choice: workgroups are spread round-robin over the CUs, so a
 // CU's work is ceil(tiles / CUs) tiles; minimise that work divided by the

@@ -5,10 +5,11 @@
 
 namespace eqlin {
 
-// Forward tile codes: five digits FM FN WM WN NBUF.  A workgroup has WM x WN
+// Forward tile codes: six digits FM FN WM WN NBUF PF.  A workgroup has WM x WN
 // waves; each wave owns FM x FN fragments of 32 x 32 per accumulator plane, so
 // the workgroup tile is (32 FM WM) rows x (32 FN WN) output groups; NBUF (1 or
-// 2) is the number of LDS stage buffers.
+// 2) is the number of LDS stage buffers and PF (1 or 2) the number of stages
+// of global loads in flight in registers.
 bool fwd_tile_known(int tile);
 // bias: nullable, one storage-dtype value per output group; act: 0 none, 1 GELU (erf)
 hipError_t launch_forward(int dtype, int tile, const void* in, const void* wp, void* out, int64_t nrows,

@@ -34,6 +34,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "eqlin_kernels.h"
 
 namespace eqlin {
@@ -57,6 +59,10 @@ constexpr int kNumXcd = 8;
 // fused backward (1: smaller LDS, more resident workgroups per CU).
 constexpr int kDwBufs = EQLIN_DW_BUFS;
 constexpr int kBwdFwdBufs = EQLIN_BWD_FWD_BUFS;
+#ifndef EQLIN_BWD_FWD_PREFETCH
+#define EQLIN_BWD_FWD_PREFETCH 1
+#endif
+constexpr int kBwdFwdPrefetch = EQLIN_BWD_FWD_PREFETCH;
 
 // LDS plane rows are 64 bytes (four 16-byte slots) with no padding; the slot
 // index is XOR-swizzled with bits 2-3 of the row, which keeps both the
@@ -173,8 +179,66 @@ __device__ __forceinline__ void pieces_to_planes<float, false, false>(const u32x
   for (int p = 0; p < 4; ++p) pl[p] = u32x4{pc[0][p], pc[1][p], pc[2][p], pc[3][p]};
 }
 
+// Group DFT of the two f16 groups of one 16-byte piece (registers lo01 =
+// (z0, z1), hi23 = (z2, z3) of group 0 and lo45 / hi67 of group 1), written as
+// packed f16 plane values: p0 = (F0_g0, F0_g1), p2 = (F2_g0, F2_g1),
+// p1r = (Re F1_g0, Re F1_g1), p1i = (+-Im F1_g0, +-Im F1_g1).  The mixed
+// precision FMA reads f16 halves directly, computes in f32 and rounds the
+// result once (nearest-even) into the low or high half of the destination:
+//   a = z0 + z2, b = z1 + z3 (f32);  F0 = a + b;  F2 = a - b;
+//   Re F1 = z0 - z2;  Im F1 = z3 - z1 (negated when kConj).
+template <bool kConj>
+__device__ __forceinline__ void dft4_f16_pair(uint32_t z01, uint32_t z23, uint32_t z45, uint32_t z67,
+                                              uint32_t& p0, uint32_t& p2, uint32_t& p1r, uint32_t& p1i) {
+  float a0, b0, a1, b1;
+  asm volatile(
+      "v_fma_mix_f32 %0, %4, 1.0, %5 op_sel:[0,0,0] op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mix_f32 %1, %4, 1.0, %5 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mix_f32 %2, %6, 1.0, %7 op_sel:[0,0,0] op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mix_f32 %3, %6, 1.0, %7 op_sel:[1,0,1] op_sel_hi:[1,0,1]"
+      : "=&v"(a0), "=&v"(b0), "=&v"(a1), "=&v"(b1)
+      : "v"(z01), "v"(z23), "v"(z45), "v"(z67));
+  asm volatile(
+      "v_fma_mixlo_f16 %0, %2, 1.0, %3 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixhi_f16 %0, %4, 1.0, %5 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixlo_f16 %1, %2, 1.0, -%3 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixhi_f16 %1, %4, 1.0, -%5 op_sel_hi:[0,0,0]"
+      : "=&v"(p0), "=&v"(p2)
+      : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
+  asm volatile(
+      "v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel:[0,0,0] op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mixhi_f16 %0, %3, 1.0, -%4 op_sel:[0,0,0] op_sel_hi:[1,0,1]"
+      : "=&v"(p1r)
+      : "v"(z01), "v"(z23), "v"(z45), "v"(z67));
+  if constexpr (!kConj) {
+    asm volatile(
+        "v_fma_mixlo_f16 %0, %2, 1.0, -%1 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\t"
+        "v_fma_mixhi_f16 %0, %4, 1.0, -%3 op_sel:[1,0,1] op_sel_hi:[1,0,1]"
+        : "=&v"(p1i)
+        : "v"(z01), "v"(z23), "v"(z45), "v"(z67));
+  } else {
+    asm volatile(
+        "v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\t"
+        "v_fma_mixhi_f16 %0, %3, 1.0, -%4 op_sel:[1,0,1] op_sel_hi:[1,0,1]"
+        : "=&v"(p1i)
+        : "v"(z01), "v"(z23), "v"(z45), "v"(z67));
+  }
+}
+
 template <bool kDft, bool kConj>
 __device__ __forceinline__ void pieces_to_planes_f16(const u32x4 (&pc)[4], u32x4 (&pl)[4]) {
+  if constexpr (kDft) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t p0, p2, p1r, p1i;
+      dft4_f16_pair<kConj>(pc[j][0], pc[j][1], pc[j][2], pc[j][3], p0, p2, p1r, p1i);
+      pl[0][j] = p0;
+      pl[1][j] = p2;
+      pl[2][j] = p1r;
+      pl[3][j] = p1i;
+    }
+    return;
+  }
   _Float16 h[4][8];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -359,7 +423,10 @@ constexpr int fwd_lds_bytes() {
 // One forward (or dX) tile: workgroup-level logical tile id `lid`.  NBUF = 2
 // double-buffers the LDS stages (one barrier per stage); NBUF = 1 halves the
 // LDS footprint (two barriers per stage) so that more workgroups fit a CU.
-template <typename E, int FM, int FN, int WM, int WN, int NBUF, int SCHED>
+// PF (1 or 2) is the number of stages whose global loads are in flight in
+// registers ahead of the stage being transformed into LDS: with f16 a stage
+// of MFMAs is short next to the memory latency, so two stages are needed.
+template <typename E, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED>
 __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __restrict__ in,
                                          const E* __restrict__ wp, E* __restrict__ out, int64_t nrows, int kg,
                                          int mg, int tiles_n, const E* __restrict__ bias, int act) {
@@ -386,8 +453,9 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
       make_rsrc(wp + (int64_t)col0 * ksteps * SG * 4, (uint64_t)(mg - col0) * (uint64_t)ksteps * 256u);
 
   const int q = tid & 3, rl = tid >> 2;
-  u32x4 ra[PA][4], rb[PB][4];
-  auto load = [&](int ks) {
+  u32x4 ra[PF][PA][4], rb[PF][PB][4];   // register ring of PF stages of loads
+  auto load = [&](int ks, auto slot_c) {
+    constexpr int sl = decltype(slot_c)::value;
 #pragma unroll
     for (int ps = 0; ps < PA; ++ps) {
       const uint32_t r = (uint32_t)(ps * RPP + rl);
@@ -395,7 +463,7 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
       for (int j = 0; j < 4; ++j) {
         const int g = ks * SG + (q + 4 * j) * GP;
         const uint32_t off = g < kg ? r * row_bytes + (uint32_t)g * 4u * (uint32_t)sizeof(E) : kOob;
-        ra[ps][j] = bload16(a_src, off);
+        ra[sl][ps][j] = bload16(a_src, off);
       }
     }
 #pragma unroll
@@ -403,16 +471,18 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
       const uint32_t m = (uint32_t)(ps * RPP + rl);
 #pragma unroll
       for (int p = 0; p < 4; ++p)
-        rb[ps][p] = bload16(b_src, ks < ksteps ? (m * (uint32_t)ksteps + (uint32_t)ks) * 256u + p * 64 + q * 16 : kOob);
+        rb[sl][ps][p] =
+            bload16(b_src, ks < ksteps ? (m * (uint32_t)ksteps + (uint32_t)ks) * 256u + p * 64 + q * 16 : kOob);
     }
   };
-  auto store = [&](char* buf) {
+  auto store = [&](char* buf, auto slot_c) {
+    constexpr int sl = decltype(slot_c)::value;
 #pragma unroll
     for (int ps = 0; ps < PA; ++ps) {
       const int r = ps * RPP + rl;
       if (BM % RPP == 0 || r < BM) {
         u32x4 pl[4];
-        pieces_to_planes<E, true, false>(ra[ps], pl);
+        pieces_to_planes<E, true, false>(ra[sl][ps], pl);
 #pragma unroll
         for (int p = 0; p < 4; ++p) st16(buf + p * A_PLANE + r * STRIDE + swz_slot(r, q) * 16, pl[p]);
       }
@@ -422,7 +492,8 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
       const int m = ps * RPP + rl;
       if (BN % RPP == 0 || m < BN) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) st16(buf + 4 * A_PLANE + p * B_PLANE + m * STRIDE + swz_slot(m, q) * 16, rb[ps][p]);
+        for (int p = 0; p < 4; ++p)
+          st16(buf + 4 * A_PLANE + p * B_PLANE + m * STRIDE + swz_slot(m, q) * 16, rb[sl][ps][p]);
       }
     }
   };
@@ -443,23 +514,41 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
   const int b_frag = 4 * A_PLANE + (wc * 32 * FN + li) * STRIDE;
   const int c0 = swz_slot(li, lh) * 16, c1 = swz_slot(li, 2 + lh) * 16;
 
-  load(0);
-  store(lds);
-  load(1);
-  __syncthreads();
-  // Branch-free steady state: past the last stage the loads read zeros (out
-  // of range) and the store fills an idle buffer, so one basic block holds
-  // the MFMAs, the next stage's transform / LDS writes and the loads two
-  // stages ahead, and the scheduler can interleave them.
-  for (int ks = 0; ks < ksteps; ++ks) {
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, PF - 1>;
+  // One pipeline step: multiply stage ks (LDS buffer of ks), then transform
+  // the registers of stage ks + 1 into the other (or, single-buffered, the
+  // same) buffer and issue the loads of stage ks + 1 + PF into the slot just
+  // freed.  Past the last stage the loads read zeros (out of range) and the
+  // stores fill an idle buffer, so the body is one basic block in which the
+  // scheduler can interleave MFMAs with the transform, LDS writes and loads.
+  auto step = [&](int ks, auto slot_next) {
     char* cur = lds + (NBUF == 2 ? (ks & 1) * BUF : 0);
     mma_chunk<E, FM, FN>(acc, cur + a_frag + c0, A_PLANE, cur + b_frag + c0, B_PLANE, STRIDE);
     mma_chunk<E, FM, FN>(acc, cur + a_frag + c1, A_PLANE, cur + b_frag + c1, B_PLANE, STRIDE);
     if constexpr (NBUF == 1) __syncthreads();   // every wave is done reading the only buffer
-    store(lds + (NBUF == 2 ? ((ks + 1) & 1) * BUF : 0));
-    load(ks + 2);
+    store(lds + (NBUF == 2 ? ((ks + 1) & 1) * BUF : 0), slot_next);
+    load(ks + 1 + PF, slot_next);
     if constexpr (SCHED == 1 && NBUF == 2) interleave_schedule<E, FM, FN, PA, PB>();
     __syncthreads();
+  };
+
+  load(0, S0{});
+  store(lds, S0{});
+  if constexpr (PF == 1) {
+    load(1, S0{});
+    __syncthreads();
+    for (int ks = 0; ks < ksteps; ++ks) step(ks, S0{});
+  } else {
+    // ring: stage s lives in slot (s + 1) % 2 once stage 0 has been stored
+    load(1, S1{});
+    load(2, S0{});
+    __syncthreads();
+    for (int ks = 0; ks < ksteps; ks += 2) {
+      step(ks, S1{});
+      if (ks + 1 >= ksteps) break;
+      step(ks + 1, S0{});
+    }
   }
 
   // epilogue: inverse group DFT in registers, optional group-invariant bias
@@ -499,12 +588,12 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
 }
 
 // Two waves per SIMD (256 registers per lane) unless a wave holds 4+ fragments.
-template <typename E, int FM, int FN, int WM, int WN, int NBUF, int SCHED>
+template <typename E, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED>
 __global__ void __launch_bounds__(64 * WM * WN, FM * FN >= 4 ? 1 : 2)
 fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ out,
            int64_t nrows, int kg, int mg, int tiles_n, const E* __restrict__ bias, int act) {
   __shared__ __attribute__((aligned(16))) char lds[fwd_lds_bytes<E, FM, FN, WM, WN, NBUF>()];
-  fwd_tile<E, FM, FN, WM, WN, NBUF, SCHED>(lds, xcd_logical_id(blockIdx.x, gridDim.x), in, wp, out, nrows, kg, mg,
+  fwd_tile<E, FM, FN, WM, WN, NBUF, PF, SCHED>(lds, xcd_logical_id(blockIdx.x, gridDim.x), in, wp, out, nrows, kg, mg,
                                      tiles_n, bias, act);
 }
 
@@ -685,7 +774,7 @@ bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E* __r
     if (lid < ndw) dw_tile<E, kDwBufs>(lds, lid, dy, x, ws, nrows, dg, cg, rows_per_split, dw_tiles_m, dw_tiles_n);
   } else {
     const int64_t nb = gridDim.x - ndw_pad;
-    fwd_tile<E, 1, 1, 2, 2, kBwdFwdBufs, SCHED>(lds, xcd_logical_id(b - ndw_pad, nb), dy, wb, dx, nrows, dg, cg, dx_tiles_n,
+    fwd_tile<E, 1, 1, 2, 2, kBwdFwdBufs, kBwdFwdPrefetch, SCHED>(lds, xcd_logical_id(b - ndw_pad, nb), dy, wb, dx, nrows, dg, cg, dx_tiles_n,
                                    nullptr, 0);
   }
 }
@@ -772,7 +861,7 @@ namespace {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 }  // namespace
 
-template <typename E, int FM, int FN, int WM, int WN, int NBUF, int SCHED>
+template <typename E, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED>
 hipError_t launch_fwd_s(const void* in, const void* wp, void* out, int64_t nrows, int kg, int mg,
                         const void* bias, int act, hipStream_t s) {
   constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
@@ -781,26 +870,27 @@ hipError_t launch_fwd_s(const void* in, const void* wp, void* out, int64_t nrows
   const int64_t grid = tiles_m * tiles_n;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_kernel<E, FM, FN, WM, WN, NBUF, SCHED>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, s,
+  hipLaunchKernelGGL((fwd_kernel<E, FM, FN, WM, WN, NBUF, PF, SCHED>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, s,
                      static_cast<const E*>(in), static_cast<const E*>(wp), static_cast<E*>(out), nrows, kg, mg,
                      tiles_n, static_cast<const E*>(bias), act);
   return hipGetLastError();
 }
 
-template <typename E, int FM, int FN, int WM, int WN, int NBUF>
+template <typename E, int FM, int FN, int WM, int WN, int NBUF, int PF>
 hipError_t launch_fwd_t(const void* in, const void* wp, void* out, int64_t nrows, int kg, int mg, const void* bias,
                         int act, hipStream_t s) {
   static const int sched = [] {
     const char* e = getenv("EQLIN_SCHED");
     return e ? atoi(e) : 1;
   }();
-  return sched == 1 ? launch_fwd_s<E, FM, FN, WM, WN, NBUF, 1>(in, wp, out, nrows, kg, mg, bias, act, s)
-                    : launch_fwd_s<E, FM, FN, WM, WN, NBUF, 0>(in, wp, out, nrows, kg, mg, bias, act, s);
+  return sched == 1 ? launch_fwd_s<E, FM, FN, WM, WN, NBUF, PF, 1>(in, wp, out, nrows, kg, mg, bias, act, s)
+                    : launch_fwd_s<E, FM, FN, WM, WN, NBUF, PF, 0>(in, wp, out, nrows, kg, mg, bias, act, s);
 }
 
-// compiled forward tiles, code = FM FN WM WN NBUF (decimal digits)
-#define EQLIN_FWD_TILES(X) \
-  X(11222) X(11122) X(11212) X(21222) X(12222) X(22222) X(21242) X(11241) X(21221) X(12221) X(11221)
+// compiled forward tiles, code = FM FN WM WN NBUF PF (decimal digits)
+#define EQLIN_FWD_TILES(X)                                                                       \
+  X(112221) X(111221) X(112121) X(222221) X(212421) X(112411) X(212211) X(122211) X(112211)      \
+  X(112212) X(112412)
 
 bool fwd_tile_known(int tile) {
   switch (tile) {
@@ -816,11 +906,10 @@ hipError_t launch_forward(int dtype, int tile, const void* in, const void* wp, v
                           int kg, int mg, const void* bias, int act, hipStream_t s) {
 #define EQLIN_CASE(T)                                                                                  \
   case T:                                                                                              \
-    return dtype == 0                                                                                      \
-               ? launch_fwd_t<float, T / 10000, (T / 1000) % 10, (T / 100) % 10, (T / 10) % 10, T % 10>(     \
-                     in, wp, out, nrows, kg, mg, bias, act, s)                                                \
-               : launch_fwd_t<_Float16, T / 10000, (T / 1000) % 10, (T / 100) % 10, (T / 10) % 10, T % 10>(  \
-                     in, wp, out, nrows, kg, mg, bias, act, s);
+    return dtype == 0 ? launch_fwd_t<float, T / 100000, (T / 10000) % 10, (T / 1000) % 10, (T / 100) % 10, \
+                                     (T / 10) % 10, T % 10>(in, wp, out, nrows, kg, mg, bias, act, s)          \
+                      : launch_fwd_t<_Float16, T / 100000, (T / 10000) % 10, (T / 1000) % 10, (T / 100) % 10,  \
+                                     (T / 10) % 10, T % 10>(in, wp, out, nrows, kg, mg, bias, act, s);
   switch (tile) {
     EQLIN_FWD_TILES(EQLIN_CASE)
     default: return hipErrorInvalidValue;

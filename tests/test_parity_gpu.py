@@ -100,8 +100,8 @@ def _forward_case(dt, N, C, D, seed=0):
     return X, w, host(Y)
 
 
-@pytest.mark.parametrize("tile", ["auto", "11222", "11122", "11212", "21222", "12222", "22222", "21242",
-                                  "11241", "21221", "12221", "11221"])
+@pytest.mark.parametrize("tile", ["auto", "112221", "111221", "112121", "222221", "212421", "112411", "212211",
+                                  "122211", "112211", "112212", "112412"])
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 def test_forward_small_shapes_all_tiles(dt, tile, monkeypatch):
     if tile != "auto":
