@@ -1,5 +1,5 @@
-// C ABI of the p4 group-circulant linear layer: argument validation, tile
-// choice and kernel launches.  The contract of every entry point is stated in
+// C ABI of the group-circulant linear layer (cyclic groups of order 4 and 8):
+// argument validation, tile choice and kernel launches.  The contract of every entry point is stated in
 // include/eqlin.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -19,14 +19,18 @@ int elem_bytes(int dtype) { return dtype == EQLIN_F32 ? 4 : 2; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Shape / dtype checks common to every entry point.
+// Shape / dtype checks common to every entry point.  f16 rows of an odd
+// number of 4-value groups would break the 16-byte alignment of the loads.
 int check_shape(int64_t N, int C, int D, int T, int dtype) {
   if (dtype != EQLIN_F32 && dtype != EQLIN_F16) return EQLIN_EINVAL;
-  if (T != 4) return EQLIN_ENOTSUP;
-  if (N < 0 || C <= 0 || D <= 0 || (C % 4) != 0 || (D % 4) != 0) return EQLIN_EINVAL;
-  if (dtype == EQLIN_F16 && (((C / 4) % 2) != 0 || ((D / 4) % 2) != 0)) return EQLIN_ENOTSUP;
+  if (T != 4 && T != 8) return EQLIN_ENOTSUP;
+  if (N < 0 || C <= 0 || D <= 0 || (C % T) != 0 || (D % T) != 0) return EQLIN_EINVAL;
+  if (dtype == EQLIN_F16 && T == 4 && (((C / 4) % 2) != 0 || ((D / 4) % 2) != 0)) return EQLIN_ENOTSUP;
   return EQLIN_OK;
 }
+
+// Launchers of the group of order T (4 or 8, checked by check_shape).
+#define EQLIN_BY_T(T, call) ((T) == 4 ? eqlin::Launch<4>::call : eqlin::Launch<8>::call)
 
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return EQLIN_OK;
@@ -35,23 +39,22 @@ int hip_status(hipError_t e) {
 }
 
 // Prepared planes of one direction: rows x ceil(groups / SG) stage blocks of
-// 256 bytes (4 planes x 64 bytes).
-size_t plane_set_bytes(int rows, int groups, int dtype) {
+// 64 T bytes (T planes x 64 bytes).
+size_t plane_set_bytes(int rows, int groups, int T, int dtype) {
   const int sg = eqlin::stage_groups(dtype);
-  return static_cast<size_t>(rows) * static_cast<size_t>(cdiv(groups, sg)) * 256u;
+  return static_cast<size_t>(rows) * static_cast<size_t>(cdiv(groups, sg)) * 64u * static_cast<size_t>(T);
 }
 
-size_t transpose_offset(int C, int D, int dtype) {
-  return (plane_set_bytes(D / 4, C / 4, dtype) + 255u) & ~size_t(255);
+size_t transpose_offset(int C, int D, int T, int dtype) {
+  return (plane_set_bytes(D / T, C / T, T, dtype) + 255u) & ~size_t(255);
 }
 
 // Buffer loads use 32-bit byte offsets inside one workgroup tile.
 constexpr int64_t kMaxTileBytes = int64_t(1) << 30;
 
-bool fwd_offsets_fit(int in_width, int out_groups, int dtype) {
+bool fwd_offsets_fit(int in_width, int T, int dtype) {
   const int64_t row_bytes = int64_t(in_width) * elem_bytes(dtype);
-  const int64_t wrow_bytes = cdiv(in_width / 4, eqlin::stage_groups(dtype)) * 256;
-  (void)out_groups;
+  const int64_t wrow_bytes = cdiv(in_width / T, eqlin::stage_groups(dtype)) * 64 * T;
   return 256 * row_bytes < kMaxTileBytes && 256 * wrow_bytes < kMaxTileBytes;
 }
 
@@ -61,20 +64,25 @@ struct TileShape {
 };
 // Forward tile candidates (code = FM FN WM WN NBUF PF) with their measured efficiency
 // on the ViT-B / ViT-H layer shapes.
-constexpr TileShape kF32Tiles[] = {{112211, 64, 64, 0.70}, {112221, 64, 64, 0.63}, {111221, 32, 64, 0.52}};
-constexpr TileShape kF16Tiles[] = {{212421, 128, 128, 0.24}, {112211, 64, 64, 0.20}, {111221, 32, 64, 0.13}};
+constexpr TileShape kP4F32Tiles[] = {{112211, 64, 64, 0.70}, {112221, 64, 64, 0.63}, {111221, 32, 64, 0.52}};
+constexpr TileShape kP4F16Tiles[] = {{212421, 128, 128, 0.24}, {112211, 64, 64, 0.20}, {111221, 32, 64, 0.13}};
+constexpr TileShape kC8F32Tiles[] = {{112211, 64, 64, 0.50}, {111221, 32, 64, 0.40}};
+constexpr TileShape kC8F16Tiles[] = {{112211, 64, 64, 0.15}, {111221, 32, 64, 0.10}};
 
 // Forward tile choice: workgroups are spread round-robin over the CUs, so a
 // CU's work is ceil(tiles / CUs) tiles; minimise that work divided by the
 // tile's efficiency.  EQLIN_FWD_TILE overrides (any compiled tile code).
-int choose_fwd_tile(int dtype, int64_t nrows, int mg) {
+int choose_fwd_tile(int T, int dtype, int64_t nrows, int mg) {
   if (const char* env = getenv("EQLIN_FWD_TILE")) {
     const int t = atoi(env);
-    if (eqlin::fwd_tile_known(t)) return t;
+    if (EQLIN_BY_T(T, fwd_tile_known(t))) return t;
   }
-  const TileShape* tiles = dtype == EQLIN_F32 ? kF32Tiles : kF16Tiles;
-  const int ntiles = dtype == EQLIN_F32 ? int(sizeof(kF32Tiles) / sizeof(TileShape))
-                                        : int(sizeof(kF16Tiles) / sizeof(TileShape));
+  const bool f32 = dtype == EQLIN_F32;
+  const TileShape* tiles = T == 4 ? (f32 ? kP4F32Tiles : kP4F16Tiles) : (f32 ? kC8F32Tiles : kC8F16Tiles);
+  const int ntiles = T == 4 ? (f32 ? int(sizeof(kP4F32Tiles) / sizeof(TileShape))
+                                   : int(sizeof(kP4F16Tiles) / sizeof(TileShape)))
+                            : (f32 ? int(sizeof(kC8F32Tiles) / sizeof(TileShape))
+                                   : int(sizeof(kC8F16Tiles) / sizeof(TileShape)));
   int best = tiles[0].code;
   double best_cost = 1e300;
   for (int i = 0; i < ntiles; ++i) {
@@ -107,11 +115,11 @@ struct DwPlan {
   int nsplit;
 };
 
-DwPlan plan_dw(int64_t N, int C, int D, int dtype) {
+DwPlan plan_dw(int64_t N, int C, int D, int T, int dtype) {
   DwPlan p{0, 0};
   if (N <= 0) return p;
   // a few 64 x 64 workgroups fit one CU; use at most two per CU in total
-  const int64_t tiles = cdiv(D / 4, 64) * cdiv(C / 4, 64);
+  const int64_t tiles = cdiv(D / T, 64) * cdiv(C / T, 64);
   const int64_t stage = eqlin::dw_rows_per_stage(dtype);
   const int64_t row_bytes = int64_t(C > D ? C : D) * elem_bytes(dtype);
   int64_t want = (2 * kNumCu) / tiles;
@@ -129,13 +137,13 @@ DwPlan plan_dw(int64_t N, int C, int D, int dtype) {
 
 extern "C" {
 
-int eqlin_version(void) { return 100; }
+int eqlin_version(void) { return 200; }
 
 const char* eqlin_status_str(int status) {
   switch (status) {
     case EQLIN_OK: return "ok";
     case EQLIN_EINVAL: return "invalid argument";
-    case EQLIN_ENOTSUP: return "unsupported configuration (T must be 4; f16 needs even group counts)";
+    case EQLIN_ENOTSUP: return "unsupported configuration (T must be 4 or 8; f16 with T = 4 needs even group counts)";
     case EQLIN_EALIGN: return "data pointer not 16-byte aligned";
     case EQLIN_EWORKSPACE: return "workspace or prepared-weight buffer too small";
     case EQLIN_EHIP: return "HIP runtime error";
@@ -147,12 +155,12 @@ int eqlin_last_hip_error(void) { return g_last_hip_error; }
 
 size_t eqlin_prepared_weight_bytes(int C, int D, int T, int dtype) {
   if (check_shape(0, C, D, T, dtype) != EQLIN_OK) return 0;
-  return transpose_offset(C, D, dtype) + plane_set_bytes(C / 4, D / 4, dtype);
+  return transpose_offset(C, D, T, dtype) + plane_set_bytes(C / T, D / T, T, dtype);
 }
 
 size_t eqlin_prepared_transpose_offset(int C, int D, int T, int dtype) {
   if (check_shape(0, C, D, T, dtype) != EQLIN_OK) return 0;
-  return transpose_offset(C, D, dtype);
+  return transpose_offset(C, D, T, dtype);
 }
 
 int eqlin_prepare_weights(const void* w, int C, int D, int T, int dtype, void* W_hat, size_t W_hat_bytes,
@@ -163,21 +171,13 @@ int eqlin_prepare_weights(const void* w, int C, int D, int T, int dtype, void* W
   if (!aligned16(w) || !aligned16(W_hat)) return EQLIN_EALIGN;
   if (W_hat_bytes < eqlin_prepared_weight_bytes(C, D, T, dtype)) return EQLIN_EWORKSPACE;
   char* base = static_cast<char*>(W_hat);
-  return hip_status(eqlin::launch_prepare(dtype, w, base, base + transpose_offset(C, D, dtype), D / 4, C / 4,
-                                          static_cast<hipStream_t>(stream)));
+  return hip_status(EQLIN_BY_T(T, prepare(dtype, w, base, base + transpose_offset(C, D, T, dtype), D / T, C / T,
+                                          static_cast<hipStream_t>(stream))));
 }
 
 int eqlin_forward(const void* X, int64_t N, int C, int D, int T, const void* W_hat, void* Y, int dtype,
                   void* stream) {
-  int st = check_shape(N, C, D, T, dtype);
-  if (st != EQLIN_OK) return st;
-  if (N == 0) return EQLIN_OK;
-  if (!X || !W_hat || !Y) return EQLIN_EINVAL;
-  if (!aligned16(X) || !aligned16(W_hat) || !aligned16(Y)) return EQLIN_EALIGN;
-  if (!fwd_offsets_fit(C, D / 4, dtype)) return EQLIN_ENOTSUP;
-  const int tile = choose_fwd_tile(dtype, N, D / 4);
-  return hip_status(eqlin::launch_forward(dtype, tile, X, W_hat, Y, N, C / 4, D / 4, nullptr, 0,
-                                          static_cast<hipStream_t>(stream)));
+  return eqlin_forward_ex(X, N, C, D, T, W_hat, nullptr, EQLIN_ACT_NONE, Y, dtype, stream);
 }
 
 int eqlin_forward_ex(const void* X, int64_t N, int C, int D, int T, const void* W_hat, const void* bias, int act,
@@ -189,17 +189,17 @@ int eqlin_forward_ex(const void* X, int64_t N, int C, int D, int T, const void* 
   if (!X || !W_hat || !Y) return EQLIN_EINVAL;
   if (!aligned16(X) || !aligned16(W_hat) || !aligned16(Y)) return EQLIN_EALIGN;
   if (bias && (reinterpret_cast<uintptr_t>(bias) % elem_bytes(dtype)) != 0) return EQLIN_EALIGN;
-  if (!fwd_offsets_fit(C, D / 4, dtype)) return EQLIN_ENOTSUP;
-  const int tile = choose_fwd_tile(dtype, N, D / 4);
-  return hip_status(eqlin::launch_forward(dtype, tile, X, W_hat, Y, N, C / 4, D / 4, bias, act,
-                                          static_cast<hipStream_t>(stream)));
+  if (!fwd_offsets_fit(C, T, dtype)) return EQLIN_ENOTSUP;
+  const int tile = choose_fwd_tile(T, dtype, N, D / T);
+  return hip_status(EQLIN_BY_T(T, forward(dtype, tile, X, W_hat, Y, N, C / T, D / T, bias, act,
+                                          static_cast<hipStream_t>(stream))));
 }
 
 size_t eqlin_backward_workspace_bytes(int64_t N, int C, int D, int T, int dtype) {
   if (check_shape(N, C, D, T, dtype) != EQLIN_OK) return 0;
-  const DwPlan p = plan_dw(N, C, D, dtype);
-  return static_cast<size_t>(p.nsplit) * 4u * static_cast<size_t>(C / 4) * static_cast<size_t>(D / 4) *
-         sizeof(float);
+  const DwPlan p = plan_dw(N, C, D, T, dtype);
+  return static_cast<size_t>(p.nsplit) * static_cast<size_t>(T) * static_cast<size_t>(C / T) *
+         static_cast<size_t>(D / T) * sizeof(float);
 }
 
 int eqlin_backward_dx(const void* dY, int64_t N, int C, int D, int T, const void* W_hat, void* dX, int dtype,
@@ -209,13 +209,13 @@ int eqlin_backward_dx(const void* dY, int64_t N, int C, int D, int T, const void
   if (N == 0) return EQLIN_OK;
   if (!dY || !W_hat || !dX) return EQLIN_EINVAL;
   if (!aligned16(dY) || !aligned16(W_hat) || !aligned16(dX)) return EQLIN_EALIGN;
-  if (!fwd_offsets_fit(D, C / 4, dtype)) return EQLIN_ENOTSUP;
+  if (!fwd_offsets_fit(D, T, dtype)) return EQLIN_ENOTSUP;
   // dX = dY W: the forward kernel with the transposed, conjugated planes
   // (input groups D', output groups C').
-  const char* wb = static_cast<const char*>(W_hat) + transpose_offset(C, D, dtype);
-  const int tile = choose_fwd_tile(dtype, N, C / 4);
-  return hip_status(eqlin::launch_forward(dtype, tile, dY, wb, dX, N, D / 4, C / 4, nullptr, 0,
-                                          static_cast<hipStream_t>(stream)));
+  const char* wb = static_cast<const char*>(W_hat) + transpose_offset(C, D, T, dtype);
+  const int tile = choose_fwd_tile(T, dtype, N, C / T);
+  return hip_status(EQLIN_BY_T(T, forward(dtype, tile, dY, wb, dX, N, D / T, C / T, nullptr, 0,
+                                          static_cast<hipStream_t>(stream))));
 }
 
 int eqlin_backward_dw(const void* dY, const void* X, int64_t N, int C, int D, int T, float* dw, void* workspace,
@@ -227,9 +227,9 @@ int eqlin_backward_dw(const void* dY, const void* X, int64_t N, int C, int D, in
   if (!aligned16(dw)) return EQLIN_EALIGN;
   if (N > 0 && (!aligned16(dY) || !aligned16(X) || !aligned16(workspace))) return EQLIN_EALIGN;
   if (workspace_bytes < eqlin_backward_workspace_bytes(N, C, D, T, dtype)) return EQLIN_EWORKSPACE;
-  const DwPlan p = plan_dw(N, C, D, dtype);
-  return hip_status(eqlin::launch_dw(dtype, dY, X, static_cast<float*>(workspace), dw, N, D / 4, C / 4,
-                                     p.rows_per_split, p.nsplit, static_cast<hipStream_t>(stream)));
+  const DwPlan p = plan_dw(N, C, D, T, dtype);
+  return hip_status(EQLIN_BY_T(T, dw(dtype, dY, X, static_cast<float*>(workspace), dw, N, D / T, C / T,
+                                     p.rows_per_split, p.nsplit, static_cast<hipStream_t>(stream))));
 }
 
 int eqlin_backward(const void* dY, const void* X, int64_t N, int C, int D, int T, const void* W_hat, void* dX,
@@ -241,7 +241,7 @@ int eqlin_backward(const void* dY, const void* X, int64_t N, int C, int D, int T
   if (dX && N > 0) {
     if (!dY || !W_hat) return EQLIN_EINVAL;
     if (!aligned16(dY) || !aligned16(W_hat) || !aligned16(dX)) return EQLIN_EALIGN;
-    if (!fwd_offsets_fit(D, C / 4, dtype)) return EQLIN_ENOTSUP;
+    if (!fwd_offsets_fit(D, T, dtype)) return EQLIN_ENOTSUP;
   }
   if (dw) {
     if (N > 0 && (!dY || !X || !workspace)) return EQLIN_EINVAL;
@@ -251,10 +251,10 @@ int eqlin_backward(const void* dY, const void* X, int64_t N, int C, int D, int T
   }
   if (dX && dw && N > 0 && use_fused_backward()) {
     // one launch for dX and the dw partials (they share dY), then the finalize
-    const DwPlan p = plan_dw(N, C, D, dtype);
-    const char* wb = static_cast<const char*>(W_hat) + transpose_offset(C, D, dtype);
-    return hip_status(eqlin::launch_bwd_fused(dtype, dY, X, wb, dX, static_cast<float*>(workspace), dw, N, D / 4,
-                                              C / 4, p.rows_per_split, p.nsplit, static_cast<hipStream_t>(stream)));
+    const DwPlan p = plan_dw(N, C, D, T, dtype);
+    const char* wb = static_cast<const char*>(W_hat) + transpose_offset(C, D, T, dtype);
+    return hip_status(EQLIN_BY_T(T, bwd_fused(dtype, dY, X, wb, dX, static_cast<float*>(workspace), dw, N, D / T,
+                                              C / T, p.rows_per_split, p.nsplit, static_cast<hipStream_t>(stream))));
   }
   if (dX) {
     st = eqlin_backward_dx(dY, N, C, D, T, W_hat, dX, dtype, stream);

@@ -1,0 +1,1042 @@
+// Device code of the group-circulant (EQ-)linear layer for gfx950 (CDNA4):
+// group transforms, the matrix-core "complex core", the forward / dX tile,
+// the dw split-partial tile, the dw finalize and the weight preparation, all
+// templated on the storage type E (float or _Float16) and the cyclic group
+// size T (4: the p4 rotation group; 8: the cyclic group C8).
+//
+// Method (Flash EQ-Linear technical summary, gist.science 2607.21271):
+//   * "Key insight": the weight is group-circulant, so the layer is a circular
+//     convolution over the group axis combined with a channel contraction.
+//   * "Algorithmic approach", items 1-2: a DFT over the group axis turns each
+//     circulant block into a pointwise product per frequency; for real data
+//     only the non-redundant frequencies are formed.
+//   * "Specialisation for the p4 rotation group": for T = 4 the transforms use
+//     only 0, +-1 and the power-of-two rescales 1/4, 1/2 (adds and subtracts),
+//     and the contraction is six real matrix products: f0 (1), f2 (1) and the
+//     complex f1 (4: Re/Im cross terms).
+//   * "Limitations": the specialisation is to p4; other groups are future
+//     work.  C8 here follows the same route with the general real-signal DFT:
+//     real f0 and f4, complex f1..f3, 2 + 3 * 4 = 14 real products.
+//   * "Implementation": fused dataflow (no intermediate global writes), Fourier
+//     fragments resident in registers / on-chip memory, shape-specialised
+//     tiles on the matrix cores.
+//
+// gfx950 mapping.  Work is expressed as one "complex-structured GEMM":
+//   out_plane[m][n] = sum_k A_plane[m][k] (*) B_plane[n][k]
+// where (*) multiplies the real planes pointwise and the (Re, Im) plane pairs
+// as complex numbers.  Both operands are staged per pipeline stage into LDS as
+// T planes [plane][row][k] with k contiguous in 64-byte rows whose four 16-byte
+// slots are XOR-swizzled (see swz_slot).  Every lane reads 16 bytes per plane
+// per 32x32 fragment: 4 fp32 k-values (four 32x32x2 f32 MFMAs) or 8 f16
+// k-values (one 32x32x16 f16 MFMA).  Waves are 64 wide; each wave owns
+// FM x FN fragments of 32 x 32 for each of the T accumulator planes.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace eqlin {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int kNumXcd = 8;
+// LDS stage buffers of the dw partial tiles and of the dX tiles inside the
+// fused backward (1: smaller LDS, more resident workgroups per CU), and the
+// register prefetch depth of those dX tiles.
+constexpr int kDwBufs = 1;
+constexpr int kBwdFwdBufs = 1;
+constexpr int kBwdFwdPrefetch = 1;
+
+// LDS plane rows are 64 bytes (four 16-byte slots) with no padding; the slot
+// index is XOR-swizzled with bits 2-3 of the row, which keeps both the
+// 4-lanes-per-row stores and the 32-rows-per-wave fragment reads free of bank
+// conflicts on gfx950 (checked with the LDS bank-conflict counter).
+constexpr int kRowBytes = 64;
+__device__ __forceinline__ int swz_slot(int row, int slot) { return slot ^ ((row >> 2) & 3); }
+
+// Group channels whose values one lane holds per 16-byte LDS slot of a plane
+// (= k-values per lane and fragment): 4 fp32, 8 f16.  A pipeline stage covers
+// four slots, i.e. 16 fp32 / 32 f16 group channels along k.
+template <typename E>
+struct Traits {
+  static constexpr int kVals = 16 / (int)sizeof(E);
+  static constexpr int kStageGroups = 4 * kVals;
+};
+
+// How one lane's slot worth of groups (kVals groups of T values) is fetched:
+// as kUnits units of kPiecesPerUnit consecutive 16-byte pieces, each unit
+// holding kGroupsPerUnit whole groups (a group of T fp32 values spans T/4
+// pieces; a 16-byte piece holds 2 f16 groups of 4 or one of 8).
+template <typename E, int T>
+struct Units {
+  static constexpr int kVals = Traits<E>::kVals;
+  static constexpr int kGroupBytes = T * (int)sizeof(E);
+  static constexpr int kGroupsPerUnit = kGroupBytes >= 16 ? 1 : 16 / kGroupBytes;
+  static constexpr int kPiecesPerUnit = kGroupBytes >= 16 ? kGroupBytes / 16 : 1;
+  static constexpr int kUnits = kVals / kGroupsPerUnit;
+  static constexpr int kPieces = kUnits * kPiecesPerUnit;  // = T
+  static_assert(kPieces == T, "a lane's slot of every plane is fed by T pieces");
+};
+
+// Group channel held by slot value s (0 .. kStageGroups-1) of a stage block:
+// lane block q = s / kVals fetches units q, q+4, q+8, ... of the stage, so
+// value v of block q is group kGroupsPerUnit * (q + 4 (v / kGroupsPerUnit)) +
+// v % kGroupsPerUnit.  The prepared weights are stored in this order so that
+// both operands of every product meet at the same k.
+template <typename E, int T>
+__host__ __device__ constexpr int slot_group(int s) {
+  constexpr int V = Traits<E>::kVals, G = Units<E, T>::kGroupsPerUnit;
+  return G * (s / V + 4 * ((s % V) / G)) + (s % V) % G;
+}
+
+// ------------------------------------------------------------------ helpers
+
+__device__ __forceinline__ void dft4(float z0, float z1, float z2, float z3,
+                                     float& f0, float& f2, float& f1r, float& f1i) {
+  const float a = z0 + z2, b = z1 + z3;
+  f0 = a + b;
+  f2 = a - b;
+  f1r = z0 - z2;
+  f1i = z3 - z1;
+}
+
+__device__ __forceinline__ void idft4(float f0, float f2, float f1r, float f1i, float y[4]) {
+  const float s = 0.25f * (f0 + f2), d = 0.25f * (f0 - f2);
+  const float r = 0.5f * f1r, i = 0.5f * f1i;
+  y[0] = s + r;
+  y[1] = d - i;
+  y[2] = s - r;
+  y[3] = d + i;
+}
+
+// ------------------------------------------------------------------ groups
+//
+// A real group signal z[0..T-1] has T real Fourier degrees of freedom (the
+// spectrum F_k = sum_u z_u exp(-2 pi i k u / T) is conjugate symmetric), kept
+// as T planes in the order
+//   F_0, F_{T/2}, Re F_1, Im F_1, ..., Re F_{T/2-1}, Im F_{T/2-1}
+// (for T = 4: F0, F2, Re F1, Im F1).  idft maps any such planes back to the
+// real signal (1/T) sum_k F_k exp(+2 pi i k u / T) with F_{T-k} = conj F_k.
+template <int T>
+struct Grp;
+
+template <>
+struct Grp<4> {
+  static constexpr int kPlanes = 4;
+  static constexpr int kProducts = 6;  // real products per (row, column, k)
+  __device__ __forceinline__ static void dft(const float* z, float* f) {
+    dft4(z[0], z[1], z[2], z[3], f[0], f[1], f[2], f[3]);
+  }
+  __device__ __forceinline__ static void idft(const float* f, float* y) { idft4(f[0], f[1], f[2], f[3], y); }
+};
+
+// C8 by one radix-2 split: the even frequencies are the 4-point DFT of
+// s_u = z_u + z_{u+4}; the odd ones come from a_u = z_u - z_{u+4}, where with
+// c = sqrt(1/2):  F1 = (a0 + c (a1 - a3)) - i (a2 + c (a1 + a3)),
+//                 F3 = (a0 - c (a1 - a3)) + i (a2 - c (a1 + a3)).
+// Inverse: s = 4-point inverse of (F0, F4, F2) and
+//   a0 = (Re F1 + Re F3)/2           a2 = (Im F3 - Im F1)/2
+//   a1 = c/2 ((Re F1 - Im F1) - (Re F3 + Im F3))
+//   a3 = c/2 ((Re F3 - Im F3) - (Re F1 + Im F1))
+//   z_u = (s_u + a_u)/2,  z_{u+4} = (s_u - a_u)/2.
+template <>
+struct Grp<8> {
+  static constexpr int kPlanes = 8;
+  static constexpr int kProducts = 14;
+  static constexpr float kC = 0.70710678118654752f;
+  __device__ __forceinline__ static void dft(const float* z, float* f) {
+    float s[4], a[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      s[u] = z[u] + z[u + 4];
+      a[u] = z[u] - z[u + 4];
+    }
+    dft4(s[0], s[1], s[2], s[3], f[0], f[1], f[4], f[5]);
+    const float p = kC * (a[1] - a[3]), q = kC * (a[1] + a[3]);
+    f[2] = a[0] + p;
+    f[3] = -a[2] - q;
+    f[6] = a[0] - p;
+    f[7] = a[2] - q;
+  }
+  __device__ __forceinline__ static void idft(const float* f, float* y) {
+    float s[4], a[4];
+    idft4(f[0], f[1], f[4], f[5], s);
+    a[0] = 0.5f * (f[2] + f[6]);
+    a[2] = 0.5f * (f[7] - f[3]);
+    a[1] = (0.5f * kC) * ((f[2] - f[3]) - (f[6] + f[7]));
+    a[3] = (0.5f * kC) * ((f[6] - f[7]) - (f[2] + f[3]));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      y[u] = 0.5f * (s[u] + a[u]);
+      y[u + 4] = 0.5f * (s[u] - a[u]);
+    }
+  }
+};
+
+__host__ __device__ constexpr bool imag_plane(int p) { return p >= 2 && (p & 1); }
+
+// erf(z) by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26: for z >= 0, erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5)
+// exp(-z^2) with t = 1 / (1 + p z); |error| <= 1.5e-7.  Odd extension for
+// z < 0.  exp(-z^2) uses the hardware base-2 exponential.
+__device__ __forceinline__ float erf_as7126(float z) {
+  const float a = fabsf(z);
+  const float t = __frcp_rn(1.0f + 0.3275911f * a);
+  const float poly = t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+  const float e = __builtin_amdgcn_exp2f(-a * a * 1.4426950408889634f);
+  const float r = 1.0f - poly * e;
+  return copysignf(r, z);
+}
+
+// GELU(x) = x * Phi(x) = x/2 * (1 + erf(x / sqrt(2)))
+__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erf_as7126(x * 0.70710678118654752f)); }
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Buffer resource over [base, base + bytes): raw buffer loads at offsets past
+// the range return zeros.  Ranges are clamped below 2^31 so that kOob is
+// always out of range.
+constexpr uint32_t kOob = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes > 0x7ffffff0ull ? 0x7ffffff0u : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Blocks are dispatched round-robin over the 8 XCDs.  Renumber so that
+// consecutive logical tile ids land on the same XCD (and share its L2).
+__device__ __forceinline__ int64_t xcd_logical_id(int64_t bid, int64_t nblocks) {
+  const int64_t xcd = bid % kNumXcd;
+  const int64_t per = nblocks / kNumXcd, rem = nblocks % kNumXcd;
+  return xcd * per + (xcd < rem ? xcd : rem) + bid / kNumXcd;
+}
+
+// Stores the T outputs of one group (float32 results) in the storage type.
+template <typename E, int T>
+__device__ __forceinline__ void store_group(E* dst, const float* y) {
+  if constexpr (sizeof(E) == 4) {
+#pragma unroll
+    for (int i = 0; i < T / 4; ++i)
+      st16(dst + 4 * i, __builtin_bit_cast(u32x4, f32x4{y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]}));
+  } else if constexpr (T == 4) {
+    const f16x4 h = {(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]};
+    *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, h);
+  } else {
+#pragma unroll
+    for (int i = 0; i < T / 8; ++i) {
+      f16x8 h;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = (_Float16)y[8 * i + e];
+      st16(dst + 8 * i, __builtin_bit_cast(u32x4, h));
+    }
+  }
+}
+
+// ------------------------------------------------------ input transforms
+//
+// T 16-byte pieces fetched in unit order (see Units) hold kVals whole groups
+// one after another: group v occupies values v*T .. v*T+T-1.  The transform
+// writes the T plane vectors pl[p] whose value v is plane p of group v.
+// kConj negates the imaginary planes (conjugate spectrum).
+
+// f16, T = 4: group DFT of the two groups of one 16-byte piece (registers
+// z01 = (z0, z1), z23 = (z2, z3) of group 0 and z45 / z67 of group 1), written
+// as packed f16 plane values: p0 = (F0_g0, F0_g1), p2 = (F2_g0, F2_g1),
+// p1r = (Re F1_g0, Re F1_g1), p1i = (+-Im F1_g0, +-Im F1_g1).  The mixed
+// precision FMA reads f16 halves directly, computes in f32 and rounds the
+// result once (nearest-even) into the low or high half of the destination:
+//   a = z0 + z2, b = z1 + z3 (f32);  F0 = a + b;  F2 = a - b;
+//   Re F1 = z0 - z2;  Im F1 = z3 - z1 (negated when kConj).
+template <bool kConj>
+__device__ __forceinline__ void dft4_f16_pair(uint32_t z01, uint32_t z23, uint32_t z45, uint32_t z67,
+                                              uint32_t& p0, uint32_t& p2, uint32_t& p1r, uint32_t& p1i) {
+  float a0, b0, a1, b1;
+  asm volatile(
+      "v_fma_mix_f32 %0, %4, 1.0, %5 op_sel:[0,0,0] op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mix_f32 %1, %4, 1.0, %5 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mix_f32 %2, %6, 1.0, %7 op_sel:[0,0,0] op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mix_f32 %3, %6, 1.0, %7 op_sel:[1,0,1] op_sel_hi:[1,0,1]"
+      : "=&v"(a0), "=&v"(b0), "=&v"(a1), "=&v"(b1)
+      : "v"(z01), "v"(z23), "v"(z45), "v"(z67));
+  asm volatile(
+      "v_fma_mixlo_f16 %0, %2, 1.0, %3 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixhi_f16 %0, %4, 1.0, %5 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixlo_f16 %1, %2, 1.0, -%3 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixhi_f16 %1, %4, 1.0, -%5 op_sel_hi:[0,0,0]"
+      : "=&v"(p0), "=&v"(p2)
+      : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
+  asm volatile(
+      "v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel:[0,0,0] op_sel_hi:[1,0,1]\n\t"
+      "v_fma_mixhi_f16 %0, %3, 1.0, -%4 op_sel:[0,0,0] op_sel_hi:[1,0,1]"
+      : "=&v"(p1r)
+      : "v"(z01), "v"(z23), "v"(z45), "v"(z67));
+  if constexpr (!kConj) {
+    asm volatile(
+        "v_fma_mixlo_f16 %0, %2, 1.0, -%1 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\t"
+        "v_fma_mixhi_f16 %0, %4, 1.0, -%3 op_sel:[1,0,1] op_sel_hi:[1,0,1]"
+        : "=&v"(p1i)
+        : "v"(z01), "v"(z23), "v"(z45), "v"(z67));
+  } else {
+    asm volatile(
+        "v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\t"
+        "v_fma_mixhi_f16 %0, %3, 1.0, -%4 op_sel:[1,0,1] op_sel_hi:[1,0,1]"
+        : "=&v"(p1i)
+        : "v"(z01), "v"(z23), "v"(z45), "v"(z67));
+  }
+}
+
+template <typename E, int T, bool kConj>
+__device__ __forceinline__ void pieces_to_planes(const u32x4 (&pc)[T], u32x4 (&pl)[T]) {
+  constexpr int V = Traits<E>::kVals;
+  if constexpr (sizeof(E) == 2 && T == 4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t p0, p2, p1r, p1i;
+      dft4_f16_pair<kConj>(pc[j][0], pc[j][1], pc[j][2], pc[j][3], p0, p2, p1r, p1i);
+      pl[0][j] = p0;
+      pl[1][j] = p2;
+      pl[2][j] = p1r;
+      pl[3][j] = p1i;
+    }
+  } else {
+    // unpack whole vectors, then index (a bit-cast of one vector element
+    // would reinterpret the vector's first element)
+    float z[V * T];
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+      if constexpr (sizeof(E) == 4) {
+        const f32x4 x = __builtin_bit_cast(f32x4, pc[j]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[4 * j + e] = x[e];
+      } else {
+        const f16x8 x = __builtin_bit_cast(f16x8, pc[j]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[8 * j + e] = (float)x[e];
+      }
+    }
+    float f[V][T];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      Grp<T>::dft(&z[v * T], f[v]);
+      if constexpr (kConj) {
+#pragma unroll
+        for (int p = 0; p < T; ++p)
+          if (imag_plane(p)) f[v][p] = -f[v][p];
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < T; ++p) {
+      if constexpr (sizeof(E) == 4) {
+        pl[p] = __builtin_bit_cast(u32x4, f32x4{f[0][p], f[1][p], f[2][p], f[3][p]});
+      } else {
+        f16x8 o;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) o[v] = (_Float16)f[v][p];
+        pl[p] = __builtin_bit_cast(u32x4, o);
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------- MFMA complex core
+//
+// One 16-byte slot per operand plane and fragment: real planes
+//   acc[0] += A0 B0,  acc[1] += A1 B1,
+// and for every (Re, Im) pair (r, i = r + 1):
+//   acc[r] += Ar Br - Ai Bi,   acc[i] += Ar Bi + Ai Br.
+// The first product of every accumulator is issued before any second one, so
+// that dependent matrix-core operations on one accumulator are far apart.
+template <typename E, int T, int FM, int FN>
+struct Core;
+
+template <int T, int FM, int FN>
+struct Core<float, T, FM, FN> {
+  __device__ __forceinline__ static void mma(f32x16 (&acc)[T][FM][FN], const u32x4 (&a)[T][FM],
+                                             const u32x4 (&b)[T][FN]) {
+    f32x4 af[T][FM], bf[T][FN];
+#pragma unroll
+    for (int p = 0; p < T; ++p) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) af[p][fm] = __builtin_bit_cast(f32x4, a[p][fm]);
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) bf[p][fn] = __builtin_bit_cast(f32x4, b[p][fn]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          // first products: 0, (r1, i1 interleaved with 1), r2, i2, ...
+          acc[0][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[0][fm][j], bf[0][fn][j], acc[0][fm][fn], 0, 0, 0);
+          acc[2][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[2][fm][j], bf[2][fn][j], acc[2][fm][fn], 0, 0, 0);
+          acc[1][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[1][fm][j], bf[1][fn][j], acc[1][fm][fn], 0, 0, 0);
+          acc[3][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[2][fm][j], bf[3][fn][j], acc[3][fm][fn], 0, 0, 0);
+#pragma unroll
+          for (int r = 4; r < T; r += 2) {
+            acc[r][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[r][fm][j], bf[r][fn][j], acc[r][fm][fn], 0, 0, 0);
+            acc[r + 1][fm][fn] =
+                __builtin_amdgcn_mfma_f32_32x32x2f32(af[r][fm][j], bf[r + 1][fn][j], acc[r + 1][fm][fn], 0, 0, 0);
+          }
+#pragma unroll
+          for (int r = 2; r < T; r += 2) {
+            acc[r][fm][fn] =
+                __builtin_amdgcn_mfma_f32_32x32x2f32(-af[r + 1][fm][j], bf[r + 1][fn][j], acc[r][fm][fn], 0, 0, 0);
+            acc[r + 1][fm][fn] =
+                __builtin_amdgcn_mfma_f32_32x32x2f32(af[r + 1][fm][j], bf[r][fn][j], acc[r + 1][fm][fn], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+};
+
+template <int T, int FM, int FN>
+struct Core<_Float16, T, FM, FN> {
+  __device__ __forceinline__ static void mma(f32x16 (&acc)[T][FM][FN], const u32x4 (&a)[T][FM],
+                                             const u32x4 (&b)[T][FN]) {
+    constexpr u32x4 kSign = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      f16x8 av[T], nai[T];
+#pragma unroll
+      for (int p = 0; p < T; ++p) {
+        av[p] = __builtin_bit_cast(f16x8, a[p][fm]);
+        if (imag_plane(p)) nai[p] = __builtin_bit_cast(f16x8, a[p][fm] ^ kSign);
+      }
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        f16x8 bv[T];
+#pragma unroll
+        for (int p = 0; p < T; ++p) bv[p] = __builtin_bit_cast(f16x8, b[p][fn]);
+        acc[0][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[0], bv[0], acc[0][fm][fn], 0, 0, 0);
+        acc[2][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[2], bv[2], acc[2][fm][fn], 0, 0, 0);
+        acc[1][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[1], bv[1], acc[1][fm][fn], 0, 0, 0);
+        acc[3][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[2], bv[3], acc[3][fm][fn], 0, 0, 0);
+#pragma unroll
+        for (int r = 4; r < T; r += 2) {
+          acc[r][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[r], bv[r], acc[r][fm][fn], 0, 0, 0);
+          acc[r + 1][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[r], bv[r + 1], acc[r + 1][fm][fn], 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 2; r < T; r += 2) {
+          acc[r][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(nai[r + 1], bv[r + 1], acc[r][fm][fn], 0, 0, 0);
+          acc[r + 1][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[r + 1], bv[r], acc[r + 1][fm][fn], 0, 0, 0);
+        }
+      }
+    }
+  }
+};
+
+// Reads this lane's 16-byte operand slot of one chunk from every LDS plane
+// and runs the complex core.  a_lds / b_lds point at the lane's slot in plane
+// 0 of its first fragment row; plane p is p * a_plane further, fragment fm
+// 32 rows further.
+template <typename E, int T, int FM, int FN>
+__device__ __forceinline__ void mma_chunk(f32x16 (&acc)[T][FM][FN], const char* a_lds, int a_plane,
+                                          const char* b_lds, int b_plane, int stride) {
+  u32x4 a[T][FM], b[T][FN];
+#pragma unroll
+  for (int p = 0; p < T; ++p) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) a[p][fm] = ld16(a_lds + p * a_plane + fm * 32 * stride);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) b[p][fn] = ld16(b_lds + p * b_plane + fn * 32 * stride);
+  }
+  Core<E, T, FM, FN>::mma(acc, a, b);
+}
+
+// Instruction interleaving for one pipeline stage of fwd_kernel: spread the
+// operand reads of the second chunk, the global loads of a later stage and
+// the next stage's transform and LDS writes between the MFMAs, so that one
+// wave keeps its matrix core busy while it prepares the next stage.
+// Masks: 0x008 MFMA, 0x100 DS read, 0x200 DS write, 0x020 VMEM read, 0x002 VALU.
+template <typename E, int T, int FM, int FN, int PA, int PB>
+__device__ __forceinline__ void interleave_schedule() {
+  constexpr int kMfma = (sizeof(E) == 4 ? 4 : 1) * Grp<T>::kProducts * FM * FN * 2;
+  constexpr int kDsRead = 2 * T * (FM + FN);
+  constexpr int kVmem = T * (PA + PB);
+  constexpr int kDsWrite = T * (PA + PB);
+  constexpr int kHalf = kDsRead / 2;
+  __builtin_amdgcn_sched_group_barrier(0x100, kHalf, 0);
+#pragma unroll
+  for (int i = 0; i < kMfma; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i < kHalf) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (i >= kMfma / 4 && i < kMfma / 4 + kVmem) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    if (i >= kMfma / 2) {
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      if ((i - kMfma / 2) % ((kMfma / 2 + kDsWrite - 1) / kDsWrite) == 0) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    }
+  }
+}
+
+// ============================================================ forward / dX
+//
+// out[n][T m + t] = IDFT_t( sum_k Ahat[n][k] (*) Bhat[m][k] )
+// A = in [nrows][T kg] (raw groups, transformed on the fly),
+// B = prepared spectra in stage blocks (see prepare_kernel), out [nrows][T mg].
+// A stage covers 64 bytes of every plane row: SG = 16 fp32 or 32 f16 groups
+// along k.  Thread t owns row t / 4 (+ NT/4 per pass) and 16-byte slot block
+// q = t % 4 of that row: it loads the units q + 4i of the stage window
+// (coalesced), transforms them and writes the contiguous LDS block q of each
+// plane; the prepared weights are stored in that same slot order, so their
+// 16-byte pieces are copied to LDS unchanged.  Global loads are buffer loads:
+// addresses past the end of the tile's range (rows >= nrows) or flagged out
+// of range (groups >= kg) return zeros without branches.
+template <typename E, int T, int FM, int FN, int WM, int WN, int NBUF>
+constexpr int fwd_lds_bytes() {
+  return NBUF * T * (32 * FM * WM + 32 * FN * WN) * kRowBytes;
+}
+
+// One forward (or dX) tile: workgroup-level logical tile id `lid`.  NBUF = 2
+// double-buffers the LDS stages (one barrier per stage); NBUF = 1 halves the
+// LDS footprint (two barriers per stage) so that more workgroups fit a CU.
+// PF (1 or 2) is the number of stages whose global loads are in flight in
+// registers ahead of the stage being transformed into LDS.
+template <typename E, int T, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED>
+__device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __restrict__ in,
+                                         const E* __restrict__ wp, E* __restrict__ out, int64_t nrows, int kg,
+                                         int mg, int tiles_n, const E* __restrict__ bias, int act) {
+  using U = Units<E, T>;
+  constexpr int NT = 64 * WM * WN;
+  constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
+  constexpr int SG = Traits<E>::kStageGroups;
+  constexpr int STRIDE = kRowBytes;
+  constexpr int A_PLANE = BM * STRIDE, B_PLANE = BN * STRIDE;
+  constexpr int BUF = T * (A_PLANE + B_PLANE);
+  constexpr int BLOCK = T * kRowBytes;      // bytes of one prepared stage block
+  constexpr int RPP = NT / 4;               // tile rows covered per load pass
+  constexpr int PA = (BM + RPP - 1) / RPP, PB = (BN + RPP - 1) / RPP;
+  static_assert(NBUF * BUF == fwd_lds_bytes<E, T, FM, FN, WM, WN, NBUF>(), "LDS size");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row0 = (lid / tiles_n) * BM;
+  const int col0 = (int)(lid % tiles_n) * BN;
+  const int ksteps = (kg + SG - 1) / SG;
+
+  const uint32_t row_bytes = (uint32_t)kg * (uint32_t)(T * sizeof(E));
+  const __amdgpu_buffer_rsrc_t a_src =
+      make_rsrc(in + row0 * T * (int64_t)kg, (uint64_t)(nrows - row0) * row_bytes);
+  const __amdgpu_buffer_rsrc_t b_src =
+      make_rsrc(wp + (int64_t)col0 * ksteps * SG * T, (uint64_t)(mg - col0) * (uint64_t)ksteps * BLOCK);
+
+  const int q = tid & 3, rl = tid >> 2;
+  u32x4 ra[PF][PA][T], rb[PF][PB][T];   // register ring of PF stages of loads
+  auto load = [&](int ks, auto slot_c) {
+    constexpr int sl = decltype(slot_c)::value;
+#pragma unroll
+    for (int ps = 0; ps < PA; ++ps) {
+      const uint32_t r = (uint32_t)(ps * RPP + rl);
+#pragma unroll
+      for (int i = 0; i < U::kUnits; ++i) {
+        const int g = ks * SG + (q + 4 * i) * U::kGroupsPerUnit;
+#pragma unroll
+        for (int h = 0; h < U::kPiecesPerUnit; ++h) {
+          const uint32_t off = g < kg ? r * row_bytes + (uint32_t)g * (uint32_t)(T * sizeof(E)) + 16u * h : kOob;
+          ra[sl][ps][i * U::kPiecesPerUnit + h] = bload16(a_src, off);
+        }
+      }
+    }
+#pragma unroll
+    for (int ps = 0; ps < PB; ++ps) {
+      const uint32_t m = (uint32_t)(ps * RPP + rl);
+#pragma unroll
+      for (int p = 0; p < T; ++p)
+        rb[sl][ps][p] =
+            bload16(b_src, ks < ksteps ? (m * (uint32_t)ksteps + (uint32_t)ks) * BLOCK + p * 64 + q * 16 : kOob);
+    }
+  };
+  auto store = [&](char* buf, auto slot_c) {
+    constexpr int sl = decltype(slot_c)::value;
+#pragma unroll
+    for (int ps = 0; ps < PA; ++ps) {
+      const int r = ps * RPP + rl;
+      if (BM % RPP == 0 || r < BM) {
+        u32x4 pl[T];
+        pieces_to_planes<E, T, false>(ra[sl][ps], pl);
+#pragma unroll
+        for (int p = 0; p < T; ++p) st16(buf + p * A_PLANE + r * STRIDE + swz_slot(r, q) * 16, pl[p]);
+      }
+    }
+#pragma unroll
+    for (int ps = 0; ps < PB; ++ps) {
+      const int m = ps * RPP + rl;
+      if (BN % RPP == 0 || m < BN) {
+#pragma unroll
+        for (int p = 0; p < T; ++p)
+          st16(buf + T * A_PLANE + p * B_PLANE + m * STRIDE + swz_slot(m, q) * 16, rb[sl][ps][p]);
+      }
+    }
+  };
+
+  f32x16 acc[T][FM][FN];
+#pragma unroll
+  for (int p = 0; p < T; ++p)
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) acc[p][fm][fn] = f32x16{};
+
+  const int wr = wave / WN, wc = wave % WN;
+  const int li = lane & 31, lh = lane >> 5;
+  // fragment rows differ from li by multiples of 32, so the swizzle of every
+  // row this lane reads is that of li
+  const int a_frag = (wr * 32 * FM + li) * STRIDE;
+  const int b_frag = T * A_PLANE + (wc * 32 * FN + li) * STRIDE;
+  const int c0 = swz_slot(li, lh) * 16, c1 = swz_slot(li, 2 + lh) * 16;
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, PF - 1>;
+  // One pipeline step: multiply stage ks (LDS buffer of ks), then transform
+  // the registers of stage ks + 1 into the other (or, single-buffered, the
+  // same) buffer and issue the loads of stage ks + 1 + PF into the slot just
+  // freed.  Past the last stage the loads read zeros (out of range) and the
+  // stores fill an idle buffer, so the body is one basic block in which the
+  // scheduler can interleave MFMAs with the transform, LDS writes and loads.
+  auto step = [&](int ks, auto slot_next) {
+    char* cur = lds + (NBUF == 2 ? (ks & 1) * BUF : 0);
+    mma_chunk<E, T, FM, FN>(acc, cur + a_frag + c0, A_PLANE, cur + b_frag + c0, B_PLANE, STRIDE);
+    mma_chunk<E, T, FM, FN>(acc, cur + a_frag + c1, A_PLANE, cur + b_frag + c1, B_PLANE, STRIDE);
+    if constexpr (NBUF == 1) __syncthreads();   // every wave is done reading the only buffer
+    store(lds + (NBUF == 2 ? ((ks + 1) & 1) * BUF : 0), slot_next);
+    load(ks + 1 + PF, slot_next);
+    if constexpr (SCHED == 1 && NBUF == 2) interleave_schedule<E, T, FM, FN, PA, PB>();
+    __syncthreads();
+  };
+
+  load(0, S0{});
+  store(lds, S0{});
+  if constexpr (PF == 1) {
+    load(1, S0{});
+    __syncthreads();
+    for (int ks = 0; ks < ksteps; ++ks) step(ks, S0{});
+  } else {
+    // ring: stage s lives in slot (s + 1) % 2 once stage 0 has been stored
+    load(1, S1{});
+    load(2, S0{});
+    __syncthreads();
+    for (int ks = 0; ks < ksteps; ks += 2) {
+      step(ks, S1{});
+      if (ks + 1 >= ksteps) break;
+      step(ks + 1, S0{});
+    }
+  }
+
+  // epilogue: inverse group DFT in registers, optional group-invariant bias
+  // and GELU, one vector store per (row, group)
+  const int64_t out_ld = T * (int64_t)mg;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int m = col0 + wc * 32 * FN + fn * 32 + li;
+      const float bm = (bias != nullptr && m < mg) ? (float)bias[m] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = row0 + wr * 32 * FM + fm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        if (row < nrows && m < mg) {
+          float f[T], y[T];
+#pragma unroll
+          for (int p = 0; p < T; ++p) f[p] = acc[p][fm][fn][r];
+          Grp<T>::idft(f, y);
+          if (bias != nullptr) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) y[t] += bm;
+          }
+          if (act == 1) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) y[t] = gelu_erf(y[t]);
+          }
+          store_group<E, T>(out + row * out_ld + T * (int64_t)m, y);
+        }
+      }
+    }
+  }
+}
+
+// Two waves per SIMD (256 registers per lane) unless a wave holds 16+
+// accumulator fragments (planes x FM x FN) or, for f16 C8, the operands with
+// their negated imaginary planes would not fit besides the eight accumulators.
+template <typename E, int T, int FM, int FN>
+constexpr int fwd_waves_per_simd() {
+  return (T * FM * FN >= 16 || (T == 8 && sizeof(E) == 2)) ? 1 : 2;
+}
+
+template <typename E, int T, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED>
+__global__ void __launch_bounds__(64 * WM * WN, (fwd_waves_per_simd<E, T, FM, FN>()))
+fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ out,
+           int64_t nrows, int kg, int mg, int tiles_n, const E* __restrict__ bias, int act) {
+  __shared__ __attribute__((aligned(16))) char lds[fwd_lds_bytes<E, T, FM, FN, WM, WN, NBUF>()];
+  fwd_tile<E, T, FM, FN, WM, WN, NBUF, PF, SCHED>(lds, xcd_logical_id(blockIdx.x, gridDim.x), in, wp, out, nrows,
+                                                  kg, mg, tiles_n, bias, act);
+}
+
+// ============================================================ dw partials
+//
+// P_k[m][n] = sum_rows G_k[row][m] conj(Xhat_k[row][n])   (m = d', n = c')
+// over the rows of one split; the T planes are written to
+// ws[split][plane][mg][ng] (float32).  Tiles 64 x 64, one 32 x 32 fragment
+// per wave and plane.  The k axis is the row axis: thread (unit column pc,
+// row block rq) loads KV consecutive rows of one unit (kGroupsPerUnit groups),
+// transforms them and writes, per group and plane, the KV rows as one
+// contiguous LDS run.  A stage is 64 bytes of every plane row (16 fp32 / 32
+// f16 rows); LDS is single- or double-buffered as in fwd_kernel.
+template <int T, int NBUF>
+constexpr int dw_lds_bytes() {
+  return NBUF * 2 * T * 64 * kRowBytes;
+}
+
+template <typename E, int T, int NBUF>
+__device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restrict__ dy, const E* __restrict__ x,
+                                        float* __restrict__ ws, int64_t nrows, int mg, int ng,
+                                        int64_t rows_per_split, int tiles_m, int tiles_n) {
+  using U = Units<E, T>;
+  constexpr int GPU = U::kGroupsPerUnit, PPU = U::kPiecesPerUnit;
+  constexpr int PR = 64 / GPU;                     // units per tile row (64 groups)
+  constexpr int RB = kThreads / PR;                // row blocks per stage
+  constexpr int SR = 64 / (int)sizeof(E);          // rows per stage: 16 (fp32) / 32 (f16)
+  constexpr int KV = SR / RB;                      // rows per thread per stage
+  constexpr int RUN = KV * (int)sizeof(E);         // LDS bytes per (group, plane) per thread
+  constexpr int STRIDE = kRowBytes;
+  constexpr int PLANE = 64 * STRIDE;
+  constexpr int BUF = 2 * T * PLANE;
+  static_assert(RB * KV == SR && (RUN == 8 || RUN == 16), "stage shape");
+  static_assert(NBUF * BUF == dw_lds_bytes<T, NBUF>(), "LDS size");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ntiles = tiles_m * tiles_n;
+  const int64_t split = lid / ntiles;
+  const int tile = (int)(lid % ntiles);
+  const int m0 = (tile / tiles_n) * 64, n0 = (tile % tiles_n) * 64;
+  const int64_t rbeg = split * rows_per_split;
+  const int64_t rend = (rbeg + rows_per_split < nrows) ? rbeg + rows_per_split : nrows;
+  const int nstages = (int)((rend - rbeg + SR - 1) / SR);
+
+  const uint32_t a_row = (uint32_t)mg * (uint32_t)(T * sizeof(E));
+  const uint32_t b_row = (uint32_t)ng * (uint32_t)(T * sizeof(E));
+  const __amdgpu_buffer_rsrc_t a_src = make_rsrc(dy + rbeg * T * (int64_t)mg, (uint64_t)(rend - rbeg) * a_row);
+  const __amdgpu_buffer_rsrc_t b_src = make_rsrc(x + rbeg * T * (int64_t)ng, (uint64_t)(rend - rbeg) * b_row);
+
+  const int pc = tid % PR, rq = tid / PR;
+  const int ga = m0 + pc * GPU, gb = n0 + pc * GPU;
+  const bool a_ok = ga < mg, b_ok = gb < ng;
+  const uint32_t a_col = (uint32_t)ga * (uint32_t)(T * sizeof(E));
+  const uint32_t b_col = (uint32_t)gb * (uint32_t)(T * sizeof(E));
+
+  u32x4 ra[KV][PPU], rb[KV][PPU];
+  auto load = [&](int st) {
+#pragma unroll
+    for (int v = 0; v < KV; ++v) {
+      const uint32_t row = (uint32_t)(st * SR + rq * KV + v);
+#pragma unroll
+      for (int h = 0; h < PPU; ++h) {
+        ra[v][h] = bload16(a_src, a_ok ? row * a_row + a_col + 16u * h : kOob);
+        rb[v][h] = bload16(b_src, b_ok ? row * b_row + b_col + 16u * h : kOob);
+      }
+    }
+  };
+  // transform one operand's KV rows and write the (group, plane) runs
+  auto put = [&](char* plane0, const u32x4 (&r)[KV][PPU], auto conj_c) {
+    constexpr bool kConj = decltype(conj_c)::value;
+    float f[KV][GPU][T];
+#pragma unroll
+    for (int v = 0; v < KV; ++v) {
+      float z[GPU * T];
+#pragma unroll
+      for (int h = 0; h < PPU; ++h) {
+        if constexpr (sizeof(E) == 4) {
+          const f32x4 xv = __builtin_bit_cast(f32x4, r[v][h]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[4 * h + e] = xv[e];
+        } else {
+          const f16x8 xv = __builtin_bit_cast(f16x8, r[v][h]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) z[8 * h + e] = (float)xv[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < GPU; ++e) {
+        Grp<T>::dft(&z[e * T], f[v][e]);
+        if constexpr (kConj) {
+#pragma unroll
+          for (int p = 0; p < T; ++p)
+            if (imag_plane(p)) f[v][e][p] = -f[v][e][p];
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < GPU; ++e) {
+      const int row = pc * GPU + e;
+      const int kb = rq * RUN;
+      const int off = row * STRIDE + swz_slot(row, kb >> 4) * 16 + (kb & 15);
+#pragma unroll
+      for (int p = 0; p < T; ++p) {
+        if constexpr (sizeof(E) == 4) {
+          st16(plane0 + p * PLANE + off, __builtin_bit_cast(u32x4, f32x4{f[0][e][p], f[1][e][p], f[2][e][p], f[3][e][p]}));
+        } else if constexpr (KV == 4) {
+          const f16x4 hv = {(_Float16)f[0][e][p], (_Float16)f[1][e][p], (_Float16)f[2][e][p], (_Float16)f[3][e][p]};
+          *reinterpret_cast<u32x2*>(plane0 + p * PLANE + off) = __builtin_bit_cast(u32x2, hv);
+        } else {
+          f16x8 hv;
+#pragma unroll
+          for (int v = 0; v < 8; ++v) hv[v] = (_Float16)f[v][e][p];
+          st16(plane0 + p * PLANE + off, __builtin_bit_cast(u32x4, hv));
+        }
+      }
+    }
+  };
+  auto store = [&](char* buf) {
+    put(buf, ra, std::false_type{});
+    put(buf + T * PLANE, rb, std::true_type{});
+  };
+
+  f32x16 acc[T][1][1];
+#pragma unroll
+  for (int p = 0; p < T; ++p) acc[p][0][0] = f32x16{};
+
+  const int wr = wave >> 1, wc = wave & 1;
+  const int li = lane & 31, lh = lane >> 5;
+  const int a_frag = (wr * 32 + li) * STRIDE;
+  const int b_frag = T * PLANE + (wc * 32 + li) * STRIDE;
+  const int c0 = swz_slot(li, lh) * 16, c1 = swz_slot(li, 2 + lh) * 16;
+
+  if (nstages > 0) {
+    load(0);
+    store(lds);
+    if (nstages > 1) load(1);
+    __syncthreads();
+  }
+  for (int st = 0; st < nstages; ++st) {
+    char* cur = lds + (NBUF == 2 ? (st & 1) * BUF : 0);
+    mma_chunk<E, T, 1, 1>(acc, cur + a_frag + c0, PLANE, cur + b_frag + c0, PLANE, STRIDE);
+    mma_chunk<E, T, 1, 1>(acc, cur + a_frag + c1, PLANE, cur + b_frag + c1, PLANE, STRIDE);
+    if (st + 1 < nstages) {
+      if constexpr (NBUF == 1) __syncthreads();   // every wave is done reading the only buffer
+      store(lds + (NBUF == 2 ? ((st + 1) & 1) * BUF : 0));
+      if (st + 2 < nstages) load(st + 2);
+    }
+    __syncthreads();
+  }
+
+  const int64_t plane_elems = (int64_t)mg * ng;
+  float* dst = ws + split * T * plane_elems;
+  const int n = n0 + wc * 32 + li;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = m0 + wr * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+    if (m < mg && n < ng) {
+#pragma unroll
+      for (int p = 0; p < T; ++p) dst[p * plane_elems + (int64_t)m * ng + n] = acc[p][0][0][r];
+    }
+  }
+}
+
+// C8 tiles hold eight 32 x 32 accumulators per wave next to the operands
+// and the load ring: one wave per SIMD (512 registers) avoids spills.
+template <int T>
+constexpr int bwd_waves_per_simd() {
+  return T == 4 ? 2 : 1;
+}
+
+template <typename E, int T>
+__global__ void __launch_bounds__(kThreads, bwd_waves_per_simd<T>())
+dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __restrict__ ws,
+                  int64_t nrows, int mg, int ng, int64_t rows_per_split, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) char lds[dw_lds_bytes<T, kDwBufs>()];
+  dw_tile<E, T, kDwBufs>(lds, xcd_logical_id(blockIdx.x, gridDim.x), dy, x, ws, nrows, mg, ng, rows_per_split,
+                         tiles_m, tiles_n);
+}
+
+// Backward in one launch: the first ndw_pad workgroups are dw split partials,
+// the rest are dX tiles (the forward structure on the transpose spectra).
+// Both roles read dY; running them in one grid lets the dispatcher fill the
+// tail of one role with work of the other.  ndw_pad is a multiple of 8, so
+// each role keeps its own XCD-aware numbering.
+template <typename E, int T, int SCHED>
+__global__ void __launch_bounds__(kThreads, bwd_waves_per_simd<T>())
+bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E* __restrict__ wb,
+                 E* __restrict__ dx, float* __restrict__ ws, int64_t nrows, int dg, int cg,
+                 int64_t rows_per_split, int dw_tiles_m, int dw_tiles_n, int64_t ndw, int64_t ndw_pad,
+                 int dx_tiles_n) {
+  constexpr int kFwd = fwd_lds_bytes<E, T, 1, 1, 2, 2, kBwdFwdBufs>();
+  constexpr int kDw = dw_lds_bytes<T, kDwBufs>();
+  __shared__ __attribute__((aligned(16))) char lds[kFwd > kDw ? kFwd : kDw];
+  const int64_t b = blockIdx.x;
+  if (b < ndw_pad) {
+    const int64_t lid = xcd_logical_id(b, ndw_pad);
+    if (lid < ndw)
+      dw_tile<E, T, kDwBufs>(lds, lid, dy, x, ws, nrows, dg, cg, rows_per_split, dw_tiles_m, dw_tiles_n);
+  } else {
+    const int64_t nb = gridDim.x - ndw_pad;
+    fwd_tile<E, T, 1, 1, 2, 2, kBwdFwdBufs, kBwdFwdPrefetch, SCHED>(lds, xcd_logical_id(b - ndw_pad, nb), dy, wb,
+                                                                     dx, nrows, dg, cg, dx_tiles_n, nullptr, 0);
+  }
+}
+
+// Sum the split partials in split order (deterministic), inverse group DFT
+// along u, write dw[m][n][0..T-1] (float32).  Thread (plane p, entry e) of a
+// 256-thread block sums plane p of one of 256/T consecutive entries; the T
+// plane sums meet in LDS and one thread per entry applies the inverse DFT.
+// nsplit == 0 writes zeros.
+template <int T>
+__global__ void __launch_bounds__(kThreads)
+dw_finalize_kernel(const float* __restrict__ ws, float* __restrict__ dw, int mg, int ng, int nsplit) {
+  constexpr int EB = kThreads / T;
+  __shared__ float part[T][EB];
+  const int64_t plane = (int64_t)mg * ng;
+  const int e = threadIdx.x % EB, p = threadIdx.x / EB;
+  const int64_t idx = (int64_t)blockIdx.x * EB + e;
+  float acc = 0.f;
+  if (idx < plane) {
+    const float* src = ws + p * plane + idx;
+    const int64_t step = T * plane;
+    int s = 0;
+    for (; s + 4 <= nsplit; s += 4) {
+      const float v0 = src[(s + 0) * step], v1 = src[(s + 1) * step];
+      const float v2 = src[(s + 2) * step], v3 = src[(s + 3) * step];
+      acc += v0;
+      acc += v1;
+      acc += v2;
+      acc += v3;
+    }
+    for (; s < nsplit; ++s) acc += src[s * step];
+  }
+  part[p][e] = acc;
+  __syncthreads();
+  if (p == 0 && idx < plane) {
+    float f[T], y[T];
+#pragma unroll
+    for (int k = 0; k < T; ++k) f[k] = part[k][e];
+    Grp<T>::idft(f, y);
+    store_group<float, T>(dw + idx * T, y);
+  }
+}
+
+// ============================================================ prepare
+//
+// Weight spectra in the stage-block layout read by fwd_kernel:
+//   dst[row][ks][plane][s]   (SG = 16 fp32 / 32 f16 slots per 64-byte block)
+// where slot s of stage ks holds group channel ks * SG + slot_group(s) (the
+// slot order fwd_kernel's loaders produce for the transformed input) and
+// groups past the end are zero.
+//   forward planes:   row = d', groups = c',  spectrum of w[d'][c'][.]
+//   transpose planes: row = c', groups = d',  conjugate spectrum of w[d'][c'][.]
+// The second set is the spectrum of the transposed, group-reversed weight
+// (a conjugate), used by the dX pass.
+template <typename E, int T, bool kTranspose>
+__global__ void __launch_bounds__(kThreads)
+prepare_kernel(const E* __restrict__ w, E* __restrict__ dst, int mg, int ng) {
+  constexpr int SG = Traits<E>::kStageGroups;
+  const int rows = kTranspose ? ng : mg;
+  const int kgr = kTranspose ? mg : ng;
+  const int nks = (kgr + SG - 1) / SG;
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= (int64_t)rows * nks * SG) return;
+  const int s = (int)(idx % SG);
+  const int64_t t = idx / SG;
+  const int ks = (int)(t % nks);
+  const int64_t row = t / nks;
+  const int g = ks * SG + slot_group<E, T>(s);
+  float f[T];
+#pragma unroll
+  for (int p = 0; p < T; ++p) f[p] = 0.f;
+  if (g < kgr) {
+    const E* src = kTranspose ? w + ((int64_t)g * ng + row) * T : w + (row * ng + g) * T;
+    float z[T];
+#pragma unroll
+    for (int u = 0; u < T; ++u) z[u] = (float)src[u];
+    Grp<T>::dft(z, f);
+    if (kTranspose) {
+#pragma unroll
+      for (int p = 0; p < T; ++p)
+        if (imag_plane(p)) f[p] = -f[p];
+    }
+  }
+  E* o = dst + (row * nks + ks) * T * SG + s;
+#pragma unroll
+  for (int p = 0; p < T; ++p) o[p * SG] = (E)f[p];
+}
+
+// ============================================================ launchers
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+template <typename E, int T, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED>
+hipError_t launch_fwd_s(const void* in, const void* wp, void* out, int64_t nrows, int kg, int mg,
+                        const void* bias, int act, hipStream_t s) {
+  constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
+  const int64_t tiles_m = cdiv(nrows, BM);
+  const int tiles_n = (int)cdiv(mg, BN);
+  const int64_t grid = tiles_m * tiles_n;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fwd_kernel<E, T, FM, FN, WM, WN, NBUF, PF, SCHED>), dim3((unsigned)grid), dim3(64 * WM * WN),
+                     0, s, static_cast<const E*>(in), static_cast<const E*>(wp), static_cast<E*>(out), nrows, kg, mg,
+                     tiles_n, static_cast<const E*>(bias), act);
+  return hipGetLastError();
+}
+
+template <typename E, int T>
+hipError_t launch_dw_t(const void* dy, const void* x, float* ws, float* dw, int64_t nrows, int mg, int ng,
+                       int64_t rows_per_split, int nsplit, hipStream_t s) {
+  const int tiles_m = (int)cdiv(mg, 64), tiles_n = (int)cdiv(ng, 64);
+  if (nsplit > 0) {
+    const int64_t grid = (int64_t)tiles_m * tiles_n * nsplit;
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((dw_partial_kernel<E, T>), dim3((unsigned)grid), dim3(kThreads), 0, s,
+                       static_cast<const E*>(dy), static_cast<const E*>(x), ws, nrows, mg, ng, rows_per_split,
+                       tiles_m, tiles_n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t fgrid = cdiv((int64_t)mg * ng, kThreads / T);
+  hipLaunchKernelGGL((dw_finalize_kernel<T>), dim3((unsigned)fgrid), dim3(kThreads), 0, s, ws, dw, mg, ng, nsplit);
+  return hipGetLastError();
+}
+
+template <typename E, int T>
+hipError_t launch_bwd_fused_t(const void* dy, const void* x, const void* wb, void* dx, float* ws, float* dw,
+                              int64_t nrows, int dg, int cg, int64_t rows_per_split, int nsplit, hipStream_t s) {
+  const int dw_tiles_m = (int)cdiv(dg, 64), dw_tiles_n = (int)cdiv(cg, 64);
+  const int64_t ndw = (int64_t)dw_tiles_m * dw_tiles_n * nsplit;
+  const int64_t ndw_pad = cdiv(ndw, 8) * 8;
+  const int dx_tiles_n = (int)cdiv(cg, 64);
+  const int64_t ndx = cdiv(nrows, 64) * dx_tiles_n;
+  const int64_t grid = ndw_pad + ndx;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (grid > 0) {
+    hipLaunchKernelGGL((bwd_fused_kernel<E, T, 1>), dim3((unsigned)grid), dim3(kThreads), 0, s,
+                       static_cast<const E*>(dy), static_cast<const E*>(x), static_cast<const E*>(wb),
+                       static_cast<E*>(dx), ws, nrows, dg, cg, rows_per_split, dw_tiles_m, dw_tiles_n, ndw, ndw_pad,
+                       dx_tiles_n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t fgrid = cdiv((int64_t)dg * cg, kThreads / T);
+  hipLaunchKernelGGL((dw_finalize_kernel<T>), dim3((unsigned)fgrid), dim3(kThreads), 0, s, ws, dw, dg, cg, nsplit);
+  return hipGetLastError();
+}
+
+template <typename E, int T>
+hipError_t launch_prepare_t(const void* w, void* wf, void* wb, int mg, int ng, hipStream_t s) {
+  constexpr int SG = Traits<E>::kStageGroups;
+  const int64_t nf = (int64_t)mg * cdiv(ng, SG) * SG, nb = (int64_t)ng * cdiv(mg, SG) * SG;
+  hipLaunchKernelGGL((prepare_kernel<E, T, false>), dim3((unsigned)cdiv(nf, kThreads)), dim3(kThreads), 0, s,
+                     static_cast<const E*>(w), static_cast<E*>(wf), mg, ng);
+  hipLaunchKernelGGL((prepare_kernel<E, T, true>), dim3((unsigned)cdiv(nb, kThreads)), dim3(kThreads), 0, s,
+                     static_cast<const E*>(w), static_cast<E*>(wb), mg, ng);
+  return hipGetLastError();
+}
+
+}  // namespace eqlin

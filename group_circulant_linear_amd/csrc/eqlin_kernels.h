@@ -10,19 +10,40 @@ namespace eqlin {
 // the workgroup tile is (32 FM WM) rows x (32 FN WN) output groups; NBUF (1 or
 // 2) is the number of LDS stage buffers and PF (1 or 2) the number of stages
 // of global loads in flight in registers.
-bool fwd_tile_known(int tile);
-// bias: nullable, one storage-dtype value per output group; act: 0 none, 1 GELU (erf)
-hipError_t launch_forward(int dtype, int tile, const void* in, const void* wp, void* out, int64_t nrows,
-                          int kg, int mg, const void* bias, int act, hipStream_t s);
-hipError_t launch_dw(int dtype, const void* dy, const void* x, float* ws, float* dw, int64_t nrows, int mg,
-                     int ng, int64_t rows_per_split, int nsplit, hipStream_t s);
-// dX (forward structure on the transpose spectra wb, tile 1122) and the dw
-// split partials in one launch, then the dw finalize.  nrows > 0.
-hipError_t launch_bwd_fused(int dtype, const void* dy, const void* x, const void* wb, void* dx, float* ws,
-                            float* dw, int64_t nrows, int dg, int cg, int64_t rows_per_split, int nsplit,
-                            hipStream_t s);
-hipError_t launch_prepare(int dtype, const void* w, void* wf, void* wb, int mg, int ng, hipStream_t s);
-int stage_groups(int dtype);       // group channels per pipeline stage (16 fp32, 32 f16)
-int dw_rows_per_stage(int dtype);  // rows per dw pipeline stage (16 fp32, 32 f16)
+//
+// Launchers of the cyclic group of order T, instantiated for T = 4 (the p4
+// rotation group) and T = 8 (C8).  dtype 0 = float32, 1 = float16; kg / mg /
+// dg / cg are group-channel counts (channels / T).
+template <int T>
+struct Launch {
+  static bool fwd_tile_known(int tile);
+  // bias: nullable, one storage-dtype value per output group; act: 0 none, 1 GELU (erf)
+  static hipError_t forward(int dtype, int tile, const void* in, const void* wp, void* out, int64_t nrows, int kg,
+                            int mg, const void* bias, int act, hipStream_t s);
+  static hipError_t dw(int dtype, const void* dy, const void* x, float* ws, float* dw, int64_t nrows, int mg, int ng,
+                       int64_t rows_per_split, int nsplit, hipStream_t s);
+  // dX (forward structure on the transpose spectra wb, 64 x 64 tiles) and the
+  // dw split partials in one launch, then the dw finalize.  nrows > 0.
+  static hipError_t bwd_fused(int dtype, const void* dy, const void* x, const void* wb, void* dx, float* ws,
+                              float* dw, int64_t nrows, int dg, int cg, int64_t rows_per_split, int nsplit,
+                              hipStream_t s);
+  static hipError_t prepare(int dtype, const void* w, void* wf, void* wb, int mg, int ng, hipStream_t s);
+};
+
+#define EQLIN_DECLARE_LAUNCH(T)                                                                                     \
+  template <> bool Launch<T>::fwd_tile_known(int tile);                                                             \
+  template <> hipError_t Launch<T>::forward(int, int, const void*, const void*, void*, int64_t, int, int,          \
+                                            const void*, int, hipStream_t);                                        \
+  template <> hipError_t Launch<T>::dw(int, const void*, const void*, float*, float*, int64_t, int, int, int64_t,   \
+                                       int, hipStream_t);                                                          \
+  template <> hipError_t Launch<T>::bwd_fused(int, const void*, const void*, const void*, void*, float*, float*,   \
+                                              int64_t, int, int, int64_t, int, hipStream_t);                       \
+  template <> hipError_t Launch<T>::prepare(int, const void*, void*, void*, int, int, hipStream_t);
+EQLIN_DECLARE_LAUNCH(4)
+EQLIN_DECLARE_LAUNCH(8)
+#undef EQLIN_DECLARE_LAUNCH
+
+inline int stage_groups(int dtype) { return dtype == 0 ? 16 : 32; }       // group channels per pipeline stage
+inline int dw_rows_per_stage(int dtype) { return dtype == 0 ? 16 : 32; }  // rows per dw pipeline stage
 
 }  // namespace eqlin

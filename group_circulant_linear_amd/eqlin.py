@@ -18,6 +18,7 @@ import torch
 from .build import LIB, INCLUDE
 
 T_P4 = 4
+GROUP_ORDERS = (4, 8)   # cyclic groups the library implements (p4 rotations and C8)
 EQLIN_F32, EQLIN_F16 = 0, 1
 STATUS = {0: "EQLIN_OK", 1: "EQLIN_EINVAL", 2: "EQLIN_ENOTSUP", 3: "EQLIN_EALIGN",
           4: "EQLIN_EWORKSPACE", 5: "EQLIN_EHIP"}
@@ -109,32 +110,34 @@ class Prepared(NamedTuple):
     C: int
     D: int
     dtype: torch.dtype
+    T: int = T_P4
 
 
-def eqlin_prepared_weight_bytes(C: int, D: int, dtype: torch.dtype) -> int:
-    return int(load_library().eqlin_prepared_weight_bytes(C, D, T_P4, _DTYPES[dtype]))
+def eqlin_prepared_weight_bytes(C: int, D: int, dtype: torch.dtype, T: int = T_P4) -> int:
+    return int(load_library().eqlin_prepared_weight_bytes(C, D, T, _DTYPES[dtype]))
 
 
-def eqlin_prepared_transpose_offset(C: int, D: int, dtype: torch.dtype) -> int:
-    return int(load_library().eqlin_prepared_transpose_offset(C, D, T_P4, _DTYPES[dtype]))
+def eqlin_prepared_transpose_offset(C: int, D: int, dtype: torch.dtype, T: int = T_P4) -> int:
+    return int(load_library().eqlin_prepared_transpose_offset(C, D, T, _DTYPES[dtype]))
 
 
 def eqlin_prepare_weights(w: torch.Tensor, out: Optional[torch.Tensor] = None) -> Prepared:
-    """w [D'][C'][4] -> prepared spectra for eqlin_forward / eqlin_backward."""
+    """w [D/T][C/T][T] -> prepared spectra for eqlin_forward / eqlin_backward (T = w.shape[2])."""
     lib = load_library()
     _need_cuda(w, "w")
     dt = _dtype_code(w)
-    if w.dim() != 3 or w.shape[2] != T_P4:
-        raise ValueError(f"w must have shape [D/4, C/4, 4], got {tuple(w.shape)}")
-    D, C = 4 * w.shape[0], 4 * w.shape[1]
-    nbytes = int(lib.eqlin_prepared_weight_bytes(C, D, T_P4, dt))
+    if w.dim() != 3:
+        raise ValueError(f"w must have shape [D/T, C/T, T], got {tuple(w.shape)}")
+    T = int(w.shape[2])
+    D, C = T * w.shape[0], T * w.shape[1]
+    nbytes = int(lib.eqlin_prepared_weight_bytes(C, D, T, dt))
     if out is None:
-        out = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+        out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=w.device)
     _need_cuda(out, "out")
     _check("eqlin_prepare_weights",
-           lib.eqlin_prepare_weights(_ptr(w), C, D, T_P4, dt, _ptr(out), out.numel() * out.element_size(),
+           lib.eqlin_prepare_weights(_ptr(w), C, D, T, dt, _ptr(out), out.numel() * out.element_size(),
                                      _stream(w)))
-    return Prepared(out, C, D, w.dtype)
+    return Prepared(out, C, D, w.dtype, T)
 
 
 def eqlin_forward(X: torch.Tensor, W_hat: Prepared, out: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -152,7 +155,7 @@ def eqlin_forward(X: torch.Tensor, W_hat: Prepared, out: Optional[torch.Tensor] 
     _need_cuda(out, "out")
     if tuple(out.shape) != (N, W_hat.D) or out.dtype != X.dtype:
         raise ValueError("out has the wrong shape or dtype")
-    _check("eqlin_forward", lib.eqlin_forward(_ptr(X), N, W_hat.C, W_hat.D, T_P4, _ptr(W_hat.buf), _ptr(out),
+    _check("eqlin_forward", lib.eqlin_forward(_ptr(X), N, W_hat.C, W_hat.D, W_hat.T, _ptr(W_hat.buf), _ptr(out),
                                               dt, _stream(X)))
     return out
 
@@ -162,7 +165,7 @@ ACT = {"none": 0, "gelu": 1}
 
 def eqlin_forward_ex(X: torch.Tensor, W_hat: Prepared, bias: Optional[torch.Tensor] = None, act: str = "none",
                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Y = act(X W^T + b) in one kernel; bias [D/4] (group-invariant, storage dtype) or None."""
+    """Y = act(X W^T + b) in one kernel; bias [D/T] (group-invariant, storage dtype) or None."""
     lib = load_library()
     _need_cuda(X, "X")
     dt = _dtype_code(X)
@@ -174,31 +177,31 @@ def eqlin_forward_ex(X: torch.Tensor, W_hat: Prepared, bias: Optional[torch.Tens
         raise ValueError(f"act must be one of {sorted(ACT)}")
     if bias is not None:
         _need_cuda(bias, "bias")
-        if bias.dtype != X.dtype or tuple(bias.shape) != (W_hat.D // 4,):
-            raise ValueError(f"bias must be [{W_hat.D // 4}] of dtype {X.dtype}")
+        if bias.dtype != X.dtype or tuple(bias.shape) != (W_hat.D // W_hat.T,):
+            raise ValueError(f"bias must be [{W_hat.D // W_hat.T}] of dtype {X.dtype}")
     N = X.shape[0]
     if out is None:
         out = torch.empty((N, W_hat.D), dtype=X.dtype, device=X.device)
     _need_cuda(out, "out")
-    _check("eqlin_forward_ex", lib.eqlin_forward_ex(_ptr(X), N, W_hat.C, W_hat.D, T_P4, _ptr(W_hat.buf),
+    _check("eqlin_forward_ex", lib.eqlin_forward_ex(_ptr(X), N, W_hat.C, W_hat.D, W_hat.T, _ptr(W_hat.buf),
                                                     _ptr(bias), ACT[act], _ptr(out), dt, _stream(X)))
     return out
 
 
-def eqlin_backward_workspace_bytes(N: int, C: int, D: int, dtype: torch.dtype) -> int:
-    return int(load_library().eqlin_backward_workspace_bytes(N, C, D, T_P4, _DTYPES[dtype]))
+def eqlin_backward_workspace_bytes(N: int, C: int, D: int, dtype: torch.dtype, T: int = T_P4) -> int:
+    return int(load_library().eqlin_backward_workspace_bytes(N, C, D, T, _DTYPES[dtype]))
 
 
 def eqlin_backward(dY: torch.Tensor, X: Optional[torch.Tensor], W_hat: Prepared, need_dx: bool = True,
                    need_dw: bool = True, workspace: Optional[torch.Tensor] = None,
                    dX_out: Optional[torch.Tensor] = None, dw_out: Optional[torch.Tensor] = None):
-    """(dX [N][C] or None, dw [D/4][C/4][4] float32 or None) for upstream gradient dY [N][D]."""
+    """(dX [N][C] or None, dw [D/T][C/T][T] float32 or None) for upstream gradient dY [N][D]."""
     lib = load_library()
     _need_cuda(dY, "dY")
     dt = _dtype_code(dY)
     if dY.dtype != W_hat.dtype:
         raise TypeError("dY and the prepared weights differ in dtype")
-    C, D = W_hat.C, W_hat.D
+    C, D, T = W_hat.C, W_hat.D, W_hat.T
     if dY.dim() != 2 or dY.shape[1] != D:
         raise ValueError(f"dY must have shape [N, {D}], got {tuple(dY.shape)}")
     N = dY.shape[0]
@@ -215,16 +218,16 @@ def eqlin_backward(dY: torch.Tensor, X: Optional[torch.Tensor], W_hat: Prepared,
         _need_cuda(X, "X")
         if X.dtype != dY.dtype or tuple(X.shape) != (N, C):
             raise ValueError(f"X must be [N, {C}] of dtype {dY.dtype}")
-        dw = dw_out if dw_out is not None else torch.empty((D // 4, C // 4, 4), dtype=torch.float32,
+        dw = dw_out if dw_out is not None else torch.empty((D // T, C // T, T), dtype=torch.float32,
                                                            device=dY.device)
         _need_cuda(dw, "dw")
-        ws_bytes = int(lib.eqlin_backward_workspace_bytes(N, C, D, T_P4, dt))
+        ws_bytes = int(lib.eqlin_backward_workspace_bytes(N, C, D, T, dt))
         if workspace is None:
             workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dY.device)
         _need_cuda(workspace, "workspace")
         ws_bytes = workspace.numel() * workspace.element_size()
     _check("eqlin_backward",
-           lib.eqlin_backward(_ptr(dY), _ptr(X) if need_dw else None, N, C, D, T_P4, _ptr(W_hat.buf),
+           lib.eqlin_backward(_ptr(dY), _ptr(X) if need_dw else None, N, C, D, T, _ptr(W_hat.buf),
                               _ptr(dX), _ptr(dw), _ptr(workspace) if need_dw else None, ws_bytes, dt,
                               _stream(dY)))
     return dX, dw
@@ -242,14 +245,14 @@ def eqlin_backward_dx(dY: torch.Tensor, W_hat: Prepared, out: Optional[torch.Ten
     if out is None:
         out = torch.empty((N, C), dtype=dY.dtype, device=dY.device)
     _need_cuda(out, "out")
-    _check("eqlin_backward_dx", lib.eqlin_backward_dx(_ptr(dY), N, C, D, T_P4, _ptr(W_hat.buf), _ptr(out), dt,
+    _check("eqlin_backward_dx", lib.eqlin_backward_dx(_ptr(dY), N, C, D, W_hat.T, _ptr(W_hat.buf), _ptr(out), dt,
                                                       _stream(dY)))
     return out
 
 
 def eqlin_backward_dw(dY: torch.Tensor, X: torch.Tensor, workspace: Optional[torch.Tensor] = None,
-                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """dw [D/4][C/4][4] (float32) from dY [N][D] and X [N][C]."""
+                      out: Optional[torch.Tensor] = None, T: int = T_P4) -> torch.Tensor:
+    """dw [D/T][C/T][T] (float32) from dY [N][D] and X [N][C]."""
     lib = load_library()
     _need_cuda(dY, "dY")
     _need_cuda(X, "X")
@@ -258,13 +261,13 @@ def eqlin_backward_dw(dY: torch.Tensor, X: torch.Tensor, workspace: Optional[tor
         raise ValueError("dY [N, D] and X [N, C] must share N and dtype")
     N, C, D = X.shape[0], X.shape[1], dY.shape[1]
     if out is None:
-        out = torch.empty((D // 4, C // 4, 4), dtype=torch.float32, device=dY.device)
+        out = torch.empty((D // T, C // T, T), dtype=torch.float32, device=dY.device)
     _need_cuda(out, "out")
-    ws_bytes = int(lib.eqlin_backward_workspace_bytes(N, C, D, T_P4, dt))
+    ws_bytes = int(lib.eqlin_backward_workspace_bytes(N, C, D, T, dt))
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dY.device)
     _need_cuda(workspace, "workspace")
     _check("eqlin_backward_dw",
-           lib.eqlin_backward_dw(_ptr(dY), _ptr(X), N, C, D, T_P4, _ptr(out), _ptr(workspace),
+           lib.eqlin_backward_dw(_ptr(dY), _ptr(X), N, C, D, T, _ptr(out), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), dt, _stream(dY)))
     return out

@@ -1,9 +1,9 @@
-"""Drop-in module for a p4 group-circulant (EQ-)linear layer.
+"""Drop-in module for a group-circulant (EQ-)linear layer (p4 rotations or C8).
 
 The Flash EQ-Linear summary (gist.science 2607.21271, "Implementation", last
 bullet) describes the method as a training-free, plug-and-play replacement:
 the naive layer's learnable parameters are reused unchanged.  FlashEQLinear
-holds exactly those parameters, w [D/4][C/4][4], and runs the forward and
+holds exactly those parameters, w [D/T][C/T][T], and runs the forward and
 backward through the HIP library (eqlin_prepare_weights / eqlin_forward /
 eqlin_backward).  The prepared spectra are cached per weight version, so they
 are recomputed only after w changes (an optimizer step or a load).
@@ -20,6 +20,7 @@ import torch
 from . import eqlin
 
 T_P4 = 4
+GROUP_ORDERS = (4, 8)
 
 
 class _SpectraCache:
@@ -68,20 +69,25 @@ class EQLinearFunction(torch.autograd.Function):
 
 
 class FlashEQLinear(torch.nn.Module):
-    """p4 group-circulant linear layer (no bias), in_features -> out_features.
+    """Group-circulant linear layer (no bias), in_features -> out_features.
 
-    Parameter ``w`` has shape [out_features/4, in_features/4, 4]; block
-    (d', c') of the dense weight is the 4 x 4 circulant
-    W[4d'+t, 4c'+s] = w[d', c', (t - s) mod 4].
+    ``group_size`` T is 4 (the p4 rotation group, the default) or 8 (C8).
+    Parameter ``w`` has shape [out_features/T, in_features/T, T]; block
+    (d', c') of the dense weight is the T x T circulant
+    W[T d'+t, T c'+s] = w[d', c', (t - s) mod T].
     """
 
-    def __init__(self, in_features: int, out_features: int, device=None, dtype=None):
+    def __init__(self, in_features: int, out_features: int, device=None, dtype=None, group_size: int = T_P4):
         super().__init__()
-        if in_features % T_P4 or out_features % T_P4:
-            raise ValueError("in_features and out_features must be multiples of 4")
+        if group_size not in GROUP_ORDERS:
+            raise ValueError(f"group_size must be one of {GROUP_ORDERS}")
+        T = group_size
+        if in_features % T or out_features % T:
+            raise ValueError(f"in_features and out_features must be multiples of {T}")
         self.in_features = in_features
         self.out_features = out_features
-        self.w = torch.nn.Parameter(torch.empty(out_features // T_P4, in_features // T_P4, T_P4,
+        self.group_size = T
+        self.w = torch.nn.Parameter(torch.empty(out_features // T, in_features // T, T,
                                                 device=device, dtype=dtype))
         self._cache = _SpectraCache()
         self.reset_parameters()
@@ -92,11 +98,11 @@ class FlashEQLinear(torch.nn.Module):
 
     @classmethod
     def from_naive(cls, w: torch.Tensor) -> "FlashEQLinear":
-        """Wrap a naive EQ-Linear's circulant parameter w [D/4][C/4][4] (copied)."""
+        """Wrap a naive EQ-Linear's circulant parameter w [D/T][C/T][T] (copied)."""
         Dp, Cp, T = w.shape
-        if T != T_P4:
-            raise ValueError("only the p4 group (T = 4) is supported")
-        m = cls(4 * Cp, 4 * Dp, device=w.device, dtype=w.dtype)
+        if T not in GROUP_ORDERS:
+            raise ValueError(f"group size {T} is not supported (use one of {GROUP_ORDERS})")
+        m = cls(T * Cp, T * Dp, device=w.device, dtype=w.dtype, group_size=T)
         with torch.no_grad():
             m.w.copy_(w)
         return m
@@ -106,13 +112,15 @@ class FlashEQLinear(torch.nn.Module):
 
     def dense_weight(self) -> torch.Tensor:
         """The expanded D x C weight (for inspection; the forward never builds it)."""
-        t = torch.arange(T_P4, device=self.w.device)
-        idx = (t.view(T_P4, 1) - t.view(1, T_P4)) % T_P4
+        T = self.group_size
+        t = torch.arange(T, device=self.w.device)
+        idx = (t.view(T, 1) - t.view(1, T)) % T
         Dp, Cp, _ = self.w.shape
-        return self.w[:, :, idx].permute(0, 2, 1, 3).reshape(Dp * T_P4, Cp * T_P4)
+        return self.w[:, :, idx].permute(0, 2, 1, 3).reshape(Dp * T, Cp * T)
 
     def extra_repr(self) -> str:
-        return f"in_features={self.in_features}, out_features={self.out_features}, group=p4"
+        group = "p4" if self.group_size == 4 else f"C{self.group_size}"
+        return f"in_features={self.in_features}, out_features={self.out_features}, group={group}"
 
 
 def convert_state_dict(naive_state: dict, key_map: Optional[dict] = None) -> dict:

@@ -1,37 +1,41 @@
 /*
- * eqlin.h -- C ABI of the MI355X (gfx950) p4 group-circulant linear layer
- * ("Flash EQ-Linear").
+ * eqlin.h -- C ABI of the MI355X (gfx950) group-circulant linear layer
+ * ("Flash EQ-Linear") for the cyclic groups of order T = 4 (the p4 rotation
+ * group) and T = 8 (C8).
  *
  * The layer (Flash EQ-Linear technical summary, gist.science 2607.21271,
  * section "Key insight"): the dense weight W (D x C) is made of
- * (D/4) x (C/4) blocks, block (d', c') being the 4 x 4 circulant of a
- * learnable vector w[d', c', 0..3]:
+ * (D/T) x (C/T) blocks, block (d', c') being the T x T circulant of a
+ * learnable vector w[d', c', 0..T-1]:
  *
- *     W[4d' + t, 4c' + s] = w[d', c', (t - s) mod 4]
- *     Y = X W^T,  Y[n, 4d' + t] = sum_{c', s} w[d', c', (t - s) mod 4] X[n, 4c' + s]
+ *     W[T d' + t, T c' + s] = w[d', c', (t - s) mod T]
+ *     Y = X W^T,  Y[n, T d' + t] = sum_{c', s} w[d', c', (t - s) mod T] X[n, T c' + s]
  *
  * It is computed exactly through the group DFT ("Algorithmic approach",
  * items 1-2; "Specialisation for the p4 rotation group"): only the
- * non-redundant frequencies f0, f2 (real) and f1 (complex) of the real
- * signals are formed, with add/sub-only transforms, and the contraction
- * becomes six real per-frequency matrix products instead of sixteen.
+ * non-redundant frequencies of the real signals are formed and the
+ * contraction becomes real per-frequency matrix products.  For T = 4: f0, f2
+ * (real) and f1 (complex), add/sub-only transforms, six real products
+ * instead of sixteen.  For T = 8 (the summary names other groups as future
+ * work, "Limitations"; this is the same route for the next cyclic group):
+ * f0, f4 (real) and f1, f2, f3 (complex), transforms with the factor
+ * sqrt(1/2), fourteen real products instead of sixty-four.
  *
  * Conventions shared by every entry point
- *   - T is the group size and must be 4 (the summary's method is specialised
- *     to the p4 rotation group, "Limitations"); any other T -> EQLIN_ENOTSUP.
- *   - C, D are the full channel widths, positive multiples of 4; C' = C/4 and
- *     D' = D/4 are the group-channel counts.  The channel index is
- *     group_channel * 4 + group_element (group element fastest).
+ *   - T is the group size, 4 or 8; any other T -> EQLIN_ENOTSUP.
+ *   - C, D are the full channel widths, positive multiples of T; C' = C/T
+ *     and D' = D/T are the group-channel counts.  The channel index is
+ *     group_channel * T + group_element (group element fastest).
  *   - All matrices are row-major and contiguous:
- *       X, dX  [N][C]      Y, dY  [N][D]      w  [D'][C'][4]     dw [D'][C'][4]
+ *       X, dX  [N][C]      Y, dY  [N][D]      w  [D'][C'][T]     dw [D'][C'][T]
  *   - dtype EQLIN_F32: X, Y, dY, dX, w in float32, arithmetic in float32
  *     (true fp32 matrix-core products).
  *     dtype EQLIN_F16: X, Y, dY, dX, w stored as IEEE binary16; the group
  *     transforms run in float32, the Fourier operands are rounded once
  *     (nearest-even) to binary16 for the matrix cores, products accumulate in
  *     float32, and outputs are rounded nearest-even to binary16.  dw is float32
- *     for both dtypes.  With EQLIN_F16, C' and D' must be even
- *     (otherwise EQLIN_ENOTSUP).
+ *     for both dtypes.  With EQLIN_F16 and T = 4, C' and D' must be
+ *     even (otherwise EQLIN_ENOTSUP).
  *   - Every data pointer is a DEVICE pointer on the current HIP device, owned
  *     by the caller, 16-byte aligned (else EQLIN_EALIGN).  The library never
  *     allocates, frees or retains memory and keeps no mutable global state;
@@ -61,7 +65,7 @@ enum { EQLIN_F32 = 0, EQLIN_F16 = 1 };
 enum {
   EQLIN_OK = 0,
   EQLIN_EINVAL = 1,     /* bad size, negative N, null required pointer, unknown dtype */
-  EQLIN_ENOTSUP = 2,    /* T != 4, or an odd group count with EQLIN_F16 */
+  EQLIN_ENOTSUP = 2,    /* T not 4 or 8, or an odd group count with EQLIN_F16 and T = 4 */
   EQLIN_EALIGN = 3,     /* a data pointer is not 16-byte aligned */
   EQLIN_EWORKSPACE = 4, /* workspace / prepared-weight buffer too small */
   EQLIN_EHIP = 5        /* the HIP runtime reported an error for a launch */
@@ -82,16 +86,21 @@ int eqlin_last_hip_error(void);
  *
  * W_hat layout (element = the storage dtype; S = 16 for EQLIN_F32, 32 for
  * EQLIN_F16 group channels per 64-byte block):
- *   offset 0: forward set  [D'][ceil(C'/S)][4 planes][S]
+ *   offset 0: forward set  [D'][ceil(C'/S)][T planes][S]
  *   offset eqlin_prepared_transpose_offset() (a multiple of 256):
- *             transpose set [C'][ceil(D'/S)][4 planes][S]
- * Planes of the forward set are (F0, F2, Re F1, Im F1) of w[d'][c'], where
- * F_k = sum_u w[d', c', u] exp(-2 pi i k u / 4) is the group DFT of each
- * circulant vector ("Algorithmic approach", item 1; F3 = conj(F1) is
- * redundant for real w, item 2).  The transpose set holds
- * (F0, F2, Re F1, -Im F1): the spectrum of the transposed, group-reversed
- * weight (a conjugate) used by the dX pass.  Within block ks of a row, slot s
- * holds group channel ks*S + g(s) with
+ *             transpose set [C'][ceil(D'/S)][T planes][S]
+ * With F_k = sum_u w[d', c', u] exp(-2 pi i k u / T) the group DFT of each
+ * circulant vector ("Algorithmic approach", item 1; F_{T-k} = conj(F_k) is
+ * redundant for real w, item 2), the planes of the forward set are
+ *   T = 4: (F0, F2, Re F1, Im F1)
+ *   T = 8: (F0, F4, Re F1, Im F1, Re F2, Im F2, Re F3, Im F3)
+ * and the transpose set holds the same planes with every Im negated: the
+ * spectrum of the transposed, group-reversed weight (a conjugate) used by
+ * the dX pass.  Within block ks of a row, slot s holds group channel
+ * ks*S + g(s); with V = 16 / element bytes (4 or 8) and G = the number of
+ * whole groups in one 16-byte piece (2 for EQLIN_F16 with T = 4, else 1),
+ *   g(s) = G ((s / V) + 4 ((s % V) / G)) + (s % V) % G
+ * which for T = 4 reads
  *   g(s) = (s >> 2) + 4 (s & 3)                              (EQLIN_F32)
  *   g(s) = 2 ((s >> 3) + 4 ((s >> 1) & 3)) + (s & 1)          (EQLIN_F16)
  * (the order in which the forward kernel's loaders deposit the transformed
@@ -101,21 +110,21 @@ size_t eqlin_prepared_weight_bytes(int C, int D, int T, int dtype);
 size_t eqlin_prepared_transpose_offset(int C, int D, int T, int dtype);
 
 /*
- * a1: group DFT of the weights.  w [D'][C'][4] (device, storage dtype) ->
+ * a1: group DFT of the weights.  w [D'][C'][T] (device, storage dtype) ->
  * W_hat (device, W_hat_bytes >= eqlin_prepared_weight_bytes, else
  * EQLIN_EWORKSPACE).  Run it once per weight version; the forward and
- * backward calls consume W_hat read-only.  The transform uses adds and
- * subtracts only ("Specialisation for the p4 rotation group").
+ * backward calls consume W_hat read-only.  For T = 4 the transform uses adds
+ * and subtracts only ("Specialisation for the p4 rotation group").
  */
 int eqlin_prepare_weights(const void* w, int C, int D, int T, int dtype,
                           void* W_hat, size_t W_hat_bytes, void* stream);
 
 /*
  * a2-a4: Y = X W^T.  X [N][C], Y [N][D] (device, storage dtype), W_hat from
- * eqlin_prepare_weights for the same (C, D, dtype).  One fused kernel: group
- * DFT of X tiles into on-chip Fourier planes, the six real per-frequency
- * products on the matrix cores, inverse DFT (scales 1/4 and 1/2) in registers
- * and a single store of Y; no intermediate global-memory writes
+ * eqlin_prepare_weights for the same (C, D, T, dtype).  One fused kernel:
+ * group DFT of X tiles into on-chip Fourier planes, the real per-frequency
+ * products on the matrix cores (6 for T = 4, 14 for T = 8), inverse DFT in
+ * registers and a single store of Y; no intermediate global-memory writes
  * ("Implementation" section).
  */
 int eqlin_forward(const void* X, int64_t N, int C, int D, int T,
@@ -126,9 +135,9 @@ enum { EQLIN_ACT_NONE = 0, EQLIN_ACT_GELU = 1 };
 
 /*
  * Forward with a fused epilogue: Y = act(X W^T + b).
- *   bias: NULL or a device pointer to D' = D/4 values in the storage dtype
+ *   bias: NULL or a device pointer to D' = D/T values in the storage dtype
  *         (element-aligned).  The bias is group-invariant: b[d'] is added to
- *         all four outputs 4d'+0..3 of output group d', which keeps the layer
+ *         all T outputs T d'+0..T-1 of output group d', which keeps the layer
  *         equivariant (the summary is silent on bias; this is the reading).
  *   act:  EQLIN_ACT_NONE or EQLIN_ACT_GELU (GELU(z) = z/2 (1 + erf(z/sqrt 2)),
  *         pointwise, so it commutes with the group shift), else EQLIN_EINVAL.
@@ -145,8 +154,8 @@ size_t eqlin_backward_workspace_bytes(int64_t N, int C, int D, int T, int dtype)
 /*
  * a5 + a6: backward pass for upstream gradient dY [N][D].
  *   dX [N][C] = dY W   (transposed group-circulant; skipped if dX == NULL)
- *   dw [D'][C'][4] (float32) = d<dY, Y>/dw
- *      = sum_n sum_t dY[n, 4d'+t] X[n, 4c' + (t-u) mod 4]   (skipped if dw == NULL)
+ *   dw [D'][C'][T] (float32) = d<dY, Y>/dw
+ *      = sum_n sum_t dY[n, T d'+t] X[n, T c' + (t-u) mod T]   (skipped if dw == NULL)
  * dw is formed per frequency as sum_n G_k conj(Xhat_k) (G = group DFT of dY),
  * reduced over row splits in a fixed order (deterministic) and inverse
  * transformed along u.  `workspace` (device, >= eqlin_backward_workspace_bytes)

@@ -54,6 +54,7 @@ __all__ = [
     "dw_direct",
     "group_spectrum",
     "kept_p4_planes",
+    "kept_planes",
     "forward_rows",
     "dw_entries",
 ]
@@ -183,6 +184,26 @@ def kept_p4_planes(w) -> np.ndarray:
         raise ValueError("p4 planes need T = 4")
     F = group_spectrum(w)
     return np.stack([F[..., 0].real, F[..., 2].real, F[..., 1].real, F[..., 1].imag], axis=-1)
+
+
+def kept_planes(w) -> np.ndarray:
+    """The T non-redundant real planes of the group spectrum, for even T.
+
+    For real circulant vectors the spectrum is conjugate symmetric
+    ("Algorithmic approach" item 2): F[T-k] = conj(F[k]), and F[0], F[T/2] are
+    real.  Returns, per (d', c'), the T reals
+    (Re F0, Re F[T/2], Re F1, Im F1, ..., Re F[T/2-1], Im F[T/2-1]),
+    shape [D'][C'][T]; for T = 4 this is kept_p4_planes.
+    """
+    w = _f64(w)
+    T = w.shape[-1]
+    if T % 2 or T < 2:
+        raise ValueError("kept planes need an even T")
+    F = group_spectrum(w)
+    planes = [F[..., 0].real, F[..., T // 2].real]
+    for k in range(1, T // 2):
+        planes += [F[..., k].real, F[..., k].imag]
+    return np.stack(planes, axis=-1)
 
 
 def forward_rows(X, w, rows) -> np.ndarray:

@@ -48,6 +48,20 @@ def test_size_queries(lib):
     assert ws > 0 and ws % (4 * 192 * 192 * 4) == 0
 
 
+def test_size_queries_c8(lib):
+    # C8: stage blocks of 8 planes x 64 bytes = 512 bytes; 96 groups -> 6 (fp32) / 3 (f16) blocks
+    assert lib.eqlin_prepared_transpose_offset(768, 768, 8, 0) == 96 * 6 * 512
+    assert lib.eqlin_prepared_weight_bytes(768, 768, 8, 0) == 2 * 96 * 6 * 512
+    assert lib.eqlin_prepared_weight_bytes(768, 3072, 8, 1) == 384 * 3 * 512 + 96 * 12 * 512
+    assert lib.eqlin_prepared_weight_bytes(8, 8, 8, 0) == 1024
+    # odd group counts are fine with f16 when a group is 16 bytes
+    assert lib.eqlin_prepared_weight_bytes(40, 24, 8, 1) == 3 * 512 + 5 * 512
+    assert lib.eqlin_prepared_weight_bytes(36, 32, 8, 0) == 0      # C not a multiple of 8
+    assert lib.eqlin_prepared_weight_bytes(48, 48, 6, 0) == 0      # only T = 4 and T = 8
+    ws = lib.eqlin_backward_workspace_bytes(12608, 768, 768, 8, 0)
+    assert ws > 0 and ws % (8 * 96 * 96 * 4) == 0
+
+
 FAKE = ctypes.c_void_p(0x1000)        # aligned, never dereferenced (validation fails first)
 MISALIGNED = ctypes.c_void_p(0x1004)
 
@@ -64,6 +78,9 @@ def test_forward_validation(lib):
     assert f(MISALIGNED, 8, 32, 32, 4, FAKE, FAKE, 0, None) == EALIGN
     assert f(FAKE, 8, 32, 32, 4, FAKE, MISALIGNED, 0, None) == EALIGN
     assert f(FAKE, 8, 20, 32, 4, FAKE, FAKE, 1, None) == ENOTSUP   # C'=5 odd with f16
+    assert f(FAKE, 8, 36, 32, 8, FAKE, FAKE, 0, None) == EINVAL    # C not a multiple of 8
+    assert f(FAKE, 8, 48, 48, 6, FAKE, FAKE, 0, None) == ENOTSUP
+    assert f(MISALIGNED, 8, 40, 32, 8, FAKE, FAKE, 1, None) == EALIGN
     assert f(None, 0, 32, 32, 4, None, None, 0, None) == OK        # empty batch: nothing enqueued
 
 

@@ -10,8 +10,9 @@ torch = pytest.importorskip("torch")
 from group_circulant_linear_amd.module import FlashEQLinear, convert_state_dict  # noqa: E402
 
 
-def test_dense_view_matches_oracle_expansion():
-    m = FlashEQLinear(24, 40)
+@pytest.mark.parametrize("T", [4, 8])
+def test_dense_view_matches_oracle_expansion(T):
+    m = FlashEQLinear(3 * T, 5 * T, group_size=T)
     W = m.dense_weight().detach().double().numpy()
     assert np.array_equal(W, oracle.dense_expand(m.w.detach().double().numpy()))
 
@@ -19,12 +20,16 @@ def test_dense_view_matches_oracle_expansion():
 def test_from_naive_copies_parameters_and_rejects_other_groups():
     w = torch.randn(5, 3, 4)
     m = FlashEQLinear.from_naive(w)
-    assert (m.in_features, m.out_features) == (12, 20)
+    assert (m.in_features, m.out_features, m.group_size) == (12, 20, 4)
     assert torch.equal(m.w.detach(), w)
+    m8 = FlashEQLinear.from_naive(torch.randn(5, 3, 8))
+    assert (m8.in_features, m8.out_features, m8.group_size) == (24, 40, 8)
     with pytest.raises(ValueError):
-        FlashEQLinear.from_naive(torch.randn(5, 3, 8))
+        FlashEQLinear.from_naive(torch.randn(5, 3, 6))
     with pytest.raises(ValueError):
         FlashEQLinear(10, 8)
+    with pytest.raises(ValueError):
+        FlashEQLinear(12, 16, group_size=8)
 
 
 def test_convert_state_dict_renames_only_keys():
@@ -41,10 +46,11 @@ def test_no_cpu_fallback():
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("T", [4, 8])
 @pytest.mark.parametrize("dt,tol", [("f32", 1e-5), ("f16", 3e-3)])
-def test_module_forward_backward_matches_oracle(dt, tol):
+def test_module_forward_backward_matches_oracle(dt, tol, T):
     B, S, C, D = 3, 197, 96, 160
-    X, w, dY = make_layer_inputs(B * S, C, D, dt, seed=11)
+    X, w, dY = make_layer_inputs(B * S, C, D, dt, seed=11, T=T)
     m = FlashEQLinear.from_naive(torch.from_numpy(w).cuda())
     Xt = torch.from_numpy(X).cuda().reshape(B, S, C).requires_grad_(True)
     Y = m(Xt)

@@ -151,7 +151,7 @@ def test_forward_rows_subset():
 
 # --------------------------------------------------------------- backward pins
 
-@pytest.mark.parametrize("T", [4, 3])
+@pytest.mark.parametrize("T", [4, 3, 8])
 def test_gradients_by_directional_derivatives(T):
     # L(X, w) = <dY, Y(X, w)> is linear in X and in w separately, so
     # dL/dX[i] = L(e_i, w) and dL/dw[j] = L(X, e_j) exactly.
@@ -178,17 +178,19 @@ def test_gradients_by_directional_derivatives(T):
     assert _rel(dw, gw) < 1e-13
 
 
-def test_gradients_match_torch_autograd():
+@pytest.mark.parametrize("T", [4, 8])
+def test_gradients_match_torch_autograd(T):
     torch = pytest.importorskip("torch")
-    X = _rand((11, 32), 23)
-    w = _rand((6, 8, 4), 24)
-    dY = _rand((11, 24), 25)
+    Cp, Dp, N = 8, 6, 11
+    X = _rand((N, Cp * T), 23)
+    w = _rand((Dp, Cp, T), 24)
+    dY = _rand((N, Dp * T), 25)
     # dense weight assembled by torch from the circulant blocks via gather of
-    # scipy-built index pattern: idx[t, s] = (t - s) mod 4
-    idx = torch.tensor(scipy.linalg.circulant(np.arange(4)), dtype=torch.long)
+    # scipy-built index pattern: idx[t, s] = (t - s) mod T
+    idx = torch.tensor(scipy.linalg.circulant(np.arange(T)), dtype=torch.long)
     wt = torch.tensor(w, dtype=torch.float64, requires_grad=True)
-    blocks = wt[:, :, idx]                               # [D', C', 4, 4]
-    Wd = blocks.permute(0, 2, 1, 3).reshape(24, 32)
+    blocks = wt[:, :, idx]                               # [D', C', T, T]
+    Wd = blocks.permute(0, 2, 1, 3).reshape(Dp * T, Cp * T)
     Xt = torch.tensor(X, dtype=torch.float64, requires_grad=True)
     Yt = torch.nn.functional.linear(Xt, Wd)
     Yt.backward(torch.tensor(dY))
@@ -248,6 +250,27 @@ def test_kept_planes_conjugate_symmetry_and_values():
     assert np.max(np.abs(P[..., 1] - F[..., 2].real)) < 1e-13
     assert np.max(np.abs(P[..., 2] - F[..., 1].real)) < 1e-13
     assert np.max(np.abs(P[..., 3] - F[..., 1].imag)) < 1e-13
+
+
+@pytest.mark.parametrize("T", [2, 4, 6, 8])
+def test_kept_planes_general_even_T(T):
+    w = _rand((3, 5, T), 33 + T)
+    P = oracle.kept_planes(w)
+    assert P.shape == (3, 5, T)
+    # numpy's real inverse FFT of the half spectrum rebuilt from the planes gives w back
+    half = np.zeros((3, 5, T // 2 + 1), dtype=complex)
+    half[..., 0] = P[..., 0]
+    half[..., T // 2] = P[..., 1]
+    for k in range(1, T // 2):
+        half[..., k] = P[..., 2 * k] + 1j * P[..., 2 * k + 1]
+    assert np.max(np.abs(np.fft.irfft(half, n=T, axis=-1) - w)) < 1e-13
+    # and the planes are numpy's forward FFT values
+    F = np.fft.rfft(w, axis=-1)
+    assert np.max(np.abs(P[..., 0] - F[..., 0].real)) < 1e-13
+    if T >= 4:
+        assert np.max(np.abs(P[..., 3] - F[..., 1].imag)) < 1e-13
+    if T == 4:
+        assert np.array_equal(P, oracle.kept_p4_planes(w))
 
 
 # ------------------------------------------------------ page facts (golden)

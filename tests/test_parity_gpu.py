@@ -1,5 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
+Both groups the library implements are covered: the p4 rotation group (T = 4)
+and the cyclic group C8 (T = 8).
+
 Metric: max|gpu - ref| / max|ref| over the compared outputs.  Bars: 1e-5 for
 fp32, 3e-3 for f16 storage with fp32 accumulation.  Small shapes span several
 tiles plus ragged row / column / k tails and are compared element by element;
@@ -41,22 +44,34 @@ def say(*a):
 
 # --------------------------------------------------------------------- a1
 
-def slot_group(s, dt):
-    """Group channel held by slot s of a 64-byte stage block (header's layout)."""
-    if dt == "f32":
-        return (s >> 2) + 4 * (s & 3)
-    return 2 * ((s >> 3) + 4 * ((s >> 1) & 3)) + (s & 1)
+def slot_group(s, dt, T):
+    """Group channel held by slot s of a 64-byte stage block (the header's g(s))."""
+    V = 4 if dt == "f32" else 8
+    gb = T * (4 if dt == "f32" else 2)
+    G = 1 if gb >= 16 else 16 // gb
+    return G * (s // V + 4 * ((s % V) // G)) + (s % V) % G
 
 
-def decode_planes(flat, rows, groups, dt):
-    """[rows][ceil(groups/S)][4][S] stage blocks -> [rows][groups][4]; checks zero padding."""
+def test_slot_group_formula_matches_header_for_p4():
+    # the general formula reduces to the two p4 formulas the header spells out
+    for s in range(16):
+        assert slot_group(s, "f32", 4) == (s >> 2) + 4 * (s & 3)
+    for s in range(32):
+        assert slot_group(s, "f16", 4) == 2 * ((s >> 3) + 4 * ((s >> 1) & 3)) + (s & 1)
+    for dt, S in (("f32", 16), ("f16", 32)):
+        for T in (4, 8):
+            assert sorted(slot_group(s, dt, T) for s in range(S)) == list(range(S))
+
+
+def decode_planes(flat, rows, groups, dt, T):
+    """[rows][ceil(groups/S)][T][S] stage blocks -> [rows][groups][T]; checks zero padding."""
     S = 16 if dt == "f32" else 32
     nks = -(-groups // S)
-    blk = flat[: rows * nks * 4 * S].reshape(rows, nks, 4, S)
-    out = np.zeros((rows, groups, 4))
+    blk = flat[: rows * nks * T * S].reshape(rows, nks, T, S)
+    out = np.zeros((rows, groups, T))
     for ks in range(nks):
         for s in range(S):
-            g = ks * S + slot_group(s, dt)
+            g = ks * S + slot_group(s, dt, T)
             if g < groups:
                 out[:, g, :] = blk[:, ks, :, s]
             else:
@@ -64,22 +79,24 @@ def decode_planes(flat, rows, groups, dt):
     return out
 
 
-@pytest.mark.parametrize("dt,Dp,Cp", [("f32", 5, 3), ("f32", 20, 36), ("f32", 192, 192), ("f16", 6, 4),
-                                       ("f16", 40, 70), ("f16", 768, 192)])
-def test_prepared_planes_match_group_spectrum(dt, Dp, Cp):
-    say(f"prepare {dt} D'={Dp} C'={Cp}")
-    _, w, _ = make_layer_inputs(4, 4 * Cp, 4 * Dp, dt, seed=1, with_dy=False)
+@pytest.mark.parametrize("T,dt,Dp,Cp", [(4, "f32", 5, 3), (4, "f32", 20, 36), (4, "f32", 192, 192),
+                                         (4, "f16", 6, 4), (4, "f16", 40, 70), (4, "f16", 768, 192),
+                                         (8, "f32", 5, 3), (8, "f32", 96, 40), (8, "f16", 7, 5),
+                                         (8, "f16", 96, 384)])
+def test_prepared_planes_match_group_spectrum(T, dt, Dp, Cp):
+    say(f"prepare T={T} {dt} D'={Dp} C'={Cp}")
+    _, w, _ = make_layer_inputs(4, T * Cp, T * Dp, dt, seed=1, T=T, with_dy=False)
     Wh = eq.eqlin_prepare_weights(dev(w))
     tdt = torch.float32 if dt == "f32" else torch.float16
     buf = Wh.buf
-    off = eq.eqlin_prepared_transpose_offset(4 * Cp, 4 * Dp, tdt)
-    wf = decode_planes(host(buf[:off].view(tdt)), Dp, Cp, dt)
-    wb = decode_planes(host(buf[off:].view(tdt)), Cp, Dp, dt)
-    ref = oracle.kept_p4_planes(w.astype(np.float64))
+    off = eq.eqlin_prepared_transpose_offset(T * Cp, T * Dp, tdt, T)
+    wf = decode_planes(host(buf[:off].view(tdt)), Dp, Cp, dt, T)
+    wb = decode_planes(host(buf[off:].view(tdt)), Cp, Dp, dt, T)
+    ref = oracle.kept_planes(w.astype(np.float64))
     tol = 1e-6 if dt == "f32" else 1e-3
     assert rel_err(wf, ref) < tol
     conj = ref.copy()
-    conj[..., 3] = -conj[..., 3]
+    conj[..., 3::2] = -conj[..., 3::2]      # imaginary planes
     assert rel_err(wb, conj.transpose(1, 0, 2)) < tol
 
 
@@ -93,8 +110,16 @@ SMALL_SHAPES = {
 }
 
 
-def _forward_case(dt, N, C, D, seed=0):
-    X, w, _ = make_layer_inputs(N, C, D, dt, seed=seed, with_dy=False)
+SMALL_SHAPES_C8 = {
+    "f32": [(64, 64, 64), (1, 8, 8), (131, 24, 40), (1000, 160, 96), (257, 8 * 34, 8 * 70),
+            (333, 8 * 100, 8 * 65)],
+    "f16": [(64, 64, 64), (1, 8, 8), (131, 24, 40), (1000, 8 * 21, 8 * 13), (257, 8 * 34, 8 * 70),
+            (333, 8 * 100, 8 * 65)],
+}
+
+
+def _forward_case(dt, N, C, D, seed=0, T=4):
+    X, w, _ = make_layer_inputs(N, C, D, dt, seed=seed, T=T, with_dy=False)
     Wh = eq.eqlin_prepare_weights(dev(w))
     Y = eq.eqlin_forward(dev(X), Wh)
     return X, w, host(Y)
@@ -113,19 +138,33 @@ def test_forward_small_shapes_all_tiles(dt, tile, monkeypatch):
         assert err <= TOL[dt], (N, C, D, err)
 
 
+@pytest.mark.parametrize("tile", ["auto", "112211", "112221", "111221", "212211", "122211"])
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_forward_c8_small_shapes_all_tiles(dt, tile, monkeypatch):
+    if tile != "auto":
+        monkeypatch.setenv("EQLIN_FWD_TILE", tile)
+    for (N, C, D) in SMALL_SHAPES_C8[dt]:
+        say(f"forward C8 {dt} tile={tile} N={N} C={C} D={D}")
+        X, w, Y = _forward_case(dt, N, C, D, T=8)
+        err = rel_err(Y, oracle.forward_direct(X, w))
+        assert err <= TOL[dt], (N, C, D, err)
+
+
 def _sample_rows(N, rng, k=96):
     rows = set(range(8)) | set(range(N - 8, N))
     rows |= set(rng.choice(N, size=k, replace=False).tolist())
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("name,dt", [("tiny", "f32"), ("vitb_attn", "f32"), ("vitb_mlp", "f16"),
-                                     ("vith_mlp", "f32"), ("vith_mlp", "f16")])
-def test_forward_workloads(name, dt):
+@pytest.mark.parametrize("name,dt,T", [("tiny", "f32", 4), ("vitb_attn", "f32", 4), ("vitb_mlp", "f16", 4),
+                                       ("vith_mlp", "f32", 4), ("vith_mlp", "f16", 4), ("tiny", "f32", 8),
+                                       ("vitb_attn", "f32", 8), ("vitb_mlp", "f16", 8), ("vith_mlp", "f32", 8),
+                                       ("vith_mlp", "f16", 8)])
+def test_forward_workloads(name, dt, T):
     wl = WORKLOADS[name]
     for li, L in enumerate(wl.layers):
-        say(f"forward workload {name} {L.name} {dt} N={L.N} C={L.C} D={L.D}")
-        X, w, _ = make_layer_inputs(L.N, L.C, L.D, dt, seed=0, layer=li, with_dy=False)
+        say(f"forward workload {name} {L.name} {dt} T={T} N={L.N} C={L.C} D={L.D}")
+        X, w, _ = make_layer_inputs(L.N, L.C, L.D, dt, seed=0, layer=li, T=T, with_dy=False)
         Wh = eq.eqlin_prepare_weights(dev(w))
         Y = host(eq.eqlin_forward(dev(X), Wh))
         if L.N * L.C * L.D <= 12608 * 768 * 768:
@@ -145,11 +184,15 @@ BWD_SHAPES = {
 }
 
 
+BWD_SHAPES_C8 = [(64, 64, 64), (1, 8, 8), (77, 24, 40), (1000, 160, 96), (3001, 8 * 70, 8 * 130)]
+
+
+@pytest.mark.parametrize("T", [4, 8])
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-def test_backward_small_shapes(dt):
-    for (N, C, D) in BWD_SHAPES[dt]:
-        say(f"backward {dt} N={N} C={C} D={D}")
-        X, w, dY = make_layer_inputs(N, C, D, dt, seed=2)
+def test_backward_small_shapes(dt, T):
+    for (N, C, D) in (BWD_SHAPES[dt] if T == 4 else BWD_SHAPES_C8):
+        say(f"backward T={T} {dt} N={N} C={C} D={D}")
+        X, w, dY = make_layer_inputs(N, C, D, dt, seed=2, T=T)
         Wh = eq.eqlin_prepare_weights(dev(w))
         dX, dw = eq.eqlin_backward(dev(dY), dev(X), Wh)
         dXr, dwr = oracle.backward_direct(dY, X, w)
@@ -158,48 +201,52 @@ def test_backward_small_shapes(dt):
         assert e2 <= TOL[dt], ("dw", N, C, D, e2)
 
 
+@pytest.mark.parametrize("T", [4, 8])
 @pytest.mark.parametrize("dt", ["f16", "f32"])
-def test_backward_workload_vitb(dt):
+def test_backward_workload_vitb(dt, T):
     L = WORKLOADS["vitb_attn_bwd"].layers[0]
-    say(f"backward workload vitb_attn_bwd {dt} N={L.N} C={L.C} D={L.D}")
-    X, w, dY = make_layer_inputs(L.N, L.C, L.D, dt, seed=0)
+    say(f"backward workload vitb_attn_bwd {dt} T={T} N={L.N} C={L.C} D={L.D}")
+    X, w, dY = make_layer_inputs(L.N, L.C, L.D, dt, seed=0, T=T)
     Wh = eq.eqlin_prepare_weights(dev(w))
     dX, dw = eq.eqlin_backward(dev(dY), dev(X), Wh)
     e1 = rel_err(host(dX), oracle.dx_direct(dY, w))
-    e2 = rel_err(host(dw), oracle.dw_direct(dY, X))
+    e2 = rel_err(host(dw), oracle.dw_direct(dY, X, T))
     say(f"  dX rel err {e1:.3e}  dw rel err {e2:.3e}")
     assert e1 <= TOL[dt] and e2 <= TOL[dt]
 
 
-def test_backward_separate_entry_points_agree():
-    X, w, dY = make_layer_inputs(500, 64, 96, "f32", seed=4)
+@pytest.mark.parametrize("T", [4, 8])
+def test_backward_separate_entry_points_agree(T):
+    X, w, dY = make_layer_inputs(500, 64, 96, "f32", seed=4, T=T)
     Wh = eq.eqlin_prepare_weights(dev(w))
     dX, dw = eq.eqlin_backward(dev(dY), dev(X), Wh)
     dX2 = eq.eqlin_backward_dx(dev(dY), Wh)
-    dw2 = eq.eqlin_backward_dw(dev(dY), dev(X))
+    dw2 = eq.eqlin_backward_dw(dev(dY), dev(X), T=T)
     assert torch.equal(dX, dX2) and torch.equal(dw, dw2)
 
 
 # -------------------------------------------------------------- edge cases
 
+@pytest.mark.parametrize("T", [4, 8])
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-def test_empty_batch(dt):
+def test_empty_batch(dt, T):
     tdt = torch.float32 if dt == "f32" else torch.float16
-    _, w, _ = make_layer_inputs(1, 32, 48, dt, seed=5, with_dy=False)
+    _, w, _ = make_layer_inputs(1, 32, 48, dt, seed=5, T=T, with_dy=False)
     Wh = eq.eqlin_prepare_weights(dev(w))
     X = torch.empty((0, 32), dtype=tdt, device=DEV)
     dY = torch.empty((0, 48), dtype=tdt, device=DEV)
     assert eq.eqlin_forward(X, Wh).shape == (0, 48)
-    dw = torch.full((12, 8, 4), float("nan"), device=DEV)
+    dw = torch.full((48 // T, 32 // T, T), float("nan"), device=DEV)
     dX, dw = eq.eqlin_backward(dY, X, Wh, dw_out=dw)
     torch.cuda.synchronize()
     assert dX.shape == (0, 32)
     assert torch.count_nonzero(dw).item() == 0
 
 
+@pytest.mark.parametrize("T", [4, 8])
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-def test_determinism(dt):
-    X, w, dY = make_layer_inputs(2000, 256, 384, dt, seed=6)
+def test_determinism(dt, T):
+    X, w, dY = make_layer_inputs(2000, 256, 384, dt, seed=6, T=T)
     Wh = eq.eqlin_prepare_weights(dev(w))
     tX, tdY = dev(X), dev(dY)
     Y1 = eq.eqlin_forward(tX, Wh).clone()
@@ -210,11 +257,12 @@ def test_determinism(dt):
     assert torch.equal(Y1, Y2) and torch.equal(dX1, dX2) and torch.equal(dw1, dw2)
 
 
+@pytest.mark.parametrize("T", [4, 8])
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-def test_row_isolation(dt):
+def test_row_isolation(dt, T):
     # a NaN in row r of X may only reach row r of Y (checks tail masking and row mapping)
     N, C, D = 300, 128, 160
-    X, w, _ = make_layer_inputs(N, C, D, dt, seed=7, with_dy=False)
+    X, w, _ = make_layer_inputs(N, C, D, dt, seed=7, T=T, with_dy=False)
     Wh = eq.eqlin_prepare_weights(dev(w))
     Y0 = host(eq.eqlin_forward(dev(X), Wh))
     Xn = X.copy()
@@ -226,14 +274,15 @@ def test_row_isolation(dt):
     assert np.array_equal(Y1[~bad], Y0[~bad])
 
 
+@pytest.mark.parametrize("T", [4, 8])
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-def test_group_shift_equivariance(dt):
+def test_group_shift_equivariance(dt, T):
     N, C, D = 512, 256, 192
-    X, w, _ = make_layer_inputs(N, C, D, dt, seed=8, with_dy=False)
-    Xr = np.roll(X.reshape(N, C // 4, 4), 1, axis=2).reshape(N, C)
+    X, w, _ = make_layer_inputs(N, C, D, dt, seed=8, T=T, with_dy=False)
+    Xr = np.roll(X.reshape(N, C // T, T), 1, axis=2).reshape(N, C)
     Wh = eq.eqlin_prepare_weights(dev(w))
-    Y = host(eq.eqlin_forward(dev(X), Wh)).reshape(N, D // 4, 4)
-    Yr = host(eq.eqlin_forward(dev(Xr), Wh)).reshape(N, D // 4, 4)
+    Y = host(eq.eqlin_forward(dev(X), Wh)).reshape(N, D // T, T)
+    Yr = host(eq.eqlin_forward(dev(Xr), Wh)).reshape(N, D // T, T)
     assert rel_err(Yr, np.roll(Y, 1, axis=2)) <= TOL[dt]
 
 
@@ -253,13 +302,14 @@ def test_non_default_stream():
 
 # ------------------------------------------------- fused bias + GELU epilogue
 
+@pytest.mark.parametrize("T", [4, 8])
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 @pytest.mark.parametrize("with_bias,act", [(True, "none"), (False, "gelu"), (True, "gelu")])
-def test_forward_ex_bias_gelu(dt, with_bias, act):
-    for (N, C, D) in [(131, 8 * 3, 8 * 5), (1000, 160, 96), (333, 4 * 200, 4 * 130)]:
-        say(f"forward_ex {dt} bias={with_bias} act={act} N={N} C={C} D={D}")
-        X, w, _ = make_layer_inputs(N, C, D, dt, seed=13, with_dy=False)
-        b = (np.random.default_rng(14).standard_normal(D // 4)).astype(X.dtype) if with_bias else None
+def test_forward_ex_bias_gelu(dt, with_bias, act, T):
+    for (N, C, D) in [(131, 8 * 3, 8 * 5), (1000, 160, 96), (333, 8 * 100, 8 * 65)]:
+        say(f"forward_ex T={T} {dt} bias={with_bias} act={act} N={N} C={C} D={D}")
+        X, w, _ = make_layer_inputs(N, C, D, dt, seed=13, T=T, with_dy=False)
+        b = (np.random.default_rng(14).standard_normal(D // T)).astype(X.dtype) if with_bias else None
         Wh = eq.eqlin_prepare_weights(dev(w))
         Y = host(eq.eqlin_forward_ex(dev(X), Wh, dev(b) if with_bias else None, act))
         ref = oracle.forward_bias_act(X, w, b, act)
