@@ -1,4 +1,4 @@
-"""Benchmark of the p4 group-circulant linear layer on one MI355X.
+"""Benchmark of the group-circulant linear layer on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 for every layer of the workload, prepare the weight spectra, run the forward
@@ -10,10 +10,11 @@ The reported metric is the forward dense-equivalent throughput
 2*N*D*C / t_forward (the same N x D x C dense GEMM counts 2NDC FLOPs), summed
 over the workload's layers, with t_forward the forward kernel time measured by
 HIP events on the launch stream inside the timed steps.  The fraction of the
-MFMA peak counts the FLOPs the kernel executes: six real products of
-N x D/4 x C/4, i.e. 0.75 NDC.
+MFMA peak counts the FLOPs the kernel executes: for the p4 group (T = 4) six
+real products of N x D/4 x C/4, i.e. 0.75 NDC; for C8 (--group 8) fourteen of
+N x D/8 x C/8, i.e. 0.4375 NDC (in general 2NDC (2T - 2) / T^2).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dtype f32|f16]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dtype f32|f16] [--group 4|8]
 """
 from __future__ import annotations
 
@@ -41,6 +42,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="vitb_attn")
     p.add_argument("--dtype", default=None)
+    p.add_argument("--group", type=int, default=4, choices=(4, 8), help="cyclic group order T")
     p.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0 = enough to exceed 600 MB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
@@ -54,19 +56,32 @@ def parse():
     return p.parse_args()
 
 
-def profiled_traffic(workload, dt, kernel_name):
+def kernel_source_sha256():
+    """sha256 over the library's HIP sources and headers (sorted by name)."""
+    import hashlib
+    csrc = os.path.join(ROOT, "group_circulant_linear_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def profile_tag(workload, dt, T):
+    return f"{workload}_{dt}" + ("" if T == 4 else f"_c{T}")
+
+
+def profiled_traffic(tag, kernel_name):
     """HBM bytes per launch of `kernel_name` from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is no
-    summary for this workload or the kernel source changed since it was taken."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{dt}.json")
-    src = os.path.join(ROOT, "group_circulant_linear_amd", "csrc", "eqlin_kernels.hip")
+    summary for this workload or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{tag}.json")
     try:
         with open(path) as f:
             d = json.load(f)
-        with open(src, "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != d["source_sha256"]:
-                return None
+        if kernel_source_sha256() != d["source_sha256"]:
+            return None
         rows = [r for k, v in d["kernels"].items() if k.startswith(kernel_name) for r in v]
         return max(r["bytes"] for r in rows) if rows else None
     except (OSError, KeyError, ValueError):
@@ -117,17 +132,18 @@ def mlp_block(args):
     if len(wl.layers) != 2:
         raise SystemExit("--mlp-block needs a two-layer workload (vitb_mlp, vith_mlp)")
     dt = args.dtype or wl.dtypes[0]
+    T = args.group
     tdt = torch.float32 if dt == "f32" else torch.float16
     dev = torch.device("cuda:0")
     L1, L2 = wl.layers
-    X, w1, _ = make_layer_inputs(L1.N, L1.C, L1.D, dt, seed=0, layer=0, with_dy=False)
-    _, w2, _ = make_layer_inputs(8, L2.C, L2.D, dt, seed=0, layer=1, with_dy=False)
+    X, w1, _ = make_layer_inputs(L1.N, L1.C, L1.D, dt, seed=0, layer=0, T=T, with_dy=False)
+    _, w2, _ = make_layer_inputs(8, L2.C, L2.D, dt, seed=0, layer=1, T=T, with_dy=False)
     rng = np.random.default_rng(1)
     nsets = 3
     Xs = [torch.from_numpy(X).to(dev) for _ in range(nsets)]
     tw1, tw2 = torch.from_numpy(w1).to(dev), torch.from_numpy(w2).to(dev)
-    b1 = torch.from_numpy(rng.standard_normal(L1.D // 4).astype(X.dtype)).to(dev)
-    b2 = torch.from_numpy(rng.standard_normal(L2.D // 4).astype(X.dtype)).to(dev)
+    b1 = torch.from_numpy(rng.standard_normal(L1.D // T).astype(X.dtype)).to(dev)
+    b2 = torch.from_numpy(rng.standard_normal(L2.D // T).astype(X.dtype)).to(dev)
     W1, W2 = eqlin.eqlin_prepare_weights(tw1), eqlin.eqlin_prepare_weights(tw2)
     Hs = [torch.empty((L1.N, L1.D), dtype=tdt, device=dev) for _ in range(nsets)]
     Ys = [torch.empty((L1.N, L2.D), dtype=tdt, device=dev) for _ in range(nsets)]
@@ -137,7 +153,7 @@ def mlp_block(args):
         eqlin.eqlin_forward_ex(Hs[i % nsets], W2, b2, "none", out=Ys[i % nsets])
 
     D1, D2 = dense_weight(torch, tw1), dense_weight(torch, tw2)
-    db1, db2 = b1.repeat_interleave(4), b2.repeat_interleave(4)
+    db1, db2 = b1.repeat_interleave(T), b2.repeat_interleave(T)
     F = torch.nn.functional
 
     def dense_block(i):
@@ -159,7 +175,7 @@ def mlp_block(args):
     eq_us = timeit(eq_block, args.steps)
     dense_us = timeit(dense_block, args.steps)
     flops = 2.0 * L1.N * (L1.C * L1.D + L2.C * L2.D)
-    print(json.dumps({"mode": "mlp_block", "workload": wl.name, "dtype": dt,
+    print(json.dumps({"mode": "mlp_block", "workload": wl.name, "dtype": dt, "T": T,
                       "block": f"fc1 {L1.C}->{L1.D} +bias+GELU, fc2 {L2.C}->{L2.D} +bias, N={L1.N}",
                       "eq_us": round(eq_us, 2), "dense_us": round(dense_us, 2),
                       "speedup": round(dense_us / eq_us, 3),
@@ -183,6 +199,7 @@ def main():
 
     wl = WORKLOADS[args.workload]
     dt = args.dtype or wl.dtypes[0]
+    T = args.group
     tdt = torch.float32 if dt == "f32" else torch.float16
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -191,12 +208,12 @@ def main():
     # ---- inputs (host, seeded) -> HBM, rotating sets
     layers = []
     for li, L in enumerate(wl.layers):
-        X, w, dY = make_layer_inputs(L.N, L.C, L.D, dt, seed=0, layer=li)
+        X, w, dY = make_layer_inputs(L.N, L.C, L.D, dt, seed=0, layer=li, T=T)
         layers.append((L, X, w, dY))
     set_bytes = 0
     for (L, X, w, dY) in layers:
         es = X.itemsize
-        set_bytes += es * L.N * (2 * L.C + 2 * L.D) + eqlin.eqlin_backward_workspace_bytes(L.N, L.C, L.D, tdt)
+        set_bytes += es * L.N * (2 * L.C + 2 * L.D) + eqlin.eqlin_backward_workspace_bytes(L.N, L.C, L.D, tdt, T)
     nsets = args.sets or max(2, int(np.ceil(600e6 / set_bytes)))
 
     sets = []
@@ -206,11 +223,11 @@ def main():
             tX = torch.from_numpy(X).to(dev)
             tw = torch.from_numpy(w).to(dev)
             tdY = torch.from_numpy(dY).to(dev)
-            Wbuf = torch.empty(eqlin.eqlin_prepared_weight_bytes(L.C, L.D, tdt), dtype=torch.uint8, device=dev)
+            Wbuf = torch.empty(eqlin.eqlin_prepared_weight_bytes(L.C, L.D, tdt, T), dtype=torch.uint8, device=dev)
             Y = torch.empty((L.N, L.D), dtype=tdt, device=dev)
             dX = torch.empty((L.N, L.C), dtype=tdt, device=dev)
-            dw = torch.empty((L.D // 4, L.C // 4, 4), dtype=torch.float32, device=dev)
-            ws = torch.empty(max(1, eqlin.eqlin_backward_workspace_bytes(L.N, L.C, L.D, tdt)), dtype=torch.uint8,
+            dw = torch.empty((L.D // T, L.C // T, T), dtype=torch.float32, device=dev)
+            ws = torch.empty(max(1, eqlin.eqlin_backward_workspace_bytes(L.N, L.C, L.D, tdt, T)), dtype=torch.uint8,
                              device=dev)
             S.append(dict(L=L, X=tX, w=tw, dY=tdY, Wbuf=Wbuf, Y=Y, dX=dX, dw=dw, ws=ws))
         sets.append(S)
@@ -267,14 +284,15 @@ def main():
     fwd_flops = sum(2.0 * L.N * L.C * L.D for (L, _, _, _) in layers)
     fwd_us = sum(ph_us["forward"])
     value = fwd_flops / (fwd_us * 1e-6) / 1e12
-    exec_flops = 0.75 * sum(L.N * L.C * L.D for (L, _, _, _) in layers)
+    exec_frac = (2 * T - 2) / T ** 2          # executed MFMA FLOPs per dense-equivalent FLOP
+    exec_flops = 2.0 * exec_frac * sum(L.N * L.C * L.D for (L, _, _, _) in layers)
 
     # roofline of the forward kernel (one launch per layer; summed over layers)
     achieved = exec_flops / (fwd_us * 1e-6) / 1e12
     peak = PEAK_TFLOPS[dt]
     es_b = 4 if dt == "f32" else 2
-    alg_bytes = sum(es_b * L.N * (L.C + L.D) + es_b * L.C * L.D / 4 for (L, _, _, _) in layers)
-    traffic = profiled_traffic(wl.name, dt, "eqlin::fwd_kernel") if len(layers) == 1 else None
+    alg_bytes = sum(es_b * L.N * (L.C + L.D) + es_b * L.C * L.D / T for (L, _, _, _) in layers)
+    traffic = profiled_traffic(profile_tag(wl.name, dt, T), "eqlin::fwd_kernel") if len(layers) == 1 else None
     roofline = {"bound": "mfma", "kernel": "eqlin::fwd_kernel", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": (round(traffic) if traffic else None),
@@ -289,12 +307,12 @@ def main():
         for p in phases:
             d[f"{p}_us"] = round(ph_us[p][li], 2)
         d["fwd_tflops_dense_equiv"] = round(2 * nd / (ph_us["forward"][li] * 1e-6) / 1e12, 2)
-        d["fwd_mfma_frac"] = round(0.75 * nd / (ph_us["forward"][li] * 1e-6) / 1e12 / peak, 4)
+        d["fwd_mfma_frac"] = round(2 * exec_frac * nd / (ph_us["forward"][li] * 1e-6) / 1e12 / peak, 4)
         d["fwd_hbm_gbs_algorithmic"] = round(
-            (es * L.N * (L.C + L.D) + es * L.C * L.D / 4) / (ph_us["forward"][li] * 1e-6) / 1e9, 1)
+            (es * L.N * (L.C + L.D) + es * L.C * L.D / T) / (ph_us["forward"][li] * 1e-6) / 1e9, 1)
         if not args.forward_only:
             d["bwd_tflops_dense_equiv"] = round(4 * nd / (ph_us["backward"][li] * 1e-6) / 1e12, 2)
-            d["bwd_mfma_frac"] = round(1.5 * nd / (ph_us["backward"][li] * 1e-6) / 1e12 / peak, 4)
+            d["bwd_mfma_frac"] = round(4 * exec_frac * nd / (ph_us["backward"][li] * 1e-6) / 1e12 / peak, 4)
         per_layer.append(d)
 
     # dense GEMM comparator: F.linear on the pre-expanded weight, same dtype, same stream
@@ -353,7 +371,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
         "config": {"workload": wl.name, "description": wl.description, "dtype": dt,
                    "layers": [{"name": L.name, "N": L.N, "C": L.C, "D": L.D} for (L, _, _, _) in layers],
-                   "T": 4, "step": ("prepare+forward" if args.forward_only else "prepare+forward+dX+dw"),
+                   "T": T, "step": ("prepare+forward" if args.forward_only else "prepare+forward+dX+dw"),
                    "buffer_sets": nsets},
         "fwd_mfma_frac": round(achieved / peak, 4),
         "roofline": roofline,

@@ -66,8 +66,8 @@ struct TileShape {
 // on the ViT-B / ViT-H layer shapes.
 constexpr TileShape kP4F32Tiles[] = {{112211, 64, 64, 0.70}, {112221, 64, 64, 0.63}, {111221, 32, 64, 0.52}};
 constexpr TileShape kP4F16Tiles[] = {{212421, 128, 128, 0.24}, {112211, 64, 64, 0.20}, {111221, 32, 64, 0.13}};
-constexpr TileShape kC8F32Tiles[] = {{112211, 64, 64, 0.50}, {111221, 32, 64, 0.40}};
-constexpr TileShape kC8F16Tiles[] = {{112211, 64, 64, 0.15}, {111221, 32, 64, 0.10}};
+constexpr TileShape kC8F32Tiles[] = {{112211, 64, 64, 0.58}, {112221, 64, 64, 0.55}, {111221, 32, 64, 0.31}};
+constexpr TileShape kC8F16Tiles[] = {{122211, 64, 128, 0.115}, {112221, 64, 64, 0.105}, {212211, 128, 64, 0.10}};
 
 // Forward tile choice: workgroups are spread round-robin over the CUs, so a
 // CU's work is ceil(tiles / CUs) tiles; minimise that work divided by the
