@@ -57,6 +57,14 @@ __all__ = [
     "kept_planes",
     "forward_rows",
     "dw_entries",
+    "cyclic_table",
+    "p4m_table",
+    "p4m_irreps",
+    "dense_expand_group",
+    "forward_group",
+    "dx_group",
+    "dw_group",
+    "p4m_planes",
 ]
 
 
@@ -247,3 +255,139 @@ def forward_bias_act(X, w, bias=None, act: str = "none") -> np.ndarray:
     elif act != "none":
         raise ValueError(act)
     return Y
+
+
+# ---------------------------------------------------------------------------
+# Finite groups given by their multiplication (Cayley) table.
+#
+# The summary's method is specialised to p4; its "Limitations" section names
+# other groups (reflections) as future work without formulas.  The plain
+# reading for a group G of order T with elements 0..T-1 is the group
+# convolution that the cyclic case already is:
+#
+#     W[d'T + g, c'T + h] = w[d', c', h^-1 g]
+#     Y3[n, d', g] = sum_{c', h} w[d', c', h^-1 g] X3[n, c', h]
+#
+# (for C_T, h^-1 g = g - h, which is the circulant above).  table[i, j] is the
+# index of the product g_i g_j.
+
+def cyclic_table(T: int) -> np.ndarray:
+    """Cayley table of the cyclic group C_T: i * j = (i + j) mod T."""
+    i = np.arange(T)
+    return (i[:, None] + i[None, :]) % T
+
+
+def p4m_table() -> np.ndarray:
+    """Cayley table of p4m (the dihedral group of order 8).
+
+    Element index u = k + 4 m stands for r^k s^m: r the rotation by 90 degrees,
+    s a reflection, with s r s = r^-1.  Hence r^k1 s^m1 r^k2 s^m2 =
+    r^(k1 + (-1)^m1 k2) s^(m1 + m2).
+    """
+    t = np.empty((8, 8), dtype=np.int64)
+    for i in range(8):
+        k1, m1 = i % 4, i // 4
+        for j in range(8):
+            k2, m2 = j % 4, j // 4
+            t[i, j] = (k1 + (k2 if m1 == 0 else -k2)) % 4 + 4 * (m1 ^ m2)
+    return t
+
+
+def _inverse(table: np.ndarray) -> np.ndarray:
+    e = int(np.nonzero(np.all(table == np.arange(len(table))[None, :], axis=1))[0][0])   # identity row
+    return np.array([int(np.nonzero(table[i] == e)[0][0]) for i in range(len(table))])
+
+
+def dense_expand_group(w, table) -> np.ndarray:
+    """Dense D x C weight W[d'T + g, c'T + h] = w[d', c', h^-1 g], entry by entry."""
+    w = _f64(w)
+    Dp, Cp, T = w.shape
+    inv = _inverse(table)
+    W = np.empty((Dp * T, Cp * T), dtype=np.float64)
+    for g in range(T):
+        for h in range(T):
+            W[g::T, h::T] = w[:, :, table[inv[h], g]]
+    return W
+
+
+def forward_group(X, w, table) -> np.ndarray:
+    """Y3[n, d', g] = sum_u sum_c' w[d', c', u] X3[n, c', g u^-1] (u = h^-1 g)."""
+    X = _f64(X)
+    w = _f64(w)
+    Dp, Cp, T = w.shape
+    inv = _inverse(table)
+    X3 = _split_groups(X, T)
+    N = X.shape[0]
+    Y3 = np.zeros((N, Dp, T), dtype=np.float64)
+    for u in range(T):
+        src = [table[g, inv[u]] for g in range(T)]          # h = g u^-1
+        Xs = X3[:, :, src]                                  # Xs[n, c', g] = X3[n, c', g u^-1]
+        prod = Xs.transpose(0, 2, 1).reshape(N * T, Cp) @ w[:, :, u].T
+        Y3 += prod.reshape(N, T, Dp).transpose(0, 2, 1)
+    return Y3.reshape(N, Dp * T)
+
+
+def dx_group(dY, w, table) -> np.ndarray:
+    """dX = dY W:  dX3[n, c', h] = sum_u sum_d' w[d', c', u] dY3[n, d', h u]."""
+    dY = _f64(dY)
+    w = _f64(w)
+    Dp, Cp, T = w.shape
+    G3 = _split_groups(dY, T)
+    N = dY.shape[0]
+    dX3 = np.zeros((N, Cp, T), dtype=np.float64)
+    for u in range(T):
+        src = [table[h, u] for h in range(T)]               # g = h u
+        Gs = G3[:, :, src]
+        prod = Gs.transpose(0, 2, 1).reshape(N * T, Dp) @ w[:, :, u]
+        dX3 += prod.reshape(N, T, Cp).transpose(0, 2, 1)
+    return dX3.reshape(N, Cp * T)
+
+
+def dw_group(dY, X, table) -> np.ndarray:
+    """dw[d', c', u] = sum_n sum_h dY3[n, d', h u] X3[n, c', h]  (= d<dY, Y>/dw)."""
+    T = len(table)
+    G3 = _split_groups(_f64(dY), T)
+    X3 = _split_groups(_f64(X), T)
+    N, Dp, _ = G3.shape
+    Cp = X3.shape[1]
+    dw = np.empty((Dp, Cp, T), dtype=np.float64)
+    Xm = X3.transpose(0, 2, 1).reshape(N * T, Cp)           # [(n, h), c']
+    for u in range(T):
+        src = [table[h, u] for h in range(T)]
+        Gm = G3[:, :, src].transpose(1, 0, 2).reshape(Dp, N * T)   # [d', (n, h)] = dY3[n, d', h u]
+        dw[:, :, u] = Gm @ Xm
+    return dw
+
+
+def p4m_irreps():
+    """The irreducible real representations of p4m, element by element.
+
+    Four one-dimensional characters A1, A2, B1, B2 with r -> (1, 1, -1, -1) and
+    s -> (1, -1, 1, -1), and the two-dimensional representation E with
+    r -> [[0, -1], [1, 0]] (rotation by 90 degrees) and s -> diag(1, -1).
+    Returns (chars [8][4], E [8][2][2]) for the elements u = k + 4 m.
+    """
+    R = np.array([[0.0, -1.0], [1.0, 0.0]])
+    S = np.diag([1.0, -1.0])
+    chars = np.empty((8, 4))
+    E = np.empty((8, 2, 2))
+    for u in range(8):
+        k, m = u % 4, u // 4
+        chars[u] = [1.0, (-1.0) ** m, (-1.0) ** k, (-1.0) ** (k + m)]
+        E[u] = np.linalg.matrix_power(R, k) @ np.linalg.matrix_power(S, m)
+    return chars, E
+
+
+def p4m_planes(w) -> np.ndarray:
+    """Group Fourier transform of p4m signals by its definition, as 8 real planes.
+
+    f_hat(rho) = sum_g f(g) rho(g): the four characters, then the 2 x 2 block
+    of E row-major: (A1, A2, B1, B2, E00, E01, E10, E11), shape [..., 8].
+    With this convention the group convolution above becomes
+    Y_hat(rho) = X_hat(rho) w_hat(rho) per representation.
+    """
+    w = _f64(w)
+    if w.shape[-1] != 8:
+        raise ValueError("p4m signals have 8 values")
+    chars, E = p4m_irreps()
+    return np.concatenate([w @ chars, (w @ E.reshape(8, 4))], axis=-1)
