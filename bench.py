@@ -12,9 +12,10 @@ over the workload's layers, with t_forward the forward kernel time measured by
 HIP events on the launch stream inside the timed steps.  The fraction of the
 MFMA peak counts the FLOPs the kernel executes: for the p4 group (T = 4) six
 real products of N x D/4 x C/4, i.e. 0.75 NDC; for C8 (--group 8) fourteen of
-N x D/8 x C/8, i.e. 0.4375 NDC (in general 2NDC (2T - 2) / T^2).
+N x D/8 x C/8, i.e. 0.4375 NDC (in general 2NDC (2T - 2) / T^2); for p4m
+(--group p4m) twelve of N x D/8 x C/8, i.e. 0.375 NDC.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dtype f32|f16] [--group 4|8]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dtype f32|f16] [--group 4|8|p4m]
 """
 from __future__ import annotations
 
@@ -42,7 +43,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="vitb_attn")
     p.add_argument("--dtype", default=None)
-    p.add_argument("--group", type=int, default=4, choices=(4, 8), help="cyclic group order T")
+    p.add_argument("--group", default="4", choices=("4", "8", "p4m"),
+                   help="group: 4 (p4 rotations), 8 (cyclic C8) or p4m (dihedral, order 8)")
     p.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0 = enough to exceed 600 MB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
@@ -68,8 +70,16 @@ def kernel_source_sha256():
     return h.hexdigest()
 
 
-def profile_tag(workload, dt, T):
-    return f"{workload}_{dt}" + ("" if T == 4 else f"_c{T}")
+def group_args(group):
+    """(group argument for the binding, group order, executed MFMA FLOPs per dense-equivalent FLOP)."""
+    if group == "p4m":
+        return "p4m", 8, 12 / 64            # 4 characters + the 2 x 2 block: 12 of 64 real products
+    T = int(group)
+    return T, T, (2 * T - 2) / T ** 2       # cyclic: F0, F_{T/2} and T/2 - 1 complex frequencies
+
+
+def profile_tag(workload, dt, group):
+    return f"{workload}_{dt}" + {"4": "", "8": "_c8", "p4m": "_p4m"}[str(group)]
 
 
 def profiled_traffic(tag, kernel_name):
@@ -88,12 +98,10 @@ def profiled_traffic(tag, kernel_name):
         return None
 
 
-def dense_weight(torch, w):
-    """Dense D x C weight of the circulant blocks for the dense-GEMM comparator."""
-    Dp, Cp, T = w.shape
-    t = torch.arange(T, device=w.device)
-    idx = (t.view(T, 1) - t.view(1, T)) % T                  # idx[t, s] = (t - s) mod T
-    return w[:, :, idx].permute(0, 2, 1, 3).reshape(Dp * T, Cp * T).contiguous()
+def dense_weight(torch, w, group):
+    """Dense D x C weight of the group-circulant blocks for the dense-GEMM comparator."""
+    from group_circulant_linear_amd.module import dense_expansion
+    return dense_expansion(w, group).contiguous()
 
 
 def cpu_baseline(layers, budget_s=12.0):
@@ -132,7 +140,7 @@ def mlp_block(args):
     if len(wl.layers) != 2:
         raise SystemExit("--mlp-block needs a two-layer workload (vitb_mlp, vith_mlp)")
     dt = args.dtype or wl.dtypes[0]
-    T = args.group
+    G, T, _ = group_args(args.group)
     tdt = torch.float32 if dt == "f32" else torch.float16
     dev = torch.device("cuda:0")
     L1, L2 = wl.layers
@@ -144,7 +152,7 @@ def mlp_block(args):
     tw1, tw2 = torch.from_numpy(w1).to(dev), torch.from_numpy(w2).to(dev)
     b1 = torch.from_numpy(rng.standard_normal(L1.D // T).astype(X.dtype)).to(dev)
     b2 = torch.from_numpy(rng.standard_normal(L2.D // T).astype(X.dtype)).to(dev)
-    W1, W2 = eqlin.eqlin_prepare_weights(tw1), eqlin.eqlin_prepare_weights(tw2)
+    W1, W2 = eqlin.eqlin_prepare_weights(tw1, group=G), eqlin.eqlin_prepare_weights(tw2, group=G)
     Hs = [torch.empty((L1.N, L1.D), dtype=tdt, device=dev) for _ in range(nsets)]
     Ys = [torch.empty((L1.N, L2.D), dtype=tdt, device=dev) for _ in range(nsets)]
 
@@ -152,7 +160,7 @@ def mlp_block(args):
         eqlin.eqlin_forward_ex(Xs[i % nsets], W1, b1, "gelu", out=Hs[i % nsets])
         eqlin.eqlin_forward_ex(Hs[i % nsets], W2, b2, "none", out=Ys[i % nsets])
 
-    D1, D2 = dense_weight(torch, tw1), dense_weight(torch, tw2)
+    D1, D2 = dense_weight(torch, tw1, G), dense_weight(torch, tw2, G)
     db1, db2 = b1.repeat_interleave(T), b2.repeat_interleave(T)
     F = torch.nn.functional
 
@@ -175,7 +183,7 @@ def mlp_block(args):
     eq_us = timeit(eq_block, args.steps)
     dense_us = timeit(dense_block, args.steps)
     flops = 2.0 * L1.N * (L1.C * L1.D + L2.C * L2.D)
-    print(json.dumps({"mode": "mlp_block", "workload": wl.name, "dtype": dt, "T": T,
+    print(json.dumps({"mode": "mlp_block", "workload": wl.name, "dtype": dt, "group": str(args.group),
                       "block": f"fc1 {L1.C}->{L1.D} +bias+GELU, fc2 {L2.C}->{L2.D} +bias, N={L1.N}",
                       "eq_us": round(eq_us, 2), "dense_us": round(dense_us, 2),
                       "speedup": round(dense_us / eq_us, 3),
@@ -199,7 +207,7 @@ def main():
 
     wl = WORKLOADS[args.workload]
     dt = args.dtype or wl.dtypes[0]
-    T = args.group
+    G, T, exec_frac = group_args(args.group)
     tdt = torch.float32 if dt == "f32" else torch.float16
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -213,7 +221,7 @@ def main():
     set_bytes = 0
     for (L, X, w, dY) in layers:
         es = X.itemsize
-        set_bytes += es * L.N * (2 * L.C + 2 * L.D) + eqlin.eqlin_backward_workspace_bytes(L.N, L.C, L.D, tdt, T)
+        set_bytes += es * L.N * (2 * L.C + 2 * L.D) + eqlin.eqlin_backward_workspace_bytes(L.N, L.C, L.D, tdt, G)
     nsets = args.sets or max(2, int(np.ceil(600e6 / set_bytes)))
 
     sets = []
@@ -223,11 +231,11 @@ def main():
             tX = torch.from_numpy(X).to(dev)
             tw = torch.from_numpy(w).to(dev)
             tdY = torch.from_numpy(dY).to(dev)
-            Wbuf = torch.empty(eqlin.eqlin_prepared_weight_bytes(L.C, L.D, tdt, T), dtype=torch.uint8, device=dev)
+            Wbuf = torch.empty(eqlin.eqlin_prepared_weight_bytes(L.C, L.D, tdt, G), dtype=torch.uint8, device=dev)
             Y = torch.empty((L.N, L.D), dtype=tdt, device=dev)
             dX = torch.empty((L.N, L.C), dtype=tdt, device=dev)
             dw = torch.empty((L.D // T, L.C // T, T), dtype=torch.float32, device=dev)
-            ws = torch.empty(max(1, eqlin.eqlin_backward_workspace_bytes(L.N, L.C, L.D, tdt, T)), dtype=torch.uint8,
+            ws = torch.empty(max(1, eqlin.eqlin_backward_workspace_bytes(L.N, L.C, L.D, tdt, G)), dtype=torch.uint8,
                              device=dev)
             S.append(dict(L=L, X=tX, w=tw, dY=tdY, Wbuf=Wbuf, Y=Y, dX=dX, dw=dw, ws=ws))
         sets.append(S)
@@ -241,7 +249,7 @@ def main():
             ev = events[li] if events is not None else None
             if ev is not None:
                 ev["prepare"][0].record()
-            Wh = eqlin.eqlin_prepare_weights(b["w"], out=b["Wbuf"])
+            Wh = eqlin.eqlin_prepare_weights(b["w"], out=b["Wbuf"], group=G)
             if ev is not None:
                 ev["prepare"][1].record()
                 ev["forward"][0].record()
@@ -284,7 +292,6 @@ def main():
     fwd_flops = sum(2.0 * L.N * L.C * L.D for (L, _, _, _) in layers)
     fwd_us = sum(ph_us["forward"])
     value = fwd_flops / (fwd_us * 1e-6) / 1e12
-    exec_frac = (2 * T - 2) / T ** 2          # executed MFMA FLOPs per dense-equivalent FLOP
     exec_flops = 2.0 * exec_frac * sum(L.N * L.C * L.D for (L, _, _, _) in layers)
 
     # roofline of the forward kernel (one launch per layer; summed over layers)
@@ -292,7 +299,7 @@ def main():
     peak = PEAK_TFLOPS[dt]
     es_b = 4 if dt == "f32" else 2
     alg_bytes = sum(es_b * L.N * (L.C + L.D) + es_b * L.C * L.D / T for (L, _, _, _) in layers)
-    traffic = profiled_traffic(profile_tag(wl.name, dt, T), "eqlin::fwd_kernel") if len(layers) == 1 else None
+    traffic = profiled_traffic(profile_tag(wl.name, dt, args.group), "eqlin::fwd_kernel") if len(layers) == 1 else None
     roofline = {"bound": "mfma", "kernel": "eqlin::fwd_kernel", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": (round(traffic) if traffic else None),
@@ -322,7 +329,7 @@ def main():
         tot_f, tot_b = 0.0, 0.0
         for li, (L, X, w, dY) in enumerate(layers):
             b = sets[0][li]
-            Wd = dense_weight(torch, b["w"])
+            Wd = dense_weight(torch, b["w"], G)
             Xs = [sets[r][li]["X"] for r in range(nsets)]
             dYs = [sets[r][li]["dY"] for r in range(nsets)]
             Yd = torch.empty((L.N, L.D), dtype=tdt, device=dev)
@@ -371,7 +378,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
         "config": {"workload": wl.name, "description": wl.description, "dtype": dt,
                    "layers": [{"name": L.name, "N": L.N, "C": L.C, "D": L.D} for (L, _, _, _) in layers],
-                   "T": T, "step": ("prepare+forward" if args.forward_only else "prepare+forward+dX+dw"),
+                   "group": str(args.group), "T": T,
+                   "step": ("prepare+forward" if args.forward_only else "prepare+forward+dX+dw"),
                    "buffer_sets": nsets},
         "fwd_mfma_frac": round(achieved / peak, 4),
         "roofline": roofline,

@@ -21,16 +21,20 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Shape / dtype checks common to every entry point.  f16 rows of an odd
 // number of 4-value groups would break the 16-byte alignment of the loads.
+// T is the group code: 4, 8 (cyclic) or EQLIN_P4M (dihedral, order 8).
 int check_shape(int64_t N, int C, int D, int T, int dtype) {
+  static_assert(EQLIN_P4M == eqlin::kP4M, "group code");
   if (dtype != EQLIN_F32 && dtype != EQLIN_F16) return EQLIN_EINVAL;
-  if (T != 4 && T != 8) return EQLIN_ENOTSUP;
-  if (N < 0 || C <= 0 || D <= 0 || (C % T) != 0 || (D % T) != 0) return EQLIN_EINVAL;
-  if (dtype == EQLIN_F16 && T == 4 && (((C / 4) % 2) != 0 || ((D / 4) % 2) != 0)) return EQLIN_ENOTSUP;
+  if (T != 4 && T != 8 && T != EQLIN_P4M) return EQLIN_ENOTSUP;
+  const int O = eqlin::group_order(T);
+  if (N < 0 || C <= 0 || D <= 0 || (C % O) != 0 || (D % O) != 0) return EQLIN_EINVAL;
+  if (dtype == EQLIN_F16 && O == 4 && (((C / 4) % 2) != 0 || ((D / 4) % 2) != 0)) return EQLIN_ENOTSUP;
   return EQLIN_OK;
 }
 
-// Launchers of the group of order T (4 or 8, checked by check_shape).
-#define EQLIN_BY_T(T, call) ((T) == 4 ? eqlin::Launch<4>::call : eqlin::Launch<8>::call)
+// Launchers of group T (a code accepted by check_shape).
+#define EQLIN_BY_T(T, call) \
+  ((T) == 4 ? eqlin::Launch<4>::call : (T) == 8 ? eqlin::Launch<8>::call : eqlin::Launch<eqlin::kP4M>::call)
 
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return EQLIN_OK;
@@ -39,22 +43,22 @@ int hip_status(hipError_t e) {
 }
 
 // Prepared planes of one direction: rows x ceil(groups / SG) stage blocks of
-// 64 T bytes (T planes x 64 bytes).
-size_t plane_set_bytes(int rows, int groups, int T, int dtype) {
+// 64 O bytes (O planes x 64 bytes; O = group order).
+size_t plane_set_bytes(int rows, int groups, int O, int dtype) {
   const int sg = eqlin::stage_groups(dtype);
-  return static_cast<size_t>(rows) * static_cast<size_t>(cdiv(groups, sg)) * 64u * static_cast<size_t>(T);
+  return static_cast<size_t>(rows) * static_cast<size_t>(cdiv(groups, sg)) * 64u * static_cast<size_t>(O);
 }
 
-size_t transpose_offset(int C, int D, int T, int dtype) {
-  return (plane_set_bytes(D / T, C / T, T, dtype) + 255u) & ~size_t(255);
+size_t transpose_offset(int C, int D, int O, int dtype) {
+  return (plane_set_bytes(D / O, C / O, O, dtype) + 255u) & ~size_t(255);
 }
 
 // Buffer loads use 32-bit byte offsets inside one workgroup tile.
 constexpr int64_t kMaxTileBytes = int64_t(1) << 30;
 
-bool fwd_offsets_fit(int in_width, int T, int dtype) {
+bool fwd_offsets_fit(int in_width, int O, int dtype) {
   const int64_t row_bytes = int64_t(in_width) * elem_bytes(dtype);
-  const int64_t wrow_bytes = cdiv(in_width / T, eqlin::stage_groups(dtype)) * 64 * T;
+  const int64_t wrow_bytes = cdiv(in_width / O, eqlin::stage_groups(dtype)) * 64 * O;
   return 256 * row_bytes < kMaxTileBytes && 256 * wrow_bytes < kMaxTileBytes;
 }
 
@@ -78,6 +82,7 @@ int choose_fwd_tile(int T, int dtype, int64_t nrows, int mg) {
     if (EQLIN_BY_T(T, fwd_tile_known(t))) return t;
   }
   const bool f32 = dtype == EQLIN_F32;
+  // p4m has the same plane count and a similar product count as C8: same table
   const TileShape* tiles = T == 4 ? (f32 ? kP4F32Tiles : kP4F16Tiles) : (f32 ? kC8F32Tiles : kC8F16Tiles);
   const int ntiles = T == 4 ? (f32 ? int(sizeof(kP4F32Tiles) / sizeof(TileShape))
                                    : int(sizeof(kP4F16Tiles) / sizeof(TileShape)))
@@ -115,11 +120,11 @@ struct DwPlan {
   int nsplit;
 };
 
-DwPlan plan_dw(int64_t N, int C, int D, int T, int dtype) {
+DwPlan plan_dw(int64_t N, int C, int D, int O, int dtype) {
   DwPlan p{0, 0};
   if (N <= 0) return p;
   // a few 64 x 64 workgroups fit one CU; use at most two per CU in total
-  const int64_t tiles = cdiv(D / T, 64) * cdiv(C / T, 64);
+  const int64_t tiles = cdiv(D / O, 64) * cdiv(C / O, 64);
   const int64_t stage = eqlin::dw_rows_per_stage(dtype);
   const int64_t row_bytes = int64_t(C > D ? C : D) * elem_bytes(dtype);
   int64_t want = (2 * kNumCu) / tiles;
@@ -143,7 +148,7 @@ const char* eqlin_status_str(int status) {
   switch (status) {
     case EQLIN_OK: return "ok";
     case EQLIN_EINVAL: return "invalid argument";
-    case EQLIN_ENOTSUP: return "unsupported configuration (T must be 4 or 8; f16 with T = 4 needs even group counts)";
+    case EQLIN_ENOTSUP: return "unsupported configuration (T must be 4, 8 or EQLIN_P4M; f16 with T = 4 needs even group counts)";
     case EQLIN_EALIGN: return "data pointer not 16-byte aligned";
     case EQLIN_EWORKSPACE: return "workspace or prepared-weight buffer too small";
     case EQLIN_EHIP: return "HIP runtime error";
@@ -155,23 +160,26 @@ int eqlin_last_hip_error(void) { return g_last_hip_error; }
 
 size_t eqlin_prepared_weight_bytes(int C, int D, int T, int dtype) {
   if (check_shape(0, C, D, T, dtype) != EQLIN_OK) return 0;
-  return transpose_offset(C, D, T, dtype) + plane_set_bytes(C / T, D / T, T, dtype);
+  const int O = eqlin::group_order(T);
+  return transpose_offset(C, D, O, dtype) + plane_set_bytes(C / O, D / O, O, dtype);
 }
 
 size_t eqlin_prepared_transpose_offset(int C, int D, int T, int dtype) {
   if (check_shape(0, C, D, T, dtype) != EQLIN_OK) return 0;
-  return transpose_offset(C, D, T, dtype);
+  const int O = eqlin::group_order(T);
+  return transpose_offset(C, D, O, dtype);
 }
 
 int eqlin_prepare_weights(const void* w, int C, int D, int T, int dtype, void* W_hat, size_t W_hat_bytes,
                           void* stream) {
   int st = check_shape(0, C, D, T, dtype);
   if (st != EQLIN_OK) return st;
+  const int O = eqlin::group_order(T);
   if (!w || !W_hat) return EQLIN_EINVAL;
   if (!aligned16(w) || !aligned16(W_hat)) return EQLIN_EALIGN;
   if (W_hat_bytes < eqlin_prepared_weight_bytes(C, D, T, dtype)) return EQLIN_EWORKSPACE;
   char* base = static_cast<char*>(W_hat);
-  return hip_status(EQLIN_BY_T(T, prepare(dtype, w, base, base + transpose_offset(C, D, T, dtype), D / T, C / T,
+  return hip_status(EQLIN_BY_T(T, prepare(dtype, w, base, base + transpose_offset(C, D, O, dtype), D / O, C / O,
                                           static_cast<hipStream_t>(stream))));
 }
 
@@ -184,37 +192,40 @@ int eqlin_forward_ex(const void* X, int64_t N, int C, int D, int T, const void* 
                      void* Y, int dtype, void* stream) {
   int st = check_shape(N, C, D, T, dtype);
   if (st != EQLIN_OK) return st;
+  const int O = eqlin::group_order(T);
   if (act != EQLIN_ACT_NONE && act != EQLIN_ACT_GELU) return EQLIN_EINVAL;
   if (N == 0) return EQLIN_OK;
   if (!X || !W_hat || !Y) return EQLIN_EINVAL;
   if (!aligned16(X) || !aligned16(W_hat) || !aligned16(Y)) return EQLIN_EALIGN;
   if (bias && (reinterpret_cast<uintptr_t>(bias) % elem_bytes(dtype)) != 0) return EQLIN_EALIGN;
-  if (!fwd_offsets_fit(C, T, dtype)) return EQLIN_ENOTSUP;
-  const int tile = choose_fwd_tile(T, dtype, N, D / T);
-  return hip_status(EQLIN_BY_T(T, forward(dtype, tile, X, W_hat, Y, N, C / T, D / T, bias, act,
+  if (!fwd_offsets_fit(C, O, dtype)) return EQLIN_ENOTSUP;
+  const int tile = choose_fwd_tile(T, dtype, N, D / O);
+  return hip_status(EQLIN_BY_T(T, forward(dtype, tile, X, W_hat, Y, N, C / O, D / O, bias, act,
                                           static_cast<hipStream_t>(stream))));
 }
 
 size_t eqlin_backward_workspace_bytes(int64_t N, int C, int D, int T, int dtype) {
   if (check_shape(N, C, D, T, dtype) != EQLIN_OK) return 0;
-  const DwPlan p = plan_dw(N, C, D, T, dtype);
-  return static_cast<size_t>(p.nsplit) * static_cast<size_t>(T) * static_cast<size_t>(C / T) *
-         static_cast<size_t>(D / T) * sizeof(float);
+  const int O = eqlin::group_order(T);
+  const DwPlan p = plan_dw(N, C, D, O, dtype);
+  return static_cast<size_t>(p.nsplit) * static_cast<size_t>(O) * static_cast<size_t>(C / O) *
+         static_cast<size_t>(D / O) * sizeof(float);
 }
 
 int eqlin_backward_dx(const void* dY, int64_t N, int C, int D, int T, const void* W_hat, void* dX, int dtype,
                       void* stream) {
   int st = check_shape(N, C, D, T, dtype);
   if (st != EQLIN_OK) return st;
+  const int O = eqlin::group_order(T);
   if (N == 0) return EQLIN_OK;
   if (!dY || !W_hat || !dX) return EQLIN_EINVAL;
   if (!aligned16(dY) || !aligned16(W_hat) || !aligned16(dX)) return EQLIN_EALIGN;
-  if (!fwd_offsets_fit(D, T, dtype)) return EQLIN_ENOTSUP;
+  if (!fwd_offsets_fit(D, O, dtype)) return EQLIN_ENOTSUP;
   // dX = dY W: the forward kernel with the transposed, conjugated planes
   // (input groups D', output groups C').
-  const char* wb = static_cast<const char*>(W_hat) + transpose_offset(C, D, T, dtype);
-  const int tile = choose_fwd_tile(T, dtype, N, C / T);
-  return hip_status(EQLIN_BY_T(T, forward(dtype, tile, dY, wb, dX, N, D / T, C / T, nullptr, 0,
+  const char* wb = static_cast<const char*>(W_hat) + transpose_offset(C, D, O, dtype);
+  const int tile = choose_fwd_tile(T, dtype, N, C / O);
+  return hip_status(EQLIN_BY_T(T, forward(dtype, tile, dY, wb, dX, N, D / O, C / O, nullptr, 0,
                                           static_cast<hipStream_t>(stream))));
 }
 
@@ -222,13 +233,14 @@ int eqlin_backward_dw(const void* dY, const void* X, int64_t N, int C, int D, in
                       size_t workspace_bytes, int dtype, void* stream) {
   int st = check_shape(N, C, D, T, dtype);
   if (st != EQLIN_OK) return st;
+  const int O = eqlin::group_order(T);
   if (!dw) return EQLIN_EINVAL;
   if (N > 0 && (!dY || !X || !workspace)) return EQLIN_EINVAL;
   if (!aligned16(dw)) return EQLIN_EALIGN;
   if (N > 0 && (!aligned16(dY) || !aligned16(X) || !aligned16(workspace))) return EQLIN_EALIGN;
   if (workspace_bytes < eqlin_backward_workspace_bytes(N, C, D, T, dtype)) return EQLIN_EWORKSPACE;
-  const DwPlan p = plan_dw(N, C, D, T, dtype);
-  return hip_status(EQLIN_BY_T(T, dw(dtype, dY, X, static_cast<float*>(workspace), dw, N, D / T, C / T,
+  const DwPlan p = plan_dw(N, C, D, O, dtype);
+  return hip_status(EQLIN_BY_T(T, dw(dtype, dY, X, static_cast<float*>(workspace), dw, N, D / O, C / O,
                                      p.rows_per_split, p.nsplit, static_cast<hipStream_t>(stream))));
 }
 
@@ -236,12 +248,13 @@ int eqlin_backward(const void* dY, const void* X, int64_t N, int C, int D, int T
                    float* dw, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
   int st = check_shape(N, C, D, T, dtype);
   if (st != EQLIN_OK) return st;
+  const int O = eqlin::group_order(T);
   if (!dX && !dw) return EQLIN_EINVAL;
   // validate both halves before launching either
   if (dX && N > 0) {
     if (!dY || !W_hat) return EQLIN_EINVAL;
     if (!aligned16(dY) || !aligned16(W_hat) || !aligned16(dX)) return EQLIN_EALIGN;
-    if (!fwd_offsets_fit(D, T, dtype)) return EQLIN_ENOTSUP;
+    if (!fwd_offsets_fit(D, O, dtype)) return EQLIN_ENOTSUP;
   }
   if (dw) {
     if (N > 0 && (!dY || !X || !workspace)) return EQLIN_EINVAL;
@@ -251,10 +264,10 @@ int eqlin_backward(const void* dY, const void* X, int64_t N, int C, int D, int T
   }
   if (dX && dw && N > 0 && use_fused_backward()) {
     // one launch for dX and the dw partials (they share dY), then the finalize
-    const DwPlan p = plan_dw(N, C, D, T, dtype);
-    const char* wb = static_cast<const char*>(W_hat) + transpose_offset(C, D, T, dtype);
-    return hip_status(EQLIN_BY_T(T, bwd_fused(dtype, dY, X, wb, dX, static_cast<float*>(workspace), dw, N, D / T,
-                                              C / T, p.rows_per_split, p.nsplit, static_cast<hipStream_t>(stream))));
+    const DwPlan p = plan_dw(N, C, D, O, dtype);
+    const char* wb = static_cast<const char*>(W_hat) + transpose_offset(C, D, O, dtype);
+    return hip_status(EQLIN_BY_T(T, bwd_fused(dtype, dY, X, wb, dX, static_cast<float*>(workspace), dw, N, D / O,
+                                              C / O, p.rows_per_split, p.nsplit, static_cast<hipStream_t>(stream))));
   }
   if (dX) {
     st = eqlin_backward_dx(dY, N, C, D, T, W_hat, dX, dtype, stream);

@@ -1,8 +1,9 @@
 // Device code of the group-circulant (EQ-)linear layer for gfx950 (CDNA4):
 // group transforms, the matrix-core "complex core", the forward / dX tile,
 // the dw split-partial tile, the dw finalize and the weight preparation, all
-// templated on the storage type E (float or _Float16) and the cyclic group
-// size T (4: the p4 rotation group; 8: the cyclic group C8).
+// templated on the storage type E (float or _Float16) and the group G: 4 (the
+// p4 rotation group, cyclic of order 4), 8 (the cyclic group C8) or kP4M (the
+// dihedral group p4m of order 8).
 //
 // Method (Flash EQ-Linear technical summary, gist.science 2607.21271):
 //   * "Key insight": the weight is group-circulant, so the layer is a circular
@@ -14,17 +15,21 @@
 //     only 0, +-1 and the power-of-two rescales 1/4, 1/2 (adds and subtracts),
 //     and the contraction is six real matrix products: f0 (1), f2 (1) and the
 //     complex f1 (4: Re/Im cross terms).
-//   * "Limitations": the specialisation is to p4; other groups are future
-//     work.  C8 here follows the same route with the general real-signal DFT:
-//     real f0 and f4, complex f1..f3, 2 + 3 * 4 = 14 real products.
+//   * "Limitations": the specialisation is to p4; other groups (reflections
+//     among them) are future work.  C8 here follows the same route with the
+//     general real-signal DFT: real f0 and f4, complex f1..f3, 2 + 3 * 4 = 14
+//     real products.  p4m uses its irreducible representations: four 1-D and
+//     one 2-D, 4 + 8 = 12 real products.
 //   * "Implementation": fused dataflow (no intermediate global writes), Fourier
 //     fragments resident in registers / on-chip memory, shape-specialised
 //     tiles on the matrix cores.
 //
-// gfx950 mapping.  Work is expressed as one "complex-structured GEMM":
+// gfx950 mapping.  Work is expressed as one "structured GEMM":
 //   out_plane[m][n] = sum_k A_plane[m][k] (*) B_plane[n][k]
-// where (*) multiplies the real planes pointwise and the (Re, Im) plane pairs
-// as complex numbers.  Both operands are staged per pipeline stage into LDS as
+// where (*) is a fixed list of plane products (Grp<G>::kFwd / kDw): for a
+// cyclic group the real planes pointwise and the (Re, Im) plane pairs as
+// complex numbers, for p4m the 1-D planes pointwise and the 2 x 2 blocks as
+// matrices.  Both operands are staged per pipeline stage into LDS as
 // T planes [plane][row][k] with k contiguous in 64-byte rows whose four 16-byte
 // slots are XOR-swizzled (see swz_slot).  Every lane reads 16 bytes per plane
 // per 32x32 fragment: 4 fp32 k-values (four 32x32x2 f32 MFMAs) or 8 f16
@@ -35,6 +40,9 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
+
+#include "eqlin_kernels.h"
 
 namespace eqlin {
 
@@ -118,23 +126,51 @@ __device__ __forceinline__ void idft4(float f0, float f2, float f1r, float f1i, 
 
 // ------------------------------------------------------------------ groups
 //
-// A real group signal z[0..T-1] has T real Fourier degrees of freedom (the
-// spectrum F_k = sum_u z_u exp(-2 pi i k u / T) is conjugate symmetric), kept
+// Grp<G> describes one group: its order T (= number of real planes per group
+// channel), the forward transform dft (T values -> T planes), the inverse
+// idft, the adjoint (the spectrum of the transposed kernel u -> w(u^-1): the
+// conjugate for a cyclic group, the transposed 2 x 2 block for p4m), and the
+// plane products of the contraction.  A product {out, a, b, neg} accumulates
+// (neg ? -1 : 1) * A[a] * B[b] into plane out.  kFwd serves the forward and
+// dX passes (out = A * B per representation); kDw the dw pass, which needs
+// B * A (the same list for the commutative cyclic groups).  Every
+// accumulator's first product comes before any second one, so dependent
+// matrix-core operations on one accumulator are far apart.
+struct Prod {
+  int out, a, b;
+  bool neg;
+};
+
+template <int G>
+struct Grp;
+
+// Cyclic groups: a real signal z[0..T-1] has T real Fourier degrees of
+// freedom (F_k = sum_u z_u exp(-2 pi i k u / T) is conjugate symmetric), kept
 // as T planes in the order
 //   F_0, F_{T/2}, Re F_1, Im F_1, ..., Re F_{T/2-1}, Im F_{T/2-1}
 // (for T = 4: F0, F2, Re F1, Im F1).  idft maps any such planes back to the
 // real signal (1/T) sum_k F_k exp(+2 pi i k u / T) with F_{T-k} = conj F_k.
+__host__ __device__ constexpr bool imag_plane(int p) { return p >= 2 && (p & 1); }
+
 template <int T>
-struct Grp;
+__device__ __forceinline__ void conj_planes(float* f) {
+#pragma unroll
+  for (int p = 0; p < T; ++p)
+    if (imag_plane(p)) f[p] = -f[p];
+}
 
 template <>
 struct Grp<4> {
-  static constexpr int kPlanes = 4;
-  static constexpr int kProducts = 6;  // real products per (row, column, k)
+  static constexpr int kOrder = 4;
+  static constexpr int kProducts = 6;
+  static constexpr Prod kFwd[kProducts] = {{0, 0, 0, false}, {2, 2, 2, false}, {1, 1, 1, false},
+                                           {3, 2, 3, false}, {2, 3, 3, true},  {3, 3, 2, false}};
+  static constexpr const Prod* kDw = kFwd;
   __device__ __forceinline__ static void dft(const float* z, float* f) {
     dft4(z[0], z[1], z[2], z[3], f[0], f[1], f[2], f[3]);
   }
   __device__ __forceinline__ static void idft(const float* f, float* y) { idft4(f[0], f[1], f[2], f[3], y); }
+  __device__ __forceinline__ static void adjoint(float* f) { conj_planes<4>(f); }
 };
 
 // C8 by one radix-2 split: the even frequencies are the 4-point DFT of
@@ -146,10 +182,16 @@ struct Grp<4> {
 //   a1 = c/2 ((Re F1 - Im F1) - (Re F3 + Im F3))
 //   a3 = c/2 ((Re F3 - Im F3) - (Re F1 + Im F1))
 //   z_u = (s_u + a_u)/2,  z_{u+4} = (s_u - a_u)/2.
+// Planes: 0 F0, 1 F4, 2/3 F1, 4/5 F2, 6/7 F3.
 template <>
 struct Grp<8> {
-  static constexpr int kPlanes = 8;
+  static constexpr int kOrder = 8;
   static constexpr int kProducts = 14;
+  static constexpr Prod kFwd[kProducts] = {
+      {0, 0, 0, false}, {2, 2, 2, false}, {1, 1, 1, false}, {3, 2, 3, false}, {4, 4, 4, false},
+      {5, 4, 5, false}, {6, 6, 6, false}, {7, 6, 7, false}, {2, 3, 3, true},  {3, 3, 2, false},
+      {4, 5, 5, true},  {5, 5, 4, false}, {6, 7, 7, true},  {7, 7, 6, false}};
+  static constexpr const Prod* kDw = kFwd;
   static constexpr float kC = 0.70710678118654752f;
   __device__ __forceinline__ static void dft(const float* z, float* f) {
     float s[4], a[4];
@@ -178,9 +220,75 @@ struct Grp<8> {
       y[u + 4] = 0.5f * (s[u] - a[u]);
     }
   }
+  __device__ __forceinline__ static void adjoint(float* f) { conj_planes<8>(f); }
 };
 
-__host__ __device__ constexpr bool imag_plane(int p) { return p >= 2 && (p & 1); }
+// p4m, the symmetry group of the square: element u = k + 4m is r^k s^m (r the
+// rotation by 90 degrees, s a reflection, s r s = r^-1).  The group
+// convolution y(g) = sum_h x(h) w(h^-1 g) becomes y_hat(rho) = x_hat(rho)
+// w_hat(rho) for every irreducible representation rho, with
+// f_hat(rho) = sum_g f(g) rho(g).  The irreducible representations are four
+// characters A1, A2, B1, B2 (r -> 1, 1, -1, -1; s -> 1, -1, 1, -1) and the 2-D
+// representation E (r -> [[0, -1], [1, 0]], s -> diag(1, -1)).  All their
+// entries are 0 or +-1, so with p_k = z_k (rotations), q_k = z_{4+k}
+// (reflections), a = p0 + p2, b = p1 + p3, c = q0 + q2, d = q1 + q3 and
+// al = p0 - p2, be = p1 - p3, ga = q0 - q2, de = q1 - q3:
+//   A1 = a + b + c + d   A2 = a + b - c - d   B1 = a - b + c - d   B2 = a - b - c + d
+//   E00 = al + ga   E01 = de - be   E10 = be + de   E11 = al - ga
+// Planes: 0 A1, 1 A2, 2 B1, 3 B2, 4 E00, 5 E01, 6 E10, 7 E11.  Inverse
+// (Fourier inversion f(g) = 1/8 [sum_chi chi(g) f_chi + 2 tr(E(g)^T F)]):
+//   z_0 = P + Q + U   z_1 = P - Q + V   z_2 = P + Q - U   z_3 = P - Q - V
+//   z_4 = P' + Q' + U'  z_5 = P' - Q' + V'  z_6 = P' + Q' - U'  z_7 = P' - Q' - V'
+// with P = (A1 + A2)/8, Q = (B1 + B2)/8, P' = (A1 - A2)/8, Q' = (B1 - B2)/8,
+// U = (E00 + E11)/4, V = (E10 - E01)/4, U' = (E00 - E11)/4, V' = (E01 + E10)/4.
+// Products: the four characters pointwise and the 2 x 2 block as a matrix
+// product (8 real products).  dX uses the spectrum of w(u^-1), i.e. the 2 x 2
+// block transposed; dw_hat = x_hat^T dy_hat per representation.
+template <>
+struct Grp<kP4M> {
+  static constexpr int kOrder = 8;
+  static constexpr int kProducts = 12;
+  // out[ij] += A[ik] B[kj]
+  static constexpr Prod kFwd[kProducts] = {
+      {0, 0, 0, false}, {1, 1, 1, false}, {2, 2, 2, false}, {3, 3, 3, false}, {4, 4, 4, false}, {5, 4, 5, false},
+      {6, 6, 4, false}, {7, 6, 5, false}, {4, 5, 6, false}, {5, 5, 7, false}, {6, 7, 6, false}, {7, 7, 7, false}};
+  // out[ij] += B[ik] A[kj]
+  static constexpr Prod kDw[kProducts] = {
+      {0, 0, 0, false}, {1, 1, 1, false}, {2, 2, 2, false}, {3, 3, 3, false}, {4, 4, 4, false}, {5, 5, 4, false},
+      {6, 4, 6, false}, {7, 5, 6, false}, {4, 6, 5, false}, {5, 7, 5, false}, {6, 6, 7, false}, {7, 7, 7, false}};
+  __device__ __forceinline__ static void dft(const float* z, float* f) {
+    const float a = z[0] + z[2], b = z[1] + z[3], c = z[4] + z[6], d = z[5] + z[7];
+    const float al = z[0] - z[2], be = z[1] - z[3], ga = z[4] - z[6], de = z[5] - z[7];
+    const float ab = a + b, amb = a - b, cd = c + d, cmd = c - d;
+    f[0] = ab + cd;
+    f[1] = ab - cd;
+    f[2] = amb + cmd;
+    f[3] = amb - cmd;
+    f[4] = al + ga;
+    f[5] = de - be;
+    f[6] = be + de;
+    f[7] = al - ga;
+  }
+  __device__ __forceinline__ static void idft(const float* f, float* y) {
+    const float P = 0.125f * (f[0] + f[1]), Q = 0.125f * (f[2] + f[3]);
+    const float P2 = 0.125f * (f[0] - f[1]), Q2 = 0.125f * (f[2] - f[3]);
+    const float U = 0.25f * (f[4] + f[7]), V = 0.25f * (f[6] - f[5]);
+    const float U2 = 0.25f * (f[4] - f[7]), V2 = 0.25f * (f[5] + f[6]);
+    y[0] = (P + Q) + U;
+    y[1] = (P - Q) + V;
+    y[2] = (P + Q) - U;
+    y[3] = (P - Q) - V;
+    y[4] = (P2 + Q2) + U2;
+    y[5] = (P2 - Q2) + V2;
+    y[6] = (P2 + Q2) - U2;
+    y[7] = (P2 - Q2) - V2;
+  }
+  __device__ __forceinline__ static void adjoint(float* f) {
+    const float t = f[5];
+    f[5] = f[6];
+    f[6] = t;
+  }
+};
 
 // erf(z) by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
 // 7.1.26: for z >= 0, erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5)
@@ -247,7 +355,7 @@ __device__ __forceinline__ void store_group(E* dst, const float* y) {
 // T 16-byte pieces fetched in unit order (see Units) hold kVals whole groups
 // one after another: group v occupies values v*T .. v*T+T-1.  The transform
 // writes the T plane vectors pl[p] whose value v is plane p of group v.
-// kConj negates the imaginary planes (conjugate spectrum).
+// kConj applies the group's adjoint (conjugate / transposed spectrum).
 
 // f16, T = 4: group DFT of the two groups of one 16-byte piece (registers
 // z01 = (z0, z1), z23 = (z2, z3) of group 0 and z45 / z67 of group 1), written
@@ -295,10 +403,10 @@ __device__ __forceinline__ void dft4_f16_pair(uint32_t z01, uint32_t z23, uint32
   }
 }
 
-template <typename E, int T, bool kConj>
-__device__ __forceinline__ void pieces_to_planes(const u32x4 (&pc)[T], u32x4 (&pl)[T]) {
-  constexpr int V = Traits<E>::kVals;
-  if constexpr (sizeof(E) == 2 && T == 4) {
+template <typename E, int G, bool kConj>
+__device__ __forceinline__ void pieces_to_planes(const u32x4 (&pc)[Grp<G>::kOrder], u32x4 (&pl)[Grp<G>::kOrder]) {
+  constexpr int V = Traits<E>::kVals, T = Grp<G>::kOrder;
+  if constexpr (sizeof(E) == 2 && G == 4) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t p0, p2, p1r, p1i;
@@ -327,12 +435,8 @@ __device__ __forceinline__ void pieces_to_planes(const u32x4 (&pc)[T], u32x4 (&p
     float f[V][T];
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-      Grp<T>::dft(&z[v * T], f[v]);
-      if constexpr (kConj) {
-#pragma unroll
-        for (int p = 0; p < T; ++p)
-          if (imag_plane(p)) f[v][p] = -f[v][p];
-      }
+      Grp<G>::dft(&z[v * T], f[v]);
+      if constexpr (kConj) Grp<G>::adjoint(f[v]);
     }
 #pragma unroll
     for (int p = 0; p < T; ++p) {
@@ -348,21 +452,48 @@ __device__ __forceinline__ void pieces_to_planes(const u32x4 (&pc)[T], u32x4 (&p
   }
 }
 
-// --------------------------------------------------------- MFMA complex core
+// ----------------------------------------------------------- MFMA core
 //
-// One 16-byte slot per operand plane and fragment: real planes
-//   acc[0] += A0 B0,  acc[1] += A1 B1,
-// and for every (Re, Im) pair (r, i = r + 1):
-//   acc[r] += Ar Br - Ai Bi,   acc[i] += Ar Bi + Ai Br.
-// The first product of every accumulator is issued before any second one, so
-// that dependent matrix-core operations on one accumulator are far apart.
-template <typename E, int T, int FM, int FN>
+// One 16-byte slot per operand plane and fragment; the plane products of the
+// group's list (kDwRole: the dw list) run as MFMAs into the T accumulators.
+template <int G, bool kDwRole, int I>
+__host__ __device__ constexpr Prod product() {
+  return (kDwRole ? Grp<G>::kDw : Grp<G>::kFwd)[I];
+}
+
+template <int G, bool kDwRole, int FM, int FN, int... I>
+__device__ __forceinline__ void products_f32(std::integer_sequence<int, I...>,
+                                             f32x16 (&acc)[Grp<G>::kOrder][FM][FN],
+                                             const f32x4 (&af)[Grp<G>::kOrder][FM],
+                                             const f32x4 (&bf)[Grp<G>::kOrder][FN], int j, int fm, int fn) {
+  ((acc[product<G, kDwRole, I>().out][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+        product<G, kDwRole, I>().neg ? -af[product<G, kDwRole, I>().a][fm][j]
+                                     : af[product<G, kDwRole, I>().a][fm][j],
+        bf[product<G, kDwRole, I>().b][fn][j], acc[product<G, kDwRole, I>().out][fm][fn], 0, 0, 0)),
+   ...);
+}
+
+template <int G, bool kDwRole, int FM, int FN, int... I>
+__device__ __forceinline__ void products_f16(std::integer_sequence<int, I...>,
+                                             f32x16 (&acc)[Grp<G>::kOrder][FM][FN],
+                                             const f16x8 (&av)[Grp<G>::kOrder], const f16x8 (&nav)[Grp<G>::kOrder],
+                                             const f16x8 (&bv)[Grp<G>::kOrder], int fm, int fn) {
+  ((acc[product<G, kDwRole, I>().out][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+        product<G, kDwRole, I>().neg ? nav[product<G, kDwRole, I>().a] : av[product<G, kDwRole, I>().a],
+        bv[product<G, kDwRole, I>().b], acc[product<G, kDwRole, I>().out][fm][fn], 0, 0, 0)),
+   ...);
+}
+
+template <typename E, int G, bool kDwRole, int FM, int FN>
 struct Core;
 
-template <int T, int FM, int FN>
-struct Core<float, T, FM, FN> {
+template <int G, bool kDwRole, int FM, int FN>
+struct Core<float, G, kDwRole, FM, FN> {
+  static constexpr int T = Grp<G>::kOrder;
   __device__ __forceinline__ static void mma(f32x16 (&acc)[T][FM][FN], const u32x4 (&a)[T][FM],
                                              const u32x4 (&b)[T][FN]) {
+    // bit-cast whole vectors, then index (a bit-cast of one vector element
+    // would reinterpret the vector's first element)
     f32x4 af[T][FM], bf[T][FN];
 #pragma unroll
     for (int p = 0; p < T; ++p) {
@@ -372,79 +503,51 @@ struct Core<float, T, FM, FN> {
       for (int fn = 0; fn < FN; ++fn) bf[p][fn] = __builtin_bit_cast(f32x4, b[p][fn]);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
+      for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          // first products: 0, (r1, i1 interleaved with 1), r2, i2, ...
-          acc[0][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[0][fm][j], bf[0][fn][j], acc[0][fm][fn], 0, 0, 0);
-          acc[2][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[2][fm][j], bf[2][fn][j], acc[2][fm][fn], 0, 0, 0);
-          acc[1][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[1][fm][j], bf[1][fn][j], acc[1][fm][fn], 0, 0, 0);
-          acc[3][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[2][fm][j], bf[3][fn][j], acc[3][fm][fn], 0, 0, 0);
-#pragma unroll
-          for (int r = 4; r < T; r += 2) {
-            acc[r][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[r][fm][j], bf[r][fn][j], acc[r][fm][fn], 0, 0, 0);
-            acc[r + 1][fm][fn] =
-                __builtin_amdgcn_mfma_f32_32x32x2f32(af[r][fm][j], bf[r + 1][fn][j], acc[r + 1][fm][fn], 0, 0, 0);
-          }
-#pragma unroll
-          for (int r = 2; r < T; r += 2) {
-            acc[r][fm][fn] =
-                __builtin_amdgcn_mfma_f32_32x32x2f32(-af[r + 1][fm][j], bf[r + 1][fn][j], acc[r][fm][fn], 0, 0, 0);
-            acc[r + 1][fm][fn] =
-                __builtin_amdgcn_mfma_f32_32x32x2f32(af[r + 1][fm][j], bf[r][fn][j], acc[r + 1][fm][fn], 0, 0, 0);
-          }
-        }
-      }
-    }
+        for (int fn = 0; fn < FN; ++fn)
+          products_f32<G, kDwRole, FM, FN>(std::make_integer_sequence<int, Grp<G>::kProducts>{}, acc, af, bf, j,
+                                           fm, fn);
   }
 };
 
-template <int T, int FM, int FN>
-struct Core<_Float16, T, FM, FN> {
+template <int G, bool kDwRole, int FM, int FN>
+struct Core<_Float16, G, kDwRole, FM, FN> {
+  static constexpr int T = Grp<G>::kOrder;
   __device__ __forceinline__ static void mma(f32x16 (&acc)[T][FM][FN], const u32x4 (&a)[T][FM],
                                              const u32x4 (&b)[T][FN]) {
     constexpr u32x4 kSign = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
-      f16x8 av[T], nai[T];
+      // nav: the negated operands (only those named by a product are used)
+      f16x8 av[T], nav[T];
 #pragma unroll
       for (int p = 0; p < T; ++p) {
         av[p] = __builtin_bit_cast(f16x8, a[p][fm]);
-        if (imag_plane(p)) nai[p] = __builtin_bit_cast(f16x8, a[p][fm] ^ kSign);
+        nav[p] = __builtin_bit_cast(f16x8, a[p][fm] ^ kSign);
       }
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         f16x8 bv[T];
 #pragma unroll
         for (int p = 0; p < T; ++p) bv[p] = __builtin_bit_cast(f16x8, b[p][fn]);
-        acc[0][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[0], bv[0], acc[0][fm][fn], 0, 0, 0);
-        acc[2][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[2], bv[2], acc[2][fm][fn], 0, 0, 0);
-        acc[1][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[1], bv[1], acc[1][fm][fn], 0, 0, 0);
-        acc[3][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[2], bv[3], acc[3][fm][fn], 0, 0, 0);
-#pragma unroll
-        for (int r = 4; r < T; r += 2) {
-          acc[r][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[r], bv[r], acc[r][fm][fn], 0, 0, 0);
-          acc[r + 1][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[r], bv[r + 1], acc[r + 1][fm][fn], 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 2; r < T; r += 2) {
-          acc[r][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(nai[r + 1], bv[r + 1], acc[r][fm][fn], 0, 0, 0);
-          acc[r + 1][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[r + 1], bv[r], acc[r + 1][fm][fn], 0, 0, 0);
-        }
+        products_f16<G, kDwRole, FM, FN>(std::make_integer_sequence<int, Grp<G>::kProducts>{}, acc, av, nav, bv, fm,
+                                         fn);
       }
     }
   }
 };
 
 // Reads this lane's 16-byte operand slot of one chunk from every LDS plane
-// and runs the complex core.  a_lds / b_lds point at the lane's slot in plane
-// 0 of its first fragment row; plane p is p * a_plane further, fragment fm
-// 32 rows further.
-template <typename E, int T, int FM, int FN>
-__device__ __forceinline__ void mma_chunk(f32x16 (&acc)[T][FM][FN], const char* a_lds, int a_plane,
+// and runs the core.  a_lds / b_lds point at the lane's slot in plane 0 of its
+// first fragment row; plane p is p * a_plane further, fragment fm 32 rows
+// further.
+template <typename E, int G, bool kDwRole, int FM, int FN>
+__device__ __forceinline__ void mma_chunk(f32x16 (&acc)[Grp<G>::kOrder][FM][FN], const char* a_lds, int a_plane,
                                           const char* b_lds, int b_plane, int stride) {
+  constexpr int T = Grp<G>::kOrder;
   u32x4 a[T][FM], b[T][FN];
 #pragma unroll
   for (int p = 0; p < T; ++p) {
@@ -453,7 +556,7 @@ __device__ __forceinline__ void mma_chunk(f32x16 (&acc)[T][FM][FN], const char* 
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) b[p][fn] = ld16(b_lds + p * b_plane + fn * 32 * stride);
   }
-  Core<E, T, FM, FN>::mma(acc, a, b);
+  Core<E, G, kDwRole, FM, FN>::mma(acc, a, b);
 }
 
 // Instruction interleaving for one pipeline stage of fwd_kernel: spread the
@@ -461,9 +564,10 @@ __device__ __forceinline__ void mma_chunk(f32x16 (&acc)[T][FM][FN], const char* 
 // the next stage's transform and LDS writes between the MFMAs, so that one
 // wave keeps its matrix core busy while it prepares the next stage.
 // Masks: 0x008 MFMA, 0x100 DS read, 0x200 DS write, 0x020 VMEM read, 0x002 VALU.
-template <typename E, int T, int FM, int FN, int PA, int PB>
+template <typename E, int G, int FM, int FN, int PA, int PB>
 __device__ __forceinline__ void interleave_schedule() {
-  constexpr int kMfma = (sizeof(E) == 4 ? 4 : 1) * Grp<T>::kProducts * FM * FN * 2;
+  constexpr int T = Grp<G>::kOrder;
+  constexpr int kMfma = (sizeof(E) == 4 ? 4 : 1) * Grp<G>::kProducts * FM * FN * 2;
   constexpr int kDsRead = 2 * T * (FM + FN);
   constexpr int kVmem = T * (PA + PB);
   constexpr int kDsWrite = T * (PA + PB);
@@ -504,10 +608,11 @@ constexpr int fwd_lds_bytes() {
 // LDS footprint (two barriers per stage) so that more workgroups fit a CU.
 // PF (1 or 2) is the number of stages whose global loads are in flight in
 // registers ahead of the stage being transformed into LDS.
-template <typename E, int T, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED>
+template <typename E, int G, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED>
 __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __restrict__ in,
                                          const E* __restrict__ wp, E* __restrict__ out, int64_t nrows, int kg,
                                          int mg, int tiles_n, const E* __restrict__ bias, int act) {
+  constexpr int T = Grp<G>::kOrder;
   using U = Units<E, T>;
   constexpr int NT = 64 * WM * WN;
   constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
@@ -564,7 +669,7 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
       const int r = ps * RPP + rl;
       if (BM % RPP == 0 || r < BM) {
         u32x4 pl[T];
-        pieces_to_planes<E, T, false>(ra[sl][ps], pl);
+        pieces_to_planes<E, G, false>(ra[sl][ps], pl);
 #pragma unroll
         for (int p = 0; p < T; ++p) st16(buf + p * A_PLANE + r * STRIDE + swz_slot(r, q) * 16, pl[p]);
       }
@@ -606,12 +711,12 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
   // scheduler can interleave MFMAs with the transform, LDS writes and loads.
   auto step = [&](int ks, auto slot_next) {
     char* cur = lds + (NBUF == 2 ? (ks & 1) * BUF : 0);
-    mma_chunk<E, T, FM, FN>(acc, cur + a_frag + c0, A_PLANE, cur + b_frag + c0, B_PLANE, STRIDE);
-    mma_chunk<E, T, FM, FN>(acc, cur + a_frag + c1, A_PLANE, cur + b_frag + c1, B_PLANE, STRIDE);
+    mma_chunk<E, G, false, FM, FN>(acc, cur + a_frag + c0, A_PLANE, cur + b_frag + c0, B_PLANE, STRIDE);
+    mma_chunk<E, G, false, FM, FN>(acc, cur + a_frag + c1, A_PLANE, cur + b_frag + c1, B_PLANE, STRIDE);
     if constexpr (NBUF == 1) __syncthreads();   // every wave is done reading the only buffer
     store(lds + (NBUF == 2 ? ((ks + 1) & 1) * BUF : 0), slot_next);
     load(ks + 1 + PF, slot_next);
-    if constexpr (SCHED == 1 && NBUF == 2) interleave_schedule<E, T, FM, FN, PA, PB>();
+    if constexpr (SCHED == 1 && NBUF == 2) interleave_schedule<E, G, FM, FN, PA, PB>();
     __syncthreads();
   };
 
@@ -649,7 +754,7 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
           float f[T], y[T];
 #pragma unroll
           for (int p = 0; p < T; ++p) f[p] = acc[p][fm][fn][r];
-          Grp<T>::idft(f, y);
+          Grp<G>::idft(f, y);
           if (bias != nullptr) {
 #pragma unroll
             for (int t = 0; t < T; ++t) y[t] += bm;
@@ -673,19 +778,20 @@ constexpr int fwd_waves_per_simd() {
   return (T * FM * FN >= 16 || (T == 8 && sizeof(E) == 2)) ? 1 : 2;
 }
 
-template <typename E, int T, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED>
-__global__ void __launch_bounds__(64 * WM * WN, (fwd_waves_per_simd<E, T, FM, FN>()))
+template <typename E, int G, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED>
+__global__ void __launch_bounds__(64 * WM * WN, (fwd_waves_per_simd<E, Grp<G>::kOrder, FM, FN>()))
 fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ out,
            int64_t nrows, int kg, int mg, int tiles_n, const E* __restrict__ bias, int act) {
-  __shared__ __attribute__((aligned(16))) char lds[fwd_lds_bytes<E, T, FM, FN, WM, WN, NBUF>()];
-  fwd_tile<E, T, FM, FN, WM, WN, NBUF, PF, SCHED>(lds, xcd_logical_id(blockIdx.x, gridDim.x), in, wp, out, nrows,
+  __shared__ __attribute__((aligned(16))) char lds[fwd_lds_bytes<E, Grp<G>::kOrder, FM, FN, WM, WN, NBUF>()];
+  fwd_tile<E, G, FM, FN, WM, WN, NBUF, PF, SCHED>(lds, xcd_logical_id(blockIdx.x, gridDim.x), in, wp, out, nrows,
                                                   kg, mg, tiles_n, bias, act);
 }
 
 // ============================================================ dw partials
 //
-// P_k[m][n] = sum_rows G_k[row][m] conj(Xhat_k[row][n])   (m = d', n = c')
-// over the rows of one split; the T planes are written to
+// P_k[m][n] = sum_rows G_k[row][m] conj(Xhat_k[row][n])   (m = d', n = c';
+// for p4m per representation Xhat^T G: the adjoint of Xhat and the dw product
+// list) over the rows of one split; the T planes are written to
 // ws[split][plane][mg][ng] (float32).  Tiles 64 x 64, one 32 x 32 fragment
 // per wave and plane.  The k axis is the row axis: thread (unit column pc,
 // row block rq) loads KV consecutive rows of one unit (kGroupsPerUnit groups),
@@ -697,10 +803,11 @@ constexpr int dw_lds_bytes() {
   return NBUF * 2 * T * 64 * kRowBytes;
 }
 
-template <typename E, int T, int NBUF>
+template <typename E, int G, int NBUF>
 __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restrict__ dy, const E* __restrict__ x,
                                         float* __restrict__ ws, int64_t nrows, int mg, int ng,
                                         int64_t rows_per_split, int tiles_m, int tiles_n) {
+  constexpr int T = Grp<G>::kOrder;
   using U = Units<E, T>;
   constexpr int GPU = U::kGroupsPerUnit, PPU = U::kPiecesPerUnit;
   constexpr int PR = 64 / GPU;                     // units per tile row (64 groups)
@@ -767,12 +874,8 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
       }
 #pragma unroll
       for (int e = 0; e < GPU; ++e) {
-        Grp<T>::dft(&z[e * T], f[v][e]);
-        if constexpr (kConj) {
-#pragma unroll
-          for (int p = 0; p < T; ++p)
-            if (imag_plane(p)) f[v][e][p] = -f[v][e][p];
-        }
+        Grp<G>::dft(&z[e * T], f[v][e]);
+        if constexpr (kConj) Grp<G>::adjoint(f[v][e]);
       }
     }
 #pragma unroll
@@ -819,8 +922,8 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
   }
   for (int st = 0; st < nstages; ++st) {
     char* cur = lds + (NBUF == 2 ? (st & 1) * BUF : 0);
-    mma_chunk<E, T, 1, 1>(acc, cur + a_frag + c0, PLANE, cur + b_frag + c0, PLANE, STRIDE);
-    mma_chunk<E, T, 1, 1>(acc, cur + a_frag + c1, PLANE, cur + b_frag + c1, PLANE, STRIDE);
+    mma_chunk<E, G, true, 1, 1>(acc, cur + a_frag + c0, PLANE, cur + b_frag + c0, PLANE, STRIDE);
+    mma_chunk<E, G, true, 1, 1>(acc, cur + a_frag + c1, PLANE, cur + b_frag + c1, PLANE, STRIDE);
     if (st + 1 < nstages) {
       if constexpr (NBUF == 1) __syncthreads();   // every wave is done reading the only buffer
       store(lds + (NBUF == 2 ? ((st + 1) & 1) * BUF : 0));
@@ -849,12 +952,12 @@ constexpr int bwd_waves_per_simd() {
   return T == 4 ? 2 : 1;
 }
 
-template <typename E, int T>
-__global__ void __launch_bounds__(kThreads, bwd_waves_per_simd<T>())
+template <typename E, int G>
+__global__ void __launch_bounds__(kThreads, bwd_waves_per_simd<Grp<G>::kOrder>())
 dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __restrict__ ws,
                   int64_t nrows, int mg, int ng, int64_t rows_per_split, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) char lds[dw_lds_bytes<T, kDwBufs>()];
-  dw_tile<E, T, kDwBufs>(lds, xcd_logical_id(blockIdx.x, gridDim.x), dy, x, ws, nrows, mg, ng, rows_per_split,
+  __shared__ __attribute__((aligned(16))) char lds[dw_lds_bytes<Grp<G>::kOrder, kDwBufs>()];
+  dw_tile<E, G, kDwBufs>(lds, xcd_logical_id(blockIdx.x, gridDim.x), dy, x, ws, nrows, mg, ng, rows_per_split,
                          tiles_m, tiles_n);
 }
 
@@ -863,12 +966,13 @@ dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __re
 // Both roles read dY; running them in one grid lets the dispatcher fill the
 // tail of one role with work of the other.  ndw_pad is a multiple of 8, so
 // each role keeps its own XCD-aware numbering.
-template <typename E, int T, int SCHED>
-__global__ void __launch_bounds__(kThreads, bwd_waves_per_simd<T>())
+template <typename E, int G, int SCHED>
+__global__ void __launch_bounds__(kThreads, bwd_waves_per_simd<Grp<G>::kOrder>())
 bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E* __restrict__ wb,
                  E* __restrict__ dx, float* __restrict__ ws, int64_t nrows, int dg, int cg,
                  int64_t rows_per_split, int dw_tiles_m, int dw_tiles_n, int64_t ndw, int64_t ndw_pad,
                  int dx_tiles_n) {
+  constexpr int T = Grp<G>::kOrder;
   constexpr int kFwd = fwd_lds_bytes<E, T, 1, 1, 2, 2, kBwdFwdBufs>();
   constexpr int kDw = dw_lds_bytes<T, kDwBufs>();
   __shared__ __attribute__((aligned(16))) char lds[kFwd > kDw ? kFwd : kDw];
@@ -876,10 +980,10 @@ bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E* __r
   if (b < ndw_pad) {
     const int64_t lid = xcd_logical_id(b, ndw_pad);
     if (lid < ndw)
-      dw_tile<E, T, kDwBufs>(lds, lid, dy, x, ws, nrows, dg, cg, rows_per_split, dw_tiles_m, dw_tiles_n);
+      dw_tile<E, G, kDwBufs>(lds, lid, dy, x, ws, nrows, dg, cg, rows_per_split, dw_tiles_m, dw_tiles_n);
   } else {
     const int64_t nb = gridDim.x - ndw_pad;
-    fwd_tile<E, T, 1, 1, 2, 2, kBwdFwdBufs, kBwdFwdPrefetch, SCHED>(lds, xcd_logical_id(b - ndw_pad, nb), dy, wb,
+    fwd_tile<E, G, 1, 1, 2, 2, kBwdFwdBufs, kBwdFwdPrefetch, SCHED>(lds, xcd_logical_id(b - ndw_pad, nb), dy, wb,
                                                                      dx, nrows, dg, cg, dx_tiles_n, nullptr, 0);
   }
 }
@@ -889,9 +993,10 @@ bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E* __r
 // 256-thread block sums plane p of one of 256/T consecutive entries; the T
 // plane sums meet in LDS and one thread per entry applies the inverse DFT.
 // nsplit == 0 writes zeros.
-template <int T>
+template <int G>
 __global__ void __launch_bounds__(kThreads)
 dw_finalize_kernel(const float* __restrict__ ws, float* __restrict__ dw, int mg, int ng, int nsplit) {
+  constexpr int T = Grp<G>::kOrder;
   constexpr int EB = kThreads / T;
   __shared__ float part[T][EB];
   const int64_t plane = (int64_t)mg * ng;
@@ -918,7 +1023,7 @@ dw_finalize_kernel(const float* __restrict__ ws, float* __restrict__ dw, int mg,
     float f[T], y[T];
 #pragma unroll
     for (int k = 0; k < T; ++k) f[k] = part[k][e];
-    Grp<T>::idft(f, y);
+    Grp<G>::idft(f, y);
     store_group<float, T>(dw + idx * T, y);
   }
 }
@@ -931,13 +1036,14 @@ dw_finalize_kernel(const float* __restrict__ ws, float* __restrict__ dw, int mg,
 // slot order fwd_kernel's loaders produce for the transformed input) and
 // groups past the end are zero.
 //   forward planes:   row = d', groups = c',  spectrum of w[d'][c'][.]
-//   transpose planes: row = c', groups = d',  conjugate spectrum of w[d'][c'][.]
-// The second set is the spectrum of the transposed, group-reversed weight
-// (a conjugate), used by the dX pass.
-template <typename E, int T, bool kTranspose>
+//   transpose planes: row = c', groups = d',  adjoint spectrum of w[d'][c'][.]
+// The second set is the spectrum of the transposed weight (u -> w(u^-1): a
+// conjugate for cyclic groups, the transposed 2 x 2 block for p4m), used by
+// the dX pass.
+template <typename E, int G, bool kTranspose>
 __global__ void __launch_bounds__(kThreads)
 prepare_kernel(const E* __restrict__ w, E* __restrict__ dst, int mg, int ng) {
-  constexpr int SG = Traits<E>::kStageGroups;
+  constexpr int SG = Traits<E>::kStageGroups, T = Grp<G>::kOrder;
   const int rows = kTranspose ? ng : mg;
   const int kgr = kTranspose ? mg : ng;
   const int nks = (kgr + SG - 1) / SG;
@@ -956,12 +1062,8 @@ prepare_kernel(const E* __restrict__ w, E* __restrict__ dst, int mg, int ng) {
     float z[T];
 #pragma unroll
     for (int u = 0; u < T; ++u) z[u] = (float)src[u];
-    Grp<T>::dft(z, f);
-    if (kTranspose) {
-#pragma unroll
-      for (int p = 0; p < T; ++p)
-        if (imag_plane(p)) f[p] = -f[p];
-    }
+    Grp<G>::dft(z, f);
+    if (kTranspose) Grp<G>::adjoint(f);
   }
   E* o = dst + (row * nks + ks) * T * SG + s;
 #pragma unroll
@@ -972,7 +1074,7 @@ prepare_kernel(const E* __restrict__ w, E* __restrict__ dst, int mg, int ng) {
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-template <typename E, int T, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED>
+template <typename E, int G, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED>
 hipError_t launch_fwd_s(const void* in, const void* wp, void* out, int64_t nrows, int kg, int mg,
                         const void* bias, int act, hipStream_t s) {
   constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
@@ -981,33 +1083,35 @@ hipError_t launch_fwd_s(const void* in, const void* wp, void* out, int64_t nrows
   const int64_t grid = tiles_m * tiles_n;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_kernel<E, T, FM, FN, WM, WN, NBUF, PF, SCHED>), dim3((unsigned)grid), dim3(64 * WM * WN),
+  hipLaunchKernelGGL((fwd_kernel<E, G, FM, FN, WM, WN, NBUF, PF, SCHED>), dim3((unsigned)grid), dim3(64 * WM * WN),
                      0, s, static_cast<const E*>(in), static_cast<const E*>(wp), static_cast<E*>(out), nrows, kg, mg,
                      tiles_n, static_cast<const E*>(bias), act);
   return hipGetLastError();
 }
 
-template <typename E, int T>
+template <typename E, int G>
 hipError_t launch_dw_t(const void* dy, const void* x, float* ws, float* dw, int64_t nrows, int mg, int ng,
                        int64_t rows_per_split, int nsplit, hipStream_t s) {
+  constexpr int T = Grp<G>::kOrder;
   const int tiles_m = (int)cdiv(mg, 64), tiles_n = (int)cdiv(ng, 64);
   if (nsplit > 0) {
     const int64_t grid = (int64_t)tiles_m * tiles_n * nsplit;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((dw_partial_kernel<E, T>), dim3((unsigned)grid), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((dw_partial_kernel<E, G>), dim3((unsigned)grid), dim3(kThreads), 0, s,
                        static_cast<const E*>(dy), static_cast<const E*>(x), ws, nrows, mg, ng, rows_per_split,
                        tiles_m, tiles_n);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int64_t fgrid = cdiv((int64_t)mg * ng, kThreads / T);
-  hipLaunchKernelGGL((dw_finalize_kernel<T>), dim3((unsigned)fgrid), dim3(kThreads), 0, s, ws, dw, mg, ng, nsplit);
+  hipLaunchKernelGGL((dw_finalize_kernel<G>), dim3((unsigned)fgrid), dim3(kThreads), 0, s, ws, dw, mg, ng, nsplit);
   return hipGetLastError();
 }
 
-template <typename E, int T>
+template <typename E, int G>
 hipError_t launch_bwd_fused_t(const void* dy, const void* x, const void* wb, void* dx, float* ws, float* dw,
                               int64_t nrows, int dg, int cg, int64_t rows_per_split, int nsplit, hipStream_t s) {
+  constexpr int T = Grp<G>::kOrder;
   const int dw_tiles_m = (int)cdiv(dg, 64), dw_tiles_n = (int)cdiv(cg, 64);
   const int64_t ndw = (int64_t)dw_tiles_m * dw_tiles_n * nsplit;
   const int64_t ndw_pad = cdiv(ndw, 8) * 8;
@@ -1016,7 +1120,7 @@ hipError_t launch_bwd_fused_t(const void* dy, const void* x, const void* wb, voi
   const int64_t grid = ndw_pad + ndx;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (grid > 0) {
-    hipLaunchKernelGGL((bwd_fused_kernel<E, T, 1>), dim3((unsigned)grid), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((bwd_fused_kernel<E, G, 1>), dim3((unsigned)grid), dim3(kThreads), 0, s,
                        static_cast<const E*>(dy), static_cast<const E*>(x), static_cast<const E*>(wb),
                        static_cast<E*>(dx), ws, nrows, dg, cg, rows_per_split, dw_tiles_m, dw_tiles_n, ndw, ndw_pad,
                        dx_tiles_n);
@@ -1024,17 +1128,17 @@ hipError_t launch_bwd_fused_t(const void* dy, const void* x, const void* wb, voi
     if (e != hipSuccess) return e;
   }
   const int64_t fgrid = cdiv((int64_t)dg * cg, kThreads / T);
-  hipLaunchKernelGGL((dw_finalize_kernel<T>), dim3((unsigned)fgrid), dim3(kThreads), 0, s, ws, dw, dg, cg, nsplit);
+  hipLaunchKernelGGL((dw_finalize_kernel<G>), dim3((unsigned)fgrid), dim3(kThreads), 0, s, ws, dw, dg, cg, nsplit);
   return hipGetLastError();
 }
 
-template <typename E, int T>
+template <typename E, int G>
 hipError_t launch_prepare_t(const void* w, void* wf, void* wb, int mg, int ng, hipStream_t s) {
   constexpr int SG = Traits<E>::kStageGroups;
   const int64_t nf = (int64_t)mg * cdiv(ng, SG) * SG, nb = (int64_t)ng * cdiv(mg, SG) * SG;
-  hipLaunchKernelGGL((prepare_kernel<E, T, false>), dim3((unsigned)cdiv(nf, kThreads)), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((prepare_kernel<E, G, false>), dim3((unsigned)cdiv(nf, kThreads)), dim3(kThreads), 0, s,
                      static_cast<const E*>(w), static_cast<E*>(wf), mg, ng);
-  hipLaunchKernelGGL((prepare_kernel<E, T, true>), dim3((unsigned)cdiv(nb, kThreads)), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((prepare_kernel<E, G, true>), dim3((unsigned)cdiv(nb, kThreads)), dim3(kThreads), 0, s,
                      static_cast<const E*>(w), static_cast<E*>(wb), mg, ng);
   return hipGetLastError();
 }

@@ -11,10 +11,15 @@ namespace eqlin {
 // 2) is the number of LDS stage buffers and PF (1 or 2) the number of stages
 // of global loads in flight in registers.
 //
-// Launchers of the cyclic group of order T, instantiated for T = 4 (the p4
-// rotation group) and T = 8 (C8).  dtype 0 = float32, 1 = float16; kg / mg /
-// dg / cg are group-channel counts (channels / T).
-template <int T>
+// Group codes: 4 and 8 are the cyclic groups of that order (4: the p4
+// rotation group), kP4M the dihedral group p4m of order 8.
+constexpr int kP4M = 108;
+inline int group_order(int g) { return g == kP4M ? 8 : g; }
+
+// Launchers of group G, instantiated for G = 4, 8 and kP4M.  dtype 0 =
+// float32, 1 = float16; kg / mg / dg / cg are group-channel counts
+// (channels / group order).
+template <int G>
 struct Launch {
   static bool fwd_tile_known(int tile);
   // bias: nullable, one storage-dtype value per output group; act: 0 none, 1 GELU (erf)
@@ -41,6 +46,7 @@ struct Launch {
   template <> hipError_t Launch<T>::prepare(int, const void*, void*, void*, int, int, hipStream_t);
 EQLIN_DECLARE_LAUNCH(4)
 EQLIN_DECLARE_LAUNCH(8)
+EQLIN_DECLARE_LAUNCH(kP4M)
 #undef EQLIN_DECLARE_LAUNCH
 
 inline int stage_groups(int dtype) { return dtype == 0 ? 16 : 32; }       // group channels per pipeline stage

@@ -18,7 +18,20 @@ import torch
 from .build import LIB, INCLUDE
 
 T_P4 = 4
-GROUP_ORDERS = (4, 8)   # cyclic groups the library implements (p4 rotations and C8)
+EQLIN_P4M = 108         # group code of p4m (dihedral, order 8); 4 and 8 are the cyclic groups
+GROUP_CODES = {"p4": 4, "c4": 4, "c8": 8, "p4m": EQLIN_P4M}
+
+
+def group_code(group) -> int:
+    """Group code for the C ABI's T argument from 4, 8, EQLIN_P4M or a name."""
+    code = GROUP_CODES.get(group, group) if isinstance(group, str) else int(group)
+    if code not in (4, 8, EQLIN_P4M):
+        raise ValueError(f"unsupported group {group!r}; use 'p4' (4), 'c8' (8) or 'p4m'")
+    return code
+
+
+def group_order(code: int) -> int:
+    return 8 if code == EQLIN_P4M else code
 EQLIN_F32, EQLIN_F16 = 0, 1
 STATUS = {0: "EQLIN_OK", 1: "EQLIN_EINVAL", 2: "EQLIN_ENOTSUP", 3: "EQLIN_EALIGN",
           4: "EQLIN_EWORKSPACE", 5: "EQLIN_EHIP"}
@@ -105,31 +118,42 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 class Prepared(NamedTuple):
-    """Prepared weight spectra (opaque byte buffer) and the layer they belong to."""
+    """Prepared weight spectra (opaque byte buffer) and the layer they belong to
+    (T is the group code: 4, 8 or EQLIN_P4M)."""
     buf: torch.Tensor
     C: int
     D: int
     dtype: torch.dtype
     T: int = T_P4
 
-
-def eqlin_prepared_weight_bytes(C: int, D: int, dtype: torch.dtype, T: int = T_P4) -> int:
-    return int(load_library().eqlin_prepared_weight_bytes(C, D, T, _DTYPES[dtype]))
-
-
-def eqlin_prepared_transpose_offset(C: int, D: int, dtype: torch.dtype, T: int = T_P4) -> int:
-    return int(load_library().eqlin_prepared_transpose_offset(C, D, T, _DTYPES[dtype]))
+    @property
+    def order(self) -> int:
+        return group_order(self.T)
 
 
-def eqlin_prepare_weights(w: torch.Tensor, out: Optional[torch.Tensor] = None) -> Prepared:
-    """w [D/T][C/T][T] -> prepared spectra for eqlin_forward / eqlin_backward (T = w.shape[2])."""
+def eqlin_prepared_weight_bytes(C: int, D: int, dtype: torch.dtype, T=T_P4) -> int:
+    return int(load_library().eqlin_prepared_weight_bytes(C, D, group_code(T), _DTYPES[dtype]))
+
+
+def eqlin_prepared_transpose_offset(C: int, D: int, dtype: torch.dtype, T=T_P4) -> int:
+    return int(load_library().eqlin_prepared_transpose_offset(C, D, group_code(T), _DTYPES[dtype]))
+
+
+def eqlin_prepare_weights(w: torch.Tensor, out: Optional[torch.Tensor] = None, group=None) -> Prepared:
+    """w [D/n][C/n][n] -> prepared spectra for eqlin_forward / eqlin_backward.
+
+    group: None for the cyclic group of order n = w.shape[2] (4 or 8), or
+    'p4m' / EQLIN_P4M for the dihedral group (n = 8)."""
     lib = load_library()
     _need_cuda(w, "w")
     dt = _dtype_code(w)
     if w.dim() != 3:
-        raise ValueError(f"w must have shape [D/T, C/T, T], got {tuple(w.shape)}")
-    T = int(w.shape[2])
-    D, C = T * w.shape[0], T * w.shape[1]
+        raise ValueError(f"w must have shape [D/n, C/n, n], got {tuple(w.shape)}")
+    T = group_code(int(w.shape[2]) if group is None else group)
+    if w.shape[2] != group_order(T):
+        raise ValueError(f"w's last dimension {w.shape[2]} is not the group order {group_order(T)}")
+    n = group_order(T)
+    D, C = n * w.shape[0], n * w.shape[1]
     nbytes = int(lib.eqlin_prepared_weight_bytes(C, D, T, dt))
     if out is None:
         out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=w.device)
@@ -165,7 +189,7 @@ ACT = {"none": 0, "gelu": 1}
 
 def eqlin_forward_ex(X: torch.Tensor, W_hat: Prepared, bias: Optional[torch.Tensor] = None, act: str = "none",
                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Y = act(X W^T + b) in one kernel; bias [D/T] (group-invariant, storage dtype) or None."""
+    """Y = act(X W^T + b) in one kernel; bias [D/n] (group-invariant, storage dtype) or None."""
     lib = load_library()
     _need_cuda(X, "X")
     dt = _dtype_code(X)
@@ -177,8 +201,8 @@ def eqlin_forward_ex(X: torch.Tensor, W_hat: Prepared, bias: Optional[torch.Tens
         raise ValueError(f"act must be one of {sorted(ACT)}")
     if bias is not None:
         _need_cuda(bias, "bias")
-        if bias.dtype != X.dtype or tuple(bias.shape) != (W_hat.D // W_hat.T,):
-            raise ValueError(f"bias must be [{W_hat.D // W_hat.T}] of dtype {X.dtype}")
+        if bias.dtype != X.dtype or tuple(bias.shape) != (W_hat.D // W_hat.order,):
+            raise ValueError(f"bias must be [{W_hat.D // W_hat.order}] of dtype {X.dtype}")
     N = X.shape[0]
     if out is None:
         out = torch.empty((N, W_hat.D), dtype=X.dtype, device=X.device)
@@ -188,20 +212,20 @@ def eqlin_forward_ex(X: torch.Tensor, W_hat: Prepared, bias: Optional[torch.Tens
     return out
 
 
-def eqlin_backward_workspace_bytes(N: int, C: int, D: int, dtype: torch.dtype, T: int = T_P4) -> int:
-    return int(load_library().eqlin_backward_workspace_bytes(N, C, D, T, _DTYPES[dtype]))
+def eqlin_backward_workspace_bytes(N: int, C: int, D: int, dtype: torch.dtype, T=T_P4) -> int:
+    return int(load_library().eqlin_backward_workspace_bytes(N, C, D, group_code(T), _DTYPES[dtype]))
 
 
 def eqlin_backward(dY: torch.Tensor, X: Optional[torch.Tensor], W_hat: Prepared, need_dx: bool = True,
                    need_dw: bool = True, workspace: Optional[torch.Tensor] = None,
                    dX_out: Optional[torch.Tensor] = None, dw_out: Optional[torch.Tensor] = None):
-    """(dX [N][C] or None, dw [D/T][C/T][T] float32 or None) for upstream gradient dY [N][D]."""
+    """(dX [N][C] or None, dw [D/n][C/n][n] float32 or None) for upstream gradient dY [N][D]."""
     lib = load_library()
     _need_cuda(dY, "dY")
     dt = _dtype_code(dY)
     if dY.dtype != W_hat.dtype:
         raise TypeError("dY and the prepared weights differ in dtype")
-    C, D, T = W_hat.C, W_hat.D, W_hat.T
+    C, D, T, n = W_hat.C, W_hat.D, W_hat.T, W_hat.order
     if dY.dim() != 2 or dY.shape[1] != D:
         raise ValueError(f"dY must have shape [N, {D}], got {tuple(dY.shape)}")
     N = dY.shape[0]
@@ -218,7 +242,7 @@ def eqlin_backward(dY: torch.Tensor, X: Optional[torch.Tensor], W_hat: Prepared,
         _need_cuda(X, "X")
         if X.dtype != dY.dtype or tuple(X.shape) != (N, C):
             raise ValueError(f"X must be [N, {C}] of dtype {dY.dtype}")
-        dw = dw_out if dw_out is not None else torch.empty((D // T, C // T, T), dtype=torch.float32,
+        dw = dw_out if dw_out is not None else torch.empty((D // n, C // n, n), dtype=torch.float32,
                                                            device=dY.device)
         _need_cuda(dw, "dw")
         ws_bytes = int(lib.eqlin_backward_workspace_bytes(N, C, D, T, dt))
@@ -251,8 +275,8 @@ def eqlin_backward_dx(dY: torch.Tensor, W_hat: Prepared, out: Optional[torch.Ten
 
 
 def eqlin_backward_dw(dY: torch.Tensor, X: torch.Tensor, workspace: Optional[torch.Tensor] = None,
-                      out: Optional[torch.Tensor] = None, T: int = T_P4) -> torch.Tensor:
-    """dw [D/T][C/T][T] (float32) from dY [N][D] and X [N][C]."""
+                      out: Optional[torch.Tensor] = None, T=T_P4) -> torch.Tensor:
+    """dw [D/n][C/n][n] (float32) from dY [N][D] and X [N][C]; T = group (4, 8, 'p4m')."""
     lib = load_library()
     _need_cuda(dY, "dY")
     _need_cuda(X, "X")
@@ -260,8 +284,10 @@ def eqlin_backward_dw(dY: torch.Tensor, X: torch.Tensor, workspace: Optional[tor
     if X.dtype != dY.dtype or X.dim() != 2 or dY.dim() != 2 or X.shape[0] != dY.shape[0]:
         raise ValueError("dY [N, D] and X [N, C] must share N and dtype")
     N, C, D = X.shape[0], X.shape[1], dY.shape[1]
+    T = group_code(T)
+    n = group_order(T)
     if out is None:
-        out = torch.empty((D // T, C // T, T), dtype=torch.float32, device=dY.device)
+        out = torch.empty((D // n, C // n, n), dtype=torch.float32, device=dY.device)
     _need_cuda(out, "out")
     ws_bytes = int(lib.eqlin_backward_workspace_bytes(N, C, D, T, dt))
     if workspace is None:

@@ -1,9 +1,9 @@
-"""Drop-in module for a group-circulant (EQ-)linear layer (p4 rotations or C8).
+"""Drop-in module for a group-circulant (EQ-)linear layer (p4, C8 or p4m).
 
 The Flash EQ-Linear summary (gist.science 2607.21271, "Implementation", last
 bullet) describes the method as a training-free, plug-and-play replacement:
 the naive layer's learnable parameters are reused unchanged.  FlashEQLinear
-holds exactly those parameters, w [D/T][C/T][T], and runs the forward and
+holds exactly those parameters, w [D/n][C/n][n] (n = group order), and runs the forward and
 backward through the HIP library (eqlin_prepare_weights / eqlin_forward /
 eqlin_backward).  The prepared spectra are cached per weight version, so they
 are recomputed only after w changes (an optimizer step or a load).
@@ -20,7 +20,30 @@ import torch
 from . import eqlin
 
 T_P4 = 4
-GROUP_ORDERS = (4, 8)
+
+
+def cayley_table(code: int) -> torch.Tensor:
+    """Multiplication table of the group (index of g_i g_j): cyclic for 4 and 8;
+    for p4m the element u = k + 4m is r^k s^m with s r s = r^-1."""
+    n = eqlin.group_order(code)
+    i = torch.arange(n)
+    if code != eqlin.EQLIN_P4M:
+        return (i.view(n, 1) + i.view(1, n)) % n
+    k, m = i % 4, i // 4
+    k1, m1, k2, m2 = k.view(n, 1), m.view(n, 1), k.view(1, n), m.view(1, n)
+    return (k1 + torch.where(m1 == 0, k2, -k2)) % 4 + 4 * (m1 ^ m2)
+
+
+def dense_expansion(w: torch.Tensor, group=None) -> torch.Tensor:
+    """The dense D x C weight W[n d'+g, n c'+h] = w[d', c', h^-1 g] of w [D/n][C/n][n]
+    (group None: cyclic of order n).  For inspection and dense comparisons only."""
+    code = eqlin.group_code(w.shape[2] if group is None else group)
+    n = eqlin.group_order(code)
+    table = cayley_table(code)
+    inv = torch.stack([torch.nonzero(table[i] == 0)[0, 0] for i in range(n)])
+    idx = table[inv.view(1, n), torch.arange(n).view(n, 1)].to(w.device)   # idx[g, h] = h^-1 g
+    Dp, Cp, _ = w.shape
+    return w[:, :, idx].permute(0, 2, 1, 3).reshape(Dp * n, Cp * n)
 
 
 class _SpectraCache:
@@ -30,22 +53,24 @@ class _SpectraCache:
         self.key = None
         self.prepared: Optional[eqlin.Prepared] = None
 
-    def get(self, w: torch.Tensor) -> eqlin.Prepared:
-        key = (w.data_ptr(), w._version, tuple(w.shape), w.dtype, w.device)
+    def get(self, w: torch.Tensor, group=None) -> eqlin.Prepared:
+        key = (w.data_ptr(), w._version, tuple(w.shape), w.dtype, w.device, group)
         if self.key != key or self.prepared is None:
-            self.prepared = eqlin.eqlin_prepare_weights(w.detach().contiguous())
+            self.prepared = eqlin.eqlin_prepare_weights(w.detach().contiguous(), group=group)
             self.key = key
         return self.prepared
 
 
 class EQLinearFunction(torch.autograd.Function):
-    """Y = X W^T with W the group-circulant expansion of w; X [..., C] -> Y [..., D]."""
+    """Y = X W^T with W the group-circulant expansion of w; X [..., C] -> Y [..., D].
+    group: None (cyclic of order w.shape[2]) or a group accepted by eqlin.group_code."""
 
     @staticmethod
-    def forward(ctx, X: torch.Tensor, w: torch.Tensor, cache: Optional[_SpectraCache] = None):
+    def forward(ctx, X: torch.Tensor, w: torch.Tensor, cache: Optional[_SpectraCache] = None, group=None):
         if X.dtype != w.dtype:
             raise TypeError(f"X ({X.dtype}) and w ({w.dtype}) must share a dtype")
-        prepared = cache.get(w) if cache is not None else eqlin.eqlin_prepare_weights(w.detach().contiguous())
+        prepared = (cache.get(w, group) if cache is not None
+                    else eqlin.eqlin_prepare_weights(w.detach().contiguous(), group=group))
         lead = X.shape[:-1]
         X2 = X.reshape(-1, X.shape[-1]).contiguous()
         Y = eqlin.eqlin_forward(X2, prepared)
@@ -60,34 +85,35 @@ class EQLinearFunction(torch.autograd.Function):
         prepared = ctx.prepared
         need_dx, need_dw = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
         if not (need_dx or need_dw):
-            return None, None, None
+            return None, None, None, None
         dY2 = dY.reshape(-1, prepared.D).contiguous().to(X2.dtype)
         dX, dw = eqlin.eqlin_backward(dY2, X2 if need_dw else None, prepared, need_dx=need_dx, need_dw=need_dw)
         dX = dX.reshape(*ctx.lead, prepared.C) if dX is not None else None
         dw = dw.to(w.dtype) if dw is not None else None
-        return dX, dw, None
+        return dX, dw, None, None
 
 
 class FlashEQLinear(torch.nn.Module):
     """Group-circulant linear layer (no bias), in_features -> out_features.
 
-    ``group_size`` T is 4 (the p4 rotation group, the default) or 8 (C8).
-    Parameter ``w`` has shape [out_features/T, in_features/T, T]; block
-    (d', c') of the dense weight is the T x T circulant
-    W[T d'+t, T c'+s] = w[d', c', (t - s) mod T].
+    ``group`` is 4 or "p4" (the p4 rotation group, the default), 8 or "c8"
+    (the cyclic group C8), or "p4m" (rotations and reflections, order 8).
+    Parameter ``w`` has shape [out_features/n, in_features/n, n] (n = group
+    order); block (d', c') of the dense weight is W[n d'+g, n c'+h] =
+    w[d', c', h^-1 g], for the cyclic groups the circulant w[d', c', (g-h) mod n].
     """
 
-    def __init__(self, in_features: int, out_features: int, device=None, dtype=None, group_size: int = T_P4):
+    def __init__(self, in_features: int, out_features: int, device=None, dtype=None, group=T_P4):
         super().__init__()
-        if group_size not in GROUP_ORDERS:
-            raise ValueError(f"group_size must be one of {GROUP_ORDERS}")
-        T = group_size
-        if in_features % T or out_features % T:
-            raise ValueError(f"in_features and out_features must be multiples of {T}")
+        code = eqlin.group_code(group)
+        n = eqlin.group_order(code)
+        if in_features % n or out_features % n:
+            raise ValueError(f"in_features and out_features must be multiples of {n}")
         self.in_features = in_features
         self.out_features = out_features
-        self.group_size = T
-        self.w = torch.nn.Parameter(torch.empty(out_features // T, in_features // T, T,
+        self.group = code
+        self.group_size = n
+        self.w = torch.nn.Parameter(torch.empty(out_features // n, in_features // n, n,
                                                 device=device, dtype=dtype))
         self._cache = _SpectraCache()
         self.reset_parameters()
@@ -97,29 +123,27 @@ class FlashEQLinear(torch.nn.Module):
         torch.nn.init.normal_(self.w, 0.0, 1.0 / math.sqrt(self.in_features))
 
     @classmethod
-    def from_naive(cls, w: torch.Tensor) -> "FlashEQLinear":
-        """Wrap a naive EQ-Linear's circulant parameter w [D/T][C/T][T] (copied)."""
-        Dp, Cp, T = w.shape
-        if T not in GROUP_ORDERS:
-            raise ValueError(f"group size {T} is not supported (use one of {GROUP_ORDERS})")
-        m = cls(T * Cp, T * Dp, device=w.device, dtype=w.dtype, group_size=T)
+    def from_naive(cls, w: torch.Tensor, group=None) -> "FlashEQLinear":
+        """Wrap a naive EQ-Linear's parameter w [D/n][C/n][n] (copied); group None
+        means the cyclic group of order n = w.shape[2]."""
+        Dp, Cp, n = w.shape
+        code = eqlin.group_code(n if group is None else group)
+        if eqlin.group_order(code) != n:
+            raise ValueError(f"w's last dimension {n} is not the order of group {group!r}")
+        m = cls(n * Cp, n * Dp, device=w.device, dtype=w.dtype, group=code)
         with torch.no_grad():
             m.w.copy_(w)
         return m
 
     def forward(self, X: torch.Tensor) -> torch.Tensor:
-        return EQLinearFunction.apply(X, self.w, self._cache)
+        return EQLinearFunction.apply(X, self.w, self._cache, self.group)
 
     def dense_weight(self) -> torch.Tensor:
         """The expanded D x C weight (for inspection; the forward never builds it)."""
-        T = self.group_size
-        t = torch.arange(T, device=self.w.device)
-        idx = (t.view(T, 1) - t.view(1, T)) % T
-        Dp, Cp, _ = self.w.shape
-        return self.w[:, :, idx].permute(0, 2, 1, 3).reshape(Dp * T, Cp * T)
+        return dense_expansion(self.w, self.group)
 
     def extra_repr(self) -> str:
-        group = "p4" if self.group_size == 4 else f"C{self.group_size}"
+        group = {4: "p4", 8: "C8", eqlin.EQLIN_P4M: "p4m"}[self.group]
         return f"in_features={self.in_features}, out_features={self.out_features}, group={group}"
 
 

@@ -1,7 +1,7 @@
 /*
  * eqlin.h -- C ABI of the MI355X (gfx950) group-circulant linear layer
- * ("Flash EQ-Linear") for the cyclic groups of order T = 4 (the p4 rotation
- * group) and T = 8 (C8).
+ * ("Flash EQ-Linear") for the cyclic groups of order 4 (the p4 rotation
+ * group) and 8 (C8), and for the dihedral group p4m (order 8).
  *
  * The layer (Flash EQ-Linear technical summary, gist.science 2607.21271,
  * section "Key insight"): the dense weight W (D x C) is made of
@@ -21,8 +21,22 @@
  * f0, f4 (real) and f1, f2, f3 (complex), transforms with the factor
  * sqrt(1/2), fourteen real products instead of sixty-four.
  *
+ * p4m (the rotations and reflections of the square, a non-abelian group of
+ * order 8; "Limitations" names reflection groups as future work): the same
+ * layer as a group convolution, with the group elements u = k + 4m standing
+ * for r^k s^m (r: rotation by 90 degrees, s: a reflection, s r s = r^-1):
+ *
+ *     W[8 d' + g, 8 c' + h] = w[d', c', h^-1 g]
+ *
+ * (for the cyclic groups h^-1 g = (g - h) mod T, the circulant above).  It is
+ * computed through the irreducible representations of p4m: four characters
+ * and one 2 x 2 block per group channel, add/sub-only transforms, twelve real
+ * products instead of sixty-four.
+ *
  * Conventions shared by every entry point
- *   - T is the group size, 4 or 8; any other T -> EQLIN_ENOTSUP.
+ *   - T selects the group: 4 or 8 (cyclic, order T) or EQLIN_P4M (order 8);
+ *     any other value -> EQLIN_ENOTSUP.  Below, "T" in sizes and layouts is
+ *     the group order.
  *   - C, D are the full channel widths, positive multiples of T; C' = C/T
  *     and D' = D/T are the group-channel counts.  The channel index is
  *     group_channel * T + group_element (group element fastest).
@@ -61,11 +75,14 @@ extern "C" {
 /* Storage dtypes. */
 enum { EQLIN_F32 = 0, EQLIN_F16 = 1 };
 
+/* Group code of p4m (order 8) for the T argument; 4 and 8 select the cyclic groups. */
+enum { EQLIN_P4M = 108 };
+
 /* Status codes returned by every int-returning entry point. */
 enum {
   EQLIN_OK = 0,
   EQLIN_EINVAL = 1,     /* bad size, negative N, null required pointer, unknown dtype */
-  EQLIN_ENOTSUP = 2,    /* T not 4 or 8, or an odd group count with EQLIN_F16 and T = 4 */
+  EQLIN_ENOTSUP = 2,    /* T not 4, 8 or EQLIN_P4M, or an odd group count with EQLIN_F16 and T = 4 */
   EQLIN_EALIGN = 3,     /* a data pointer is not 16-byte aligned */
   EQLIN_EWORKSPACE = 4, /* workspace / prepared-weight buffer too small */
   EQLIN_EHIP = 5        /* the HIP runtime reported an error for a launch */
@@ -96,7 +113,11 @@ int eqlin_last_hip_error(void);
  *   T = 8: (F0, F4, Re F1, Im F1, Re F2, Im F2, Re F3, Im F3)
  * and the transpose set holds the same planes with every Im negated: the
  * spectrum of the transposed, group-reversed weight (a conjugate) used by
- * the dX pass.  Within block ks of a row, slot s holds group channel
+ * the dX pass.  For EQLIN_P4M the planes are w_hat(rho) = sum_u w(u) rho(u)
+ * for the characters A1, A2, B1, B2 (r -> 1, 1, -1, -1; s -> 1, -1, 1, -1)
+ * and the 2 x 2 representation E (r -> [[0,-1],[1,0]], s -> diag(1,-1)),
+ * ordered (A1, A2, B1, B2, E00, E01, E10, E11); the transpose set holds the
+ * spectrum of u -> w(u^-1), i.e. the same planes with E01 and E10 swapped.  Within block ks of a row, slot s holds group channel
  * ks*S + g(s); with V = 16 / element bytes (4 or 8) and G = the number of
  * whole groups in one 16-byte piece (2 for EQLIN_F16 with T = 4, else 1),
  *   g(s) = G ((s / V) + 4 ((s % V) / G)) + (s % V) % G
@@ -104,7 +125,8 @@ int eqlin_last_hip_error(void);
  *   g(s) = (s >> 2) + 4 (s & 3)                              (EQLIN_F32)
  *   g(s) = 2 ((s >> 3) + 4 ((s >> 1) & 3)) + (s & 1)          (EQLIN_F16)
  * (the order in which the forward kernel's loaders deposit the transformed
- * input on chip), and slots past the last group channel hold zeros.
+ * input on chip), and slots past the last group channel hold zeros.  The
+ * layout depends on the group order only (EQLIN_P4M as T = 8).
  */
 size_t eqlin_prepared_weight_bytes(int C, int D, int T, int dtype);
 size_t eqlin_prepared_transpose_offset(int C, int D, int T, int dtype);
@@ -156,9 +178,10 @@ size_t eqlin_backward_workspace_bytes(int64_t N, int C, int D, int T, int dtype)
  *   dX [N][C] = dY W   (transposed group-circulant; skipped if dX == NULL)
  *   dw [D'][C'][T] (float32) = d<dY, Y>/dw
  *      = sum_n sum_t dY[n, T d'+t] X[n, T c' + (t-u) mod T]   (skipped if dw == NULL)
- * dw is formed per frequency as sum_n G_k conj(Xhat_k) (G = group DFT of dY),
- * reduced over row splits in a fixed order (deterministic) and inverse
- * transformed along u.  `workspace` (device, >= eqlin_backward_workspace_bytes)
+ *      (EQLIN_P4M: sum_n sum_h dY[n, 8 d' + h u] X[n, 8 c' + h])
+ * dw is formed per frequency as sum_n G_k conj(Xhat_k) (G = group DFT of dY;
+ * for EQLIN_P4M per representation sum_n Xhat^T G), reduced over row splits
+ * in a fixed order (deterministic) and inverse transformed along u.  `workspace` (device, >= eqlin_backward_workspace_bytes)
  * holds the per-split partial spectra; it may be NULL only when dw == NULL.
  * X may be NULL when dw == NULL.
  */

@@ -62,6 +62,19 @@ def test_size_queries_c8(lib):
     assert ws > 0 and ws % (8 * 96 * 96 * 4) == 0
 
 
+P4M = 108   # EQLIN_P4M
+
+
+def test_size_queries_p4m(lib):
+    # p4m has 8 planes per group channel like C8: identical layout sizes
+    for C, D, dt in ((768, 768, 0), (768, 3072, 1), (40, 24, 1), (8, 8, 0)):
+        assert lib.eqlin_prepared_weight_bytes(C, D, P4M, dt) == lib.eqlin_prepared_weight_bytes(C, D, 8, dt)
+        assert lib.eqlin_prepared_transpose_offset(C, D, P4M, dt) == lib.eqlin_prepared_transpose_offset(C, D, 8, dt)
+    assert lib.eqlin_backward_workspace_bytes(12608, 768, 768, P4M, 0) == \
+        lib.eqlin_backward_workspace_bytes(12608, 768, 768, 8, 0)
+    assert lib.eqlin_prepared_weight_bytes(36, 32, P4M, 0) == 0
+
+
 FAKE = ctypes.c_void_p(0x1000)        # aligned, never dereferenced (validation fails first)
 MISALIGNED = ctypes.c_void_p(0x1004)
 
@@ -80,6 +93,8 @@ def test_forward_validation(lib):
     assert f(FAKE, 8, 20, 32, 4, FAKE, FAKE, 1, None) == ENOTSUP   # C'=5 odd with f16
     assert f(FAKE, 8, 36, 32, 8, FAKE, FAKE, 0, None) == EINVAL    # C not a multiple of 8
     assert f(FAKE, 8, 48, 48, 6, FAKE, FAKE, 0, None) == ENOTSUP
+    assert f(FAKE, 8, 36, 32, P4M, FAKE, FAKE, 0, None) == EINVAL   # C not a multiple of 8
+    assert f(FAKE, 8, 48, 48, 107, FAKE, FAKE, 0, None) == ENOTSUP
     assert f(MISALIGNED, 8, 40, 32, 8, FAKE, FAKE, 1, None) == EALIGN
     assert f(None, 0, 32, 32, 4, None, None, 0, None) == OK        # empty batch: nothing enqueued
 

@@ -10,11 +10,13 @@ torch = pytest.importorskip("torch")
 from group_circulant_linear_amd.module import FlashEQLinear, convert_state_dict  # noqa: E402
 
 
-@pytest.mark.parametrize("T", [4, 8])
-def test_dense_view_matches_oracle_expansion(T):
-    m = FlashEQLinear(3 * T, 5 * T, group_size=T)
+@pytest.mark.parametrize("g", [4, 8, "p4m"])
+def test_dense_view_matches_oracle_expansion(g):
+    m = FlashEQLinear(3 * 8, 5 * 8, group=g)
     W = m.dense_weight().detach().double().numpy()
-    assert np.array_equal(W, oracle.dense_expand(m.w.detach().double().numpy()))
+    w = m.w.detach().double().numpy()
+    ref = oracle.dense_expand_group(w, oracle.p4m_table()) if g == "p4m" else oracle.dense_expand(w)
+    assert np.array_equal(W, ref)
 
 
 def test_from_naive_copies_parameters_and_rejects_other_groups():
@@ -24,12 +26,16 @@ def test_from_naive_copies_parameters_and_rejects_other_groups():
     assert torch.equal(m.w.detach(), w)
     m8 = FlashEQLinear.from_naive(torch.randn(5, 3, 8))
     assert (m8.in_features, m8.out_features, m8.group_size) == (24, 40, 8)
+    mm = FlashEQLinear.from_naive(torch.randn(5, 3, 8), group="p4m")
+    assert (mm.group, mm.group_size) == (108, 8) and "p4m" in mm.extra_repr()
     with pytest.raises(ValueError):
         FlashEQLinear.from_naive(torch.randn(5, 3, 6))
     with pytest.raises(ValueError):
+        FlashEQLinear.from_naive(torch.randn(5, 3, 4), group="p4m")
+    with pytest.raises(ValueError):
         FlashEQLinear(10, 8)
     with pytest.raises(ValueError):
-        FlashEQLinear(12, 16, group_size=8)
+        FlashEQLinear(12, 16, group=8)
 
 
 def test_convert_state_dict_renames_only_keys():
@@ -46,19 +52,23 @@ def test_no_cpu_fallback():
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("T", [4, 8])
+@pytest.mark.parametrize("g", [4, 8, "p4m"])
 @pytest.mark.parametrize("dt,tol", [("f32", 1e-5), ("f16", 3e-3)])
-def test_module_forward_backward_matches_oracle(dt, tol, T):
+def test_module_forward_backward_matches_oracle(dt, tol, g):
     B, S, C, D = 3, 197, 96, 160
-    X, w, dY = make_layer_inputs(B * S, C, D, dt, seed=11, T=T)
-    m = FlashEQLinear.from_naive(torch.from_numpy(w).cuda())
+    X, w, dY = make_layer_inputs(B * S, C, D, dt, seed=11, T=8 if g == "p4m" else g)
+    m = FlashEQLinear.from_naive(torch.from_numpy(w).cuda(), group=g)
     Xt = torch.from_numpy(X).cuda().reshape(B, S, C).requires_grad_(True)
     Y = m(Xt)
     assert Y.shape == (B, S, D)
     Y.backward(torch.from_numpy(dY).cuda().reshape(B, S, D))
     torch.cuda.synchronize()
-    Yr = oracle.forward_direct(X, w)
-    dXr, dwr = oracle.backward_direct(dY, X, w)
+    if g == "p4m":
+        t = oracle.p4m_table()
+        Yr, dXr, dwr = oracle.forward_group(X, w, t), oracle.dx_group(dY, w, t), oracle.dw_group(dY, X, t)
+    else:
+        Yr = oracle.forward_direct(X, w)
+        dXr, dwr = oracle.backward_direct(dY, X, w)
 
     def rel(a, b):
         return float(np.max(np.abs(a - b)) / np.max(np.abs(b)))

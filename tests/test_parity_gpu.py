@@ -1,7 +1,7 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
-Both groups the library implements are covered: the p4 rotation group (T = 4)
-and the cyclic group C8 (T = 8).
+Every group the library implements is covered: the p4 rotation group
+(cyclic, order 4), the cyclic group C8 and the dihedral group p4m (order 8).
 
 Metric: max|gpu - ref| / max|ref| over the compared outputs.  Bars: 1e-5 for
 fp32, 3e-3 for f16 storage with fp32 accumulation.  Small shapes span several
@@ -42,6 +42,30 @@ def say(*a):
     print(*a, flush=True)
 
 
+P4M_TABLE = oracle.p4m_table()
+GROUPS = [4, 8, "p4m"]
+
+
+def order(g):
+    return 8 if g == "p4m" else g
+
+
+def prep(w, g):
+    return eq.eqlin_prepare_weights(dev(w), group=None if g != "p4m" else "p4m")
+
+
+def ref_forward(X, w, g):
+    return oracle.forward_group(X, w, P4M_TABLE) if g == "p4m" else oracle.forward_direct(X, w)
+
+
+def ref_dx(dY, w, g):
+    return oracle.dx_group(dY, w, P4M_TABLE) if g == "p4m" else oracle.dx_direct(dY, w)
+
+
+def ref_dw(dY, X, g):
+    return oracle.dw_group(dY, X, P4M_TABLE) if g == "p4m" else oracle.dw_direct(dY, X, g)
+
+
 # --------------------------------------------------------------------- a1
 
 def slot_group(s, dt, T):
@@ -79,25 +103,32 @@ def decode_planes(flat, rows, groups, dt, T):
     return out
 
 
-@pytest.mark.parametrize("T,dt,Dp,Cp", [(4, "f32", 5, 3), (4, "f32", 20, 36), (4, "f32", 192, 192),
+@pytest.mark.parametrize("g,dt,Dp,Cp", [(4, "f32", 5, 3), (4, "f32", 20, 36), (4, "f32", 192, 192),
                                          (4, "f16", 6, 4), (4, "f16", 40, 70), (4, "f16", 768, 192),
                                          (8, "f32", 5, 3), (8, "f32", 96, 40), (8, "f16", 7, 5),
-                                         (8, "f16", 96, 384)])
-def test_prepared_planes_match_group_spectrum(T, dt, Dp, Cp):
-    say(f"prepare T={T} {dt} D'={Dp} C'={Cp}")
+                                         (8, "f16", 96, 384), ("p4m", "f32", 5, 3), ("p4m", "f32", 96, 40),
+                                         ("p4m", "f16", 7, 5), ("p4m", "f16", 96, 384)])
+def test_prepared_planes_match_group_spectrum(g, dt, Dp, Cp):
+    T = order(g)
+    say(f"prepare group={g} {dt} D'={Dp} C'={Cp}")
     _, w, _ = make_layer_inputs(4, T * Cp, T * Dp, dt, seed=1, T=T, with_dy=False)
-    Wh = eq.eqlin_prepare_weights(dev(w))
+    Wh = prep(w, g)
     tdt = torch.float32 if dt == "f32" else torch.float16
     buf = Wh.buf
-    off = eq.eqlin_prepared_transpose_offset(T * Cp, T * Dp, tdt, T)
+    off = eq.eqlin_prepared_transpose_offset(T * Cp, T * Dp, tdt, g)
     wf = decode_planes(host(buf[:off].view(tdt)), Dp, Cp, dt, T)
     wb = decode_planes(host(buf[off:].view(tdt)), Cp, Dp, dt, T)
-    ref = oracle.kept_planes(w.astype(np.float64))
     tol = 1e-6 if dt == "f32" else 1e-3
+    if g == "p4m":
+        ref = oracle.p4m_planes(w.astype(np.float64))
+        adj = ref.copy()
+        adj[..., 5], adj[..., 6] = ref[..., 6], ref[..., 5]     # transposed 2 x 2 block
+    else:
+        ref = oracle.kept_planes(w.astype(np.float64))
+        adj = ref.copy()
+        adj[..., 3::2] = -adj[..., 3::2]      # imaginary planes
     assert rel_err(wf, ref) < tol
-    conj = ref.copy()
-    conj[..., 3::2] = -conj[..., 3::2]      # imaginary planes
-    assert rel_err(wb, conj.transpose(1, 0, 2)) < tol
+    assert rel_err(wb, adj.transpose(1, 0, 2)) < tol
 
 
 # ----------------------------------------------------------------- forward
@@ -118,9 +149,9 @@ SMALL_SHAPES_C8 = {
 }
 
 
-def _forward_case(dt, N, C, D, seed=0, T=4):
-    X, w, _ = make_layer_inputs(N, C, D, dt, seed=seed, T=T, with_dy=False)
-    Wh = eq.eqlin_prepare_weights(dev(w))
+def _forward_case(dt, N, C, D, seed=0, g=4):
+    X, w, _ = make_layer_inputs(N, C, D, dt, seed=seed, T=order(g), with_dy=False)
+    Wh = prep(w, g)
     Y = eq.eqlin_forward(dev(X), Wh)
     return X, w, host(Y)
 
@@ -140,13 +171,14 @@ def test_forward_small_shapes_all_tiles(dt, tile, monkeypatch):
 
 @pytest.mark.parametrize("tile", ["auto", "112211", "112221", "111221", "212211", "122211"])
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-def test_forward_c8_small_shapes_all_tiles(dt, tile, monkeypatch):
+@pytest.mark.parametrize("g", [8, "p4m"])
+def test_forward_order8_small_shapes_all_tiles(g, dt, tile, monkeypatch):
     if tile != "auto":
         monkeypatch.setenv("EQLIN_FWD_TILE", tile)
     for (N, C, D) in SMALL_SHAPES_C8[dt]:
-        say(f"forward C8 {dt} tile={tile} N={N} C={C} D={D}")
-        X, w, Y = _forward_case(dt, N, C, D, T=8)
-        err = rel_err(Y, oracle.forward_direct(X, w))
+        say(f"forward group={g} {dt} tile={tile} N={N} C={C} D={D}")
+        X, w, Y = _forward_case(dt, N, C, D, g=g)
+        err = rel_err(Y, ref_forward(X, w, g))
         assert err <= TOL[dt], (N, C, D, err)
 
 
@@ -156,22 +188,24 @@ def _sample_rows(N, rng, k=96):
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("name,dt,T", [("tiny", "f32", 4), ("vitb_attn", "f32", 4), ("vitb_mlp", "f16", 4),
+@pytest.mark.parametrize("name,dt,g", [("tiny", "f32", 4), ("vitb_attn", "f32", 4), ("vitb_mlp", "f16", 4),
                                        ("vith_mlp", "f32", 4), ("vith_mlp", "f16", 4), ("tiny", "f32", 8),
                                        ("vitb_attn", "f32", 8), ("vitb_mlp", "f16", 8), ("vith_mlp", "f32", 8),
-                                       ("vith_mlp", "f16", 8)])
-def test_forward_workloads(name, dt, T):
+                                       ("vith_mlp", "f16", 8), ("tiny", "f32", "p4m"), ("vitb_attn", "f32", "p4m"),
+                                       ("vitb_mlp", "f16", "p4m"), ("vith_mlp", "f32", "p4m"),
+                                       ("vith_mlp", "f16", "p4m")])
+def test_forward_workloads(name, dt, g):
     wl = WORKLOADS[name]
     for li, L in enumerate(wl.layers):
-        say(f"forward workload {name} {L.name} {dt} T={T} N={L.N} C={L.C} D={L.D}")
-        X, w, _ = make_layer_inputs(L.N, L.C, L.D, dt, seed=0, layer=li, T=T, with_dy=False)
-        Wh = eq.eqlin_prepare_weights(dev(w))
+        say(f"forward workload {name} {L.name} {dt} group={g} N={L.N} C={L.C} D={L.D}")
+        X, w, _ = make_layer_inputs(L.N, L.C, L.D, dt, seed=0, layer=li, T=order(g), with_dy=False)
+        Wh = prep(w, g)
         Y = host(eq.eqlin_forward(dev(X), Wh))
         if L.N * L.C * L.D <= 12608 * 768 * 768:
-            err = rel_err(Y, oracle.forward_direct(X, w))
+            err = rel_err(Y, ref_forward(X, w, g))
         else:
             rows = _sample_rows(L.N, np.random.default_rng(li))
-            err = rel_err(Y[rows], oracle.forward_rows(X, w, rows))
+            err = rel_err(Y[rows], ref_forward(X[rows], w, g))
         say(f"  rel err {err:.3e}")
         assert err <= TOL[dt]
 
@@ -187,52 +221,53 @@ BWD_SHAPES = {
 BWD_SHAPES_C8 = [(64, 64, 64), (1, 8, 8), (77, 24, 40), (1000, 160, 96), (3001, 8 * 70, 8 * 130)]
 
 
-@pytest.mark.parametrize("T", [4, 8])
+@pytest.mark.parametrize("g", GROUPS)
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-def test_backward_small_shapes(dt, T):
-    for (N, C, D) in (BWD_SHAPES[dt] if T == 4 else BWD_SHAPES_C8):
-        say(f"backward T={T} {dt} N={N} C={C} D={D}")
-        X, w, dY = make_layer_inputs(N, C, D, dt, seed=2, T=T)
-        Wh = eq.eqlin_prepare_weights(dev(w))
+def test_backward_small_shapes(dt, g):
+    for (N, C, D) in (BWD_SHAPES[dt] if g == 4 else BWD_SHAPES_C8):
+        say(f"backward group={g} {dt} N={N} C={C} D={D}")
+        X, w, dY = make_layer_inputs(N, C, D, dt, seed=2, T=order(g))
+        Wh = prep(w, g)
         dX, dw = eq.eqlin_backward(dev(dY), dev(X), Wh)
-        dXr, dwr = oracle.backward_direct(dY, X, w)
+        dXr, dwr = ref_dx(dY, w, g), ref_dw(dY, X, g)
         e1, e2 = rel_err(host(dX), dXr), rel_err(host(dw), dwr)
         assert e1 <= TOL[dt], ("dX", N, C, D, e1)
         assert e2 <= TOL[dt], ("dw", N, C, D, e2)
 
 
-@pytest.mark.parametrize("T", [4, 8])
+@pytest.mark.parametrize("g", GROUPS)
 @pytest.mark.parametrize("dt", ["f16", "f32"])
-def test_backward_workload_vitb(dt, T):
+def test_backward_workload_vitb(dt, g):
     L = WORKLOADS["vitb_attn_bwd"].layers[0]
-    say(f"backward workload vitb_attn_bwd {dt} T={T} N={L.N} C={L.C} D={L.D}")
-    X, w, dY = make_layer_inputs(L.N, L.C, L.D, dt, seed=0, T=T)
-    Wh = eq.eqlin_prepare_weights(dev(w))
+    say(f"backward workload vitb_attn_bwd {dt} group={g} N={L.N} C={L.C} D={L.D}")
+    X, w, dY = make_layer_inputs(L.N, L.C, L.D, dt, seed=0, T=order(g))
+    Wh = prep(w, g)
     dX, dw = eq.eqlin_backward(dev(dY), dev(X), Wh)
-    e1 = rel_err(host(dX), oracle.dx_direct(dY, w))
-    e2 = rel_err(host(dw), oracle.dw_direct(dY, X, T))
+    e1 = rel_err(host(dX), ref_dx(dY, w, g))
+    e2 = rel_err(host(dw), ref_dw(dY, X, g))
     say(f"  dX rel err {e1:.3e}  dw rel err {e2:.3e}")
     assert e1 <= TOL[dt] and e2 <= TOL[dt]
 
 
-@pytest.mark.parametrize("T", [4, 8])
-def test_backward_separate_entry_points_agree(T):
-    X, w, dY = make_layer_inputs(500, 64, 96, "f32", seed=4, T=T)
-    Wh = eq.eqlin_prepare_weights(dev(w))
+@pytest.mark.parametrize("g", GROUPS)
+def test_backward_separate_entry_points_agree(g):
+    X, w, dY = make_layer_inputs(500, 64, 96, "f32", seed=4, T=order(g))
+    Wh = prep(w, g)
     dX, dw = eq.eqlin_backward(dev(dY), dev(X), Wh)
     dX2 = eq.eqlin_backward_dx(dev(dY), Wh)
-    dw2 = eq.eqlin_backward_dw(dev(dY), dev(X), T=T)
+    dw2 = eq.eqlin_backward_dw(dev(dY), dev(X), T=g)
     assert torch.equal(dX, dX2) and torch.equal(dw, dw2)
 
 
 # -------------------------------------------------------------- edge cases
 
-@pytest.mark.parametrize("T", [4, 8])
+@pytest.mark.parametrize("g", GROUPS)
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-def test_empty_batch(dt, T):
+def test_empty_batch(dt, g):
+    T = order(g)
     tdt = torch.float32 if dt == "f32" else torch.float16
     _, w, _ = make_layer_inputs(1, 32, 48, dt, seed=5, T=T, with_dy=False)
-    Wh = eq.eqlin_prepare_weights(dev(w))
+    Wh = prep(w, g)
     X = torch.empty((0, 32), dtype=tdt, device=DEV)
     dY = torch.empty((0, 48), dtype=tdt, device=DEV)
     assert eq.eqlin_forward(X, Wh).shape == (0, 48)
@@ -243,11 +278,11 @@ def test_empty_batch(dt, T):
     assert torch.count_nonzero(dw).item() == 0
 
 
-@pytest.mark.parametrize("T", [4, 8])
+@pytest.mark.parametrize("g", GROUPS)
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-def test_determinism(dt, T):
-    X, w, dY = make_layer_inputs(2000, 256, 384, dt, seed=6, T=T)
-    Wh = eq.eqlin_prepare_weights(dev(w))
+def test_determinism(dt, g):
+    X, w, dY = make_layer_inputs(2000, 256, 384, dt, seed=6, T=order(g))
+    Wh = prep(w, g)
     tX, tdY = dev(X), dev(dY)
     Y1 = eq.eqlin_forward(tX, Wh).clone()
     Y2 = eq.eqlin_forward(tX, Wh)
@@ -257,13 +292,13 @@ def test_determinism(dt, T):
     assert torch.equal(Y1, Y2) and torch.equal(dX1, dX2) and torch.equal(dw1, dw2)
 
 
-@pytest.mark.parametrize("T", [4, 8])
+@pytest.mark.parametrize("g", GROUPS)
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-def test_row_isolation(dt, T):
+def test_row_isolation(dt, g):
     # a NaN in row r of X may only reach row r of Y (checks tail masking and row mapping)
     N, C, D = 300, 128, 160
-    X, w, _ = make_layer_inputs(N, C, D, dt, seed=7, T=T, with_dy=False)
-    Wh = eq.eqlin_prepare_weights(dev(w))
+    X, w, _ = make_layer_inputs(N, C, D, dt, seed=7, T=order(g), with_dy=False)
+    Wh = prep(w, g)
     Y0 = host(eq.eqlin_forward(dev(X), Wh))
     Xn = X.copy()
     for r in (0, 131, N - 1):
@@ -272,6 +307,25 @@ def test_row_isolation(dt, T):
     bad = np.isnan(Y1).any(axis=1)
     assert set(np.nonzero(bad)[0].tolist()) == {0, 131, N - 1}
     assert np.array_equal(Y1[~bad], Y0[~bad])
+
+
+def _left_translate(Z, a, table):
+    """(L_a z)(g) = z(a^-1 g) on every group block of Z [N][G*n]."""
+    n = len(table)
+    inv = [int(np.nonzero(table[i] == 0)[0][0]) for i in range(n)]
+    src = [table[inv[a], h] for h in range(n)]
+    return Z.reshape(Z.shape[0], -1, n)[:, :, src].reshape(Z.shape)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_p4m_equivariance_under_every_element(dt):
+    N, C, D = 256, 128, 192
+    X, w, _ = make_layer_inputs(N, C, D, dt, seed=8, T=8, with_dy=False)
+    Wh = prep(w, "p4m")
+    Y = host(eq.eqlin_forward(dev(X), Wh))
+    for a in range(8):
+        Ya = host(eq.eqlin_forward(dev(_left_translate(X, a, P4M_TABLE)), Wh))
+        assert rel_err(Ya, _left_translate(Y, a, P4M_TABLE)) <= TOL[dt], a
 
 
 @pytest.mark.parametrize("T", [4, 8])
@@ -302,17 +356,23 @@ def test_non_default_stream():
 
 # ------------------------------------------------- fused bias + GELU epilogue
 
-@pytest.mark.parametrize("T", [4, 8])
+@pytest.mark.parametrize("g", GROUPS)
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 @pytest.mark.parametrize("with_bias,act", [(True, "none"), (False, "gelu"), (True, "gelu")])
-def test_forward_ex_bias_gelu(dt, with_bias, act, T):
+def test_forward_ex_bias_gelu(dt, with_bias, act, g):
+    T = order(g)
     for (N, C, D) in [(131, 8 * 3, 8 * 5), (1000, 160, 96), (333, 8 * 100, 8 * 65)]:
-        say(f"forward_ex T={T} {dt} bias={with_bias} act={act} N={N} C={C} D={D}")
+        say(f"forward_ex group={g} {dt} bias={with_bias} act={act} N={N} C={C} D={D}")
         X, w, _ = make_layer_inputs(N, C, D, dt, seed=13, T=T, with_dy=False)
         b = (np.random.default_rng(14).standard_normal(D // T)).astype(X.dtype) if with_bias else None
-        Wh = eq.eqlin_prepare_weights(dev(w))
+        Wh = prep(w, g)
         Y = host(eq.eqlin_forward_ex(dev(X), Wh, dev(b) if with_bias else None, act))
-        ref = oracle.forward_bias_act(X, w, b, act)
+        if g == "p4m":
+            # the oracle's bias/act step applied to the p4m group convolution
+            Z = ref_forward(X, w, g) + (np.repeat(b.astype(np.float64), T)[None, :] if with_bias else 0.0)
+            ref = oracle.gelu_erf(Z) if act == "gelu" else Z
+        else:
+            ref = oracle.forward_bias_act(X, w, b, act)
         assert rel_err(Y, ref) <= TOL[dt]
 
 
