@@ -10,7 +10,7 @@ namespace eqlin {
 // compiled forward tiles, code = FM FN WM WN NBUF PF (decimal digits)
 #define EQLIN_P4_TILES(X)                                                                                 \
   X(112221) X(111221) X(112121) X(222221) X(212421) X(112411) X(212211) X(122211) X(112211) X(112212)     \
-  X(112412)
+  X(112412) X(111211)
 
 namespace {
 // EQLIN_SCHED=0 drops the explicit MFMA / memory interleave of the
