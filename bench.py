@@ -4,7 +4,10 @@ A step is one pass of the whole hot path over one batch of synthetic input:
 for every layer of the workload, prepare the weight spectra, run the forward
 (Y = X W^T), and the backward (dX = dY W, then dw).  Inputs live in HBM before
 the timed region starts; R rotating buffer sets (more than the 256 MB
-Infinity Cache) keep consecutive steps from being served by the cache.
+Infinity Cache) keep consecutive steps from being served by the cache.  The
+K timed steps run phase by phase (all K prepares of a layer, then its K
+forwards, then its K backwards), each phase between one pair of HIP events on
+the launch stream, so a phase's per-launch time is its event time / K.
 
 The reported metric is the forward dense-equivalent throughput
 2*N*D*C / t_forward (the same N x D x C dense GEMM counts 2NDC FLOPs), summed
@@ -46,6 +49,8 @@ def parse():
     p.add_argument("--group", default="4", choices=("4", "8", "p4m"),
                    help="group: 4 (p4 rotations), 8 (cyclic C8) or p4m (dihedral, order 8)")
     p.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0 = enough to exceed 600 MB)")
+    p.add_argument("--settle", type=float, default=0.5,
+                   help="seconds of untimed steps before the warmup steps (GPU clock ramp)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--forward-only", action="store_true",
@@ -169,6 +174,11 @@ def mlp_block(args):
         return F.linear(h, D2, db2)
 
     def timeit(fn, reps):
+        t_settle = time.perf_counter()
+        while time.perf_counter() - t_settle < args.settle:
+            for i in range(4):
+                fn(i)
+            torch.cuda.synchronize()
         for i in range(args.warmup):
             fn(i)
         torch.cuda.synchronize()
@@ -241,53 +251,60 @@ def main():
         sets.append(S)
     torch.cuda.synchronize()
 
-    phases = ("prepare", "forward", "backward")
+    phases = ("prepare", "forward") if args.forward_only else ("prepare", "forward", "backward")
+    prepared = [[None] * len(layers) for _ in range(nsets)]
 
-    def step(i, events=None):
-        S = sets[i % nsets]
-        for li, b in enumerate(S):
-            ev = events[li] if events is not None else None
-            if ev is not None:
-                ev["prepare"][0].record()
-            Wh = eqlin.eqlin_prepare_weights(b["w"], out=b["Wbuf"], group=G)
-            if ev is not None:
-                ev["prepare"][1].record()
-                ev["forward"][0].record()
-            eqlin.eqlin_forward(b["X"], Wh, out=b["Y"])
-            if ev is not None:
-                ev["forward"][1].record()
-            if args.forward_only:
-                continue
-            if ev is not None:
-                ev["backward"][0].record()
-            eqlin.eqlin_backward(b["dY"], b["X"], Wh, workspace=b["ws"], dX_out=b["dX"], dw_out=b["dw"])
-            if ev is not None:
-                ev["backward"][1].record()
+    def run_phase(p, li, i0, count):
+        for i in range(i0, i0 + count):
+            b = sets[i % nsets][li]
+            if p == "prepare":
+                prepared[i % nsets][li] = eqlin.eqlin_prepare_weights(b["w"], out=b["Wbuf"], group=G)
+            elif p == "forward":
+                eqlin.eqlin_forward(b["X"], prepared[i % nsets][li], out=b["Y"])
+            else:
+                eqlin.eqlin_backward(b["dY"], b["X"], prepared[i % nsets][li], workspace=b["ws"], dX_out=b["dX"],
+                                     dw_out=b["dw"])
 
-    for i in range(args.warmup):
-        step(i)
+    def run_steps(i0, count, events=None):
+        """`count` steps (batches i0, i0+1, ...): for each layer, each phase runs for
+        all the batches back to back between one event pair, so the per-launch time
+        carries no event overhead (an event pair around a single launch adds a few
+        microseconds to it)."""
+        for li in range(len(layers)):
+            for p in phases:
+                if events is not None:
+                    events[li][p][0].record()
+                run_phase(p, li, i0, count)
+                if events is not None:
+                    events[li][p][1].record()
+
+    # untimed clock settle: the GPU ramps its clocks over the first tens of
+    # milliseconds of work, longer than a few warmup steps take
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle:
+        run_steps(0, 4)
+        torch.cuda.synchronize()
+    if args.warmup:
+        run_steps(0, args.warmup)
     torch.cuda.synchronize()
-    print(f"# warmup done ({args.warmup} steps, {nsets} buffer sets)", file=sys.stderr, flush=True)
+    print(f"# warmup done ({args.warmup} steps after {args.settle} s of clock settle, {nsets} buffer sets)",
+          file=sys.stderr, flush=True)
 
     K = args.steps
-    evs = [[{p: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for p in phases}
-            for _ in layers] for _ in range(K)]
+    evs = [{p: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for p in phases}
+           for _ in layers]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K):
-        step(i, evs[i])
+    run_steps(0, K, evs)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
 
-    ph_us = {p: [0.0] * len(layers) for p in phases}
-    for i in range(K):
-        for li in range(len(layers)):
-            for p in phases:
-                if args.forward_only and p == "backward":
-                    continue
-                a, b = evs[i][li][p]
-                ph_us[p][li] += a.elapsed_time(b) * 1e3 / K
+    ph_us = {p: [0.0] * len(layers) for p in ("prepare", "forward", "backward")}
+    for li in range(len(layers)):
+        for p in phases:
+            a, b = evs[li][p]
+            ph_us[p][li] = a.elapsed_time(b) * 1e3 / K
 
     fwd_flops = sum(2.0 * L.N * L.C * L.D for (L, _, _, _) in layers)
     fwd_us = sum(ph_us["forward"])

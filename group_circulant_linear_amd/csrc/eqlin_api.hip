@@ -64,12 +64,12 @@ bool fwd_offsets_fit(int in_width, int O, int dtype) {
 
 struct TileShape {
   int code, bm, bn;
-  double eff;  // measured fraction of the MFMA peak on large shapes (MI355X)
+  double eff;  // measured fraction of the MFMA peak on large shapes (MI355X, clocks settled)
 };
 // Forward tile candidates (code = FM FN WM WN NBUF PF) with their measured efficiency
 // on the ViT-B / ViT-H layer shapes.
-constexpr TileShape kP4F32Tiles[] = {{112211, 64, 64, 0.69}, {112221, 64, 64, 0.65}, {111211, 32, 64, 0.68}};
-constexpr TileShape kP4F16Tiles[] = {{212421, 128, 128, 0.24}, {112211, 64, 64, 0.20}, {111221, 32, 64, 0.13}};
+constexpr TileShape kP4F32Tiles[] = {{112211, 64, 64, 0.745}, {112221, 64, 64, 0.70}, {111211, 32, 64, 0.70}};
+constexpr TileShape kP4F16Tiles[] = {{212421, 128, 128, 0.24}, {112211, 64, 64, 0.17}, {111221, 32, 64, 0.12}};
 constexpr TileShape kC8F32Tiles[] = {{112211, 64, 64, 0.58}, {112221, 64, 64, 0.55}, {111221, 32, 64, 0.31}};
 constexpr TileShape kC8F16Tiles[] = {{122211, 64, 128, 0.115}, {112221, 64, 64, 0.105}, {212211, 128, 64, 0.10}};
 
