@@ -603,6 +603,46 @@ constexpr int fwd_lds_bytes() {
   return NBUF * T * (32 * FM * WM + 32 * FN * WN) * kRowBytes;
 }
 
+// Epilogue of a forward / dX tile: inverse group DFT in registers, optional
+// group-invariant bias and GELU, one vector store per (row, group).
+template <typename E, int G, int FM, int FN, int WM, int WN>
+__device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[Grp<G>::kOrder][FM][FN], int64_t row0, int col0,
+                                             E* __restrict__ out, int64_t nrows, int mg,
+                                             const E* __restrict__ bias, int act) {
+  constexpr int T = Grp<G>::kOrder;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = wave / WN, wc = wave % WN;
+  const int li = lane & 31, lh = lane >> 5;
+  const int64_t out_ld = T * (int64_t)mg;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int m = col0 + wc * 32 * FN + fn * 32 + li;
+      const float bm = (bias != nullptr && m < mg) ? (float)bias[m] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = row0 + wr * 32 * FM + fm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        if (row < nrows && m < mg) {
+          float f[T], y[T];
+#pragma unroll
+          for (int p = 0; p < T; ++p) f[p] = acc[p][fm][fn][r];
+          Grp<G>::idft(f, y);
+          if (bias != nullptr) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) y[t] += bm;
+          }
+          if (act == 1) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) y[t] = gelu_erf(y[t]);
+          }
+          store_group<E, T>(out + row * out_ld + T * (int64_t)m, y);
+        }
+      }
+    }
+  }
+}
+
 // One forward (or dX) tile: workgroup-level logical tile id `lid`.  NBUF = 2
 // double-buffers the LDS stages (one barrier per stage); NBUF = 1 halves the
 // LDS footprint (two barriers per stage) so that more workgroups fit a CU.
@@ -738,35 +778,154 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
     }
   }
 
-  // epilogue: inverse group DFT in registers, optional group-invariant bias
-  // and GELU, one vector store per (row, group)
-  const int64_t out_ld = T * (int64_t)mg;
+  fwd_epilogue<E, G, FM, FN, WM, WN>(acc, row0, col0, out, nrows, mg, bias, act);
+}
+
+// Persistent forward: workgroup `first` runs the tiles first, first + stride,
+// first + 2 stride, ... (< ntiles) as one stream of pipeline stages.  A tile's
+// epilogue runs right after its last stage, when the loads of the next tile's
+// first stages are already in flight and its LDS stage is stored, and its
+// global stores drain behind the next tile's MFMAs; no workgroup launch,
+// prologue or store drain separates the tiles.  The stage pipeline, LDS
+// layout and transforms are those of fwd_tile.
+template <typename E, int G, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED>
+__device__ __forceinline__ void fwd_stream(char* lds, int64_t first, int64_t stride, int64_t ntiles,
+                                           const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ out,
+                                           int64_t nrows, int kg, int mg, int tiles_n, const E* __restrict__ bias,
+                                           int act) {
+  constexpr int T = Grp<G>::kOrder;
+  using U = Units<E, T>;
+  constexpr int NT = 64 * WM * WN;
+  constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
+  constexpr int SG = Traits<E>::kStageGroups;
+  constexpr int STRIDE = kRowBytes;
+  constexpr int A_PLANE = BM * STRIDE, B_PLANE = BN * STRIDE;
+  constexpr int BUF = T * (A_PLANE + B_PLANE);
+  constexpr int BLOCK = T * kRowBytes;
+  constexpr int RPP = NT / 4;
+  constexpr int PA = (BM + RPP - 1) / RPP, PB = (BN + RPP - 1) / RPP;
+
+  if (first >= ntiles) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ksteps = (kg + SG - 1) / SG;
+  const int64_t nt = (ntiles - first + stride - 1) / stride;
+  const int64_t S = nt * ksteps;
+  const uint32_t row_bytes = (uint32_t)kg * (uint32_t)(T * sizeof(E));
+
+  const int q = tid & 3, rl = tid >> 2;
+  u32x4 ra[PF][PA][T], rb[PF][PB][T];
+  // Load cursor: the loads are issued for consecutive global stages, so the
+  // cursor steps through (tile, stage) with selects only (no division, no
+  // branch: the stage loop stays one basic block).  Past the stream's last
+  // stage the loads read zeros.
+  const int64_t sq = stride / tiles_n;
+  const int sr = (int)(stride % tiles_n);
+  int lks = 0, lcol = (int)(first % tiles_n);
+  int64_t lrow = first / tiles_n, lleft = S;
+  auto load = [&](auto slot_c) {
+    constexpr int sl = decltype(slot_c)::value;
+    const int ks = lks;
+    const int kcap = lleft > 0 ? kg : 0;           // no live stage left: every load out of range
+    const int64_t row0 = lrow * BM;
+    const int col0 = lcol * BN;
+    const __amdgpu_buffer_rsrc_t a_src =
+        make_rsrc(in + row0 * T * (int64_t)kg, (uint64_t)(nrows > row0 ? nrows - row0 : 0) * row_bytes);
+    const __amdgpu_buffer_rsrc_t b_src =
+        make_rsrc(wp + (int64_t)col0 * ksteps * SG * T, (uint64_t)(mg - col0) * (uint64_t)ksteps * BLOCK);
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
+    for (int ps = 0; ps < PA; ++ps) {
+      const uint32_t r = (uint32_t)(ps * RPP + rl);
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      const int m = col0 + wc * 32 * FN + fn * 32 + li;
-      const float bm = (bias != nullptr && m < mg) ? (float)bias[m] : 0.f;
+      for (int i = 0; i < U::kUnits; ++i) {
+        const int g = ks * SG + (q + 4 * i) * U::kGroupsPerUnit;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = row0 + wr * 32 * FM + fm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (row < nrows && m < mg) {
-          float f[T], y[T];
-#pragma unroll
-          for (int p = 0; p < T; ++p) f[p] = acc[p][fm][fn][r];
-          Grp<G>::idft(f, y);
-          if (bias != nullptr) {
-#pragma unroll
-            for (int t = 0; t < T; ++t) y[t] += bm;
-          }
-          if (act == 1) {
-#pragma unroll
-            for (int t = 0; t < T; ++t) y[t] = gelu_erf(y[t]);
-          }
-          store_group<E, T>(out + row * out_ld + T * (int64_t)m, y);
+        for (int h = 0; h < U::kPiecesPerUnit; ++h) {
+          const uint32_t off = g < kcap ? r * row_bytes + (uint32_t)g * (uint32_t)(T * sizeof(E)) + 16u * h : kOob;
+          ra[sl][ps][i * U::kPiecesPerUnit + h] = bload16(a_src, off);
         }
       }
     }
+#pragma unroll
+    for (int ps = 0; ps < PB; ++ps) {
+      const uint32_t m = (uint32_t)(ps * RPP + rl);
+#pragma unroll
+      for (int p = 0; p < T; ++p)
+        rb[sl][ps][p] =
+            bload16(b_src, kcap > 0 ? (m * (uint32_t)ksteps + (uint32_t)ks) * BLOCK + p * 64 + q * 16 : kOob);
+    }
+    // advance the cursor by one stage (selects only)
+    --lleft;
+    const bool wrap = ++lks == ksteps;
+    lks = wrap ? 0 : lks;
+    const int c = lcol + sr;
+    const bool carry = c >= tiles_n;
+    lcol = wrap ? (carry ? c - tiles_n : c) : lcol;
+    lrow = wrap ? lrow + sq + (carry ? 1 : 0) : lrow;
+  };
+  auto store = [&](char* buf, auto slot_c) {
+    constexpr int sl = decltype(slot_c)::value;
+#pragma unroll
+    for (int ps = 0; ps < PA; ++ps) {
+      const int r = ps * RPP + rl;
+      if (BM % RPP == 0 || r < BM) {
+        u32x4 pl[T];
+        pieces_to_planes<E, G, false>(ra[sl][ps], pl);
+#pragma unroll
+        for (int p = 0; p < T; ++p) st16(buf + p * A_PLANE + r * STRIDE + swz_slot(r, q) * 16, pl[p]);
+      }
+    }
+#pragma unroll
+    for (int ps = 0; ps < PB; ++ps) {
+      const int m = ps * RPP + rl;
+      if (BN % RPP == 0 || m < BN) {
+#pragma unroll
+        for (int p = 0; p < T; ++p)
+          st16(buf + T * A_PLANE + p * B_PLANE + m * STRIDE + swz_slot(m, q) * 16, rb[sl][ps][p]);
+      }
+    }
+  };
+
+  f32x16 acc[T][FM][FN];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int p = 0; p < T; ++p)
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) acc[p][fm][fn] = f32x16{};
+  };
+  zero_acc();
+
+  const int wr = wave / WN, wc = wave % WN;
+  const int li = lane & 31, lh = lane >> 5;
+  const int a_frag = (wr * 32 * FM + li) * STRIDE;
+  const int b_frag = T * A_PLANE + (wc * 32 * FN + li) * STRIDE;
+  const int c0 = swz_slot(li, lh) * 16, c1 = swz_slot(li, 2 + lh) * 16;
+
+  using S0 = std::integral_constant<int, 0>;
+  static_assert(PF == 1, "the persistent stream keeps one stage of loads in flight");
+  auto step = [&](int64_t gs) {
+    char* cur = lds + (NBUF == 2 ? (int)(gs & 1) * BUF : 0);
+    mma_chunk<E, G, false, FM, FN>(acc, cur + a_frag + c0, A_PLANE, cur + b_frag + c0, B_PLANE, STRIDE);
+    mma_chunk<E, G, false, FM, FN>(acc, cur + a_frag + c1, A_PLANE, cur + b_frag + c1, B_PLANE, STRIDE);
+    if constexpr (NBUF == 1) __syncthreads();
+    store(lds + (NBUF == 2 ? (int)((gs + 1) & 1) * BUF : 0), S0{});
+    load(S0{});
+    if constexpr (SCHED == 1 && NBUF == 2) interleave_schedule<E, G, FM, FN, PA, PB>();
+    __syncthreads();
+  };
+
+  load(S0{});
+  store(lds, S0{});
+  load(S0{});
+  __syncthreads();
+  int64_t gs = 0, tile = first;
+  for (int64_t j = 0; j < nt; ++j) {
+    for (int ks = 0; ks < ksteps; ++ks) step(gs++);
+    fwd_epilogue<E, G, FM, FN, WM, WN>(acc, (tile / tiles_n) * BM, (int)(tile % tiles_n) * BN, out, nrows, mg, bias,
+                                       act);
+    zero_acc();
+    tile += stride;
   }
 }
 
@@ -778,13 +937,21 @@ constexpr int fwd_waves_per_simd() {
   return (T * FM * FN >= 16 || (T == 8 && sizeof(E) == 2)) ? 1 : 2;
 }
 
-template <typename E, int G, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED>
+// PERSIST = 0: one workgroup per tile.  PERSIST = 1: a grid of resident
+// workgroups, each running every gridDim.x-th tile (fwd_stream); ntiles is the
+// tile count.
+template <typename E, int G, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED, int PERSIST>
 __global__ void __launch_bounds__(64 * WM * WN, (fwd_waves_per_simd<E, Grp<G>::kOrder, FM, FN>()))
 fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ out,
-           int64_t nrows, int kg, int mg, int tiles_n, const E* __restrict__ bias, int act) {
+           int64_t nrows, int kg, int mg, int tiles_n, const E* __restrict__ bias, int act, int64_t ntiles) {
   __shared__ __attribute__((aligned(16))) char lds[fwd_lds_bytes<E, Grp<G>::kOrder, FM, FN, WM, WN, NBUF>()];
-  fwd_tile<E, G, FM, FN, WM, WN, NBUF, PF, SCHED>(lds, xcd_logical_id(blockIdx.x, gridDim.x), in, wp, out, nrows,
-                                                  kg, mg, tiles_n, bias, act);
+  if constexpr (PERSIST) {
+    fwd_stream<E, G, FM, FN, WM, WN, NBUF, PF, SCHED>(lds, xcd_logical_id(blockIdx.x, gridDim.x), gridDim.x, ntiles,
+                                                      in, wp, out, nrows, kg, mg, tiles_n, bias, act);
+  } else {
+    fwd_tile<E, G, FM, FN, WM, WN, NBUF, PF, SCHED>(lds, xcd_logical_id(blockIdx.x, gridDim.x), in, wp, out, nrows,
+                                                    kg, mg, tiles_n, bias, act);
+  }
 }
 
 // ============================================================ dw partials
@@ -1074,18 +1241,38 @@ prepare_kernel(const E* __restrict__ w, E* __restrict__ dst, int mg, int ng) {
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-template <typename E, int G, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED>
+// Resident workgroups of one kernel on the current device (occupancy x CUs),
+// queried once per kernel instantiation.
+template <typename K>
+int64_t resident_workgroups(K kernel, int threads) {
+  static const int64_t n = [&] {
+    int dev = 0, per_cu = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return int64_t(0);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return int64_t(0);
+    return int64_t(per_cu) * prop.multiProcessorCount;
+  }();
+  return n;
+}
+
+template <typename E, int G, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED, int PERSIST>
 hipError_t launch_fwd_s(const void* in, const void* wp, void* out, int64_t nrows, int kg, int mg,
                         const void* bias, int act, hipStream_t s) {
   constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
   const int64_t tiles_m = cdiv(nrows, BM);
   const int tiles_n = (int)cdiv(mg, BN);
-  const int64_t grid = tiles_m * tiles_n;
-  if (grid <= 0) return hipSuccess;
+  const int64_t tiles = tiles_m * tiles_n;
+  if (tiles <= 0) return hipSuccess;
+  int64_t grid = tiles;
+  auto kernel = fwd_kernel<E, G, FM, FN, WM, WN, NBUF, PF, SCHED, PERSIST>;
+  if constexpr (PERSIST) {
+    const int64_t resident = resident_workgroups(kernel, 64 * WM * WN);
+    if (resident > 0 && resident < grid) grid = resident;
+  }
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_kernel<E, G, FM, FN, WM, WN, NBUF, PF, SCHED>), dim3((unsigned)grid), dim3(64 * WM * WN),
-                     0, s, static_cast<const E*>(in), static_cast<const E*>(wp), static_cast<E*>(out), nrows, kg, mg,
-                     tiles_n, static_cast<const E*>(bias), act);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(64 * WM * WN), 0, s, static_cast<const E*>(in),
+                     static_cast<const E*>(wp), static_cast<E*>(out), nrows, kg, mg, tiles_n,
+                     static_cast<const E*>(bias), act, tiles);
   return hipGetLastError();
 }
 

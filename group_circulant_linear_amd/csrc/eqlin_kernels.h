@@ -5,11 +5,17 @@
 
 namespace eqlin {
 
-// Forward tile codes: six digits FM FN WM WN NBUF PF.  A workgroup has WM x WN
-// waves; each wave owns FM x FN fragments of 32 x 32 per accumulator plane, so
-// the workgroup tile is (32 FM WM) rows x (32 FN WN) output groups; NBUF (1 or
-// 2) is the number of LDS stage buffers and PF (1 or 2) the number of stages
-// of global loads in flight in registers.
+// Forward tile codes: six digits FM FN WM WN NBUF PF, optionally a seventh P.
+// A workgroup has WM x WN waves; each wave owns FM x FN fragments of 32 x 32
+// per accumulator plane, so the workgroup tile is (32 FM WM) rows x (32 FN WN)
+// output groups; NBUF (1 or 2) is the number of LDS stage buffers, PF (1 or
+// 2) the number of stages of global loads in flight in registers, and P = 1
+// selects the persistent kernel (resident workgroups stream over the tiles).
+#define EQLIN_TILE_BASE(C) ((C) >= 1000000 ? (C) / 10 : (C))
+#define EQLIN_TILE_ARGS(C)                                                                                  \
+  EQLIN_TILE_BASE(C) / 100000, (EQLIN_TILE_BASE(C) / 10000) % 10, (EQLIN_TILE_BASE(C) / 1000) % 10,         \
+      (EQLIN_TILE_BASE(C) / 100) % 10, (EQLIN_TILE_BASE(C) / 10) % 10, EQLIN_TILE_BASE(C) % 10
+#define EQLIN_TILE_PERSIST(C) ((C) >= 1000000 ? (C) % 10 : 0)
 //
 // Group codes: 4 and 8 are the cyclic groups of that order (4: the p4
 // rotation group), kP4M the dihedral group p4m of order 8.

@@ -7,23 +7,23 @@
 
 namespace eqlin {
 
-// compiled forward tiles, code = FM FN WM WN NBUF PF (decimal digits)
+// compiled forward tiles, code = FM FN WM WN NBUF PF [P] (decimal digits)
 #define EQLIN_P4_TILES(X)                                                                                 \
   X(112221) X(111221) X(112121) X(222221) X(212421) X(112411) X(212211) X(122211) X(112211) X(112212)     \
-  X(112412) X(111211)
+  X(112412) X(111211) X(2124211) X(1122111) X(1122211) X(1112111)
 
 namespace {
 // EQLIN_SCHED=0 drops the explicit MFMA / memory interleave of the
 // double-buffered tiles (for comparisons).
-template <typename E, int FM, int FN, int WM, int WN, int NBUF, int PF>
+template <typename E, int FM, int FN, int WM, int WN, int NBUF, int PF, int P>
 hipError_t launch_fwd_p4(const void* in, const void* wp, void* out, int64_t nrows, int kg, int mg, const void* bias,
                          int act, hipStream_t s) {
   static const int sched = [] {
     const char* e = getenv("EQLIN_SCHED");
     return e ? atoi(e) : 1;
   }();
-  return sched == 1 ? launch_fwd_s<E, 4, FM, FN, WM, WN, NBUF, PF, 1>(in, wp, out, nrows, kg, mg, bias, act, s)
-                    : launch_fwd_s<E, 4, FM, FN, WM, WN, NBUF, PF, 0>(in, wp, out, nrows, kg, mg, bias, act, s);
+  return sched == 1 ? launch_fwd_s<E, 4, FM, FN, WM, WN, NBUF, PF, 1, P>(in, wp, out, nrows, kg, mg, bias, act, s)
+                    : launch_fwd_s<E, 4, FM, FN, WM, WN, NBUF, PF, 0, P>(in, wp, out, nrows, kg, mg, bias, act, s);
 }
 }  // namespace
 
@@ -41,12 +41,13 @@ bool Launch<4>::fwd_tile_known(int tile) {
 template <>
 hipError_t Launch<4>::forward(int dtype, int tile, const void* in, const void* wp, void* out, int64_t nrows, int kg,
                               int mg, const void* bias, int act, hipStream_t s) {
-#define EQLIN_CASE(C)                                                                                              \
-  case C:                                                                                                          \
-    return dtype == 0 ? launch_fwd_p4<float, C / 100000, (C / 10000) % 10, (C / 1000) % 10, (C / 100) % 10,         \
-                                      (C / 10) % 10, C % 10>(in, wp, out, nrows, kg, mg, bias, act, s)              \
-                      : launch_fwd_p4<_Float16, C / 100000, (C / 10000) % 10, (C / 1000) % 10, (C / 100) % 10,      \
-                                      (C / 10) % 10, C % 10>(in, wp, out, nrows, kg, mg, bias, act, s);
+#define EQLIN_CASE(C)                                                                                       \
+  case C:                                                                                                   \
+    return dtype == 0                                                                                       \
+               ? launch_fwd_p4<float, EQLIN_TILE_ARGS(C), EQLIN_TILE_PERSIST(C)>(in, wp, out, nrows, kg, mg, bias, \
+                                                                                 act, s)                   \
+               : launch_fwd_p4<_Float16, EQLIN_TILE_ARGS(C), EQLIN_TILE_PERSIST(C)>(in, wp, out, nrows, kg, mg,    \
+                                                                                    bias, act, s);
   switch (tile) {
     EQLIN_P4_TILES(EQLIN_CASE)
     default: return hipErrorInvalidValue;

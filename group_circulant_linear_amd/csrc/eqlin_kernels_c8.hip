@@ -5,10 +5,10 @@
 
 namespace eqlin {
 
-// compiled forward tiles, code = FM FN WM WN NBUF PF (decimal digits)
+// compiled forward tiles, code = FM FN WM WN NBUF PF [P] (decimal digits)
 // (the eight accumulators of a C8 tile rule out 8-wave workgroups with one
 // fragment per wave: 512 threads leave 256 registers per lane)
-#define EQLIN_C8_TILES(X) X(112211) X(112221) X(111221) X(212211) X(122211)
+#define EQLIN_C8_TILES(X) X(112211) X(112221) X(111221) X(212211) X(122211) X(1122111) X(1222111) X(2122111)
 
 template <>
 bool Launch<8>::fwd_tile_known(int tile) {
@@ -24,12 +24,12 @@ bool Launch<8>::fwd_tile_known(int tile) {
 template <>
 hipError_t Launch<8>::forward(int dtype, int tile, const void* in, const void* wp, void* out, int64_t nrows, int kg,
                               int mg, const void* bias, int act, hipStream_t s) {
-#define EQLIN_CASE(C)                                                                                               \
-  case C:                                                                                                           \
-    return dtype == 0 ? launch_fwd_s<float, 8, C / 100000, (C / 10000) % 10, (C / 1000) % 10, (C / 100) % 10,        \
-                                     (C / 10) % 10, C % 10, 1>(in, wp, out, nrows, kg, mg, bias, act, s)             \
-                      : launch_fwd_s<_Float16, 8, C / 100000, (C / 10000) % 10, (C / 1000) % 10, (C / 100) % 10,     \
-                                     (C / 10) % 10, C % 10, 1>(in, wp, out, nrows, kg, mg, bias, act, s);
+#define EQLIN_CASE(C)                                                                                      \
+  case C:                                                                                                  \
+    return dtype == 0 ? launch_fwd_s<float, 8, EQLIN_TILE_ARGS(C), 1, EQLIN_TILE_PERSIST(C)>(in, wp, out, nrows, kg,  \
+                                                                                          mg, bias, act, s) \
+                      : launch_fwd_s<_Float16, 8, EQLIN_TILE_ARGS(C), 1, EQLIN_TILE_PERSIST(C)>(in, wp, out, nrows,  \
+                                                                                             kg, mg, bias, act, s);
   switch (tile) {
     EQLIN_C8_TILES(EQLIN_CASE)
     default: return hipErrorInvalidValue;

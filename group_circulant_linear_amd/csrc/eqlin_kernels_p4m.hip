@@ -5,9 +5,9 @@
 
 namespace eqlin {
 
-// compiled forward tiles, code = FM FN WM WN NBUF PF (decimal digits)
+// compiled forward tiles, code = FM FN WM WN NBUF PF [P] (decimal digits)
 // (eight accumulators per fragment, as for C8)
-#define EQLIN_P4M_TILES(X) X(112211) X(112221) X(111221) X(212211) X(122211)
+#define EQLIN_P4M_TILES(X) X(112211) X(112221) X(111221) X(212211) X(122211) X(1122111) X(1222111) X(2122111)
 
 template <>
 bool Launch<kP4M>::fwd_tile_known(int tile) {
@@ -23,12 +23,12 @@ bool Launch<kP4M>::fwd_tile_known(int tile) {
 template <>
 hipError_t Launch<kP4M>::forward(int dtype, int tile, const void* in, const void* wp, void* out, int64_t nrows, int kg,
                               int mg, const void* bias, int act, hipStream_t s) {
-#define EQLIN_CASE(C)                                                                                               \
-  case C:                                                                                                           \
-    return dtype == 0 ? launch_fwd_s<float, kP4M, C / 100000, (C / 10000) % 10, (C / 1000) % 10, (C / 100) % 10,        \
-                                     (C / 10) % 10, C % 10, 1>(in, wp, out, nrows, kg, mg, bias, act, s)             \
-                      : launch_fwd_s<_Float16, kP4M, C / 100000, (C / 10000) % 10, (C / 1000) % 10, (C / 100) % 10,     \
-                                     (C / 10) % 10, C % 10, 1>(in, wp, out, nrows, kg, mg, bias, act, s);
+#define EQLIN_CASE(C)                                                                                      \
+  case C:                                                                                                  \
+    return dtype == 0 ? launch_fwd_s<float, kP4M, EQLIN_TILE_ARGS(C), 1, EQLIN_TILE_PERSIST(C)>(in, wp, out, nrows, kg,  \
+                                                                                          mg, bias, act, s) \
+                      : launch_fwd_s<_Float16, kP4M, EQLIN_TILE_ARGS(C), 1, EQLIN_TILE_PERSIST(C)>(in, wp, out, nrows,  \
+                                                                                             kg, mg, bias, act, s);
   switch (tile) {
     EQLIN_P4M_TILES(EQLIN_CASE)
     default: return hipErrorInvalidValue;

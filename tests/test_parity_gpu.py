@@ -157,7 +157,8 @@ def _forward_case(dt, N, C, D, seed=0, g=4):
 
 
 @pytest.mark.parametrize("tile", ["auto", "112221", "111221", "112121", "222221", "212421", "112411", "212211",
-                                  "122211", "112211", "112212", "112412"])
+                                  "122211", "112211", "112212", "112412", "111211", "2124211", "1122111", "1122211",
+                                  "1112111"])
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 def test_forward_small_shapes_all_tiles(dt, tile, monkeypatch):
     if tile != "auto":
@@ -169,7 +170,8 @@ def test_forward_small_shapes_all_tiles(dt, tile, monkeypatch):
         assert err <= TOL[dt], (N, C, D, err)
 
 
-@pytest.mark.parametrize("tile", ["auto", "112211", "112221", "111221", "212211", "122211"])
+@pytest.mark.parametrize("tile", ["auto", "112211", "112221", "111221", "212211", "122211", "1122111", "1222111",
+                                  "2122111"])
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 @pytest.mark.parametrize("g", [8, "p4m"])
 def test_forward_order8_small_shapes_all_tiles(g, dt, tile, monkeypatch):
