@@ -18,6 +18,10 @@ real products of N x D/4 x C/4, i.e. 0.75 NDC; for C8 (--group 8) fourteen of
 N x D/8 x C/8, i.e. 0.4375 NDC (in general 2NDC (2T - 2) / T^2); for p4m
 (--group p4m) twelve of N x D/8 x C/8, i.e. 0.375 NDC.
 
+The p4 group convolution workloads (--workload p4conv | p4conv_tiny) time
+the convolution's prepare, forward and backward the same way and print their
+own JSON line (metric: dense-equivalent K x K convolution TFLOP/s).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dtype f32|f16] [--group 4|8|p4m]
 """
 from __future__ import annotations
@@ -202,6 +206,181 @@ def mlp_block(args):
           flush=True)
 
 
+def conv_bench(args):
+    """p4 group convolution: prepare, forward and backward (dX and dpsi) of one
+    layer per step, timed phase by phase as the linear workloads; prints one
+    JSON line.  The metric is the forward dense-equivalent throughput
+    2 * P * (C K^2) * D / t_forward (P = N H W pixels: the FLOPs of the dense
+    K x K convolution with the expanded filter bank); the executed MFMA FLOPs
+    are those of the gathered group-circulant layer, 0.75 * P * C K^2 * D."""
+    import torch
+    from group_circulant_linear_amd import eqlin
+    from group_circulant_linear_amd.inputs import CONV_WORKLOADS, make_conv_inputs
+    from group_circulant_linear_amd.module import conv_dense_filter
+
+    wl = CONV_WORKLOADS[args.workload]
+    L = wl.layers[0]
+    dt = args.dtype or wl.dtypes[0]
+    tdt = torch.float32 if dt == "f32" else torch.float16
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    eqlin.load_library()
+    X, psi, dY = make_conv_inputs(L.N, L.H, L.W, L.C, L.D, L.K, dt, seed=0)
+    es = X.itemsize
+    P = L.N * L.H * L.W
+    ws_bytes = eqlin.eqconv_backward_workspace_bytes(L.N, L.H, L.W, L.C, L.D, L.K, tdt)
+    set_bytes = es * P * (2 * L.C + 2 * L.D) + ws_bytes
+    nsets = args.sets or max(2, int(np.ceil(600e6 / set_bytes)))
+    sets = []
+    for r in range(nsets):
+        sets.append(dict(X=torch.from_numpy(X).to(dev), psi=torch.from_numpy(psi).to(dev),
+                         dY=torch.from_numpy(dY).to(dev),
+                         buf=torch.empty(eqlin.eqconv_prepared_weight_bytes(L.C, L.D, L.K, tdt), dtype=torch.uint8,
+                                         device=dev),
+                         Y=torch.empty((L.N, L.H, L.W, L.D), dtype=tdt, device=dev),
+                         ws=torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)))
+    torch.cuda.synchronize()
+    phases = ("prepare", "forward") if args.forward_only else ("prepare", "forward", "backward")
+    prepared = [None] * nsets
+
+    def run_phase(ph, i0, count):
+        for i in range(i0, i0 + count):
+            b = sets[i % nsets]
+            if ph == "prepare":
+                prepared[i % nsets] = eqlin.eqconv_prepare_weights(b["psi"], out=b["buf"])
+            elif ph == "forward":
+                eqlin.eqconv_forward(b["X"], prepared[i % nsets], out=b["Y"])
+            else:
+                eqlin.eqconv_backward(b["dY"], b["X"], prepared[i % nsets], workspace=b["ws"])
+
+    def run_steps(i0, count, events=None):
+        for ph in phases:
+            if events is not None:
+                events[ph][0].record()
+            run_phase(ph, i0, count)
+            if events is not None:
+                events[ph][1].record()
+
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle:
+        run_steps(0, 2)
+        torch.cuda.synchronize()
+    if args.warmup:
+        run_steps(0, args.warmup)
+    torch.cuda.synchronize()
+    print(f"# warmup done ({args.warmup} steps after {args.settle} s of clock settle, {nsets} buffer sets)",
+          file=sys.stderr, flush=True)
+    K = args.steps
+    evs = {ph: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for ph in phases}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_steps(0, K, evs)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / K
+    us = {ph: evs[ph][0].elapsed_time(evs[ph][1]) * 1e3 / K for ph in phases}
+
+    ck = L.C * L.K * L.K
+    dense_flops = 2.0 * P * ck * L.D
+    value = dense_flops / (us["forward"] * 1e-6) / 1e12
+    exec_flops = 0.75 * P * ck * L.D
+    peak = PEAK_TFLOPS[dt]
+    achieved = exec_flops / (us["forward"] * 1e-6) / 1e12
+    alg_bytes = es * P * (L.C + L.D) + es * ck * L.D / 4
+    traffic = profiled_traffic(f"{wl.name}_{dt}", "eqlin::conv_fwd_kernel")
+    roofline = {"bound": "mfma", "kernel": "eqlin::conv_fwd_kernel", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": (round(traffic) if traffic else None), "traffic_algorithmic": round(alg_bytes),
+                "traffic_unit": "bytes per launch", "flops_per_launch": exec_flops}
+    layer = {"layer": L.name, "N": P, "C": ck, "D": L.D, "images": L.N, "H": L.H, "W": L.W, "C_in": L.C, "K": L.K}
+    for ph in phases:
+        layer[f"{ph}_us"] = round(us[ph], 2)
+    layer["fwd_tflops_dense_equiv"] = round(value, 2)
+    layer["fwd_mfma_frac"] = round(achieved / peak, 4)
+    if not args.forward_only:
+        layer["bwd_tflops_dense_equiv"] = round(2 * dense_flops / (us["backward"] * 1e-6) / 1e12, 2)
+
+    dense = None
+    if not args.no_dense:
+        # the dense K x K convolution with the expanded filter bank (MIOpen through torch), channels last
+        Wd = conv_dense_filter(sets[0]["psi"]).contiguous(memory_format=torch.channels_last)
+        xs = [sets[r]["X"].permute(0, 3, 1, 2) for r in range(nsets)]         # NCHW views, channels-last memory
+        gs = [sets[r]["dY"].permute(0, 3, 1, 2) for r in range(nsets)]
+        pad = L.K // 2
+        F = torch.nn.functional
+
+        def dfwd(i):
+            return F.conv2d(xs[i % nsets], Wd, padding=pad)
+
+        def dbwd(i):
+            return torch.ops.aten.convolution_backward(gs[i % nsets], xs[i % nsets], Wd, None, [1, 1], [pad, pad],
+                                                       [1, 1], False, [0, 0], 1, [True, True, False])
+
+        for i in range(3):
+            dfwd(i)
+            dbwd(i)
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        reps = max(5, K)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(reps):
+            dfwd(i)
+        e1.record()
+        for i in range(reps):
+            dbwd(i)
+        e2.record()
+        torch.cuda.synchronize()
+        tf = e0.elapsed_time(e1) * 1e3 / reps
+        tb = e1.elapsed_time(e2) * 1e3 / reps
+        dense = {"fwd_us": round(tf, 2), "fwd_tflops": round(dense_flops / (tf * 1e-6) / 1e12, 2),
+                 "fwd_speedup": round(tf / us["forward"], 3), "bwd_us": round(tb, 2),
+                 "bwd_speedup": (round(tb / us["backward"], 3) if not args.forward_only else None),
+                 "what": "torch conv2d / convolution_backward (MIOpen) with the expanded K x K filter bank, "
+                         "channels-last, same dtype"}
+        del Wd
+
+    if args.copy_calibration_mb:
+        nb = args.copy_calibration_mb * (1 << 20)
+        src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            cores = os.cpu_count() or 1
+        flops, elapsed, n = 0.0, 0.0, 0
+        while elapsed < 10.0:
+            t = time.perf_counter()
+            oracle.conv_forward(X[n % L.N:n % L.N + 1], psi)
+            elapsed += time.perf_counter() - t
+            flops += 2.0 * L.H * L.W * ck * L.D
+            n += 1
+        cpu = {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+               "sample": f"fp64 oracle conv_forward on single {L.H}x{L.W} images ({n} images, {elapsed:.1f} s)"}
+
+    out = {
+        "metric": "p4 group conv fwd dense-equiv TFLOP/s (2 P C K^2 D) + % MFMA peak", "value": round(value, 3),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description, "dtype": dt,
+                   "layers": [{"name": L.name, "N": L.N, "H": L.H, "W": L.W, "C": L.C, "D": L.D, "K": L.K}],
+                   "group": "4", "T": 4,
+                   "step": "prepare+forward" if args.forward_only else "prepare+forward+dX+dpsi",
+                   "buffer_sets": nsets},
+        "fwd_mfma_frac": round(achieved / peak, 4), "roofline": roofline, "cpu_baseline": cpu,
+        "dense_gemm": dense, "per_layer": [layer],
+    }
+    if args.forward_only:
+        out["note"] = "forward-only profiling run, not a bench line"
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -209,6 +388,10 @@ def main():
         sys.exit(2)
     if args.mlp_block:
         mlp_block(args)
+        return
+    from group_circulant_linear_amd.inputs import CONV_WORKLOADS
+    if args.workload in CONV_WORKLOADS:
+        conv_bench(args)
         return
 
     import torch

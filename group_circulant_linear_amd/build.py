@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libeqlin.so")
-SOURCES = ("eqlin_api.hip", "eqlin_kernels.hip", "eqlin_kernels_c8.hip", "eqlin_kernels_p4m.hip")
+SOURCES = ("eqlin_api.hip", "eqlin_kernels.hip", "eqlin_kernels_c8.hip", "eqlin_kernels_p4m.hip", "eqconv_kernels.hip")
 ARCH = "gfx950"
 
 

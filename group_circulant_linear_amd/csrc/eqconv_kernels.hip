@@ -1,0 +1,278 @@
+// Kernels and launchers of the p4 group convolution.  The convolution is one
+// group-circulant layer over a rotation-aware gather of each output pixel's
+// K x K window (ConvGeom in eqlin_device.h):
+//   - forward and dX: the forward tile of the linear layer with the gather
+//     done by its A-side loads (no gathered copy in global memory);
+//   - filter preparation: the group DFT of the gathered layer's weight, read
+//     from the filter through the block decode (forward and adjoint sets);
+//   - filter gradient: the gathered rows written out once, the linear layer's
+//     dw reduction over them, and a scatter of that gradient onto the filter.
+#include <stdlib.h>
+
+#include "eqlin_device.h"
+#include "eqlin_kernels.h"
+
+namespace eqlin {
+
+// compiled convolution tiles (the p4 tile table's candidates), code = FM FN WM WN NBUF PF
+#define EQCONV_TILES(X) X(112211) X(112221) X(111211) X(212421) X(111221)
+
+namespace {
+
+template <typename E>
+ConvGeom make_geom(int H, int W, int cpix, int K, int64_t npix) {
+  constexpr int G = Units<E, 4>::kGroupsPerUnit;
+  ConvGeom g;
+  g.H = H;
+  g.W = W;
+  g.cpix = cpix;
+  g.p = K / 2;
+  g.ncb = cpix / (4 * G);
+  g.bpo = cpix / G;
+  g.nblk = cpix * K * K / (4 * G);
+  g.inv_bpo = 1.0f / (float)g.bpo;
+  g.inv_p1 = 1.0f / (float)(g.p + 1);
+  g.in_bytes = (uint32_t)(npix * (int64_t)cpix * 4 * (int64_t)sizeof(E));
+  return g;
+}
+
+// R^r (a, b) with R(a, b) = (-b, a)
+__device__ __forceinline__ void turn_tap(int r, int& a, int& b) {
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    if (k < (r & 3)) {
+      const int t = a;
+      a = -b;
+      b = t;
+    }
+  }
+}
+
+// Gathered-layer group channel g (of a row padded to whole stages) -> the
+// filter entries of its weight w_lin[.][g][u], u = 0..3: input channel c,
+// tap (ti, tj) and group offset v per u.  Centre: psi[., c, 0, u].  Orbit
+// block with shift b = unit i: psi[., c, R^-u delta_o, (u - b) mod 4]
+// (each filter entry feeds exactly one (g, u)).  Returns false for the
+// padding of a partial last stage.
+template <int G>
+__device__ __forceinline__ bool conv_weight_source(int g, const ConvGeom& geo, int& c, int (&ti)[4], int (&tj)[4],
+                                                   int (&v)[4]) {
+  constexpr int SG = 16 * G;
+  const int w = (g % SG) / G;  // unit position q + 4 i in the stage
+  const int cb = (g / SG) * 4 + (w & 3), i = w >> 2, e = g % G;
+  const ConvBlock k = conv_block<G>(cb, geo);
+  c = k.centre ? k.ch0 + G * i + e : k.ch0 + e;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int mu = (4 - u) & 3;  // R^-u = R^(4 - u)
+    ti[u] = k.di[mu];
+    tj[u] = k.dj[mu];
+    v[u] = k.centre ? u : ((u - i) & 3);
+  }
+  return k.live;
+}
+
+}  // namespace
+
+// Forward (or dX) tile with the gather in its loads.
+template <typename E, int FM, int FN, int WM, int WN, int NBUF, int PF>
+__global__ void __launch_bounds__(64 * WM * WN, (fwd_waves_per_simd<E, 4, FM, FN>()))
+conv_fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ out, int64_t npix, int kg,
+                int mg, int tiles_n, const E* __restrict__ bias, int act, ConvGeom geo) {
+  __shared__ __attribute__((aligned(16))) char lds[fwd_lds_bytes<E, 4, FM, FN, WM, WN, NBUF>()];
+  fwd_tile<E, 4, FM, FN, WM, WN, NBUF, PF, 1, true>(lds, xcd_logical_id(blockIdx.x, gridDim.x), in, wp, out, npix,
+                                                    kg, mg, tiles_n, bias, act, geo);
+}
+
+// Prepared spectra of the gathered layer, in the stage-block layout of the
+// linear layer (rows x stages x 4 planes x SG slots).  Forward (kAdj false):
+// rows = D', w_lin[d'][g][u] = psi[d', c, tap, v] with (c, tap, v) from the
+// block decode over C' input channels.  Adjoint (kAdj true, the dX pass is a
+// convolution of dY): rows = C', the decode runs over D' channels, and the
+// filter is psi'[c', d', delta, v] = psi[d', c', -R^v delta, -v mod 4].
+template <typename E, bool kAdj>
+__global__ void __launch_bounds__(kThreads)
+conv_prepare_kernel(const E* __restrict__ psi, E* __restrict__ dst, int rows, int kg, int Cp, int K, ConvGeom geo) {
+  constexpr int SG = Traits<E>::kStageGroups, T = 4;
+  constexpr int G = Units<E, T>::kGroupsPerUnit;
+  const int nks = kg / SG;
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= (int64_t)rows * nks * SG) return;
+  const int s = (int)(idx % SG);
+  const int64_t t = idx / SG;
+  const int ks = (int)(t % nks);
+  const int row = (int)(t / nks);
+  const int g = ks * SG + slot_group<E, T>(s);
+  float f[T] = {0.f, 0.f, 0.f, 0.f};
+  int c, ti[4], tj[4], v[4];
+  if (conv_weight_source<G>(g, geo, c, ti, tj, v)) {
+    const int p = K / 2;
+    float z[T];
+#pragma unroll
+    for (int u = 0; u < T; ++u) {
+      int64_t src;
+      if constexpr (!kAdj) {
+        src = ((((int64_t)row * Cp + c) * K + ti[u] + p) * K + tj[u] + p) * 4 + v[u];
+      } else {
+        int a = ti[u], b = tj[u];
+        turn_tap(v[u], a, b);
+        src = ((((int64_t)c * Cp + row) * K + (p - a)) * K + (p - b)) * 4 + ((-v[u]) & 3);
+      }
+      z[u] = (float)psi[src];
+    }
+    Grp<4>::dft(z, f);
+  }
+  E* o = dst + ((int64_t)row * nks + ks) * T * SG + s;
+#pragma unroll
+  for (int q = 0; q < T; ++q) o[q * SG] = (E)f[q];
+}
+
+// Whole gathered rows xlin [npix][kg][4] for the filter gradient (padding of
+// a partial last stage written as zeros).  One thread per (pixel, block).
+template <typename E>
+__global__ void __launch_bounds__(kThreads)
+conv_gather_kernel(const E* __restrict__ in, E* __restrict__ xlin, int64_t npix, int kg, ConvGeom geo) {
+  constexpr int T = 4, G = Units<E, T>::kGroupsPerUnit, SG = 16 * G;
+  const int bpr = kg / (4 * G);  // blocks per padded row
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= npix * bpr) return;
+  const int64_t n = idx / bpr;
+  const int cb = (int)(idx - n * bpr);
+  const ConvBlock k = conv_block<G>(cb, geo);
+  const int hw = geo.H * geo.W;
+  const int img = (int)(n / hw), rem = (int)(n - (int64_t)img * hw);
+  const int y = rem / geo.W, x = rem - y * geo.W;
+  const char* base = reinterpret_cast<const char*>(in) + n * (int64_t)geo.cpix * T * (int64_t)sizeof(E);
+  u32x4 M[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool ok = k.live && (unsigned)(y + k.di[i]) < (unsigned)geo.H && (unsigned)(x + k.dj[i]) < (unsigned)geo.W;
+    const int64_t delta =
+        ((int64_t)(k.di[i] * geo.W + k.dj[i]) * geo.cpix + k.ch0 + k.chstep * i) * T * (int64_t)sizeof(E);
+    M[i] = ok ? *reinterpret_cast<const u32x4*>(base + delta) : u32x4{0u, 0u, 0u, 0u};
+  }
+  u32x4 pc[4];
+  conv_diag<E>(M, k.centre, pc);
+  char* orow = reinterpret_cast<char*>(xlin) + n * (int64_t)kg * T * (int64_t)sizeof(E);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = (cb / 4) * SG + G * ((cb & 3) + 4 * i);
+    *reinterpret_cast<u32x4*>(orow + (int64_t)j * T * sizeof(E)) = pc[i];
+  }
+}
+
+// Filter gradient from the gathered layer's dw: dpsi[d'][c][tap][v] =
+// dwlin[d'][g][u] through the block decode (a permutation).
+template <typename E>
+__global__ void __launch_bounds__(kThreads)
+conv_dw_scatter_kernel(const float* __restrict__ dwlin, float* __restrict__ dpsi, int Dp, int kg, int Cp, int K,
+                       ConvGeom geo) {
+  constexpr int G = Units<E, 4>::kGroupsPerUnit;
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= (int64_t)Dp * kg) return;
+  const int d = (int)(idx / kg), g = (int)(idx % kg);
+  int c, ti[4], tj[4], v[4];
+  if (!conv_weight_source<G>(g, geo, c, ti, tj, v)) return;
+  const int p = K / 2;
+  const f32x4 src = *reinterpret_cast<const f32x4*>(dwlin + idx * 4);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    dpsi[((((int64_t)d * Cp + c) * K + ti[u] + p) * K + tj[u] + p) * 4 + v[u]] = src[u];
+}
+
+namespace {
+
+template <typename E, int FM, int FN, int WM, int WN, int NBUF, int PF>
+hipError_t launch_conv_fwd(const void* in, const void* wp, void* out, int64_t npix, int H, int W, int cpix, int K,
+                           int mg, const void* bias, int act, hipStream_t s) {
+  constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
+  const int64_t tiles = cdiv(npix, BM) * cdiv(mg, BN);
+  if (tiles <= 0) return hipSuccess;
+  if (tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const ConvGeom g = make_geom<E>(H, W, cpix, K, npix);
+  const int kg = conv_gathered_groups(cpix, K, sizeof(E) == 4 ? 0 : 1);
+  hipLaunchKernelGGL((conv_fwd_kernel<E, FM, FN, WM, WN, NBUF, PF>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0, s,
+                     static_cast<const E*>(in), static_cast<const E*>(wp), static_cast<E*>(out), npix, kg, mg,
+                     (int)cdiv(mg, BN), static_cast<const E*>(bias), act, g);
+  return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_conv_prepare(const void* psi, void* wf, void* wb, int Dp, int Cp, int K, hipStream_t s) {
+  const int dt = sizeof(E) == 4 ? 0 : 1;
+  const int kgf = conv_gathered_groups(Cp, K, dt), kgb = conv_gathered_groups(Dp, K, dt);
+  const ConvGeom gf = make_geom<E>(1, 1, Cp, K, 0), gb = make_geom<E>(1, 1, Dp, K, 0);
+  const int64_t nf = (int64_t)Dp * kgf, nb = (int64_t)Cp * kgb;
+  hipLaunchKernelGGL((conv_prepare_kernel<E, false>), dim3((unsigned)cdiv(nf, kThreads)), dim3(kThreads), 0, s,
+                     static_cast<const E*>(psi), static_cast<E*>(wf), Dp, kgf, Cp, K, gf);
+  hipLaunchKernelGGL((conv_prepare_kernel<E, true>), dim3((unsigned)cdiv(nb, kThreads)), dim3(kThreads), 0, s,
+                     static_cast<const E*>(psi), static_cast<E*>(wb), Cp, kgb, Cp, K, gb);
+  return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_conv_gather(const void* in, void* xlin, int64_t npix, int H, int W, int cpix, int K,
+                              hipStream_t s) {
+  const int kg = conv_gathered_groups(cpix, K, sizeof(E) == 4 ? 0 : 1);
+  const int64_t n = npix * (kg / (4 * Units<E, 4>::kGroupsPerUnit));
+  if (n <= 0) return hipSuccess;
+  if (cdiv(n, kThreads) > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((conv_gather_kernel<E>), dim3((unsigned)cdiv(n, kThreads)), dim3(kThreads), 0, s,
+                     static_cast<const E*>(in), static_cast<E*>(xlin), npix, kg, make_geom<E>(H, W, cpix, K, npix));
+  return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_conv_dw_scatter(const float* dwlin, float* dpsi, int Dp, int Cp, int K, hipStream_t s) {
+  const int kg = conv_gathered_groups(Cp, K, sizeof(E) == 4 ? 0 : 1);
+  const int64_t n = (int64_t)Dp * kg;
+  hipLaunchKernelGGL((conv_dw_scatter_kernel<E>), dim3((unsigned)cdiv(n, kThreads)), dim3(kThreads), 0, s, dwlin,
+                     dpsi, Dp, kg, Cp, K, make_geom<E>(1, 1, Cp, K, 0));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool ConvLaunch::tile_known(int tile) {
+  switch (tile) {
+#define EQCONV_CASE(C) case C:
+    EQCONV_TILES(EQCONV_CASE)
+#undef EQCONV_CASE
+    return true;
+    default: return false;
+  }
+}
+
+hipError_t ConvLaunch::forward(int dtype, int tile, const void* in, const void* wp, void* out, int64_t npix, int H,
+                               int W, int cpix, int K, int mg, const void* bias, int act, hipStream_t s) {
+#define EQCONV_CASE(C)                                                                                         \
+  case C:                                                                                                      \
+    return dtype == 0 ? launch_conv_fwd<float, EQLIN_TILE_ARGS(C)>(in, wp, out, npix, H, W, cpix, K, mg, bias,  \
+                                                                   act, s)                                     \
+                      : launch_conv_fwd<_Float16, EQLIN_TILE_ARGS(C)>(in, wp, out, npix, H, W, cpix, K, mg,     \
+                                                                      bias, act, s);
+  switch (tile) {
+    EQCONV_TILES(EQCONV_CASE)
+    default: return hipErrorInvalidValue;
+  }
+#undef EQCONV_CASE
+}
+
+hipError_t ConvLaunch::prepare(int dtype, const void* psi, void* wf, void* wb, int Dp, int Cp, int K,
+                               hipStream_t s) {
+  return dtype == 0 ? launch_conv_prepare<float>(psi, wf, wb, Dp, Cp, K, s)
+                    : launch_conv_prepare<_Float16>(psi, wf, wb, Dp, Cp, K, s);
+}
+
+hipError_t ConvLaunch::gather(int dtype, const void* in, void* xlin, int64_t npix, int H, int W, int cpix, int K,
+                              hipStream_t s) {
+  return dtype == 0 ? launch_conv_gather<float>(in, xlin, npix, H, W, cpix, K, s)
+                    : launch_conv_gather<_Float16>(in, xlin, npix, H, W, cpix, K, s);
+}
+
+hipError_t ConvLaunch::dw_scatter(int dtype, const float* dwlin, float* dpsi, int Dp, int Cp, int K, hipStream_t s) {
+  return dtype == 0 ? launch_conv_dw_scatter<float>(dwlin, dpsi, Dp, Cp, K, s)
+                    : launch_conv_dw_scatter<_Float16>(dwlin, dpsi, Dp, Cp, K, s);
+}
+
+}  // namespace eqlin

@@ -1,10 +1,12 @@
-// C ABI of the group-circulant linear layer (cyclic groups of order 4 and 8):
-// argument validation, tile choice and kernel launches.  The contract of every entry point is stated in
-// include/eqlin.h.
+// C ABI of the group-circulant linear layer (cyclic groups of order 4 and 8,
+// the dihedral group p4m) and of the p4 group convolution built on it:
+// argument validation, tile choice and kernel launches.  The contract of
+// every entry point is stated in include/eqlin.h and include/eqconv.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
 
+#include "eqconv.h"
 #include "eqlin.h"
 #include "eqlin_kernels.h"
 
@@ -81,6 +83,8 @@ constexpr TileShape kC8F16Tiles[] = {
 // Forward tile choice: workgroups are spread round-robin over the CUs, so a
 // CU's work is ceil(tiles / CUs) tiles; minimise that work divided by the
 // tile's efficiency.  EQLIN_FWD_TILE overrides (any compiled tile code).
+int choose_from_table(const TileShape* tiles, int ntiles, int64_t nrows, int mg);
+
 int choose_fwd_tile(int T, int dtype, int64_t nrows, int mg) {
   if (const char* env = getenv("EQLIN_FWD_TILE")) {
     const int t = atoi(env);
@@ -93,6 +97,22 @@ int choose_fwd_tile(int T, int dtype, int64_t nrows, int mg) {
                                    : int(sizeof(kP4F16Tiles) / sizeof(TileShape)))
                             : (f32 ? int(sizeof(kC8F32Tiles) / sizeof(TileShape))
                                    : int(sizeof(kC8F16Tiles) / sizeof(TileShape)));
+  return choose_from_table(tiles, ntiles, nrows, mg);
+}
+
+// The p4 convolution runs the p4 forward tiles (one workgroup per tile);
+// EQCONV_FWD_TILE overrides the choice (any tile compiled for it).
+int choose_conv_tile(int dtype, int64_t npix, int mg) {
+  if (const char* env = getenv("EQCONV_FWD_TILE")) {
+    const int t = atoi(env);
+    if (eqlin::ConvLaunch::tile_known(t)) return t;
+  }
+  return dtype == EQLIN_F32
+             ? choose_from_table(kP4F32Tiles, int(sizeof(kP4F32Tiles) / sizeof(TileShape)), npix, mg)
+             : choose_from_table(kP4F16Tiles, int(sizeof(kP4F16Tiles) / sizeof(TileShape)), npix, mg);
+}
+
+int choose_from_table(const TileShape* tiles, int ntiles, int64_t nrows, int mg) {
   int best = tiles[0].code;
   double best_cost = 1e300;
   for (int i = 0; i < ntiles; ++i) {
@@ -143,11 +163,65 @@ DwPlan plan_dw(int64_t N, int C, int D, int O, int dtype) {
   return p;
 }
 
+// ------------------------------------------------ p4 group convolution
+
+int check_conv_shape(int64_t N, int H, int W, int C, int D, int K, int dtype) {
+  if (dtype != EQLIN_F32 && dtype != EQLIN_F16) return EQLIN_EINVAL;
+  if (N < 0 || H < 0 || W < 0 || C <= 0 || D <= 0 || (C % 4) != 0 || (D % 4) != 0) return EQLIN_EINVAL;
+  if (K <= 0 || (K % 2) == 0) return EQLIN_EINVAL;
+  if (K > 15) return EQLIN_ENOTSUP;
+  // whole centre blocks: 4 group channels per 16-byte load group of 1 (f32) or 2 (f16)
+  const int blk = dtype == EQLIN_F32 ? 4 : 8;
+  if (((C / 4) % blk) != 0 || ((D / 4) % blk) != 0) return EQLIN_ENOTSUP;
+  return EQLIN_OK;
+}
+
+// pixels of a batch, or -1 when N H W does not fit the 32-bit tile grid
+int64_t conv_pixels(int64_t N, int H, int W) {
+  if (N == 0 || H == 0 || W == 0) return 0;
+  const int64_t hw = int64_t(H) * W;
+  if (hw > (int64_t(1) << 31) || N > (int64_t(1) << 31) / hw) return -1;
+  return N * hw;
+}
+
+size_t conv_set_bytes(int rows, int cpix, int K, int dtype) {
+  return plane_set_bytes(rows, eqlin::conv_gathered_groups(cpix, K, dtype), 4, dtype);
+}
+
+size_t conv_adjoint_offset(int C, int D, int K, int dtype) {
+  return (conv_set_bytes(D / 4, C / 4, K, dtype) + 255u) & ~size_t(255);
+}
+
+// the prepared rows of a launch must stay inside 32-bit buffer offsets of one workgroup tile
+bool conv_weights_fit(int cpix, int K, int dtype) {
+  const int64_t wrow = cdiv(eqlin::conv_gathered_groups(cpix, K, dtype), eqlin::stage_groups(dtype)) * 64 * 4;
+  return 256 * wrow < kMaxTileBytes;
+}
+
+bool conv_map_fits(int64_t npix, int C, int dtype) { return npix * C * elem_bytes(dtype) < (int64_t(1) << 31); }
+
+// Filter-gradient workspace: gathered rows, the gathered layer's dw, split partials.
+struct ConvWs {
+  size_t xlin, dwlin, split, total;
+  DwPlan plan;
+};
+
+ConvWs conv_workspace(int64_t npix, int C, int D, int K, int dtype) {
+  ConvWs w{};
+  const int kg = eqlin::conv_gathered_groups(C / 4, K, dtype);
+  w.plan = plan_dw(npix, 4 * kg, D, 4, dtype);
+  w.xlin = (static_cast<size_t>(npix) * kg * 4 * elem_bytes(dtype) + 255u) & ~size_t(255);
+  w.dwlin = (static_cast<size_t>(D / 4) * kg * 4 * sizeof(float) + 255u) & ~size_t(255);
+  w.split = static_cast<size_t>(w.plan.nsplit) * 4u * kg * static_cast<size_t>(D / 4) * sizeof(float);
+  w.total = w.xlin + w.dwlin + w.split;
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
 
-int eqlin_version(void) { return 200; }
+int eqlin_version(void) { return 210; }
 
 const char* eqlin_status_str(int status) {
   switch (status) {
@@ -279,6 +353,105 @@ int eqlin_backward(const void* dY, const void* X, int64_t N, int C, int D, int T
     if (st != EQLIN_OK) return st;
   }
   if (dw) return eqlin_backward_dw(dY, X, N, C, D, T, dw, workspace, workspace_bytes, dtype, stream);
+  return EQLIN_OK;
+}
+
+// ------------------------------------------------ p4 group convolution
+
+size_t eqconv_prepared_weight_bytes(int C, int D, int K, int dtype) {
+  if (check_conv_shape(0, 0, 0, C, D, K, dtype) != EQLIN_OK) return 0;
+  return conv_adjoint_offset(C, D, K, dtype) + conv_set_bytes(C / 4, D / 4, K, dtype);
+}
+
+size_t eqconv_prepared_adjoint_offset(int C, int D, int K, int dtype) {
+  if (check_conv_shape(0, 0, 0, C, D, K, dtype) != EQLIN_OK) return 0;
+  return conv_adjoint_offset(C, D, K, dtype);
+}
+
+int eqconv_prepare_weights(const void* psi, int C, int D, int K, int dtype, void* prepared, size_t prepared_bytes,
+                           void* stream) {
+  const int st = check_conv_shape(0, 0, 0, C, D, K, dtype);
+  if (st != EQLIN_OK) return st;
+  if (!psi || !prepared) return EQLIN_EINVAL;
+  if (!aligned16(psi) || !aligned16(prepared)) return EQLIN_EALIGN;
+  if (prepared_bytes < eqconv_prepared_weight_bytes(C, D, K, dtype)) return EQLIN_EWORKSPACE;
+  char* base = static_cast<char*>(prepared);
+  return hip_status(eqlin::ConvLaunch::prepare(dtype, psi, base, base + conv_adjoint_offset(C, D, K, dtype), D / 4,
+                                               C / 4, K, static_cast<hipStream_t>(stream)));
+}
+
+int eqconv_forward(const void* X, int64_t N, int H, int W, int C, int D, int K, const void* prepared,
+                   const void* bias, int act, void* Y, int dtype, void* stream) {
+  const int st = check_conv_shape(N, H, W, C, D, K, dtype);
+  if (st != EQLIN_OK) return st;
+  if (act != EQLIN_ACT_NONE && act != EQLIN_ACT_GELU) return EQLIN_EINVAL;
+  const int64_t npix = conv_pixels(N, H, W);
+  if (npix < 0) return EQLIN_ENOTSUP;
+  if (npix == 0) return EQLIN_OK;
+  if (!X || !prepared || !Y) return EQLIN_EINVAL;
+  if (!aligned16(X) || !aligned16(prepared) || !aligned16(Y)) return EQLIN_EALIGN;
+  if (bias && (reinterpret_cast<uintptr_t>(bias) % elem_bytes(dtype)) != 0) return EQLIN_EALIGN;
+  if (!conv_map_fits(npix, C, dtype) || !conv_weights_fit(C / 4, K, dtype)) return EQLIN_ENOTSUP;
+  const int tile = choose_conv_tile(dtype, npix, D / 4);
+  return hip_status(eqlin::ConvLaunch::forward(dtype, tile, X, prepared, Y, npix, H, W, C / 4, K, D / 4, bias, act,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+size_t eqconv_backward_workspace_bytes(int64_t N, int H, int W, int C, int D, int K, int dtype) {
+  if (check_conv_shape(N, H, W, C, D, K, dtype) != EQLIN_OK) return 0;
+  const int64_t npix = conv_pixels(N, H, W);
+  if (npix < 0) return 0;
+  return conv_workspace(npix, C, D, K, dtype).total;
+}
+
+int eqconv_backward(const void* dY, const void* X, int64_t N, int H, int W, int C, int D, int K,
+                    const void* prepared, void* dX, float* dpsi, void* workspace, size_t workspace_bytes, int dtype,
+                    void* stream) {
+  const int st = check_conv_shape(N, H, W, C, D, K, dtype);
+  if (st != EQLIN_OK) return st;
+  if (!dX && !dpsi) return EQLIN_EINVAL;
+  const int64_t npix = conv_pixels(N, H, W);
+  if (npix < 0) return EQLIN_ENOTSUP;
+  // validate both halves before launching either
+  if (dX && npix > 0) {
+    if (!dY || !prepared) return EQLIN_EINVAL;
+    if (!aligned16(dY) || !aligned16(prepared) || !aligned16(dX)) return EQLIN_EALIGN;
+    if (!conv_map_fits(npix, D, dtype) || !conv_weights_fit(D / 4, K, dtype)) return EQLIN_ENOTSUP;
+  }
+  ConvWs ws{};
+  if (dpsi) {
+    if (!workspace) return EQLIN_EINVAL;
+    if (npix > 0 && (!dY || !X)) return EQLIN_EINVAL;
+    if (!aligned16(dpsi) || !aligned16(workspace)) return EQLIN_EALIGN;
+    if (npix > 0 && (!aligned16(dY) || !aligned16(X))) return EQLIN_EALIGN;
+    ws = conv_workspace(npix, C, D, K, dtype);
+    if (workspace_bytes < ws.total) return EQLIN_EWORKSPACE;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dX && npix > 0) {
+    // dX: the convolution of dY with the adjoint filter (input D', output C')
+    const char* wb = static_cast<const char*>(prepared) + conv_adjoint_offset(C, D, K, dtype);
+    const int tile = choose_conv_tile(dtype, npix, C / 4);
+    const int e = hip_status(eqlin::ConvLaunch::forward(dtype, tile, dY, wb, dX, npix, H, W, D / 4, K, C / 4, nullptr,
+                                                        EQLIN_ACT_NONE, s));
+    if (e != EQLIN_OK) return e;
+  }
+  if (dpsi) {
+    char* wsb = static_cast<char*>(workspace);
+    float* dwlin = reinterpret_cast<float*>(wsb + ws.xlin);
+    float* split = reinterpret_cast<float*>(wsb + ws.xlin + ws.dwlin);
+    const int kg = eqlin::conv_gathered_groups(C / 4, K, dtype);
+    if (npix > 0) {
+      const int e = hip_status(eqlin::ConvLaunch::gather(dtype, X, wsb, npix, H, W, C / 4, K, s));
+      if (e != EQLIN_OK) return e;
+    }
+    // the gathered layer's dw (zeros for an empty batch), then onto the filter
+    int e = hip_status(eqlin::Launch<4>::dw(dtype, dY, wsb, split, dwlin, npix, D / 4, kg, ws.plan.rows_per_split,
+                                            ws.plan.nsplit, s));
+    if (e != EQLIN_OK) return e;
+    e = hip_status(eqlin::ConvLaunch::dw_scatter(dtype, dwlin, dpsi, D / 4, C / 4, K, s));
+    if (e != EQLIN_OK) return e;
+  }
   return EQLIN_OK;
 }
 

@@ -643,15 +643,101 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[Grp<G>::kOrder]
   }
 }
 
+// ============================================================ p4 group convolution gather
+//
+// A p4 group convolution with a K x K filter (K = 2p + 1) is one group-
+// circulant layer over a gathered row per output pixel.  The row's group
+// channels are the centre taps (channel c', rotations m = 0..3 read at the
+// pixel itself) and, for every quarter-turn orbit {R^m delta_o, m = 0..3} of
+// the other taps (delta_o = (a, b), a = 1..p, b = 0..p; R(a, b) = (-b, a))
+// and every shift b of the rotation axis, the four values
+// f[x + R^m delta_o, c', (m + b) mod 4].  The lane slot of a stage is filled
+// by one block: a centre block holds 4 G consecutive channels at the pixel
+// (G = group channels per 16-byte load), an orbit block the G channels
+// cg G .. cg G + G - 1 at the four taps of one orbit, one 16-byte load per
+// tap; the shifts b are the diagonals of those loads' (tap, rotation) values.
+// Block cb's unit i lands at group channel (cb / 4) 16 G + G (cb % 4 + 4 i).
+struct ConvGeom {
+  int H, W;              // image height and width (pixels)
+  int cpix;              // group channels per input pixel
+  int p;                 // filter half width
+  int ncb;               // centre blocks: cpix / (4 G)
+  int bpo;               // blocks per orbit: cpix / G
+  int nblk;              // blocks per gathered row: cpix K^2 / (4 G)
+  float inv_bpo, inv_p1; // 1 / bpo and 1 / (p + 1), for the block decode
+  uint32_t in_bytes;     // bytes of the input map (< 2^31)
+};
+
+struct ConvBlock {
+  int ch0, chstep;  // group channel of unit i: ch0 + chstep i
+  int di[4], dj[4]; // tap of unit i (pixel offset)
+  bool live, centre;
+};
+
+// floor(n / d) for 0 <= n < 2^22 from a float estimate, corrected by one either way.
+__device__ __forceinline__ int div_small(int n, int d, float inv_d) {
+  int q = (int)((float)n * inv_d);
+  q += (q + 1) * d <= n ? 1 : 0;
+  q -= q * d > n ? 1 : 0;
+  return q;
+}
+
+template <int G>
+__device__ __forceinline__ ConvBlock conv_block(int cb, const ConvGeom& g) {
+  ConvBlock k;
+  k.live = cb < g.nblk;
+  k.centre = cb < g.ncb;
+  const int cbo = k.centre ? 0 : cb - g.ncb;
+  const int o = div_small(cbo, g.bpo, g.inv_bpo);
+  const int oa = div_small(o, g.p + 1, g.inv_p1);
+  const int a = 1 + oa, b = o - oa * (g.p + 1);
+  k.ch0 = k.centre ? cb * 4 * G : (cbo - o * g.bpo) * G;
+  k.chstep = k.centre ? G : 0;
+  const int ta[4] = {a, -b, -a, b}, tb[4] = {b, a, -b, -a};  // R^m (a, b)
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    k.di[m] = k.centre ? 0 : ta[m];
+    k.dj[m] = k.centre ? 0 : tb[m];
+  }
+  return k;
+}
+
+// The four loads M[m] of a block -> the four pieces of its group channels:
+// orbit block, piece b value m = M[m] at rotation (m + b) mod 4 (per channel
+// of the piece); centre block, the loads themselves.
+template <typename E>
+__device__ __forceinline__ void conv_diag(const u32x4 (&M)[4], bool centre, u32x4 (&pc)[4]) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t d;
+      if constexpr (sizeof(E) == 4) {
+        d = M[k][(k + b) & 3];
+      } else {
+        const int e = k >> 1, m0 = 2 * (k & 1);
+        const int hl = 4 * e + ((m0 + b) & 3), hh = 4 * e + ((m0 + 1 + b) & 3);
+        const uint32_t lo = (M[m0][hl >> 1] >> (16 * (hl & 1))) & 0xffffu;
+        const uint32_t hi = (M[m0 + 1][hh >> 1] >> (16 * (hh & 1))) & 0xffffu;
+        d = lo | (hi << 16);
+      }
+      pc[b][k] = centre ? M[b][k] : d;
+    }
+  }
+}
+
 // One forward (or dX) tile: workgroup-level logical tile id `lid`.  NBUF = 2
 // double-buffers the LDS stages (one barrier per stage); NBUF = 1 halves the
 // LDS footprint (two barriers per stage) so that more workgroups fit a CU.
 // PF (1 or 2) is the number of stages whose global loads are in flight in
 // registers ahead of the stage being transformed into LDS.
-template <typename E, int G, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED>
+// CONV: the A rows are output pixels of a p4 group convolution whose
+// gathered rows (see ConvGeom) are read straight from the input map `in`.
+template <typename E, int G, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED, bool CONV = false>
 __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __restrict__ in,
                                          const E* __restrict__ wp, E* __restrict__ out, int64_t nrows, int kg,
-                                         int mg, int tiles_n, const E* __restrict__ bias, int act) {
+                                         int mg, int tiles_n, const E* __restrict__ bias, int act,
+                                         const ConvGeom& geo = ConvGeom{}) {
   constexpr int T = Grp<G>::kOrder;
   using U = Units<E, T>;
   constexpr int NT = 64 * WM * WN;
@@ -672,14 +758,48 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
 
   const uint32_t row_bytes = (uint32_t)kg * (uint32_t)(T * sizeof(E));
   const __amdgpu_buffer_rsrc_t a_src =
-      make_rsrc(in + row0 * T * (int64_t)kg, (uint64_t)(nrows - row0) * row_bytes);
+      CONV ? make_rsrc(in, geo.in_bytes) : make_rsrc(in + row0 * T * (int64_t)kg, (uint64_t)(nrows - row0) * row_bytes);
   const __amdgpu_buffer_rsrc_t b_src =
       make_rsrc(wp + (int64_t)col0 * ksteps * SG * T, (uint64_t)(mg - col0) * (uint64_t)ksteps * BLOCK);
 
   const int q = tid & 3, rl = tid >> 2;
   u32x4 ra[PF][PA][T], rb[PF][PB][T];   // register ring of PF stages of loads
+
+  // convolution: pixel of each A row this lane loads, and per ring slot
+  // whether its block is a centre block
+  int py[PA], px[PA];
+  uint32_t pbase[PA];
+  bool prow[PA], cen[PF];
+  if constexpr (CONV) {
+    static_assert(T == 4 && U::kPiecesPerUnit == 1, "p4 convolution");
+#pragma unroll
+    for (int ps = 0; ps < PA; ++ps) {
+      const int64_t n = row0 + ps * RPP + rl;
+      prow[ps] = n < nrows;
+      const int nn = prow[ps] ? (int)n : 0;
+      const int hw = geo.H * geo.W;
+      const int img = nn / hw, rem = nn - img * hw;
+      py[ps] = rem / geo.W;
+      px[ps] = rem - py[ps] * geo.W;
+      pbase[ps] = (uint32_t)nn * (uint32_t)(geo.cpix * T * sizeof(E));
+    }
+  }
   auto load = [&](int ks, auto slot_c) {
     constexpr int sl = decltype(slot_c)::value;
+    if constexpr (CONV) {
+      const ConvBlock k = conv_block<U::kGroupsPerUnit>(4 * ks + q, geo);
+      cen[sl] = k.centre;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int delta = ((k.di[i] * geo.W + k.dj[i]) * geo.cpix + k.ch0 + k.chstep * i) * (int)(T * sizeof(E));
+#pragma unroll
+        for (int ps = 0; ps < PA; ++ps) {
+          const bool ok = k.live && prow[ps] && (unsigned)(py[ps] + k.di[i]) < (unsigned)geo.H &&
+                          (unsigned)(px[ps] + k.dj[i]) < (unsigned)geo.W;
+          ra[sl][ps][i] = bload16(a_src, ok ? pbase[ps] + (uint32_t)delta : kOob);
+        }
+      }
+    } else {
 #pragma unroll
     for (int ps = 0; ps < PA; ++ps) {
       const uint32_t r = (uint32_t)(ps * RPP + rl);
@@ -692,6 +812,7 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
           ra[sl][ps][i * U::kPiecesPerUnit + h] = bload16(a_src, off);
         }
       }
+    }
     }
 #pragma unroll
     for (int ps = 0; ps < PB; ++ps) {
@@ -709,7 +830,13 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
       const int r = ps * RPP + rl;
       if (BM % RPP == 0 || r < BM) {
         u32x4 pl[T];
-        pieces_to_planes<E, G, false>(ra[sl][ps], pl);
+        if constexpr (CONV) {
+          u32x4 pcs[T];
+          conv_diag<E>(ra[sl][ps], cen[sl], pcs);
+          pieces_to_planes<E, G, false>(pcs, pl);
+        } else {
+          pieces_to_planes<E, G, false>(ra[sl][ps], pl);
+        }
 #pragma unroll
         for (int p = 0; p < T; ++p) st16(buf + p * A_PLANE + r * STRIDE + swz_slot(r, q) * 16, pl[p]);
       }

@@ -58,4 +58,24 @@ EQLIN_DECLARE_LAUNCH(kP4M)
 inline int stage_groups(int dtype) { return dtype == 0 ? 16 : 32; }       // group channels per pipeline stage
 inline int dw_rows_per_stage(int dtype) { return dtype == 0 ? 16 : 32; }  // rows per dw pipeline stage
 
+// p4 group convolution (eqconv_kernels.hip): group channels of one gathered
+// row (cpix K^2), padded to whole pipeline stages.
+inline int conv_gathered_groups(int cpix, int K, int dtype) {
+  const int sg = stage_groups(dtype);
+  return (cpix * K * K + sg - 1) / sg * sg;
+}
+
+// Launchers of the p4 group convolution (T = 4).  cpix: group channels of the
+// input map; mg: output group channels; K: odd filter width.
+struct ConvLaunch {
+  static bool tile_known(int tile);
+  static hipError_t forward(int dtype, int tile, const void* in, const void* wp, void* out, int64_t npix, int H,
+                            int W, int cpix, int K, int mg, const void* bias, int act, hipStream_t s);
+  // forward set (rows D', gathered over C') into wf, adjoint set (rows C', gathered over D') into wb
+  static hipError_t prepare(int dtype, const void* psi, void* wf, void* wb, int Dp, int Cp, int K, hipStream_t s);
+  static hipError_t gather(int dtype, const void* in, void* xlin, int64_t npix, int H, int W, int cpix, int K,
+                           hipStream_t s);
+  static hipError_t dw_scatter(int dtype, const float* dwlin, float* dpsi, int Dp, int Cp, int K, hipStream_t s);
+};
+
 }  // namespace eqlin

@@ -3,7 +3,7 @@
 Every step of the layer runs in the HIP library; this module checks tensor
 shapes, dtypes, devices and contiguity, allocates outputs with PyTorch (device
 memory plumbing) and passes raw pointers plus torch's current HIP stream to the
-C ABI declared in include/eqlin.h.  There is no fallback: if the library is not
+C ABI declared in include/eqlin.h and include/eqconv.h.  There is no fallback: if the library is not
 built, every call raises.
 """
 from __future__ import annotations
@@ -47,11 +47,15 @@ class EqlinError(RuntimeError):
 
 
 def header_symbols() -> list:
-    """Names of every function include/eqlin.h declares."""
-    with open(os.path.join(INCLUDE, "eqlin.h")) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(eqlin_\w+)\s*\(", text)))
+    """Names of every function the headers under include/ declare."""
+    names = set()
+    for name in sorted(os.listdir(INCLUDE)):
+        if not name.endswith(".h"):
+            continue
+        with open(os.path.join(INCLUDE, name)) as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        names.update(re.findall(r"\b((?:eqlin|eqconv)_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def load_library(path: str = LIB) -> ctypes.CDLL:
@@ -78,6 +82,14 @@ def load_library(path: str = LIB) -> ctypes.CDLL:
                                    c_int, c_vp]),
         "eqlin_backward_dx": (c_int, [c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_int, c_vp]),
         "eqlin_backward_dw": (c_int, [c_vp, c_vp, c_i64, c_int, c_int, c_int, c_fp, c_vp, c_sz, c_int, c_vp]),
+        "eqconv_prepared_weight_bytes": (c_sz, [c_int, c_int, c_int, c_int]),
+        "eqconv_prepared_adjoint_offset": (c_sz, [c_int, c_int, c_int, c_int]),
+        "eqconv_prepare_weights": (c_int, [c_vp, c_int, c_int, c_int, c_int, c_vp, c_sz, c_vp]),
+        "eqconv_forward": (c_int, [c_vp, c_i64, c_int, c_int, c_int, c_int, c_int, c_vp, c_vp, c_int, c_vp,
+                                   c_int, c_vp]),
+        "eqconv_backward_workspace_bytes": (c_sz, [c_i64, c_int, c_int, c_int, c_int, c_int, c_int]),
+        "eqconv_backward": (c_int, [c_vp, c_vp, c_i64, c_int, c_int, c_int, c_int, c_int, c_vp, c_vp, c_fp,
+                                    c_vp, c_sz, c_int, c_vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -297,3 +309,103 @@ def eqlin_backward_dw(dY: torch.Tensor, X: torch.Tensor, workspace: Optional[tor
            lib.eqlin_backward_dw(_ptr(dY), _ptr(X), N, C, D, T, _ptr(out), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), dt, _stream(dY)))
     return out
+
+
+# ------------------------------------------------------------ p4 group convolution
+
+class ConvPrepared(NamedTuple):
+    """Prepared filter spectra of a p4 group convolution (opaque byte buffer)."""
+    buf: torch.Tensor
+    C: int
+    D: int
+    K: int
+    dtype: torch.dtype
+
+
+def eqconv_prepared_weight_bytes(C: int, D: int, K: int, dtype: torch.dtype) -> int:
+    return int(load_library().eqconv_prepared_weight_bytes(C, D, K, _DTYPES[dtype]))
+
+
+def eqconv_prepare_weights(psi: torch.Tensor, out: Optional[torch.Tensor] = None) -> ConvPrepared:
+    """psi [D/4][C/4][K][K][4] -> prepared spectra for eqconv_forward / eqconv_backward."""
+    lib = load_library()
+    _need_cuda(psi, "psi")
+    dt = _dtype_code(psi)
+    if psi.dim() != 5 or psi.shape[2] != psi.shape[3] or psi.shape[4] != 4:
+        raise ValueError(f"psi must have shape [D/4, C/4, K, K, 4], got {tuple(psi.shape)}")
+    D, C, K = 4 * psi.shape[0], 4 * psi.shape[1], int(psi.shape[2])
+    nbytes = int(lib.eqconv_prepared_weight_bytes(C, D, K, dt))
+    if out is None:
+        out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=psi.device)
+    _need_cuda(out, "out")
+    _check("eqconv_prepare_weights",
+           lib.eqconv_prepare_weights(_ptr(psi), C, D, K, dt, _ptr(out), out.numel() * out.element_size(),
+                                      _stream(psi)))
+    return ConvPrepared(out, C, D, K, psi.dtype)
+
+
+def eqconv_forward(X: torch.Tensor, P: ConvPrepared, bias: Optional[torch.Tensor] = None, act: str = "none",
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = act(conv(X, psi) + b), X [N][H][W][C] -> Y [N][H][W][D] (channels last, rotation fastest)."""
+    lib = load_library()
+    _need_cuda(X, "X")
+    dt = _dtype_code(X)
+    if X.dtype != P.dtype:
+        raise TypeError("X and the prepared filter differ in dtype")
+    if X.dim() != 4 or X.shape[3] != P.C:
+        raise ValueError(f"X must have shape [N, H, W, {P.C}], got {tuple(X.shape)}")
+    if act not in ACT:
+        raise ValueError(f"act must be one of {sorted(ACT)}")
+    if bias is not None:
+        _need_cuda(bias, "bias")
+        if bias.dtype != X.dtype or tuple(bias.shape) != (P.D // 4,):
+            raise ValueError(f"bias must be [{P.D // 4}] of dtype {X.dtype}")
+    N, H, W = X.shape[:3]
+    if out is None:
+        out = torch.empty((N, H, W, P.D), dtype=X.dtype, device=X.device)
+    _need_cuda(out, "out")
+    if tuple(out.shape) != (N, H, W, P.D) or out.dtype != X.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    _check("eqconv_forward", lib.eqconv_forward(_ptr(X), N, H, W, P.C, P.D, P.K, _ptr(P.buf), _ptr(bias), ACT[act],
+                                                _ptr(out), dt, _stream(X)))
+    return out
+
+
+def eqconv_backward_workspace_bytes(N: int, H: int, W: int, C: int, D: int, K: int, dtype: torch.dtype) -> int:
+    return int(load_library().eqconv_backward_workspace_bytes(N, H, W, C, D, K, _DTYPES[dtype]))
+
+
+def eqconv_backward(dY: torch.Tensor, X: Optional[torch.Tensor], P: ConvPrepared, need_dx: bool = True,
+                    need_dpsi: bool = True, workspace: Optional[torch.Tensor] = None):
+    """(dX [N][H][W][C] or None, dpsi [D/4][C/4][K][K][4] float32 or None) for dY [N][H][W][D]."""
+    lib = load_library()
+    _need_cuda(dY, "dY")
+    dt = _dtype_code(dY)
+    if dY.dtype != P.dtype:
+        raise TypeError("dY and the prepared filter differ in dtype")
+    if dY.dim() != 4 or dY.shape[3] != P.D:
+        raise ValueError(f"dY must have shape [N, H, W, {P.D}], got {tuple(dY.shape)}")
+    if not (need_dx or need_dpsi):
+        raise ValueError("nothing to compute")
+    N, H, W = dY.shape[:3]
+    dX = dpsi = None
+    ws_bytes = 0
+    if need_dx:
+        dX = torch.empty((N, H, W, P.C), dtype=dY.dtype, device=dY.device)
+    if need_dpsi:
+        if X is None:
+            raise ValueError("dpsi needs X")
+        _need_cuda(X, "X")
+        if X.dtype != dY.dtype or tuple(X.shape) != (N, H, W, P.C):
+            raise ValueError(f"X must be [N, H, W, {P.C}] of dtype {dY.dtype}")
+        dpsi = torch.empty((P.D // 4, P.C // 4, P.K, P.K, 4), dtype=torch.float32, device=dY.device)
+        ws_bytes = int(lib.eqconv_backward_workspace_bytes(N, H, W, P.C, P.D, P.K, dt))
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dY.device)
+        _need_cuda(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check("eqconv_backward",
+           lib.eqconv_backward(_ptr(dY), _ptr(X) if need_dpsi else None, N, H, W, P.C, P.D, P.K, _ptr(P.buf),
+                               _ptr(dX), _ptr(dpsi), _ptr(workspace) if need_dpsi else None, ws_bytes, dt,
+                               _stream(dY)))
+    return dX, dpsi

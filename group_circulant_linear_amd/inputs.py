@@ -83,3 +83,47 @@ def workload_inputs(name: str, dtype: str | None = None, seed: int = 0, with_dy:
         X, w, dY = make_layer_inputs(L.N, L.C, L.D, dt, seed=seed, layer=i, with_dy=with_dy)
         out.append((L, X, w, dY))
     return out
+
+
+# ------------------------------------------------------------ p4 group convolution
+#
+# The summary names equivariant convolution as future work ("Limitations and
+# future work") and measures none, so its workload is a stand-in: one 3 x 3
+# p4 group convolution of a ResNet-stage shape, 32 images of 56 x 56 pixels,
+# C = D = 256 channels (64 group channels x 4 rotations).
+# Recipe: default_rng([seed, layer]), draws in the order X, psi, dY as float64
+# standard normals, psi scaled by 1/sqrt(C K^2) (a dense conv's fan-in), cast
+# round-to-nearest-even to the storage dtype.
+
+@dataclass(frozen=True)
+class ConvLayer:
+    name: str
+    N: int
+    H: int
+    W: int
+    C: int
+    D: int
+    K: int
+
+
+CONV_WORKLOADS = {
+    "p4conv": Workload(
+        "p4conv", "p4 group convolution 3x3, 32 images of 56x56, C=D=256 (64 group channels in and out)",
+        ("f32", "f16"), (ConvLayer("conv3x3", 32, 56, 56, 256, 256, 3),)),
+    "p4conv_tiny": Workload(
+        "p4conv_tiny", "tiny p4 group convolution 3x3, 2 images of 8x8, C=D=16",
+        ("f32",), (ConvLayer("tiny", 2, 8, 8, 16, 16, 3),)),
+}
+
+
+def make_conv_inputs(N: int, H: int, W: int, C: int, D: int, K: int, dtype: str = "f32", seed: int = 0,
+                     layer: int = 0, with_dy: bool = True):
+    """Return (X [N][H][W][C], psi [D/4][C/4][K][K][4], dY [N][H][W][D] or None) in the storage dtype."""
+    if C % 4 or D % 4:
+        raise ValueError("C and D must be multiples of 4")
+    rng = np.random.default_rng([seed, layer])
+    npdt = NP_DTYPE[dtype]
+    X = rng.standard_normal((N, H, W, C)).astype(npdt)
+    psi = (rng.standard_normal((D // 4, C // 4, K, K, 4)) / np.sqrt(C * K * K)).astype(npdt)
+    dY = rng.standard_normal((N, H, W, D)).astype(npdt) if with_dy else None
+    return X, psi, dY

@@ -160,3 +160,96 @@ def convert_state_dict(naive_state: dict, key_map: Optional[dict] = None) -> dic
         new = key_map.get(name, name)
         out[f"{prefix}.{new}" if prefix else new] = v
     return out
+
+
+# ------------------------------------------------------------ p4 group convolution
+
+def conv_dense_filter(psi: torch.Tensor) -> torch.Tensor:
+    """The ordinary K x K filter bank [D][C][K][K] of the p4 group convolution
+    with filter psi [D/4][C/4][K][K][4]: output channel d'*4 + r, input channel
+    c'*4 + s holds psi[d', c', R^-r delta, (r - s) mod 4] at tap delta, i.e.
+    the filter turned r times (torch.rot90 on the tap axes).  For inspection
+    and dense comparisons only; the convolution never builds it."""
+    Dp, Cp, K = psi.shape[0], psi.shape[1], psi.shape[2]
+    flat = torch.arange(psi.numel()).reshape(psi.shape)
+    idx = torch.empty((4 * Dp, 4 * Cp, K, K), dtype=torch.long)
+    for r in range(4):
+        turned = torch.rot90(flat, r, dims=(2, 3))
+        for s in range(4):
+            idx[r::4, s::4] = turned[..., (r - s) % 4]
+    return psi.reshape(-1)[idx.to(psi.device)]
+
+
+class _ConvSpectraCache:
+    """Prepared filter spectra of one filter tensor, keyed on its storage and version."""
+
+    def __init__(self):
+        self.key = None
+        self.prepared: Optional[eqlin.ConvPrepared] = None
+
+    def get(self, psi: torch.Tensor) -> eqlin.ConvPrepared:
+        key = (psi.data_ptr(), psi._version, tuple(psi.shape), psi.dtype, psi.device)
+        if self.key != key or self.prepared is None:
+            self.prepared = eqlin.eqconv_prepare_weights(psi.detach().contiguous())
+            self.key = key
+        return self.prepared
+
+
+class EQConvFunction(torch.autograd.Function):
+    """p4 group convolution, X [N][H][W][C] -> Y [N][H][W][D] (channels last,
+    rotation fastest), optional group-invariant bias and GELU (forward only)."""
+
+    @staticmethod
+    def forward(ctx, X: torch.Tensor, psi: torch.Tensor, cache: Optional[_ConvSpectraCache] = None):
+        if X.dtype != psi.dtype:
+            raise TypeError(f"X ({X.dtype}) and psi ({psi.dtype}) must share a dtype")
+        prepared = cache.get(psi) if cache is not None else eqlin.eqconv_prepare_weights(psi.detach().contiguous())
+        Xc = X.contiguous()
+        Y = eqlin.eqconv_forward(Xc, prepared)
+        ctx.save_for_backward(Xc, psi)
+        ctx.prepared = prepared
+        return Y
+
+    @staticmethod
+    def backward(ctx, dY: torch.Tensor):
+        X, psi = ctx.saved_tensors
+        need_dx, need_dpsi = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        if not (need_dx or need_dpsi):
+            return None, None, None
+        dX, dpsi = eqlin.eqconv_backward(dY.contiguous().to(X.dtype), X if need_dpsi else None, ctx.prepared,
+                                         need_dx=need_dx, need_dpsi=need_dpsi)
+        return dX, (dpsi.to(psi.dtype) if dpsi is not None else None), None
+
+
+class FlashEQConv2d(torch.nn.Module):
+    """p4 group convolution of regular feature maps (the 1 x 1 case is FlashEQLinear).
+
+    Input and output are channels-last maps [N][H][W][C] with channel
+    c'*4 + s (rotation s fastest); ``kernel_size`` K is odd and the padding
+    keeps the image size.  Parameter ``psi`` [out/4][in/4][K][K][4]:
+    Y[x, d'*4 + r] = sum X[x + delta, c'*4 + s] psi[d', c', R^-r delta, (r - s) mod 4]
+    with R the quarter turn of the pixel grid.
+    """
+
+    def __init__(self, in_channels: int, out_channels: int, kernel_size: int = 3, device=None, dtype=None):
+        super().__init__()
+        if in_channels % 4 or out_channels % 4:
+            raise ValueError("in_channels and out_channels must be multiples of 4")
+        if kernel_size % 2 != 1:
+            raise ValueError("kernel_size must be odd")
+        self.in_channels = in_channels
+        self.out_channels = out_channels
+        self.kernel_size = kernel_size
+        self.psi = torch.nn.Parameter(torch.empty(out_channels // 4, in_channels // 4, kernel_size, kernel_size, 4,
+                                                  device=device, dtype=dtype))
+        self._cache = _ConvSpectraCache()
+        self.reset_parameters()
+
+    def reset_parameters(self) -> None:
+        torch.nn.init.normal_(self.psi, 0.0, 1.0 / math.sqrt(self.in_channels * self.kernel_size ** 2))
+
+    def forward(self, X: torch.Tensor) -> torch.Tensor:
+        return EQConvFunction.apply(X, self.psi, self._cache)
+
+    def extra_repr(self) -> str:
+        return f"in_channels={self.in_channels}, out_channels={self.out_channels}, kernel_size={self.kernel_size}, group=p4"

@@ -49,6 +49,8 @@ __all__ = [
     "conv_dw",
     "conv_dense_filter",
     "conv_forward_pixels",
+    "conv_dx_pixels",
+    "conv_dw_entries",
 ]
 
 T4 = 4
@@ -185,3 +187,47 @@ def conv_dense_filter(psi) -> np.ndarray:
             for s in range(T4):
                 Wd[r::T4, s::T4, di + p, dj + p] = kr[:, :, s]
     return Wd
+
+
+def conv_dx_pixels(dy, psi, H: int, W: int, pix) -> np.ndarray:
+    """Rows of conv_dx at the flat pixel indices pix, one by one from the
+    adjoint's definition: dX[y, c'*4 + s] = sum_{r, delta} dY[y - delta, d'*4 + r]
+    psi[d', c', R^-r delta, (r - s) mod 4]."""
+    dy, psi = _f64(dy), _f64(psi)
+    Dp, Cp, K = psi.shape[0], psi.shape[1], psi.shape[2]
+    N = dy.shape[0]
+    dY = dy.reshape(N, H, W, Dp, T4)
+    out = np.zeros((len(pix), Cp * T4))
+    for row, q in enumerate(pix):
+        n, rem = divmod(int(q), H * W)
+        i, j = divmod(rem, W)
+        for r in range(T4):
+            for di, dj in _taps(K):
+                if 0 <= i - di < H and 0 <= j - dj < W:
+                    kr = _kernel_for(psi, r, di, dj).reshape(Dp, Cp * T4)
+                    out[row] += dY[n, i - di, j - dj, :, r] @ kr
+    return out
+
+
+def conv_dw_entries(dy, f, K: int, idx) -> np.ndarray:
+    """Entries dpsi[d', c', a, b, v] for idx rows (d', c', a, b, v), one by one:
+    sum_{x, r} dY[x, d'*4 + r] f[x + R^r (a - p, b - p), c'*4 + (r - v) mod 4]."""
+    dy, f = _f64(dy), _f64(f)
+    N, H, W, C = f.shape
+    Cp, p = C // T4, K // 2
+    Dp = dy.shape[3] // T4
+    dY = dy.reshape(N, H, W, Dp, T4)
+    f5 = f.reshape(N, H, W, Cp, T4)
+    out = np.zeros(len(idx))
+    for e, (d, c, a, b, v) in enumerate(idx):
+        acc = 0.0
+        for r in range(T4):
+            di, dj = rot_offset(r, a - p, b - p)
+            i0, i1 = max(0, -di), min(H, H - di)
+            j0, j1 = max(0, -dj), min(W, W - dj)
+            if i0 >= i1 or j0 >= j1:
+                continue
+            acc += float(np.sum(dY[:, i0:i1, j0:j1, d, r] *
+                                f5[:, i0 + di:i1 + di, j0 + dj:j1 + dj, c, (r - v) % T4]))
+        out[e] = acc
+    return out

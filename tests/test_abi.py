@@ -139,3 +139,72 @@ def test_forward_ex_validation(lib):
     assert f(FAKE, 8, 32, 32, 4, FAKE, ctypes.c_void_p(0x1001), 1, FAKE, 0, None) == EALIGN  # misaligned fp32 bias
     assert f(FAKE, 8, 32, 32, 3, FAKE, None, 1, FAKE, 0, None) == ENOTSUP
     assert f(None, 0, 32, 32, 4, None, None, 1, None, 0, None) == OK            # empty batch
+
+
+# ------------------------------------------------------------ p4 group convolution
+
+def test_conv_size_queries(lib):
+    # gathered groups C'K^2 padded to whole 16 (fp32) / 32 (f16) group blocks of 256 bytes
+    # C = D = 256, K = 3, fp32: 64 * 9 = 576 groups = 36 blocks per row, 64 rows per set
+    assert lib.eqconv_prepared_adjoint_offset(256, 256, 3, 0) == 64 * 36 * 256
+    assert lib.eqconv_prepared_weight_bytes(256, 256, 3, 0) == 2 * 64 * 36 * 256
+    # C' = 4, K = 3: 36 groups -> 3 fp32 blocks; D' = 8: 72 groups -> 5 blocks
+    assert lib.eqconv_prepared_adjoint_offset(16, 32, 3, 0) == 8 * 3 * 256
+    assert lib.eqconv_prepared_weight_bytes(16, 32, 3, 0) == 8 * 3 * 256 + 4 * 5 * 256
+    # K = 1 is the linear layer's layout
+    assert lib.eqconv_prepared_weight_bytes(768, 768, 1, 0) == lib.eqlin_prepared_weight_bytes(768, 768, 4, 0)
+    # f16 needs C', D' multiples of 8; fp32 multiples of 4
+    assert lib.eqconv_prepared_weight_bytes(16, 32, 3, 1) == 0
+    assert lib.eqconv_prepared_weight_bytes(32, 32, 3, 1) > 0
+    assert lib.eqconv_prepared_weight_bytes(24, 32, 3, 0) == 0
+    for K in (0, 2, -1, 17):
+        assert lib.eqconv_prepared_weight_bytes(16, 16, K, 0) == 0
+    assert lib.eqconv_backward_workspace_bytes(-1, 8, 8, 16, 16, 3, 0) == 0
+    ws0 = lib.eqconv_backward_workspace_bytes(0, 8, 8, 16, 16, 3, 0)
+    assert ws0 == (4 * 48 * 4 * 4 + 255) // 256 * 256        # the gathered layer's dw only
+    ws = lib.eqconv_backward_workspace_bytes(2, 8, 8, 16, 16, 3, 0)
+    assert ws >= ws0 + 128 * 48 * 4 * 4
+
+
+def test_conv_validation(lib):
+    st = lib.eqconv_forward
+    # bad dtype, sizes, K, act
+    assert st(FAKE, 1, 4, 4, 16, 16, 3, FAKE, None, 0, FAKE, 2, None) == EINVAL
+    assert st(FAKE, -1, 4, 4, 16, 16, 3, FAKE, None, 0, FAKE, 0, None) == EINVAL
+    assert st(FAKE, 1, -4, 4, 16, 16, 3, FAKE, None, 0, FAKE, 0, None) == EINVAL
+    assert st(FAKE, 1, 4, 4, 18, 16, 3, FAKE, None, 0, FAKE, 0, None) == EINVAL
+    assert st(FAKE, 1, 4, 4, 16, 16, 2, FAKE, None, 0, FAKE, 0, None) == EINVAL
+    assert st(FAKE, 1, 4, 4, 16, 16, 17, FAKE, None, 0, FAKE, 0, None) == ENOTSUP
+    assert st(FAKE, 1, 4, 4, 24, 16, 3, FAKE, None, 0, FAKE, 0, None) == ENOTSUP   # C' = 6
+    assert st(FAKE, 1, 4, 4, 16, 16, 3, FAKE, None, 0, FAKE, 1, None) == ENOTSUP   # f16 needs C' % 8
+    assert st(FAKE, 1, 4, 4, 16, 16, 3, FAKE, None, 7, FAKE, 0, None) == EINVAL
+    # null and misaligned pointers
+    assert st(None, 1, 4, 4, 16, 16, 3, FAKE, None, 0, FAKE, 0, None) == EINVAL
+    assert st(FAKE, 1, 4, 4, 16, 16, 3, None, None, 0, FAKE, 0, None) == EINVAL
+    assert st(MISALIGNED, 1, 4, 4, 16, 16, 3, FAKE, None, 0, FAKE, 0, None) == EALIGN
+    assert st(FAKE, 1, 4, 4, 16, 16, 3, FAKE, ctypes.c_void_p(0x1001), 0, FAKE, 0, None) == EALIGN
+    # an input map of 2^31 bytes or more
+    assert st(FAKE, 1 << 12, 128, 128, 32, 16, 3, FAKE, None, 0, FAKE, 0, None) == ENOTSUP
+    # empty batches are no-ops (nothing launched)
+    assert st(None, 0, 4, 4, 16, 16, 3, None, None, 0, None, 0, None) == OK
+    assert st(None, 3, 0, 4, 16, 16, 3, None, None, 0, None, 0, None) == OK
+    # prepare
+    pw = lib.eqconv_prepare_weights
+    need = lib.eqconv_prepared_weight_bytes(16, 16, 3, 0)
+    assert pw(FAKE, 16, 16, 3, 0, FAKE, need - 1, None) == EWORKSPACE
+    assert pw(None, 16, 16, 3, 0, FAKE, need, None) == EINVAL
+    assert pw(FAKE, 16, 16, 3, 0, MISALIGNED, need, None) == EALIGN
+    assert pw(FAKE, 16, 16, 4, 0, FAKE, need, None) == EINVAL
+    # backward
+    bw = lib.eqconv_backward
+    ws = lib.eqconv_backward_workspace_bytes(1, 4, 4, 16, 16, 3, 0)
+    assert bw(FAKE, FAKE, 1, 4, 4, 16, 16, 3, FAKE, None, None, FAKE, ws, 0, None) == EINVAL   # nothing asked
+    assert bw(FAKE, FAKE, 1, 4, 4, 16, 16, 3, FAKE, None, FAKE, FAKE, ws - 1, 0, None) == EWORKSPACE
+    assert bw(FAKE, FAKE, 1, 4, 4, 16, 16, 3, FAKE, None, FAKE, None, ws, 0, None) == EINVAL
+    assert bw(FAKE, None, 1, 4, 4, 16, 16, 3, FAKE, None, FAKE, FAKE, ws, 0, None) == EINVAL
+    assert bw(FAKE, FAKE, 1, 4, 4, 16, 16, 3, FAKE, MISALIGNED, FAKE, FAKE, ws, 0, None) == EALIGN
+    assert bw(None, FAKE, 1, 4, 4, 16, 16, 3, FAKE, FAKE, None, None, 0, 0, None) == EINVAL
+    # validation of the dpsi half runs before the dX launch
+    assert bw(FAKE, FAKE, 1, 4, 4, 16, 16, 3, FAKE, FAKE, FAKE, FAKE, ws - 1, 0, None) == EWORKSPACE
+    # empty batch with dX only: no-op
+    assert bw(None, None, 0, 4, 4, 16, 16, 3, None, FAKE, None, None, 0, 0, None) == OK

@@ -111,3 +111,15 @@ def test_sgd_step_through_module():
         opt.step()
         losses.append(loss.item())
     assert losses[-1] < losses[0]
+
+
+def test_conv_dense_filter_matches_the_oracle_cpu():
+    # the dense filter bank of the p4 convolution (used by the benchmark's
+    # dense comparator) is the oracle's, entry for entry
+    import numpy as np
+    import oracle
+    torch = pytest.importorskip("torch")
+    from group_circulant_linear_amd.module import conv_dense_filter
+    psi = np.random.default_rng(0).standard_normal((3, 2, 5, 5, 4))
+    got = conv_dense_filter(torch.from_numpy(psi)).numpy()
+    assert np.array_equal(got, oracle.conv_dense_filter(psi))

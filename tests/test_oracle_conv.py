@@ -241,3 +241,16 @@ def test_input_gradient_is_a_convolution_of_dy():
                 ti, tj = oracle.rot_offset(u, a - p, b - p)
                 psi_t[:, :, a, b, u] = psi[:, :, -ti + p, -tj + p, (-u) % 4].T
     assert _rel(oracle.conv_forward(dy, psi_t), oracle.conv_dx(dy, psi, H, W)) < 1e-13
+
+
+def test_per_pixel_and_per_entry_routines_match_the_whole_tensor_ones():
+    N, H, W, Cp, Dp, K = 2, 5, 4, 2, 3, 3
+    f = _rand((N, H, W, 4 * Cp), 26)
+    psi = _rand((Dp, Cp, K, K, 4), 27)
+    dy = _rand((N, H, W, 4 * Dp), 28)
+    pix = [0, 3, 7, 19, 39]
+    dx = oracle.conv_dx(dy, psi, H, W).reshape(-1, 4 * Cp)
+    assert _rel(oracle.conv_dx_pixels(dy, psi, H, W, pix), dx[pix]) < 1e-14
+    dw = oracle.conv_dw(dy, f, K)
+    idx = [(0, 0, 0, 0, 0), (2, 1, 1, 2, 3), (1, 0, 2, 1, 1), (2, 1, 1, 1, 2)]
+    assert _rel(oracle.conv_dw_entries(dy, f, K, idx), np.array([dw[i] for i in idx])) < 1e-13
