@@ -5,8 +5,9 @@
 //     done by its A-side loads (no gathered copy in global memory);
 //   - filter preparation: the group DFT of the gathered layer's weight, read
 //     from the filter through the block decode (forward and adjoint sets);
-//   - filter gradient: the gathered rows written out once, the linear layer's
-//     dw reduction over them, and a scatter of that gradient onto the filter.
+//   - filter gradient: the linear layer's dw reduction (split partials, ordered
+//     finalize) with the gather done by its loads, and a scatter of that
+//     gradient onto the filter.
 #include <stdlib.h>
 
 #include "eqlin_device.h"
@@ -33,6 +34,15 @@ ConvGeom make_geom(int H, int W, int cpix, int K, int64_t npix) {
   g.inv_bpo = 1.0f / (float)g.bpo;
   g.inv_p1 = 1.0f / (float)(g.p + 1);
   g.in_bytes = (uint32_t)(npix * (int64_t)cpix * 4 * (int64_t)sizeof(E));
+  // floor(n / d) = (n mul) >> shift for n < 2^31: shift = 31 + ceil(log2 d), mul = ceil(2^shift / d) < 2^32
+  auto magic = [](int64_t d, uint32_t& mul, int& shift) {
+    int l = 0;
+    while ((int64_t(1) << l) < d) ++l;
+    shift = 31 + l;
+    mul = (uint32_t)(((uint64_t(1) << shift) + (uint64_t)d - 1) / (uint64_t)d);
+  };
+  magic(W > 0 ? W : 1, g.w_mul, g.w_shift);
+  magic(H > 0 && W > 0 ? (int64_t)H * W : 1, g.hw_mul, g.hw_shift);
   return g;
 }
 
@@ -127,38 +137,14 @@ conv_prepare_kernel(const E* __restrict__ psi, E* __restrict__ dst, int rows, in
   for (int q = 0; q < T; ++q) o[q * SG] = (E)f[q];
 }
 
-// Whole gathered rows xlin [npix][kg][4] for the filter gradient (padding of
-// a partial last stage written as zeros).  One thread per (pixel, block).
+// Split partials of the gathered layer's dw, the gather done by the loads.
 template <typename E>
-__global__ void __launch_bounds__(kThreads)
-conv_gather_kernel(const E* __restrict__ in, E* __restrict__ xlin, int64_t npix, int kg, ConvGeom geo) {
-  constexpr int T = 4, G = Units<E, T>::kGroupsPerUnit, SG = 16 * G;
-  const int bpr = kg / (4 * G);  // blocks per padded row
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= npix * bpr) return;
-  const int64_t n = idx / bpr;
-  const int cb = (int)(idx - n * bpr);
-  const ConvBlock k = conv_block<G>(cb, geo);
-  const int hw = geo.H * geo.W;
-  const int img = (int)(n / hw), rem = (int)(n - (int64_t)img * hw);
-  const int y = rem / geo.W, x = rem - y * geo.W;
-  const char* base = reinterpret_cast<const char*>(in) + n * (int64_t)geo.cpix * T * (int64_t)sizeof(E);
-  u32x4 M[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bool ok = k.live && (unsigned)(y + k.di[i]) < (unsigned)geo.H && (unsigned)(x + k.dj[i]) < (unsigned)geo.W;
-    const int64_t delta =
-        ((int64_t)(k.di[i] * geo.W + k.dj[i]) * geo.cpix + k.ch0 + k.chstep * i) * T * (int64_t)sizeof(E);
-    M[i] = ok ? *reinterpret_cast<const u32x4*>(base + delta) : u32x4{0u, 0u, 0u, 0u};
-  }
-  u32x4 pc[4];
-  conv_diag<E>(M, k.centre, pc);
-  char* orow = reinterpret_cast<char*>(xlin) + n * (int64_t)kg * T * (int64_t)sizeof(E);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int j = (cb / 4) * SG + G * ((cb & 3) + 4 * i);
-    *reinterpret_cast<u32x4*>(orow + (int64_t)j * T * sizeof(E)) = pc[i];
-  }
+__global__ void __launch_bounds__(kThreads, bwd_waves_per_simd<4>())
+conv_dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __restrict__ ws, int64_t npix,
+                       int mg, int kg, int64_t rows_per_split, int tiles_m, int tiles_n, ConvGeom geo) {
+  __shared__ __attribute__((aligned(16))) char lds[dw_lds_bytes<4, kDwBufs>()];
+  dw_tile<E, 4, kDwBufs, true>(lds, xcd_logical_id(blockIdx.x, gridDim.x), dy, x, ws, npix, mg, kg, rows_per_split,
+                               tiles_m, tiles_n, geo);
 }
 
 // Filter gradient from the gathered layer's dw: dpsi[d'][c][tap][v] =
@@ -211,14 +197,21 @@ hipError_t launch_conv_prepare(const void* psi, void* wf, void* wb, int Dp, int 
 }
 
 template <typename E>
-hipError_t launch_conv_gather(const void* in, void* xlin, int64_t npix, int H, int W, int cpix, int K,
-                              hipStream_t s) {
-  const int kg = conv_gathered_groups(cpix, K, sizeof(E) == 4 ? 0 : 1);
-  const int64_t n = npix * (kg / (4 * Units<E, 4>::kGroupsPerUnit));
-  if (n <= 0) return hipSuccess;
-  if (cdiv(n, kThreads) > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((conv_gather_kernel<E>), dim3((unsigned)cdiv(n, kThreads)), dim3(kThreads), 0, s,
-                     static_cast<const E*>(in), static_cast<E*>(xlin), npix, kg, make_geom<E>(H, W, cpix, K, npix));
+hipError_t launch_conv_dw(const void* dy, const void* x, float* ws, float* dwlin, int64_t npix, int H, int W, int Dp,
+                          int Cp, int K, int64_t rows_per_split, int nsplit, hipStream_t s) {
+  const int kg = conv_gathered_groups(Cp, K, sizeof(E) == 4 ? 0 : 1);
+  const int tiles_m = (int)cdiv(Dp, 64), tiles_n = (int)cdiv(kg, 64);
+  if (nsplit > 0) {
+    const int64_t grid = (int64_t)tiles_m * tiles_n * nsplit;
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((conv_dw_partial_kernel<E>), dim3((unsigned)grid), dim3(kThreads), 0, s,
+                       static_cast<const E*>(dy), static_cast<const E*>(x), ws, npix, Dp, kg, rows_per_split, tiles_m,
+                       tiles_n, make_geom<E>(H, W, Cp, K, npix));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t fgrid = cdiv((int64_t)Dp * kg, kThreads / 4);
+  hipLaunchKernelGGL((dw_finalize_kernel<4>), dim3((unsigned)fgrid), dim3(kThreads), 0, s, ws, dwlin, Dp, kg, nsplit);
   return hipGetLastError();
 }
 
@@ -264,10 +257,10 @@ hipError_t ConvLaunch::prepare(int dtype, const void* psi, void* wf, void* wb, i
                     : launch_conv_prepare<_Float16>(psi, wf, wb, Dp, Cp, K, s);
 }
 
-hipError_t ConvLaunch::gather(int dtype, const void* in, void* xlin, int64_t npix, int H, int W, int cpix, int K,
-                              hipStream_t s) {
-  return dtype == 0 ? launch_conv_gather<float>(in, xlin, npix, H, W, cpix, K, s)
-                    : launch_conv_gather<_Float16>(in, xlin, npix, H, W, cpix, K, s);
+hipError_t ConvLaunch::dw(int dtype, const void* dy, const void* x, float* ws, float* dwlin, int64_t npix, int H,
+                          int W, int Dp, int Cp, int K, int64_t rows_per_split, int nsplit, hipStream_t s) {
+  return dtype == 0 ? launch_conv_dw<float>(dy, x, ws, dwlin, npix, H, W, Dp, Cp, K, rows_per_split, nsplit, s)
+                    : launch_conv_dw<_Float16>(dy, x, ws, dwlin, npix, H, W, Dp, Cp, K, rows_per_split, nsplit, s);
 }
 
 hipError_t ConvLaunch::dw_scatter(int dtype, const float* dwlin, float* dpsi, int Dp, int Cp, int K, hipStream_t s) {

@@ -200,9 +200,9 @@ bool conv_weights_fit(int cpix, int K, int dtype) {
 
 bool conv_map_fits(int64_t npix, int C, int dtype) { return npix * C * elem_bytes(dtype) < (int64_t(1) << 31); }
 
-// Filter-gradient workspace: gathered rows, the gathered layer's dw, split partials.
+// Filter-gradient workspace: the gathered layer's dw, then its split partials.
 struct ConvWs {
-  size_t xlin, dwlin, split, total;
+  size_t dwlin, split, total;
   DwPlan plan;
 };
 
@@ -210,10 +210,9 @@ ConvWs conv_workspace(int64_t npix, int C, int D, int K, int dtype) {
   ConvWs w{};
   const int kg = eqlin::conv_gathered_groups(C / 4, K, dtype);
   w.plan = plan_dw(npix, 4 * kg, D, 4, dtype);
-  w.xlin = (static_cast<size_t>(npix) * kg * 4 * elem_bytes(dtype) + 255u) & ~size_t(255);
   w.dwlin = (static_cast<size_t>(D / 4) * kg * 4 * sizeof(float) + 255u) & ~size_t(255);
   w.split = static_cast<size_t>(w.plan.nsplit) * 4u * kg * static_cast<size_t>(D / 4) * sizeof(float);
-  w.total = w.xlin + w.dwlin + w.split;
+  w.total = w.dwlin + w.split;
   return w;
 }
 
@@ -438,16 +437,11 @@ int eqconv_backward(const void* dY, const void* X, int64_t N, int H, int W, int 
   }
   if (dpsi) {
     char* wsb = static_cast<char*>(workspace);
-    float* dwlin = reinterpret_cast<float*>(wsb + ws.xlin);
-    float* split = reinterpret_cast<float*>(wsb + ws.xlin + ws.dwlin);
-    const int kg = eqlin::conv_gathered_groups(C / 4, K, dtype);
-    if (npix > 0) {
-      const int e = hip_status(eqlin::ConvLaunch::gather(dtype, X, wsb, npix, H, W, C / 4, K, s));
-      if (e != EQLIN_OK) return e;
-    }
+    float* dwlin = reinterpret_cast<float*>(wsb);
+    float* split = reinterpret_cast<float*>(wsb + ws.dwlin);
     // the gathered layer's dw (zeros for an empty batch), then onto the filter
-    int e = hip_status(eqlin::Launch<4>::dw(dtype, dY, wsb, split, dwlin, npix, D / 4, kg, ws.plan.rows_per_split,
-                                            ws.plan.nsplit, s));
+    int e = hip_status(eqlin::ConvLaunch::dw(dtype, dY, X, split, dwlin, npix, H, W, D / 4, C / 4, K,
+                                             ws.plan.rows_per_split, ws.plan.nsplit, s));
     if (e != EQLIN_OK) return e;
     e = hip_status(eqlin::ConvLaunch::dw_scatter(dtype, dwlin, dpsi, D / 4, C / 4, K, s));
     if (e != EQLIN_OK) return e;

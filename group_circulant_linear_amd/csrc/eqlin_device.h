@@ -319,6 +319,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // Blocks are dispatched round-robin over the 8 XCDs.  Renumber so that
@@ -666,7 +669,14 @@ struct ConvGeom {
   int nblk;              // blocks per gathered row: cpix K^2 / (4 G)
   float inv_bpo, inv_p1; // 1 / bpo and 1 / (p + 1), for the block decode
   uint32_t in_bytes;     // bytes of the input map (< 2^31)
+  uint32_t w_mul, hw_mul;  // floor(n / W) = (n w_mul) >> w_shift for n < 2^31 (same for H W)
+  int w_shift, hw_shift;
 };
+
+// floor(n / d) for n < 2^31 with mul = ceil(2^shift / d), shift = 31 + ceil(log2 d)
+__device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t mul, int shift) {
+  return (uint32_t)(((uint64_t)n * mul) >> shift);
+}
 
 struct ConvBlock {
   int ch0, chstep;  // group channel of unit i: ch0 + chstep i
@@ -1097,10 +1107,15 @@ constexpr int dw_lds_bytes() {
   return NBUF * 2 * T * 64 * kRowBytes;
 }
 
-template <typename E, int G, int NBUF>
+// CONV: x is the input map of a p4 group convolution and the n axis runs over
+// the gathered group channels (see ConvGeom): each lane reads, per row, the
+// one value of each of the four taps (or, for a centre block, the four values
+// of its channel) that its gathered group channel needs, as 32-bit loads.
+template <typename E, int G, int NBUF, bool CONV = false>
 __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restrict__ dy, const E* __restrict__ x,
                                         float* __restrict__ ws, int64_t nrows, int mg, int ng,
-                                        int64_t rows_per_split, int tiles_m, int tiles_n) {
+                                        int64_t rows_per_split, int tiles_m, int tiles_n,
+                                        const ConvGeom& geo = ConvGeom{}) {
   constexpr int T = Grp<G>::kOrder;
   using U = Units<E, T>;
   constexpr int GPU = U::kGroupsPerUnit, PPU = U::kPiecesPerUnit;
@@ -1127,7 +1142,8 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
   const uint32_t a_row = (uint32_t)mg * (uint32_t)(T * sizeof(E));
   const uint32_t b_row = (uint32_t)ng * (uint32_t)(T * sizeof(E));
   const __amdgpu_buffer_rsrc_t a_src = make_rsrc(dy + rbeg * T * (int64_t)mg, (uint64_t)(rend - rbeg) * a_row);
-  const __amdgpu_buffer_rsrc_t b_src = make_rsrc(x + rbeg * T * (int64_t)ng, (uint64_t)(rend - rbeg) * b_row);
+  const __amdgpu_buffer_rsrc_t b_src =
+      CONV ? make_rsrc(x, geo.in_bytes) : make_rsrc(x + rbeg * T * (int64_t)ng, (uint64_t)(rend - rbeg) * b_row);
 
   const int pc = tid % PR, rq = tid / PR;
   const int ga = m0 + pc * GPU, gb = n0 + pc * GPU;
@@ -1135,7 +1151,30 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
   const uint32_t a_col = (uint32_t)ga * (uint32_t)(T * sizeof(E));
   const uint32_t b_col = (uint32_t)gb * (uint32_t)(T * sizeof(E));
 
-  u32x4 ra[KV][PPU], rb[KV][PPU];
+  // convolution: the sources of this lane's gathered group channel gb (fixed
+  // for the tile).  Source m is tap m of the block (orbit) or the lane's
+  // channel at the pixel (centre); jj[m] is the rotation read from it.
+  constexpr int NW = CONV ? 2 * GPU : 1;       // 32-bit loads per source and row
+  bool c_live = false;
+  int c_dy[4], c_dx[4], c_jj[4], c_off[4];
+  if constexpr (CONV) {
+    static_assert(T == 4 && PPU == 1, "p4 convolution");
+    constexpr int SGc = 16 * GPU;
+    const int w = (gb % SGc) / GPU, ui = w >> 2;
+    const ConvBlock k = conv_block<GPU>((gb / SGc) * 4 + (w & 3), geo);
+    c_live = b_ok && k.live;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      c_dy[m] = k.centre ? 0 : k.di[m];
+      c_dx[m] = k.centre ? 0 : k.dj[m];
+      c_jj[m] = k.centre ? m : ((m + ui) & 3);
+      const int ch = k.centre ? k.ch0 + k.chstep * ui : k.ch0;
+      c_off[m] = ((c_dy[m] * geo.W + c_dx[m]) * geo.cpix + ch) * (int)(T * sizeof(E));
+    }
+  }
+
+  u32x4 ra[KV][PPU], rb[CONV ? 1 : KV][PPU];
+  uint32_t rc[CONV ? KV : 1][4][NW];
   auto load = [&](int st) {
 #pragma unroll
     for (int v = 0; v < KV; ++v) {
@@ -1143,7 +1182,30 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
 #pragma unroll
       for (int h = 0; h < PPU; ++h) {
         ra[v][h] = bload16(a_src, a_ok ? row * a_row + a_col + 16u * h : kOob);
-        rb[v][h] = bload16(b_src, b_ok ? row * b_row + b_col + 16u * h : kOob);
+        if constexpr (!CONV) rb[v][h] = bload16(b_src, b_ok ? row * b_row + b_col + 16u * h : kOob);
+      }
+      if constexpr (CONV) {
+        const int64_t n = rbeg + row;
+        const bool rok = c_live && n < rend;
+        const uint32_t nn = rok ? (uint32_t)n : 0u;
+        const uint32_t img = div_magic(nn, geo.hw_mul, geo.hw_shift);
+        const uint32_t rem = nn - img * (uint32_t)(geo.H * geo.W);
+        const uint32_t py = div_magic(rem, geo.w_mul, geo.w_shift);
+        const uint32_t px = rem - py * (uint32_t)geo.W;
+        const uint32_t base = nn * (uint32_t)(geo.cpix * T * sizeof(E));
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const bool ok = rok && (unsigned)((int)py + c_dy[m]) < (unsigned)geo.H &&
+                          (unsigned)((int)px + c_dx[m]) < (unsigned)geo.W;
+          const uint32_t src = base + (uint32_t)c_off[m];
+          if constexpr (sizeof(E) == 4) {
+            rc[v][m][0] = bload4(b_src, ok ? src + 4u * (uint32_t)c_jj[m] : kOob);
+          } else {
+            // halves jj (channel e = 0) and 4 + jj (e = 1) of the 8-half source
+            rc[v][m][0] = bload4(b_src, ok ? src + 4u * (uint32_t)(c_jj[m] >> 1) : kOob);
+            rc[v][m][1] = bload4(b_src, ok ? src + 8u + 4u * (uint32_t)(c_jj[m] >> 1) : kOob);
+          }
+        }
       }
     }
   };
@@ -1195,7 +1257,27 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
   };
   auto store = [&](char* buf) {
     put(buf, ra, std::false_type{});
-    put(buf + T * PLANE, rb, std::true_type{});
+    if constexpr (CONV) {
+      // the gathered pieces: value m of channel e = the selected rotation of source m
+      u32x4 pcs[KV][PPU];
+#pragma unroll
+      for (int v = 0; v < KV; ++v) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if constexpr (sizeof(E) == 4) {
+            pcs[v][0][k] = rc[v][k][0];
+          } else {
+            const int e = k >> 1, m0 = 2 * (k & 1);
+            const uint32_t lo = (rc[v][m0][e] >> (16 * (c_jj[m0] & 1))) & 0xffffu;
+            const uint32_t hi = (rc[v][m0 + 1][e] >> (16 * (c_jj[m0 + 1] & 1))) & 0xffffu;
+            pcs[v][0][k] = lo | (hi << 16);
+          }
+        }
+      }
+      put(buf + T * PLANE, pcs, std::true_type{});
+    } else {
+      put(buf + T * PLANE, rb, std::true_type{});
+    }
   };
 
   f32x16 acc[T][1][1];

@@ -73,8 +73,10 @@ struct ConvLaunch {
                             int W, int cpix, int K, int mg, const void* bias, int act, hipStream_t s);
   // forward set (rows D', gathered over C') into wf, adjoint set (rows C', gathered over D') into wb
   static hipError_t prepare(int dtype, const void* psi, void* wf, void* wb, int Dp, int Cp, int K, hipStream_t s);
-  static hipError_t gather(int dtype, const void* in, void* xlin, int64_t npix, int H, int W, int cpix, int K,
-                           hipStream_t s);
+  // split partials of the gathered layer's dw (the gather in the loads) and their ordered
+  // finalize into dwlin [Dp][gathered groups][4]
+  static hipError_t dw(int dtype, const void* dy, const void* x, float* ws, float* dwlin, int64_t npix, int H, int W,
+                       int Dp, int Cp, int K, int64_t rows_per_split, int nsplit, hipStream_t s);
   static hipError_t dw_scatter(int dtype, const float* dwlin, float* dpsi, int Dp, int Cp, int K, hipStream_t s);
 };
 

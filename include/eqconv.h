@@ -31,7 +31,7 @@
  * The forward kernel of eqlin.h runs that layer with the gather done by its
  * loads (no gathered copy in global memory).  dX is the same kind of
  * convolution of dY with psi'[c', d', delta, v] = psi[d', c', -R^v delta,
- * -v mod 4]; the filter gradient is the layer's dw over the gathered rows.
+ * -v mod 4]; the filter gradient is the layer's dw, gathered the same way.
  *
  * Conventions (as eqlin.h unless stated):
  *   - dtype EQLIN_F32 or EQLIN_F16 with the arithmetic of eqlin.h; dpsi is
@@ -102,8 +102,9 @@ size_t eqconv_backward_workspace_bytes(int64_t N, int H, int W, int C, int D, in
  * Backward for upstream gradient dY [N][H][W][D]:
  *   dX [N][H][W][C] = d<dY, Y>/dX   (skipped if dX == NULL)
  *   dpsi [D'][C'][K][K][4] float32 = d<dY, Y>/dpsi   (skipped if dpsi == NULL)
- * dpsi is reduced over row splits in a fixed order (deterministic).  The
- * workspace holds the gathered rows of X, the split partials and the
+ * dpsi is the gathered layer's dw, with the gather done by the loads of its
+ * reduction, reduced over row splits in a fixed order (deterministic) and
+ * permuted onto the filter.  The workspace holds the split partials and the
  * gathered layer's gradient; it may be NULL only when dpsi == NULL, and X
  * may be NULL only when dpsi == NULL.  At least one output is required.
  */
