@@ -74,7 +74,7 @@ struct TileShape {
 // long-K and wide layers (up to 15 % over the best one-tile-per-workgroup
 // kernel): the tile epilogue, which dominates there, overlaps the next
 // tile's loads and MFMAs.
-constexpr TileShape kP4F32Tiles[] = {{112211, 64, 64, 0.745}, {112221, 64, 64, 0.70}, {111211, 32, 64, 0.70}};
+constexpr TileShape kP4F32Tiles[] = {{112211, 64, 64, 0.745}, {112221, 64, 64, 0.70}, {111211, 32, 64, 0.59}};
 constexpr TileShape kP4F16Tiles[] = {{212421, 128, 128, 0.24}, {112211, 64, 64, 0.17}, {111221, 32, 64, 0.12}};
 constexpr TileShape kC8F32Tiles[] = {{112211, 64, 64, 0.58}, {112221, 64, 64, 0.55}, {111221, 32, 64, 0.31}};
 constexpr TileShape kC8F16Tiles[] = {
