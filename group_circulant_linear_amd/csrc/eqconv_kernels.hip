@@ -147,6 +147,32 @@ conv_dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float*
                                tiles_m, tiles_n, geo);
 }
 
+// Backward in one launch, as the linear layer's: the first ndw_pad
+// workgroups are the dpsi split partials (gathered over the C' channels of
+// X), the rest are dX tiles (the convolution of dY with the adjoint spectra,
+// gathered over its D' channels).  Both read dY; one grid lets the dispatcher
+// fill the tail of one role with work of the other.
+template <typename E>
+__global__ void __launch_bounds__(kThreads, bwd_waves_per_simd<4>())
+conv_bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E* __restrict__ wb,
+                      E* __restrict__ dx, float* __restrict__ ws, int64_t npix, int Dp, int Cp, int kgw, int kgx,
+                      int64_t rows_per_split, int dw_tiles_m, int dw_tiles_n, int64_t ndw, int64_t ndw_pad,
+                      int dx_tiles_n, ConvGeom gw, ConvGeom gx) {
+  constexpr int kFwd = fwd_lds_bytes<E, 4, 1, 1, 2, 2, kBwdFwdBufs>();
+  constexpr int kDw = dw_lds_bytes<4, kDwBufs>();
+  __shared__ __attribute__((aligned(16))) char lds[kFwd > kDw ? kFwd : kDw];
+  const int64_t b = blockIdx.x;
+  if (b < ndw_pad) {
+    const int64_t lid = xcd_logical_id(b, ndw_pad);
+    if (lid < ndw)
+      dw_tile<E, 4, kDwBufs, true>(lds, lid, dy, x, ws, npix, Dp, kgw, rows_per_split, dw_tiles_m, dw_tiles_n, gw);
+  } else {
+    const int64_t nb = gridDim.x - ndw_pad;
+    fwd_tile<E, 4, 1, 1, 2, 2, kBwdFwdBufs, kBwdFwdPrefetch, 1, true>(lds, xcd_logical_id(b - ndw_pad, nb), dy, wb, dx,
+                                                                       npix, kgx, Cp, dx_tiles_n, nullptr, 0, gx);
+  }
+}
+
 // Filter gradient from the gathered layer's dw: dpsi[d'][c][tap][v] =
 // dwlin[d'][g][u] through the block decode (a permutation).
 template <typename E>
@@ -216,6 +242,31 @@ hipError_t launch_conv_dw(const void* dy, const void* x, float* ws, float* dwlin
 }
 
 template <typename E>
+hipError_t launch_conv_bwd_fused(const void* dy, const void* x, const void* wb, void* dx, float* ws, float* dwlin,
+                                 int64_t npix, int H, int W, int Dp, int Cp, int K, int64_t rows_per_split, int nsplit,
+                                 hipStream_t s) {
+  const int dt = sizeof(E) == 4 ? 0 : 1;
+  const int kgw = conv_gathered_groups(Cp, K, dt), kgx = conv_gathered_groups(Dp, K, dt);
+  const int dw_tiles_m = (int)cdiv(Dp, 64), dw_tiles_n = (int)cdiv(kgw, 64);
+  const int64_t ndw = (int64_t)dw_tiles_m * dw_tiles_n * nsplit;
+  const int64_t ndw_pad = cdiv(ndw, 8) * 8;
+  const int dx_tiles_n = (int)cdiv(Cp, 64);
+  const int64_t grid = ndw_pad + cdiv(npix, 64) * dx_tiles_n;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (grid > 0) {
+    hipLaunchKernelGGL((conv_bwd_fused_kernel<E>), dim3((unsigned)grid), dim3(kThreads), 0, s,
+                       static_cast<const E*>(dy), static_cast<const E*>(x), static_cast<const E*>(wb),
+                       static_cast<E*>(dx), ws, npix, Dp, Cp, kgw, kgx, rows_per_split, dw_tiles_m, dw_tiles_n, ndw,
+                       ndw_pad, dx_tiles_n, make_geom<E>(H, W, Cp, K, npix), make_geom<E>(H, W, Dp, K, npix));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t fgrid = cdiv((int64_t)Dp * kgw, kThreads / 4);
+  hipLaunchKernelGGL((dw_finalize_kernel<4>), dim3((unsigned)fgrid), dim3(kThreads), 0, s, ws, dwlin, Dp, kgw, nsplit);
+  return hipGetLastError();
+}
+
+template <typename E>
 hipError_t launch_conv_dw_scatter(const float* dwlin, float* dpsi, int Dp, int Cp, int K, hipStream_t s) {
   const int kg = conv_gathered_groups(Cp, K, sizeof(E) == 4 ? 0 : 1);
   const int64_t n = (int64_t)Dp * kg;
@@ -261,6 +312,15 @@ hipError_t ConvLaunch::dw(int dtype, const void* dy, const void* x, float* ws, f
                           int W, int Dp, int Cp, int K, int64_t rows_per_split, int nsplit, hipStream_t s) {
   return dtype == 0 ? launch_conv_dw<float>(dy, x, ws, dwlin, npix, H, W, Dp, Cp, K, rows_per_split, nsplit, s)
                     : launch_conv_dw<_Float16>(dy, x, ws, dwlin, npix, H, W, Dp, Cp, K, rows_per_split, nsplit, s);
+}
+
+hipError_t ConvLaunch::bwd_fused(int dtype, const void* dy, const void* x, const void* wb, void* dx, float* ws,
+                                 float* dwlin, int64_t npix, int H, int W, int Dp, int Cp, int K,
+                                 int64_t rows_per_split, int nsplit, hipStream_t s) {
+  return dtype == 0 ? launch_conv_bwd_fused<float>(dy, x, wb, dx, ws, dwlin, npix, H, W, Dp, Cp, K, rows_per_split,
+                                                   nsplit, s)
+                    : launch_conv_bwd_fused<_Float16>(dy, x, wb, dx, ws, dwlin, npix, H, W, Dp, Cp, K,
+                                                      rows_per_split, nsplit, s);
 }
 
 hipError_t ConvLaunch::dw_scatter(int dtype, const float* dwlin, float* dpsi, int Dp, int Cp, int K, hipStream_t s) {

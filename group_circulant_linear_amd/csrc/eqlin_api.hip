@@ -433,6 +433,16 @@ int eqconv_backward(const void* dY, const void* X, int64_t N, int H, int W, int 
     if (workspace_bytes < ws.total) return EQLIN_EWORKSPACE;
   }
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dX && dpsi && npix > 0 && use_fused_backward()) {
+    // one launch for dX and the dpsi partials (they share dY), the finalize, then onto the filter
+    char* wsb = static_cast<char*>(workspace);
+    const char* wb = static_cast<const char*>(prepared) + conv_adjoint_offset(C, D, K, dtype);
+    int e = hip_status(eqlin::ConvLaunch::bwd_fused(dtype, dY, X, wb, dX, reinterpret_cast<float*>(wsb + ws.dwlin),
+                                                    reinterpret_cast<float*>(wsb), npix, H, W, D / 4, C / 4, K,
+                                                    ws.plan.rows_per_split, ws.plan.nsplit, s));
+    if (e != EQLIN_OK) return e;
+    return hip_status(eqlin::ConvLaunch::dw_scatter(dtype, reinterpret_cast<float*>(wsb), dpsi, D / 4, C / 4, K, s));
+  }
   if (dX && npix > 0) {
     // dX: the convolution of dY with the adjoint filter (input D', output C')
     const char* wb = static_cast<const char*>(prepared) + conv_adjoint_offset(C, D, K, dtype);

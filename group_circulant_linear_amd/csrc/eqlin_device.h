@@ -345,16 +345,29 @@ __device__ __forceinline__ void store_group(E* dst, const float* y) {
       __builtin_nontemporal_store(
           __builtin_bit_cast(u32x4, f32x4{y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]}),
           reinterpret_cast<u32x4*>(dst + 4 * i));
-  } else if constexpr (T == 4) {
-    const f16x4 h = {(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]};
-    __builtin_nontemporal_store(__builtin_bit_cast(u32x2, h), reinterpret_cast<u32x2*>(dst));
   } else {
+    // Every kernel rounds the float32 result to binary16 the same way (float32
+    // first, then nearest-even): the empty asm keeps the compiler from folding
+    // the inverse transform's last multiply-add into a mixed-precision FMA that
+    // rounds once, which it does in some kernels and not in others, so the
+    // same output would differ by one unit in the last place between paths.
+    float v[T];
 #pragma unroll
-    for (int i = 0; i < T / 8; ++i) {
-      f16x8 h;
+    for (int i = 0; i < T; ++i) {
+      v[i] = y[i];
+      asm volatile("" : "+v"(v[i]));
+    }
+    if constexpr (T == 4) {
+      const f16x4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x2, h), reinterpret_cast<u32x2*>(dst));
+    } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) h[e] = (_Float16)y[8 * i + e];
-      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, h), reinterpret_cast<u32x4*>(dst + 8 * i));
+      for (int i = 0; i < T / 8; ++i) {
+        f16x8 h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (_Float16)v[8 * i + e];
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, h), reinterpret_cast<u32x4*>(dst + 8 * i));
+      }
     }
   }
 }

@@ -77,6 +77,11 @@ struct ConvLaunch {
   // finalize into dwlin [Dp][gathered groups][4]
   static hipError_t dw(int dtype, const void* dy, const void* x, float* ws, float* dwlin, int64_t npix, int H, int W,
                        int Dp, int Cp, int K, int64_t rows_per_split, int nsplit, hipStream_t s);
+  // dX (64 x 64 tiles on the adjoint spectra wb) and the dw split partials in one launch,
+  // then the finalize into dwlin.  npix > 0.
+  static hipError_t bwd_fused(int dtype, const void* dy, const void* x, const void* wb, void* dx, float* ws,
+                              float* dwlin, int64_t npix, int H, int W, int Dp, int Cp, int K, int64_t rows_per_split,
+                              int nsplit, hipStream_t s);
   static hipError_t dw_scatter(int dtype, const float* dwlin, float* dpsi, int Dp, int Cp, int K, hipStream_t s);
 };
 
