@@ -1,9 +1,12 @@
 // Device code of the group-circulant (EQ-)linear layer for gfx950 (CDNA4):
-// group transforms, the matrix-core "complex core", the forward / dX tile,
-// the dw split-partial tile, the dw finalize and the weight preparation, all
+// group transforms, the matrix-core "complex core", the forward / dX tile
+// (one tile per workgroup, or the persistent stage stream), the dw
+// split-partial tile, the dw finalize and the weight preparation, all
 // templated on the storage type E (float or _Float16) and the group G: 4 (the
 // p4 rotation group, cyclic of order 4), 8 (the cyclic group C8) or kP4M (the
-// dihedral group p4m of order 8).
+// dihedral group p4m of order 8).  The forward and dw tiles also have a p4
+// convolution mode (ConvGeom) whose operand loads gather a K x K window;
+// the convolution's own kernels are in eqconv_kernels.hip.
 //
 // Method (Flash EQ-Linear technical summary, gist.science 2607.21271):
 //   * "Key insight": the weight is group-circulant, so the layer is a circular
@@ -16,10 +19,11 @@
 //     and the contraction is six real matrix products: f0 (1), f2 (1) and the
 //     complex f1 (4: Re/Im cross terms).
 //   * "Limitations": the specialisation is to p4; other groups (reflections
-//     among them) are future work.  C8 here follows the same route with the
-//     general real-signal DFT: real f0 and f4, complex f1..f3, 2 + 3 * 4 = 14
-//     real products.  p4m uses its irreducible representations: four 1-D and
-//     one 2-D, 4 + 8 = 12 real products.
+//     among them) and other equivariant operators (convolution) are future
+//     work.  C8 here follows the same route with the general real-signal DFT:
+//     real f0 and f4, complex f1..f3, 2 + 3 * 4 = 14 real products.  p4m uses
+//     its irreducible representations: four 1-D and one 2-D, 4 + 8 = 12 real
+//     products.  The p4 convolution is the p4 layer over a gathered window.
 //   * "Implementation": fused dataflow (no intermediate global writes), Fourier
 //     fragments resident in registers / on-chip memory, shape-specialised
 //     tiles on the matrix cores.

@@ -3,8 +3,8 @@
 Every step of the layer runs in the HIP library; this module checks tensor
 shapes, dtypes, devices and contiguity, allocates outputs with PyTorch (device
 memory plumbing) and passes raw pointers plus torch's current HIP stream to the
-C ABI declared in include/eqlin.h and include/eqconv.h.  There is no fallback: if the library is not
-built, every call raises.
+C ABI declared in include/eqlin.h and include/eqconv.h.  There is no fallback:
+if the library is not built, every call raises.
 """
 from __future__ import annotations
 

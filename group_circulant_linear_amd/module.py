@@ -8,6 +8,12 @@ backward through the HIP library (eqlin_prepare_weights / eqlin_forward /
 eqlin_backward).  The prepared spectra are cached per weight version, so they
 are recomputed only after w changes (an optimizer step or a load).
 
+FlashEQConv2d does the same for the p4 group convolution with K x K filters
+(the summary's "Limitations and future work" names equivariant convolution
+as the next operator): parameter psi [D/4][C/4][K][K][4], channels-last maps,
+forward and backward through eqconv_prepare_weights / eqconv_forward /
+eqconv_backward; its 1 x 1 case is FlashEQLinear with group p4.
+
 There is no CPU or eager fallback: tensors must live on the GPU.
 """
 from __future__ import annotations
