@@ -429,6 +429,8 @@ int eqconv_backward(const void* dY, const void* X, int64_t N, int H, int W, int 
     if (npix > 0 && (!dY || !X)) return EQLIN_EINVAL;
     if (!aligned16(dpsi) || !aligned16(workspace)) return EQLIN_EALIGN;
     if (npix > 0 && (!aligned16(dY) || !aligned16(X))) return EQLIN_EALIGN;
+    // the gather reads X through 32-bit buffer offsets
+    if (!conv_map_fits(npix, C, dtype)) return EQLIN_ENOTSUP;
     ws = conv_workspace(npix, C, D, K, dtype);
     if (workspace_bytes < ws.total) return EQLIN_EWORKSPACE;
   }

@@ -40,9 +40,9 @@
  *     of 4 (EQLIN_F32) or 8 (EQLIN_F16), else EQLIN_ENOTSUP.
  *   - K: odd, 1 <= K <= 15, else EQLIN_ENOTSUP (K <= 0 or even: EQLIN_EINVAL).
  *   - N, H, W >= 0; N*H*W == 0 is an empty batch (forward and dX enqueue
- *     nothing; dpsi is written as zeros).  The input map of a launch (X for
- *     the forward, dY for dX) must be smaller than 2^31 bytes, else
- *     EQLIN_ENOTSUP.
+ *     nothing; dpsi is written as zeros).  The maps a launch gathers from (X
+ *     for the forward and for dpsi, dY for dX) must be smaller than 2^31
+ *     bytes, else EQLIN_ENOTSUP.
  *   - Device pointers, caller-owned, 16-byte aligned (else EQLIN_EALIGN); the
  *     library allocates nothing; calls only enqueue work on `stream`; all
  *     arguments are validated before anything is enqueued; a HIP launch

@@ -209,3 +209,7 @@ def test_conv_validation(lib):
     assert bw(FAKE, FAKE, 1, 4, 4, 16, 16, 3, FAKE, FAKE, FAKE, FAKE, ws - 1, 0, None) == EWORKSPACE
     # empty batch with dX only: no-op
     assert bw(None, None, 0, 4, 4, 16, 16, 3, None, FAKE, None, None, 0, 0, None) == OK
+    # an X map of 2^31 bytes or more is refused for dpsi (dY small: C = 4 D)
+    big = (1 << 12, 128, 128, 64, 16, 3)
+    wsb = lib.eqconv_backward_workspace_bytes(*big, 0)
+    assert bw(FAKE, FAKE, *big, FAKE, None, FAKE, FAKE, wsb, 0, None) == ENOTSUP
