@@ -171,6 +171,20 @@ def test_full_size_workload_sampled(dt):
     assert rel_err(got, ref) < TOL[dt]
 
 
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_wide_filter_on_a_small_map(dt):
+    # C = 1024, K = 5: 6400 gathered group channels (200 f32 / 100 f16 stages), D' = 72
+    N, H, W, C, D, K = 1, 6, 7, 1024, 288, 5
+    say(f"conv wide {dt}")
+    X, psi, dY = make_conv_inputs(N, H, W, C, D, K, dt, seed=12)
+    P = eq.eqconv_prepare_weights(dev(psi))
+    Y = eq.eqconv_forward(dev(X), P)
+    dX, dpsi = eq.eqconv_backward(dev(dY), dev(X), P)
+    assert rel_err(host(Y), oracle.conv_forward(X, psi)) < TOL[dt]
+    assert rel_err(host(dX), oracle.conv_dx(dY, psi, H, W)) < TOL[dt]
+    assert rel_err(host(dpsi), oracle.conv_dw(dY, X, K)) < TOL[dt]
+
+
 def test_module_autograd_matches_oracle():
     from group_circulant_linear_amd.module import FlashEQConv2d
     N, H, W, C, D, K = 2, 8, 10, 16, 32, 3

@@ -263,6 +263,25 @@ def test_backward_separate_entry_points_agree(g):
 
 # -------------------------------------------------------------- edge cases
 
+@pytest.mark.parametrize("g", [4, 8])
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_extreme_widths_and_heights(dt, g):
+    # a very wide layer (C = 2^17: 512 KiB rows in fp32, 8192 pipeline stages),
+    # then a tall thin one (about a million rows: many dw splits, ragged last split)
+    T = order(g)
+    for (N, C, D) in ((40, 1 << 17, 64), ((1 << 20) + 37, 16, 32)):
+        say(f"extreme group={g} {dt} N={N} C={C} D={D}")
+        X, w, dY = make_layer_inputs(N, C, D, dt, seed=11, T=T)
+        Wh = prep(w, g)
+        Y = eq.eqlin_forward(dev(X), Wh)
+        dX, dw = eq.eqlin_backward(dev(dY), dev(X), Wh)
+        e = (rel_err(host(Y), ref_forward(X, w, g)), rel_err(host(dX), ref_dx(dY, w, g)),
+             rel_err(host(dw), ref_dw(dY, X, g)))
+        say(f"  Y {e[0]:.2e} dX {e[1]:.2e} dw {e[2]:.2e}")
+        assert max(e) <= TOL[dt], e
+        del X, dY, Y, dX, dw
+
+
 @pytest.mark.parametrize("g", GROUPS)
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 def test_empty_batch(dt, g):
