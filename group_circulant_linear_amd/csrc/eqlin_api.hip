@@ -64,6 +64,9 @@ bool fwd_offsets_fit(int in_width, int O, int dtype) {
   return 256 * row_bytes < kMaxTileBytes && 256 * wrow_bytes < kMaxTileBytes;
 }
 
+// The tile epilogue stores through 32-bit offsets within the tile's rows.
+bool out_rows_fit(int out_width, int dtype) { return 256 * int64_t(out_width) * elem_bytes(dtype) < kMaxTileBytes; }
+
 struct TileShape {
   int code, bm, bn;
   double eff;  // measured fraction of the MFMA peak on large shapes (MI355X, clocks settled)
@@ -282,7 +285,7 @@ int eqlin_forward_ex(const void* X, int64_t N, int C, int D, int T, const void* 
   if (!X || !W_hat || !Y) return EQLIN_EINVAL;
   if (!aligned16(X) || !aligned16(W_hat) || !aligned16(Y)) return EQLIN_EALIGN;
   if (bias && (reinterpret_cast<uintptr_t>(bias) % elem_bytes(dtype)) != 0) return EQLIN_EALIGN;
-  if (!fwd_offsets_fit(C, O, dtype)) return EQLIN_ENOTSUP;
+  if (!fwd_offsets_fit(C, O, dtype) || !out_rows_fit(D, dtype)) return EQLIN_ENOTSUP;
   const int tile = choose_fwd_tile(T, dtype, N, D / O);
   return hip_status(EQLIN_BY_T(T, forward(dtype, tile, X, W_hat, Y, N, C / O, D / O, bias, act,
                                           static_cast<hipStream_t>(stream))));
@@ -304,7 +307,7 @@ int eqlin_backward_dx(const void* dY, int64_t N, int C, int D, int T, const void
   if (N == 0) return EQLIN_OK;
   if (!dY || !W_hat || !dX) return EQLIN_EINVAL;
   if (!aligned16(dY) || !aligned16(W_hat) || !aligned16(dX)) return EQLIN_EALIGN;
-  if (!fwd_offsets_fit(D, O, dtype)) return EQLIN_ENOTSUP;
+  if (!fwd_offsets_fit(D, O, dtype) || !out_rows_fit(C, dtype)) return EQLIN_ENOTSUP;
   // dX = dY W: the forward kernel with the transposed, conjugated planes
   // (input groups D', output groups C').
   const char* wb = static_cast<const char*>(W_hat) + transpose_offset(C, D, O, dtype);
@@ -338,7 +341,7 @@ int eqlin_backward(const void* dY, const void* X, int64_t N, int C, int D, int T
   if (dX && N > 0) {
     if (!dY || !W_hat) return EQLIN_EINVAL;
     if (!aligned16(dY) || !aligned16(W_hat) || !aligned16(dX)) return EQLIN_EALIGN;
-    if (!fwd_offsets_fit(D, O, dtype)) return EQLIN_ENOTSUP;
+    if (!fwd_offsets_fit(D, O, dtype) || !out_rows_fit(C, dtype)) return EQLIN_ENOTSUP;
   }
   if (dw) {
     if (N > 0 && (!dY || !X || !workspace)) return EQLIN_EINVAL;
@@ -396,7 +399,8 @@ int eqconv_forward(const void* X, int64_t N, int H, int W, int C, int D, int K, 
   if (!X || !prepared || !Y) return EQLIN_EINVAL;
   if (!aligned16(X) || !aligned16(prepared) || !aligned16(Y)) return EQLIN_EALIGN;
   if (bias && (reinterpret_cast<uintptr_t>(bias) % elem_bytes(dtype)) != 0) return EQLIN_EALIGN;
-  if (!conv_map_fits(npix, C, dtype) || !conv_weights_fit(C / 4, K, dtype)) return EQLIN_ENOTSUP;
+  if (!conv_map_fits(npix, C, dtype) || !conv_weights_fit(C / 4, K, dtype) || !out_rows_fit(D, dtype))
+    return EQLIN_ENOTSUP;
   const int tile = choose_conv_tile(dtype, npix, D / 4);
   return hip_status(eqlin::ConvLaunch::forward(dtype, tile, X, prepared, Y, npix, H, W, C / 4, K, D / 4, bias, act,
                                                static_cast<hipStream_t>(stream)));
@@ -421,7 +425,8 @@ int eqconv_backward(const void* dY, const void* X, int64_t N, int H, int W, int 
   if (dX && npix > 0) {
     if (!dY || !prepared) return EQLIN_EINVAL;
     if (!aligned16(dY) || !aligned16(prepared) || !aligned16(dX)) return EQLIN_EALIGN;
-    if (!conv_map_fits(npix, D, dtype) || !conv_weights_fit(D / 4, K, dtype)) return EQLIN_ENOTSUP;
+    if (!conv_map_fits(npix, D, dtype) || !conv_weights_fit(D / 4, K, dtype) || !out_rows_fit(C, dtype))
+      return EQLIN_ENOTSUP;
   }
   ConvWs ws{};
   if (dpsi) {

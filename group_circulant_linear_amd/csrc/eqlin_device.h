@@ -376,6 +376,41 @@ __device__ __forceinline__ void store_group(E* dst, const float* y) {
   }
 }
 
+// The same group store through a buffer resource: offsets at or past its
+// range (a row beyond the last, or kOob for a column beyond the last) drop
+// the store.  aux 2 = non-temporal.
+template <typename E, int T>
+__device__ __forceinline__ void store_group_buf(__amdgpu_buffer_rsrc_t dst, uint32_t off, const float* y) {
+  constexpr int kNt = 2;
+  if constexpr (sizeof(E) == 4) {
+#pragma unroll
+    for (int i = 0; i < T / 4; ++i)
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(u32x4, f32x4{y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]}), dst, off + 16u * i,
+          0, kNt);
+  } else {
+    // float32 first, then binary16, in every kernel (see store_group)
+    float v[T];
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      v[i] = y[i];
+      asm volatile("" : "+v"(v[i]));
+    }
+    if constexpr (T == 4) {
+      const f16x4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), dst, off, 0, kNt);
+    } else {
+#pragma unroll
+      for (int i = 0; i < T / 8; ++i) {
+        f16x8 h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (_Float16)v[8 * i + e];
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, h), dst, off + 16u * i, 0, kNt);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------ input transforms
 //
 // T 16-byte pieces fetched in unit order (see Units) hold kVals whole groups
@@ -499,14 +534,19 @@ __device__ __forceinline__ void products_f32(std::integer_sequence<int, I...>,
    ...);
 }
 
-template <int G, bool kDwRole, int FM, int FN, int... I>
+// kNegB: a negated product flips the sign of its B operand instead of its A
+// operand (the same products; the sign flips cost 4 XORs per plane and
+// fragment, so they go to the operand with fewer fragments).
+template <int G, bool kDwRole, int FM, int FN, bool kNegB, int... I>
 __device__ __forceinline__ void products_f16(std::integer_sequence<int, I...>,
                                              f32x16 (&acc)[Grp<G>::kOrder][FM][FN],
                                              const f16x8 (&av)[Grp<G>::kOrder], const f16x8 (&nav)[Grp<G>::kOrder],
-                                             const f16x8 (&bv)[Grp<G>::kOrder], int fm, int fn) {
+                                             const f16x8 (&bv)[Grp<G>::kOrder], const f16x8 (&nbv)[Grp<G>::kOrder],
+                                             int fm, int fn) {
   ((acc[product<G, kDwRole, I>().out][fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-        product<G, kDwRole, I>().neg ? nav[product<G, kDwRole, I>().a] : av[product<G, kDwRole, I>().a],
-        bv[product<G, kDwRole, I>().b], acc[product<G, kDwRole, I>().out][fm][fn], 0, 0, 0)),
+        product<G, kDwRole, I>().neg && !kNegB ? nav[product<G, kDwRole, I>().a] : av[product<G, kDwRole, I>().a],
+        product<G, kDwRole, I>().neg && kNegB ? nbv[product<G, kDwRole, I>().b] : bv[product<G, kDwRole, I>().b],
+        acc[product<G, kDwRole, I>().out][fm][fn], 0, 0, 0)),
    ...);
 }
 
@@ -545,23 +585,28 @@ struct Core<_Float16, G, kDwRole, FM, FN> {
   __device__ __forceinline__ static void mma(f32x16 (&acc)[T][FM][FN], const u32x4 (&a)[T][FM],
                                              const u32x4 (&b)[T][FN]) {
     constexpr u32x4 kSign = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    constexpr bool kNegB = FN < FM;
+    // nbv / nav: the negated operands (only those named by a product are used)
+    f16x8 bv[FN][T], nbv[FN][T];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int p = 0; p < T; ++p) {
+        bv[fn][p] = __builtin_bit_cast(f16x8, b[p][fn]);
+        nbv[fn][p] = __builtin_bit_cast(f16x8, kNegB ? b[p][fn] ^ kSign : b[p][fn]);
+      }
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
-      // nav: the negated operands (only those named by a product are used)
       f16x8 av[T], nav[T];
 #pragma unroll
       for (int p = 0; p < T; ++p) {
         av[p] = __builtin_bit_cast(f16x8, a[p][fm]);
-        nav[p] = __builtin_bit_cast(f16x8, a[p][fm] ^ kSign);
+        nav[p] = __builtin_bit_cast(f16x8, kNegB ? a[p][fm] : a[p][fm] ^ kSign);
       }
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        f16x8 bv[T];
-#pragma unroll
-        for (int p = 0; p < T; ++p) bv[p] = __builtin_bit_cast(f16x8, b[p][fn]);
-        products_f16<G, kDwRole, FM, FN>(std::make_integer_sequence<int, Grp<G>::kProducts>{}, acc, av, nav, bv, fm,
-                                         fn);
-      }
+      for (int fn = 0; fn < FN; ++fn)
+        products_f16<G, kDwRole, FM, FN, kNegB>(std::make_integer_sequence<int, Grp<G>::kProducts>{}, acc, av, nav,
+                                                bv[fn], nbv[fn], fm, fn);
     }
   }
 };
@@ -639,31 +684,36 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[Grp<G>::kOrder]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr = wave / WN, wc = wave % WN;
   const int li = lane & 31, lh = lane >> 5;
-  const int64_t out_ld = T * (int64_t)mg;
+  const uint32_t row_bytes = (uint32_t)(T * mg) * (uint32_t)sizeof(E);
+  // The tile's rows as one buffer: rows past nrows lie beyond its range and
+  // their stores are dropped, as are those of a column past mg (kOob), so the
+  // row loop needs no bounds test and only 32-bit offsets.
+  const __amdgpu_buffer_rsrc_t dst = make_rsrc(out + row0 * (int64_t)T * mg, (uint64_t)(nrows - row0) * row_bytes);
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
       const int m = col0 + wc * 32 * FN + fn * 32 + li;
-      const float bm = (bias != nullptr && m < mg) ? (float)bias[m] : 0.f;
+      const bool mok = m < mg;
+      const float bm = (bias != nullptr && mok) ? (float)bias[m] : 0.f;
+      const uint32_t lane_off =
+          mok ? (uint32_t)(wr * 32 * FM + fm * 32 + 4 * lh) * row_bytes + (uint32_t)m * (uint32_t)(T * sizeof(E))
+              : kOob;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = row0 + wr * 32 * FM + fm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (row < nrows && m < mg) {
-          float f[T], y[T];
+        float f[T], y[T];
 #pragma unroll
-          for (int p = 0; p < T; ++p) f[p] = acc[p][fm][fn][r];
-          Grp<G>::idft(f, y);
-          if (bias != nullptr) {
+        for (int p = 0; p < T; ++p) f[p] = acc[p][fm][fn][r];
+        Grp<G>::idft(f, y);
+        if (bias != nullptr) {
 #pragma unroll
-            for (int t = 0; t < T; ++t) y[t] += bm;
-          }
-          if (act == 1) {
-#pragma unroll
-            for (int t = 0; t < T; ++t) y[t] = gelu_erf(y[t]);
-          }
-          store_group<E, T>(out + row * out_ld + T * (int64_t)m, y);
+          for (int t = 0; t < T; ++t) y[t] += bm;
         }
+        if (act == 1) {
+#pragma unroll
+          for (int t = 0; t < T; ++t) y[t] = gelu_erf(y[t]);
+        }
+        store_group_buf<E, T>(dst, lane_off + (uint32_t)(8 * (r >> 2) + (r & 3)) * row_bytes, y);
       }
     }
   }
