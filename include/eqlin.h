@@ -61,6 +61,9 @@
  *     by the HIP runtime returns EQLIN_EHIP (see eqlin_last_hip_error()).
  *   - N == 0 is a valid empty batch: forward and dX enqueue nothing, dw is
  *     written as zeros.
+ *   - Kernels address one tile (at most 256 rows) with 32-bit offsets: C and D
+ *     must keep 256 rows of X, Y, dY and dX below 1 GiB (C, D < 2^20 in
+ *     float32), else EQLIN_ENOTSUP.
  */
 #ifndef EQLIN_H
 #define EQLIN_H
@@ -82,7 +85,8 @@ enum { EQLIN_P4M = 108 };
 enum {
   EQLIN_OK = 0,
   EQLIN_EINVAL = 1,     /* bad size, negative N, null required pointer, unknown dtype */
-  EQLIN_ENOTSUP = 2,    /* T not 4, 8 or EQLIN_P4M, or an odd group count with EQLIN_F16 and T = 4 */
+  EQLIN_ENOTSUP = 2,    /* T not 4, 8 or EQLIN_P4M, an odd group count with EQLIN_F16 and T = 4, or
+                           rows so wide that 256 of them (input or output) pass 1 GiB */
   EQLIN_EALIGN = 3,     /* a data pointer is not 16-byte aligned */
   EQLIN_EWORKSPACE = 4, /* workspace / prepared-weight buffer too small */
   EQLIN_EHIP = 5        /* the HIP runtime reported an error for a launch */
