@@ -323,6 +323,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
+// Same with a wave-uniform offset added in the scalar operand (a stage
+// advance); the range test is made on `off`, which alone decides whether the
+// lane reads memory or zeros.
+__device__ __forceinline__ u32x4 bload16s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0);
+}
 __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
@@ -883,27 +889,33 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
         }
       }
     } else {
+      // the stage advance is wave-uniform (scalar offset); a unit reads only
+      // below the row's last group channel (lim <= 0 past the last stage)
+      const int lim = kg - ks * SG;
+      const uint32_t soff = (uint32_t)(ks * SG) * (uint32_t)(T * sizeof(E));
 #pragma unroll
-    for (int ps = 0; ps < PA; ++ps) {
-      const uint32_t r = (uint32_t)(ps * RPP + rl);
+      for (int ps = 0; ps < PA; ++ps) {
+        const uint32_t r = (uint32_t)(ps * RPP + rl);
 #pragma unroll
-      for (int i = 0; i < U::kUnits; ++i) {
-        const int g = ks * SG + (q + 4 * i) * U::kGroupsPerUnit;
+        for (int i = 0; i < U::kUnits; ++i) {
+          const int u = (q + 4 * i) * U::kGroupsPerUnit;
 #pragma unroll
-        for (int h = 0; h < U::kPiecesPerUnit; ++h) {
-          const uint32_t off = g < kg ? r * row_bytes + (uint32_t)g * (uint32_t)(T * sizeof(E)) + 16u * h : kOob;
-          ra[sl][ps][i * U::kPiecesPerUnit + h] = bload16(a_src, off);
+          for (int h = 0; h < U::kPiecesPerUnit; ++h) {
+            const uint32_t off = u < lim ? r * row_bytes + (uint32_t)u * (uint32_t)(T * sizeof(E)) + 16u * h : kOob;
+            ra[sl][ps][i * U::kPiecesPerUnit + h] = bload16s(a_src, off, soff);
+          }
         }
       }
     }
-    }
+    // weights: past the last stage the loads re-read it (the pipeline's idle
+    // stage, never multiplied), so the scalar offset stays inside each row
+    const uint32_t soffb = (uint32_t)(ks < ksteps ? ks : ksteps - 1) * (uint32_t)BLOCK;
 #pragma unroll
     for (int ps = 0; ps < PB; ++ps) {
       const uint32_t m = (uint32_t)(ps * RPP + rl);
 #pragma unroll
       for (int p = 0; p < T; ++p)
-        rb[sl][ps][p] =
-            bload16(b_src, ks < ksteps ? (m * (uint32_t)ksteps + (uint32_t)ks) * BLOCK + p * 64 + q * 16 : kOob);
+        rb[sl][ps][p] = bload16s(b_src, m * (uint32_t)ksteps * BLOCK + p * 64 + q * 16, soffb);
     }
   };
   auto store = [&](char* buf, auto slot_c) {
