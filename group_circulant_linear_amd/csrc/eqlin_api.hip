@@ -12,7 +12,6 @@
 
 namespace {
 
-constexpr int kNumCu = 256;  // MI355X compute units (8 XCDs x 32)
 thread_local int g_last_hip_error = 0;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -78,20 +77,26 @@ struct TileShape {
 // kernel): the tile epilogue, which dominates there, overlaps the next
 // tile's loads and MFMAs.
 constexpr TileShape kP4F32Tiles[] = {{112211, 64, 64, 0.745}, {112221, 64, 64, 0.70}, {111211, 32, 64, 0.59}};
-constexpr TileShape kP4F16Tiles[] = {{212421, 128, 128, 0.24}, {112211, 64, 64, 0.17}, {111221, 32, 64, 0.12}};
+// In f16 the 64 x 128 tile fills the chip better than 128 x 128 where the
+// larger tile leaves a CU one extra tile (ViT-B fc1: 41.6 against 44.6 us).
+constexpr TileShape kP4F16Tiles[] = {
+    {212421, 128, 128, 0.24}, {122211, 64, 128, 0.22}, {112211, 64, 64, 0.17}, {111221, 32, 64, 0.12}};
 // The p4 convolution in fp32: its gathered rows are 9x deeper than the linear
 // layers' at K = 3, where the 128 x 128 tile's higher reuse per LDS byte pays
 // once the pixel count leaves few tiles (28 x 28 and 14 x 14 maps, C = 512 and
 // 1024: 7-8% faster than 64 x 64).
 constexpr TileShape kConvF32Tiles[] = {{112211, 64, 64, 0.745}, {212421, 128, 128, 0.80}, {111211, 32, 64, 0.59}};
+constexpr TileShape kConvF16Tiles[] = {{212421, 128, 128, 0.24}, {112211, 64, 64, 0.17}, {111221, 32, 64, 0.12}};
 constexpr TileShape kC8F32Tiles[] = {{112211, 64, 64, 0.58}, {112221, 64, 64, 0.55}, {111221, 32, 64, 0.31}};
 constexpr TileShape kC8F16Tiles[] = {
     {1222111, 64, 128, 0.137}, {2122111, 128, 64, 0.112}, {122211, 64, 128, 0.12}, {1122111, 64, 64, 0.105}};
 
 // Forward tile choice: workgroups are spread round-robin over the CUs, so a
-// CU's work is ceil(tiles / CUs) tiles; minimise that work divided by the
-// tile's efficiency.  EQLIN_FWD_TILE overrides (any compiled tile code).
-int choose_from_table(const TileShape* tiles, int ntiles, int64_t nrows, int mg);
+// CU's work is ceil(tiles / CUs) tiles, or the whole rounds plus half a tile
+// where the launch splits its tail (eqlin::fwd_full_tiles); minimise that
+// work divided by the tile's efficiency.  EQLIN_FWD_TILE overrides (any
+// compiled tile code).
+int choose_from_table(const TileShape* tiles, int ntiles, int64_t nrows, int mg, bool f32, bool split);
 
 int choose_fwd_tile(int T, int dtype, int64_t nrows, int mg) {
   if (const char* env = getenv("EQLIN_FWD_TILE")) {
@@ -105,7 +110,7 @@ int choose_fwd_tile(int T, int dtype, int64_t nrows, int mg) {
                                    : int(sizeof(kP4F16Tiles) / sizeof(TileShape)))
                             : (f32 ? int(sizeof(kC8F32Tiles) / sizeof(TileShape))
                                    : int(sizeof(kC8F16Tiles) / sizeof(TileShape)));
-  return choose_from_table(tiles, ntiles, nrows, mg);
+  return choose_from_table(tiles, ntiles, nrows, mg, f32, eqlin::fwd_tail_split_enabled());
 }
 
 // The p4 convolution runs the p4 forward tiles (one workgroup per tile) with
@@ -117,17 +122,19 @@ int choose_conv_tile(int dtype, int64_t npix, int mg) {
     if (eqlin::ConvLaunch::tile_known(t)) return t;
   }
   return dtype == EQLIN_F32
-             ? choose_from_table(kConvF32Tiles, int(sizeof(kConvF32Tiles) / sizeof(TileShape)), npix, mg)
-             : choose_from_table(kP4F16Tiles, int(sizeof(kP4F16Tiles) / sizeof(TileShape)), npix, mg);
+             ? choose_from_table(kConvF32Tiles, int(sizeof(kConvF32Tiles) / sizeof(TileShape)), npix, mg, true, false)
+             : choose_from_table(kConvF16Tiles, int(sizeof(kConvF16Tiles) / sizeof(TileShape)), npix, mg, false, false);
 }
 
-int choose_from_table(const TileShape* tiles, int ntiles, int64_t nrows, int mg) {
+int choose_from_table(const TileShape* tiles, int ntiles, int64_t nrows, int mg, bool f32, bool split) {
   int best = tiles[0].code;
   double best_cost = 1e300;
   for (int i = 0; i < ntiles; ++i) {
     const TileShape& t = tiles[i];
     const int64_t n = cdiv(nrows, t.bm) * cdiv(mg, t.bn);
-    const double cost = double(cdiv(n, kNumCu)) * t.bm * t.bn / t.eff;
+    const int64_t full = (split && eqlin::fwd_tail_split_fits_code(t.code, f32)) ? eqlin::fwd_full_tiles(n) : n;
+    const double rounds = full == n ? double(cdiv(n, eqlin::kNumCu)) : double(full / eqlin::kNumCu) + 0.5;
+    const double cost = rounds * t.bm * t.bn / t.eff;
     if (cost < best_cost * 0.97) {  // keep the earlier (larger) tile unless clearly better
       best_cost = cost;
       best = t.code;
@@ -161,7 +168,7 @@ DwPlan plan_dw(int64_t N, int C, int D, int O, int dtype) {
   const int64_t tiles = cdiv(D / O, 64) * cdiv(C / O, 64);
   const int64_t stage = eqlin::dw_rows_per_stage(dtype);
   const int64_t row_bytes = int64_t(C > D ? C : D) * elem_bytes(dtype);
-  int64_t want = (2 * kNumCu) / tiles;
+  int64_t want = (2 * eqlin::kNumCu) / tiles;
   const int64_t max_split = cdiv(N, stage);
   if (want > max_split) want = max_split;
   if (want < 1) want = 1;

@@ -641,11 +641,12 @@ __device__ __forceinline__ void mma_chunk(f32x16 (&acc)[Grp<G>::kOrder][FM][FN],
 // the next stage's transform and LDS writes between the MFMAs, so that one
 // wave keeps its matrix core busy while it prepares the next stage.
 // Masks: 0x008 MFMA, 0x100 DS read, 0x200 DS write, 0x020 VMEM read, 0x002 VALU.
-template <typename E, int G, int FM, int FN, int PA, int PB>
+// CH: k chunks a wave multiplies per stage (2, or 1 in a tail-split half).
+template <typename E, int G, int FM, int FN, int PA, int PB, int CH = 2>
 __device__ __forceinline__ void interleave_schedule() {
   constexpr int T = Grp<G>::kOrder;
-  constexpr int kMfma = (sizeof(E) == 4 ? 4 : 1) * Grp<G>::kProducts * FM * FN * 2;
-  constexpr int kDsRead = 2 * T * (FM + FN);
+  constexpr int kMfma = (sizeof(E) == 4 ? 4 : 1) * Grp<G>::kProducts * FM * FN * CH;
+  constexpr int kDsRead = CH * T * (FM + FN);
   constexpr int kVmem = T * (PA + PB);
   constexpr int kDsWrite = T * (PA + PB);
   constexpr int kHalf = kDsRead / 2;
@@ -682,13 +683,14 @@ constexpr int fwd_lds_bytes() {
 
 // Epilogue of a forward / dX tile: inverse group DFT in registers, optional
 // group-invariant bias and GELU, one vector store per (row, group).
-template <typename E, int G, int FM, int FN, int WM, int WN>
+// HALF: a tail-split half, whose fragments all start at the half's row 0.
+template <typename E, int G, int FM, int FN, int WM, int WN, bool HALF = false>
 __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[Grp<G>::kOrder][FM][FN], int64_t row0, int col0,
                                              E* __restrict__ out, int64_t nrows, int mg,
                                              const E* __restrict__ bias, int act) {
   constexpr int T = Grp<G>::kOrder;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wr = wave / WN, wc = wave % WN;
+  const int wr = HALF ? 0 : wave / WN, wc = wave % WN;
   const int li = lane & 31, lh = lane >> 5;
   const uint32_t row_bytes = (uint32_t)(T * mg) * (uint32_t)sizeof(E);
   // The tile's rows as one buffer: rows past nrows lie beyond its range and
@@ -822,7 +824,11 @@ __device__ __forceinline__ void conv_diag(const u32x4 (&M)[4], bool centre, u32x
 // registers ahead of the stage being transformed into LDS.
 // CONV: the A rows are output pixels of a p4 group convolution whose
 // gathered rows (see ConvGeom) are read straight from the input map `in`.
-template <typename E, int G, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED, bool CONV = false>
+// HALF: lid = 2 tile + h runs rows h BM/2 .. h BM/2 + BM/2 - 1 of the tile
+// (tail split): wave row wr multiplies k chunk wr of every stage for all of
+// those rows and the two rows' sums are added through LDS.
+template <typename E, int G, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED, bool CONV = false,
+          bool HALF = false>
 __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __restrict__ in,
                                          const E* __restrict__ wp, E* __restrict__ out, int64_t nrows, int kg,
                                          int mg, int tiles_n, const E* __restrict__ bias, int act,
@@ -839,15 +845,21 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
   constexpr int RPP = NT / 4;               // tile rows covered per load pass
   constexpr int PA = (BM + RPP - 1) / RPP, PB = (BN + RPP - 1) / RPP;
   static_assert(NBUF * BUF == fwd_lds_bytes<E, T, FM, FN, WM, WN, NBUF>(), "LDS size");
+  static_assert(!HALF || (!CONV && fwd_tail_split_fits(sizeof(E) == 4, FM, FN, WM, WN, NBUF)), "tail split");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t row0 = (lid / tiles_n) * BM;
-  const int col0 = (int)(lid % tiles_n) * BN;
+  const int64_t tile = HALF ? lid >> 1 : lid;
+  const int64_t row0 = (tile / tiles_n) * BM + (HALF ? (lid & 1) * (BM / 2) : 0);
+  const int col0 = (int)(tile % tiles_n) * BN;
   const int ksteps = (kg + SG - 1) / SG;
+  if (HALF && row0 >= nrows) return;   // second half of a last tile with no rows there (uniform)
+  // this workgroup's rows end at row_end; the A range stops there, so the
+  // unused rows of a half read zeros without memory traffic
+  const int64_t row_end = HALF ? (nrows < row0 + BM / 2 ? nrows : row0 + BM / 2) : nrows;
 
   const uint32_t row_bytes = (uint32_t)kg * (uint32_t)(T * sizeof(E));
   const __amdgpu_buffer_rsrc_t a_src =
-      CONV ? make_rsrc(in, geo.in_bytes) : make_rsrc(in + row0 * T * (int64_t)kg, (uint64_t)(nrows - row0) * row_bytes);
+      CONV ? make_rsrc(in, geo.in_bytes) : make_rsrc(in + row0 * T * (int64_t)kg, (uint64_t)(row_end - row0) * row_bytes);
   const __amdgpu_buffer_rsrc_t b_src =
       make_rsrc(wp + (int64_t)col0 * ksteps * SG * T, (uint64_t)(mg - col0) * (uint64_t)ksteps * BLOCK);
 
@@ -959,9 +971,10 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
   const int li = lane & 31, lh = lane >> 5;
   // fragment rows differ from li by multiples of 32, so the swizzle of every
   // row this lane reads is that of li
-  const int a_frag = (wr * 32 * FM + li) * STRIDE;
+  const int a_frag = ((HALF ? 0 : wr * 32 * FM) + li) * STRIDE;
   const int b_frag = T * A_PLANE + (wc * 32 * FN + li) * STRIDE;
   const int c0 = swz_slot(li, lh) * 16, c1 = swz_slot(li, 2 + lh) * 16;
+  const int cw = swz_slot(li, 2 * wr + lh) * 16;   // HALF: this wave row's k chunk
 
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, PF - 1>;
@@ -973,12 +986,16 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
   // scheduler can interleave MFMAs with the transform, LDS writes and loads.
   auto step = [&](int ks, auto slot_next) {
     char* cur = lds + (NBUF == 2 ? (ks & 1) * BUF : 0);
-    mma_chunk<E, G, false, FM, FN>(acc, cur + a_frag + c0, A_PLANE, cur + b_frag + c0, B_PLANE, STRIDE);
-    mma_chunk<E, G, false, FM, FN>(acc, cur + a_frag + c1, A_PLANE, cur + b_frag + c1, B_PLANE, STRIDE);
+    if constexpr (HALF) {
+      mma_chunk<E, G, false, FM, FN>(acc, cur + a_frag + cw, A_PLANE, cur + b_frag + cw, B_PLANE, STRIDE);
+    } else {
+      mma_chunk<E, G, false, FM, FN>(acc, cur + a_frag + c0, A_PLANE, cur + b_frag + c0, B_PLANE, STRIDE);
+      mma_chunk<E, G, false, FM, FN>(acc, cur + a_frag + c1, A_PLANE, cur + b_frag + c1, B_PLANE, STRIDE);
+    }
     if constexpr (NBUF == 1) __syncthreads();   // every wave is done reading the only buffer
     store(lds + (NBUF == 2 ? ((ks + 1) & 1) * BUF : 0), slot_next);
     load(ks + 1 + PF, slot_next);
-    if constexpr (SCHED == 1 && NBUF == 2) interleave_schedule<E, G, FM, FN, PA, PB>();
+    if constexpr (SCHED == 1 && NBUF == 2 && !HALF) interleave_schedule<E, G, FM, FN, PA, PB>();
     __syncthreads();
   };
 
@@ -1000,7 +1017,44 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
     }
   }
 
-  fwd_epilogue<E, G, FM, FN, WM, WN>(acc, row0, col0, out, nrows, mg, bias, act);
+  if constexpr (HALF) {
+    // after the last stage's barrier LDS is free: wave row 1 leaves its sums
+    // there (16-byte pieces, lane-minor) and wave row 0 adds them
+    f32x4* red = reinterpret_cast<f32x4*>(lds) + wc * (T * FM * FN * 4 * 64) + lane;
+    if (wr == 1) {
+#pragma unroll
+      for (int p = 0; p < T; ++p)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              red[(((p * FM + fm) * FN + fn) * 4 + j) * 64] =
+                  f32x4{acc[p][fm][fn][4 * j], acc[p][fm][fn][4 * j + 1], acc[p][fm][fn][4 * j + 2],
+                        acc[p][fm][fn][4 * j + 3]};
+    }
+    __syncthreads();
+    if (wr == 1) return;
+#pragma unroll
+    for (int p = 0; p < T; ++p) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 v = red[(((p * FM + fm) * FN + fn) * 4 + j) * 64];
+            f32x4 s = {acc[p][fm][fn][4 * j] + v[0], acc[p][fm][fn][4 * j + 1] + v[1],
+                       acc[p][fm][fn][4 * j + 2] + v[2], acc[p][fm][fn][4 * j + 3] + v[3]};
+            asm volatile("" : "+v"(s));   // the sum is formed here, not in the epilogue
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[p][fm][fn][4 * j + e] = s[e];
+          }
+      asm volatile("" ::: "memory");   // one plane's reads in flight at a time
+    }
+  }
+  fwd_epilogue<E, G, FM, FN, WM, WN, HALF>(acc, row0, col0, out, row_end, mg, bias, act);
 }
 
 // Persistent forward: workgroup `first` runs the tiles first, first + stride,
@@ -1165,14 +1219,27 @@ constexpr int fwd_waves_per_simd() {
 template <typename E, int G, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED, int PERSIST>
 __global__ void __launch_bounds__(64 * WM * WN, (fwd_waves_per_simd<E, Grp<G>::kOrder, FM, FN>()))
 fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ out,
-           int64_t nrows, int kg, int mg, int tiles_n, const E* __restrict__ bias, int act, int64_t ntiles) {
+           int64_t nrows, int kg, int mg, int tiles_n, const E* __restrict__ bias, int act, int64_t ntiles,
+           int64_t nfull) {
   __shared__ __attribute__((aligned(16))) char lds[fwd_lds_bytes<E, Grp<G>::kOrder, FM, FN, WM, WN, NBUF>()];
   if constexpr (PERSIST) {
     fwd_stream<E, G, FM, FN, WM, WN, NBUF, PF, SCHED>(lds, xcd_logical_id(blockIdx.x, gridDim.x), gridDim.x, ntiles,
                                                       in, wp, out, nrows, kg, mg, tiles_n, bias, act);
   } else {
-    fwd_tile<E, G, FM, FN, WM, WN, NBUF, PF, SCHED>(lds, xcd_logical_id(blockIdx.x, gridDim.x), in, wp, out, nrows,
-                                                    kg, mg, tiles_n, bias, act);
+    // workgroups 0 .. nfull - 1 run whole tiles; the rest, dispatched last
+    // and so at most one per CU beyond the whole rounds, run the halves of
+    // tiles nfull .. ntiles - 1 (tail split)
+    const int64_t bid = blockIdx.x;
+    if constexpr (fwd_tail_split_fits(sizeof(E) == 4, FM, FN, WM, WN, NBUF)) {
+      if (bid >= nfull) {
+        fwd_tile<E, G, FM, FN, WM, WN, NBUF, PF, SCHED, false, true>(
+            lds, 2 * nfull + xcd_logical_id(bid - nfull, (int64_t)gridDim.x - nfull), in, wp, out, nrows, kg, mg,
+            tiles_n, bias, act);
+        return;
+      }
+    }
+    fwd_tile<E, G, FM, FN, WM, WN, NBUF, PF, SCHED>(lds, xcd_logical_id(bid, nfull), in, wp, out, nrows, kg, mg,
+                                                    tiles_n, bias, act);
   }
 }
 
@@ -1557,16 +1624,21 @@ hipError_t launch_fwd_s(const void* in, const void* wp, void* out, int64_t nrows
   const int tiles_n = (int)cdiv(mg, BN);
   const int64_t tiles = tiles_m * tiles_n;
   if (tiles <= 0) return hipSuccess;
-  int64_t grid = tiles;
+  int64_t grid = tiles, nfull = tiles;
   auto kernel = fwd_kernel<E, G, FM, FN, WM, WN, NBUF, PF, SCHED, PERSIST>;
   if constexpr (PERSIST) {
     const int64_t resident = resident_workgroups(kernel, 64 * WM * WN);
     if (resident > 0 && resident < grid) grid = resident;
+  } else if constexpr (fwd_tail_split_fits(sizeof(E) == 4, FM, FN, WM, WN, NBUF)) {
+    if (fwd_tail_split_enabled()) {
+      nfull = fwd_full_tiles(tiles);
+      grid = nfull + 2 * (tiles - nfull);
+    }
   }
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(64 * WM * WN), 0, s, static_cast<const E*>(in),
                      static_cast<const E*>(wp), static_cast<E*>(out), nrows, kg, mg, tiles_n,
-                     static_cast<const E*>(bias), act, tiles);
+                     static_cast<const E*>(bias), act, tiles, nfull);
   return hipGetLastError();
 }
 

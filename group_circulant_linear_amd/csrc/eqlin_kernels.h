@@ -2,6 +2,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 namespace eqlin {
 
@@ -16,6 +17,42 @@ namespace eqlin {
   EQLIN_TILE_BASE(C) / 100000, (EQLIN_TILE_BASE(C) / 10000) % 10, (EQLIN_TILE_BASE(C) / 1000) % 10,         \
       (EQLIN_TILE_BASE(C) / 100) % 10, (EQLIN_TILE_BASE(C) / 10) % 10, EQLIN_TILE_BASE(C) % 10
 #define EQLIN_TILE_PERSIST(C) ((C) >= 1000000 ? (C) % 10 : 0)
+
+constexpr int kNumCu = 256;  // MI355X compute units (8 XCDs x 32)
+
+// Tail split of a one-workgroup-per-tile forward launch.  Workgroups are
+// spread evenly over the CUs, so a launch of `tiles` tiles costs each CU
+// ceil(tiles / kNumCu) tiles.  When the last, partial round holds at most
+// half the CUs' worth of tiles, each of those tiles runs as two workgroups
+// of half its rows: the two wave rows of a half each multiply one of the two
+// k chunks of every stage into the same fragments and add their partial sums
+// through LDS at the end, so no CU runs more than half a tile beyond the
+// whole rounds.  fp32 tiles with two wave rows, at most two fragments per
+// wave (registers for the partial sums beside the accumulators) and LDS
+// that holds the second row's accumulators run split.  The f16 tiles do not:
+// they hold one or two workgroups per CU and their stages are bound by
+// latency rather than by the matrix cores, so a half costs about as much as
+// a whole tile (measured: no gain on the ViT-B and ViT-H layers).
+constexpr bool fwd_tail_split_fits(bool f32, int FM, int FN, int WM, int WN, int NBUF) {
+  return f32 && WM == 2 && FM * FN <= 2 && 2 * WN * FM * FN <= NBUF * (2 * FM + FN * WN);
+}
+inline bool fwd_tail_split_fits_code(int code, bool f32) {
+  const int c = EQLIN_TILE_BASE(code);
+  return !EQLIN_TILE_PERSIST(code) &&
+         fwd_tail_split_fits(f32, c / 100000, (c / 10000) % 10, (c / 1000) % 10, (c / 100) % 10, (c / 10) % 10);
+}
+// Tiles that run whole when `tiles` tiles are launched with the tail split
+// (the rest run as halves); == tiles when the split does not pay.
+inline int64_t fwd_full_tiles(int64_t tiles) {
+  const int64_t r = tiles % kNumCu;
+  return (tiles > kNumCu && 2 * r <= kNumCu) ? tiles - r : tiles;
+}
+// EQLIN_FWD_SPLIT=0 turns the tail split off (every tile whole); read at
+// every launch, as the tile override is.
+inline bool fwd_tail_split_enabled() {
+  const char* e = getenv("EQLIN_FWD_SPLIT");
+  return !(e && atoi(e) == 0);
+}
 //
 // Group codes: 4 and 8 are the cyclic groups of that order (4: the p4
 // rotation group), kP4M the dihedral group p4m of order 8.

@@ -184,6 +184,54 @@ def test_forward_order8_small_shapes_all_tiles(g, dt, tile, monkeypatch):
         assert err <= TOL[dt], (N, C, D, err)
 
 
+# Tail split (fp32 tiles): when the last round of tiles over the 256 CUs
+# fills at most half of them, each of those tiles runs as two half-height
+# workgroups whose wave rows split every stage's k range; EQLIN_FWD_SPLIT=0
+# runs every tile whole.  Shapes: one column of 300 tiles
+# whose last tile has rows in its first half only, then in both halves, and
+# three columns of 99 row tiles (the split starts inside a row of tiles).
+SPLIT_TILES = [(4, "112211"), (4, "112221"), (4, "112121"), (4, "212421"), (4, "112212"), (8, "112211"),
+               (8, "112221"), ("p4m", "112211"), ("p4m", "112221")]
+
+
+def _split_shapes(tile):
+    FM, FN, WM, WN = (int(c) for c in tile[:4])
+    BM, BN = 32 * FM * WM, 32 * FN * WN
+    return [(299 * BM + BM // 4 + 3, BN), (299 * BM + BM // 2 + 5, BN), (98 * BM + BM // 2 + 5, 3 * BN)]
+
+
+@pytest.mark.parametrize("g,tile", SPLIT_TILES)
+def test_forward_tail_split(g, tile, monkeypatch):
+    dt = "f32"
+    T = order(g)
+    monkeypatch.setenv("EQLIN_FWD_TILE", tile)
+    for (N, mg) in _split_shapes(tile):
+        C, D = T * 42, T * mg
+        say(f"tail split group={g} {dt} tile={tile} N={N} C={C} D={D}")
+        X, w, _ = make_layer_inputs(N, C, D, dt, seed=15, T=T, with_dy=False)
+        Wh = prep(w, g)
+        ref = ref_forward(X, w, g)
+        monkeypatch.setenv("EQLIN_FWD_SPLIT", "1")
+        Ys = host(eq.eqlin_forward(dev(X), Wh))
+        monkeypatch.setenv("EQLIN_FWD_SPLIT", "0")
+        Yw = host(eq.eqlin_forward(dev(X), Wh))
+        es, ew = rel_err(Ys, ref), rel_err(Yw, ref)
+        say(f"  split {es:.2e} whole {ew:.2e}")
+        assert es <= TOL[dt] and ew <= TOL[dt]
+    # bias and GELU in the halves' epilogue, and dX through the same launch
+    monkeypatch.setenv("EQLIN_FWD_SPLIT", "1")
+    N, mg = _split_shapes(tile)[1]
+    C, D = T * 42, T * mg
+    X, w, dY = make_layer_inputs(N, C, D, dt, seed=16, T=T)
+    b = np.random.default_rng(17).standard_normal(D // T).astype(X.dtype)
+    Wh = prep(w, g)
+    Y = host(eq.eqlin_forward_ex(dev(X), Wh, dev(b), "gelu"))
+    Z = ref_forward(X, w, g) + np.repeat(b.astype(np.float64), T)[None, :]
+    assert rel_err(Y, oracle.gelu_erf(Z)) <= TOL[dt]
+    dX = host(eq.eqlin_backward_dx(dev(dY), Wh))
+    assert rel_err(dX, ref_dx(dY, w, g)) <= TOL[dt]
+
+
 def _sample_rows(N, rng, k=96):
     rows = set(range(8)) | set(range(N - 8, N))
     rows |= set(rng.choice(N, size=k, replace=False).tolist())
