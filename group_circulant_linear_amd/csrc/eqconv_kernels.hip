@@ -88,10 +88,20 @@ __device__ __forceinline__ bool conv_weight_source(int g, const ConvGeom& geo, i
 template <typename E, int FM, int FN, int WM, int WN, int NBUF, int PF>
 __global__ void __launch_bounds__(64 * WM * WN, (fwd_waves_per_simd<E, 4, FM, FN>()))
 conv_fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ out, int64_t npix, int kg,
-                int mg, int tiles_n, const E* __restrict__ bias, int act, ConvGeom geo) {
+                int mg, int tiles_n, const E* __restrict__ bias, int act, ConvGeom geo, int64_t nfull) {
   __shared__ __attribute__((aligned(16))) char lds[fwd_lds_bytes<E, 4, FM, FN, WM, WN, NBUF>()];
-  fwd_tile<E, 4, FM, FN, WM, WN, NBUF, PF, 1, true>(lds, xcd_logical_id(blockIdx.x, gridDim.x), in, wp, out, npix,
-                                                    kg, mg, tiles_n, bias, act, geo);
+  // workgroups past nfull run the halves of the tail tiles (as fwd_kernel)
+  const int64_t bid = blockIdx.x;
+  if constexpr (fwd_tail_split_fits(sizeof(E) == 4, FM, FN, WM, WN, NBUF)) {
+    if (bid >= nfull) {
+      fwd_tile<E, 4, FM, FN, WM, WN, NBUF, PF, 1, true, true>(
+          lds, 2 * nfull + xcd_logical_id(bid - nfull, (int64_t)gridDim.x - nfull), in, wp, out, npix, kg, mg,
+          tiles_n, bias, act, geo);
+      return;
+    }
+  }
+  fwd_tile<E, 4, FM, FN, WM, WN, NBUF, PF, 1, true>(lds, xcd_logical_id(bid, nfull), in, wp, out, npix, kg, mg,
+                                                    tiles_n, bias, act, geo);
 }
 
 // Prepared spectra of the gathered layer, in the stage-block layout of the
@@ -200,12 +210,17 @@ hipError_t launch_conv_fwd(const void* in, const void* wp, void* out, int64_t np
   constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
   const int64_t tiles = cdiv(npix, BM) * cdiv(mg, BN);
   if (tiles <= 0) return hipSuccess;
-  if (tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
+  int64_t nfull = tiles, grid = tiles;
+  if (fwd_tail_split_fits(sizeof(E) == 4, FM, FN, WM, WN, NBUF) && fwd_tail_split_enabled()) {
+    nfull = fwd_full_tiles(tiles);
+    grid = nfull + 2 * (tiles - nfull);
+  }
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const ConvGeom g = make_geom<E>(H, W, cpix, K, npix);
   const int kg = conv_gathered_groups(cpix, K, sizeof(E) == 4 ? 0 : 1);
-  hipLaunchKernelGGL((conv_fwd_kernel<E, FM, FN, WM, WN, NBUF, PF>), dim3((unsigned)tiles), dim3(64 * WM * WN), 0, s,
+  hipLaunchKernelGGL((conv_fwd_kernel<E, FM, FN, WM, WN, NBUF, PF>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, s,
                      static_cast<const E*>(in), static_cast<const E*>(wp), static_cast<E*>(out), npix, kg, mg,
-                     (int)cdiv(mg, BN), static_cast<const E*>(bias), act, g);
+                     (int)cdiv(mg, BN), static_cast<const E*>(bias), act, g, nfull);
   return hipGetLastError();
 }
 

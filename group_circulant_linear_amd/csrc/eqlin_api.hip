@@ -113,17 +113,18 @@ int choose_fwd_tile(int T, int dtype, int64_t nrows, int mg) {
   return choose_from_table(tiles, ntiles, nrows, mg, f32, eqlin::fwd_tail_split_enabled());
 }
 
-// The p4 convolution runs the p4 forward tiles (one workgroup per tile) with
-// its own fp32 table; EQCONV_FWD_TILE overrides the choice (any tile compiled
-// for it).
+// The p4 convolution runs the p4 forward tiles (one workgroup per tile, with
+// the fp32 tail split of the linear layer) with its own tables;
+// EQCONV_FWD_TILE overrides the choice (any tile compiled for it).
 int choose_conv_tile(int dtype, int64_t npix, int mg) {
   if (const char* env = getenv("EQCONV_FWD_TILE")) {
     const int t = atoi(env);
     if (eqlin::ConvLaunch::tile_known(t)) return t;
   }
+  const bool split = eqlin::fwd_tail_split_enabled();
   return dtype == EQLIN_F32
-             ? choose_from_table(kConvF32Tiles, int(sizeof(kConvF32Tiles) / sizeof(TileShape)), npix, mg, true, false)
-             : choose_from_table(kConvF16Tiles, int(sizeof(kConvF16Tiles) / sizeof(TileShape)), npix, mg, false, false);
+             ? choose_from_table(kConvF32Tiles, int(sizeof(kConvF32Tiles) / sizeof(TileShape)), npix, mg, true, split)
+             : choose_from_table(kConvF16Tiles, int(sizeof(kConvF16Tiles) / sizeof(TileShape)), npix, mg, false, split);
 }
 
 int choose_from_table(const TileShape* tiles, int ntiles, int64_t nrows, int mg, bool f32, bool split) {

@@ -845,7 +845,7 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
   constexpr int RPP = NT / 4;               // tile rows covered per load pass
   constexpr int PA = (BM + RPP - 1) / RPP, PB = (BN + RPP - 1) / RPP;
   static_assert(NBUF * BUF == fwd_lds_bytes<E, T, FM, FN, WM, WN, NBUF>(), "LDS size");
-  static_assert(!HALF || (!CONV && fwd_tail_split_fits(sizeof(E) == 4, FM, FN, WM, WN, NBUF)), "tail split");
+  static_assert(!HALF || fwd_tail_split_fits(sizeof(E) == 4, FM, FN, WM, WN, NBUF), "tail split");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t tile = HALF ? lid >> 1 : lid;
@@ -876,7 +876,7 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
 #pragma unroll
     for (int ps = 0; ps < PA; ++ps) {
       const int64_t n = row0 + ps * RPP + rl;
-      prow[ps] = n < nrows;
+      prow[ps] = n < row_end;
       const int nn = prow[ps] ? (int)n : 0;
       const int hw = geo.H * geo.W;
       const int img = nn / hw, rem = nn - img * hw;
