@@ -167,7 +167,7 @@ __global__ void __launch_bounds__(kThreads, bwd_waves_per_simd<4>())
 conv_bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E* __restrict__ wb,
                       E* __restrict__ dx, float* __restrict__ ws, int64_t npix, int Dp, int Cp, int kgw, int kgx,
                       int64_t rows_per_split, int dw_tiles_m, int dw_tiles_n, int64_t ndw, int64_t ndw_pad,
-                      int dx_tiles_n, ConvGeom gw, ConvGeom gx) {
+                      int dx_tiles_n, ConvGeom gw, ConvGeom gx, int64_t ndx_full) {
   constexpr int kFwd = fwd_lds_bytes<E, 4, 1, 1, 2, 2, kBwdFwdBufs>();
   constexpr int kDw = dw_lds_bytes<4, kDwBufs>();
   __shared__ __attribute__((aligned(16))) char lds[kFwd > kDw ? kFwd : kDw];
@@ -177,8 +177,17 @@ conv_bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E
     if (lid < ndw)
       dw_tile<E, 4, kDwBufs, true>(lds, lid, dy, x, ws, npix, Dp, kgw, rows_per_split, dw_tiles_m, dw_tiles_n, gw);
   } else {
-    const int64_t nb = gridDim.x - ndw_pad;
-    fwd_tile<E, 4, 1, 1, 2, 2, kBwdFwdBufs, kBwdFwdPrefetch, 1, true>(lds, xcd_logical_id(b - ndw_pad, nb), dy, wb, dx,
+    // dX tiles past ndx_full run as halves (the tail split of the forward)
+    const int64_t bx = b - ndw_pad;
+    if constexpr (fwd_tail_split_fits(sizeof(E) == 4, 1, 1, 2, 2, kBwdFwdBufs)) {
+      if (bx >= ndx_full) {
+        fwd_tile<E, 4, 1, 1, 2, 2, kBwdFwdBufs, kBwdFwdPrefetch, 1, true, true>(
+            lds, 2 * ndx_full + xcd_logical_id(bx - ndx_full, (int64_t)gridDim.x - ndw_pad - ndx_full), dy, wb, dx,
+            npix, kgx, Cp, dx_tiles_n, nullptr, 0, gx);
+        return;
+      }
+    }
+    fwd_tile<E, 4, 1, 1, 2, 2, kBwdFwdBufs, kBwdFwdPrefetch, 1, true>(lds, xcd_logical_id(bx, ndx_full), dy, wb, dx,
                                                                        npix, kgx, Cp, dx_tiles_n, nullptr, 0, gx);
   }
 }
@@ -266,13 +275,18 @@ hipError_t launch_conv_bwd_fused(const void* dy, const void* x, const void* wb, 
   const int64_t ndw = (int64_t)dw_tiles_m * dw_tiles_n * nsplit;
   const int64_t ndw_pad = cdiv(ndw, 8) * 8;
   const int dx_tiles_n = (int)cdiv(Cp, 64);
-  const int64_t grid = ndw_pad + cdiv(npix, 64) * dx_tiles_n;
+  const int64_t ndx = cdiv(npix, 64) * dx_tiles_n;
+  int64_t ndx_full = ndx, grid = ndw_pad + ndx;
+  if (fwd_tail_split_fits(sizeof(E) == 4, 1, 1, 2, 2, kBwdFwdBufs) && fwd_tail_split_enabled()) {
+    ndx_full = fwd_full_tiles(ndx);
+    grid = ndw_pad + ndx_full + 2 * (ndx - ndx_full);
+  }
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (grid > 0) {
     hipLaunchKernelGGL((conv_bwd_fused_kernel<E>), dim3((unsigned)grid), dim3(kThreads), 0, s,
                        static_cast<const E*>(dy), static_cast<const E*>(x), static_cast<const E*>(wb),
                        static_cast<E*>(dx), ws, npix, Dp, Cp, kgw, kgx, rows_per_split, dw_tiles_m, dw_tiles_n, ndw,
-                       ndw_pad, dx_tiles_n, make_geom<E>(H, W, Cp, K, npix), make_geom<E>(H, W, Dp, K, npix));
+                       ndw_pad, dx_tiles_n, make_geom<E>(H, W, Cp, K, npix), make_geom<E>(H, W, Dp, K, npix), ndx_full);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

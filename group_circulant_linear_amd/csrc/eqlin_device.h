@@ -1499,7 +1499,7 @@ __global__ void __launch_bounds__(kThreads, bwd_waves_per_simd<Grp<G>::kOrder>()
 bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E* __restrict__ wb,
                  E* __restrict__ dx, float* __restrict__ ws, int64_t nrows, int dg, int cg,
                  int64_t rows_per_split, int dw_tiles_m, int dw_tiles_n, int64_t ndw, int64_t ndw_pad,
-                 int dx_tiles_n) {
+                 int dx_tiles_n, int64_t ndx_full) {
   constexpr int T = Grp<G>::kOrder;
   constexpr int kFwd = fwd_lds_bytes<E, T, 1, 1, 2, 2, kBwdFwdBufs>();
   constexpr int kDw = dw_lds_bytes<T, kDwBufs>();
@@ -1510,9 +1510,18 @@ bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E* __r
     if (lid < ndw)
       dw_tile<E, G, kDwBufs>(lds, lid, dy, x, ws, nrows, dg, cg, rows_per_split, dw_tiles_m, dw_tiles_n);
   } else {
-    const int64_t nb = gridDim.x - ndw_pad;
-    fwd_tile<E, G, 1, 1, 2, 2, kBwdFwdBufs, kBwdFwdPrefetch, SCHED>(lds, xcd_logical_id(b - ndw_pad, nb), dy, wb,
-                                                                     dx, nrows, dg, cg, dx_tiles_n, nullptr, 0);
+    // dX tiles past ndx_full run as halves (the tail split of fwd_kernel)
+    const int64_t bx = b - ndw_pad;
+    if constexpr (fwd_tail_split_fits(sizeof(E) == 4, 1, 1, 2, 2, kBwdFwdBufs)) {
+      if (bx >= ndx_full) {
+        fwd_tile<E, G, 1, 1, 2, 2, kBwdFwdBufs, kBwdFwdPrefetch, SCHED, false, true>(
+            lds, 2 * ndx_full + xcd_logical_id(bx - ndx_full, (int64_t)gridDim.x - ndw_pad - ndx_full), dy, wb, dx,
+            nrows, dg, cg, dx_tiles_n, nullptr, 0);
+        return;
+      }
+    }
+    fwd_tile<E, G, 1, 1, 2, 2, kBwdFwdBufs, kBwdFwdPrefetch, SCHED>(lds, xcd_logical_id(bx, ndx_full), dy, wb, dx,
+                                                                     nrows, dg, cg, dx_tiles_n, nullptr, 0);
   }
 }
 
@@ -1670,13 +1679,17 @@ hipError_t launch_bwd_fused_t(const void* dy, const void* x, const void* wb, voi
   const int64_t ndw_pad = cdiv(ndw, 8) * 8;
   const int dx_tiles_n = (int)cdiv(cg, 64);
   const int64_t ndx = cdiv(nrows, 64) * dx_tiles_n;
-  const int64_t grid = ndw_pad + ndx;
+  int64_t ndx_full = ndx, grid = ndw_pad + ndx;
+  if (fwd_tail_split_fits(sizeof(E) == 4, 1, 1, 2, 2, kBwdFwdBufs) && fwd_tail_split_enabled()) {
+    ndx_full = fwd_full_tiles(ndx);
+    grid = ndw_pad + ndx_full + 2 * (ndx - ndx_full);
+  }
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (grid > 0) {
     hipLaunchKernelGGL((bwd_fused_kernel<E, G, 1>), dim3((unsigned)grid), dim3(kThreads), 0, s,
                        static_cast<const E*>(dy), static_cast<const E*>(x), static_cast<const E*>(wb),
                        static_cast<E*>(dx), ws, nrows, dg, cg, rows_per_split, dw_tiles_m, dw_tiles_n, ndw, ndw_pad,
-                       dx_tiles_n);
+                       dx_tiles_n, ndx_full);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -188,8 +188,9 @@ def test_wide_filter_on_a_small_map(dt):
 @pytest.mark.parametrize("tile", ["112211", "112221", "212421"])
 def test_tail_split(tile, monkeypatch):
     # fp32: 301 row tiles over the 256 CUs, so the last 45 run as half-height
-    # workgroups; the last tile has rows in its first half only.  Forward and
-    # the separate dX launch, split and whole, against the oracle.
+    # workgroups; the last tile has rows in its first half only.  Forward, the
+    # separate dX launch and the fused backward (dX and dpsi), split and
+    # whole, against the oracle.
     BM = 128 if tile == "212421" else 64
     N, H, W = (4 if BM == 128 else 2), 97, 99
     C, D, K = 32, 4 * BM, 3
@@ -198,12 +199,16 @@ def test_tail_split(tile, monkeypatch):
     monkeypatch.setenv("EQCONV_FWD_TILE", tile)
     P = eq.eqconv_prepare_weights(dev(psi))
     ref, dref = oracle.conv_forward(X, psi), oracle.conv_dx(dY, psi, H, W)
+    pref = oracle.conv_dw(dY, X, K)
     for split in ("1", "0"):
         monkeypatch.setenv("EQLIN_FWD_SPLIT", split)
         Y = eq.eqconv_forward(dev(X), P)
         dX, _ = eq.eqconv_backward(dev(dY), None, P, need_dpsi=False)
         assert rel_err(host(Y), ref) < TOL["f32"]
         assert rel_err(host(dX), dref) < TOL["f32"]
+        dX2, dpsi = eq.eqconv_backward(dev(dY), dev(X), P)
+        assert rel_err(host(dX2), dref) < TOL["f32"]
+        assert rel_err(host(dpsi), pref) < TOL["f32"]
 
 
 def test_module_autograd_matches_oracle():
