@@ -89,7 +89,8 @@ int eqconv_prepare_weights(const void* psi, int C, int D, int K, int dtype,
  * or D' values of the storage dtype, element-aligned) is added to the four
  * rotations of output channel d'; act is EQLIN_ACT_NONE or EQLIN_ACT_GELU
  * (else EQLIN_EINVAL); both run in the register epilogue as in
- * eqlin_forward_ex.
+ * eqlin_forward_ex.  Reproducibility as eqlin_forward (per output pixel;
+ * EQLIN_FWD_SPLIT=0 keeps every pixel in the fixed summation order).
  */
 int eqconv_forward(const void* X, int64_t N, int H, int W, int C, int D, int K,
                    const void* prepared, const void* bias, int act, void* Y,

@@ -152,6 +152,14 @@ int eqlin_prepare_weights(const void* w, int C, int D, int T, int dtype,
  * products on the matrix cores (6 for T = 4, 14 for T = 8), inverse DFT in
  * registers and a single store of Y; no intermediate global-memory writes
  * ("Implementation" section).
+ * Reproducibility: for given (N, C, D, T, dtype) the result is the same on
+ * every call.  Every row normally sums its k range in one fixed order, so a
+ * row does not depend on N either, except in float32 when the last, at most
+ * half-full round of tiles runs split (the rows of those tiles add two
+ * partial sums over the two halves of every k stage): there a row can
+ * differ in the last bits from the same row computed with another N.
+ * Setting the environment variable EQLIN_FWD_SPLIT=0 keeps every row in
+ * the fixed order (and may run slower).  The same holds for dX below.
  */
 int eqlin_forward(const void* X, int64_t N, int C, int D, int T,
                   const void* W_hat, void* Y, int dtype, void* stream);

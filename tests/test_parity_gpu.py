@@ -232,6 +232,27 @@ def test_forward_tail_split(g, tile, monkeypatch):
     assert rel_err(dX, ref_dx(dY, w, g)) <= TOL[dt]
 
 
+def test_rows_and_batch_size(monkeypatch):
+    # a row's output does not depend on the other rows of the call: bit for
+    # bit with the tail split off, and for rows of whole tiles with it on;
+    # rows of split tiles (two partial sums over k) agree to the tolerance
+    monkeypatch.setenv("EQLIN_FWD_TILE", "112211")
+    N, C, D = 299 * 64 + 50, 4 * 42, 256          # 300 tiles: the last 44 run split
+    X, w, _ = make_layer_inputs(N, C, D, "f32", seed=19, with_dy=False)
+    Wh = prep(w, 4)
+    whole_rows = 256 * 64
+    for split in ("0", "1"):
+        monkeypatch.setenv("EQLIN_FWD_SPLIT", split)
+        Y = host(eq.eqlin_forward(dev(X), Wh))
+        Ya = host(eq.eqlin_forward(dev(X[:6400]), Wh))          # 100 tiles, never split
+        Yb = host(eq.eqlin_forward(dev(X[whole_rows:]), Wh))    # 44 tiles, never split
+        assert np.array_equal(Y[:6400], Ya)
+        if split == "0":
+            assert np.array_equal(Y[whole_rows:], Yb)
+        else:
+            assert rel_err(Y[whole_rows:], Yb) <= 1e-6
+
+
 def _sample_rows(N, rng, k=96):
     rows = set(range(8)) | set(range(N - 8, N))
     rows |= set(rng.choice(N, size=k, replace=False).tolist())
