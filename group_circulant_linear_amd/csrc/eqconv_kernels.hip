@@ -110,13 +110,14 @@ conv_fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restric
 // block decode over C' input channels.  Adjoint (kAdj true, the dX pass is a
 // convolution of dY): rows = C', the decode runs over D' channels, and the
 // filter is psi'[c', d', delta, v] = psi[d', c', -R^v delta, -v mod 4].
+// One launch writes both sets: blocks below nbf the forward set, the others
+// the adjoint set.
 template <typename E, bool kAdj>
-__global__ void __launch_bounds__(kThreads)
-conv_prepare_kernel(const E* __restrict__ psi, E* __restrict__ dst, int rows, int kg, int Cp, int K, ConvGeom geo) {
+__device__ __forceinline__ void conv_prepare_entry(const E* __restrict__ psi, E* __restrict__ dst, int rows, int kg,
+                                                   int Cp, int K, const ConvGeom& geo, int64_t idx) {
   constexpr int SG = Traits<E>::kStageGroups, T = 4;
   constexpr int G = Units<E, T>::kGroupsPerUnit;
   const int nks = kg / SG;
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (idx >= (int64_t)rows * nks * SG) return;
   const int s = (int)(idx % SG);
   const int64_t t = idx / SG;
@@ -145,6 +146,17 @@ conv_prepare_kernel(const E* __restrict__ psi, E* __restrict__ dst, int rows, in
   E* o = dst + ((int64_t)row * nks + ks) * T * SG + s;
 #pragma unroll
   for (int q = 0; q < T; ++q) o[q * SG] = (E)f[q];
+}
+
+template <typename E>
+__global__ void __launch_bounds__(kThreads)
+conv_prepare_kernel(const E* __restrict__ psi, E* __restrict__ wf, E* __restrict__ wb, int Dp, int Cp, int kgf,
+                    int kgb, int K, ConvGeom gf, ConvGeom gb, int64_t nbf) {
+  const int64_t b = blockIdx.x;
+  if (b < nbf)
+    conv_prepare_entry<E, false>(psi, wf, Dp, kgf, Cp, K, gf, b * kThreads + threadIdx.x);
+  else
+    conv_prepare_entry<E, true>(psi, wb, Cp, kgb, Cp, K, gb, (b - nbf) * kThreads + threadIdx.x);
 }
 
 // Split partials of the gathered layer's dw, the gather done by the loads.
@@ -239,10 +251,10 @@ hipError_t launch_conv_prepare(const void* psi, void* wf, void* wb, int Dp, int 
   const int kgf = conv_gathered_groups(Cp, K, dt), kgb = conv_gathered_groups(Dp, K, dt);
   const ConvGeom gf = make_geom<E>(1, 1, Cp, K, 0), gb = make_geom<E>(1, 1, Dp, K, 0);
   const int64_t nf = (int64_t)Dp * kgf, nb = (int64_t)Cp * kgb;
-  hipLaunchKernelGGL((conv_prepare_kernel<E, false>), dim3((unsigned)cdiv(nf, kThreads)), dim3(kThreads), 0, s,
-                     static_cast<const E*>(psi), static_cast<E*>(wf), Dp, kgf, Cp, K, gf);
-  hipLaunchKernelGGL((conv_prepare_kernel<E, true>), dim3((unsigned)cdiv(nb, kThreads)), dim3(kThreads), 0, s,
-                     static_cast<const E*>(psi), static_cast<E*>(wb), Cp, kgb, Cp, K, gb);
+  const int64_t nbf = cdiv(nf, kThreads), grid = nbf + cdiv(nb, kThreads);
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((conv_prepare_kernel<E>), dim3((unsigned)grid), dim3(kThreads), 0, s, static_cast<const E*>(psi),
+                     static_cast<E*>(wf), static_cast<E*>(wb), Dp, Cp, kgf, kgb, K, gf, gb, nbf);
   return hipGetLastError();
 }
 

@@ -1576,15 +1576,15 @@ dw_finalize_kernel(const float* __restrict__ ws, float* __restrict__ dw, int mg,
 //   transpose planes: row = c', groups = d',  adjoint spectrum of w[d'][c'][.]
 // The second set is the spectrum of the transposed weight (u -> w(u^-1): a
 // conjugate for cyclic groups, the transposed 2 x 2 block for p4m), used by
-// the dX pass.
+// the dX pass.  Both sets are written by one launch: blocks below nbf write
+// the forward set, the others the transpose set.
 template <typename E, int G, bool kTranspose>
-__global__ void __launch_bounds__(kThreads)
-prepare_kernel(const E* __restrict__ w, E* __restrict__ dst, int mg, int ng) {
+__device__ __forceinline__ void prepare_entry(const E* __restrict__ w, E* __restrict__ dst, int mg, int ng,
+                                              int64_t idx) {
   constexpr int SG = Traits<E>::kStageGroups, T = Grp<G>::kOrder;
   const int rows = kTranspose ? ng : mg;
   const int kgr = kTranspose ? mg : ng;
   const int nks = (kgr + SG - 1) / SG;
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (idx >= (int64_t)rows * nks * SG) return;
   const int s = (int)(idx % SG);
   const int64_t t = idx / SG;
@@ -1605,6 +1605,16 @@ prepare_kernel(const E* __restrict__ w, E* __restrict__ dst, int mg, int ng) {
   E* o = dst + (row * nks + ks) * T * SG + s;
 #pragma unroll
   for (int p = 0; p < T; ++p) o[p * SG] = (E)f[p];
+}
+
+template <typename E, int G>
+__global__ void __launch_bounds__(kThreads)
+prepare_kernel(const E* __restrict__ w, E* __restrict__ wf, E* __restrict__ wb, int mg, int ng, int64_t nbf) {
+  const int64_t b = blockIdx.x;
+  if (b < nbf)
+    prepare_entry<E, G, false>(w, wf, mg, ng, b * kThreads + threadIdx.x);
+  else
+    prepare_entry<E, G, true>(w, wb, mg, ng, (b - nbf) * kThreads + threadIdx.x);
 }
 
 // ============================================================ launchers
@@ -1702,10 +1712,10 @@ template <typename E, int G>
 hipError_t launch_prepare_t(const void* w, void* wf, void* wb, int mg, int ng, hipStream_t s) {
   constexpr int SG = Traits<E>::kStageGroups;
   const int64_t nf = (int64_t)mg * cdiv(ng, SG) * SG, nb = (int64_t)ng * cdiv(mg, SG) * SG;
-  hipLaunchKernelGGL((prepare_kernel<E, G, false>), dim3((unsigned)cdiv(nf, kThreads)), dim3(kThreads), 0, s,
-                     static_cast<const E*>(w), static_cast<E*>(wf), mg, ng);
-  hipLaunchKernelGGL((prepare_kernel<E, G, true>), dim3((unsigned)cdiv(nb, kThreads)), dim3(kThreads), 0, s,
-                     static_cast<const E*>(w), static_cast<E*>(wb), mg, ng);
+  const int64_t nbf = cdiv(nf, kThreads), grid = nbf + cdiv(nb, kThreads);
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((prepare_kernel<E, G>), dim3((unsigned)grid), dim3(kThreads), 0, s, static_cast<const E*>(w),
+                     static_cast<E*>(wf), static_cast<E*>(wb), mg, ng, nbf);
   return hipGetLastError();
 }
 
