@@ -1364,6 +1364,30 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
   // transform one operand's KV rows and write the (group, plane) runs
   auto put = [&](char* plane0, const u32x4 (&r)[KV][PPU], auto conj_c) {
     constexpr bool kConj = decltype(conj_c)::value;
+    if constexpr (sizeof(E) == 2 && G == 4 && KV == 4 && PPU == 1) {
+      // f16 p4: the mixed-precision DFT of group e of rows (2 j, 2 j + 1)
+      // yields each plane's values of that row pair, packed as the run needs
+#pragma unroll
+      for (int e = 0; e < GPU; ++e) {
+        u32x2 run[T];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          uint32_t q0, q2, q1r, q1i;
+          dft4_f16_pair<kConj>(r[2 * j][0][2 * e], r[2 * j][0][2 * e + 1], r[2 * j + 1][0][2 * e],
+                               r[2 * j + 1][0][2 * e + 1], q0, q2, q1r, q1i);
+          run[0][j] = q0;
+          run[1][j] = q2;
+          run[2][j] = q1r;
+          run[3][j] = q1i;
+        }
+        const int row = pc * GPU + e;
+        const int kb = rq * RUN;
+        const int off = row * STRIDE + swz_slot(row, kb >> 4) * 16 + (kb & 15);
+#pragma unroll
+        for (int p = 0; p < T; ++p) *reinterpret_cast<u32x2*>(plane0 + p * PLANE + off) = run[p];
+      }
+      return;
+    }
     float f[KV][GPU][T];
 #pragma unroll
     for (int v = 0; v < KV; ++v) {
