@@ -470,10 +470,107 @@ __device__ __forceinline__ void dft4_f16_pair(uint32_t z01, uint32_t z23, uint32
   }
 }
 
+// f16, C8: group DFT of two groups (x: group 0, y: group 1; word k holds
+// (z_2k, z_2k+1)), written as packed f16 plane values o[p] = (plane p of
+// group 0, plane p of group 1) in the plane order of Grp<8>.  As in
+// dft4_f16_pair the mixed-precision FMAs read the f16 halves directly and
+// every plane is rounded once to f16 from a float32 expression:
+//   s_u = z_u + z_u+4, a_u = z_u - z_u+4 (f32);  A = s0 + s2, B = s1 + s3,
+//   t = a1 - a3, v = a1 + a3;  F0 = A + B, F4 = A - B, Re F2 = s0 - s2,
+//   Im F2 = s3 - s1, Re F1 = a0 + c t, Im F1 = -a2 - c v, Re F3 = a0 - c t,
+//   Im F3 = a2 - c v  (c = sqrt 1/2; the imaginary planes negated when kConj).
+template <bool kConj>
+__device__ __forceinline__ void dft8_f16_pair(const u32x4& x, const u32x4& y, uint32_t (&o)[8]) {
+  float s[2][4], a[2][4];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const u32x4& z = g == 0 ? x : y;
+    asm volatile(
+        "v_fma_mix_f32 %0, %8, 1.0, %10 op_sel:[0,0,0] op_sel_hi:[1,0,1]\n\t"
+        "v_fma_mix_f32 %1, %8, 1.0, %10 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\t"
+        "v_fma_mix_f32 %2, %9, 1.0, %11 op_sel:[0,0,0] op_sel_hi:[1,0,1]\n\t"
+        "v_fma_mix_f32 %3, %9, 1.0, %11 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\t"
+        "v_fma_mix_f32 %4, %8, 1.0, -%10 op_sel:[0,0,0] op_sel_hi:[1,0,1]\n\t"
+        "v_fma_mix_f32 %5, %8, 1.0, -%10 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\t"
+        "v_fma_mix_f32 %6, %9, 1.0, -%11 op_sel:[0,0,0] op_sel_hi:[1,0,1]\n\t"
+        "v_fma_mix_f32 %7, %9, 1.0, -%11 op_sel:[1,0,1] op_sel_hi:[1,0,1]"
+        : "=&v"(s[g][0]), "=&v"(s[g][1]), "=&v"(s[g][2]), "=&v"(s[g][3]), "=&v"(a[g][0]), "=&v"(a[g][1]),
+          "=&v"(a[g][2]), "=&v"(a[g][3])
+        : "v"(z[0]), "v"(z[1]), "v"(z[2]), "v"(z[3]));
+  }
+  float A[2], B[2], t[2], v[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    A[g] = s[g][0] + s[g][2];
+    B[g] = s[g][1] + s[g][3];
+    t[g] = a[g][1] - a[g][3];
+    v[g] = a[g][1] + a[g][3];
+  }
+  const float c = Grp<8>::kC;
+  // planes 0, 1, 4, 5: the 4-point DFT of s
+  asm volatile(
+      "v_fma_mixlo_f16 %0, %3, 1.0, %5 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixhi_f16 %0, %4, 1.0, %6 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixlo_f16 %1, %3, 1.0, -%5 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixhi_f16 %1, %4, 1.0, -%6 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixlo_f16 %2, %7, 1.0, -%9 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixhi_f16 %2, %8, 1.0, -%10 op_sel_hi:[0,0,0]"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[4])
+      : "v"(A[0]), "v"(A[1]), "v"(B[0]), "v"(B[1]), "v"(s[0][0]), "v"(s[1][0]), "v"(s[0][2]), "v"(s[1][2]));
+  if constexpr (!kConj) {
+    asm volatile(
+        "v_fma_mixlo_f16 %0, %1, 1.0, -%3 op_sel_hi:[0,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %2, 1.0, -%4 op_sel_hi:[0,0,0]"
+        : "=&v"(o[5])
+        : "v"(s[0][3]), "v"(s[1][3]), "v"(s[0][1]), "v"(s[1][1]));
+  } else {
+    asm volatile(
+        "v_fma_mixlo_f16 %0, %1, 1.0, -%3 op_sel_hi:[0,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %2, 1.0, -%4 op_sel_hi:[0,0,0]"
+        : "=&v"(o[5])
+        : "v"(s[0][1]), "v"(s[1][1]), "v"(s[0][3]), "v"(s[1][3]));
+  }
+  // planes 2 and 6 (real parts of F1, F3): a0 +- c t
+  asm volatile(
+      "v_fma_mixlo_f16 %0, %2, %6, %4 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixhi_f16 %0, %3, %6, %5 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixlo_f16 %1, %2, -%6, %4 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixhi_f16 %1, %3, -%6, %5 op_sel_hi:[0,0,0]"
+      : "=&v"(o[2]), "=&v"(o[6])
+      : "v"(t[0]), "v"(t[1]), "v"(a[0][0]), "v"(a[1][0]), "v"(c));
+  // planes 3 and 7 (imaginary parts): -a2 - c v and a2 - c v, or their negatives
+  if constexpr (!kConj) {
+    asm volatile(
+        "v_fma_mixlo_f16 %0, %2, -%6, -%4 op_sel_hi:[0,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %3, -%6, -%5 op_sel_hi:[0,0,0]\n\t"
+        "v_fma_mixlo_f16 %1, %2, -%6, %4 op_sel_hi:[0,0,0]\n\t"
+        "v_fma_mixhi_f16 %1, %3, -%6, %5 op_sel_hi:[0,0,0]"
+        : "=&v"(o[3]), "=&v"(o[7])
+        : "v"(v[0]), "v"(v[1]), "v"(a[0][2]), "v"(a[1][2]), "v"(c));
+  } else {
+    asm volatile(
+        "v_fma_mixlo_f16 %0, %2, %6, %4 op_sel_hi:[0,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %3, %6, %5 op_sel_hi:[0,0,0]\n\t"
+        "v_fma_mixlo_f16 %1, %2, %6, -%4 op_sel_hi:[0,0,0]\n\t"
+        "v_fma_mixhi_f16 %1, %3, %6, -%5 op_sel_hi:[0,0,0]"
+        : "=&v"(o[3]), "=&v"(o[7])
+        : "v"(v[0]), "v"(v[1]), "v"(a[0][2]), "v"(a[1][2]), "v"(c));
+  }
+}
+
 template <typename E, int G, bool kConj>
 __device__ __forceinline__ void pieces_to_planes(const u32x4 (&pc)[Grp<G>::kOrder], u32x4 (&pl)[Grp<G>::kOrder]) {
   constexpr int V = Traits<E>::kVals, T = Grp<G>::kOrder;
-  if constexpr (sizeof(E) == 2 && G == 4) {
+  if constexpr (sizeof(E) == 2 && G == 8) {
+    // piece j is group j; groups 2k and 2k + 1 fill word k of every plane
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t o[8];
+      dft8_f16_pair<kConj>(pc[2 * k], pc[2 * k + 1], o);
+#pragma unroll
+      for (int p = 0; p < 8; ++p) pl[p][k] = o[p];
+    }
+  } else if constexpr (sizeof(E) == 2 && G == 4) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t p0, p2, p1r, p1i;
@@ -1386,6 +1483,23 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
 #pragma unroll
         for (int p = 0; p < T; ++p) *reinterpret_cast<u32x2*>(plane0 + p * PLANE + off) = run[p];
       }
+      return;
+    }
+    if constexpr (sizeof(E) == 2 && G == 8 && KV == 8 && PPU == 1 && GPU == 1) {
+      // f16 C8: rows 2 j and 2 j + 1 of the one group fill word j of every run
+      u32x4 run[T];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t o[8];
+        dft8_f16_pair<kConj>(r[2 * j][0], r[2 * j + 1][0], o);
+#pragma unroll
+        for (int p = 0; p < T; ++p) run[p][j] = o[p];
+      }
+      const int row = pc;
+      const int kb = rq * RUN;
+      const int off = row * STRIDE + swz_slot(row, kb >> 4) * 16 + (kb & 15);
+#pragma unroll
+      for (int p = 0; p < T; ++p) st16(plane0 + p * PLANE + off, run[p]);
       return;
     }
     float f[KV][GPU][T];
