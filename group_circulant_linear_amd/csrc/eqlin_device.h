@@ -395,7 +395,9 @@ __device__ __forceinline__ void store_group_buf(__amdgpu_buffer_rsrc_t dst, uint
           __builtin_bit_cast(u32x4, f32x4{y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]}), dst, off + 16u * i,
           0, kNt);
   } else {
-    // float32 first, then binary16, in every kernel (see store_group)
+    // float32 first, then binary16, in every kernel (see store_group); the
+    // p4 epilogue without activation instead rounds each output once from
+    // its mixed-precision FMA, also alike in every kernel that runs it
     float v[T];
 #pragma unroll
     for (int i = 0; i < T; ++i) {
@@ -804,6 +806,31 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[Grp<G>::kOrder]
       const uint32_t lane_off =
           mok ? (uint32_t)(wr * 32 * FM + fm * 32 + 4 * lh) * row_bytes + (uint32_t)m * (uint32_t)(T * sizeof(E))
               : kOob;
+      if constexpr (sizeof(E) == 2 && G == 4) {
+        if (act == 0) {
+          // f16 p4 without activation: a = F0 + F2 and b = F0 - F2 in float32,
+          // a / 4 + bias and b / 4 + bias, then each output is one mixed-
+          // precision FMA (+- Re F1 / 2 or +- Im F1 / 2) rounded once into
+          // its half of the packed store
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float f0 = acc[0][fm][fn][r], f2 = acc[1][fm][fn][r];
+            const float f1r = acc[2][fm][fn][r], f1i = acc[3][fm][fn][r];
+            const float qa = __builtin_fmaf(f0 + f2, 0.25f, bm), qb = __builtin_fmaf(f0 - f2, 0.25f, bm);
+            uint32_t w0, w1;
+            asm volatile(
+                "v_fma_mixlo_f16 %0, %2, 0.5, %3 op_sel_hi:[0,0,0]\n\t"
+                "v_fma_mixhi_f16 %0, %4, -0.5, %5 op_sel_hi:[0,0,0]\n\t"
+                "v_fma_mixlo_f16 %1, %2, -0.5, %3 op_sel_hi:[0,0,0]\n\t"
+                "v_fma_mixhi_f16 %1, %4, 0.5, %5 op_sel_hi:[0,0,0]"
+                : "=&v"(w0), "=&v"(w1)
+                : "v"(f1r), "v"(qa), "v"(f1i), "v"(qb));
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, dst,
+                                                  lane_off + (uint32_t)(8 * (r >> 2) + (r & 3)) * row_bytes, 0, 2);
+          }
+          continue;
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float f[T], y[T];
