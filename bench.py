@@ -384,7 +384,7 @@ def conv_bench(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "bench.py measures a single GPU; --gpus must be 1"}))
         sys.exit(2)
     if args.mlp_block:
         mlp_block(args)
