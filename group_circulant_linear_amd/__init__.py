@@ -12,7 +12,7 @@ that importing the input generator does not load the library.
 import importlib
 
 _BINDING = {
-    "eqlin_prepare_weights", "eqlin_forward", "eqlin_forward_ex", "eqlin_backward", "eqlin_backward_dx",
+    "eqlin_prepare_weights", "eqlin_forward", "eqlin_forward_ex", "eqlin_forward_plan", "eqlin_backward", "eqlin_backward_dx",
     "eqlin_backward_dw", "eqlin_prepared_weight_bytes", "eqlin_prepared_transpose_offset",
     "eqlin_backward_workspace_bytes", "load_library", "Prepared", "EqlinError",
     "eqconv_prepare_weights", "eqconv_forward", "eqconv_backward", "eqconv_prepared_weight_bytes",

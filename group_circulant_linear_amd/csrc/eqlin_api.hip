@@ -237,7 +237,7 @@ ConvWs conv_workspace(int64_t npix, int C, int D, int K, int dtype) {
 
 extern "C" {
 
-int eqlin_version(void) { return 210; }
+int eqlin_version(void) { return 211; }
 
 const char* eqlin_status_str(int status) {
   switch (status) {
@@ -276,6 +276,24 @@ int eqlin_prepare_weights(const void* w, int C, int D, int T, int dtype, void* W
   char* base = static_cast<char*>(W_hat);
   return hip_status(EQLIN_BY_T(T, prepare(dtype, w, base, base + transpose_offset(C, D, O, dtype), D / O, C / O,
                                           static_cast<hipStream_t>(stream))));
+}
+
+int eqlin_forward_plan(int64_t N, int C, int D, int T, int dtype, int* tile, int64_t* tiles, int64_t* whole) {
+  const int st = check_shape(N, C, D, T, dtype);
+  if (st != EQLIN_OK) return st;
+  const int O = eqlin::group_order(T);
+  // as eqlin_forward: an empty batch is accepted before the width checks
+  if (N > 0 && (!fwd_offsets_fit(C, O, dtype) || !out_rows_fit(D, dtype))) return EQLIN_ENOTSUP;
+  const int mg = D / O;
+  const int code = choose_fwd_tile(T, dtype, N, mg);
+  const int c = EQLIN_TILE_BASE(code);
+  const int bm = 32 * (c / 100000) * ((c / 1000) % 10), bn = 32 * ((c / 10000) % 10) * ((c / 100) % 10);
+  const int64_t n = cdiv(N, bm) * cdiv(mg, bn);
+  const bool split = eqlin::fwd_tail_split_enabled() && eqlin::fwd_tail_split_fits_code(code, dtype == EQLIN_F32);
+  if (tile) *tile = code;
+  if (tiles) *tiles = n;
+  if (whole) *whole = split ? eqlin::fwd_full_tiles(n) : n;
+  return EQLIN_OK;
 }
 
 int eqlin_forward(const void* X, int64_t N, int C, int D, int T, const void* W_hat, void* Y, int dtype,

@@ -75,6 +75,8 @@ def load_library(path: str = LIB) -> ctypes.CDLL:
         "eqlin_prepared_weight_bytes": (c_sz, [c_int, c_int, c_int, c_int]),
         "eqlin_prepared_transpose_offset": (c_sz, [c_int, c_int, c_int, c_int]),
         "eqlin_prepare_weights": (c_int, [c_vp, c_int, c_int, c_int, c_int, c_vp, c_sz, c_vp]),
+        "eqlin_forward_plan": (c_int, [c_i64, c_int, c_int, c_int, c_int, ctypes.POINTER(c_int),
+                                       ctypes.POINTER(c_i64), ctypes.POINTER(c_i64)]),
         "eqlin_forward": (c_int, [c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_int, c_vp]),
         "eqlin_forward_ex": (c_int, [c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_int, c_vp, c_int, c_vp]),
         "eqlin_backward_workspace_bytes": (c_sz, [c_i64, c_int, c_int, c_int, c_int]),
@@ -174,6 +176,15 @@ def eqlin_prepare_weights(w: torch.Tensor, out: Optional[torch.Tensor] = None, g
            lib.eqlin_prepare_weights(_ptr(w), C, D, T, dt, _ptr(out), out.numel() * out.element_size(),
                                      _stream(w)))
     return Prepared(out, C, D, w.dtype, T)
+
+
+def eqlin_forward_plan(N: int, C: int, D: int, dtype: torch.dtype, T=T_P4) -> dict:
+    """The forward launch's tile code, tile count and whole-tile count for this shape (no device work)."""
+    lib = load_library()
+    tile, tiles, whole = ctypes.c_int(0), ctypes.c_int64(0), ctypes.c_int64(0)
+    _check("eqlin_forward_plan", lib.eqlin_forward_plan(N, C, D, group_code(T), _DTYPES[dtype], ctypes.byref(tile),
+                                                         ctypes.byref(tiles), ctypes.byref(whole)))
+    return {"tile": tile.value, "tiles": tiles.value, "whole": whole.value}
 
 
 def eqlin_forward(X: torch.Tensor, W_hat: Prepared, out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -164,6 +164,21 @@ int eqlin_prepare_weights(const void* w, int C, int D, int T, int dtype,
 int eqlin_forward(const void* X, int64_t N, int C, int D, int T,
                   const void* W_hat, void* Y, int dtype, void* stream);
 
+/*
+ * Launch plan of eqlin_forward (and of eqlin_backward_dx, whose launch has
+ * the same structure with C and D exchanged) for this shape, in the
+ * environment of the call (EQLIN_FWD_TILE, EQLIN_FWD_SPLIT); enqueues
+ * nothing and needs no device.  Writes, for non-NULL pointers:
+ *   tile   the tile code, FM FN WM WN NBUF PF [P] as EQLIN_FWD_TILE takes it:
+ *          (32 FM WM) rows x (32 FN WN) output groups, WM x WN waves;
+ *   tiles  the number of tiles (0 for N == 0);
+ *   whole  how many run as one workgroup each; the other tiles - whole run
+ *          as two workgroups of half the rows (the float32 tail split).
+ * Returns EQLIN_OK, or the status eqlin_forward would return for the shape.
+ */
+int eqlin_forward_plan(int64_t N, int C, int D, int T, int dtype, int* tile, int64_t* tiles,
+                       int64_t* whole);
+
 /* Epilogue activations for eqlin_forward_ex. */
 enum { EQLIN_ACT_NONE = 0, EQLIN_ACT_GELU = 1 };
 

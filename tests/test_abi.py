@@ -213,3 +213,37 @@ def test_conv_validation(lib):
     big = (1 << 12, 128, 128, 64, 16, 3)
     wsb = lib.eqconv_backward_workspace_bytes(*big, 0)
     assert bw(FAKE, FAKE, *big, FAKE, None, FAKE, FAKE, wsb, 0, None) == ENOTSUP
+
+
+def _plan(lib, N, C, D, T, dt):
+    tile, tiles, whole = ctypes.c_int(-1), ctypes.c_int64(-1), ctypes.c_int64(-1)
+    st = lib.eqlin_forward_plan(N, C, D, T, dt, ctypes.byref(tile), ctypes.byref(tiles), ctypes.byref(whole))
+    return st, tile.value, tiles.value, whole.value
+
+
+def test_forward_plan_tiles_and_tail_split(lib, monkeypatch):
+    # the host's tile choice and float32 tail split for the benchmark shapes
+    # (no device work): tiles = ceil(N / rows) * ceil(D' / cols); the last
+    # round over the 256 CUs runs as halves when it is at most half full
+    monkeypatch.delenv("EQLIN_FWD_TILE", raising=False)
+    monkeypatch.delenv("EQLIN_FWD_SPLIT", raising=False)
+    assert _plan(lib, 12608, 768, 768, 4, 0) == (OK, 112211, 197 * 3, 512)       # ViT-B attention fp32
+    assert _plan(lib, 8224, 1280, 5120, 4, 0) == (OK, 112211, 129 * 20, 2560)    # ViT-H fc1 fp32
+    assert _plan(lib, 8224, 5120, 1280, 4, 0) == (OK, 112211, 129 * 5, 645)      # last round 133 > 128
+    assert _plan(lib, 12608, 768, 3072, 4, 1) == (OK, 122211, 197 * 6, 1182)     # f16: 64 x 128, no split
+    assert _plan(lib, 8224, 1280, 5120, 4, 1) == (OK, 212421, 65 * 10, 650)      # f16: 128 x 128
+    assert _plan(lib, 12608, 768, 768, 8, 0) == (OK, 112211, 197 * 2, 394)       # C8: last round 138
+    assert _plan(lib, 0, 768, 768, 4, 0) == (OK, 112211, 0, 0)
+    monkeypatch.setenv("EQLIN_FWD_SPLIT", "0")
+    assert _plan(lib, 12608, 768, 768, 4, 0)[3] == 591
+    monkeypatch.delenv("EQLIN_FWD_SPLIT")
+    monkeypatch.setenv("EQLIN_FWD_TILE", "111211")                                # one wave row: never split
+    assert _plan(lib, 12608, 768, 768, 4, 0) == (OK, 111211, 394 * 3, 1182)
+    monkeypatch.setenv("EQLIN_FWD_TILE", "212421")
+    assert _plan(lib, 12608, 768, 768, 4, 0) == (OK, 212421, 99 * 2, 198)
+    monkeypatch.setenv("EQLIN_FWD_TILE", "123456")                                # not compiled: ignored
+    assert _plan(lib, 12608, 768, 768, 4, 0)[1] == 112211
+    assert _plan(lib, 12608, 770, 768, 4, 0)[0] == EINVAL
+    assert _plan(lib, 16, 12, 16, 4, 1)[0] == ENOTSUP                             # odd C' with f16
+    st = lib.eqlin_forward_plan(12608, 768, 768, 4, 0, None, None, None)
+    assert st == OK
