@@ -154,22 +154,18 @@ bool use_fused_backward() {
   return fused;
 }
 
-// Row splits of the dw reduction: enough workgroups to cover the chip twice,
-// each split a whole number of pipeline stages, and small enough for 32-bit
-// offsets inside a split.
+// Row splits of the dw reduction: each split a whole number of pipeline
+// stages and small enough for 32-bit offsets inside a split.
 struct DwPlan {
   int64_t rows_per_split;
   int nsplit;
 };
 
-DwPlan plan_dw(int64_t N, int C, int D, int O, int dtype) {
+DwPlan dw_plan_for(int64_t N, int C, int D, int dtype, int64_t want) {
   DwPlan p{0, 0};
   if (N <= 0) return p;
-  // a few 64 x 64 workgroups fit one CU; use at most two per CU in total
-  const int64_t tiles = cdiv(D / O, 64) * cdiv(C / O, 64);
   const int64_t stage = eqlin::dw_rows_per_stage(dtype);
   const int64_t row_bytes = int64_t(C > D ? C : D) * elem_bytes(dtype);
-  int64_t want = (2 * eqlin::kNumCu) / tiles;
   const int64_t max_split = cdiv(N, stage);
   if (want > max_split) want = max_split;
   if (want < 1) want = 1;
@@ -178,6 +174,36 @@ DwPlan plan_dw(int64_t N, int C, int D, int O, int dtype) {
   if (p.rows_per_split > cap) p.rows_per_split = cap > stage ? cap : stage;
   p.nsplit = static_cast<int>(cdiv(N, p.rows_per_split));
   return p;
+}
+
+// The dw launch (alone): a few 64 x 64 workgroups fit one CU; use two per CU
+// in total.  The workspace holds this plan's splits, the most of the two.
+DwPlan plan_dw(int64_t N, int C, int D, int O, int dtype) {
+  const int64_t tiles = cdiv(D / O, 64) * cdiv(C / O, 64);
+  return dw_plan_for(N, C, D, dtype, (2 * eqlin::kNumCu) / tiles);
+}
+
+// The fused backward launch: its dX tiles fill the chip besides the dw
+// splits, so half as many splits (one dw workgroup per CU) pay, with less
+// partial traffic and finalize work, unless one split grows long enough to
+// set the launch's end: kept when a split's pipeline stages are at most 1.75
+// times the launch's stages per resident workgroup (dw: tiles x row stages,
+// dX: tiles x k stages; p4 fp32 three, p4 f16 two, order 8 one workgroup per
+// CU), else two per CU as plan_dw.  Measured against two per CU: ViT-B
+// attention fp32 113 -> 104 us and f16 -4%, ViT-H f16 and C8 -2% to -6%;
+// the ViT-H fp32 layers (ratio 1.9) keep two per CU, where one per CU is 1%
+// (fc1) and 9% (fc2) slower.
+DwPlan plan_dw_fused(int64_t N, int C, int D, int O, int dtype) {
+  const int64_t tiles = cdiv(D / O, 64) * cdiv(C / O, 64);
+  const DwPlan one = dw_plan_for(N, C, D, dtype, eqlin::kNumCu / tiles);
+  if (one.nsplit > 0) {
+    const int64_t split_stages = cdiv(one.rows_per_split, eqlin::dw_rows_per_stage(dtype));
+    const int64_t dw_work = tiles * cdiv(N, eqlin::dw_rows_per_stage(dtype));
+    const int64_t dx_work = cdiv(N, 64) * cdiv(C / O, 64) * cdiv(D / O, eqlin::stage_groups(dtype));
+    const int64_t per_cu = O == 4 ? (dtype == EQLIN_F32 ? 3 : 2) : 1;
+    if (4 * split_stages * per_cu * eqlin::kNumCu <= 7 * (dw_work + dx_work)) return one;
+  }
+  return plan_dw(N, C, D, O, dtype);
 }
 
 // ------------------------------------------------ p4 group convolution
@@ -377,7 +403,7 @@ int eqlin_backward(const void* dY, const void* X, int64_t N, int C, int D, int T
   }
   if (dX && dw && N > 0 && use_fused_backward()) {
     // one launch for dX and the dw partials (they share dY), then the finalize
-    const DwPlan p = plan_dw(N, C, D, O, dtype);
+    const DwPlan p = plan_dw_fused(N, C, D, O, dtype);
     const char* wb = static_cast<const char*>(W_hat) + transpose_offset(C, D, O, dtype);
     return hip_status(EQLIN_BY_T(T, bwd_fused(dtype, dY, X, wb, dX, static_cast<float*>(workspace), dw, N, D / O,
                                               C / O, p.rows_per_split, p.nsplit, static_cast<hipStream_t>(stream))));
