@@ -185,6 +185,22 @@ def test_wide_filter_on_a_small_map(dt):
     assert rel_err(host(dpsi), oracle.conv_dw(dY, X, K)) < TOL[dt]
 
 
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("K", [9, 11, 13, 15])
+def test_large_filters(dt, K):
+    # the largest filters the header allows (odd K <= 15: (K^2 - 1) / 4 orbits,
+    # up to 56), on maps narrower and shorter than the filter
+    N, H, W, C, D = 2, 9, 18, 32, 32
+    say(f"conv large filter {dt} K={K}")
+    X, psi, dY = make_conv_inputs(N, H, W, C, D, K, dt, seed=20 + K)
+    P = eq.eqconv_prepare_weights(dev(psi))
+    Y = eq.eqconv_forward(dev(X), P)
+    dX, dpsi = eq.eqconv_backward(dev(dY), dev(X), P)
+    assert rel_err(host(Y), oracle.conv_forward(X, psi)) < TOL[dt]
+    assert rel_err(host(dX), oracle.conv_dx(dY, psi, H, W)) < TOL[dt]
+    assert rel_err(host(dpsi), oracle.conv_dw(dY, X, K)) < TOL[dt]
+
+
 @pytest.mark.parametrize("tile", ["112211", "112221", "212421"])
 def test_tail_split(tile, monkeypatch):
     # fp32: 301 row tiles over the 256 CUs, so the last 45 run as half-height
