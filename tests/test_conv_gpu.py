@@ -227,23 +227,25 @@ def test_tail_split(tile, monkeypatch):
         assert rel_err(host(dpsi), pref) < TOL["f32"]
 
 
-def test_module_autograd_matches_oracle():
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_module_autograd_matches_oracle(dt):
     from group_circulant_linear_amd.module import FlashEQConv2d
-    N, H, W, C, D, K = 2, 8, 10, 16, 32, 3
-    say("conv module autograd")
+    N, H, W, C, D, K = 2, 8, 10, 32, 32, 3
+    tdt, tol = (torch.float32, TOL["f32"]) if dt == "f32" else (torch.float16, TOL["f16"])
+    say(f"conv module autograd {dt}")
     torch.manual_seed(0)
-    m = FlashEQConv2d(C, D, K, device=DEV, dtype=torch.float32)
-    X = torch.randn(N, H, W, C, device=DEV, requires_grad=True)
+    m = FlashEQConv2d(C, D, K, device=DEV, dtype=tdt)
+    X = torch.randn(N, H, W, C, device=DEV).to(tdt).requires_grad_(True)
     Y = m(X)
     dY = torch.randn_like(Y)
     Y.backward(dY)
     psi = m.psi.detach().double().cpu().numpy()
     Xn, dYn = X.detach().double().cpu().numpy(), dY.double().cpu().numpy()
-    assert rel_err(host(Y.detach()), oracle.conv_forward(Xn, psi)) < 1e-5
-    assert rel_err(host(X.grad), oracle.conv_dx(dYn, psi, H, W)) < 1e-5
-    assert rel_err(host(m.psi.grad), oracle.conv_dw(dYn, Xn, K)) < 1e-5
+    assert rel_err(host(Y.detach()), oracle.conv_forward(Xn, psi)) < tol
+    assert rel_err(host(X.grad), oracle.conv_dx(dYn, psi, H, W)) < tol
+    assert rel_err(host(m.psi.grad), oracle.conv_dw(dYn, Xn, K)) < tol
     # the cached spectra follow an in-place update of the filter
     with torch.no_grad():
         m.psi.mul_(2.0)
     Y2 = m(X.detach())
-    assert rel_err(host(Y2.detach()), 2.0 * oracle.conv_forward(Xn, psi)) < 1e-5
+    assert rel_err(host(Y2.detach()), 2.0 * oracle.conv_forward(Xn, psi)) < tol
