@@ -18,6 +18,12 @@ real products of N x D/4 x C/4, i.e. 0.75 NDC; for C8 (--group 8) fourteen of
 N x D/8 x C/8, i.e. 0.4375 NDC (in general 2NDC (2T - 2) / T^2); for p4m
 (--group p4m) twelve of N x D/8 x C/8, i.e. 0.375 NDC.
 
+The roofline object names the forward kernel's bound by the roofline model:
+HBM when its algorithmic bytes (X read once, Y written once, the weight
+spectra read once) take longer at 8 TB/s than its executed FLOPs at the
+dtype's MFMA peak, else MFMA; both fractions are reported beside it.  The
+"narrow" workload (C = D = 64 over 201728 rows) is the HBM-bound case.
+
 The p4 group convolution workloads (--workload p4conv | p4conv_tiny) time
 the convolution's prepare, forward and backward the same way and print their
 own JSON line (metric: dense-equivalent K x K convolution TFLOP/s).
@@ -500,11 +506,20 @@ def main():
     es_b = 4 if dt == "f32" else 2
     alg_bytes = sum(es_b * L.N * (L.C + L.D) + es_b * L.C * L.D / T for (L, _, _, _) in layers)
     traffic = profiled_traffic(profile_tag(wl.name, dt, args.group), "eqlin::fwd_kernel") if len(layers) == 1 else None
-    roofline = {"bound": "mfma", "kernel": "eqlin::fwd_kernel", "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+    gbs = alg_bytes / (fwd_us * 1e-6) / 1e9
+    # the bound is the roofline's: executed FLOPs at the MFMA peak against the
+    # algorithmic bytes at the HBM peak, whichever takes longer
+    hbm_bound = alg_bytes / (HBM_PEAK_GBS * 1e9) > exec_flops / (peak * 1e12)
+    roofline = {"bound": "hbm" if hbm_bound else "mfma", "kernel": "eqlin::fwd_kernel",
+                "achieved": round(gbs, 1) if hbm_bound else round(achieved, 2),
+                "peak": HBM_PEAK_GBS if hbm_bound else peak,
+                "unit": "GB/s" if hbm_bound else "TFLOP/s",
+                "frac": round(gbs / HBM_PEAK_GBS if hbm_bound else achieved / peak, 4),
                 "traffic": (round(traffic) if traffic else None),
                 "traffic_algorithmic": round(alg_bytes), "traffic_unit": "bytes per launch",
-                "flops_per_launch": exec_flops}
+                "flops_per_launch": exec_flops,
+                "mfma_tflops": round(achieved, 2), "mfma_frac": round(achieved / peak, 4),
+                "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
     per_layer = []
     for li, (L, _, _, _) in enumerate(layers):

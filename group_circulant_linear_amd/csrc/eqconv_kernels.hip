@@ -272,9 +272,7 @@ hipError_t launch_conv_dw(const void* dy, const void* x, float* ws, float* dwlin
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t fgrid = cdiv((int64_t)Dp * kg, kThreads / 4);
-  hipLaunchKernelGGL((dw_finalize_kernel<4>), dim3((unsigned)fgrid), dim3(kThreads), 0, s, ws, dwlin, Dp, kg, nsplit);
-  return hipGetLastError();
+  return launch_dw_finalize<4>(ws, dwlin, Dp, kg, nsplit, s);
 }
 
 template <typename E>
@@ -302,9 +300,7 @@ hipError_t launch_conv_bwd_fused(const void* dy, const void* x, const void* wb, 
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t fgrid = cdiv((int64_t)Dp * kgw, kThreads / 4);
-  hipLaunchKernelGGL((dw_finalize_kernel<4>), dim3((unsigned)fgrid), dim3(kThreads), 0, s, ws, dwlin, Dp, kgw, nsplit);
-  return hipGetLastError();
+  return launch_dw_finalize<4>(ws, dwlin, Dp, kgw, nsplit, s);
 }
 
 template <typename E>

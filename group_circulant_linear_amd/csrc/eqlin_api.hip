@@ -76,11 +76,21 @@ struct TileShape {
 // long-K and wide layers (up to 15 % over the best one-tile-per-workgroup
 // kernel): the tile epilogue, which dominates there, overlaps the next
 // tile's loads and MFMAs.
-constexpr TileShape kP4F32Tiles[] = {{112211, 64, 64, 0.745}, {112221, 64, 64, 0.70}, {111211, 32, 64, 0.59}};
+// The last entry of each p4 table is the 64 x 32 tile of narrow layers (32 or
+// fewer output groups), bound by HBM: its two-wave workgroups use half the
+// LDS of 64 x 64 and six fit a CU, so more loads are in flight (C = D = 64 over
+// 201728 rows: fp32 24.3 against 35.6 us, f16 persistent 14.3 against
+// 25.1 us).  Its factor is set so that it wins only where 64 x 64 would leave
+// at least a quarter of its columns empty.
+constexpr TileShape kP4F32Tiles[] = {
+    {112211, 64, 64, 0.745}, {112221, 64, 64, 0.70}, {111211, 32, 64, 0.59}, {112111, 64, 32, 0.55}};
 // In f16 the 64 x 128 tile fills the chip better than 128 x 128 where the
 // larger tile leaves a CU one extra tile (ViT-B fc1: 41.6 against 44.6 us).
-constexpr TileShape kP4F16Tiles[] = {
-    {212421, 128, 128, 0.24}, {122211, 64, 128, 0.22}, {112211, 64, 64, 0.17}, {111221, 32, 64, 0.12}};
+constexpr TileShape kP4F16Tiles[] = {{212421, 128, 128, 0.24},
+                                     {122211, 64, 128, 0.22},
+                                     {112211, 64, 64, 0.17},
+                                     {111221, 32, 64, 0.12},
+                                     {1121111, 64, 32, 0.12}};
 // The p4 convolution in fp32: its gathered rows are 9x deeper than the linear
 // layers' at K = 3, where the 128 x 128 tile's higher reuse per LDS byte pays
 // once the pixel count leaves few tiles (28 x 28 and 14 x 14 maps, C = 512 and

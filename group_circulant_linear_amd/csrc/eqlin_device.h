@@ -1332,16 +1332,19 @@ __device__ __forceinline__ void fwd_stream(char* lds, int64_t first, int64_t str
 // Two waves per SIMD (256 registers per lane) unless a wave holds 16+
 // accumulator fragments (planes x FM x FN) or, for f16 C8, the operands with
 // their negated imaginary planes would not fit besides the eight accumulators.
-template <typename E, int T, int FM, int FN>
+// The p4 tiles of one fragment per plane in a single wave column (32 output
+// groups: the narrow-layer tiles, whose time goes to HBM latency) ask for
+// three, so that more of their workgroups, and so more loads, are resident.
+template <typename E, int T, int FM, int FN, int WN = 0>
 constexpr int fwd_waves_per_simd() {
-  return (T * FM * FN >= 16 || (T == 8 && sizeof(E) == 2)) ? 1 : 2;
+  return (T * FM * FN >= 16 || (T == 8 && sizeof(E) == 2)) ? 1 : (T == 4 && FM * FN == 1 && WN == 1) ? 3 : 2;
 }
 
 // PERSIST = 0: one workgroup per tile.  PERSIST = 1: a grid of resident
 // workgroups, each running every gridDim.x-th tile (fwd_stream); ntiles is the
 // tile count.
 template <typename E, int G, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED, int PERSIST>
-__global__ void __launch_bounds__(64 * WM * WN, (fwd_waves_per_simd<E, Grp<G>::kOrder, FM, FN>()))
+__global__ void __launch_bounds__(64 * WM * WN, (fwd_waves_per_simd<E, Grp<G>::kOrder, FM, FN, WN>()))
 fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ out,
            int64_t nrows, int kg, int mg, int tiles_n, const E* __restrict__ bias, int act, int64_t ntiles,
            int64_t nfull) {
@@ -1690,44 +1693,82 @@ bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E* __r
   }
 }
 
-// Sum the split partials in split order (deterministic), inverse group DFT
-// along u, write dw[m][n][0..T-1] (float32).  Thread (plane p, entry e) of a
-// 256-thread block sums plane p of one of 256/T consecutive entries; the T
-// plane sums meet in LDS and one thread per entry applies the inverse DFT.
-// nsplit == 0 writes zeros.
+// Sum the split partials (deterministic), inverse group DFT along u, write
+// dw[m][n][0..T-1] (float32).  A 256-thread block covers EB = 256 / (T R)
+// consecutive entries: thread (chunk r, plane p, entry e) sums the splits
+// s = r, r + R, r + 2R, ... of plane p in increasing s, the R chunk sums of
+// a (plane, entry) meet in LDS and are added in chunk order, then the T plane
+// sums of an entry meet and one thread per entry applies the inverse DFT.
+// R (a power of two, T R <= 256) is set by the host from the entry and split
+// counts alone (dw_finalize_chunks), so a given call always adds in the same
+// order; R = 1 is the plain split-order sum.  nsplit == 0 writes zeros.
 template <int G>
 __global__ void __launch_bounds__(kThreads)
-dw_finalize_kernel(const float* __restrict__ ws, float* __restrict__ dw, int mg, int ng, int nsplit) {
+dw_finalize_kernel(const float* __restrict__ ws, float* __restrict__ dw, int mg, int ng, int nsplit, int R) {
   constexpr int T = Grp<G>::kOrder;
-  constexpr int EB = kThreads / T;
-  __shared__ float part[T][EB];
+  __shared__ float red[kThreads];
+  const int cols = kThreads / R;  // (plane, entry) columns of the block
+  const int EB = cols / T;
+  const int t = threadIdx.x;
+  const int col = t % cols, r = t / cols;
+  const int e = col % EB, p = col / EB;
   const int64_t plane = (int64_t)mg * ng;
-  const int e = threadIdx.x % EB, p = threadIdx.x / EB;
   const int64_t idx = (int64_t)blockIdx.x * EB + e;
   float acc = 0.f;
   if (idx < plane) {
     const float* src = ws + p * plane + idx;
     const int64_t step = T * plane;
-    int s = 0;
-    for (; s + 4 <= nsplit; s += 4) {
-      const float v0 = src[(s + 0) * step], v1 = src[(s + 1) * step];
-      const float v2 = src[(s + 2) * step], v3 = src[(s + 3) * step];
+    int s = r;
+    for (; s + 3 * R < nsplit; s += 4 * R) {
+      const float v0 = src[(int64_t)s * step], v1 = src[(int64_t)(s + R) * step];
+      const float v2 = src[(int64_t)(s + 2 * R) * step], v3 = src[(int64_t)(s + 3 * R) * step];
       acc += v0;
       acc += v1;
       acc += v2;
       acc += v3;
     }
-    for (; s < nsplit; ++s) acc += src[s * step];
+    for (; s < nsplit; s += R) acc += src[(int64_t)s * step];
   }
-  part[p][e] = acc;
+  red[t] = acc;
   __syncthreads();
-  if (p == 0 && idx < plane) {
+  if (r == 0) {  // each column reads its own chunk slots only: no race with the writes
+    float sum = red[t];
+    for (int q = 1; q < R; ++q) sum += red[q * cols + t];
+    red[t] = sum;
+  }
+  __syncthreads();
+  if (t < EB && idx < plane) {
     float f[T], y[T];
 #pragma unroll
-    for (int k = 0; k < T; ++k) f[k] = part[k][e];
+    for (int k = 0; k < T; ++k) f[k] = red[k * EB + t];
     Grp<G>::idft(f, y);
     store_group<float, T>(dw + idx * T, y);
   }
+}
+
+// Chunks per (plane, entry) of dw_finalize_kernel: doubled while the launch
+// holds fewer than two blocks per CU and every chunk keeps at least four
+// splits, so a layer with few weight entries and many row splits (narrow
+// layers over many rows) reads its partials with the whole chip rather than
+// a few CUs each walking every split.
+inline int dw_finalize_chunks(int64_t entries, int T, int nsplit) {
+  int R = 1;
+  while (2 * R * T <= kThreads && (int64_t)nsplit >= 8 * R &&
+         (entries + kThreads / (T * R) - 1) / (kThreads / (T * R)) < 2 * kNumCu)
+    R *= 2;
+  return R;
+}
+
+template <int G>
+hipError_t launch_dw_finalize(const float* ws, float* dw, int mg, int ng, int nsplit, hipStream_t s) {
+  constexpr int T = Grp<G>::kOrder;
+  const int64_t entries = (int64_t)mg * ng;
+  const int R = dw_finalize_chunks(entries, T, nsplit);
+  const int64_t grid = (entries + kThreads / (T * R) - 1) / (kThreads / (T * R));
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (grid > 0)
+    hipLaunchKernelGGL((dw_finalize_kernel<G>), dim3((unsigned)grid), dim3(kThreads), 0, s, ws, dw, mg, ng, nsplit, R);
+  return hipGetLastError();
 }
 
 // ============================================================ prepare
@@ -1840,9 +1881,7 @@ hipError_t launch_dw_t(const void* dy, const void* x, float* ws, float* dw, int6
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t fgrid = cdiv((int64_t)mg * ng, kThreads / T);
-  hipLaunchKernelGGL((dw_finalize_kernel<G>), dim3((unsigned)fgrid), dim3(kThreads), 0, s, ws, dw, mg, ng, nsplit);
-  return hipGetLastError();
+  return launch_dw_finalize<G>(ws, dw, mg, ng, nsplit, s);
 }
 
 template <typename E, int G>
@@ -1868,9 +1907,7 @@ hipError_t launch_bwd_fused_t(const void* dy, const void* x, const void* wb, voi
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t fgrid = cdiv((int64_t)dg * cg, kThreads / T);
-  hipLaunchKernelGGL((dw_finalize_kernel<G>), dim3((unsigned)fgrid), dim3(kThreads), 0, s, ws, dw, dg, cg, nsplit);
-  return hipGetLastError();
+  return launch_dw_finalize<G>(ws, dw, dg, cg, nsplit, s);
 }
 
 template <typename E, int G>

@@ -6,7 +6,10 @@ the fp64 oracle, so a parity comparison never depends on how they were drawn.
 
 Workloads stand in for the ViT-B / ViT-H layers that the Flash EQ-Linear
 summary evaluates (gist.science 2607.21271, "Network-level results"): token
-counts are batch x (patches + 1), 197 = 14*14 + 1 and 257 = 16*16 + 1.
+counts are batch x (patches + 1), 197 = 14*14 + 1 and 257 = 16*16 + 1.  The
+"narrow" workload (16 group channels over 16 ViT-B batches of tokens) is the
+small-width regime, where the layer moves far more bytes than it multiplies
+and HBM bandwidth rather than the matrix cores bounds it.
 No dataset or trained weight is involved: X ~ N(0, 1), dY ~ N(0, 1) and the
 circulant vectors w ~ N(0, 1/C), C being the layer's full input width.
 
@@ -53,6 +56,9 @@ WORKLOADS = {
     "vith_mlp": Workload(
         "vith_mlp", "ViT-H-shaped MLP pair, N=32*257=8224, fc1 1280->5120 and fc2 5120->1280",
         ("f32", "f16"), (Layer("fc1", 8224, 1280, 5120), Layer("fc2", 8224, 5120, 1280))),
+    "narrow": Workload(
+        "narrow", "narrow p4 EQ-Linear over many rows, N=16*12608=201728, C=D=64 (16 group channels in and out)",
+        ("f32", "f16"), (Layer("narrow", 201728, 64, 64),)),
     "vitb_attn_bwd": Workload(
         "vitb_attn_bwd", "backward of the ViT-B attention projection shapes (dX and dw)",
         ("f16", "f32"), (Layer("attn", 12608, 768, 768),), backward=True),

@@ -233,6 +233,9 @@ def test_forward_plan_tiles_and_tail_split(lib, monkeypatch):
     assert _plan(lib, 12608, 768, 3072, 4, 1) == (OK, 122211, 197 * 6, 1182)     # f16: 64 x 128, no split
     assert _plan(lib, 8224, 1280, 5120, 4, 1) == (OK, 212421, 65 * 10, 650)      # f16: 128 x 128
     assert _plan(lib, 12608, 768, 768, 8, 0) == (OK, 112211, 197 * 2, 394)       # C8: last round 138
+    assert _plan(lib, 201728, 64, 64, 4, 0) == (OK, 112111, 3152, 3072)         # narrow fp32: 64 x 32
+    assert _plan(lib, 201728, 64, 64, 4, 1) == (OK, 1121111, 3152, 3152)        # narrow f16: persistent 64 x 32
+    assert _plan(lib, 201728, 64, 192, 4, 0)[1] == 112211                       # 48 output groups: 64 x 64
     assert _plan(lib, 0, 768, 768, 4, 0) == (OK, 112211, 0, 0)
     monkeypatch.setenv("EQLIN_FWD_SPLIT", "0")
     assert _plan(lib, 12608, 768, 768, 4, 0)[3] == 591

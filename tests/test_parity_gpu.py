@@ -158,7 +158,7 @@ def _forward_case(dt, N, C, D, seed=0, g=4):
 
 @pytest.mark.parametrize("tile", ["auto", "112221", "111221", "112121", "222221", "212421", "112411", "212211",
                                   "122211", "112211", "112212", "112412", "111211", "2124211", "1122111", "1122211",
-                                  "1112111"])
+                                  "1112111", "112111", "1121111"])
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 def test_forward_small_shapes_all_tiles(dt, tile, monkeypatch):
     if tile != "auto":
@@ -264,7 +264,7 @@ def _sample_rows(N, rng, k=96):
                                        ("vitb_attn", "f32", 8), ("vitb_mlp", "f16", 8), ("vith_mlp", "f32", 8),
                                        ("vith_mlp", "f16", 8), ("tiny", "f32", "p4m"), ("vitb_attn", "f32", "p4m"),
                                        ("vitb_mlp", "f16", "p4m"), ("vith_mlp", "f32", "p4m"),
-                                       ("vith_mlp", "f16", "p4m")])
+                                       ("vith_mlp", "f16", "p4m"), ("narrow", "f32", 4), ("narrow", "f16", 4)])
 def test_forward_workloads(name, dt, g):
     wl = WORKLOADS[name]
     for li, L in enumerate(wl.layers):
@@ -316,6 +316,21 @@ def test_backward_workload_vitb(dt, g):
     dX, dw = eq.eqlin_backward(dev(dY), dev(X), Wh)
     e1 = rel_err(host(dX), ref_dx(dY, w, g))
     e2 = rel_err(host(dw), ref_dw(dY, X, g))
+    say(f"  dX rel err {e1:.3e}  dw rel err {e2:.3e}")
+    assert e1 <= TOL[dt] and e2 <= TOL[dt]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_backward_workload_narrow(dt):
+    """The HBM-bound narrow layer (16 group channels, 201728 rows): dw reduces
+    over every row through many split partials."""
+    L = WORKLOADS["narrow"].layers[0]
+    say(f"backward workload narrow {dt} N={L.N} C={L.C} D={L.D}")
+    X, w, dY = make_layer_inputs(L.N, L.C, L.D, dt, seed=0)
+    Wh = prep(w, 4)
+    dX, dw = eq.eqlin_backward(dev(dY), dev(X), Wh)
+    e1 = rel_err(host(dX), ref_dx(dY, w, 4))
+    e2 = rel_err(host(dw), ref_dw(dY, X, 4))
     say(f"  dX rel err {e1:.3e}  dw rel err {e2:.3e}")
     assert e1 <= TOL[dt] and e2 <= TOL[dt]
 
