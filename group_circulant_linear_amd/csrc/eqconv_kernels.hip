@@ -166,7 +166,7 @@ conv_dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float*
                        int mg, int kg, int64_t rows_per_split, int tiles_m, int tiles_n, ConvGeom geo) {
   __shared__ __attribute__((aligned(16))) char lds[dw_lds_bytes<4, kDwBufs>()];
   dw_tile<E, 4, kDwBufs, true>(lds, xcd_logical_id(blockIdx.x, gridDim.x), dy, x, ws, npix, mg, kg, rows_per_split,
-                               tiles_m, tiles_n, geo);
+                               tiles_m, tiles_n, mg, kg, geo);
 }
 
 // Backward in one launch, as the linear layer's: the first ndw_pad
@@ -187,7 +187,8 @@ conv_bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E
   if (b < ndw_pad) {
     const int64_t lid = xcd_logical_id(b, ndw_pad);
     if (lid < ndw)
-      dw_tile<E, 4, kDwBufs, true>(lds, lid, dy, x, ws, npix, Dp, kgw, rows_per_split, dw_tiles_m, dw_tiles_n, gw);
+      dw_tile<E, 4, kDwBufs, true>(lds, lid, dy, x, ws, npix, Dp, kgw, rows_per_split, dw_tiles_m, dw_tiles_n, Dp,
+                                   kgw, gw);
   } else {
     // dX tiles past ndx_full run as halves (the tail split of the forward)
     const int64_t bx = b - ndw_pad;
@@ -272,7 +273,7 @@ hipError_t launch_conv_dw(const void* dy, const void* x, float* ws, float* dwlin
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_dw_finalize<4>(ws, dwlin, Dp, kg, nsplit, s);
+  return launch_dw_finalize<4>(ws, dwlin, Dp, kg, nsplit, 1, s);
 }
 
 template <typename E>
@@ -300,7 +301,7 @@ hipError_t launch_conv_bwd_fused(const void* dy, const void* x, const void* wb, 
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_dw_finalize<4>(ws, dwlin, Dp, kgw, nsplit, s);
+  return launch_dw_finalize<4>(ws, dwlin, Dp, kgw, nsplit, 1, s);
 }
 
 template <typename E>

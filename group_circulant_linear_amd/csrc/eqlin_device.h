@@ -1393,7 +1393,7 @@ constexpr int dw_lds_bytes() {
 template <typename E, int G, int NBUF, bool CONV = false>
 __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restrict__ dy, const E* __restrict__ x,
                                         float* __restrict__ ws, int64_t nrows, int mg, int ng,
-                                        int64_t rows_per_split, int tiles_m, int tiles_n,
+                                        int64_t rows_per_split, int tiles_m, int tiles_n, int cw_m, int cw_n,
                                         const ConvGeom& geo = ConvGeom{}) {
   constexpr int T = Grp<G>::kOrder;
   using U = Units<E, T>;
@@ -1616,10 +1616,24 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
     if (nstages > 1) load(1);
     __syncthreads();
   }
+  // Row chunks (cw_m < mg, fp32): the rows of a narrow layer are read as rows of
+  // CH = mg / cw_m = ng / cw_n consecutive rows, so the tile is CH x CH blocks
+  // of cw_m x cw_n and only the diagonal blocks (block c of dY against block c
+  // of X, the same rows) belong to dw.  A wave whose 32 x 32 fragment meets no
+  // diagonal block, or lies wholly past mg or ng, loads and transforms its
+  // share of the stages but issues no MFMA: its products would be dropped.
+  const int fr = m0 + wr * 32, fc = n0 + wc * 32;
+  const bool live = fr < mg && fc < ng &&
+                    (fr / cw_m > fc / cw_n ? fr / cw_m <= (min(fc + 31, ng - 1) / cw_n)
+                                           : fc / cw_n <= (min(fr + 31, mg - 1) / cw_m));
   for (int st = 0; st < nstages; ++st) {
     char* cur = lds + (NBUF == 2 ? (st & 1) * BUF : 0);
-    mma_chunk<E, G, true, 1, 1>(acc, cur + a_frag + c0, PLANE, cur + b_frag + c0, PLANE, STRIDE);
-    mma_chunk<E, G, true, 1, 1>(acc, cur + a_frag + c1, PLANE, cur + b_frag + c1, PLANE, STRIDE);
+    // f16: the MFMAs are short and a branch around them costs more than
+    // they do (the compiler guards MFMA hazards at the block edges)
+    if (sizeof(E) == 2 || live) {
+      mma_chunk<E, G, true, 1, 1>(acc, cur + a_frag + c0, PLANE, cur + b_frag + c0, PLANE, STRIDE);
+      mma_chunk<E, G, true, 1, 1>(acc, cur + a_frag + c1, PLANE, cur + b_frag + c1, PLANE, STRIDE);
+    }
     if (st + 1 < nstages) {
       if constexpr (NBUF == 1) __syncthreads();   // every wave is done reading the only buffer
       store(lds + (NBUF == 2 ? ((st + 1) & 1) * BUF : 0));
@@ -1631,6 +1645,19 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
   const int64_t plane_elems = (int64_t)mg * ng;
   float* dst = ws + split * T * plane_elems;
   const int n = n0 + wc * 32 + li;
+  if (sizeof(E) == 4 && cw_m < mg) {
+    // row chunks (fp32 only): the diagonal blocks only
+    const int nblk = n / cw_n;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + wr * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+      if (m < mg && n < ng && m / cw_m == nblk) {
+#pragma unroll
+        for (int p = 0; p < T; ++p) dst[p * plane_elems + (int64_t)m * ng + n] = acc[p][0][0][r];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int m = m0 + wr * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
@@ -1651,10 +1678,11 @@ constexpr int bwd_waves_per_simd() {
 template <typename E, int G>
 __global__ void __launch_bounds__(kThreads, bwd_waves_per_simd<Grp<G>::kOrder>())
 dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __restrict__ ws,
-                  int64_t nrows, int mg, int ng, int64_t rows_per_split, int tiles_m, int tiles_n) {
+                  int64_t nrows, int mg, int ng, int64_t rows_per_split, int tiles_m, int tiles_n, int cw_m,
+                  int cw_n) {
   __shared__ __attribute__((aligned(16))) char lds[dw_lds_bytes<Grp<G>::kOrder, kDwBufs>()];
   dw_tile<E, G, kDwBufs>(lds, xcd_logical_id(blockIdx.x, gridDim.x), dy, x, ws, nrows, mg, ng, rows_per_split,
-                         tiles_m, tiles_n);
+                         tiles_m, tiles_n, cw_m, cw_n);
 }
 
 // Backward in one launch: the first ndw_pad workgroups are dw split partials,
@@ -1667,7 +1695,7 @@ __global__ void __launch_bounds__(kThreads, bwd_waves_per_simd<Grp<G>::kOrder>()
 bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E* __restrict__ wb,
                  E* __restrict__ dx, float* __restrict__ ws, int64_t nrows, int dg, int cg,
                  int64_t rows_per_split, int dw_tiles_m, int dw_tiles_n, int64_t ndw, int64_t ndw_pad,
-                 int dx_tiles_n, int64_t ndx_full) {
+                 int dx_tiles_n, int64_t ndx_full, int chunks) {
   constexpr int T = Grp<G>::kOrder;
   constexpr int kFwd = fwd_lds_bytes<E, T, 1, 1, 2, 2, kBwdFwdBufs>();
   constexpr int kDw = dw_lds_bytes<T, kDwBufs>();
@@ -1676,7 +1704,8 @@ bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E* __r
   if (b < ndw_pad) {
     const int64_t lid = xcd_logical_id(b, ndw_pad);
     if (lid < ndw)
-      dw_tile<E, G, kDwBufs>(lds, lid, dy, x, ws, nrows, dg, cg, rows_per_split, dw_tiles_m, dw_tiles_n);
+      dw_tile<E, G, kDwBufs>(lds, lid, dy, x, ws, (sizeof(E) == 2 || chunks == 1) ? nrows : nrows / chunks,
+                             chunks * dg, chunks * cg, rows_per_split, dw_tiles_m, dw_tiles_n, dg, cg);
   } else {
     // dX tiles past ndx_full run as halves (the tail split of fwd_kernel)
     const int64_t bx = b - ndw_pad;
@@ -1701,10 +1730,14 @@ bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E* __r
 // sums of an entry meet and one thread per entry applies the inverse DFT.
 // R (a power of two, T R <= 256) is set by the host from the entry and split
 // counts alone (dw_finalize_chunks), so a given call always adds in the same
-// order; R = 1 is the plain split-order sum.  nsplit == 0 writes zeros.
+// order; R = 1 is the plain split-order sum.  CH > 1: the partials are those
+// of the row-chunked product (CH mg x CH ng per plane, see dw_tile), and each
+// split contributes its CH diagonal blocks, added in block order.
+// nsplit == 0 writes zeros.
 template <int G>
 __global__ void __launch_bounds__(kThreads)
-dw_finalize_kernel(const float* __restrict__ ws, float* __restrict__ dw, int mg, int ng, int nsplit, int R) {
+dw_finalize_kernel(const float* __restrict__ ws, float* __restrict__ dw, int mg, int ng, int nsplit, int R,
+                   int CH) {
   constexpr int T = Grp<G>::kOrder;
   __shared__ float red[kThreads];
   const int cols = kThreads / R;  // (plane, entry) columns of the block
@@ -1716,18 +1749,27 @@ dw_finalize_kernel(const float* __restrict__ ws, float* __restrict__ dw, int mg,
   const int64_t idx = (int64_t)blockIdx.x * EB + e;
   float acc = 0.f;
   if (idx < plane) {
-    const float* src = ws + p * plane + idx;
-    const int64_t step = T * plane;
-    int s = r;
-    for (; s + 3 * R < nsplit; s += 4 * R) {
-      const float v0 = src[(int64_t)s * step], v1 = src[(int64_t)(s + R) * step];
-      const float v2 = src[(int64_t)(s + 2 * R) * step], v3 = src[(int64_t)(s + 3 * R) * step];
-      acc += v0;
-      acc += v1;
-      acc += v2;
-      acc += v3;
+    if (CH == 1) {
+      const float* src = ws + p * plane + idx;
+      const int64_t step = T * plane;
+      int s = r;
+      for (; s + 3 * R < nsplit; s += 4 * R) {
+        const float v0 = src[(int64_t)s * step], v1 = src[(int64_t)(s + R) * step];
+        const float v2 = src[(int64_t)(s + 2 * R) * step], v3 = src[(int64_t)(s + 3 * R) * step];
+        acc += v0;
+        acc += v1;
+        acc += v2;
+        acc += v3;
+      }
+      for (; s < nsplit; s += R) acc += src[(int64_t)s * step];
+    } else {
+      const int64_t ngc = (int64_t)CH * ng, cplane = (int64_t)CH * mg * ngc;
+      const int64_t m = idx / ng, n = idx - m * ng;
+      const float* src = ws + p * cplane + m * ngc + n;
+      const int64_t step = T * cplane, cstep = mg * ngc + ng;  // next split; next diagonal block
+      for (int s = r; s < nsplit; s += R)
+        for (int c = 0; c < CH; ++c) acc += src[(int64_t)s * step + c * cstep];
     }
-    for (; s < nsplit; s += R) acc += src[(int64_t)s * step];
   }
   red[t] = acc;
   __syncthreads();
@@ -1760,14 +1802,15 @@ inline int dw_finalize_chunks(int64_t entries, int T, int nsplit) {
 }
 
 template <int G>
-hipError_t launch_dw_finalize(const float* ws, float* dw, int mg, int ng, int nsplit, hipStream_t s) {
+hipError_t launch_dw_finalize(const float* ws, float* dw, int mg, int ng, int nsplit, int chunks, hipStream_t s) {
   constexpr int T = Grp<G>::kOrder;
   const int64_t entries = (int64_t)mg * ng;
   const int R = dw_finalize_chunks(entries, T, nsplit);
   const int64_t grid = (entries + kThreads / (T * R) - 1) / (kThreads / (T * R));
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (grid > 0)
-    hipLaunchKernelGGL((dw_finalize_kernel<G>), dim3((unsigned)grid), dim3(kThreads), 0, s, ws, dw, mg, ng, nsplit, R);
+    hipLaunchKernelGGL((dw_finalize_kernel<G>), dim3((unsigned)grid), dim3(kThreads), 0, s, ws, dw, mg, ng, nsplit, R,
+                       chunks);
   return hipGetLastError();
 }
 
@@ -1867,28 +1910,29 @@ hipError_t launch_fwd_s(const void* in, const void* wp, void* out, int64_t nrows
   return hipGetLastError();
 }
 
+// chunks > 1 (it divides nrows; chunks x mg and chunks x ng <= 64): the dw
+// partials of the row-chunked product, rows_per_split counting chunked rows.
 template <typename E, int G>
 hipError_t launch_dw_t(const void* dy, const void* x, float* ws, float* dw, int64_t nrows, int mg, int ng,
-                       int64_t rows_per_split, int nsplit, hipStream_t s) {
-  constexpr int T = Grp<G>::kOrder;
-  const int tiles_m = (int)cdiv(mg, 64), tiles_n = (int)cdiv(ng, 64);
+                       int64_t rows_per_split, int nsplit, int chunks, hipStream_t s) {
+  const int tiles_m = (int)cdiv(chunks * mg, 64), tiles_n = (int)cdiv(chunks * ng, 64);
   if (nsplit > 0) {
     const int64_t grid = (int64_t)tiles_m * tiles_n * nsplit;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((dw_partial_kernel<E, G>), dim3((unsigned)grid), dim3(kThreads), 0, s,
-                       static_cast<const E*>(dy), static_cast<const E*>(x), ws, nrows, mg, ng, rows_per_split,
-                       tiles_m, tiles_n);
+                       static_cast<const E*>(dy), static_cast<const E*>(x), ws, nrows / chunks, chunks * mg,
+                       chunks * ng, rows_per_split, tiles_m, tiles_n, mg, ng);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_dw_finalize<G>(ws, dw, mg, ng, nsplit, s);
+  return launch_dw_finalize<G>(ws, dw, mg, ng, nsplit, chunks, s);
 }
 
 template <typename E, int G>
 hipError_t launch_bwd_fused_t(const void* dy, const void* x, const void* wb, void* dx, float* ws, float* dw,
-                              int64_t nrows, int dg, int cg, int64_t rows_per_split, int nsplit, hipStream_t s) {
-  constexpr int T = Grp<G>::kOrder;
-  const int dw_tiles_m = (int)cdiv(dg, 64), dw_tiles_n = (int)cdiv(cg, 64);
+                              int64_t nrows, int dg, int cg, int64_t rows_per_split, int nsplit, int chunks,
+                              hipStream_t s) {
+  const int dw_tiles_m = (int)cdiv(chunks * dg, 64), dw_tiles_n = (int)cdiv(chunks * cg, 64);
   const int64_t ndw = (int64_t)dw_tiles_m * dw_tiles_n * nsplit;
   const int64_t ndw_pad = cdiv(ndw, 8) * 8;
   const int dx_tiles_n = (int)cdiv(cg, 64);
@@ -1903,11 +1947,11 @@ hipError_t launch_bwd_fused_t(const void* dy, const void* x, const void* wb, voi
     hipLaunchKernelGGL((bwd_fused_kernel<E, G, 1>), dim3((unsigned)grid), dim3(kThreads), 0, s,
                        static_cast<const E*>(dy), static_cast<const E*>(x), static_cast<const E*>(wb),
                        static_cast<E*>(dx), ws, nrows, dg, cg, rows_per_split, dw_tiles_m, dw_tiles_n, ndw, ndw_pad,
-                       dx_tiles_n, ndx_full);
+                       dx_tiles_n, ndx_full, chunks);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_dw_finalize<G>(ws, dw, dg, cg, nsplit, s);
+  return launch_dw_finalize<G>(ws, dw, dg, cg, nsplit, chunks, s);
 }
 
 template <typename E, int G>

@@ -68,13 +68,16 @@ struct Launch {
   // bias: nullable, one storage-dtype value per output group; act: 0 none, 1 GELU (erf)
   static hipError_t forward(int dtype, int tile, const void* in, const void* wp, void* out, int64_t nrows, int kg,
                             int mg, const void* bias, int act, hipStream_t s);
+  // chunks (1, or a divisor of nrows with chunks x mg, chunks x ng <= 64): rows
+  // read as rows of `chunks` consecutive rows (narrow layers), rows_per_split
+  // counting those
   static hipError_t dw(int dtype, const void* dy, const void* x, float* ws, float* dw, int64_t nrows, int mg, int ng,
-                       int64_t rows_per_split, int nsplit, hipStream_t s);
+                       int64_t rows_per_split, int nsplit, int chunks, hipStream_t s);
   // dX (forward structure on the transpose spectra wb, 64 x 64 tiles) and the
   // dw split partials in one launch, then the dw finalize.  nrows > 0.
   static hipError_t bwd_fused(int dtype, const void* dy, const void* x, const void* wb, void* dx, float* ws,
                               float* dw, int64_t nrows, int dg, int cg, int64_t rows_per_split, int nsplit,
-                              hipStream_t s);
+                              int chunks, hipStream_t s);
   static hipError_t prepare(int dtype, const void* w, void* wf, void* wb, int mg, int ng, hipStream_t s);
 };
 
@@ -83,9 +86,9 @@ struct Launch {
   template <> hipError_t Launch<T>::forward(int, int, const void*, const void*, void*, int64_t, int, int,          \
                                             const void*, int, hipStream_t);                                        \
   template <> hipError_t Launch<T>::dw(int, const void*, const void*, float*, float*, int64_t, int, int, int64_t,   \
-                                       int, hipStream_t);                                                          \
+                                       int, int, hipStream_t);                                                     \
   template <> hipError_t Launch<T>::bwd_fused(int, const void*, const void*, const void*, void*, float*, float*,   \
-                                              int64_t, int, int, int64_t, int, hipStream_t);                       \
+                                              int64_t, int, int, int64_t, int, int, hipStream_t);                  \
   template <> hipError_t Launch<T>::prepare(int, const void*, void*, void*, int, int, hipStream_t);
 EQLIN_DECLARE_LAUNCH(4)
 EQLIN_DECLARE_LAUNCH(8)

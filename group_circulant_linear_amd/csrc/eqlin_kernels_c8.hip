@@ -39,18 +39,19 @@ hipError_t Launch<8>::forward(int dtype, int tile, const void* in, const void* w
 
 template <>
 hipError_t Launch<8>::dw(int dtype, const void* dy, const void* x, float* ws, float* dw, int64_t nrows, int mg,
-                         int ng, int64_t rows_per_split, int nsplit, hipStream_t s) {
-  return dtype == 0 ? launch_dw_t<float, 8>(dy, x, ws, dw, nrows, mg, ng, rows_per_split, nsplit, s)
-                    : launch_dw_t<_Float16, 8>(dy, x, ws, dw, nrows, mg, ng, rows_per_split, nsplit, s);
+                         int ng, int64_t rows_per_split, int nsplit, int chunks, hipStream_t s) {
+  return dtype == 0 ? launch_dw_t<float, 8>(dy, x, ws, dw, nrows, mg, ng, rows_per_split, nsplit, chunks, s)
+                    : launch_dw_t<_Float16, 8>(dy, x, ws, dw, nrows, mg, ng, rows_per_split, nsplit, chunks, s);
 }
 
 template <>
 hipError_t Launch<8>::bwd_fused(int dtype, const void* dy, const void* x, const void* wb, void* dx, float* ws,
                                 float* dw, int64_t nrows, int dg, int cg, int64_t rows_per_split, int nsplit,
-                                hipStream_t s) {
-  return dtype == 0
-             ? launch_bwd_fused_t<float, 8>(dy, x, wb, dx, ws, dw, nrows, dg, cg, rows_per_split, nsplit, s)
-             : launch_bwd_fused_t<_Float16, 8>(dy, x, wb, dx, ws, dw, nrows, dg, cg, rows_per_split, nsplit, s);
+                                int chunks, hipStream_t s) {
+  return dtype == 0 ? launch_bwd_fused_t<float, 8>(dy, x, wb, dx, ws, dw, nrows, dg, cg, rows_per_split, nsplit,
+                                                     chunks, s)
+                    : launch_bwd_fused_t<_Float16, 8>(dy, x, wb, dx, ws, dw, nrows, dg, cg, rows_per_split,
+                                                        nsplit, chunks, s);
 }
 
 template <>

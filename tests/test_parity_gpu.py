@@ -283,9 +283,13 @@ def test_forward_workloads(name, dt, g):
 
 # ---------------------------------------------------------------- backward
 
+# (64, 32, 32): rows read in chunks of 4 by the dw tile; (1002, 64, 32) and
+# (2000, 112, 128): chunks of 2 (N = 2 mod 4; 32 group channels)
 BWD_SHAPES = {
-    "f32": [(64, 32, 32), (1, 4, 4), (77, 12, 20), (1000, 160, 96), (3001, 4 * 70, 4 * 130)],
-    "f16": [(64, 32, 32), (1, 8, 8), (77, 8 * 3, 8 * 5), (1000, 8 * 20, 8 * 12), (3001, 4 * 70, 4 * 130)],
+    "f32": [(64, 32, 32), (1, 4, 4), (77, 12, 20), (1000, 160, 96), (3001, 4 * 70, 4 * 130), (1002, 64, 32),
+            (2000, 112, 128)],
+    "f16": [(64, 32, 32), (1, 8, 8), (77, 8 * 3, 8 * 5), (1000, 8 * 20, 8 * 12), (3001, 4 * 70, 4 * 130),
+            (1002, 64, 32), (2000, 112, 128)],
 }
 
 
