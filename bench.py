@@ -583,6 +583,28 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
+    if hbm_bound and not args.no_dense:
+        # practical streaming ceiling beside the HBM peak: a device copy moving
+        # the forward's algorithmic bytes (half read, half written), rotating
+        # over buffer sets as the layer's launches do
+        half = int(alg_bytes) // 2 // 4
+        cps = [(torch.empty(half, dtype=torch.float32, device=dev).fill_(1.0),
+                torch.empty(half, dtype=torch.float32, device=dev)) for _ in range(nsets)]
+        for (a, b) in cps:
+            b.copy_(a)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(10, K)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(reps):
+            cps[i % nsets][1].copy_(cps[i % nsets][0])
+        e1.record()
+        torch.cuda.synchronize()
+        cp_us = e0.elapsed_time(e1) * 1e3 / reps
+        roofline["copy_gbs"] = round(2 * half * 4 / (cp_us * 1e-6) / 1e9, 1)
+        roofline["copy_us"] = round(cp_us, 2)
+        del cps
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(layers)

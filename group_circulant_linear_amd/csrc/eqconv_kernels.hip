@@ -273,7 +273,7 @@ hipError_t launch_conv_dw(const void* dy, const void* x, float* ws, float* dwlin
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_dw_finalize<4>(ws, dwlin, Dp, kg, nsplit, 1, s);
+  return launch_dw_finalize<4>(ws, dwlin, Dp, kg, nsplit, s);
 }
 
 template <typename E>
@@ -301,7 +301,7 @@ hipError_t launch_conv_bwd_fused(const void* dy, const void* x, const void* wb, 
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_dw_finalize<4>(ws, dwlin, Dp, kgw, nsplit, 1, s);
+  return launch_dw_finalize<4>(ws, dwlin, Dp, kgw, nsplit, s);
 }
 
 template <typename E>

@@ -177,10 +177,10 @@ struct DwPlan {
 // group-channel counts are at most 16 (32), the rows are read as rows of 4
 // (2) consecutive rows, so that the 64 x 64 dw tile holds 4 (2) row blocks
 // side by side: every lane of its loads reads live data, and only its
-// diagonal blocks are multiplied and summed (dw_tile, dw_finalize_kernel).
-// chunks divides N.  Measured (dw alone, 201728 rows): C = D = 64 fp32 96.7
-// -> 52 us, C = D = 128 fp32 105 -> 75.5 us, C8 C = D = 128 over 100000 rows
-// 132 -> 87 us.  f16 keeps whole rows: its MFMAs are cheap and its stage
+// diagonal blocks are multiplied and summed (dw_tile).
+// chunks divides N.  Measured (dw alone, 201728 rows): C = D = 64 fp32 96.5
+// -> 38.2 us, C = D = 128 fp32 105 -> 68 us, C8 C = D = 128 over 100000 rows
+// 132 -> 62 us.  f16 keeps whole rows: its MFMAs are cheap and its stage
 // loop is bound by latency, and chunked it ran slower (C = D = 64 28.6 ->
 // 33.0 us, C = D = 128 37.5 -> 44.6 us).
 int dw_chunks(int64_t N, int mg, int ng, int dtype) {
@@ -382,8 +382,8 @@ size_t eqlin_backward_workspace_bytes(int64_t N, int C, int D, int T, int dtype)
   if (check_shape(N, C, D, T, dtype) != EQLIN_OK) return 0;
   const int O = eqlin::group_order(T);
   const DwPlan p = plan_dw(N, C, D, O, dtype, true);
-  return static_cast<size_t>(p.nsplit) * static_cast<size_t>(O) * static_cast<size_t>(p.chunks * C / O) *
-         static_cast<size_t>(p.chunks * D / O) * sizeof(float);
+  return static_cast<size_t>(p.nsplit) * static_cast<size_t>(O) * static_cast<size_t>(C / O) *
+         static_cast<size_t>(D / O) * sizeof(float);
 }
 
 int eqlin_backward_dx(const void* dY, int64_t N, int C, int D, int T, const void* W_hat, void* dX, int dtype,

@@ -1619,18 +1619,23 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
   // Row chunks (cw_m < mg, fp32): the rows of a narrow layer are read as rows of
   // CH = mg / cw_m = ng / cw_n consecutive rows, so the tile is CH x CH blocks
   // of cw_m x cw_n and only the diagonal blocks (block c of dY against block c
-  // of X, the same rows) belong to dw.  A wave whose 32 x 32 fragment meets no
-  // diagonal block, or lies wholly past mg or ng, loads and transforms its
-  // share of the stages but issues no MFMA: its products would be dropped.
+  // of X, the same rows) belong to dw.  A p4 fp32 wave whose 32 x 32 fragment
+  // meets no diagonal block, or lies wholly past mg or ng, loads and
+  // transforms its share of the stages but issues no MFMA: its products
+  // would be dropped.
   const int fr = m0 + wr * 32, fc = n0 + wc * 32;
   const bool live = fr < mg && fc < ng &&
                     (fr / cw_m > fc / cw_n ? fr / cw_m <= (min(fc + 31, ng - 1) / cw_n)
                                            : fc / cw_n <= (min(fr + 31, mg - 1) / cw_m));
+  // Only the p4 fp32 tiles skip: in f16 the MFMAs are short, and for the
+  // order-8 groups, whose eight planes fill the registers, a branch around
+  // them inside the loop costs more than it saves (the compiler guards MFMA
+  // hazards at block edges; measured: C8 ViT-B fp32 dw 86.6 -> 94.4 us),
+  // while a second copy of the loop without them costs occupancy.
+  const bool mma = !(sizeof(E) == 4 && T == 4) || live;
   for (int st = 0; st < nstages; ++st) {
     char* cur = lds + (NBUF == 2 ? (st & 1) * BUF : 0);
-    // f16: the MFMAs are short and a branch around them costs more than
-    // they do (the compiler guards MFMA hazards at the block edges)
-    if (sizeof(E) == 2 || live) {
+    if (mma) {
       mma_chunk<E, G, true, 1, 1>(acc, cur + a_frag + c0, PLANE, cur + b_frag + c0, PLANE, STRIDE);
       mma_chunk<E, G, true, 1, 1>(acc, cur + a_frag + c1, PLANE, cur + b_frag + c1, PLANE, STRIDE);
     }
@@ -1642,22 +1647,35 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
     __syncthreads();
   }
 
-  const int64_t plane_elems = (int64_t)mg * ng;
-  float* dst = ws + split * T * plane_elems;
   const int n = n0 + wc * 32 + li;
   if (sizeof(E) == 4 && cw_m < mg) {
-    // row chunks (fp32 only): the diagonal blocks only
+    // row chunks (fp32): the CH diagonal blocks meet in LDS (free after the
+    // stage loop's last barrier), are added in block order and written as
+    // one cw_m x cw_n partial per plane
+    const int CH = mg / cw_m, cell = cw_m * cw_n;
+    float* red = reinterpret_cast<float*>(lds);  // [T][CH][cw_m][cw_n]: T x 64 x 64 floats at most
     const int nblk = n / cw_n;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m = m0 + wr * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
       if (m < mg && n < ng && m / cw_m == nblk) {
+        const int o = nblk * cell + (m - nblk * cw_m) * cw_n + (n - nblk * cw_n);
 #pragma unroll
-        for (int p = 0; p < T; ++p) dst[p * plane_elems + (int64_t)m * ng + n] = acc[p][0][0][r];
+        for (int p = 0; p < T; ++p) red[p * CH * cell + o] = acc[p][0][0][r];
       }
+    }
+    __syncthreads();
+    float* dstc = ws + split * T * (int64_t)cell;
+    for (int i = tid; i < T * cell; i += kThreads) {
+      const int p = i / cell, e = i - p * cell;
+      float sum = red[p * CH * cell + e];
+      for (int c = 1; c < CH; ++c) sum += red[(p * CH + c) * cell + e];
+      dstc[i] = sum;
     }
     return;
   }
+  const int64_t plane_elems = (int64_t)mg * ng;
+  float* dst = ws + split * T * plane_elems;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int m = m0 + wr * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
@@ -1730,14 +1748,10 @@ bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E* __r
 // sums of an entry meet and one thread per entry applies the inverse DFT.
 // R (a power of two, T R <= 256) is set by the host from the entry and split
 // counts alone (dw_finalize_chunks), so a given call always adds in the same
-// order; R = 1 is the plain split-order sum.  CH > 1: the partials are those
-// of the row-chunked product (CH mg x CH ng per plane, see dw_tile), and each
-// split contributes its CH diagonal blocks, added in block order.
-// nsplit == 0 writes zeros.
+// order; R = 1 is the plain split-order sum.  nsplit == 0 writes zeros.
 template <int G>
 __global__ void __launch_bounds__(kThreads)
-dw_finalize_kernel(const float* __restrict__ ws, float* __restrict__ dw, int mg, int ng, int nsplit, int R,
-                   int CH) {
+dw_finalize_kernel(const float* __restrict__ ws, float* __restrict__ dw, int mg, int ng, int nsplit, int R) {
   constexpr int T = Grp<G>::kOrder;
   __shared__ float red[kThreads];
   const int cols = kThreads / R;  // (plane, entry) columns of the block
@@ -1749,27 +1763,18 @@ dw_finalize_kernel(const float* __restrict__ ws, float* __restrict__ dw, int mg,
   const int64_t idx = (int64_t)blockIdx.x * EB + e;
   float acc = 0.f;
   if (idx < plane) {
-    if (CH == 1) {
-      const float* src = ws + p * plane + idx;
-      const int64_t step = T * plane;
-      int s = r;
-      for (; s + 3 * R < nsplit; s += 4 * R) {
-        const float v0 = src[(int64_t)s * step], v1 = src[(int64_t)(s + R) * step];
-        const float v2 = src[(int64_t)(s + 2 * R) * step], v3 = src[(int64_t)(s + 3 * R) * step];
-        acc += v0;
-        acc += v1;
-        acc += v2;
-        acc += v3;
-      }
-      for (; s < nsplit; s += R) acc += src[(int64_t)s * step];
-    } else {
-      const int64_t ngc = (int64_t)CH * ng, cplane = (int64_t)CH * mg * ngc;
-      const int64_t m = idx / ng, n = idx - m * ng;
-      const float* src = ws + p * cplane + m * ngc + n;
-      const int64_t step = T * cplane, cstep = mg * ngc + ng;  // next split; next diagonal block
-      for (int s = r; s < nsplit; s += R)
-        for (int c = 0; c < CH; ++c) acc += src[(int64_t)s * step + c * cstep];
+    const float* src = ws + p * plane + idx;
+    const int64_t step = T * plane;
+    int s = r;
+    for (; s + 3 * R < nsplit; s += 4 * R) {
+      const float v0 = src[(int64_t)s * step], v1 = src[(int64_t)(s + R) * step];
+      const float v2 = src[(int64_t)(s + 2 * R) * step], v3 = src[(int64_t)(s + 3 * R) * step];
+      acc += v0;
+      acc += v1;
+      acc += v2;
+      acc += v3;
     }
+    for (; s < nsplit; s += R) acc += src[(int64_t)s * step];
   }
   red[t] = acc;
   __syncthreads();
@@ -1802,15 +1807,14 @@ inline int dw_finalize_chunks(int64_t entries, int T, int nsplit) {
 }
 
 template <int G>
-hipError_t launch_dw_finalize(const float* ws, float* dw, int mg, int ng, int nsplit, int chunks, hipStream_t s) {
+hipError_t launch_dw_finalize(const float* ws, float* dw, int mg, int ng, int nsplit, hipStream_t s) {
   constexpr int T = Grp<G>::kOrder;
   const int64_t entries = (int64_t)mg * ng;
   const int R = dw_finalize_chunks(entries, T, nsplit);
   const int64_t grid = (entries + kThreads / (T * R) - 1) / (kThreads / (T * R));
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (grid > 0)
-    hipLaunchKernelGGL((dw_finalize_kernel<G>), dim3((unsigned)grid), dim3(kThreads), 0, s, ws, dw, mg, ng, nsplit, R,
-                       chunks);
+    hipLaunchKernelGGL((dw_finalize_kernel<G>), dim3((unsigned)grid), dim3(kThreads), 0, s, ws, dw, mg, ng, nsplit, R);
   return hipGetLastError();
 }
 
@@ -1925,7 +1929,7 @@ hipError_t launch_dw_t(const void* dy, const void* x, float* ws, float* dw, int6
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_dw_finalize<G>(ws, dw, mg, ng, nsplit, chunks, s);
+  return launch_dw_finalize<G>(ws, dw, mg, ng, nsplit, s);
 }
 
 template <typename E, int G>
@@ -1951,7 +1955,7 @@ hipError_t launch_bwd_fused_t(const void* dy, const void* x, const void* wb, voi
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_dw_finalize<G>(ws, dw, dg, cg, nsplit, chunks, s);
+  return launch_dw_finalize<G>(ws, dw, dg, cg, nsplit, s);
 }
 
 template <typename E, int G>

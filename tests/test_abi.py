@@ -46,12 +46,11 @@ def test_size_queries(lib):
     assert lib.eqlin_backward_workspace_bytes(0, 768, 768, 4, 0) == 0
     ws = lib.eqlin_backward_workspace_bytes(12608, 768, 768, 4, 0)
     assert ws > 0 and ws % (4 * 192 * 192 * 4) == 0
-    # narrow layers: the dw partials are those of rows read in chunks of 4
-    # (16 group channels) or 2 (32 group channels, or N = 2 mod 4): 64 x 64 per plane
-    assert lib.eqlin_backward_workspace_bytes(201728, 64, 64, 4, 0) % (4 * 64 * 64 * 4) == 0
-    assert lib.eqlin_backward_workspace_bytes(201728, 128, 128, 4, 0) % (4 * 64 * 64 * 4) == 0
-    assert lib.eqlin_backward_workspace_bytes(1002, 64, 32, 4, 0) % (4 * 32 * 16 * 4) == 0
-    assert lib.eqlin_backward_workspace_bytes(1001, 64, 32, 4, 0) % (4 * 16 * 8 * 4) == 0
+    # narrow fp32 layers read rows in chunks of 4 (here 50432 chunked rows, 112
+    # per split: 451 splits, two per CU), each split still one D' x C' partial per plane
+    assert lib.eqlin_backward_workspace_bytes(201728, 64, 64, 4, 0) == 451 * 4 * 16 * 16 * 4
+    assert lib.eqlin_backward_workspace_bytes(201728, 64, 64, 4, 1) == 485 * 4 * 16 * 16 * 4   # f16: whole rows
+    assert lib.eqlin_backward_workspace_bytes(1002, 64, 32, 4, 0) % (4 * 8 * 16 * 4) == 0
 
 
 def test_size_queries_c8(lib):
