@@ -96,12 +96,12 @@ conv_fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restric
     if (bid >= nfull) {
       fwd_tile<E, 4, FM, FN, WM, WN, NBUF, PF, 1, true, true>(
           lds, 2 * nfull + xcd_logical_id(bid - nfull, (int64_t)gridDim.x - nfull), in, wp, out, npix, kg, mg,
-          tiles_n, bias, act, geo);
+          tiles_n, bias, act, nullptr, geo);
       return;
     }
   }
   fwd_tile<E, 4, FM, FN, WM, WN, NBUF, PF, 1, true>(lds, xcd_logical_id(bid, nfull), in, wp, out, npix, kg, mg,
-                                                    tiles_n, bias, act, geo);
+                                                    tiles_n, bias, act, nullptr, geo);
 }
 
 // Prepared spectra of the gathered layer, in the stage-block layout of the
@@ -196,12 +196,12 @@ conv_bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E
       if (bx >= ndx_full) {
         fwd_tile<E, 4, 1, 1, 2, 2, kBwdFwdBufs, kBwdFwdPrefetch, 1, true, true>(
             lds, 2 * ndx_full + xcd_logical_id(bx - ndx_full, (int64_t)gridDim.x - ndw_pad - ndx_full), dy, wb, dx,
-            npix, kgx, Cp, dx_tiles_n, nullptr, 0, gx);
+            npix, kgx, Cp, dx_tiles_n, nullptr, 0, nullptr, gx);
         return;
       }
     }
     fwd_tile<E, 4, 1, 1, 2, 2, kBwdFwdBufs, kBwdFwdPrefetch, 1, true>(lds, xcd_logical_id(bx, ndx_full), dy, wb, dx,
-                                                                       npix, kgx, Cp, dx_tiles_n, nullptr, 0, gx);
+                                                                       npix, kgx, Cp, dx_tiles_n, nullptr, 0, nullptr, gx);
   }
 }
 

@@ -298,7 +298,7 @@ ConvWs conv_workspace(int64_t npix, int C, int D, int K, int dtype) {
 
 extern "C" {
 
-int eqlin_version(void) { return 211; }
+int eqlin_version(void) { return 212; }
 
 const char* eqlin_status_str(int status) {
   switch (status) {
@@ -364,6 +364,11 @@ int eqlin_forward(const void* X, int64_t N, int C, int D, int T, const void* W_h
 
 int eqlin_forward_ex(const void* X, int64_t N, int C, int D, int T, const void* W_hat, const void* bias, int act,
                      void* Y, int dtype, void* stream) {
+  return eqlin_forward_residual(X, N, C, D, T, W_hat, bias, act, nullptr, Y, dtype, stream);
+}
+
+int eqlin_forward_residual(const void* X, int64_t N, int C, int D, int T, const void* W_hat, const void* bias, int act,
+                           const void* R, void* Y, int dtype, void* stream) {
   int st = check_shape(N, C, D, T, dtype);
   if (st != EQLIN_OK) return st;
   const int O = eqlin::group_order(T);
@@ -371,10 +376,11 @@ int eqlin_forward_ex(const void* X, int64_t N, int C, int D, int T, const void* 
   if (N == 0) return EQLIN_OK;
   if (!X || !W_hat || !Y) return EQLIN_EINVAL;
   if (!aligned16(X) || !aligned16(W_hat) || !aligned16(Y)) return EQLIN_EALIGN;
+  if (R && !aligned16(R)) return EQLIN_EALIGN;
   if (bias && (reinterpret_cast<uintptr_t>(bias) % elem_bytes(dtype)) != 0) return EQLIN_EALIGN;
   if (!fwd_offsets_fit(C, O, dtype) || !out_rows_fit(D, dtype)) return EQLIN_ENOTSUP;
   const int tile = choose_fwd_tile(T, dtype, N, D / O);
-  return hip_status(EQLIN_BY_T(T, forward(dtype, tile, X, W_hat, Y, N, C / O, D / O, bias, act,
+  return hip_status(EQLIN_BY_T(T, forward(dtype, tile, X, W_hat, Y, N, C / O, D / O, bias, act, R,
                                           static_cast<hipStream_t>(stream))));
 }
 
@@ -399,7 +405,7 @@ int eqlin_backward_dx(const void* dY, int64_t N, int C, int D, int T, const void
   // (input groups D', output groups C').
   const char* wb = static_cast<const char*>(W_hat) + transpose_offset(C, D, O, dtype);
   const int tile = choose_fwd_tile(T, dtype, N, C / O);
-  return hip_status(EQLIN_BY_T(T, forward(dtype, tile, dY, wb, dX, N, D / O, C / O, nullptr, 0,
+  return hip_status(EQLIN_BY_T(T, forward(dtype, tile, dY, wb, dX, N, D / O, C / O, nullptr, 0, nullptr,
                                           static_cast<hipStream_t>(stream))));
 }
 

@@ -419,6 +419,31 @@ __device__ __forceinline__ void store_group_buf(__amdgpu_buffer_rsrc_t dst, uint
   }
 }
 
+// T values of one output group (a residual) as float32, read through a buffer
+// range like store_group_buf's (out of range: zeros).
+template <typename E, int T>
+__device__ __forceinline__ void load_group_buf(__amdgpu_buffer_rsrc_t src, uint32_t off, float* v) {
+  if constexpr (sizeof(E) == 4) {
+#pragma unroll
+    for (int i = 0; i < T / 4; ++i) {
+      const f32x4 x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(src, off + 16u * i, 0, 0));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * i + e] = x[e];
+    }
+  } else if constexpr (T == 4) {
+    const f16x4 h = __builtin_bit_cast(f16x4, __builtin_amdgcn_raw_buffer_load_b64(src, off, 0, 0));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (float)h[e];
+  } else {
+#pragma unroll
+    for (int i = 0; i < T / 8; ++i) {
+      const f16x8 h = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(src, off + 16u * i, 0, 0));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[8 * i + e] = (float)h[e];
+    }
+  }
+}
+
 // ------------------------------------------------------ input transforms
 //
 // T 16-byte pieces fetched in unit order (see Units) hold kVals whole groups
@@ -786,7 +811,7 @@ constexpr int fwd_lds_bytes() {
 template <typename E, int G, int FM, int FN, int WM, int WN, bool HALF = false>
 __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[Grp<G>::kOrder][FM][FN], int64_t row0, int col0,
                                              E* __restrict__ out, int64_t nrows, int mg,
-                                             const E* __restrict__ bias, int act) {
+                                             const E* __restrict__ bias, int act, const E* __restrict__ res) {
   constexpr int T = Grp<G>::kOrder;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr = HALF ? 0 : wave / WN, wc = wave % WN;
@@ -796,6 +821,9 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[Grp<G>::kOrder]
   // their stores are dropped, as are those of a column past mg (kOob), so the
   // row loop needs no bounds test and only 32-bit offsets.
   const __amdgpu_buffer_rsrc_t dst = make_rsrc(out + row0 * (int64_t)T * mg, (uint64_t)(nrows - row0) * row_bytes);
+  // residual rows, read through the same offsets as the stores
+  const __amdgpu_buffer_rsrc_t rsd = make_rsrc(res != nullptr ? res + row0 * (int64_t)T * mg : out,
+                                               res != nullptr ? (uint64_t)(nrows - row0) * row_bytes : 0);
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
@@ -807,7 +835,7 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[Grp<G>::kOrder]
           mok ? (uint32_t)(wr * 32 * FM + fm * 32 + 4 * lh) * row_bytes + (uint32_t)m * (uint32_t)(T * sizeof(E))
               : kOob;
       if constexpr (sizeof(E) == 2 && G == 4) {
-        if (act == 0) {
+        if (act == 0 && res == nullptr) {
           // f16 p4 without activation: a = F0 + F2 and b = F0 - F2 in float32,
           // a / 4 + bias and b / 4 + bias, then each output is one mixed-
           // precision FMA (+- Re F1 / 2 or +- Im F1 / 2) rounded once into
@@ -845,7 +873,14 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[Grp<G>::kOrder]
 #pragma unroll
           for (int t = 0; t < T; ++t) y[t] = gelu_erf(y[t]);
         }
-        store_group_buf<E, T>(dst, lane_off + (uint32_t)(8 * (r >> 2) + (r & 3)) * row_bytes, y);
+        const uint32_t off = lane_off + (uint32_t)(8 * (r >> 2) + (r & 3)) * row_bytes;
+        if (res != nullptr) {
+          float rv[T];
+          load_group_buf<E, T>(rsd, off, rv);
+#pragma unroll
+          for (int t = 0; t < T; ++t) y[t] += rv[t];
+        }
+        store_group_buf<E, T>(dst, off, y);
       }
     }
   }
@@ -956,7 +991,7 @@ template <typename E, int G, int FM, int FN, int WM, int WN, int NBUF, int PF, i
 __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __restrict__ in,
                                          const E* __restrict__ wp, E* __restrict__ out, int64_t nrows, int kg,
                                          int mg, int tiles_n, const E* __restrict__ bias, int act,
-                                         const ConvGeom& geo = ConvGeom{}) {
+                                         const E* __restrict__ res, const ConvGeom& geo = ConvGeom{}) {
   constexpr int T = Grp<G>::kOrder;
   using U = Units<E, T>;
   constexpr int NT = 64 * WM * WN;
@@ -1178,7 +1213,7 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
       asm volatile("" ::: "memory");   // one plane's reads in flight at a time
     }
   }
-  fwd_epilogue<E, G, FM, FN, WM, WN, HALF>(acc, row0, col0, out, row_end, mg, bias, act);
+  fwd_epilogue<E, G, FM, FN, WM, WN, HALF>(acc, row0, col0, out, row_end, mg, bias, act, res);
 }
 
 // Persistent forward: workgroup `first` runs the tiles first, first + stride,
@@ -1192,7 +1227,7 @@ template <typename E, int G, int FM, int FN, int WM, int WN, int NBUF, int PF, i
 __device__ __forceinline__ void fwd_stream(char* lds, int64_t first, int64_t stride, int64_t ntiles,
                                            const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ out,
                                            int64_t nrows, int kg, int mg, int tiles_n, const E* __restrict__ bias,
-                                           int act) {
+                                           int act, const E* __restrict__ res) {
   constexpr int T = Grp<G>::kOrder;
   using U = Units<E, T>;
   constexpr int NT = 64 * WM * WN;
@@ -1323,7 +1358,7 @@ __device__ __forceinline__ void fwd_stream(char* lds, int64_t first, int64_t str
   for (int64_t j = 0; j < nt; ++j) {
     for (int ks = 0; ks < ksteps; ++ks) step(gs++);
     fwd_epilogue<E, G, FM, FN, WM, WN>(acc, (tile / tiles_n) * BM, (int)(tile % tiles_n) * BN, out, nrows, mg, bias,
-                                       act);
+                                       act, res);
     zero_acc();
     tile += stride;
   }
@@ -1346,12 +1381,12 @@ constexpr int fwd_waves_per_simd() {
 template <typename E, int G, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED, int PERSIST>
 __global__ void __launch_bounds__(64 * WM * WN, (fwd_waves_per_simd<E, Grp<G>::kOrder, FM, FN, WN>()))
 fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ out,
-           int64_t nrows, int kg, int mg, int tiles_n, const E* __restrict__ bias, int act, int64_t ntiles,
-           int64_t nfull) {
+           int64_t nrows, int kg, int mg, int tiles_n, const E* __restrict__ bias, int act,
+           const E* __restrict__ res, int64_t ntiles, int64_t nfull) {
   __shared__ __attribute__((aligned(16))) char lds[fwd_lds_bytes<E, Grp<G>::kOrder, FM, FN, WM, WN, NBUF>()];
   if constexpr (PERSIST) {
     fwd_stream<E, G, FM, FN, WM, WN, NBUF, PF, SCHED>(lds, xcd_logical_id(blockIdx.x, gridDim.x), gridDim.x, ntiles,
-                                                      in, wp, out, nrows, kg, mg, tiles_n, bias, act);
+                                                      in, wp, out, nrows, kg, mg, tiles_n, bias, act, res);
   } else {
     // workgroups 0 .. nfull - 1 run whole tiles; the rest, dispatched last
     // and so at most one per CU beyond the whole rounds, run the halves of
@@ -1361,12 +1396,12 @@ fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ o
       if (bid >= nfull) {
         fwd_tile<E, G, FM, FN, WM, WN, NBUF, PF, SCHED, false, true>(
             lds, 2 * nfull + xcd_logical_id(bid - nfull, (int64_t)gridDim.x - nfull), in, wp, out, nrows, kg, mg,
-            tiles_n, bias, act);
+            tiles_n, bias, act, res);
         return;
       }
     }
     fwd_tile<E, G, FM, FN, WM, WN, NBUF, PF, SCHED>(lds, xcd_logical_id(bid, nfull), in, wp, out, nrows, kg, mg,
-                                                    tiles_n, bias, act);
+                                                    tiles_n, bias, act, res);
   }
 }
 
@@ -1731,12 +1766,12 @@ bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E* __r
       if (bx >= ndx_full) {
         fwd_tile<E, G, 1, 1, 2, 2, kBwdFwdBufs, kBwdFwdPrefetch, SCHED, false, true>(
             lds, 2 * ndx_full + xcd_logical_id(bx - ndx_full, (int64_t)gridDim.x - ndw_pad - ndx_full), dy, wb, dx,
-            nrows, dg, cg, dx_tiles_n, nullptr, 0);
+            nrows, dg, cg, dx_tiles_n, nullptr, 0, nullptr);
         return;
       }
     }
     fwd_tile<E, G, 1, 1, 2, 2, kBwdFwdBufs, kBwdFwdPrefetch, SCHED>(lds, xcd_logical_id(bx, ndx_full), dy, wb, dx,
-                                                                     nrows, dg, cg, dx_tiles_n, nullptr, 0);
+                                                                     nrows, dg, cg, dx_tiles_n, nullptr, 0, nullptr);
   }
 }
 
@@ -1890,7 +1925,7 @@ int64_t resident_workgroups(K kernel, int threads) {
 
 template <typename E, int G, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED, int PERSIST>
 hipError_t launch_fwd_s(const void* in, const void* wp, void* out, int64_t nrows, int kg, int mg,
-                        const void* bias, int act, hipStream_t s) {
+                        const void* bias, int act, const void* res, hipStream_t s) {
   constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
   const int64_t tiles_m = cdiv(nrows, BM);
   const int tiles_n = (int)cdiv(mg, BN);
@@ -1910,7 +1945,7 @@ hipError_t launch_fwd_s(const void* in, const void* wp, void* out, int64_t nrows
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(64 * WM * WN), 0, s, static_cast<const E*>(in),
                      static_cast<const E*>(wp), static_cast<E*>(out), nrows, kg, mg, tiles_n,
-                     static_cast<const E*>(bias), act, tiles, nfull);
+                     static_cast<const E*>(bias), act, static_cast<const E*>(res), tiles, nfull);
   return hipGetLastError();
 }
 

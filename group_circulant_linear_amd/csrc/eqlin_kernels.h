@@ -65,9 +65,10 @@ inline int group_order(int g) { return g == kP4M ? 8 : g; }
 template <int G>
 struct Launch {
   static bool fwd_tile_known(int tile);
-  // bias: nullable, one storage-dtype value per output group; act: 0 none, 1 GELU (erf)
+  // bias: nullable, one storage-dtype value per output group; act: 0 none, 1 GELU (erf);
+  // res: nullable, a residual laid out as out, added after the activation
   static hipError_t forward(int dtype, int tile, const void* in, const void* wp, void* out, int64_t nrows, int kg,
-                            int mg, const void* bias, int act, hipStream_t s);
+                            int mg, const void* bias, int act, const void* res, hipStream_t s);
   // chunks (1, or a divisor of nrows with chunks x mg, chunks x ng <= 64): rows
   // read as rows of `chunks` consecutive rows (narrow layers), rows_per_split
   // counting those
@@ -84,7 +85,7 @@ struct Launch {
 #define EQLIN_DECLARE_LAUNCH(T)                                                                                     \
   template <> bool Launch<T>::fwd_tile_known(int tile);                                                             \
   template <> hipError_t Launch<T>::forward(int, int, const void*, const void*, void*, int64_t, int, int,          \
-                                            const void*, int, hipStream_t);                                        \
+                                            const void*, int, const void*, hipStream_t);                           \
   template <> hipError_t Launch<T>::dw(int, const void*, const void*, float*, float*, int64_t, int, int, int64_t,   \
                                        int, int, hipStream_t);                                                     \
   template <> hipError_t Launch<T>::bwd_fused(int, const void*, const void*, const void*, void*, float*, float*,   \

@@ -23,13 +23,13 @@ bool Launch<8>::fwd_tile_known(int tile) {
 
 template <>
 hipError_t Launch<8>::forward(int dtype, int tile, const void* in, const void* wp, void* out, int64_t nrows, int kg,
-                              int mg, const void* bias, int act, hipStream_t s) {
+                              int mg, const void* bias, int act, const void* res, hipStream_t s) {
 #define EQLIN_CASE(C)                                                                                      \
   case C:                                                                                                  \
     return dtype == 0 ? launch_fwd_s<float, 8, EQLIN_TILE_ARGS(C), 1, EQLIN_TILE_PERSIST(C)>(in, wp, out, nrows, kg,  \
-                                                                                          mg, bias, act, s) \
+                                                                                          mg, bias, act, res, s) \
                       : launch_fwd_s<_Float16, 8, EQLIN_TILE_ARGS(C), 1, EQLIN_TILE_PERSIST(C)>(in, wp, out, nrows,  \
-                                                                                             kg, mg, bias, act, s);
+                                                                                             kg, mg, bias, act, res, s);
   switch (tile) {
     EQLIN_C8_TILES(EQLIN_CASE)
     default: return hipErrorInvalidValue;

@@ -22,13 +22,13 @@ bool Launch<kP4M>::fwd_tile_known(int tile) {
 
 template <>
 hipError_t Launch<kP4M>::forward(int dtype, int tile, const void* in, const void* wp, void* out, int64_t nrows, int kg,
-                              int mg, const void* bias, int act, hipStream_t s) {
+                              int mg, const void* bias, int act, const void* res, hipStream_t s) {
 #define EQLIN_CASE(C)                                                                                      \
   case C:                                                                                                  \
     return dtype == 0 ? launch_fwd_s<float, kP4M, EQLIN_TILE_ARGS(C), 1, EQLIN_TILE_PERSIST(C)>(in, wp, out, nrows, kg,  \
-                                                                                          mg, bias, act, s) \
+                                                                                          mg, bias, act, res, s) \
                       : launch_fwd_s<_Float16, kP4M, EQLIN_TILE_ARGS(C), 1, EQLIN_TILE_PERSIST(C)>(in, wp, out, nrows,  \
-                                                                                             kg, mg, bias, act, s);
+                                                                                             kg, mg, bias, act, res, s);
   switch (tile) {
     EQLIN_P4M_TILES(EQLIN_CASE)
     default: return hipErrorInvalidValue;

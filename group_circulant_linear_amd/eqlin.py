@@ -79,6 +79,8 @@ def load_library(path: str = LIB) -> ctypes.CDLL:
                                        ctypes.POINTER(c_i64), ctypes.POINTER(c_i64)]),
         "eqlin_forward": (c_int, [c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_int, c_vp]),
         "eqlin_forward_ex": (c_int, [c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_int, c_vp, c_int, c_vp]),
+        "eqlin_forward_residual": (c_int, [c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_int, c_vp, c_vp, c_int,
+                                           c_vp]),
         "eqlin_backward_workspace_bytes": (c_sz, [c_i64, c_int, c_int, c_int, c_int]),
         "eqlin_backward": (c_int, [c_vp, c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_fp, c_vp, c_sz,
                                    c_int, c_vp]),
@@ -211,8 +213,9 @@ ACT = {"none": 0, "gelu": 1}
 
 
 def eqlin_forward_ex(X: torch.Tensor, W_hat: Prepared, bias: Optional[torch.Tensor] = None, act: str = "none",
-                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Y = act(X W^T + b) in one kernel; bias [D/n] (group-invariant, storage dtype) or None."""
+                     out: Optional[torch.Tensor] = None, residual: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = act(X W^T + b) (+ residual) in one kernel; bias [D/n] (group-invariant, storage dtype) or None;
+    residual [N][D] in X's dtype or None (it may be `out` itself: an in-place update)."""
     lib = load_library()
     _need_cuda(X, "X")
     dt = _dtype_code(X)
@@ -227,11 +230,20 @@ def eqlin_forward_ex(X: torch.Tensor, W_hat: Prepared, bias: Optional[torch.Tens
         if bias.dtype != X.dtype or tuple(bias.shape) != (W_hat.D // W_hat.order,):
             raise ValueError(f"bias must be [{W_hat.D // W_hat.order}] of dtype {X.dtype}")
     N = X.shape[0]
+    if residual is not None:
+        _need_cuda(residual, "residual")
+        if residual.dtype != X.dtype or tuple(residual.shape) != (N, W_hat.D):
+            raise ValueError(f"residual must be [{N}, {W_hat.D}] of dtype {X.dtype}")
     if out is None:
         out = torch.empty((N, W_hat.D), dtype=X.dtype, device=X.device)
     _need_cuda(out, "out")
-    _check("eqlin_forward_ex", lib.eqlin_forward_ex(_ptr(X), N, W_hat.C, W_hat.D, W_hat.T, _ptr(W_hat.buf),
-                                                    _ptr(bias), ACT[act], _ptr(out), dt, _stream(X)))
+    if residual is None:
+        _check("eqlin_forward_ex", lib.eqlin_forward_ex(_ptr(X), N, W_hat.C, W_hat.D, W_hat.T, _ptr(W_hat.buf),
+                                                        _ptr(bias), ACT[act], _ptr(out), dt, _stream(X)))
+    else:
+        _check("eqlin_forward_residual",
+               lib.eqlin_forward_residual(_ptr(X), N, W_hat.C, W_hat.D, W_hat.T, _ptr(W_hat.buf), _ptr(bias),
+                                          ACT[act], _ptr(residual), _ptr(out), dt, _stream(X)))
     return out
 
 

@@ -197,6 +197,23 @@ enum { EQLIN_ACT_NONE = 0, EQLIN_ACT_GELU = 1 };
 int eqlin_forward_ex(const void* X, int64_t N, int C, int D, int T, const void* W_hat,
                      const void* bias, int act, void* Y, int dtype, void* stream);
 
+/*
+ * Forward with a fused epilogue and a residual: Y = act(X W^T + b) + R.
+ * The residual is the transformer block's skip connection around the MLP
+ * (x + MLP(x)) of the ViT networks the summary measures ("Network-level
+ * results"; the pages do not spell it out: this is the reading).  Adding a
+ * tensor that is itself laid out by group channel keeps the layer
+ * equivariant.
+ *   R: NULL (then exactly eqlin_forward_ex) or a device pointer to [N][D] in
+ *      the storage dtype, 16-byte aligned (else EQLIN_EALIGN).  R may be Y
+ *      itself (an in-place update: every element is read before it is
+ *      written, by the same lane); otherwise R must not overlap Y.
+ * The residual is added in float32 after the activation, before the single
+ * rounding to the storage dtype.  Everything else as eqlin_forward_ex.
+ */
+int eqlin_forward_residual(const void* X, int64_t N, int C, int D, int T, const void* W_hat,
+                           const void* bias, int act, const void* R, void* Y, int dtype, void* stream);
+
 /* Workspace bytes eqlin_backward / eqlin_backward_dw need for this shape. */
 size_t eqlin_backward_workspace_bytes(int64_t N, int C, int D, int T, int dtype);
 

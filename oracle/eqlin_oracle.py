@@ -242,10 +242,13 @@ def gelu_erf(z) -> np.ndarray:
     return 0.5 * z * (1.0 + verf(z / sqrt(2.0)))
 
 
-def forward_bias_act(X, w, bias=None, act: str = "none") -> np.ndarray:
-    """act(X W^T + b) with a group-invariant bias b[d'] added to the T outputs of
-    output group d' (reading: the summary is silent on bias; a bias shared by the
-    group elements keeps the layer equivariant) and an optional GELU."""
+def forward_bias_act(X, w, bias=None, act: str = "none", residual=None) -> np.ndarray:
+    """act(X W^T + b) (+ R) with a group-invariant bias b[d'] added to the T
+    outputs of output group d' (reading: the summary is silent on bias; a bias
+    shared by the group elements keeps the layer equivariant), an optional GELU,
+    and an optional residual R [N][D] added after the activation (reading: the
+    skip connection around the MLP of the ViT blocks of "Network-level
+    results", which the summary does not spell out)."""
     Y = forward_direct(X, w)
     T = _f64(w).shape[2]
     if bias is not None:
@@ -254,6 +257,8 @@ def forward_bias_act(X, w, bias=None, act: str = "none") -> np.ndarray:
         Y = gelu_erf(Y)
     elif act != "none":
         raise ValueError(act)
+    if residual is not None:
+        Y = Y + _f64(residual)
     return Y
 
 

@@ -146,6 +146,15 @@ def test_forward_ex_validation(lib):
     assert f(None, 0, 32, 32, 4, None, None, 1, None, 0, None) == OK            # empty batch
 
 
+def test_forward_residual_validation(lib):
+    f = lib.eqlin_forward_residual
+    assert f(FAKE, 8, 32, 32, 4, FAKE, None, 2, FAKE, FAKE, 0, None) == EINVAL        # unknown activation
+    assert f(FAKE, 8, 32, 32, 4, FAKE, None, 1, ctypes.c_void_p(0x1008), FAKE, 0, None) == EALIGN  # residual
+    assert f(FAKE, 8, 32, 32, 4, FAKE, None, 1, FAKE, None, 0, None) == EINVAL        # no output
+    assert f(FAKE, 8, 32, 32, 3, FAKE, None, 1, FAKE, FAKE, 0, None) == ENOTSUP
+    assert f(None, 0, 32, 32, 4, None, None, 1, None, None, 0, None) == OK            # empty batch
+
+
 # ------------------------------------------------------------ p4 group convolution
 
 def test_conv_size_queries(lib):

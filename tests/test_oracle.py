@@ -396,3 +396,28 @@ def test_bias_act_forward_is_equivariant_and_reduces_to_forward():
     Z = oracle.forward_bias_act(X, w, b) - oracle.forward_direct(X, w)
     assert np.allclose(Z.reshape(7, 5, 4), b[None, :, None], rtol=0, atol=1e-14)
 
+
+def test_residual_forward_adds_after_the_activation_and_stays_equivariant():
+    X = _rand((7, 24), 43)
+    w = _rand((5, 6, 4), 44)
+    b = _rand(5, 45)
+    R = _rand((7, 20), 46)
+    # a zero residual changes nothing; the residual is added after GELU, not inside it
+    assert np.array_equal(oracle.forward_bias_act(X, w, b, "gelu", np.zeros((7, 20))),
+                          oracle.forward_bias_act(X, w, b, "gelu"))
+    Y = oracle.forward_bias_act(X, w, b, "gelu", R)
+    assert _rel(Y - R, oracle.gelu_erf(oracle.forward_bias_act(X, w, b))) < 1e-14
+    # the dense expansion, written out on this tiny case: Y = GELU(X Wd^T + b) + R
+    Wd = np.zeros((20, 24))
+    for d in range(5):
+        for c in range(6):
+            for t in range(4):
+                for s in range(4):
+                    Wd[4 * d + t, 4 * c + s] = w[d, c, (t - s) % 4]
+    assert _rel(Y, oracle.gelu_erf(X @ Wd.T + np.repeat(b, 4)[None, :]) + R) < 1e-14
+    # shifting the group index of the input and of the residual shifts the output
+    Xr = np.roll(X.reshape(7, 6, 4), 1, axis=2).reshape(7, 24)
+    Rr = np.roll(R.reshape(7, 5, 4), 1, axis=2).reshape(7, 20)
+    Yr = oracle.forward_bias_act(Xr, w, b, "gelu", Rr).reshape(7, 5, 4)
+    assert _rel(Yr, np.roll(Y.reshape(7, 5, 4), 1, axis=2)) < 1e-14
+

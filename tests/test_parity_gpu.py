@@ -485,6 +485,50 @@ def test_forward_ex_bias_gelu(dt, with_bias, act, g):
         assert rel_err(Y, ref) <= TOL[dt]
 
 
+@pytest.mark.parametrize("g", GROUPS)
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("with_bias,act,inplace", [(False, "none", False), (True, "gelu", False),
+                                                   (True, "none", True)])
+def test_forward_residual(dt, with_bias, act, inplace, g):
+    """Y = act(X W^T + b) + R, R added in float32 after the activation; R may be Y."""
+    T = order(g)
+    for (N, C, D) in [(131, 8 * 3, 8 * 5), (1000, 160, 96), (333, 8 * 100, 8 * 65), (3001, 64, 64)]:
+        say(f"forward_residual group={g} {dt} bias={with_bias} act={act} inplace={inplace} N={N} C={C} D={D}")
+        X, w, R = make_layer_inputs(N, C, D, dt, seed=17, T=T)
+        b = (np.random.default_rng(18).standard_normal(D // T)).astype(X.dtype) if with_bias else None
+        Wh = prep(w, g)
+        tR = dev(R)
+        Y = eq.eqlin_forward_ex(dev(X), Wh, dev(b) if with_bias else None, act, out=tR if inplace else None,
+                                residual=tR)
+        Z = ref_forward(X, w, g) + (np.repeat(b.astype(np.float64), T)[None, :] if with_bias else 0.0)
+        ref = (oracle.gelu_erf(Z) if act == "gelu" else Z) + R.astype(np.float64)
+        if g != "p4m":
+            assert np.array_equal(ref, oracle.forward_bias_act(X, w, b, act, R))
+        err = rel_err(host(Y), ref)
+        say(f"  rel err {err:.3e}")
+        assert err <= TOL[dt]
+
+
+def test_forward_residual_mlp_block_vitb_f16_sampled():
+    # the ViT block's MLP with its skip connection: X + fc2(GELU(fc1(X) + b1)) + b2
+    wl = WORKLOADS["vitb_mlp"]
+    (L1, L2) = wl.layers
+    X, w1, _ = make_layer_inputs(L1.N, L1.C, L1.D, "f16", seed=0, layer=0, with_dy=False)
+    _, w2, _ = make_layer_inputs(8, L2.C, L2.D, "f16", seed=0, layer=1, with_dy=False)
+    rng = np.random.default_rng(19)
+    b1 = rng.standard_normal(L1.D // 4).astype(np.float16)
+    b2 = rng.standard_normal(L2.D // 4).astype(np.float16)
+    W1, W2 = eq.eqlin_prepare_weights(dev(w1)), eq.eqlin_prepare_weights(dev(w2))
+    tX = dev(X)
+    H = eq.eqlin_forward_ex(tX, W1, dev(b1), "gelu")
+    Y = host(eq.eqlin_forward_ex(H, W2, dev(b2), "none", residual=tX))
+    rows = _sample_rows(L1.N, np.random.default_rng(20), k=48)
+    Hh = host(H)[rows]
+    err = rel_err(Y[rows], oracle.forward_bias_act(Hh.astype(np.float16), w2, b2, "none", X[rows]))
+    say(f"  block rel err {err:.3e}")
+    assert err <= 3e-3
+
+
 def test_forward_ex_mlp_block_vitb_f16_sampled():
     # fc1 768->3072 (+bias, GELU) then fc2 3072->768 (+bias), f16 storage
     wl = WORKLOADS["vitb_mlp"]
