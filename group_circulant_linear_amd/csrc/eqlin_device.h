@@ -1688,7 +1688,10 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
     // stage loop's last barrier), are added in block order and written as
     // one cw_m x cw_n partial per plane
     const int CH = mg / cw_m, cell = cw_m * cw_n;
-    float* red = reinterpret_cast<float*>(lds);  // [T][CH][cw_m][cw_n]: T x 64 x 64 floats at most
+    // [T][CH][cw_m][cw_n]: T mg ng / CH <= T x 2048 floats (CH >= 2, mg, ng <= 64),
+    // the size of the dw stage buffers (T x 2 x 64 x 64 bytes per buffer)
+    static_assert(BUF >= T * 2048 * (int)sizeof(float), "chunk reduction fits the stage buffer");
+    float* red = reinterpret_cast<float*>(lds);
     const int nblk = n / cw_n;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -1777,12 +1780,12 @@ bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E* __r
 
 // Sum the split partials (deterministic), inverse group DFT along u, write
 // dw[m][n][0..T-1] (float32).  A 256-thread block covers EB = 256 / (T R)
-// consecutive entries: thread (chunk r, plane p, entry e) sums the splits
-// s = r, r + R, r + 2R, ... of plane p in increasing s, the R chunk sums of
-// a (plane, entry) meet in LDS and are added in chunk order, then the T plane
+// consecutive entries: thread (part r, plane p, entry e) sums the splits
+// s = r, r + R, r + 2R, ... of plane p in increasing s, the R part sums of
+// a (plane, entry) meet in LDS and are added in part order, then the T plane
 // sums of an entry meet and one thread per entry applies the inverse DFT.
 // R (a power of two, T R <= 256) is set by the host from the entry and split
-// counts alone (dw_finalize_chunks), so a given call always adds in the same
+// counts alone (dw_finalize_parts), so a given call always adds in the same
 // order; R = 1 is the plain split-order sum.  nsplit == 0 writes zeros.
 template <int G>
 __global__ void __launch_bounds__(kThreads)
@@ -1828,12 +1831,12 @@ dw_finalize_kernel(const float* __restrict__ ws, float* __restrict__ dw, int mg,
   }
 }
 
-// Chunks per (plane, entry) of dw_finalize_kernel: doubled while the launch
-// holds fewer than two blocks per CU and every chunk keeps at least four
+// Parts per (plane, entry) of dw_finalize_kernel: doubled while the launch
+// holds fewer than two blocks per CU and every part keeps at least four
 // splits, so a layer with few weight entries and many row splits (narrow
 // layers over many rows) reads its partials with the whole chip rather than
 // a few CUs each walking every split.
-inline int dw_finalize_chunks(int64_t entries, int T, int nsplit) {
+inline int dw_finalize_parts(int64_t entries, int T, int nsplit) {
   int R = 1;
   while (2 * R * T <= kThreads && (int64_t)nsplit >= 8 * R &&
          (entries + kThreads / (T * R) - 1) / (kThreads / (T * R)) < 2 * kNumCu)
@@ -1845,7 +1848,7 @@ template <int G>
 hipError_t launch_dw_finalize(const float* ws, float* dw, int mg, int ng, int nsplit, hipStream_t s) {
   constexpr int T = Grp<G>::kOrder;
   const int64_t entries = (int64_t)mg * ng;
-  const int R = dw_finalize_chunks(entries, T, nsplit);
+  const int R = dw_finalize_parts(entries, T, nsplit);
   const int64_t grid = (entries + kThreads / (T * R) - 1) / (kThreads / (T * R));
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (grid > 0)
