@@ -93,6 +93,18 @@ def group_args(group):
     return T, T, (2 * T - 2) / T ** 2       # cyclic: F0, F_{T/2} and T/2 - 1 complex frequencies
 
 
+def layer_roofline(layers, es, T, exec_frac, peak_tflops):
+    """(bound, algorithmic bytes, executed FLOPs) of the forward over `layers`
+    (objects with N, C, D): X read once, Y written once, the T-plane weight
+    spectra (C D / T values) read once; executed FLOPs 2 NCD exec_frac.  The
+    bound is the roofline model's: "hbm" when the bytes at the HBM peak take
+    longer than the FLOPs at the MFMA peak, else "mfma"."""
+    alg_bytes = sum(es * L.N * (L.C + L.D) + es * L.C * L.D / T for L in layers)
+    exec_flops = 2.0 * exec_frac * sum(L.N * L.C * L.D for L in layers)
+    bound = "hbm" if alg_bytes / (HBM_PEAK_GBS * 1e9) > exec_flops / (peak_tflops * 1e12) else "mfma"
+    return bound, alg_bytes, exec_flops
+
+
 def profile_tag(workload, dt, group):
     return f"{workload}_{dt}" + {"4": "", "8": "_c8", "p4m": "_p4m"}[str(group)]
 
@@ -506,12 +518,10 @@ def main():
     achieved = exec_flops / (fwd_us * 1e-6) / 1e12
     peak = PEAK_TFLOPS[dt]
     es_b = 4 if dt == "f32" else 2
-    alg_bytes = sum(es_b * L.N * (L.C + L.D) + es_b * L.C * L.D / T for (L, _, _, _) in layers)
+    bound, alg_bytes, _ = layer_roofline([L for (L, _, _, _) in layers], es_b, T, exec_frac, peak)
     traffic = profiled_traffic(profile_tag(wl.name, dt, args.group), "eqlin::fwd_kernel") if len(layers) == 1 else None
     gbs = alg_bytes / (fwd_us * 1e-6) / 1e9
-    # the bound is the roofline's: executed FLOPs at the MFMA peak against the
-    # algorithmic bytes at the HBM peak, whichever takes longer
-    hbm_bound = alg_bytes / (HBM_PEAK_GBS * 1e9) > exec_flops / (peak * 1e12)
+    hbm_bound = bound == "hbm"
     roofline = {"bound": "hbm" if hbm_bound else "mfma", "kernel": "eqlin::fwd_kernel",
                 "achieved": round(gbs, 1) if hbm_bound else round(achieved, 2),
                 "peak": HBM_PEAK_GBS if hbm_bound else peak,
