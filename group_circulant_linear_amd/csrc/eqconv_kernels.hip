@@ -143,9 +143,10 @@ __device__ __forceinline__ void conv_prepare_entry(const E* __restrict__ psi, E*
     }
     Grp<4>::dft(z, f);
   }
+  // f16: scaled into the operand range of the f16 products (Grp<4>::kF16Scale)
   E* o = dst + ((int64_t)row * nks + ks) * T * SG + s;
 #pragma unroll
-  for (int q = 0; q < T; ++q) o[q * SG] = (E)f[q];
+  for (int q = 0; q < T; ++q) o[q * SG] = (E)(sizeof(E) == 2 ? f[q] * Grp<4>::kF16Scale[q] : f[q]);
 }
 
 template <typename E>
@@ -273,7 +274,7 @@ hipError_t launch_conv_dw(const void* dy, const void* x, float* ws, float* dwlin
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_dw_finalize<4>(ws, dwlin, Dp, kg, nsplit, s);
+  return launch_dw_finalize<E, 4>(ws, dwlin, Dp, kg, nsplit, s);
 }
 
 template <typename E>
@@ -301,7 +302,7 @@ hipError_t launch_conv_bwd_fused(const void* dy, const void* x, const void* wb, 
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_dw_finalize<4>(ws, dwlin, Dp, kgw, nsplit, s);
+  return launch_dw_finalize<E, 4>(ws, dwlin, Dp, kgw, nsplit, s);
 }
 
 template <typename E>

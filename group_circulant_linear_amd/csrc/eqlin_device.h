@@ -163,6 +163,21 @@ __device__ __forceinline__ void conj_planes(float* f) {
     if (imag_plane(p)) f[p] = -f[p];
 }
 
+// Range of the f16 Fourier operands.  A plane of the transform of T values
+// bounded by M is bounded by b_p M (F0 sums all T values).  In f16 every
+// operand plane p (the transformed input, dY and the prepared weights) is
+// multiplied by kF16Scale[p], the largest power of two with
+// kF16Scale[p] b_p <= 1, before its one rounding to binary16, so no finite
+// binary16 input can overflow an operand (the page's dyadic coefficients
+// put the normalisation on either side; here part of it moves to the forward
+// transform).  Every product of an output plane p meets operands of equal
+// scale, so the accumulated plane carries kF16Scale[p]^2, which the epilogue
+// and the dw finalize multiply back out (exact powers of two).
+template <int G>
+__host__ __device__ constexpr float f16_unscale(int p) {
+  return 1.0f / (Grp<G>::kF16Scale[p] * Grp<G>::kF16Scale[p]);
+}
+
 template <>
 struct Grp<4> {
   static constexpr int kOrder = 4;
@@ -170,6 +185,8 @@ struct Grp<4> {
   static constexpr Prod kFwd[kProducts] = {{0, 0, 0, false}, {2, 2, 2, false}, {1, 1, 1, false},
                                            {3, 2, 3, false}, {2, 3, 3, true},  {3, 3, 2, false}};
   static constexpr const Prod* kDw = kFwd;
+  // |F0|, |F2| <= 4 M; |Re F1|, |Im F1| <= 2 M
+  static constexpr float kF16Scale[kOrder] = {0.25f, 0.25f, 0.5f, 0.5f};
   __device__ __forceinline__ static void dft(const float* z, float* f) {
     dft4(z[0], z[1], z[2], z[3], f[0], f[1], f[2], f[3]);
   }
@@ -197,6 +214,8 @@ struct Grp<8> {
       {4, 5, 5, true},  {5, 5, 4, false}, {6, 7, 7, true},  {7, 7, 6, false}};
   static constexpr const Prod* kDw = kFwd;
   static constexpr float kC = 0.70710678118654752f;
+  // |F0|, |F4| <= 8 M; |Re F2|, |Im F2| <= 4 M; the parts of F1 and F3 <= (2 + 4c) M < 8 M
+  static constexpr float kF16Scale[kOrder] = {0.125f, 0.125f, 0.125f, 0.125f, 0.25f, 0.25f, 0.125f, 0.125f};
   __device__ __forceinline__ static void dft(const float* z, float* f) {
     float s[4], a[4];
 #pragma unroll
@@ -260,6 +279,8 @@ struct Grp<kP4M> {
   static constexpr Prod kDw[kProducts] = {
       {0, 0, 0, false}, {1, 1, 1, false}, {2, 2, 2, false}, {3, 3, 3, false}, {4, 4, 4, false}, {5, 5, 4, false},
       {6, 4, 6, false}, {7, 5, 6, false}, {4, 6, 5, false}, {5, 7, 5, false}, {6, 6, 7, false}, {7, 7, 7, false}};
+  // the characters sum all eight values (<= 8 M); the entries of E four (<= 4 M)
+  static constexpr float kF16Scale[kOrder] = {0.125f, 0.125f, 0.125f, 0.125f, 0.25f, 0.25f, 0.25f, 0.25f};
   __device__ __forceinline__ static void dft(const float* z, float* f) {
     const float a = z[0] + z[2], b = z[1] + z[3], c = z[4] + z[6], d = z[5] + z[7];
     const float al = z[0] - z[2], be = z[1] - z[3], ga = z[4] - z[6], de = z[5] - z[7];
@@ -453,15 +474,20 @@ __device__ __forceinline__ void load_group_buf(__amdgpu_buffer_rsrc_t src, uint3
 
 // f16, T = 4: group DFT of the two groups of one 16-byte piece (registers
 // z01 = (z0, z1), z23 = (z2, z3) of group 0 and z45 / z67 of group 1), written
-// as packed f16 plane values: p0 = (F0_g0, F0_g1), p2 = (F2_g0, F2_g1),
-// p1r = (Re F1_g0, Re F1_g1), p1i = (+-Im F1_g0, +-Im F1_g1).  The mixed
-// precision FMA reads f16 halves directly, computes in f32 and rounds the
-// result once (nearest-even) into the low or high half of the destination:
-//   a = z0 + z2, b = z1 + z3 (f32);  F0 = a + b;  F2 = a - b;
-//   Re F1 = z0 - z2;  Im F1 = z3 - z1 (negated when kConj).
+// as packed f16 plane values scaled by Grp<4>::kF16Scale: p0 = (F0_g0,
+// F0_g1) / 4, p2 = (F2_g0, F2_g1) / 4, p1r = (Re F1_g0, Re F1_g1) / 2,
+// p1i = (+-Im F1_g0, +-Im F1_g1) / 2.  The mixed precision FMA reads f16
+// halves (or f32 registers) directly, computes in f32 and rounds the result
+// once (nearest-even) into the low or high half of the destination:
+//   a = z0 + z2, b = z1 + z3 (f32);  F0/4 = a/4 + b/4;  F2/4 = a/4 - b/4;
+//   Re F1/2 = a/2 - z2 (= (z0 - z2)/2);  Im F1/2 = b/2 - z1 (= (z3 - z1)/2,
+//   negated when kConj).
 template <bool kConj>
 __device__ __forceinline__ void dft4_f16_pair(uint32_t z01, uint32_t z23, uint32_t z45, uint32_t z67,
                                               uint32_t& p0, uint32_t& p2, uint32_t& p1r, uint32_t& p1i) {
+  static_assert(Grp<4>::kF16Scale[0] == 0.25f && Grp<4>::kF16Scale[1] == 0.25f && Grp<4>::kF16Scale[2] == 0.5f &&
+                    Grp<4>::kF16Scale[3] == 0.5f,
+                "the p4 f16 transform applies the scales 1/4, 1/4, 1/2, 1/2");
   float a0, b0, a1, b1;
   asm volatile(
       "v_fma_mix_f32 %0, %4, 1.0, %5 op_sel:[0,0,0] op_sel_hi:[1,0,1]\n\t"
@@ -470,42 +496,46 @@ __device__ __forceinline__ void dft4_f16_pair(uint32_t z01, uint32_t z23, uint32
       "v_fma_mix_f32 %3, %6, 1.0, %7 op_sel:[1,0,1] op_sel_hi:[1,0,1]"
       : "=&v"(a0), "=&v"(b0), "=&v"(a1), "=&v"(b1)
       : "v"(z01), "v"(z23), "v"(z45), "v"(z67));
+  const float bq0 = 0.25f * b0, bq1 = 0.25f * b1;
   asm volatile(
-      "v_fma_mixlo_f16 %0, %2, 1.0, %3 op_sel_hi:[0,0,0]\n\t"
-      "v_fma_mixhi_f16 %0, %4, 1.0, %5 op_sel_hi:[0,0,0]\n\t"
-      "v_fma_mixlo_f16 %1, %2, 1.0, -%3 op_sel_hi:[0,0,0]\n\t"
-      "v_fma_mixhi_f16 %1, %4, 1.0, -%5 op_sel_hi:[0,0,0]"
+      "v_fma_mixlo_f16 %0, %2, %6, %4 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixhi_f16 %0, %3, %6, %5 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixlo_f16 %1, %2, %6, -%4 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixhi_f16 %1, %3, %6, -%5 op_sel_hi:[0,0,0]"
       : "=&v"(p0), "=&v"(p2)
-      : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
+      : "v"(a0), "v"(a1), "v"(bq0), "v"(bq1), "s"(0.25f));
+  // src2 an f16 half (op_sel_hi 1), selected by op_sel
   asm volatile(
-      "v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel:[0,0,0] op_sel_hi:[1,0,1]\n\t"
-      "v_fma_mixhi_f16 %0, %3, 1.0, -%4 op_sel:[0,0,0] op_sel_hi:[1,0,1]"
+      "v_fma_mixlo_f16 %0, %1, 0.5, -%3 op_sel:[0,0,0] op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %0, %2, 0.5, -%4 op_sel:[0,0,0] op_sel_hi:[0,0,1]"
       : "=&v"(p1r)
-      : "v"(z01), "v"(z23), "v"(z45), "v"(z67));
+      : "v"(a0), "v"(a1), "v"(z23), "v"(z67));
   if constexpr (!kConj) {
     asm volatile(
-        "v_fma_mixlo_f16 %0, %2, 1.0, -%1 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\t"
-        "v_fma_mixhi_f16 %0, %4, 1.0, -%3 op_sel:[1,0,1] op_sel_hi:[1,0,1]"
+        "v_fma_mixlo_f16 %0, %1, 0.5, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+        "v_fma_mixhi_f16 %0, %2, 0.5, -%4 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
         : "=&v"(p1i)
-        : "v"(z01), "v"(z23), "v"(z45), "v"(z67));
+        : "v"(b0), "v"(b1), "v"(z01), "v"(z45));
   } else {
     asm volatile(
-        "v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel:[1,0,1] op_sel_hi:[1,0,1]\n\t"
-        "v_fma_mixhi_f16 %0, %3, 1.0, -%4 op_sel:[1,0,1] op_sel_hi:[1,0,1]"
+        "v_fma_mixlo_f16 %0, %1, -0.5, %3 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+        "v_fma_mixhi_f16 %0, %2, -0.5, %4 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
         : "=&v"(p1i)
-        : "v"(z01), "v"(z23), "v"(z45), "v"(z67));
+        : "v"(b0), "v"(b1), "v"(z01), "v"(z45));
   }
 }
 
 // f16, C8: group DFT of two groups (x: group 0, y: group 1; word k holds
 // (z_2k, z_2k+1)), written as packed f16 plane values o[p] = (plane p of
-// group 0, plane p of group 1) in the plane order of Grp<8>.  As in
-// dft4_f16_pair the mixed-precision FMAs read the f16 halves directly and
-// every plane is rounded once to f16 from a float32 expression:
+// group 0, plane p of group 1) in the plane order of Grp<8>, scaled by
+// Grp<8>::kF16Scale (1/8, except 1/4 for F2).  As in dft4_f16_pair the
+// mixed-precision FMAs read the f16 halves directly and every plane is
+// rounded once to f16 from a float32 expression:
 //   s_u = z_u + z_u+4, a_u = z_u - z_u+4 (f32);  A = s0 + s2, B = s1 + s3,
-//   t = a1 - a3, v = a1 + a3;  F0 = A + B, F4 = A - B, Re F2 = s0 - s2,
-//   Im F2 = s3 - s1, Re F1 = a0 + c t, Im F1 = -a2 - c v, Re F3 = a0 - c t,
-//   Im F3 = a2 - c v  (c = sqrt 1/2; the imaginary planes negated when kConj).
+//   t = a1 - a3, v = a1 + a3;  F0/8 = A/8 + B/8, F4/8 = A/8 - B/8,
+//   Re F2/4 = A/4 - s2/2, Im F2/4 = B/4 - s1/2, Re F1/8 = a0/8 + (c/8) t,
+//   Im F1/8 = -a2/8 - (c/8) v, Re F3/8 = a0/8 - (c/8) t, Im F3/8 = a2/8 - (c/8) v
+//   (c = sqrt 1/2; the imaginary planes negated when kConj).
 template <bool kConj>
 __device__ __forceinline__ void dft8_f16_pair(const u32x4& x, const u32x4& y, uint32_t (&o)[8]) {
   float s[2][4], a[2][4];
@@ -525,47 +555,57 @@ __device__ __forceinline__ void dft8_f16_pair(const u32x4& x, const u32x4& y, ui
           "=&v"(a[g][2]), "=&v"(a[g][3])
         : "v"(z[0]), "v"(z[1]), "v"(z[2]), "v"(z[3]));
   }
-  float A[2], B[2], t[2], v[2];
+  static_assert(Grp<8>::kF16Scale[0] == 0.125f && Grp<8>::kF16Scale[1] == 0.125f &&
+                    Grp<8>::kF16Scale[2] == 0.125f && Grp<8>::kF16Scale[3] == 0.125f &&
+                    Grp<8>::kF16Scale[4] == 0.25f && Grp<8>::kF16Scale[5] == 0.25f &&
+                    Grp<8>::kF16Scale[6] == 0.125f && Grp<8>::kF16Scale[7] == 0.125f,
+                "the C8 f16 transform applies the scales 1/8 (F0, F4, F1, F3) and 1/4 (F2)");
+  float A[2], Bq[2], t[2], v[2], s1h[2], s2h[2], a0q[2], a2q[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
     A[g] = s[g][0] + s[g][2];
-    B[g] = s[g][1] + s[g][3];
+    Bq[g] = 0.125f * (s[g][1] + s[g][3]);
     t[g] = a[g][1] - a[g][3];
     v[g] = a[g][1] + a[g][3];
+    s1h[g] = 0.5f * s[g][1];
+    s2h[g] = 0.5f * s[g][2];
+    a0q[g] = 0.125f * a[g][0];
+    a2q[g] = 0.125f * a[g][2];
   }
-  const float c = Grp<8>::kC;
-  // planes 0, 1, 4, 5: the 4-point DFT of s
+  const float c8 = 0.125f * Grp<8>::kC;
+  // planes 0, 1 (F0/8, F4/8) and 4 (Re F2/4)
   asm volatile(
-      "v_fma_mixlo_f16 %0, %3, 1.0, %5 op_sel_hi:[0,0,0]\n\t"
-      "v_fma_mixhi_f16 %0, %4, 1.0, %6 op_sel_hi:[0,0,0]\n\t"
-      "v_fma_mixlo_f16 %1, %3, 1.0, -%5 op_sel_hi:[0,0,0]\n\t"
-      "v_fma_mixhi_f16 %1, %4, 1.0, -%6 op_sel_hi:[0,0,0]\n\t"
-      "v_fma_mixlo_f16 %2, %7, 1.0, -%9 op_sel_hi:[0,0,0]\n\t"
-      "v_fma_mixhi_f16 %2, %8, 1.0, -%10 op_sel_hi:[0,0,0]"
+      "v_fma_mixlo_f16 %0, %3, %9, %5 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixhi_f16 %0, %4, %9, %6 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixlo_f16 %1, %3, %9, -%5 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixhi_f16 %1, %4, %9, -%6 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixlo_f16 %2, %3, %10, -%7 op_sel_hi:[0,0,0]\n\t"
+      "v_fma_mixhi_f16 %2, %4, %10, -%8 op_sel_hi:[0,0,0]"
       : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[4])
-      : "v"(A[0]), "v"(A[1]), "v"(B[0]), "v"(B[1]), "v"(s[0][0]), "v"(s[1][0]), "v"(s[0][2]), "v"(s[1][2]));
+      : "v"(A[0]), "v"(A[1]), "v"(Bq[0]), "v"(Bq[1]), "v"(s2h[0]), "v"(s2h[1]), "s"(0.125f), "s"(0.25f));
+  // plane 5 (Im F2/4 = B/4 - s1/2, or its negative), B/4 = 2 Bq
   if constexpr (!kConj) {
     asm volatile(
-        "v_fma_mixlo_f16 %0, %1, 1.0, -%3 op_sel_hi:[0,0,0]\n\t"
-        "v_fma_mixhi_f16 %0, %2, 1.0, -%4 op_sel_hi:[0,0,0]"
+        "v_fma_mixlo_f16 %0, %1, 2.0, -%3 op_sel_hi:[0,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %2, 2.0, -%4 op_sel_hi:[0,0,0]"
         : "=&v"(o[5])
-        : "v"(s[0][3]), "v"(s[1][3]), "v"(s[0][1]), "v"(s[1][1]));
+        : "v"(Bq[0]), "v"(Bq[1]), "v"(s1h[0]), "v"(s1h[1]));
   } else {
     asm volatile(
-        "v_fma_mixlo_f16 %0, %1, 1.0, -%3 op_sel_hi:[0,0,0]\n\t"
-        "v_fma_mixhi_f16 %0, %2, 1.0, -%4 op_sel_hi:[0,0,0]"
+        "v_fma_mixlo_f16 %0, %1, -2.0, %3 op_sel_hi:[0,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %2, -2.0, %4 op_sel_hi:[0,0,0]"
         : "=&v"(o[5])
-        : "v"(s[0][1]), "v"(s[1][1]), "v"(s[0][3]), "v"(s[1][3]));
+        : "v"(Bq[0]), "v"(Bq[1]), "v"(s1h[0]), "v"(s1h[1]));
   }
-  // planes 2 and 6 (real parts of F1, F3): a0 +- c t
+  // planes 2 and 6 (real parts of F1, F3, over 8): a0/8 +- (c/8) t
   asm volatile(
       "v_fma_mixlo_f16 %0, %2, %6, %4 op_sel_hi:[0,0,0]\n\t"
       "v_fma_mixhi_f16 %0, %3, %6, %5 op_sel_hi:[0,0,0]\n\t"
       "v_fma_mixlo_f16 %1, %2, -%6, %4 op_sel_hi:[0,0,0]\n\t"
       "v_fma_mixhi_f16 %1, %3, -%6, %5 op_sel_hi:[0,0,0]"
       : "=&v"(o[2]), "=&v"(o[6])
-      : "v"(t[0]), "v"(t[1]), "v"(a[0][0]), "v"(a[1][0]), "v"(c));
-  // planes 3 and 7 (imaginary parts): -a2 - c v and a2 - c v, or their negatives
+      : "v"(t[0]), "v"(t[1]), "v"(a0q[0]), "v"(a0q[1]), "s"(c8));
+  // planes 3 and 7 (imaginary parts, over 8): -a2/8 - (c/8) v and a2/8 - (c/8) v, or their negatives
   if constexpr (!kConj) {
     asm volatile(
         "v_fma_mixlo_f16 %0, %2, -%6, -%4 op_sel_hi:[0,0,0]\n\t"
@@ -573,7 +613,7 @@ __device__ __forceinline__ void dft8_f16_pair(const u32x4& x, const u32x4& y, ui
         "v_fma_mixlo_f16 %1, %2, -%6, %4 op_sel_hi:[0,0,0]\n\t"
         "v_fma_mixhi_f16 %1, %3, -%6, %5 op_sel_hi:[0,0,0]"
         : "=&v"(o[3]), "=&v"(o[7])
-        : "v"(v[0]), "v"(v[1]), "v"(a[0][2]), "v"(a[1][2]), "v"(c));
+        : "v"(v[0]), "v"(v[1]), "v"(a2q[0]), "v"(a2q[1]), "s"(c8));
   } else {
     asm volatile(
         "v_fma_mixlo_f16 %0, %2, %6, %4 op_sel_hi:[0,0,0]\n\t"
@@ -581,7 +621,7 @@ __device__ __forceinline__ void dft8_f16_pair(const u32x4& x, const u32x4& y, ui
         "v_fma_mixlo_f16 %1, %2, %6, -%4 op_sel_hi:[0,0,0]\n\t"
         "v_fma_mixhi_f16 %1, %3, %6, -%5 op_sel_hi:[0,0,0]"
         : "=&v"(o[3]), "=&v"(o[7])
-        : "v"(v[0]), "v"(v[1]), "v"(a[0][2]), "v"(a[1][2]), "v"(c));
+        : "v"(v[0]), "v"(v[1]), "v"(a2q[0]), "v"(a2q[1]), "s"(c8));
   }
 }
 
@@ -634,9 +674,10 @@ __device__ __forceinline__ void pieces_to_planes(const u32x4 (&pc)[Grp<G>::kOrde
       if constexpr (sizeof(E) == 4) {
         pl[p] = __builtin_bit_cast(u32x4, f32x4{f[0][p], f[1][p], f[2][p], f[3][p]});
       } else {
+        // scaled into the f16 operand range (Grp<G>::kF16Scale, exact)
         f16x8 o;
 #pragma unroll
-        for (int v = 0; v < 8; ++v) o[v] = (_Float16)f[v][p];
+        for (int v = 0; v < 8; ++v) o[v] = (_Float16)(f[v][p] * Grp<G>::kF16Scale[p]);
         pl[p] = __builtin_bit_cast(u32x4, o);
       }
     }
@@ -836,21 +877,26 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[Grp<G>::kOrder]
               : kOob;
       if constexpr (sizeof(E) == 2 && G == 4) {
         if (act == 0 && res == nullptr) {
-          // f16 p4 without activation: a = F0 + F2 and b = F0 - F2 in float32,
-          // a / 4 + bias and b / 4 + bias, then each output is one mixed-
-          // precision FMA (+- Re F1 / 2 or +- Im F1 / 2) rounded once into
-          // its half of the packed store
+          // f16 p4 without activation: the accumulators hold F0/16, F2/16
+          // and F1/4 (the operand scales), so with a = F0 + F2 and
+          // b = F0 - F2 in float32, a / 4 + bias and b / 4 + bias are
+          // 4 (acc0 +- acc2) + bias; then each output is one mixed-precision
+          // FMA (+- Re F1 / 2 or +- Im F1 / 2, i.e. +- 2 acc) rounded once
+          // into its half of the packed store
+          static_assert(f16_unscale<4>(0) == 16.f && f16_unscale<4>(1) == 16.f && f16_unscale<4>(2) == 4.f &&
+                            f16_unscale<4>(3) == 4.f,
+                        "p4 f16 accumulator scales");
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float f0 = acc[0][fm][fn][r], f2 = acc[1][fm][fn][r];
             const float f1r = acc[2][fm][fn][r], f1i = acc[3][fm][fn][r];
-            const float qa = __builtin_fmaf(f0 + f2, 0.25f, bm), qb = __builtin_fmaf(f0 - f2, 0.25f, bm);
+            const float qa = __builtin_fmaf(f0 + f2, 4.0f, bm), qb = __builtin_fmaf(f0 - f2, 4.0f, bm);
             uint32_t w0, w1;
             asm volatile(
-                "v_fma_mixlo_f16 %0, %2, 0.5, %3 op_sel_hi:[0,0,0]\n\t"
-                "v_fma_mixhi_f16 %0, %4, -0.5, %5 op_sel_hi:[0,0,0]\n\t"
-                "v_fma_mixlo_f16 %1, %2, -0.5, %3 op_sel_hi:[0,0,0]\n\t"
-                "v_fma_mixhi_f16 %1, %4, 0.5, %5 op_sel_hi:[0,0,0]"
+                "v_fma_mixlo_f16 %0, %2, 2.0, %3 op_sel_hi:[0,0,0]\n\t"
+                "v_fma_mixhi_f16 %0, %4, -2.0, %5 op_sel_hi:[0,0,0]\n\t"
+                "v_fma_mixlo_f16 %1, %2, -2.0, %3 op_sel_hi:[0,0,0]\n\t"
+                "v_fma_mixhi_f16 %1, %4, 2.0, %5 op_sel_hi:[0,0,0]"
                 : "=&v"(w0), "=&v"(w1)
                 : "v"(f1r), "v"(qa), "v"(f1i), "v"(qb));
             __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, dst,
@@ -862,8 +908,9 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[Grp<G>::kOrder]
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float f[T], y[T];
+        // f16: undo the operand scales (exact powers of two)
 #pragma unroll
-        for (int p = 0; p < T; ++p) f[p] = acc[p][fm][fn][r];
+        for (int p = 0; p < T; ++p) f[p] = sizeof(E) == 2 ? acc[p][fm][fn][r] * f16_unscale<G>(p) : acc[p][fm][fn][r];
         Grp<G>::idft(f, y);
         if (bias != nullptr) {
 #pragma unroll
@@ -1599,12 +1646,16 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
         if constexpr (sizeof(E) == 4) {
           st16(plane0 + p * PLANE + off, __builtin_bit_cast(u32x4, f32x4{f[0][e][p], f[1][e][p], f[2][e][p], f[3][e][p]}));
         } else if constexpr (KV == 4) {
-          const f16x4 hv = {(_Float16)f[0][e][p], (_Float16)f[1][e][p], (_Float16)f[2][e][p], (_Float16)f[3][e][p]};
+          // f16: scaled into the operand range (Grp<G>::kF16Scale, exact)
+          const float sc = Grp<G>::kF16Scale[p];
+          const f16x4 hv = {(_Float16)(f[0][e][p] * sc), (_Float16)(f[1][e][p] * sc), (_Float16)(f[2][e][p] * sc),
+                            (_Float16)(f[3][e][p] * sc)};
           *reinterpret_cast<u32x2*>(plane0 + p * PLANE + off) = __builtin_bit_cast(u32x2, hv);
         } else {
+          const float sc = Grp<G>::kF16Scale[p];
           f16x8 hv;
 #pragma unroll
-          for (int v = 0; v < 8; ++v) hv[v] = (_Float16)f[v][e][p];
+          for (int v = 0; v < 8; ++v) hv[v] = (_Float16)(f[v][e][p] * sc);
           st16(plane0 + p * PLANE + off, __builtin_bit_cast(u32x4, hv));
         }
       }
@@ -1787,7 +1838,10 @@ bwd_fused_kernel(const E* __restrict__ dy, const E* __restrict__ x, const E* __r
 // R (a power of two, T R <= 256) is set by the host from the entry and split
 // counts alone (dw_finalize_parts), so a given call always adds in the same
 // order; R = 1 is the plain split-order sum.  nsplit == 0 writes zeros.
-template <int G>
+// kF16: the partials are products of f16 operands, which carry the operand
+// scales (Grp<G>::kF16Scale); they are multiplied back out before the
+// inverse DFT.
+template <int G, bool kF16>
 __global__ void __launch_bounds__(kThreads)
 dw_finalize_kernel(const float* __restrict__ ws, float* __restrict__ dw, int mg, int ng, int nsplit, int R) {
   constexpr int T = Grp<G>::kOrder;
@@ -1825,7 +1879,7 @@ dw_finalize_kernel(const float* __restrict__ ws, float* __restrict__ dw, int mg,
   if (t < EB && idx < plane) {
     float f[T], y[T];
 #pragma unroll
-    for (int k = 0; k < T; ++k) f[k] = red[k * EB + t];
+    for (int k = 0; k < T; ++k) f[k] = kF16 ? red[k * EB + t] * f16_unscale<G>(k) : red[k * EB + t];
     Grp<G>::idft(f, y);
     store_group<float, T>(dw + idx * T, y);
   }
@@ -1844,7 +1898,7 @@ inline int dw_finalize_parts(int64_t entries, int T, int nsplit) {
   return R;
 }
 
-template <int G>
+template <typename E, int G>
 hipError_t launch_dw_finalize(const float* ws, float* dw, int mg, int ng, int nsplit, hipStream_t s) {
   constexpr int T = Grp<G>::kOrder;
   const int64_t entries = (int64_t)mg * ng;
@@ -1852,7 +1906,8 @@ hipError_t launch_dw_finalize(const float* ws, float* dw, int mg, int ng, int ns
   const int64_t grid = (entries + kThreads / (T * R) - 1) / (kThreads / (T * R));
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (grid > 0)
-    hipLaunchKernelGGL((dw_finalize_kernel<G>), dim3((unsigned)grid), dim3(kThreads), 0, s, ws, dw, mg, ng, nsplit, R);
+    hipLaunchKernelGGL((dw_finalize_kernel<G, sizeof(E) == 2>), dim3((unsigned)grid), dim3(kThreads), 0, s, ws, dw, mg,
+                       ng, nsplit, R);
   return hipGetLastError();
 }
 
@@ -1893,9 +1948,10 @@ __device__ __forceinline__ void prepare_entry(const E* __restrict__ w, E* __rest
     Grp<G>::dft(z, f);
     if (kTranspose) Grp<G>::adjoint(f);
   }
+  // f16: scaled into the operand range of the f16 products (Grp<G>::kF16Scale)
   E* o = dst + (row * nks + ks) * T * SG + s;
 #pragma unroll
-  for (int p = 0; p < T; ++p) o[p * SG] = (E)f[p];
+  for (int p = 0; p < T; ++p) o[p * SG] = (E)(sizeof(E) == 2 ? f[p] * Grp<G>::kF16Scale[p] : f[p]);
 }
 
 template <typename E, int G>
@@ -1967,7 +2023,7 @@ hipError_t launch_dw_t(const void* dy, const void* x, float* ws, float* dw, int6
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_dw_finalize<G>(ws, dw, mg, ng, nsplit, s);
+  return launch_dw_finalize<E, G>(ws, dw, mg, ng, nsplit, s);
 }
 
 template <typename E, int G>
@@ -1993,7 +2049,7 @@ hipError_t launch_bwd_fused_t(const void* dy, const void* x, const void* wb, voi
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_dw_finalize<G>(ws, dw, dg, cg, nsplit, s);
+  return launch_dw_finalize<E, G>(ws, dw, dg, cg, nsplit, s);
 }
 
 template <typename E, int G>

@@ -125,6 +125,15 @@ def _need_cuda(t: torch.Tensor, name: str) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _check_out(t: torch.Tensor, name: str, shape: tuple, dtype: torch.dtype) -> None:
+    """A caller-supplied output: the C ABI takes no output size, so a wrong
+    shape or dtype would be written past the buffer; refuse it before any
+    launch."""
+    _need_cuda(t, name)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {list(shape)} of dtype {dtype}, got {list(t.shape)} of {t.dtype}")
+
+
 def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
@@ -201,9 +210,7 @@ def eqlin_forward(X: torch.Tensor, W_hat: Prepared, out: Optional[torch.Tensor] 
     N = X.shape[0]
     if out is None:
         out = torch.empty((N, W_hat.D), dtype=X.dtype, device=X.device)
-    _need_cuda(out, "out")
-    if tuple(out.shape) != (N, W_hat.D) or out.dtype != X.dtype:
-        raise ValueError("out has the wrong shape or dtype")
+    _check_out(out, "out", (N, W_hat.D), X.dtype)
     _check("eqlin_forward", lib.eqlin_forward(_ptr(X), N, W_hat.C, W_hat.D, W_hat.T, _ptr(W_hat.buf), _ptr(out),
                                               dt, _stream(X)))
     return out
@@ -236,7 +243,7 @@ def eqlin_forward_ex(X: torch.Tensor, W_hat: Prepared, bias: Optional[torch.Tens
             raise ValueError(f"residual must be [{N}, {W_hat.D}] of dtype {X.dtype}")
     if out is None:
         out = torch.empty((N, W_hat.D), dtype=X.dtype, device=X.device)
-    _need_cuda(out, "out")
+    _check_out(out, "out", (N, W_hat.D), X.dtype)
     if residual is None:
         _check("eqlin_forward_ex", lib.eqlin_forward_ex(_ptr(X), N, W_hat.C, W_hat.D, W_hat.T, _ptr(W_hat.buf),
                                                         _ptr(bias), ACT[act], _ptr(out), dt, _stream(X)))
@@ -269,7 +276,7 @@ def eqlin_backward(dY: torch.Tensor, X: Optional[torch.Tensor], W_hat: Prepared,
     dX = dw = None
     if need_dx:
         dX = dX_out if dX_out is not None else torch.empty((N, C), dtype=dY.dtype, device=dY.device)
-        _need_cuda(dX, "dX")
+        _check_out(dX, "dX_out", (N, C), dY.dtype)
     ws_bytes = 0
     if need_dw:
         if X is None:
@@ -279,7 +286,7 @@ def eqlin_backward(dY: torch.Tensor, X: Optional[torch.Tensor], W_hat: Prepared,
             raise ValueError(f"X must be [N, {C}] of dtype {dY.dtype}")
         dw = dw_out if dw_out is not None else torch.empty((D // n, C // n, n), dtype=torch.float32,
                                                            device=dY.device)
-        _need_cuda(dw, "dw")
+        _check_out(dw, "dw_out", (D // n, C // n, n), torch.float32)
         ws_bytes = int(lib.eqlin_backward_workspace_bytes(N, C, D, T, dt))
         if workspace is None:
             workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dY.device)
@@ -303,7 +310,7 @@ def eqlin_backward_dx(dY: torch.Tensor, W_hat: Prepared, out: Optional[torch.Ten
     N = dY.shape[0]
     if out is None:
         out = torch.empty((N, C), dtype=dY.dtype, device=dY.device)
-    _need_cuda(out, "out")
+    _check_out(out, "out", (N, C), dY.dtype)
     _check("eqlin_backward_dx", lib.eqlin_backward_dx(_ptr(dY), N, C, D, W_hat.T, _ptr(W_hat.buf), _ptr(out), dt,
                                                       _stream(dY)))
     return out
@@ -323,7 +330,7 @@ def eqlin_backward_dw(dY: torch.Tensor, X: torch.Tensor, workspace: Optional[tor
     n = group_order(T)
     if out is None:
         out = torch.empty((D // n, C // n, n), dtype=torch.float32, device=dY.device)
-    _need_cuda(out, "out")
+    _check_out(out, "out", (D // n, C // n, n), torch.float32)
     ws_bytes = int(lib.eqlin_backward_workspace_bytes(N, C, D, T, dt))
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dY.device)
@@ -386,9 +393,7 @@ def eqconv_forward(X: torch.Tensor, P: ConvPrepared, bias: Optional[torch.Tensor
     N, H, W = X.shape[:3]
     if out is None:
         out = torch.empty((N, H, W, P.D), dtype=X.dtype, device=X.device)
-    _need_cuda(out, "out")
-    if tuple(out.shape) != (N, H, W, P.D) or out.dtype != X.dtype:
-        raise ValueError("out has the wrong shape or dtype")
+    _check_out(out, "out", (N, H, W, P.D), X.dtype)
     _check("eqconv_forward", lib.eqconv_forward(_ptr(X), N, H, W, P.C, P.D, P.K, _ptr(P.buf), _ptr(bias), ACT[act],
                                                 _ptr(out), dt, _stream(X)))
     return out

@@ -80,6 +80,40 @@ def make_layer_inputs(N: int, C: int, D: int, dtype: str = "f32", seed: int = 0,
     return X, w, dY
 
 
+# f16 range cases: values at the top of binary16 (|x| in [3e4, 6e4], the
+# largest finite value being 65504) and just above its smallest normal
+# (|x| in [2^-14, 2^-12]).  Within every group of T channels of the first
+# half of the group channels all T values share one sign, so that a sum of
+# the T values (the zero frequency of a group transform) reaches T max|x|;
+# the other half draw their signs independently.  Weights are scaled so that
+# the exact outputs stay finite in binary16: large regime w ~ U(-1, 1) /
+# max(C, D) (every output is a sum of at most max(C, D) terms of |w x| <
+# 6e4 / max(C, D)), small regime w ~ U(-1, 1).
+RANGE_REGIMES = {"large": (3.0e4, 6.0e4), "small": (2.0 ** -14, 2.0 ** -12)}
+
+
+def _range_values(rng, shape, T, lo, hi):
+    mag = rng.uniform(lo, hi, size=shape)
+    n, cg = shape[0], shape[1] // T
+    sign = rng.choice([-1.0, 1.0], size=shape).reshape(n, cg, T)
+    coherent = rng.choice([-1.0, 1.0], size=(n, cg, 1))
+    sign[:, : cg // 2, :] = coherent[:, : cg // 2, :]
+    return mag * sign.reshape(shape)
+
+
+def make_range_inputs(N: int, C: int, D: int, regime: str, seed: int = 0, T: int = T_P4):
+    """f16 (X [N][C], w [D/T][C/T][T], dY [N][D]) at one end of the binary16 range (RANGE_REGIMES)."""
+    if C % T or D % T:
+        raise ValueError("C and D must be multiples of T")
+    lo, hi = RANGE_REGIMES[regime]
+    rng = np.random.default_rng([seed, 7])
+    X = _range_values(rng, (N, C), T, lo, hi).astype(np.float16)
+    wscale = 1.0 / max(C, D) if regime == "large" else 1.0
+    w = (rng.uniform(-1.0, 1.0, size=(D // T, C // T, T)) * wscale).astype(np.float16)
+    dY = _range_values(rng, (N, D), T, lo, hi).astype(np.float16)
+    return X, w, dY
+
+
 def workload_inputs(name: str, dtype: str | None = None, seed: int = 0, with_dy: bool = True):
     """Inputs for every layer of a named workload: list of (Layer, X, w, dY)."""
     wl = WORKLOADS[name]
@@ -132,4 +166,21 @@ def make_conv_inputs(N: int, H: int, W: int, C: int, D: int, K: int, dtype: str 
     X = rng.standard_normal((N, H, W, C)).astype(npdt)
     psi = (rng.standard_normal((D // 4, C // 4, K, K, 4)) / np.sqrt(C * K * K)).astype(npdt)
     dY = rng.standard_normal((N, H, W, D)).astype(npdt) if with_dy else None
+    return X, psi, dY
+
+
+def make_conv_range_inputs(N: int, H: int, W: int, C: int, D: int, K: int, regime: str, seed: int = 0):
+    """f16 (X [N][H][W][C], psi [D/4][C/4][K][K][4], dY [N][H][W][D]) at one end of the binary16
+    range, drawn as make_range_inputs draws a layer over the N H W pixels (equal-sign groups of
+    rotations in the first half of the group channels); psi ~ U(-1, 1) / max(C K^2, D K^2) in the
+    large regime (every output a sum of at most that many terms), U(-1, 1) in the small one."""
+    if C % 4 or D % 4:
+        raise ValueError("C and D must be multiples of 4")
+    lo, hi = RANGE_REGIMES[regime]
+    rng = np.random.default_rng([seed, 8])
+    P = N * H * W
+    X = _range_values(rng, (P, C), 4, lo, hi).astype(np.float16).reshape(N, H, W, C)
+    scale = 1.0 / (max(C, D) * K * K) if regime == "large" else 1.0
+    psi = (rng.uniform(-1.0, 1.0, size=(D // 4, C // 4, K, K, 4)) * scale).astype(np.float16)
+    dY = _range_values(rng, (P, D), 4, lo, hi).astype(np.float16).reshape(N, H, W, D)
     return X, psi, dY

@@ -50,6 +50,25 @@
  *     float32, and outputs are rounded nearest-even to binary16.  dw is float32
  *     for both dtypes.  With EQLIN_F16 and T = 4, C' and D' must be
  *     even (otherwise EQLIN_ENOTSUP).
+ *   - f16 range.  A plane of a group transform can be as large as T times its
+ *     inputs (the zero frequency sums all T values of a group), so before the
+ *     rounding to binary16 every Fourier operand plane (of X, of dY and of the
+ *     prepared weights) is multiplied by a fixed power of two that keeps it
+ *     within the largest magnitude of its inputs; the exact inverse power is
+ *     applied to the float32 accumulators in the inverse transform.  The
+ *     summary's dyadic coefficients ("Specialisation for the p4 rotation
+ *     group", first bullet) allow the normalisation on either side.  Scales
+ *     per plane, in the plane order of eqlin_prepared_weight_bytes below:
+ *       f16 operand scales, T = 4: (1/4, 1/4, 1/2, 1/2)
+ *       f16 operand scales, T = 8: (1/8, 1/8, 1/8, 1/8, 1/4, 1/4, 1/8, 1/8)
+ *       f16 operand scales, EQLIN_P4M: (1/8, 1/8, 1/8, 1/8, 1/4, 1/4, 1/4, 1/4)
+ *     Consequences: every finite binary16 input (|x| <= 65504) gives finite
+ *     operands; an output is inf only where the exact result itself exceeds
+ *     the binary16 range (Y, dX; dw is float32).  At the small end a scaled
+ *     operand below 2^-14 is a binary16 subnormal (spacing 2^-24): an operand
+ *     plane whose inputs are near the smallest normal 2^-14 keeps an absolute
+ *     rounding error of at most 2^-25 per operand instead of a relative one.
+ *     float32 has no such scaling (its planes overflow only past about 8e37).
  *   - Every data pointer is a DEVICE pointer on the current HIP device, owned
  *     by the caller, 16-byte aligned (else EQLIN_EALIGN).  The library never
  *     allocates, frees or retains memory and keeps no mutable global state;
@@ -57,8 +76,11 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call only enqueues work on it and returns without synchronising.
  *   - All arguments are validated before any kernel is enqueued: on any error
- *     nothing is launched and no output is touched.  A launch failure reported
- *     by the HIP runtime returns EQLIN_EHIP (see eqlin_last_hip_error()).
+ *     nothing is launched and no output is touched.  A launch the device
+ *     cannot take returns EQLIN_EHIP and records the hipError_t for
+ *     eqlin_last_hip_error(): a launch error the HIP runtime reports, or a
+ *     grid beyond 2^31 - 1 workgroups (hipErrorInvalidConfiguration, refused
+ *     before anything of that launch is enqueued; e.g. more than 2^37 rows).
  *   - N == 0 is a valid empty batch: forward and dX enqueue nothing, dw is
  *     written as zeros.
  *   - Kernels address one tile (at most 256 rows) with 32-bit offsets: C and D
@@ -117,7 +139,8 @@ int eqlin_last_hip_error(void);
  *   T = 8: (F0, F4, Re F1, Im F1, Re F2, Im F2, Re F3, Im F3)
  * and the transpose set holds the same planes with every Im negated: the
  * spectrum of the transposed, group-reversed weight (a conjugate) used by
- * the dX pass.  For EQLIN_P4M the planes are w_hat(rho) = sum_u w(u) rho(u)
+ * the dX pass.  With EQLIN_F16 each plane is stored multiplied by its f16
+ * operand scale (see "f16 range" above).  For EQLIN_P4M the planes are w_hat(rho) = sum_u w(u) rho(u)
  * for the characters A1, A2, B1, B2 (r -> 1, 1, -1, -1; s -> 1, -1, 1, -1)
  * and the 2 x 2 representation E (r -> [[0,-1],[1,0]], s -> diag(1,-1)),
  * ordered (A1, A2, B1, B2, E00, E01, E10, E11); the transpose set holds the
@@ -218,26 +241,49 @@ int eqlin_forward_residual(const void* X, int64_t N, int C, int D, int T, const 
 size_t eqlin_backward_workspace_bytes(int64_t N, int C, int D, int T, int dtype);
 
 /*
- * a5 + a6: backward pass for upstream gradient dY [N][D].
+ * a5 + a6: backward pass for upstream gradient dY [N][D].  The summary's
+ * kernels cover the backward pass as well as the forward ("Implementation",
+ * first bullet: dedicated forward and backward kernels); its operator-level
+ * results report the backward speed-up beside the forward's ("Experimental
+ * results", "Operator level").  It gives no formulas for it: the two
+ * gradients below are plain calculus on the layer's definition ("Key
+ * insight"), computed through the same group DFT ("Algorithmic approach",
+ * items 1-2).
  *   dX [N][C] = dY W   (transposed group-circulant; skipped if dX == NULL)
  *   dw [D'][C'][T] (float32) = d<dY, Y>/dw
  *      = sum_n sum_t dY[n, T d'+t] X[n, T c' + (t-u) mod T]   (skipped if dw == NULL)
  *      (EQLIN_P4M: sum_n sum_h dY[n, 8 d' + h u] X[n, 8 c' + h])
- * dw is formed per frequency as sum_n G_k conj(Xhat_k) (G = group DFT of dY;
+ * dX runs the forward's fused structure on the transpose spectra; dw is
+ * formed per frequency as sum_n G_k conj(Xhat_k) (G = group DFT of dY;
  * for EQLIN_P4M per representation sum_n Xhat^T G), reduced over row splits
- * in a fixed order (deterministic) and inverse transformed along u.  `workspace` (device, >= eqlin_backward_workspace_bytes)
- * holds the per-split partial spectra; it may be NULL only when dw == NULL.
- * X may be NULL when dw == NULL.
+ * in a fixed order (deterministic) and inverse transformed along u.
+ * `workspace` (device, >= eqlin_backward_workspace_bytes) holds the
+ * per-split partial spectra; it may be NULL only when dw == NULL.
+ * X may be NULL when dw == NULL.  With both outputs asked for, dX and the dw
+ * partials run in one launch (both read dY), then the ordered finalize.
+ * Errors as for every entry point: EINVAL, ENOTSUP, EALIGN, EWORKSPACE
+ * (workspace_bytes too small), EHIP; both halves are validated before
+ * either is launched.
  */
 int eqlin_backward(const void* dY, const void* X, int64_t N, int C, int D, int T,
                    const void* W_hat, void* dX, float* dw,
                    void* workspace, size_t workspace_bytes, int dtype, void* stream);
 
-/* a5 alone: dX = dY W.  Same contract as eqlin_backward with dw == NULL. */
+/*
+ * a5 alone: dX = dY W (the transpose of the layer's circulant blocks: the
+ * backward of "Key insight"'s map, run as the forward structure of
+ * "Implementation", first bullet, on the transpose spectra).  Same contract
+ * as eqlin_backward with dw == NULL.
+ */
 int eqlin_backward_dx(const void* dY, int64_t N, int C, int D, int T,
                       const void* W_hat, void* dX, int dtype, void* stream);
 
-/* a6 alone: dw only.  Same contract as eqlin_backward with dX == NULL. */
+/*
+ * a6 alone: dw only, the weight gradient of "Key insight"'s map formed per
+ * frequency ("Algorithmic approach", items 1-2) as a row reduction over the
+ * batch ("Experimental results", "Operator level": the backward pass).  Same
+ * contract as eqlin_backward with dX == NULL.
+ */
 int eqlin_backward_dw(const void* dY, const void* X, int64_t N, int C, int D, int T,
                       float* dw, void* workspace, size_t workspace_bytes,
                       int dtype, void* stream);

@@ -264,3 +264,85 @@ def test_forward_plan_tiles_and_tail_split(lib, monkeypatch):
     assert _plan(lib, 16, 12, 16, 4, 1)[0] == ENOTSUP                             # odd C' with f16
     st = lib.eqlin_forward_plan(12608, 768, 768, 4, 0, None, None, None)
     assert st == OK
+
+
+# ------------------------------------------------------------ refused launches
+
+EHIP = 5
+HIP_ERROR_INVALID_CONFIGURATION = 9
+
+
+def test_refused_launch_returns_ehip(lib, monkeypatch):
+    # A grid the device cannot take (more than 2^31 - 1 workgroups) is refused
+    # by the launcher before anything of that launch is enqueued: the call
+    # returns EQLIN_EHIP and records hipErrorInvalidConfiguration.  2^38 rows
+    # of a 16-channel layer make 2^32 tiles of 64 rows.  The pointers are
+    # never dereferenced (no kernel is launched), so this holds with or
+    # without a GPU; only the one-workgroup-per-tile float32 tiles are used
+    # (a persistent tile's grid is the resident count, which would launch).
+    monkeypatch.delenv("EQLIN_FWD_TILE", raising=False)
+    N = 1 << 38
+    st, tile, tiles, _ = _plan(lib, N, 16, 16, 4, 0)
+    assert st == OK and tile < 1000000 and tiles > 0x7fffffff
+    assert lib.eqlin_forward(FAKE, N, 16, 16, 4, FAKE, FAKE, 0, None) == EHIP
+    assert lib.eqlin_last_hip_error() == HIP_ERROR_INVALID_CONFIGURATION
+    assert lib.eqlin_backward_dx(FAKE, N, 16, 16, 4, FAKE, FAKE, 0, None) == EHIP
+    ws = lib.eqlin_backward_workspace_bytes(N, 16, 16, 4, 0)
+    assert ws > 0
+    assert lib.eqlin_backward(FAKE, FAKE, N, 16, 16, 4, FAKE, FAKE, FAKE, FAKE, ws, 0, None) == EHIP
+    assert lib.eqlin_last_hip_error() == HIP_ERROR_INVALID_CONFIGURATION
+    # the binding turns the status into an exception naming the HIP error
+    with pytest.raises(eqlin.EqlinError, match="EQLIN_EHIP.*hipError 9"):
+        eqlin._check("eqlin_forward", lib.eqlin_forward(FAKE, N, 16, 16, 4, FAKE, FAKE, 0, None))
+
+
+# ------------------------------------------------------- binding output checks
+
+class _RecordingLib:
+    """Stands in for libeqlin.so: size queries answer 1, every other entry
+    point records that it was called (and would have enqueued work)."""
+
+    def __init__(self):
+        self.calls = []
+
+    def __getattr__(self, name):
+        def fn(*args):
+            if not name.endswith(("_bytes", "_offset")):
+                self.calls.append(name)
+            return 1 if name.endswith(("_bytes", "_offset")) else 0
+        return fn
+
+
+def test_binding_rejects_wrong_outputs_before_any_launch(monkeypatch):
+    # the C ABI takes no output sizes: an output tensor of the wrong shape or
+    # dtype must be refused in Python, before the library is called
+    torch = pytest.importorskip("torch")
+    fake = _RecordingLib()
+    monkeypatch.setattr(eqlin, "load_library", lambda path=None: fake)
+    monkeypatch.setattr(eqlin, "_need_cuda", lambda t, name: None)
+    monkeypatch.setattr(eqlin, "_stream", lambda t: 0)
+    N, C, D = 16, 32, 48
+    f32, f16 = torch.float32, torch.float16
+    W = eqlin.Prepared(torch.zeros(64, dtype=torch.uint8), C, D, f32, 4)
+    X, dY = torch.zeros(N, C), torch.zeros(N, D)
+    cases = [
+        lambda: eqlin.eqlin_forward(X, W, out=torch.zeros(N, D - 4)),
+        lambda: eqlin.eqlin_forward(X, W, out=torch.zeros(N, D, dtype=f16)),
+        lambda: eqlin.eqlin_forward_ex(X, W, None, "gelu", out=torch.zeros(N - 1, D)),
+        lambda: eqlin.eqlin_forward_ex(X, W, None, "none", out=torch.zeros(N, D, dtype=f16)),
+        lambda: eqlin.eqlin_backward(dY, X, W, dX_out=torch.zeros(N, C + 4)),
+        lambda: eqlin.eqlin_backward(dY, X, W, dX_out=torch.zeros(N, C, dtype=f16)),
+        lambda: eqlin.eqlin_backward(dY, X, W, dw_out=torch.zeros(D // 4, C // 4, 4, dtype=f16)),
+        lambda: eqlin.eqlin_backward(dY, X, W, dw_out=torch.zeros(D // 4, C // 4)),
+        lambda: eqlin.eqlin_backward_dx(dY, W, out=torch.zeros(N, D)),
+        lambda: eqlin.eqlin_backward_dw(dY, X, out=torch.zeros(C // 4, D // 4, 4)),
+        lambda: eqlin.eqlin_backward_dw(dY, X, out=torch.zeros(D // 4, C // 4, 4, dtype=torch.float64)),
+    ]
+    for i, case in enumerate(cases):
+        with pytest.raises(ValueError):
+            case()
+        assert fake.calls == [], (i, fake.calls)
+    # correctly shaped outputs reach the library
+    eqlin.eqlin_forward(X, W, out=torch.zeros(N, D))
+    eqlin.eqlin_backward(dY, X, W, dX_out=torch.zeros(N, C), dw_out=torch.zeros(D // 4, C // 4, 4))
+    assert fake.calls == ["eqlin_forward", "eqlin_backward"]

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from group_circulant_linear_amd.inputs import CONV_WORKLOADS, make_conv_inputs
+from group_circulant_linear_amd.inputs import CONV_WORKLOADS, make_conv_inputs, make_conv_range_inputs
 
 torch = pytest.importorskip("torch")
 eq = pytest.importorskip("group_circulant_linear_amd.eqlin")
@@ -249,3 +249,23 @@ def test_module_autograd_matches_oracle(dt):
         m.psi.mul_(2.0)
     Y2 = m(X.detach())
     assert rel_err(host(Y2.detach()), 2.0 * oracle.conv_forward(Xn, psi)) < tol
+
+
+@pytest.mark.parametrize("regime", ["large", "small"])
+def test_f16_operand_range(regime):
+    # binary16 inputs up to 6e4 (rotation groups of equal sign, whose plain
+    # zero-frequency sums pass 65504) and just above the smallest normal; the
+    # f16 Fourier operands are scaled into range before rounding
+    N, H, W, C, D, K = 2, 9, 11, 32, 64, 3
+    say(f"conv f16 range {regime}")
+    X, psi, dY = make_conv_range_inputs(N, H, W, C, D, K, regime, seed=3)
+    Yr, dXr, dpr = oracle.conv_forward(X, psi), oracle.conv_dx(dY, psi, H, W), oracle.conv_dw(dY, X, K)
+    assert np.max(np.abs(Yr)) < 65504 and np.max(np.abs(dXr)) < 65504
+    P = eq.eqconv_prepare_weights(dev(psi))
+    Y = host(eq.eqconv_forward(dev(X), P))
+    dX, dpsi = eq.eqconv_backward(dev(dY), dev(X), P)
+    dX, dpsi = host(dX), host(dpsi)
+    errs = (rel_err(Y, Yr), rel_err(dX, dXr), rel_err(dpsi, dpr))
+    say(f"  Y {errs[0]:.2e}  dX {errs[1]:.2e}  dpsi {errs[2]:.2e}")
+    assert all(np.all(np.isfinite(a)) for a in (Y, dX, dpsi))
+    assert max(errs) <= TOL["f16"], errs

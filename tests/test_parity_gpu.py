@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
-from group_circulant_linear_amd.inputs import WORKLOADS, make_layer_inputs
+from group_circulant_linear_amd.inputs import WORKLOADS, make_layer_inputs, make_range_inputs
 
 torch = pytest.importorskip("torch")
 eq = pytest.importorskip("group_circulant_linear_amd.eqlin")
@@ -87,6 +87,12 @@ def test_slot_group_formula_matches_header_for_p4():
             assert sorted(slot_group(s, dt, T) for s in range(S)) == list(range(S))
 
 
+# per-plane scales of the f16 Fourier operands, as include/eqlin.h states them
+F16_PLANE_SCALE = {4: [1 / 4, 1 / 4, 1 / 2, 1 / 2],
+                   8: [1 / 8, 1 / 8, 1 / 8, 1 / 8, 1 / 4, 1 / 4, 1 / 8, 1 / 8],
+                   "p4m": [1 / 8, 1 / 8, 1 / 8, 1 / 8, 1 / 4, 1 / 4, 1 / 4, 1 / 4]}
+
+
 def decode_planes(flat, rows, groups, dt, T):
     """[rows][ceil(groups/S)][T][S] stage blocks -> [rows][groups][T]; checks zero padding."""
     S = 16 if dt == "f32" else 32
@@ -127,6 +133,10 @@ def test_prepared_planes_match_group_spectrum(g, dt, Dp, Cp):
         ref = oracle.kept_planes(w.astype(np.float64))
         adj = ref.copy()
         adj[..., 3::2] = -adj[..., 3::2]      # imaginary planes
+    if dt == "f16":
+        # f16 planes are stored scaled into the operand range (include/eqlin.h)
+        sc = np.array(F16_PLANE_SCALE[g])
+        ref, adj = ref * sc, adj * sc
     assert rel_err(wf, ref) < tol
     assert rel_err(wb, adj.transpose(1, 0, 2)) < tol
 
@@ -266,13 +276,15 @@ def _sample_rows(N, rng, k=96):
                                        ("vitb_mlp", "f16", "p4m"), ("vith_mlp", "f32", "p4m"),
                                        ("vith_mlp", "f16", "p4m"), ("narrow", "f32", 4), ("narrow", "f16", 4)])
 def test_forward_workloads(name, dt, g):
+    # the p4 workloads (the layer shapes the method is measured on) whole;
+    # the order-8 groups' largest layers on sampled rows (rows are independent)
     wl = WORKLOADS[name]
     for li, L in enumerate(wl.layers):
         say(f"forward workload {name} {L.name} {dt} group={g} N={L.N} C={L.C} D={L.D}")
         X, w, _ = make_layer_inputs(L.N, L.C, L.D, dt, seed=0, layer=li, T=order(g), with_dy=False)
         Wh = prep(w, g)
         Y = host(eq.eqlin_forward(dev(X), Wh))
-        if L.N * L.C * L.D <= 12608 * 768 * 768:
+        if g == 4 or L.N * L.C * L.D <= 12608 * 768 * 768:
             err = rel_err(Y, ref_forward(X, w, g))
         else:
             rows = _sample_rows(L.N, np.random.default_rng(li))
@@ -399,6 +411,33 @@ def test_determinism(dt, g):
     dX2, dw2 = eq.eqlin_backward(tdY, tX, Wh)
     torch.cuda.synchronize()
     assert torch.equal(Y1, Y2) and torch.equal(dX1, dX2) and torch.equal(dw1, dw2)
+
+
+@pytest.mark.parametrize("pair", [("112211", "112221"), ("111211", "111221"), ("112211", "112212"),
+                                  ("112411", "112412")])
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_lds_buffering_is_bitwise_invisible(dt, pair, monkeypatch):
+    """Race check: one fragment layout run single-buffered (NBUF = 1: two
+    barriers per stage, the stage stored into the buffer just read) and
+    double-buffered (NBUF = 2: one barrier, the next stage stored into the
+    other buffer while this one is read), or with one and with two stages of
+    global loads in flight, multiplies the same operands in the same order:
+    the outputs must agree bit for bit.  A missing wait or barrier shows up
+    as a difference."""
+    a, b = pair
+    shapes = [(1000, 160, 96), (333, 800, 520), (299 * 64 + 37, 4 * 42, 256)]
+    for (N, C, D) in shapes:
+        say(f"buffering {dt} tiles {a} / {b} N={N} C={C} D={D}")
+        X, w, _ = make_layer_inputs(N, C, D, dt, seed=24, with_dy=False)
+        Wh = prep(w, 4)
+        tX = dev(X)
+        out = {}
+        for tile in (a, b):
+            monkeypatch.setenv("EQLIN_FWD_TILE", tile)
+            out[tile] = eq.eqlin_forward(tX, Wh)
+        torch.cuda.synchronize()
+        assert torch.equal(out[a], out[b]), (N, C, D)
+        assert rel_err(host(out[a]), oracle.forward_direct(X, w)) <= TOL[dt]
 
 
 @pytest.mark.parametrize("g", GROUPS)
@@ -548,3 +587,57 @@ def test_forward_ex_mlp_block_vitb_f16_sampled():
     err2 = rel_err(Y[rows], oracle.forward_bias_act(Hh.astype(np.float16), w2, b2, "none"))
     say(f"  fc1 rel err {err1:.3e}  fc2 rel err {err2:.3e}")
     assert err1 <= 3e-3 and err2 <= 3e-3
+
+
+# ------------------------------------------- f16 range of the Fourier operands
+
+# The f16 route rounds every Fourier operand (transformed X, dY and the
+# prepared weights) to binary16.  A zero-frequency plane sums all T values of
+# a group, so each plane is scaled by a power of two that keeps it within
+# max|input| before the rounding: no finite input overflows an operand.
+# Inputs at |x| up to 6e4 (groups of equal sign, whose plain sums pass
+# 65504) and just above the smallest normal 2^-14; the exact outputs are
+# finite binary16 numbers (dw is float32).
+RANGE_SHAPES = {4: [(257, 160, 96), (1000, 64, 64)], 8: [(257, 320, 192)], "p4m": [(257, 320, 192)]}
+
+
+@pytest.mark.parametrize("regime", ["large", "small"])
+@pytest.mark.parametrize("g", GROUPS)
+def test_f16_operand_range(g, regime):
+    T = order(g)
+    for (N, C, D) in RANGE_SHAPES[g]:
+        say(f"f16 range {regime} group={g} N={N} C={C} D={D}")
+        X, w, dY = make_range_inputs(N, C, D, regime, seed=21, T=T)
+        Yr, dXr, dwr = ref_forward(X, w, g), ref_dx(dY, w, g), ref_dw(dY, X, g)
+        assert np.max(np.abs(Yr)) < 65504 and np.max(np.abs(dXr)) < 65504
+        Wh = prep(w, g)
+        tX, tdY = dev(X), dev(dY)
+        Y = host(eq.eqlin_forward(tX, Wh))
+        dX, dw = eq.eqlin_backward(tdY, tX, Wh)
+        dX, dw = host(dX), host(dw)
+        dX2 = host(eq.eqlin_backward_dx(tdY, Wh))
+        dw2 = host(eq.eqlin_backward_dw(tdY, tX, T=g))
+        errs = {"Y": rel_err(Y, Yr), "dX": rel_err(dX, dXr), "dw": rel_err(dw, dwr), "dX alone": rel_err(dX2, dXr),
+                "dw alone": rel_err(dw2, dwr)}
+        say("  " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+        for a in (Y, dX, dw, dX2, dw2):
+            assert np.all(np.isfinite(a))
+        assert max(errs.values()) <= TOL["f16"], errs
+
+
+@pytest.mark.parametrize("tile", ["212421", "122211", "112211", "111221", "2124211", "1121111"])
+def test_f16_operand_range_forward_tiles(tile, monkeypatch):
+    # every p4 f16 tile, with the bias + GELU epilogue (the general inverse
+    # transform) beside the plain one
+    monkeypatch.setenv("EQLIN_FWD_TILE", tile)
+    N, C, D = 333, 4 * 40, 4 * 70
+    X, w, _ = make_range_inputs(N, C, D, "large", seed=22)
+    b = (np.random.default_rng(23).uniform(-1e3, 1e3, size=D // 4)).astype(np.float16)
+    Wh = prep(w, 4)
+    Y = host(eq.eqlin_forward(dev(X), Wh))
+    Yg = host(eq.eqlin_forward_ex(dev(X), Wh, dev(b), "gelu"))
+    e1 = rel_err(Y, oracle.forward_direct(X, w))
+    e2 = rel_err(Yg, oracle.forward_bias_act(X, w, b, "gelu"))
+    say(f"  tile {tile}: Y {e1:.2e}  bias+GELU {e2:.2e}")
+    assert np.all(np.isfinite(Y)) and np.all(np.isfinite(Yg))
+    assert e1 <= TOL["f16"] and e2 <= TOL["f16"]
