@@ -63,6 +63,8 @@ def parse():
                    help="seconds of untimed steps before the warmup steps (GPU clock ramp)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--no-per-config", action="store_true",
+                   help="the headline line only (no per-configuration entries)")
     p.add_argument("--forward-only", action="store_true",
                    help="time only the forward (for profiling the forward kernel); not a valid bench line")
     p.add_argument("--mlp-block", action="store_true",
@@ -101,6 +103,17 @@ def layer_roofline(layers, es, T, exec_frac, peak_tflops):
     longer than the FLOPs at the MFMA peak, else "mfma"."""
     alg_bytes = sum(es * L.N * (L.C + L.D) + es * L.C * L.D / T for L in layers)
     exec_flops = 2.0 * exec_frac * sum(L.N * L.C * L.D for L in layers)
+    bound = "hbm" if alg_bytes / (HBM_PEAK_GBS * 1e9) > exec_flops / (peak_tflops * 1e12) else "mfma"
+    return bound, alg_bytes, exec_flops
+
+
+def backward_roofline(layers, es, T, exec_frac, peak_tflops):
+    """(bound, algorithmic bytes, executed FLOPs) of the backward (dX and dw) over
+    `layers`: X and dY read once, dX written once, the transpose spectra read
+    once, dw (float32, C D / T values) written once; executed FLOPs twice the
+    forward's (the dX and the dw products)."""
+    alg_bytes = sum(es * L.N * (2 * L.C + L.D) + es * L.C * L.D / T + 4 * L.C * L.D / T for L in layers)
+    exec_flops = 4.0 * exec_frac * sum(L.N * L.C * L.D for L in layers)
     bound = "hbm" if alg_bytes / (HBM_PEAK_GBS * 1e9) > exec_flops / (peak_tflops * 1e12) else "mfma"
     return bound, alg_bytes, exec_flops
 
@@ -401,26 +414,16 @@ def conv_bench(args):
     print(json.dumps(out), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "bench.py measures a single GPU; --gpus must be 1"}))
-        sys.exit(2)
-    if args.mlp_block:
-        mlp_block(args)
-        return
-    from group_circulant_linear_amd.inputs import CONV_WORKLOADS
-    if args.workload in CONV_WORKLOADS:
-        conv_bench(args)
-        return
-
+def run_linear(args, workload, dtype, group, with_cpu):
+    """One linear-layer workload: inputs to HBM, the timed steps, the dense
+    comparator; returns the bench dictionary (not printed)."""
     import torch
     from group_circulant_linear_amd import eqlin
     from group_circulant_linear_amd.inputs import WORKLOADS, make_layer_inputs
 
-    wl = WORKLOADS[args.workload]
-    dt = args.dtype or wl.dtypes[0]
-    G, T, exec_frac = group_args(args.group)
+    wl = WORKLOADS[workload]
+    dt = dtype or wl.dtypes[0]
+    G, T, exec_frac = group_args(group)
     tdt = torch.float32 if dt == "f32" else torch.float16
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -519,7 +522,7 @@ def main():
     peak = PEAK_TFLOPS[dt]
     es_b = 4 if dt == "f32" else 2
     bound, alg_bytes, _ = layer_roofline([L for (L, _, _, _) in layers], es_b, T, exec_frac, peak)
-    traffic = profiled_traffic(profile_tag(wl.name, dt, args.group), "eqlin::fwd_kernel") if len(layers) == 1 else None
+    traffic = profiled_traffic(profile_tag(wl.name, dt, group), "eqlin::fwd_kernel") if len(layers) == 1 else None
     gbs = alg_bytes / (fwd_us * 1e-6) / 1e9
     hbm_bound = bound == "hbm"
     roofline = {"bound": "hbm" if hbm_bound else "mfma", "kernel": "eqlin::fwd_kernel",
@@ -617,8 +620,26 @@ def main():
         roofline["copy_us"] = round(cp_us, 2)
         del cps
 
+    roofline_bwd = None
+    if not args.forward_only:
+        bwd_us = sum(ph_us["backward"])
+        bbound, bbytes, bflops = backward_roofline([L for (L, _, _, _) in layers], es_b, T, exec_frac, peak)
+        b_hbm = bbound == "hbm"
+        b_tf = bflops / (bwd_us * 1e-6) / 1e12
+        b_gbs = bbytes / (bwd_us * 1e-6) / 1e9
+        roofline_bwd = {"bound": bbound, "kernel": "eqlin::bwd_fused_kernel (+ dw finalize)",
+                        "achieved": round(b_gbs, 1) if b_hbm else round(b_tf, 2),
+                        "peak": HBM_PEAK_GBS if b_hbm else peak, "unit": "GB/s" if b_hbm else "TFLOP/s",
+                        "frac": round(b_gbs / HBM_PEAK_GBS if b_hbm else b_tf / peak, 4),
+                        "traffic": None, "traffic_algorithmic": round(bbytes), "flops_per_launch": bflops,
+                        "mfma_tflops": round(b_tf, 2), "mfma_frac": round(b_tf / peak, 4),
+                        "hbm_gbs": round(b_gbs, 1), "hbm_frac": round(b_gbs / HBM_PEAK_GBS, 4)}
+        if len(layers) == 1:
+            t = profiled_traffic(profile_tag(wl.name, dt, group), "eqlin::bwd_fused_kernel")
+            roofline_bwd["traffic"] = round(t) if t else None
+
     cpu = None
-    if not args.no_cpu_baseline:
+    if with_cpu:
         cpu = cpu_baseline(layers)
 
     out = {
@@ -627,17 +648,62 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
         "config": {"workload": wl.name, "description": wl.description, "dtype": dt,
                    "layers": [{"name": L.name, "N": L.N, "C": L.C, "D": L.D} for (L, _, _, _) in layers],
-                   "group": str(args.group), "T": T,
+                   "group": str(group), "T": T,
                    "step": ("prepare+forward" if args.forward_only else "prepare+forward+dX+dw"),
                    "buffer_sets": nsets},
         "fwd_mfma_frac": round(achieved / peak, 4),
         "roofline": roofline,
+        "roofline_backward": roofline_bwd,
         "cpu_baseline": cpu,
         "dense_gemm": dense,
         "per_layer": per_layer,
     }
     if args.forward_only:
         out["note"] = "forward-only profiling run, not a bench line"
+    del sets, prepared
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+# The configurations beside the headline (the ViT-B attention projection in
+# fp32), each with its own timing, roofline and dense comparison: the layer
+# shapes at which the method's speed-up is stated (large widths, ViT-H), the
+# f16 MLP pair and the backward of the attention shapes.
+PER_CONFIG = (("vith_mlp", "f32"), ("vith_mlp", "f16"), ("vitb_mlp", "f16"), ("vitb_attn_bwd", "f16"),
+              ("vitb_attn_bwd", "f32"))
+
+
+def config_summary(r):
+    """The per-configuration entry of the bench line."""
+    keys = ("value", "unit", "ms_per_step", "dtype", "fwd_mfma_frac", "roofline", "roofline_backward",
+            "dense_gemm", "per_layer")
+    d = {"workload": r["config"]["workload"], "description": r["config"]["description"]}
+    d.update({k: r[k] for k in keys})
+    d["metric"] = "forward dense-equivalent TFLOP/s (2NDC), summed over the layers"
+    return d
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "bench.py measures a single GPU; --gpus must be 1"}))
+        sys.exit(2)
+    if args.mlp_block:
+        mlp_block(args)
+        return
+    from group_circulant_linear_amd.inputs import CONV_WORKLOADS
+    if args.workload in CONV_WORKLOADS:
+        conv_bench(args)
+        return
+    out = run_linear(args, args.workload, args.dtype, args.group, not args.no_cpu_baseline)
+    headline = (args.workload == "vitb_attn" and args.dtype in (None, "f32") and str(args.group) == "4"
+                and not args.forward_only)
+    if headline and not args.no_per_config:
+        out["per_config"] = []
+        for (wl, dt) in PER_CONFIG:
+            print(f"# per-config {wl} {dt}", file=sys.stderr, flush=True)
+            out["per_config"].append(config_summary(run_linear(args, wl, dt, "4", False)))
     print(json.dumps(out), flush=True)
 
 

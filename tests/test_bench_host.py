@@ -27,3 +27,25 @@ def test_roofline_bound_of_the_workloads():
     assert _bound("narrow", "f32")[0] == "hbm"                        # 6 FLOP/B
     assert _bound("narrow", "f16")[0] == "hbm"
     assert _bound("vitb_attn", "f32", "8")[0] == "mfma"
+
+
+def test_backward_roofline_of_the_attention_shapes():
+    # dX and dw: X and dY read once, dX written once, the transpose spectra read once, dw (float32)
+    # written once; twice the forward's executed FLOPs
+    L = WORKLOADS["vitb_attn_bwd"].layers
+    _, T, frac = bench.group_args("4")
+    b16, n16, f16 = bench.backward_roofline(L, 2, T, frac, bench.PEAK_TFLOPS["f16"])
+    b32, n32, f32 = bench.backward_roofline(L, 4, T, frac, bench.PEAK_TFLOPS["f32"])
+    N, C, D = 12608, 768, 768
+    assert n16 == 2 * N * (2 * C + D) + 2 * C * D / 4 + 4 * C * D / 4
+    assert n32 == 4 * N * (2 * C + D) + 4 * C * D / 4 + 4 * C * D / 4
+    assert f16 == f32 == 1.5 * N * C * D
+    assert b16 == "hbm" and b32 == "mfma"     # 189 FLOP/B below the f16 ridge; 95 above the fp32 ridge of 20
+
+
+def test_per_config_entries_name_measured_workloads():
+    # every entry beside the headline is a linear workload the bench runs, in a dtype it declares
+    assert len(bench.PER_CONFIG) == len(set(bench.PER_CONFIG))
+    for name, dt in bench.PER_CONFIG:
+        assert name in WORKLOADS and dt in WORKLOADS[name].dtypes, (name, dt)
+    assert ("vith_mlp", "f32") in bench.PER_CONFIG and ("vith_mlp", "f16") in bench.PER_CONFIG
