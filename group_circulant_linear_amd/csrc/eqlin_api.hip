@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "eqconv.h"
 #include "eqlin.h"
 #include "eqlin_kernels.h"
@@ -206,12 +208,19 @@ DwPlan dw_plan_for(int64_t N, int C, int D, int dtype, int64_t want) {
   return p;
 }
 
+// No cap on the number of dw row splits (the caller's workspace is sized by
+// eqlin_backward_workspace_bytes).
+constexpr int64_t kAnySplits = INT64_MAX;
+
 // The dw launch (alone): a few 64 x 64 workgroups fit one CU; use two per CU
 // in total.  The workspace holds this plan's splits, the most of the two.
-DwPlan plan_dw(int64_t N, int C, int D, int O, int dtype, bool chunked = false) {
+// max_splits caps the splits asked for (a fixed-size scratch); the 32-bit
+// offset cap inside a split can still ask for more, which the callers check.
+DwPlan plan_dw(int64_t N, int C, int D, int O, int dtype, bool chunked = false, int64_t max_splits = kAnySplits) {
   const int ch = chunked ? dw_chunks(N, D / O, C / O, dtype) : 1;
   const int64_t tiles = cdiv(ch * D / O, 64) * cdiv(ch * C / O, 64);
-  DwPlan p = dw_plan_for(N / ch, ch * C, ch * D, dtype, (2 * eqlin::kNumCu) / tiles);
+  const int64_t want = (2 * eqlin::kNumCu) / tiles;
+  DwPlan p = dw_plan_for(N / ch, ch * C, ch * D, dtype, want < max_splits ? want : max_splits);
   p.chunks = ch;
   return p;
 }
@@ -226,10 +235,11 @@ DwPlan plan_dw(int64_t N, int C, int D, int O, int dtype, bool chunked = false) 
 // attention fp32 113 -> 104 us and f16 -4%, ViT-H f16 and C8 -2% to -6%;
 // the ViT-H fp32 layers (ratio 1.9) keep two per CU, where one per CU is 1%
 // (fc1) and 9% (fc2) slower.
-DwPlan plan_dw_fused(int64_t N, int C, int D, int O, int dtype) {
+DwPlan plan_dw_fused(int64_t N, int C, int D, int O, int dtype, int64_t max_splits = kAnySplits) {
   const int ch = dw_chunks(N, D / O, C / O, dtype);
   const int64_t tiles = cdiv(ch * D / O, 64) * cdiv(ch * C / O, 64);
-  DwPlan one = dw_plan_for(N / ch, ch * C, ch * D, dtype, eqlin::kNumCu / tiles);
+  const int64_t want = eqlin::kNumCu / tiles;
+  DwPlan one = dw_plan_for(N / ch, ch * C, ch * D, dtype, want < max_splits ? want : max_splits);
   one.chunks = ch;
   if (one.nsplit > 0) {
     const int64_t split_stages = cdiv(one.rows_per_split, eqlin::dw_rows_per_stage(dtype));
@@ -238,7 +248,18 @@ DwPlan plan_dw_fused(int64_t N, int C, int D, int O, int dtype) {
     const int64_t per_cu = O == 4 ? (dtype == EQLIN_F32 ? 3 : 2) : 1;
     if (4 * split_stages * per_cu * eqlin::kNumCu <= 7 * (dw_work + dx_work)) return one;
   }
-  return plan_dw(N, C, D, O, dtype, true);
+  return plan_dw(N, C, D, O, dtype, true, max_splits);
+}
+
+// Workspace bytes of the dw split partials (T planes of D' x C' float32 per
+// split) for the plan of at most max_splits splits.  The fused plan never
+// has more splits than this one (fewer splits asked for, the same offset cap).
+size_t dw_split_bytes(int C, int D, int O) {
+  return static_cast<size_t>(O) * static_cast<size_t>(C / O) * static_cast<size_t>(D / O) * sizeof(float);
+}
+size_t dw_workspace_need(int64_t N, int C, int D, int O, int dtype, int64_t max_splits) {
+  const DwPlan p = plan_dw(N, C, D, O, dtype, true, max_splits);
+  return static_cast<size_t>(p.nsplit) * dw_split_bytes(C, D, O);
 }
 
 // ------------------------------------------------ p4 group convolution
@@ -386,10 +407,7 @@ int eqlin_forward_residual(const void* X, int64_t N, int C, int D, int T, const 
 
 size_t eqlin_backward_workspace_bytes(int64_t N, int C, int D, int T, int dtype) {
   if (check_shape(N, C, D, T, dtype) != EQLIN_OK) return 0;
-  const int O = eqlin::group_order(T);
-  const DwPlan p = plan_dw(N, C, D, O, dtype, true);
-  return static_cast<size_t>(p.nsplit) * static_cast<size_t>(O) * static_cast<size_t>(C / O) *
-         static_cast<size_t>(D / O) * sizeof(float);
+  return dw_workspace_need(N, C, D, eqlin::group_order(T), dtype, kAnySplits);
 }
 
 int eqlin_backward_dx(const void* dY, int64_t N, int C, int D, int T, const void* W_hat, void* dX, int dtype,
@@ -409,8 +427,13 @@ int eqlin_backward_dx(const void* dY, int64_t N, int C, int D, int T, const void
                                           static_cast<hipStream_t>(stream))));
 }
 
-int eqlin_backward_dw(const void* dY, const void* X, int64_t N, int C, int D, int T, float* dw, void* workspace,
-                      size_t workspace_bytes, int dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// dw alone with at most max_splits row splits in the workspace.
+int backward_dw_impl(const void* dY, const void* X, int64_t N, int C, int D, int T, float* dw, void* workspace,
+                     size_t workspace_bytes, int dtype, void* stream, int64_t max_splits) {
   int st = check_shape(N, C, D, T, dtype);
   if (st != EQLIN_OK) return st;
   const int O = eqlin::group_order(T);
@@ -418,14 +441,15 @@ int eqlin_backward_dw(const void* dY, const void* X, int64_t N, int C, int D, in
   if (N > 0 && (!dY || !X || !workspace)) return EQLIN_EINVAL;
   if (!aligned16(dw)) return EQLIN_EALIGN;
   if (N > 0 && (!aligned16(dY) || !aligned16(X) || !aligned16(workspace))) return EQLIN_EALIGN;
-  if (workspace_bytes < eqlin_backward_workspace_bytes(N, C, D, T, dtype)) return EQLIN_EWORKSPACE;
-  const DwPlan p = plan_dw(N, C, D, O, dtype, true);
+  if (workspace_bytes < dw_workspace_need(N, C, D, O, dtype, max_splits)) return EQLIN_EWORKSPACE;
+  const DwPlan p = plan_dw(N, C, D, O, dtype, true, max_splits);
   return hip_status(EQLIN_BY_T(T, dw(dtype, dY, X, static_cast<float*>(workspace), dw, N, D / O, C / O,
                                      p.rows_per_split, p.nsplit, p.chunks, static_cast<hipStream_t>(stream))));
 }
 
-int eqlin_backward(const void* dY, const void* X, int64_t N, int C, int D, int T, const void* W_hat, void* dX,
-                   float* dw, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+// eqlin_backward with the dw row splits capped at max_splits.
+int backward_impl(const void* dY, const void* X, int64_t N, int C, int D, int T, const void* W_hat, void* dX,
+                  float* dw, void* workspace, size_t workspace_bytes, int dtype, void* stream, int64_t max_splits) {
   int st = check_shape(N, C, D, T, dtype);
   if (st != EQLIN_OK) return st;
   const int O = eqlin::group_order(T);
@@ -440,7 +464,7 @@ int eqlin_backward(const void* dY, const void* X, int64_t N, int C, int D, int T
     if (N > 0 && (!dY || !X || !workspace)) return EQLIN_EINVAL;
     if (!aligned16(dw)) return EQLIN_EALIGN;
     if (N > 0 && (!aligned16(dY) || !aligned16(X) || !aligned16(workspace))) return EQLIN_EALIGN;
-    if (workspace_bytes < eqlin_backward_workspace_bytes(N, C, D, T, dtype)) return EQLIN_EWORKSPACE;
+    if (workspace_bytes < dw_workspace_need(N, C, D, O, dtype, max_splits)) return EQLIN_EWORKSPACE;
   }
   // One fused launch for dX and the dw partials, except for f16 p4 layers of
   // 16 or fewer input groups: their dX runs faster as the forward's narrow
@@ -450,7 +474,7 @@ int eqlin_backward(const void* dY, const void* X, int64_t N, int C, int D, int T
   const bool narrow_f16 = dtype == EQLIN_F16 && O == 4 && C / O <= 16;
   if (dX && dw && N > 0 && use_fused_backward() && !narrow_f16) {
     // one launch for dX and the dw partials (they share dY), then the finalize
-    const DwPlan p = plan_dw_fused(N, C, D, O, dtype);
+    const DwPlan p = plan_dw_fused(N, C, D, O, dtype, max_splits);
     const char* wb = static_cast<const char*>(W_hat) + transpose_offset(C, D, O, dtype);
     return hip_status(EQLIN_BY_T(T, bwd_fused(dtype, dY, X, wb, dX, static_cast<float*>(workspace), dw, N, D / O,
                                               C / O, p.rows_per_split, p.nsplit, p.chunks,
@@ -460,8 +484,80 @@ int eqlin_backward(const void* dY, const void* X, int64_t N, int C, int D, int T
     st = eqlin_backward_dx(dY, N, C, D, T, W_hat, dX, dtype, stream);
     if (st != EQLIN_OK) return st;
   }
-  if (dw) return eqlin_backward_dw(dY, X, N, C, D, T, dw, workspace, workspace_bytes, dtype, stream);
+  if (dw) return backward_dw_impl(dY, X, N, C, D, T, dw, workspace, workspace_bytes, dtype, stream, max_splits);
   return EQLIN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int eqlin_backward_dw(const void* dY, const void* X, int64_t N, int C, int D, int T, float* dw, void* workspace,
+                      size_t workspace_bytes, int dtype, void* stream) {
+  return backward_dw_impl(dY, X, N, C, D, T, dw, workspace, workspace_bytes, dtype, stream, kAnySplits);
+}
+
+int eqlin_backward(const void* dY, const void* X, int64_t N, int C, int D, int T, const void* W_hat, void* dX,
+                   float* dw, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  return backward_impl(dY, X, N, C, D, T, W_hat, dX, dw, workspace, workspace_bytes, dtype, stream, kAnySplits);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------ allocation-free backward
+//
+// The dw split partials of eqlin_backward_noalloc live in this file-scope
+// device array: one copy per device, loaded with the library's code object
+// and held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: the kernels get the device address that
+// hipGetSymbolAddress returns, looked up once per device (with that device
+// current) and kept in g_scratch_addr.
+static __device__ __align__(256) unsigned char scratch[EQLIN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`.
+hipError_t scratch_address(void** addr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int eqlin_backward_noalloc(const void* dY, const void* X, int64_t N, int C, int D, int T, const void* W_hat,
+                           void* dX, float* dw, int dtype, void* stream) {
+  const int st = check_shape(N, C, D, T, dtype);
+  if (st != EQLIN_OK) return st;
+  if (!dw) return backward_impl(dY, X, N, C, D, T, W_hat, dX, dw, nullptr, 0, dtype, stream, kAnySplits);
+  // The splits are capped to what the scratch holds; a layer whose one
+  // split (T planes of D' x C' float32) does not fit is refused.
+  const int O = eqlin::group_order(T);
+  const int64_t max_splits = static_cast<int64_t>(EQLIN_NOALLOC_SCRATCH_BYTES / dw_split_bytes(C, D, O));
+  if (max_splits < 1 || dw_workspace_need(N, C, D, O, dtype, max_splits) > EQLIN_NOALLOC_SCRATCH_BYTES)
+    return EQLIN_EWORKSPACE;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return hip_status(e);
+  return backward_impl(dY, X, N, C, D, T, W_hat, dX, dw, ws, EQLIN_NOALLOC_SCRATCH_BYTES, dtype, stream,
+                       max_splits);
 }
 
 // ------------------------------------------------ p4 group convolution

@@ -86,6 +86,7 @@ def load_library(path: str = LIB) -> ctypes.CDLL:
                                    c_int, c_vp]),
         "eqlin_backward_dx": (c_int, [c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_int, c_vp]),
         "eqlin_backward_dw": (c_int, [c_vp, c_vp, c_i64, c_int, c_int, c_int, c_fp, c_vp, c_sz, c_int, c_vp]),
+        "eqlin_backward_noalloc": (c_int, [c_vp, c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_fp, c_int, c_vp]),
         "eqconv_prepared_weight_bytes": (c_sz, [c_int, c_int, c_int, c_int]),
         "eqconv_prepared_adjoint_offset": (c_sz, [c_int, c_int, c_int, c_int]),
         "eqconv_prepare_weights": (c_int, [c_vp, c_int, c_int, c_int, c_int, c_vp, c_sz, c_vp]),
@@ -297,6 +298,40 @@ def eqlin_backward(dY: torch.Tensor, X: Optional[torch.Tensor], W_hat: Prepared,
                               _ptr(dX), _ptr(dw), _ptr(workspace) if need_dw else None, ws_bytes, dt,
                               _stream(dY)))
     return dX, dw
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # EQLIN_NOALLOC_SCRATCH_BYTES
+
+
+def eqlin_backward_noalloc(dY: torch.Tensor, X: Optional[torch.Tensor], W_hat: Prepared,
+                           dX_out: Optional[torch.Tensor], dw_out: Optional[torch.Tensor] = None) -> None:
+    """eqlin_backward without a workspace, into caller-allocated outputs: the dw
+    split partials use the library's per-device static scratch (calls on one
+    device must not overlap).  dX_out [N][C] (storage dtype) or None, dw_out
+    [D/n][C/n][n] float32 or None.  The binding allocates nothing either."""
+    lib = load_library()
+    _need_cuda(dY, "dY")
+    dt = _dtype_code(dY)
+    if dY.dtype != W_hat.dtype:
+        raise TypeError("dY and the prepared weights differ in dtype")
+    C, D, T, n = W_hat.C, W_hat.D, W_hat.T, W_hat.order
+    if dY.dim() != 2 or dY.shape[1] != D:
+        raise ValueError(f"dY must have shape [N, {D}], got {tuple(dY.shape)}")
+    N = dY.shape[0]
+    if dX_out is None and dw_out is None:
+        raise ValueError("nothing to compute")
+    if dX_out is not None:
+        _check_out(dX_out, "dX_out", (N, C), dY.dtype)
+    if dw_out is not None:
+        if X is None:
+            raise ValueError("dw needs X")
+        _need_cuda(X, "X")
+        if X.dtype != dY.dtype or tuple(X.shape) != (N, C):
+            raise ValueError(f"X must be [N, {C}] of dtype {dY.dtype}")
+        _check_out(dw_out, "dw_out", (D // n, C // n, n), torch.float32)
+    _check("eqlin_backward_noalloc",
+           lib.eqlin_backward_noalloc(_ptr(dY), _ptr(X) if dw_out is not None else None, N, C, D, T,
+                                      _ptr(W_hat.buf), _ptr(dX_out), _ptr(dw_out), dt, _stream(dY)))
 
 
 def eqlin_backward_dx(dY: torch.Tensor, W_hat: Prepared, out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -71,8 +71,9 @@
  *     float32 has no such scaling (its planes overflow only past about 8e37).
  *   - Every data pointer is a DEVICE pointer on the current HIP device, owned
  *     by the caller, 16-byte aligned (else EQLIN_EALIGN).  The library never
- *     allocates, frees or retains memory and keeps no mutable global state;
- *     calls are thread-safe.  Outputs must not alias inputs.
+ *     allocates, frees or retains memory and keeps no mutable global state
+ *     (apart from eqlin_backward_noalloc's static scratch, see there); calls
+ *     are thread-safe.  Outputs must not alias inputs.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call only enqueues work on it and returns without synchronising.
  *   - All arguments are validated before any kernel is enqueued: on any error
@@ -287,6 +288,32 @@ int eqlin_backward_dx(const void* dY, int64_t N, int C, int D, int T,
 int eqlin_backward_dw(const void* dY, const void* X, int64_t N, int C, int D, int T,
                       float* dw, void* workspace, size_t workspace_bytes,
                       int dtype, void* stream);
+
+/* Bytes of the per-device scratch of eqlin_backward_noalloc (32 MiB). */
+#define EQLIN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * eqlin_backward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, outputs and errors as eqlin_backward, without the
+ * workspace: the dw split partials go to a scratch array inside the library
+ * (EQLIN_NOALLOC_SCRATCH_BYTES per device, a static device array that every
+ * device the library runs on holds until the process ends).  The call
+ * allocates and frees nothing.
+ *   - The row splits of the dw reduction are capped to what the scratch
+ *     holds (each split T x D' x C' float32 values).  Where the cap binds,
+ *     dw is summed in fewer, longer splits than eqlin_backward uses (the
+ *     same values to rounding; the p4 layers of the ViT-B and ViT-H shapes
+ *     are not capped and give the same bits as eqlin_backward).  A layer one split
+ *     of which does not fit (T D' C' > 8 Mi values) -> EQLIN_EWORKSPACE.
+ *   - Every call on a device shares that device's scratch, which keeps the
+ *     last call's partials; nothing in it needs clearing (every partial is
+ *     written before it is read).  Calls that overlap on one device (other
+ *     streams, other threads) race on the scratch: serialise them.
+ *   - dw == NULL needs no scratch (dX only, as eqlin_backward).
+ */
+int eqlin_backward_noalloc(const void* dY, const void* X, int64_t N, int C, int D, int T,
+                           const void* W_hat, void* dX, float* dw, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

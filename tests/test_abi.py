@@ -346,3 +346,16 @@ def test_binding_rejects_wrong_outputs_before_any_launch(monkeypatch):
     eqlin.eqlin_forward(X, W, out=torch.zeros(N, D))
     eqlin.eqlin_backward(dY, X, W, dX_out=torch.zeros(N, C), dw_out=torch.zeros(D // 4, C // 4, 4))
     assert fake.calls == ["eqlin_forward", "eqlin_backward"]
+
+
+def test_noalloc_backward_refuses_layers_beyond_its_scratch(lib):
+    # eqlin_backward_noalloc keeps its dw split partials in a static 32 MiB
+    # scratch; a layer one split of which (4 planes x D' x C' float32) does
+    # not fit is refused before any launch.  The pointers are placeholders
+    # that must never reach a kernel, so the size is checked here first: a
+    # layer whose split fits would be launched.
+    scratch = 32 << 20
+    assert eqlin.NOALLOC_SCRATCH_BYTES == scratch
+    C = D = 4 * 1456
+    assert 4 * (C // 4) * (D // 4) * 4 > scratch            # 33.9 MB: one split does not fit
+    assert lib.eqlin_backward_noalloc(FAKE, FAKE, 64, C, D, 4, FAKE, None, FAKE, 0, None) == EWORKSPACE
