@@ -173,7 +173,31 @@ struct DwPlan {
   int64_t rows_per_split;
   int nsplit;
   int chunks;
+  int width;   // dw partial tile: 64, or 128 (p4, whole rows)
 };
+
+// f16 p4 layers whose group-channel counts both reach 256 (the ViT-H MLP
+// layers): the backward runs as separate launches, dX through the forward's
+// tile choice (128 x 128 there, where the fused launch has 64 x 64) and dw
+// alone with the 128-wide tile.  Measured (ViT-H f16, MI355X): fc1 159 ->
+// 151 us, fc2 178 -> 155 us; the 128-wide dw alone 93 -> 88 us.  Smaller f16
+// layers and fp32 keep the fused launch (ViT-B attention f16 34 against 40
+// us separate, fp32 104 against 120 us).
+bool wide_f16_layer(int O, int mg, int ng, int dtype) {
+  return dtype == EQLIN_F16 && O == 4 && mg >= 256 && ng >= 256;
+}
+
+// Width of the stand-alone dw launch's tile: 64, or 128 for the wide f16 p4
+// layers read in whole rows; EQLIN_DW_WIDTH=64|128 overrides for p4 (read at
+// every call).
+int dw_width(int O, int chunks, int mg, int ng, int dtype) {
+  if (O != 4 || chunks != 1) return 64;
+  if (const char* e = getenv("EQLIN_DW_WIDTH")) {
+    const int w = atoi(e);
+    if (w == 64 || w == 128) return w;
+  }
+  return wide_f16_layer(O, mg, ng, dtype) ? 128 : 64;
+}
 
 // Row chunks of the dw reduction of a narrow fp32 layer: when both
 // group-channel counts are at most 16 (32), the rows are read as rows of 4
@@ -194,7 +218,7 @@ int dw_chunks(int64_t N, int mg, int ng, int dtype) {
 }
 
 DwPlan dw_plan_for(int64_t N, int C, int D, int dtype, int64_t want) {
-  DwPlan p{0, 0, 1};
+  DwPlan p{0, 0, 1, 64};
   if (N <= 0) return p;
   const int64_t stage = eqlin::dw_rows_per_stage(dtype);
   const int64_t row_bytes = int64_t(C > D ? C : D) * elem_bytes(dtype);
@@ -216,13 +240,23 @@ constexpr int64_t kAnySplits = INT64_MAX;
 // in total.  The workspace holds this plan's splits, the most of the two.
 // max_splits caps the splits asked for (a fixed-size scratch); the 32-bit
 // offset cap inside a split can still ask for more, which the callers check.
-DwPlan plan_dw(int64_t N, int C, int D, int O, int dtype, bool chunked = false, int64_t max_splits = kAnySplits) {
+// The 128-wide tile runs one workgroup per CU: one per CU in total.
+DwPlan plan_dw(int64_t N, int C, int D, int O, int dtype, bool chunked = false, int64_t max_splits = kAnySplits,
+               int width = 64) {
   const int ch = chunked ? dw_chunks(N, D / O, C / O, dtype) : 1;
-  const int64_t tiles = cdiv(ch * D / O, 64) * cdiv(ch * C / O, 64);
-  const int64_t want = (2 * eqlin::kNumCu) / tiles;
+  const int W = ch == 1 ? width : 64;
+  const int64_t tiles = cdiv(ch * D / O, W) * cdiv(ch * C / O, W);
+  const int64_t want = ((W == 64 ? 2 : 1) * eqlin::kNumCu) / tiles;
   DwPlan p = dw_plan_for(N / ch, ch * C, ch * D, dtype, want < max_splits ? want : max_splits);
   p.chunks = ch;
+  p.width = W;
   return p;
+}
+
+// The stand-alone dw launch's plan.
+DwPlan plan_dw_alone(int64_t N, int C, int D, int O, int dtype, int64_t max_splits = kAnySplits) {
+  const int ch = dw_chunks(N, D / O, C / O, dtype);
+  return plan_dw(N, C, D, O, dtype, true, max_splits, dw_width(O, ch, D / O, C / O, dtype));
 }
 
 // The fused backward launch: its dX tiles fill the chip besides the dw
@@ -258,8 +292,13 @@ size_t dw_split_bytes(int C, int D, int O) {
   return static_cast<size_t>(O) * static_cast<size_t>(C / O) * static_cast<size_t>(D / O) * sizeof(float);
 }
 size_t dw_workspace_need(int64_t N, int C, int D, int O, int dtype, int64_t max_splits) {
-  const DwPlan p = plan_dw(N, C, D, O, dtype, true, max_splits);
-  return static_cast<size_t>(p.nsplit) * dw_split_bytes(C, D, O);
+  // the most splits of any plan a call may run (the 64-wide stand-alone plan
+  // has the most: the fused plan asks for fewer, the 128-wide one too)
+  const DwPlan a = plan_dw(N, C, D, O, dtype, true, max_splits);
+  const DwPlan b = plan_dw_alone(N, C, D, O, dtype, max_splits);
+  const DwPlan c = plan_dw_fused(N, C, D, O, dtype, max_splits);
+  const int n = a.nsplit > b.nsplit ? (a.nsplit > c.nsplit ? a.nsplit : c.nsplit) : (b.nsplit > c.nsplit ? b.nsplit : c.nsplit);
+  return static_cast<size_t>(n) * dw_split_bytes(C, D, O);
 }
 
 // ------------------------------------------------ p4 group convolution
@@ -442,9 +481,10 @@ int backward_dw_impl(const void* dY, const void* X, int64_t N, int C, int D, int
   if (!aligned16(dw)) return EQLIN_EALIGN;
   if (N > 0 && (!aligned16(dY) || !aligned16(X) || !aligned16(workspace))) return EQLIN_EALIGN;
   if (workspace_bytes < dw_workspace_need(N, C, D, O, dtype, max_splits)) return EQLIN_EWORKSPACE;
-  const DwPlan p = plan_dw(N, C, D, O, dtype, true, max_splits);
+  const DwPlan p = plan_dw_alone(N, C, D, O, dtype, max_splits);
   return hip_status(EQLIN_BY_T(T, dw(dtype, dY, X, static_cast<float*>(workspace), dw, N, D / O, C / O,
-                                     p.rows_per_split, p.nsplit, p.chunks, static_cast<hipStream_t>(stream))));
+                                     p.rows_per_split, p.nsplit, p.chunks, p.width,
+                                     static_cast<hipStream_t>(stream))));
 }
 
 // eqlin_backward with the dw row splits capped at max_splits.
@@ -467,12 +507,13 @@ int backward_impl(const void* dY, const void* X, int64_t N, int C, int D, int T,
     if (workspace_bytes < dw_workspace_need(N, C, D, O, dtype, max_splits)) return EQLIN_EWORKSPACE;
   }
   // One fused launch for dX and the dw partials, except for f16 p4 layers of
-  // 16 or fewer input groups: their dX runs faster as the forward's narrow
-  // tile than as the fused launch's 64 x 64 one (C = D = 64 over 201728 rows:
+  // 16 or fewer input groups (their dX runs faster as the forward's narrow
+  // tile than as the fused launch's 64 x 64 one: C = D = 64 over 201728 rows,
   // 42.6 against 45.9 us; at 32 groups the fused launch still wins, 52.7
-  // against 58.3 us).
+  // against 58.3 us) and for the wide f16 p4 layers (wide_f16_layer).
   const bool narrow_f16 = dtype == EQLIN_F16 && O == 4 && C / O <= 16;
-  if (dX && dw && N > 0 && use_fused_backward() && !narrow_f16) {
+  const bool wide_f16 = wide_f16_layer(O, D / O, C / O, dtype);
+  if (dX && dw && N > 0 && use_fused_backward() && !narrow_f16 && !wide_f16) {
     // one launch for dX and the dw partials (they share dY), then the finalize
     const DwPlan p = plan_dw_fused(N, C, D, O, dtype, max_splits);
     const char* wb = static_cast<const char*>(W_hat) + transpose_offset(C, D, O, dtype);

@@ -1457,45 +1457,60 @@ fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ o
 // P_k[m][n] = sum_rows G_k[row][m] conj(Xhat_k[row][n])   (m = d', n = c';
 // for p4m per representation Xhat^T G: the adjoint of Xhat and the dw product
 // list) over the rows of one split; the T planes are written to
-// ws[split][plane][mg][ng] (float32).  Tiles 64 x 64, one 32 x 32 fragment
-// per wave and plane.  The k axis is the row axis: thread (unit column pc,
-// row block rq) loads KV consecutive rows of one unit (kGroupsPerUnit groups),
+// ws[split][plane][mg][ng] (float32).  Tiles W x W: W = 64 with four waves of
+// one 32 x 32 fragment per plane, or W = 128 with eight waves (two rows of
+// four) of two fragments each (each dY and X column slab is then read by half
+// as many tiles).  The k axis is the row axis: thread (unit column pc, row
+// block rq) loads KV consecutive rows of one unit (kGroupsPerUnit groups),
 // transforms them and writes, per group and plane, the KV rows as one
-// contiguous LDS run.  A stage is 64 bytes of every plane row (16 fp32 / 32
+// contiguous LDS run (KV = 4 for both widths: twice the threads cover the
+// twice wider rows).  A stage is 64 bytes of every plane row (16 fp32 / 32
 // f16 rows); LDS is single- or double-buffered as in fwd_kernel.
-template <int T, int NBUF>
+template <int W>
+struct DwShape {
+  static_assert(W == 64 || W == 128, "dw tile width");
+  static constexpr int kThreads = W == 64 ? 256 : 512;
+  static constexpr int kWaveRows = 2, kWaveCols = W == 64 ? 2 : 4;
+  static constexpr int kFragRows = W / (32 * kWaveRows), kFragCols = W / (32 * kWaveCols);
+};
+
+template <int T, int NBUF, int W = 64>
 constexpr int dw_lds_bytes() {
-  return NBUF * 2 * T * 64 * kRowBytes;
+  return NBUF * 2 * T * W * kRowBytes;
 }
 
 // CONV: x is the input map of a p4 group convolution and the n axis runs over
 // the gathered group channels (see ConvGeom): each lane reads, per row, the
 // one value of each of the four taps (or, for a centre block, the four values
 // of its channel) that its gathered group channel needs, as 32-bit loads.
-template <typename E, int G, int NBUF, bool CONV = false>
+template <typename E, int G, int NBUF, bool CONV = false, int W = 64>
 __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restrict__ dy, const E* __restrict__ x,
                                         float* __restrict__ ws, int64_t nrows, int mg, int ng,
                                         int64_t rows_per_split, int tiles_m, int tiles_n, int cw_m, int cw_n,
                                         const ConvGeom& geo = ConvGeom{}) {
   constexpr int T = Grp<G>::kOrder;
   using U = Units<E, T>;
+  using S = DwShape<W>;
+  constexpr int NT = S::kThreads;
+  constexpr int WC = S::kWaveCols, FR = S::kFragRows, FC = S::kFragCols;
   constexpr int GPU = U::kGroupsPerUnit, PPU = U::kPiecesPerUnit;
-  constexpr int PR = 64 / GPU;                     // units per tile row (64 groups)
-  constexpr int RB = kThreads / PR;                // row blocks per stage
+  constexpr int PR = W / GPU;                      // units per tile row (W groups)
+  constexpr int RB = NT / PR;                      // row blocks per stage
   constexpr int SR = 64 / (int)sizeof(E);          // rows per stage: 16 (fp32) / 32 (f16)
   constexpr int KV = SR / RB;                      // rows per thread per stage
   constexpr int RUN = KV * (int)sizeof(E);         // LDS bytes per (group, plane) per thread
   constexpr int STRIDE = kRowBytes;
-  constexpr int PLANE = 64 * STRIDE;
+  constexpr int PLANE = W * STRIDE;
   constexpr int BUF = 2 * T * PLANE;
   static_assert(RB * KV == SR && (RUN == 8 || RUN == 16), "stage shape");
-  static_assert(NBUF * BUF == dw_lds_bytes<T, NBUF>(), "LDS size");
+  static_assert(NBUF * BUF == dw_lds_bytes<T, NBUF, W>(), "LDS size");
+  static_assert(!CONV || W == 64, "the convolution's gathered loads use the 64-wide tile");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ntiles = tiles_m * tiles_n;
   const int64_t split = lid / ntiles;
   const int tile = (int)(lid % ntiles);
-  const int m0 = (tile / tiles_n) * 64, n0 = (tile % tiles_n) * 64;
+  const int m0 = (tile / tiles_n) * W, n0 = (tile % tiles_n) * W;
   const int64_t rbeg = split * rows_per_split;
   const int64_t rend = (rbeg + rows_per_split < nrows) ? rbeg + rows_per_split : nrows;
   const int nstages = (int)((rend - rbeg + SR - 1) / SR);
@@ -1686,14 +1701,18 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
     }
   };
 
-  f32x16 acc[T][1][1];
+  f32x16 acc[T][FR][FC];
 #pragma unroll
-  for (int p = 0; p < T; ++p) acc[p][0][0] = f32x16{};
+  for (int p = 0; p < T; ++p)
+#pragma unroll
+    for (int fm = 0; fm < FR; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FC; ++fn) acc[p][fm][fn] = f32x16{};
 
-  const int wr = wave >> 1, wc = wave & 1;
+  const int wr = wave / WC, wc = wave % WC;
   const int li = lane & 31, lh = lane >> 5;
-  const int a_frag = (wr * 32 + li) * STRIDE;
-  const int b_frag = T * PLANE + (wc * 32 + li) * STRIDE;
+  const int a_frag = (wr * 32 * FR + li) * STRIDE;
+  const int b_frag = T * PLANE + (wc * 32 * FC + li) * STRIDE;
   const int c0 = swz_slot(li, lh) * 16, c1 = swz_slot(li, 2 + lh) * 16;
 
   if (nstages > 0) {
@@ -1709,21 +1728,23 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
   // meets no diagonal block, or lies wholly past mg or ng, loads and
   // transforms its share of the stages but issues no MFMA: its products
   // would be dropped.
-  const int fr = m0 + wr * 32, fc = n0 + wc * 32;
-  const bool live = fr < mg && fc < ng &&
-                    (fr / cw_m > fc / cw_n ? fr / cw_m <= (min(fc + 31, ng - 1) / cw_n)
-                                           : fc / cw_n <= (min(fr + 31, mg - 1) / cw_m));
+  const int fr = m0 + wr * 32 * FR, fc = n0 + wc * 32 * FC;
+  const bool live = W != 64 || (fr < mg && fc < ng &&
+                                (fr / cw_m > fc / cw_n ? fr / cw_m <= (min(fc + 31, ng - 1) / cw_n)
+                                                       : fc / cw_n <= (min(fr + 31, mg - 1) / cw_m)));
   // Only the p4 fp32 tiles skip: in f16 the MFMAs are short, and for the
   // order-8 groups, whose eight planes fill the registers, a branch around
   // them inside the loop costs more than it saves (the compiler guards MFMA
   // hazards at block edges; measured: C8 ViT-B fp32 dw 86.6 -> 94.4 us),
   // while a second copy of the loop without them costs occupancy.
   const bool mma = !(sizeof(E) == 4 && T == 4) || live;
+  // multiply stage st, then transform stage st + 1 (slot of st + 1) into LDS
+  // and refill that slot with the loads of stage st + 1 + PF
   for (int st = 0; st < nstages; ++st) {
     char* cur = lds + (NBUF == 2 ? (st & 1) * BUF : 0);
     if (mma) {
-      mma_chunk<E, G, true, 1, 1>(acc, cur + a_frag + c0, PLANE, cur + b_frag + c0, PLANE, STRIDE);
-      mma_chunk<E, G, true, 1, 1>(acc, cur + a_frag + c1, PLANE, cur + b_frag + c1, PLANE, STRIDE);
+      mma_chunk<E, G, true, FR, FC>(acc, cur + a_frag + c0, PLANE, cur + b_frag + c0, PLANE, STRIDE);
+      mma_chunk<E, G, true, FR, FC>(acc, cur + a_frag + c1, PLANE, cur + b_frag + c1, PLANE, STRIDE);
     }
     if (st + 1 < nstages) {
       if constexpr (NBUF == 1) __syncthreads();   // every wave is done reading the only buffer
@@ -1733,46 +1754,54 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
     __syncthreads();
   }
 
-  const int n = n0 + wc * 32 + li;
-  if (sizeof(E) == 4 && cw_m < mg) {
-    // row chunks (fp32): the CH diagonal blocks meet in LDS (free after the
-    // stage loop's last barrier), are added in block order and written as
-    // one cw_m x cw_n partial per plane
-    const int CH = mg / cw_m, cell = cw_m * cw_n;
-    // [T][CH][cw_m][cw_n]: T mg ng / CH <= T x 2048 floats (CH >= 2, mg, ng <= 64),
-    // the size of the dw stage buffers (T x 2 x 64 x 64 bytes per buffer)
-    static_assert(BUF >= T * 2048 * (int)sizeof(float), "chunk reduction fits the stage buffer");
-    float* red = reinterpret_cast<float*>(lds);
-    const int nblk = n / cw_n;
+  if constexpr (W == 64) {   // row chunks: narrow fp32 layers (64-wide tile only)
+    const int n = n0 + wc * 32 + li;
+    if (sizeof(E) == 4 && cw_m < mg) {
+      // row chunks (fp32): the CH diagonal blocks meet in LDS (free after the
+      // stage loop's last barrier), are added in block order and written as
+      // one cw_m x cw_n partial per plane
+      const int CH = mg / cw_m, cell = cw_m * cw_n;
+      // [T][CH][cw_m][cw_n]: T mg ng / CH <= T x 2048 floats (CH >= 2, mg, ng <= 64),
+      // the size of the dw stage buffers (T x 2 x 64 x 64 bytes per buffer)
+      static_assert(BUF >= T * 2048 * (int)sizeof(float), "chunk reduction fits the stage buffer");
+      float* red = reinterpret_cast<float*>(lds);
+      const int nblk = n / cw_n;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wr * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-      if (m < mg && n < ng && m / cw_m == nblk) {
-        const int o = nblk * cell + (m - nblk * cw_m) * cw_n + (n - nblk * cw_n);
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wr * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        if (m < mg && n < ng && m / cw_m == nblk) {
+          const int o = nblk * cell + (m - nblk * cw_m) * cw_n + (n - nblk * cw_n);
 #pragma unroll
-        for (int p = 0; p < T; ++p) red[p * CH * cell + o] = acc[p][0][0][r];
+          for (int p = 0; p < T; ++p) red[p * CH * cell + o] = acc[p][0][0][r];
+        }
       }
+      __syncthreads();
+      float* dstc = ws + split * T * (int64_t)cell;
+      for (int i = tid; i < T * cell; i += NT) {
+        const int p = i / cell, e = i - p * cell;
+        float sum = red[p * CH * cell + e];
+        for (int c = 1; c < CH; ++c) sum += red[(p * CH + c) * cell + e];
+        dstc[i] = sum;
+      }
+      return;
     }
-    __syncthreads();
-    float* dstc = ws + split * T * (int64_t)cell;
-    for (int i = tid; i < T * cell; i += kThreads) {
-      const int p = i / cell, e = i - p * cell;
-      float sum = red[p * CH * cell + e];
-      for (int c = 1; c < CH; ++c) sum += red[(p * CH + c) * cell + e];
-      dstc[i] = sum;
-    }
-    return;
   }
   const int64_t plane_elems = (int64_t)mg * ng;
   float* dst = ws + split * T * plane_elems;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int m = m0 + wr * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-    if (m < mg && n < ng) {
+  for (int fm = 0; fm < FR; ++fm)
 #pragma unroll
-      for (int p = 0; p < T; ++p) dst[p * plane_elems + (int64_t)m * ng + n] = acc[p][0][0][r];
+    for (int fn = 0; fn < FC; ++fn) {
+      const int n = n0 + wc * 32 * FC + fn * 32 + li;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wr * 32 * FR + fm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+        if (m < mg && n < ng) {
+#pragma unroll
+          for (int p = 0; p < T; ++p) dst[p * plane_elems + (int64_t)m * ng + n] = acc[p][fm][fn][r];
+        }
+      }
     }
-  }
 }
 
 // C8 tiles hold eight 32 x 32 accumulators per wave next to the operands
@@ -1782,14 +1811,17 @@ constexpr int bwd_waves_per_simd() {
   return T == 4 ? 2 : 1;
 }
 
-template <typename E, int G>
-__global__ void __launch_bounds__(kThreads, bwd_waves_per_simd<Grp<G>::kOrder>())
+// W = 128 (p4 only: two fragments of eight planes would not fit the registers
+// of two waves per SIMD) runs one 512-thread workgroup per CU.
+template <typename E, int G, int W = 64>
+__global__ void __launch_bounds__(DwShape<W>::kThreads, bwd_waves_per_simd<Grp<G>::kOrder>())
 dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __restrict__ ws,
                   int64_t nrows, int mg, int ng, int64_t rows_per_split, int tiles_m, int tiles_n, int cw_m,
                   int cw_n) {
-  __shared__ __attribute__((aligned(16))) char lds[dw_lds_bytes<Grp<G>::kOrder, kDwBufs>()];
-  dw_tile<E, G, kDwBufs>(lds, xcd_logical_id(blockIdx.x, gridDim.x), dy, x, ws, nrows, mg, ng, rows_per_split,
-                         tiles_m, tiles_n, cw_m, cw_n);
+  static_assert(W == 64 || G == 4, "the 128-wide dw tile is built for p4");
+  __shared__ __attribute__((aligned(16))) char lds[dw_lds_bytes<Grp<G>::kOrder, kDwBufs, W>()];
+  dw_tile<E, G, kDwBufs, false, W>(lds, xcd_logical_id(blockIdx.x, gridDim.x), dy, x, ws, nrows, mg, ng,
+                                   rows_per_split, tiles_m, tiles_n, cw_m, cw_n);
 }
 
 // Backward in one launch: the first ndw_pad workgroups are dw split partials,
@@ -2010,16 +2042,28 @@ hipError_t launch_fwd_s(const void* in, const void* wp, void* out, int64_t nrows
 
 // chunks > 1 (it divides nrows; chunks x mg and chunks x ng <= 64): the dw
 // partials of the row-chunked product, rows_per_split counting chunked rows.
+// width: the dw tile, 64 or (p4, chunks == 1) 128.
 template <typename E, int G>
 hipError_t launch_dw_t(const void* dy, const void* x, float* ws, float* dw, int64_t nrows, int mg, int ng,
-                       int64_t rows_per_split, int nsplit, int chunks, hipStream_t s) {
-  const int tiles_m = (int)cdiv(chunks * mg, 64), tiles_n = (int)cdiv(chunks * ng, 64);
+                       int64_t rows_per_split, int nsplit, int chunks, int width, hipStream_t s) {
+  const bool wide = G == 4 && width == 128 && chunks == 1;
+  const int W = wide ? 128 : 64;
+  const int tiles_m = (int)cdiv(chunks * mg, W), tiles_n = (int)cdiv(chunks * ng, W);
   if (nsplit > 0) {
     const int64_t grid = (int64_t)tiles_m * tiles_n * nsplit;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((dw_partial_kernel<E, G>), dim3((unsigned)grid), dim3(kThreads), 0, s,
-                       static_cast<const E*>(dy), static_cast<const E*>(x), ws, nrows / chunks, chunks * mg,
-                       chunks * ng, rows_per_split, tiles_m, tiles_n, mg, ng);
+    if constexpr (G == 4) {
+      if (wide) {
+        hipLaunchKernelGGL((dw_partial_kernel<E, G, 128>), dim3((unsigned)grid), dim3(DwShape<128>::kThreads), 0, s, static_cast<const E*>(dy),
+                           static_cast<const E*>(x), ws, nrows, mg, ng, rows_per_split, tiles_m, tiles_n, mg, ng);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_dw_finalize<E, G>(ws, dw, mg, ng, nsplit, s);
+      }
+    }
+    hipLaunchKernelGGL((dw_partial_kernel<E, G>), dim3((unsigned)grid), dim3(kThreads), 0, s, static_cast<const E*>(dy),
+                       static_cast<const E*>(x), ws, nrows / chunks, chunks * mg, chunks * ng, rows_per_split, tiles_m,
+                       tiles_n, mg, ng);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -72,8 +72,9 @@ struct Launch {
   // chunks (1, or a divisor of nrows with chunks x mg, chunks x ng <= 64): rows
   // read as rows of `chunks` consecutive rows (narrow layers), rows_per_split
   // counting those
+  // width: dw tile 64, or 128 (p4 only; chunks == 1)
   static hipError_t dw(int dtype, const void* dy, const void* x, float* ws, float* dw, int64_t nrows, int mg, int ng,
-                       int64_t rows_per_split, int nsplit, int chunks, hipStream_t s);
+                       int64_t rows_per_split, int nsplit, int chunks, int width, hipStream_t s);
   // dX (forward structure on the transpose spectra wb, 64 x 64 tiles) and the
   // dw split partials in one launch, then the dw finalize.  nrows > 0.
   static hipError_t bwd_fused(int dtype, const void* dy, const void* x, const void* wb, void* dx, float* ws,
@@ -87,7 +88,7 @@ struct Launch {
   template <> hipError_t Launch<T>::forward(int, int, const void*, const void*, void*, int64_t, int, int,          \
                                             const void*, int, const void*, hipStream_t);                           \
   template <> hipError_t Launch<T>::dw(int, const void*, const void*, float*, float*, int64_t, int, int, int64_t,   \
-                                       int, int, hipStream_t);                                                     \
+                                       int, int, int, hipStream_t);                                                \
   template <> hipError_t Launch<T>::bwd_fused(int, const void*, const void*, const void*, void*, float*, float*,   \
                                               int64_t, int, int, int64_t, int, int, hipStream_t);                  \
   template <> hipError_t Launch<T>::prepare(int, const void*, void*, void*, int, int, hipStream_t);

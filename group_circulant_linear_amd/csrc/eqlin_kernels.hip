@@ -57,9 +57,9 @@ hipError_t Launch<4>::forward(int dtype, int tile, const void* in, const void* w
 
 template <>
 hipError_t Launch<4>::dw(int dtype, const void* dy, const void* x, float* ws, float* dw, int64_t nrows, int mg,
-                         int ng, int64_t rows_per_split, int nsplit, int chunks, hipStream_t s) {
-  return dtype == 0 ? launch_dw_t<float, 4>(dy, x, ws, dw, nrows, mg, ng, rows_per_split, nsplit, chunks, s)
-                    : launch_dw_t<_Float16, 4>(dy, x, ws, dw, nrows, mg, ng, rows_per_split, nsplit, chunks, s);
+                         int ng, int64_t rows_per_split, int nsplit, int chunks, int width, hipStream_t s) {
+  return dtype == 0 ? launch_dw_t<float, 4>(dy, x, ws, dw, nrows, mg, ng, rows_per_split, nsplit, chunks, width, s)
+                    : launch_dw_t<_Float16, 4>(dy, x, ws, dw, nrows, mg, ng, rows_per_split, nsplit, chunks, width, s);
 }
 
 template <>

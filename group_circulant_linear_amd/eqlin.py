@@ -9,6 +9,7 @@ if the library is not built, every call raises.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 import re
 from typing import NamedTuple, Optional
@@ -136,7 +137,15 @@ def _check_out(t: torch.Tensor, name: str, shape: tuple, dtype: torch.dtype) -> 
 
 
 def _stream(t: torch.Tensor) -> int:
-    return torch.cuda.current_stream(t.device).cuda_stream
+    """torch's current HIP stream on t's device, as the raw hipStream_t (the
+    same value torch.cuda.current_stream(dev).cuda_stream gives, without
+    building a stream object on every call)."""
+    return torch._C._cuda_getCurrentRawStream(t.device.index)
+
+
+@functools.lru_cache(maxsize=256)
+def _prepared_bytes(C: int, D: int, T: int, dt: int) -> int:
+    return int(load_library().eqlin_prepared_weight_bytes(C, D, T, dt))
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -180,7 +189,7 @@ def eqlin_prepare_weights(w: torch.Tensor, out: Optional[torch.Tensor] = None, g
         raise ValueError(f"w's last dimension {w.shape[2]} is not the group order {group_order(T)}")
     n = group_order(T)
     D, C = n * w.shape[0], n * w.shape[1]
-    nbytes = int(lib.eqlin_prepared_weight_bytes(C, D, T, dt))
+    nbytes = _prepared_bytes(C, D, T, dt)
     if out is None:
         out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=w.device)
     _need_cuda(out, "out")

@@ -336,6 +336,26 @@ def test_backward_workload_vitb(dt, g):
     assert e1 <= TOL[dt] and e2 <= TOL[dt]
 
 
+def test_backward_wide_f16_layers():
+    """f16 p4 layers with 256 or more group channels in and out run dX through
+    the forward's tile choice and dw alone with the 128-wide tile: a ragged
+    wide layer whole, and the ViT-H fc1 layer (dX on sampled rows, dw whole)."""
+    for (N, C, D) in ((3001, 4 * 300, 4 * 260), (8224, 1280, 5120)):
+        say(f"backward wide f16 N={N} C={C} D={D}")
+        X, w, dY = make_layer_inputs(N, C, D, "f16", seed=26)
+        Wh = prep(w, 4)
+        dX, dw = eq.eqlin_backward(dev(dY), dev(X), Wh)
+        dX = host(dX)
+        if N * C * D <= 3001 * 1200 * 1040:
+            e1 = rel_err(dX, oracle.dx_direct(dY, w))
+        else:
+            rows = _sample_rows(N, np.random.default_rng(27))
+            e1 = rel_err(dX[rows], oracle.dx_direct(dY[rows], w))
+        e2 = rel_err(host(dw), oracle.dw_direct(dY, X, 4))
+        say(f"  dX rel err {e1:.3e}  dw rel err {e2:.3e}")
+        assert e1 <= TOL["f16"] and e2 <= TOL["f16"]
+
+
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 def test_backward_workload_narrow(dt):
     """The HBM-bound narrow layer (16 group channels, 201728 rows): dw reduces
@@ -349,6 +369,24 @@ def test_backward_workload_narrow(dt):
     e2 = rel_err(host(dw), ref_dw(dY, X, 4))
     say(f"  dX rel err {e1:.3e}  dw rel err {e2:.3e}")
     assert e1 <= TOL[dt] and e2 <= TOL[dt]
+
+
+@pytest.mark.parametrize("width", ["128", "64"])
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_dw_tile_widths(dt, width, monkeypatch):
+    """The stand-alone dw launch with the 128 x 128 partial tile (eight waves,
+    two fragments each) and the 64 x 64 one: ragged rows, group channels past
+    the tile, the ViT shapes whole."""
+    monkeypatch.setenv("EQLIN_DW_WIDTH", width)
+    shapes = [(77, 8 * 20, 8 * 12), (1000, 4 * 130, 4 * 70), (3001, 4 * 300, 4 * 260), (12608, 768, 768),
+              (8224, 1280, 5120), (8224, 5120, 1280)]
+    for (N, C, D) in shapes:
+        say(f"dw tile width {width} {dt} N={N} C={C} D={D}")
+        X, w, dY = make_layer_inputs(N, C, D, dt, seed=25)
+        dw = host(eq.eqlin_backward_dw(dev(dY), dev(X)))
+        err = rel_err(dw, oracle.dw_direct(dY, X, 4))
+        say(f"  rel err {err:.2e}")
+        assert err <= TOL[dt], (N, C, D, err)
 
 
 @pytest.mark.parametrize("g", GROUPS)
