@@ -73,6 +73,19 @@ constexpr int kBwdFwdPrefetch = 1;
 constexpr int kRowBytes = 64;
 __device__ __forceinline__ int swz_slot(int row, int slot) { return slot ^ ((row >> 2) & 3); }
 
+// The dw tile's placement of the same 64-byte plane rows (rows = group
+// channels, k along the batch rows).  Its f16 p4 writes are transposed: eight
+// lanes fill the eight 8-byte runs of one row and a 32-lane write spans four
+// rows two apart, so row r goes to physical row dw_row(r) (the low three bits
+// rotated to b1 b2 b0, which puts those four rows in distinct 64-byte bank
+// windows) and its 16-byte slots are XOR-ed with bits 0 and 3 of r; sixteen
+// consecutive rows of a fragment read then also meet all 64 banks once.
+__device__ __forceinline__ int dw_row(int r) { return (r & ~7) | ((r >> 1) & 3) | ((r & 1) << 2); }
+__device__ __forceinline__ int dw_slot(int r, int slot) { return slot ^ ((r & 1) | (((r >> 3) & 1) << 1)); }
+__device__ __forceinline__ int dw_off(int r, int kb) {
+  return dw_row(r) * kRowBytes + dw_slot(r, kb >> 4) * 16 + (kb & 15);
+}
+
 // Group channels whose values one lane holds per 16-byte LDS slot of a plane
 // (= k-values per lane and fragment): 4 fp32, 8 f16.  A pipeline stage covers
 // four slots, i.e. 16 fp32 / 32 f16 group channels along k.
@@ -1521,7 +1534,14 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
   const __amdgpu_buffer_rsrc_t b_src =
       CONV ? make_rsrc(x, geo.in_bytes) : make_rsrc(x + rbeg * T * (int64_t)ng, (uint64_t)(rend - rbeg) * b_row);
 
-  const int pc = tid % PR, rq = tid / PR;
+  // thread (unit column pc, row block rq).  With two groups per unit (f16
+  // p4) a wave's 32-lane half holds eight consecutive unit columns (128
+  // contiguous bytes of a row per load) of four row blocks, so that its
+  // transposed LDS writes cover all 64 banks (see dw_row); otherwise the unit
+  // column runs fastest.
+  static_assert(GPU != 2 || RB == 8, "eight row blocks per stage");
+  const int pc = GPU == 2 ? (tid & 7) | ((tid >> 6) << 3) : tid % PR;
+  const int rq = GPU == 2 ? ((tid >> 3) & 3) | (((tid >> 5) & 1) << 2) : tid / PR;
   const int ga = m0 + pc * GPU, gb = n0 + pc * GPU;
   const bool a_ok = ga < mg, b_ok = gb < ng;
   const uint32_t a_col = (uint32_t)ga * (uint32_t)(T * sizeof(E));
@@ -1604,9 +1624,7 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
           run[2][j] = q1r;
           run[3][j] = q1i;
         }
-        const int row = pc * GPU + e;
-        const int kb = rq * RUN;
-        const int off = row * STRIDE + swz_slot(row, kb >> 4) * 16 + (kb & 15);
+        const int off = dw_off(pc * GPU + e, rq * RUN);
 #pragma unroll
         for (int p = 0; p < T; ++p) *reinterpret_cast<u32x2*>(plane0 + p * PLANE + off) = run[p];
       }
@@ -1622,9 +1640,7 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
 #pragma unroll
         for (int p = 0; p < T; ++p) run[p][j] = o[p];
       }
-      const int row = pc;
-      const int kb = rq * RUN;
-      const int off = row * STRIDE + swz_slot(row, kb >> 4) * 16 + (kb & 15);
+      const int off = dw_off(pc, rq * RUN);
 #pragma unroll
       for (int p = 0; p < T; ++p) st16(plane0 + p * PLANE + off, run[p]);
       return;
@@ -1653,9 +1669,7 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
     }
 #pragma unroll
     for (int e = 0; e < GPU; ++e) {
-      const int row = pc * GPU + e;
-      const int kb = rq * RUN;
-      const int off = row * STRIDE + swz_slot(row, kb >> 4) * 16 + (kb & 15);
+      const int off = dw_off(pc * GPU + e, rq * RUN);
 #pragma unroll
       for (int p = 0; p < T; ++p) {
         if constexpr (sizeof(E) == 4) {
@@ -1711,9 +1725,11 @@ __device__ __forceinline__ void dw_tile(char* lds, int64_t lid, const E* __restr
 
   const int wr = wave / WC, wc = wave % WC;
   const int li = lane & 31, lh = lane >> 5;
-  const int a_frag = (wr * 32 * FR + li) * STRIDE;
-  const int b_frag = T * PLANE + (wc * 32 * FC + li) * STRIDE;
-  const int c0 = swz_slot(li, lh) * 16, c1 = swz_slot(li, 2 + lh) * 16;
+  // fragment rows differ from li by multiples of 32, which dw_row and
+  // dw_slot leave unchanged
+  const int a_frag = (wr * 32 * FR + dw_row(li)) * STRIDE;
+  const int b_frag = T * PLANE + (wc * 32 * FC + dw_row(li)) * STRIDE;
+  const int c0 = dw_slot(li, lh) * 16, c1 = dw_slot(li, 2 + lh) * 16;
 
   if (nstages > 0) {
     load(0);
