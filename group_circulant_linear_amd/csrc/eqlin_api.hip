@@ -241,12 +241,14 @@ constexpr int64_t kAnySplits = INT64_MAX;
 // max_splits caps the splits asked for (a fixed-size scratch); the 32-bit
 // offset cap inside a split can still ask for more, which the callers check.
 // The 128-wide tile runs one workgroup per CU: one per CU in total.
+// round_up: the split count rounded up instead of down (the fused fallback).
 DwPlan plan_dw(int64_t N, int C, int D, int O, int dtype, bool chunked = false, int64_t max_splits = kAnySplits,
-               int width = 64) {
+               int width = 64, bool round_up = false) {
   const int ch = chunked ? dw_chunks(N, D / O, C / O, dtype) : 1;
   const int W = ch == 1 ? width : 64;
   const int64_t tiles = cdiv(ch * D / O, W) * cdiv(ch * C / O, W);
-  const int64_t want = ((W == 64 ? 2 : 1) * eqlin::kNumCu) / tiles;
+  const int64_t slots = (W == 64 ? 2 : 1) * eqlin::kNumCu;
+  const int64_t want = round_up ? cdiv(slots, tiles) : slots / tiles;
   DwPlan p = dw_plan_for(N / ch, ch * C, ch * D, dtype, want < max_splits ? want : max_splits);
   p.chunks = ch;
   p.width = W;
@@ -268,7 +270,9 @@ DwPlan plan_dw_alone(int64_t N, int C, int D, int O, int dtype, int64_t max_spli
 // CU), else two per CU as plan_dw.  Measured against two per CU: ViT-B
 // attention fp32 113 -> 104 us and f16 -4%, ViT-H f16 and C8 -2% to -6%;
 // the ViT-H fp32 layers (ratio 1.9) keep two per CU, where one per CU is 1%
-// (fc1) and 9% (fc2) slower.
+// (fc1) and 9% (fc2) slower.  For p4 that fallback rounds its split count
+// up: at ViT-H (100 dw tiles) 6 splits, not 5 (fp32 fused backward, fc1 744
+// -> 655 us, fc2 646 -> 642 us; 3, 4 and 8 splits also beat 5 at fc1).
 DwPlan plan_dw_fused(int64_t N, int C, int D, int O, int dtype, int64_t max_splits = kAnySplits) {
   const int ch = dw_chunks(N, D / O, C / O, dtype);
   const int64_t tiles = cdiv(ch * D / O, 64) * cdiv(ch * C / O, 64);
@@ -282,7 +286,7 @@ DwPlan plan_dw_fused(int64_t N, int C, int D, int O, int dtype, int64_t max_spli
     const int64_t per_cu = O == 4 ? (dtype == EQLIN_F32 ? 3 : 2) : 1;
     if (4 * split_stages * per_cu * eqlin::kNumCu <= 7 * (dw_work + dx_work)) return one;
   }
-  return plan_dw(N, C, D, O, dtype, true, max_splits);
+  return plan_dw(N, C, D, O, dtype, true, max_splits, 64, O == 4);
 }
 
 // Workspace bytes of the dw split partials (T planes of D' x C' float32 per
@@ -292,8 +296,8 @@ size_t dw_split_bytes(int C, int D, int O) {
   return static_cast<size_t>(O) * static_cast<size_t>(C / O) * static_cast<size_t>(D / O) * sizeof(float);
 }
 size_t dw_workspace_need(int64_t N, int C, int D, int O, int dtype, int64_t max_splits) {
-  // the most splits of any plan a call may run (the 64-wide stand-alone plan
-  // has the most: the fused plan asks for fewer, the 128-wide one too)
+  // the most splits of any plan a call may run (the 64-wide stand-alone plan,
+  // or the p4 fused fallback, which rounds its count up)
   const DwPlan a = plan_dw(N, C, D, O, dtype, true, max_splits);
   const DwPlan b = plan_dw_alone(N, C, D, O, dtype, max_splits);
   const DwPlan c = plan_dw_fused(N, C, D, O, dtype, max_splits);

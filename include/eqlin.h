@@ -303,9 +303,9 @@ int eqlin_backward_dw(const void* dY, const void* X, int64_t N, int C, int D, in
  *   - The row splits of the dw reduction are capped to what the scratch
  *     holds (each split T x D' x C' float32 values).  Where the cap binds,
  *     dw is summed in fewer, longer splits than eqlin_backward uses (the
- *     same values to rounding; the p4 layers of the ViT-B shapes and the
- *     float32 ViT-H layers are not capped and give the same bits as
- *     eqlin_backward; the f16 ViT-H layers, whose dw runs 128-wide tiles in 8
+ *     same values to rounding; the p4 layers of the ViT-B shapes are not
+ *     capped and give the same bits as eqlin_backward; the ViT-H layers,
+ *     whose dw runs in 6 (float32, fused with dX) or 8 (f16, 128-wide tiles)
  *     splits of 6.5 MB, run 5).  A layer one split
  *     of which does not fit (T D' C' > 8 Mi values) -> EQLIN_EWORKSPACE.
  *   - Every call on a device shares that device's scratch, which keeps the
