@@ -16,9 +16,11 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libeqlin.so")
 SOURCES = ("eqlin_api.hip", "eqlin_kernels.hip", "eqlin_kernels_c8.hip", "eqlin_kernels_p4m.hip", "eqconv_kernels.hip")
-# measured ceilings of the GPU (matrix-core rates, LDS reads, HBM copy): a standalone program
-CEILINGS_SRC = "ceilings.hip"
-CEILINGS = os.path.join(LIBDIR, "eqlin_ceilings")
+# standalone programs: the measured ceilings of the GPU (matrix-core rates, LDS
+# reads, HBM copy) and the stage timeline of the forward tile
+PROGRAMS = {"ceilings.hip": os.path.join(LIBDIR, "eqlin_ceilings"),
+            "stage_trace.hip": os.path.join(LIBDIR, "eqlin_stage_trace")}
+CEILINGS = PROGRAMS["ceilings.hip"]
 ARCH = "gfx950"
 
 
@@ -54,10 +56,11 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
         objs.append(obj)
-    ceil_cmd = [hipcc_path(), *compile_flags(), os.path.join(CSRC, CEILINGS_SRC), "-o", CEILINGS + ".tmp"]
-    if verbose:
-        print(" ".join(ceil_cmd), flush=True)
-    procs.append((CEILINGS_SRC, subprocess.Popen(ceil_cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+    for src, exe in PROGRAMS.items():
+        cmd = [hipcc_path(), *compile_flags(), os.path.join(CSRC, src), "-o", exe + ".tmp"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
     failed = []
     for src, p in procs:
         out, _ = p.communicate()
@@ -74,7 +77,8 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
-    os.replace(CEILINGS + ".tmp", CEILINGS)
+    for exe in PROGRAMS.values():
+        os.replace(exe + ".tmp", exe)
     return LIB
 
 

@@ -58,6 +58,38 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
+
+// Stage timestamps of the forward tile, for the diagnostic program
+// stage_trace.hip, which defines EQLIN_STAGE_TRACE before including this
+// header; in the library the hook is empty.  Event ev of workgroup b: the
+// shader clock and the 100 MHz real-time counter, written by thread 0 to
+// g_stage_trace[(b * 64 + ev) * 2 + {0, 1}] (b < 8192; event 61 holds the
+// wave's hardware id).  Events: 0 start, 1 first stage in LDS, 2 first stage
+// multiplied, 3 last stage multiplied, 62 output stores issued, 63 stores
+// completed.
+#ifdef EQLIN_STAGE_TRACE
+__device__ unsigned long long* g_stage_trace;
+__device__ __forceinline__ void stage_mark(int ev) {
+  unsigned long long* t = g_stage_trace;
+  if (threadIdx.x == 0 && t != nullptr && blockIdx.x < 8192) {
+    t[(blockIdx.x * 64 + ev) * 2] = __builtin_amdgcn_s_memtime();
+    t[(blockIdx.x * 64 + ev) * 2 + 1] = __builtin_amdgcn_s_memrealtime();
+    if (ev == 0) {
+      unsigned id;
+      asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(id));
+      t[(blockIdx.x * 64 + 61) * 2] = id;
+    }
+  }
+}
+// the tile's output stores have completed
+__device__ __forceinline__ void stage_mark_drained() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  stage_mark(63);
+}
+#else
+__device__ __forceinline__ void stage_mark(int) {}
+__device__ __forceinline__ void stage_mark_drained() {}
+#endif
 constexpr int kNumXcd = 8;
 // LDS stage buffers of the dw partial tiles and of the dX tiles inside the
 // fused backward (1: smaller LDS, more resident workgroups per CU), and the
@@ -1218,12 +1250,18 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
     __syncthreads();
   };
 
+  stage_mark(0);
   load(0, S0{});
   store(lds, S0{});
   if constexpr (PF == 1) {
     load(1, S0{});
     __syncthreads();
-    for (int ks = 0; ks < ksteps; ++ks) step(ks, S0{});
+    stage_mark(1);
+    for (int ks = 0; ks < ksteps; ++ks) {
+      step(ks, S0{});
+      if (ks == 0) stage_mark(2);
+    }
+    stage_mark(3);
   } else {
     // ring: stage s lives in slot (s + 1) % 2 once stage 0 has been stored
     load(1, S1{});
@@ -1274,6 +1312,8 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
     }
   }
   fwd_epilogue<E, G, FM, FN, WM, WN, HALF>(acc, row0, col0, out, row_end, mg, bias, act, res);
+  stage_mark(62);
+  stage_mark_drained();
 }
 
 // Persistent forward: workgroup `first` runs the tiles first, first + stride,
