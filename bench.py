@@ -33,6 +33,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -294,22 +295,22 @@ def conv_bench(args):
             if events is not None:
                 events[ph][1].record()
 
-    t_settle = time.perf_counter()
-    while time.perf_counter() - t_settle < args.settle:
-        run_steps(0, 2)
-        torch.cuda.synchronize()
-    if args.warmup:
-        run_steps(0, args.warmup)
-    torch.cuda.synchronize()
-    print(f"# warmup done ({args.warmup} steps after {args.settle} s of clock settle, {nsets} buffer sets)",
-          file=sys.stderr, flush=True)
     K = args.steps
     evs = {ph: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for ph in phases}
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    run_steps(0, K, evs)
-    torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / K
+    with NoGC():
+        t_settle = time.perf_counter()
+        while time.perf_counter() - t_settle < args.settle:
+            run_steps(0, 2)
+            torch.cuda.synchronize()
+        if args.warmup:
+            run_steps(0, args.warmup)
+        torch.cuda.synchronize()
+        print(f"# warmup done ({args.warmup} steps after {args.settle} s of clock settle, {nsets} buffer sets)",
+              file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        run_steps(0, K, evs)
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / K
     us = {ph: evs[ph][0].elapsed_time(evs[ph][1]) * 1e3 / K for ph in phases}
 
     ck = L.C * L.K * L.K
@@ -414,6 +415,24 @@ def conv_bench(args):
     print(json.dumps(out), flush=True)
 
 
+class NoGC:
+    """No garbage-collector pass from the clock settle to the end of the timed
+    steps: a pass over the objects of earlier workloads can stall the
+    launching thread long enough to starve the GPU in phases of short
+    launches.  The collection runs before the settle, never between warmup
+    and timing: an idle GPU drops its clocks within milliseconds (measured:
+    a collection there made every timed kernel about 15% slower)."""
+
+    def __enter__(self):
+        gc.collect()
+        self.was_enabled = gc.isenabled()
+        gc.disable()
+
+    def __exit__(self, *exc):
+        if self.was_enabled:
+            gc.enable()
+
+
 def run_linear(args, workload, dtype, group, with_cpu):
     """One linear-layer workload: inputs to HBM, the timed steps, the dense
     comparator; returns the bench dictionary (not printed)."""
@@ -484,26 +503,25 @@ def run_linear(args, workload, dtype, group, with_cpu):
                 if events is not None:
                     events[li][p][1].record()
 
-    # untimed clock settle: the GPU ramps its clocks over the first tens of
-    # milliseconds of work, longer than a few warmup steps take
-    t_settle = time.perf_counter()
-    while time.perf_counter() - t_settle < args.settle:
-        run_steps(0, 4)
-        torch.cuda.synchronize()
-    if args.warmup:
-        run_steps(0, args.warmup)
-    torch.cuda.synchronize()
-    print(f"# warmup done ({args.warmup} steps after {args.settle} s of clock settle, {nsets} buffer sets)",
-          file=sys.stderr, flush=True)
-
     K = args.steps
     evs = [{p: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for p in phases}
            for _ in layers]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    run_steps(0, K, evs)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with NoGC():
+        # untimed clock settle: the GPU ramps its clocks over the first tens of
+        # milliseconds of work, longer than a few warmup steps take
+        t_settle = time.perf_counter()
+        while time.perf_counter() - t_settle < args.settle:
+            run_steps(0, 4)
+            torch.cuda.synchronize()
+        if args.warmup:
+            run_steps(0, args.warmup)
+        torch.cuda.synchronize()
+        print(f"# warmup done ({args.warmup} steps after {args.settle} s of clock settle, {nsets} buffer sets)",
+              file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        run_steps(0, K, evs)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
 
     ph_us = {p: [0.0] * len(layers) for p in ("prepare", "forward", "backward")}
