@@ -3,11 +3,16 @@
 // 32x32x2 and f16 32x32x16, every SIMD running independent back-to-back
 // products), the rate of 16-byte LDS reads per compute unit (the operand
 // reads of the product tiles), and the HBM rate of a device-to-device copy.
-// A standalone program (not part of the library); prints one JSON line.
+// Then the f16 product rate against the waves per SIMD and the independent
+// accumulator chains per wave (how much issue parallelism the matrix core
+// needs).  A standalone program (not part of the library); prints one JSON
+// line of ceilings and one of the rate table.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
+
+#include <type_traits>
 
 namespace {
 
@@ -28,7 +33,7 @@ constexpr int kChains = 4;   // independent accumulators per wave
 
 // KIND 0: v_mfma_f32_32x32x2_f32 (4096 FLOP), KIND 1: v_mfma_f32_32x32x16_f16 (32768 FLOP).
 // Operands come from the lane id, the sums are written once (one float per thread).
-template <int KIND>
+template <int KIND, int kChains = kChains>
 __global__ void __launch_bounds__(256) mfma_loop(float* out, int iters) {
   const int lane = threadIdx.x & 63;
   f32x16 acc[kChains];
@@ -122,6 +127,29 @@ int main() {
   const double cms = time_ms([&] { CHECK(hipMemcpyAsync(dst, src, nbytes, hipMemcpyDeviceToDevice, 0)); }, 10);
   const double copy_gbs = 2.0 * (double)nbytes / (cms * 1e-3) / 1e9;
   CHECK(hipDeviceSynchronize());
+
+  // f16 rate against waves per SIMD (1, 2, 4: 1, 2, 4 workgroups of four
+  // waves per CU) and independent chains per wave (1, 2, 4, 8)
+  printf("{\"f16_32x32x16_rate\": [");
+  bool first = true;
+  for (int wps : {1, 2, 4}) {
+    const int nb = cus * wps;
+    auto row = [&](auto chains_c) {
+      constexpr int ch = decltype(chains_c)::value;
+      const int it = 16000 / ch;
+      const double ms =
+          time_ms([&] { hipLaunchKernelGGL((mfma_loop<1, ch>), dim3(nb), dim3(256), 0, 0, out, it); }, 5);
+      const double tf = (double)nb * 4 * it * ch * 32768.0 / (ms * 1e-3) / 1e12;
+      printf("%s{\"waves_per_simd\": %d, \"chains_per_wave\": %d, \"tflops\": %.1f, \"cycles_per_mfma_at_peak_clock\": %.1f}",
+             first ? "" : ", ", wps, ch, tf, (double)cus * 4 * (prop.clockRate * 1e3) * 32768.0 / (tf * 1e12));
+      first = false;
+    };
+    row(std::integral_constant<int, 1>{});
+    row(std::integral_constant<int, 2>{});
+    row(std::integral_constant<int, 4>{});
+    row(std::integral_constant<int, 8>{});
+  }
+  printf("]}\n");
 
   printf("{\"device\": \"%s\", \"compute_units\": %d, \"peak_clock_mhz\": %d, "
          "\"mfma_f32_32x32x2_tflops\": %.1f, \"mfma_f32_32x32x2_frac_of_157.3\": %.3f, "
