@@ -5,7 +5,9 @@
 // reads of the product tiles), and the HBM rate of a device-to-device copy.
 // Then the f16 product rate against the waves per SIMD and the independent
 // accumulator chains per wave (how much issue parallelism the matrix core
-// needs).  A standalone program (not part of the library); prints one JSON
+// needs), and the rate of 16-byte global loads that hit the caches, in the
+// shape of a forward stage (a 128-row x 256-byte window per workgroup, rows
+// 2560 bytes apart, 64 or 256 contiguous bytes per row and instruction).  A standalone program (not part of the library); prints one JSON
 // line of ceilings and one of the rate table.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -76,6 +78,30 @@ __global__ void __launch_bounds__(256) lds_loop(float* out, int iters) {
     idx += 64;
   }
   out[blockIdx.x * blockDim.x + t] = s[0] + s[1] + s[2] + s[3];
+}
+
+// Workgroup b reads 128 rows x 256 bytes of slab b % 64 per iteration,
+// advancing 256 bytes per iteration over ten columns (a 21 MB array, rows
+// 2560 bytes apart: an f16 ViT-H input): LPR lanes per row, each loading
+// 16 / LPR 16-byte units of it.
+template <int LPR>
+__global__ void __launch_bounds__(512) load_loop(const char* __restrict__ src, int iters, unsigned* out) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  constexpr unsigned kRowBytes = 2560;
+  constexpr int RPP = 512 / LPR, UPL = 16 / LPR;
+  const int t = threadIdx.x, q = t % LPR, r = t / LPR;
+  const unsigned slab = (blockIdx.x % 64) * 128u;
+  u32x4 acc = {0, 0, 0, 0};
+  for (int it = 0; it < iters; ++it) {
+    const unsigned col = (unsigned)(it % 10) * 256u;
+#pragma unroll
+    for (int ps = 0; ps < 128 / RPP; ++ps)
+#pragma unroll
+      for (int u = 0; u < UPL; ++u)
+        acc += *reinterpret_cast<const u32x4*>(src + (slab + ps * RPP + r) * kRowBytes + col +
+                                               (unsigned)(q + LPR * u) * 16u);
+  }
+  if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x9e3779b9u) out[0] = acc[0];   // keeps the loads
 }
 
 template <typename K>
@@ -150,6 +176,23 @@ int main() {
     row(std::integral_constant<int, 8>{});
   }
   printf("]}\n");
+
+  // cache-resident 16-byte loads in the shape of a forward stage
+  {
+    const size_t nsrc = (size_t)64 * 128 * 2560;
+    char* src = nullptr;
+    CHECK(hipMalloc(&src, nsrc));
+    CHECK(hipMemset(src, 1, nsrc));
+    const int lb = 1024, lit = 200;
+    const double lbytes = (double)lb * lit * 128 * 256;
+    const double l64 = time_ms([&] { hipLaunchKernelGGL(load_loop<4>, dim3(lb), dim3(512), 0, 0, src, lit, (unsigned*)out); }, 5);
+    const double l256 = time_ms([&] { hipLaunchKernelGGL(load_loop<16>, dim3(lb), dim3(512), 0, 0, src, lit, (unsigned*)out); }, 5);
+    printf("{\"cached_load_tb_per_s_64B_rows\": %.2f, \"cached_load_tb_per_s_256B_rows\": %.2f, "
+           "\"cached_load_bytes_per_clk_per_cu_at_peak_clock\": %.1f}\n",
+           lbytes / (l64 * 1e-3) / 1e12, lbytes / (l256 * 1e-3) / 1e12,
+           lbytes / (l64 * 1e-3) / cus / (prop.clockRate * 1e3));
+    CHECK(hipFree(src));
+  }
 
   printf("{\"device\": \"%s\", \"compute_units\": %d, \"peak_clock_mhz\": %d, "
          "\"mfma_f32_32x32x2_tflops\": %.1f, \"mfma_f32_32x32x2_frac_of_157.3\": %.3f, "
