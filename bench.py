@@ -123,10 +123,13 @@ def profile_tag(workload, dt, group):
     return f"{workload}_{dt}" + {"4": "", "8": "_c8", "p4m": "_p4m"}[str(group)]
 
 
-def profiled_traffic(tag, kernel_name):
+def profiled_traffic(tag, kernel_name, nlayers=1):
     """HBM bytes per launch of `kernel_name` from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is no
-    summary for this workload or the kernel sources changed since it was taken."""
+    summary for this workload or the kernel sources changed since it was taken.
+    The summary keeps one row per grid size; with nlayers > 1 (one launch per
+    layer, the layers' grids distinct) the rows are summed, and a count other
+    than nlayers gives None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{tag}.json")
     try:
         with open(path) as f:
@@ -134,6 +137,8 @@ def profiled_traffic(tag, kernel_name):
         if kernel_source_sha256() != d["source_sha256"]:
             return None
         rows = [r for k, v in d["kernels"].items() if k.startswith(kernel_name) for r in v]
+        if nlayers > 1:
+            return sum(r["bytes"] for r in rows) if len(rows) == nlayers else None
         return max(r["bytes"] for r in rows) if rows else None
     except (OSError, KeyError, ValueError):
         return None
@@ -540,7 +545,7 @@ def run_linear(args, workload, dtype, group, with_cpu):
     peak = PEAK_TFLOPS[dt]
     es_b = 4 if dt == "f32" else 2
     bound, alg_bytes, _ = layer_roofline([L for (L, _, _, _) in layers], es_b, T, exec_frac, peak)
-    traffic = profiled_traffic(profile_tag(wl.name, dt, group), "eqlin::fwd_kernel") if len(layers) == 1 else None
+    traffic = profiled_traffic(profile_tag(wl.name, dt, group), "eqlin::fwd_kernel", len(layers))
     gbs = alg_bytes / (fwd_us * 1e-6) / 1e9
     hbm_bound = bound == "hbm"
     roofline = {"bound": "hbm" if hbm_bound else "mfma", "kernel": "eqlin::fwd_kernel",

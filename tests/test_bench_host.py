@@ -49,3 +49,23 @@ def test_per_config_entries_name_measured_workloads():
     for name, dt in bench.PER_CONFIG:
         assert name in WORKLOADS and dt in WORKLOADS[name].dtypes, (name, dt)
     assert ("vith_mlp", "f32") in bench.PER_CONFIG and ("vith_mlp", "f16") in bench.PER_CONFIG
+
+
+def test_profiled_traffic_sums_one_row_per_layer(tmp_path, monkeypatch):
+    # a summary keeps one row per grid size: one launch per layer sums them, a
+    # row count other than the layer count (grids that coincide) gives no figure,
+    # and a summary of other kernel sources gives none either
+    import json
+    (tmp_path / "profiles").mkdir()
+    rows = {"eqlin::fwd_kernel<_Float16, 4>": [{"grid": 1, "bytes": 10.0}, {"grid": 2, "bytes": 32.0}],
+            "eqlin::dw_finalize_kernel<4, true>": [{"grid": 3, "bytes": 5.0}]}
+    doc = {"source_sha256": "1" * 64, "kernels": rows}
+    (tmp_path / "profiles" / "traffic_pair.json").write_text(json.dumps(doc))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_sha256", lambda: "1" * 64)
+    assert bench.profiled_traffic("pair", "eqlin::fwd_kernel", 2) == 42.0
+    assert bench.profiled_traffic("pair", "eqlin::fwd_kernel", 3) is None
+    assert bench.profiled_traffic("pair", "eqlin::fwd_kernel") == 32.0
+    doc["source_sha256"] = "0" * 64
+    (tmp_path / "profiles" / "traffic_pair.json").write_text(json.dumps(doc))
+    assert bench.profiled_traffic("pair", "eqlin::fwd_kernel", 2) is None
