@@ -76,15 +76,23 @@ def parse():
     return p.parse_args()
 
 
+# standalone diagnostic programs beside the library's sources (not in its kernels)
+_NOT_LIBRARY = ("ceilings.hip", "stage_trace.hip")
+
+
 def kernel_source_sha256():
-    """sha256 over the library's HIP sources and headers (sorted by name)."""
+    """sha256 over the library's HIP sources and headers (sorted by name), without
+    their blank and whole-line comment lines, so that a profile stays matched to
+    the kernels it measured across edits of comments only."""
     import hashlib
     csrc = os.path.join(ROOT, "group_circulant_linear_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
+        if name.endswith((".hip", ".h")) and name not in _NOT_LIBRARY:
             with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+                code = [l.rstrip() for l in f.read().split(b"\n")]
+            code = [l for l in code if l.strip() and not l.lstrip().startswith(b"//")]
+            h.update(name.encode() + b"\0" + b"\n".join(code))
     return h.hexdigest()
 
 

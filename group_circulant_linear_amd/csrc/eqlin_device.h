@@ -106,12 +106,13 @@ constexpr int kRowBytes = 64;
 __device__ __forceinline__ int swz_slot(int row, int slot) { return slot ^ ((row >> 2) & 3); }
 
 // The dw tile's placement of the same 64-byte plane rows (rows = group
-// channels, k along the batch rows).  Its f16 p4 writes are transposed: eight
-// lanes fill the eight 8-byte runs of one row and a 32-lane write spans four
-// rows two apart, so row r goes to physical row dw_row(r) (the low three bits
-// rotated to b1 b2 b0, which puts those four rows in distinct 64-byte bank
-// windows) and its 16-byte slots are XOR-ed with bits 0 and 3 of r; sixteen
-// consecutive rows of a fragment read then also meet all 64 banks once.
+// channels, k along the batch rows).  Its f16 p4 writes are transposed: a
+// 32-lane write covers eight rows two apart (the two groups' rows of eight
+// consecutive unit columns), four 8-byte runs in each.  Row r goes to
+// physical row dw_row(r) (the low three bits rotated to b1 b2 b0) and its
+// 16-byte slots are XOR-ed with bits 0 and 3 of r, which spreads those 32
+// runs over all 64 banks; sixteen consecutive rows of a fragment read also
+// meet all 64 banks once.
 __device__ __forceinline__ int dw_row(int r) { return (r & ~7) | ((r >> 1) & 3) | ((r & 1) << 2); }
 __device__ __forceinline__ int dw_slot(int r, int slot) { return slot ^ ((r & 1) | (((r >> 3) & 1) << 1)); }
 __device__ __forceinline__ int dw_off(int r, int kb) {

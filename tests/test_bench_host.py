@@ -69,3 +69,19 @@ def test_profiled_traffic_sums_one_row_per_layer(tmp_path, monkeypatch):
     doc["source_sha256"] = "0" * 64
     (tmp_path / "profiles" / "traffic_pair.json").write_text(json.dumps(doc))
     assert bench.profiled_traffic("pair", "eqlin::fwd_kernel", 2) is None
+
+
+def test_kernel_source_sha_ignores_comment_lines(tmp_path, monkeypatch):
+    # the profiles' key changes with the kernels' code, not with comments, blank
+    # lines or the standalone diagnostic programs beside the sources
+    csrc = tmp_path / "group_circulant_linear_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (csrc / "k.hip").write_text("int f() {\n  return 1;   // one\n}\n")
+    base = bench.kernel_source_sha256()
+    (csrc / "k.hip").write_text("// a comment\nint f() {\n\n  return 1;   // one\n}\n")
+    assert bench.kernel_source_sha256() == base
+    (csrc / "stage_trace.hip").write_text("int main() { return 0; }\n")
+    assert bench.kernel_source_sha256() == base
+    (csrc / "k.hip").write_text("int f() {\n  return 2;   // one\n}\n")
+    assert bench.kernel_source_sha256() != base
