@@ -356,6 +356,24 @@ def test_backward_wide_f16_layers():
         assert e1 <= TOL["f16"] and e2 <= TOL["f16"]
 
 
+@pytest.mark.parametrize("C,D", [(1280, 5120), (5120, 1280)])
+def test_backward_fused_fallback_f32(C, D):
+    """fp32 p4 layers of the ViT-H widths over 2056 rows: one dw split per CU
+    would run 65 stages against 26100 stage units of work (over 1.75 x the
+    average per resident workgroup), so the fused launch takes its two-per-CU
+    fallback, whose split count rounds up (512 / 100 dw tiles -> 6 splits of
+    352 rows, the last 296)."""
+    N = 2056
+    say(f"backward fused fallback f32 N={N} C={C} D={D}")
+    X, w, dY = make_layer_inputs(N, C, D, "f32", seed=28)
+    Wh = prep(w, 4)
+    dX, dw = eq.eqlin_backward(dev(dY), dev(X), Wh)
+    dXr, dwr = oracle.backward_direct(dY, X, w)
+    e1, e2 = rel_err(host(dX), dXr), rel_err(host(dw), dwr)
+    say(f"  dX rel err {e1:.3e}  dw rel err {e2:.3e}")
+    assert e1 <= TOL["f32"] and e2 <= TOL["f32"]
+
+
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 def test_backward_workload_narrow(dt):
     """The HBM-bound narrow layer (16 group channels, 201728 rows): dw reduces
@@ -679,3 +697,23 @@ def test_f16_operand_range_forward_tiles(tile, monkeypatch):
     say(f"  tile {tile}: Y {e1:.2e}  bias+GELU {e2:.2e}")
     assert np.all(np.isfinite(Y)) and np.all(np.isfinite(Yg))
     assert e1 <= TOL["f16"] and e2 <= TOL["f16"]
+
+
+def test_stage_trace_program_runs():
+    """The stage-timeline diagnostic (csrc/stage_trace.hip, built beside the
+    library) traces one launch of each of its four layer shapes: every line
+    has its rounds, each with a positive stage time, within the launch."""
+    import json
+    import os
+    import subprocess
+    exe = os.path.join(os.path.dirname(eq.LIB), "eqlin_stage_trace")
+    assert os.path.exists(exe), "stage trace program not built"
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=120, check=True).stdout
+    lines = [json.loads(l) for l in out.splitlines() if l.startswith("{")]
+    assert [l["layer"] for l in lines] == ["vith_fc1", "vith_fc2", "vitb_fc1", "vitb_attn"]
+    for l in lines:
+        say(f"  {l['layer']} {l['dtype']}: {l['launch_us']} us, clock {l['shader_clock_ghz']} GHz")
+        assert l["launch_us"] > 0 and l["groups"]
+        assert sum(g["workgroups"] for g in l["groups"]) == l["workgroups"]
+        for g in l["groups"]:
+            assert 0 < g["stage_us"] < l["launch_us"] and g["end_us"][1] <= 2 * l["launch_us"]
