@@ -1876,9 +1876,14 @@ dw_partial_kernel(const E* __restrict__ dy, const E* __restrict__ x, float* __re
                   int64_t nrows, int mg, int ng, int64_t rows_per_split, int tiles_m, int tiles_n, int cw_m,
                   int cw_n) {
   static_assert(W == 64 || G == 4, "the 128-wide dw tile is built for p4");
-  __shared__ __attribute__((aligned(16))) char lds[dw_lds_bytes<Grp<G>::kOrder, kDwBufs, W>()];
-  dw_tile<E, G, kDwBufs, false, W>(lds, xcd_logical_id(blockIdx.x, gridDim.x), dy, x, ws, nrows, mg, ng,
-                                   rows_per_split, tiles_m, tiles_n, cw_m, cw_n);
+  // The 128-wide tile runs one workgroup per CU (registers), so its LDS has
+  // room for two stage buffers: the next chunk's loads are written while the
+  // current one is multiplied, one barrier per chunk instead of two.  The
+  // 64-wide tile gained nothing from a second buffer (measured), so it keeps one.
+  constexpr int NB = W == 128 ? 2 : kDwBufs;
+  __shared__ __attribute__((aligned(16))) char lds[dw_lds_bytes<Grp<G>::kOrder, NB, W>()];
+  dw_tile<E, G, NB, false, W>(lds, xcd_logical_id(blockIdx.x, gridDim.x), dy, x, ws, nrows, mg, ng,
+                              rows_per_split, tiles_m, tiles_n, cw_m, cw_n);
 }
 
 // Backward in one launch: the first ndw_pad workgroups are dw split partials,
