@@ -387,6 +387,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   const uint32_t n = bytes > 0x7ffffff0ull ? 0x7ffffff0u : (uint32_t)bytes;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
 }
+// The same resource as four scalar words (an inline-assembly operand).
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes > 0x7ffffff0ull ? 0x7ffffff0u : (uint32_t)bytes;
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  auto uni = [](uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); };
+  return u32x4{uni((uint32_t)a), uni((uint32_t)(a >> 32) & 0xffffu), uni(n), 0x00020000u};
+}
 __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
@@ -400,6 +407,30 @@ __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t of
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Direct global-to-LDS load of 16 bytes per lane (gfx950): lane l's bytes land
+// at LDS address lds_addr + 16 l (wave-uniform lds_addr, through M0); a lane
+// whose offset is out of the buffer's range writes zeros.  Issued from inline
+// assembly so that the compiler's wait-count analysis does not see it: the
+// compiler would otherwise wait for every such load before each LDS read.
+// The caller orders it so that a wait the compiler emits for a later
+// ordinary load also covers it (vector-memory loads complete in issue order),
+// and `dep` (any register the asm must follow) pins it after a given
+// instruction.  M0 is saved and restored around it.
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff, uint32_t dep) {
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0 ; after %5"
+      : "=&s"(keep)
+      : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff), "v"(dep)
+      : "memory");
+}
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ __forceinline__ uint32_t lds_address(const char* p) { return (uint32_t)(uintptr_t)(lds_char*)p; }
 
 // Blocks are dispatched round-robin over the 8 XCDs.  Renumber so that
 // consecutive logical tile ids land on the same XCD (and share its L2).
@@ -887,9 +918,12 @@ __device__ __forceinline__ void interleave_schedule() {
 // 16-byte pieces are copied to LDS unchanged.  Global loads are buffer loads:
 // addresses past the end of the tile's range (rows >= nrows) or flagged out
 // of range (groups >= kg) return zeros without branches.
+// NBUF = 3 (weight operand by DMA, see fwd_tile): two buffers of the
+// transformed input and three of the weight planes.
 template <typename E, int T, int FM, int FN, int WM, int WN, int NBUF>
 constexpr int fwd_lds_bytes() {
-  return NBUF * T * (32 * FM * WM + 32 * FN * WN) * kRowBytes;
+  return NBUF == 3 ? T * (2 * 32 * FM * WM + 3 * 32 * FN * WN) * kRowBytes
+                   : NBUF * T * (32 * FM * WM + 32 * FN * WN) * kRowBytes;
 }
 
 // Epilogue of a forward / dX tile: inverse group DFT in registers, optional
@@ -1096,8 +1130,14 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
   constexpr int BLOCK = T * kRowBytes;      // bytes of one prepared stage block
   constexpr int RPP = NT / 4;               // tile rows covered per load pass
   constexpr int PA = (BM + RPP - 1) / RPP, PB = (BN + RPP - 1) / RPP;
-  static_assert(NBUF * BUF == fwd_lds_bytes<E, T, FM, FN, WM, WN, NBUF>(), "LDS size");
+  // NBUF = 3: the weight operand goes from memory straight into LDS (dma16)
+  // through three buffers, two stages ahead like the input's register ring;
+  // the transformed input keeps two buffers.  Otherwise NBUF buffers of both.
+  constexpr bool kDma = NBUF == 3;
+  constexpr int XBUF = kDma ? T * A_PLANE : BUF, WBUF = kDma ? T * B_PLANE : BUF;
+  static_assert((kDma ? 2 * XBUF + 3 * WBUF : NBUF * BUF) == fwd_lds_bytes<E, T, FM, FN, WM, WN, NBUF>(), "LDS size");
   static_assert(!HALF || fwd_tail_split_fits(sizeof(E) == 4, FM, FN, WM, WN, NBUF), "tail split");
+  static_assert(!kDma || (PF == 1 && !HALF), "weight DMA: one register stage, whole tiles");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t tile = HALF ? lid >> 1 : lid;
@@ -1116,6 +1156,35 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
       make_rsrc(wp + (int64_t)col0 * ksteps * SG * T, (uint64_t)(mg - col0) * (uint64_t)ksteps * BLOCK);
 
   const int q = tid & 3, rl = tid >> 2;
+  // Weight DMA: a stage's T x BN plane rows are blocks of 16 rows (1 KB,
+  // one DMA of a wave); wave w copies blocks w KD .. w KD + KD - 1.  Lane l
+  // fills physical slot l % 4 of block row l / 4, so it reads the logical
+  // slot that the XOR swizzle puts there (bits 2-3 of the row are bits 4-5
+  // of l).  Rows past the layer's groups are out of range and land as zeros.
+  constexpr int KD = kDma ? T * BN / 16 / (NT / 64) : 1;
+  static_assert(!kDma || KD * (NT / 64) * 16 == T * BN, "whole 16-row blocks per wave");
+  u32x4 b_words{};
+  uint32_t dma_off[KD], dma_lds[KD];
+  if constexpr (kDma) {
+    b_words = rsrc_words(wp + (int64_t)col0 * ksteps * SG * T, (uint64_t)(mg - col0) * (uint64_t)ksteps * BLOCK);
+#pragma unroll
+    for (int i = 0; i < KD; ++i) {
+      const int j = wave * KD + i, p = j / (BN / 16), blk = j % (BN / 16);
+      const int m = blk * 16 + (lane >> 2), slot = (lane & 3) ^ ((lane >> 4) & 3);
+      dma_off[i] = (uint32_t)m * (uint32_t)ksteps * BLOCK + p * 64 + slot * 16;
+      dma_lds[i] = __builtin_amdgcn_readfirstlane((uint32_t)(p * B_PLANE + blk * 16 * STRIDE));
+    }
+  }
+  // W buffer of stage s (DMA mode) and its LDS address
+  auto wbuf = [&](int s) -> char* { return lds + 2 * XBUF + (s % 3) * WBUF; };
+  // copy the weight block of stage ks into its buffer; `dep` orders the copy
+  // after the input loads it follows (see step)
+  auto dma_w = [&](int ks, uint32_t dep) {
+    const uint32_t soffb = __builtin_amdgcn_readfirstlane((uint32_t)(ks < ksteps ? ks : ksteps - 1) * (uint32_t)BLOCK);
+    const uint32_t base = lds_address(wbuf(ks));
+#pragma unroll
+    for (int i = 0; i < KD; ++i) dma16(b_words, __builtin_amdgcn_readfirstlane(base + dma_lds[i]), dma_off[i], soffb, dep);
+  };
   u32x4 ra[PF][PA][T], rb[PF][PB][T];   // register ring of PF stages of loads
 
   // convolution: pixel of each A row this lane loads, and per ring slot
@@ -1173,17 +1242,30 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
     }
     // weights: past the last stage the loads re-read it (the pipeline's idle
     // stage, never multiplied), so the scalar offset stays inside each row
-    const uint32_t soffb = (uint32_t)(ks < ksteps ? ks : ksteps - 1) * (uint32_t)BLOCK;
+    if constexpr (!kDma) {
+      const uint32_t soffb = (uint32_t)(ks < ksteps ? ks : ksteps - 1) * (uint32_t)BLOCK;
 #pragma unroll
-    for (int ps = 0; ps < PB; ++ps) {
-      const uint32_t m = (uint32_t)(ps * RPP + rl);
+      for (int ps = 0; ps < PB; ++ps) {
+        const uint32_t m = (uint32_t)(ps * RPP + rl);
 #pragma unroll
-      for (int p = 0; p < T; ++p)
-        rb[sl][ps][p] = bload16s(b_src, m * (uint32_t)ksteps * BLOCK + p * 64 + q * 16, soffb);
+        for (int p = 0; p < T; ++p)
+          rb[sl][ps][p] = bload16s(b_src, m * (uint32_t)ksteps * BLOCK + p * 64 + q * 16, soffb);
+      }
     }
   };
-  auto store = [&](char* buf, auto slot_c) {
+  // Transform the input registers of a stage into buf; in DMA mode first
+  // copy the weight block of stage dma_ks, after every input register of the
+  // stage has arrived (the copy's operand `dep` is made of them).
+  auto store = [&](char* buf, auto slot_c, int dma_ks) {
     constexpr int sl = decltype(slot_c)::value;
+    if constexpr (kDma) {
+      uint32_t dep = 0;
+#pragma unroll
+      for (int ps = 0; ps < PA; ++ps)
+#pragma unroll
+        for (int i = 0; i < T; ++i) dep ^= ra[sl][ps][i][0];
+      dma_w(dma_ks, dep);
+    }
 #pragma unroll
     for (int ps = 0; ps < PA; ++ps) {
       const int r = ps * RPP + rl;
@@ -1201,7 +1283,7 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
       }
     }
 #pragma unroll
-    for (int ps = 0; ps < PB; ++ps) {
+    for (int ps = 0; ps < (kDma ? 0 : PB); ++ps) {
       const int m = ps * RPP + rl;
       if (BN % RPP == 0 || m < BN) {
 #pragma unroll
@@ -1236,24 +1318,34 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
   // freed.  Past the last stage the loads read zeros (out of range) and the
   // stores fill an idle buffer, so the body is one basic block in which the
   // scheduler can interleave MFMAs with the transform, LDS writes and loads.
+  //
+  // DMA mode: the weight block of stage ks + 2 is copied during step ks, into
+  // the buffer stage ks - 1 used (free since the previous barrier), right
+  // after the input registers of stage ks + 1 have arrived and before the
+  // input loads of stage ks + 2 are issued.  Loads complete in issue order,
+  // so the wait for those input registers in step ks + 1 (before they are
+  // transformed, and so before that step's barrier) also covers the copy.
   auto step = [&](int ks, auto slot_next) {
-    char* cur = lds + (NBUF == 2 ? (ks & 1) * BUF : 0);
+    const char* cur = lds + (kDma ? (ks & 1) * XBUF : NBUF == 2 ? (ks & 1) * BUF : 0);
+    const char* bcur = kDma ? wbuf(ks) - T * A_PLANE : cur;   // b_frag counts from the A planes
     if constexpr (HALF) {
-      mma_chunk<E, G, false, FM, FN>(acc, cur + a_frag + cw, A_PLANE, cur + b_frag + cw, B_PLANE, STRIDE);
+      mma_chunk<E, G, false, FM, FN>(acc, cur + a_frag + cw, A_PLANE, bcur + b_frag + cw, B_PLANE, STRIDE);
     } else {
-      mma_chunk<E, G, false, FM, FN>(acc, cur + a_frag + c0, A_PLANE, cur + b_frag + c0, B_PLANE, STRIDE);
-      mma_chunk<E, G, false, FM, FN>(acc, cur + a_frag + c1, A_PLANE, cur + b_frag + c1, B_PLANE, STRIDE);
+      mma_chunk<E, G, false, FM, FN>(acc, cur + a_frag + c0, A_PLANE, bcur + b_frag + c0, B_PLANE, STRIDE);
+      mma_chunk<E, G, false, FM, FN>(acc, cur + a_frag + c1, A_PLANE, bcur + b_frag + c1, B_PLANE, STRIDE);
     }
     if constexpr (NBUF == 1) __syncthreads();   // every wave is done reading the only buffer
-    store(lds + (NBUF == 2 ? ((ks + 1) & 1) * BUF : 0), slot_next);
+    store(lds + (kDma ? ((ks + 1) & 1) * XBUF : NBUF == 2 ? ((ks + 1) & 1) * BUF : 0), slot_next, ks + 2);
     load(ks + 1 + PF, slot_next);
+    // (the DMA mode runs faster with the compiler's own order: measured)
     if constexpr (SCHED == 1 && NBUF == 2 && !HALF) interleave_schedule<E, G, FM, FN, PA, PB>();
     __syncthreads();
   };
 
   stage_mark(0);
+  if constexpr (kDma) dma_w(0, 0u);   // issued before the input loads of stage 0
   load(0, S0{});
-  store(lds, S0{});
+  store(lds, S0{}, 1);
   if constexpr (PF == 1) {
     load(1, S0{});
     __syncthreads();
@@ -1263,6 +1355,9 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
       if (ks == 0) stage_mark(2);
     }
     stage_mark(3);
+    // the last steps' copies (of the idle stages past the end) must land
+    // before the workgroup can leave its LDS
+    if constexpr (kDma) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   } else {
     // ring: stage s lives in slot (s + 1) % 2 once stage 0 has been stored
     load(1, S1{});
