@@ -483,6 +483,10 @@ def test_lds_buffering_is_bitwise_invisible(dt, pair, monkeypatch):
     memory into three LDS buffers (NBUF = 3) instead of through registers.
     The first shape has one k stage (the copies of the idle stages only)."""
     a, b = pair
+    if max(int(a[4]), int(b[4])) >= 3:
+        # the DMA tile runs no tail split, whose halves add their k ranges
+        # in another order: compare whole tiles with whole tiles
+        monkeypatch.setenv("EQLIN_FWD_SPLIT", "0")
     shapes = [(200, 64, 136), (1000, 160, 96), (333, 800, 520), (299 * 64 + 37, 4 * 42, 256)]
     for (N, C, D) in shapes:
         say(f"buffering {dt} tiles {a} / {b} N={N} C={C} D={D}")
