@@ -716,7 +716,7 @@ def test_stage_trace_program_runs():
     assert os.path.exists(exe), "stage trace program not built"
     out = subprocess.run([exe], capture_output=True, text=True, timeout=120, check=True).stdout
     lines = [json.loads(l) for l in out.splitlines() if l.startswith("{")]
-    assert [l["layer"] for l in lines] == ["vith_fc1", "vith_fc2", "vitb_fc1", "vitb_attn"]
+    assert [l["layer"] for l in lines] == ["vith_fc1", "vith_fc2", "vitb_fc2", "vitb_attn"]
     for l in lines:
         say(f"  {l['layer']} {l['dtype']}: {l['launch_us']} us, clock {l['shader_clock_ghz']} GHz")
         assert l["launch_us"] > 0 and l["groups"]
