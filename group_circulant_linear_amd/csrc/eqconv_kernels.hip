@@ -16,7 +16,7 @@
 namespace eqlin {
 
 // compiled convolution tiles (the p4 tile table's candidates), code = FM FN WM WN NBUF PF
-#define EQCONV_TILES(X) X(112211) X(112221) X(111211) X(212421) X(212431) X(111221)
+#define EQCONV_TILES(X) X(112211) X(112221) X(111211) X(212421) X(212431) X(112241) X(111221)
 
 namespace {
 

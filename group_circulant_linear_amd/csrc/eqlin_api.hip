@@ -86,13 +86,14 @@ struct TileShape {
 // at least a quarter of its columns empty.
 constexpr TileShape kP4F32Tiles[] = {
     {112211, 64, 64, 0.745}, {112221, 64, 64, 0.70}, {111211, 32, 64, 0.59}, {112111, 64, 32, 0.55}};
-// In f16 the 64 x 128 tile fills the chip better than 128 x 128 where the
-// larger tile leaves a CU one extra tile (ViT-B fc1: 40.0 against 43.2 us).
-// The 128 x 128 tile copies its weight operand straight into LDS (NBUF = 3):
-// 5-13% faster than through registers (212421) at the ViT shapes.
+// The f16 tiles copy their weight operand straight into LDS (NBUF 3 and 4):
+// 5-14% faster than through registers (212421, 122211, 112211) at the ViT
+// shapes and in the convolution.  The 64 x 128 tile fills the chip better
+// than 128 x 128 where the larger tile leaves a CU one extra tile (ViT-B fc1:
+// 37.6 against 43.1 us).
 constexpr TileShape kP4F16Tiles[] = {{212431, 128, 128, 0.25},
-                                     {122211, 64, 128, 0.22},
-                                     {112211, 64, 64, 0.17},
+                                     {122241, 64, 128, 0.24},
+                                     {112241, 64, 64, 0.18},
                                      {111221, 32, 64, 0.12},
                                      {1121111, 64, 32, 0.12}};
 // The p4 convolution in fp32: its gathered rows are 9x deeper than the linear
@@ -100,7 +101,7 @@ constexpr TileShape kP4F16Tiles[] = {{212431, 128, 128, 0.25},
 // once the pixel count leaves few tiles (28 x 28 and 14 x 14 maps, C = 512 and
 // 1024: 7-8% faster than 64 x 64).
 constexpr TileShape kConvF32Tiles[] = {{112211, 64, 64, 0.745}, {212421, 128, 128, 0.80}, {111211, 32, 64, 0.59}};
-constexpr TileShape kConvF16Tiles[] = {{212431, 128, 128, 0.25}, {112211, 64, 64, 0.17}, {111221, 32, 64, 0.12}};
+constexpr TileShape kConvF16Tiles[] = {{212431, 128, 128, 0.25}, {112241, 64, 64, 0.18}, {111221, 32, 64, 0.12}};
 constexpr TileShape kC8F32Tiles[] = {{112211, 64, 64, 0.58}, {112221, 64, 64, 0.55}, {111221, 32, 64, 0.31}};
 constexpr TileShape kC8F16Tiles[] = {
     {1222111, 64, 128, 0.137}, {2122111, 128, 64, 0.112}, {122211, 64, 128, 0.12}, {1122111, 64, 64, 0.105}};

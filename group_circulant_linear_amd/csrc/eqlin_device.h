@@ -918,12 +918,14 @@ __device__ __forceinline__ void interleave_schedule() {
 // 16-byte pieces are copied to LDS unchanged.  Global loads are buffer loads:
 // addresses past the end of the tile's range (rows >= nrows) or flagged out
 // of range (groups >= kg) return zeros without branches.
-// NBUF = 3 (weight operand by DMA, see fwd_tile): two buffers of the
-// transformed input and three of the weight planes.
+// NBUF = 3 and 4 copy the weight operand by DMA (see fwd_tile): NBUF = 3
+// keeps two buffers of the transformed input and three of the weight
+// planes, NBUF = 4 one of the input and two of the weights.
 template <typename E, int T, int FM, int FN, int WM, int WN, int NBUF>
 constexpr int fwd_lds_bytes() {
-  return NBUF == 3 ? T * (2 * 32 * FM * WM + 3 * 32 * FN * WN) * kRowBytes
-                   : NBUF * T * (32 * FM * WM + 32 * FN * WN) * kRowBytes;
+  return NBUF == 3   ? T * (2 * 32 * FM * WM + 3 * 32 * FN * WN) * kRowBytes
+         : NBUF == 4 ? T * (32 * FM * WM + 2 * 32 * FN * WN) * kRowBytes
+                     : NBUF * T * (32 * FM * WM + 32 * FN * WN) * kRowBytes;
 }
 
 // Epilogue of a forward / dX tile: inverse group DFT in registers, optional
@@ -1132,10 +1134,14 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
   constexpr int PA = (BM + RPP - 1) / RPP, PB = (BN + RPP - 1) / RPP;
   // NBUF = 3: the weight operand goes from memory straight into LDS (dma16)
   // through three buffers, two stages ahead like the input's register ring;
-  // the transformed input keeps two buffers.  Otherwise NBUF buffers of both.
-  constexpr bool kDma = NBUF == 3;
+  // the transformed input keeps two buffers.  NBUF = 4: one input buffer
+  // (two barriers per stage, as NBUF = 1) and two weight buffers, the copy
+  // one stage ahead.  Otherwise NBUF buffers of both.
+  constexpr bool kDma = NBUF >= 3;
+  constexpr int kXB = NBUF == 3 ? 2 : 1, kWB = NBUF == 3 ? 3 : 2;
   constexpr int XBUF = kDma ? T * A_PLANE : BUF, WBUF = kDma ? T * B_PLANE : BUF;
-  static_assert((kDma ? 2 * XBUF + 3 * WBUF : NBUF * BUF) == fwd_lds_bytes<E, T, FM, FN, WM, WN, NBUF>(), "LDS size");
+  static_assert((kDma ? kXB * XBUF + kWB * WBUF : NBUF * BUF) == fwd_lds_bytes<E, T, FM, FN, WM, WN, NBUF>(),
+                "LDS size");
   static_assert(!HALF || fwd_tail_split_fits(sizeof(E) == 4, FM, FN, WM, WN, NBUF), "tail split");
   static_assert(!kDma || (PF == 1 && !HALF), "weight DMA: one register stage, whole tiles");
 
@@ -1176,7 +1182,7 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
     }
   }
   // W buffer of stage s (DMA mode) and its LDS address
-  auto wbuf = [&](int s) -> char* { return lds + 2 * XBUF + (s % 3) * WBUF; };
+  auto wbuf = [&](int s) -> char* { return lds + kXB * XBUF + (s % kWB) * WBUF; };
   // copy the weight block of stage ks into its buffer; `dep` orders the copy
   // after the input loads it follows (see step)
   auto dma_w = [&](int ks, uint32_t dep) {
@@ -1258,7 +1264,7 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
   // stage has arrived (the copy's operand `dep` is made of them).
   auto store = [&](char* buf, auto slot_c, int dma_ks) {
     constexpr int sl = decltype(slot_c)::value;
-    if constexpr (kDma) {
+    if constexpr (NBUF == 3) {
       uint32_t dep = 0;
 #pragma unroll
       for (int ps = 0; ps < PA; ++ps)
@@ -1326,7 +1332,12 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
   // so the wait for those input registers in step ks + 1 (before they are
   // transformed, and so before that step's barrier) also covers the copy.
   auto step = [&](int ks, auto slot_next) {
-    const char* cur = lds + (kDma ? (ks & 1) * XBUF : NBUF == 2 ? (ks & 1) * BUF : 0);
+    // NBUF = 4: the next stage's weight block goes into the buffer stage
+    // ks - 1 read (free since the barrier that closed step ks - 1); it is
+    // issued after the input loads of stage ks + 1, so the wait for those in
+    // this step's store (before the second barrier) covers it
+    if constexpr (NBUF == 4) dma_w(ks + 1, 0u);
+    const char* cur = lds + (NBUF == 3 ? (ks & 1) * XBUF : NBUF == 2 ? (ks & 1) * BUF : 0);
     const char* bcur = kDma ? wbuf(ks) - T * A_PLANE : cur;   // b_frag counts from the A planes
     if constexpr (HALF) {
       mma_chunk<E, G, false, FM, FN>(acc, cur + a_frag + cw, A_PLANE, bcur + b_frag + cw, B_PLANE, STRIDE);
@@ -1334,8 +1345,8 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
       mma_chunk<E, G, false, FM, FN>(acc, cur + a_frag + c0, A_PLANE, bcur + b_frag + c0, B_PLANE, STRIDE);
       mma_chunk<E, G, false, FM, FN>(acc, cur + a_frag + c1, A_PLANE, bcur + b_frag + c1, B_PLANE, STRIDE);
     }
-    if constexpr (NBUF == 1) __syncthreads();   // every wave is done reading the only buffer
-    store(lds + (kDma ? ((ks + 1) & 1) * XBUF : NBUF == 2 ? ((ks + 1) & 1) * BUF : 0), slot_next, ks + 2);
+    if constexpr (NBUF == 1 || NBUF == 4) __syncthreads();   // every wave is done reading the only buffer
+    store(lds + (NBUF == 3 ? ((ks + 1) & 1) * XBUF : NBUF == 2 ? ((ks + 1) & 1) * BUF : 0), slot_next, ks + 2);
     load(ks + 1 + PF, slot_next);
     // (the DMA mode runs faster with the compiler's own order: measured)
     if constexpr (SCHED == 1 && NBUF == 2 && !HALF) interleave_schedule<E, G, FM, FN, PA, PB>();

@@ -34,7 +34,7 @@ constexpr int kNumCu = 256;  // MI355X compute units (8 XCDs x 32)
 // latency rather than by the matrix cores, so a half costs about as much as
 // a whole tile (measured: no gain on the ViT-B and ViT-H layers).
 constexpr bool fwd_tail_split_fits(bool f32, int FM, int FN, int WM, int WN, int NBUF) {
-  return f32 && WM == 2 && NBUF != 3 && FM * FN <= 2 && 2 * WN * FM * FN <= NBUF * (2 * FM + FN * WN);
+  return f32 && WM == 2 && NBUF < 3 && FM * FN <= 2 && 2 * WN * FM * FN <= NBUF * (2 * FM + FN * WN);
 }
 inline bool fwd_tail_split_fits_code(int code, bool f32) {
   const int c = EQLIN_TILE_BASE(code);

@@ -9,8 +9,9 @@ namespace eqlin {
 
 // compiled forward tiles, code = FM FN WM WN NBUF PF [P] (decimal digits)
 #define EQLIN_P4_TILES(X)                                                                                 \
-  X(112221) X(111221) X(112121) X(222221) X(212421) X(212431) X(112411) X(212211) X(122211) X(112211) X(112212)     \
-  X(112412) X(111211) X(2124211) X(1122111) X(1122211) X(1112111) X(112111) X(1121111)
+  X(112221) X(111221) X(112121) X(222221) X(212421) X(212431) X(122241) X(112241) X(112411) X(212211)     \
+  X(122211) X(112211) X(112212) X(112412) X(111211) X(2124211) X(1122111) X(1122211) X(1112111) X(112111) \
+  X(1121111)
 
 namespace {
 // EQLIN_SCHED=0 drops the explicit MFMA / memory interleave of the

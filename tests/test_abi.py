@@ -244,7 +244,7 @@ def test_forward_plan_tiles_and_tail_split(lib, monkeypatch):
     assert _plan(lib, 12608, 768, 768, 4, 0) == (OK, 112211, 197 * 3, 512)       # ViT-B attention fp32
     assert _plan(lib, 8224, 1280, 5120, 4, 0) == (OK, 112211, 129 * 20, 2560)    # ViT-H fc1 fp32
     assert _plan(lib, 8224, 5120, 1280, 4, 0) == (OK, 112211, 129 * 5, 645)      # last round 133 > 128
-    assert _plan(lib, 12608, 768, 3072, 4, 1) == (OK, 122211, 197 * 6, 1182)     # f16: 64 x 128, no split
+    assert _plan(lib, 12608, 768, 3072, 4, 1) == (OK, 122241, 197 * 6, 1182)     # f16: 64 x 128, no split
     assert _plan(lib, 8224, 1280, 5120, 4, 1) == (OK, 212431, 65 * 10, 650)      # f16: 128 x 128
     assert _plan(lib, 12608, 768, 768, 8, 0) == (OK, 112211, 197 * 2, 394)       # C8: last round 138
     assert _plan(lib, 201728, 64, 64, 4, 0) == (OK, 112111, 3152, 3072)         # narrow fp32: 64 x 32

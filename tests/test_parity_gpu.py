@@ -166,9 +166,9 @@ def _forward_case(dt, N, C, D, seed=0, g=4):
     return X, w, host(Y)
 
 
-@pytest.mark.parametrize("tile", ["auto", "112221", "111221", "112121", "222221", "212421", "212431", "112411", "212211",
-                                  "122211", "112211", "112212", "112412", "111211", "2124211", "1122111", "1122211",
-                                  "1112111", "112111", "1121111"])
+@pytest.mark.parametrize("tile", ["auto", "112221", "111221", "112121", "222221", "212421", "212431", "122241",
+                                  "112241", "112411", "212211", "122211", "112211", "112212", "112412", "111211",
+                                  "2124211", "1122111", "1122211", "1112111", "112111", "1121111"])
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 def test_forward_small_shapes_all_tiles(dt, tile, monkeypatch):
     if tile != "auto":
@@ -470,7 +470,8 @@ def test_determinism(dt, g):
 
 
 @pytest.mark.parametrize("pair", [("112211", "112221"), ("111211", "111221"), ("112211", "112212"),
-                                  ("112411", "112412"), ("212421", "212431")])
+                                  ("112411", "112412"), ("212421", "212431"), ("122211", "122241"),
+                                  ("112211", "112241")])
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 def test_lds_buffering_is_bitwise_invisible(dt, pair, monkeypatch):
     """Race check: one fragment layout run single-buffered (NBUF = 1: two
@@ -479,12 +480,13 @@ def test_lds_buffering_is_bitwise_invisible(dt, pair, monkeypatch):
     other buffer while this one is read), or with one and with two stages of
     global loads in flight, multiplies the same operands in the same order:
     the outputs must agree bit for bit.  A missing wait or barrier shows up
-    as a difference.  The last pair copies the weight operand straight from
-    memory into three LDS buffers (NBUF = 3) instead of through registers.
+    as a difference.  The last three pairs copy the weight operand straight
+    from memory into LDS (NBUF = 3: three weight buffers beside two of the
+    input; NBUF = 4: two beside one) instead of through registers.
     The first shape has one k stage (the copies of the idle stages only)."""
     a, b = pair
     if max(int(a[4]), int(b[4])) >= 3:
-        # the DMA tile runs no tail split, whose halves add their k ranges
+        # the DMA tiles run no tail split, whose halves add their k ranges
         # in another order: compare whole tiles with whole tiles
         monkeypatch.setenv("EQLIN_FWD_SPLIT", "0")
     shapes = [(200, 64, 136), (1000, 160, 96), (333, 800, 520), (299 * 64 + 37, 4 * 42, 256)]
