@@ -374,8 +374,24 @@ __device__ __forceinline__ float erf_as7126(float z) {
   return copysignf(r, z);
 }
 
-// GELU(x) = x * Phi(x) = x/2 * (1 + erf(x / sqrt(2)))
-__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erf_as7126(x * 0.70710678118654752f)); }
+// erf(z) by Abramowitz & Stegun formula 7.1.27: for z >= 0,
+// erf(z) = 1 - 1 / (1 + a1 z + a2 z^2 + a3 z^3 + a4 z^4)^4, |error| <= 5e-4;
+// one reciprocal and no exponential.  Odd extension for z < 0.  Used for
+// binary16 outputs, whose own rounding (2^-11 relative) is of the same size.
+__device__ __forceinline__ float erf_as7127(float z) {
+  const float a = fabsf(z);
+  const float p = 1.0f + a * (0.278393f + a * (0.230389f + a * (0.000972f + a * 0.078108f)));
+  const float p2 = p * p;
+  return copysignf(1.0f - __frcp_rn(p2 * p2), z);
+}
+
+// GELU(x) = x * Phi(x) = x/2 * (1 + erf(x / sqrt(2))), evaluated in float32
+// with erf by 7.1.26 for float32 outputs and by 7.1.27 for binary16 ones
+template <typename E>
+__device__ __forceinline__ float gelu_erf(float x) {
+  const float z = x * 0.70710678118654752f;
+  return 0.5f * x * (1.0f + (sizeof(E) == 2 ? erf_as7127(z) : erf_as7126(z)));
+}
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
@@ -987,29 +1003,46 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[Grp<G>::kOrder]
           continue;
         }
       }
+      // The residual rows of a chunk of RC rows are all read before any of
+      // them is written.  The residual may be `out` itself (in place), so the
+      // compiler cannot move a row's load above the previous row's store;
+      // each thread reads and writes only its own elements, so reading ahead
+      // is safe, and the loads' latencies then overlap instead of adding up
+      // row by row.
+      constexpr int RC = T == 4 ? 16 : 8;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float f[T], y[T];
-        // f16: undo the operand scales (exact powers of two)
-#pragma unroll
-        for (int p = 0; p < T; ++p) f[p] = sizeof(E) == 2 ? acc[p][fm][fn][r] * f16_unscale<G>(p) : acc[p][fm][fn][r];
-        Grp<G>::idft(f, y);
-        if (bias != nullptr) {
-#pragma unroll
-          for (int t = 0; t < T; ++t) y[t] += bm;
-        }
-        if (act == 1) {
-#pragma unroll
-          for (int t = 0; t < T; ++t) y[t] = gelu_erf(y[t]);
-        }
-        const uint32_t off = lane_off + (uint32_t)(8 * (r >> 2) + (r & 3)) * row_bytes;
+      for (int r0 = 0; r0 < 16; r0 += RC) {
+        float rv[RC][T];
         if (res != nullptr) {
-          float rv[T];
-          load_group_buf<E, T>(rsd, off, rv);
 #pragma unroll
-          for (int t = 0; t < T; ++t) y[t] += rv[t];
+          for (int i = 0; i < RC; ++i) {
+            const int r = r0 + i;
+            load_group_buf<E, T>(rsd, lane_off + (uint32_t)(8 * (r >> 2) + (r & 3)) * row_bytes, rv[i]);
+          }
         }
-        store_group_buf<E, T>(dst, off, y);
+#pragma unroll
+        for (int i = 0; i < RC; ++i) {
+          const int r = r0 + i;
+          float f[T], y[T];
+          // f16: undo the operand scales (exact powers of two)
+#pragma unroll
+          for (int p = 0; p < T; ++p)
+            f[p] = sizeof(E) == 2 ? acc[p][fm][fn][r] * f16_unscale<G>(p) : acc[p][fm][fn][r];
+          Grp<G>::idft(f, y);
+          if (bias != nullptr) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) y[t] += bm;
+          }
+          if (act == 1) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) y[t] = gelu_erf<E>(y[t]);
+          }
+          if (res != nullptr) {
+#pragma unroll
+            for (int t = 0; t < T; ++t) y[t] += rv[i][t];
+          }
+          store_group_buf<E, T>(dst, lane_off + (uint32_t)(8 * (r >> 2) + (r & 3)) * row_bytes, y);
+        }
       }
     }
   }
