@@ -517,9 +517,13 @@ int backward_impl(const void* dY, const void* X, int64_t N, int C, int D, int T,
   // 16 or fewer input groups (their dX runs faster as the forward's narrow
   // tile than as the fused launch's 64 x 64 one: C = D = 64 over 201728 rows,
   // 42.6 against 45.9 us; at 32 groups the fused launch still wins, 52.7
-  // against 58.3 us) and for the wide f16 p4 layers (wide_f16_layer).
+  // against 58.3 us), for the wide f16 p4 layers (wide_f16_layer) and for f16
+  // p4 layers of 512 or more output groups, whose dX (an input-gradient of
+  // that many k groups) runs on the forward's faster f16 tiles (ViT-B fc1:
+  // 95.9 against 99.7 us fused; ViT-B attention and fc2, 192 output groups,
+  // stay fused: 35.1 against 38.1 us, and a tie).
   const bool narrow_f16 = dtype == EQLIN_F16 && O == 4 && C / O <= 16;
-  const bool wide_f16 = wide_f16_layer(O, D / O, C / O, dtype);
+  const bool wide_f16 = wide_f16_layer(O, D / O, C / O, dtype) || (dtype == EQLIN_F16 && O == 4 && D / O >= 512);
   if (dX && dw && N > 0 && use_fused_backward() && !narrow_f16 && !wide_f16) {
     // one launch for dX and the dw partials (they share dY), then the finalize
     const DwPlan p = plan_dw_fused(N, C, D, O, dtype, max_splits);
