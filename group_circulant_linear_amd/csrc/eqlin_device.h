@@ -1366,9 +1366,12 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
   // transformed, and so before that step's barrier) also covers the copy.
   auto step = [&](int ks, auto slot_next) {
     // NBUF = 4: the next stage's weight block goes into the buffer stage
-    // ks - 1 read (free since the barrier that closed step ks - 1); it is
-    // issued after the input loads of stage ks + 1, so the wait for those in
-    // this step's store (before the second barrier) covers it
+    // ks - 1 read (free since the barrier that closed step ks - 1).  The copy
+    // follows the input loads of stage ks + 1 and precedes, as a memory
+    // barrier in program order, every load issued after it; the compiler's
+    // wait for those input registers in this step's store (before the second
+    // barrier) may leave only such later loads outstanding, so it completes
+    // the copy too (loads complete in issue order)
     if constexpr (NBUF == 4) dma_w(ks + 1, 0u);
     const char* cur = lds + (NBUF == 3 ? (ks & 1) * XBUF : NBUF == 2 ? (ks & 1) * BUF : 0);
     const char* bcur = kDma ? wbuf(ks) - T * A_PLANE : cur;   // b_frag counts from the A planes
