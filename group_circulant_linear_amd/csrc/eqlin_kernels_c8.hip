@@ -8,7 +8,7 @@ namespace eqlin {
 // compiled forward tiles, code = FM FN WM WN NBUF PF [P] (decimal digits)
 // (the eight accumulators of a C8 tile rule out 8-wave workgroups with one
 // fragment per wave: 512 threads leave 256 registers per lane)
-#define EQLIN_C8_TILES(X) X(112211) X(112221) X(111221) X(212211) X(122211) X(1122111) X(1222111) X(2122111)
+#define EQLIN_C8_TILES(X) X(112211) X(112221) X(111221) X(212211) X(122211) X(1122111) X(1222111) X(2122111) X(122241)
 
 template <>
 bool Launch<8>::fwd_tile_known(int tile) {

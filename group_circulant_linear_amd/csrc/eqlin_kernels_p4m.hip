@@ -7,7 +7,7 @@ namespace eqlin {
 
 // compiled forward tiles, code = FM FN WM WN NBUF PF [P] (decimal digits)
 // (eight accumulators per fragment, as for C8)
-#define EQLIN_P4M_TILES(X) X(112211) X(112221) X(111221) X(212211) X(122211) X(1122111) X(1222111) X(2122111)
+#define EQLIN_P4M_TILES(X) X(112211) X(112221) X(111221) X(212211) X(122211) X(1122111) X(1222111) X(2122111) X(122241)
 
 template <>
 bool Launch<kP4M>::fwd_tile_known(int tile) {

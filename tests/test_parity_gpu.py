@@ -181,7 +181,7 @@ def test_forward_small_shapes_all_tiles(dt, tile, monkeypatch):
 
 
 @pytest.mark.parametrize("tile", ["auto", "112211", "112221", "111221", "212211", "122211", "1122111", "1222111",
-                                  "2122111"])
+                                  "2122111", "122241"])
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 @pytest.mark.parametrize("g", [8, "p4m"])
 def test_forward_order8_small_shapes_all_tiles(g, dt, tile, monkeypatch):

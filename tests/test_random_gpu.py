@@ -26,7 +26,7 @@ P4M_TABLE = oracle.p4m_table()
 
 P4_TILES = ["112221", "111221", "112121", "222221", "212421", "112411", "212211", "122211", "112211", "112212",
             "112412", "111211", "2124211", "1122111", "1122211", "1112111", "112111", "1121111"]
-ORDER8_TILES = ["112211", "112221", "111221", "212211", "122211", "1122111", "1222111", "2122111"]
+ORDER8_TILES = ["112211", "112221", "111221", "212211", "122211", "1122111", "1222111", "2122111", "122241"]
 CONV_TILES = ["112211", "112221", "111211", "212421", "111221"]
 
 
