@@ -247,6 +247,9 @@ def test_forward_plan_tiles_and_tail_split(lib, monkeypatch):
     assert _plan(lib, 12608, 768, 3072, 4, 1) == (OK, 122241, 197 * 6, 1182)     # f16: 64 x 128, no split
     assert _plan(lib, 8224, 1280, 5120, 4, 1) == (OK, 212431, 65 * 10, 650)      # f16: 128 x 128
     assert _plan(lib, 12608, 768, 768, 8, 0) == (OK, 112211, 197 * 2, 394)       # C8: last round 138
+    assert _plan(lib, 12608, 768, 768, 8, 1) == (OK, 122241, 197, 197)          # C8 f16: 64 x 128, weight DMA
+    assert _plan(lib, 12608, 768, 768, 108, 1) == (OK, 122241, 197, 197)        # p4m f16: same table
+    assert _plan(lib, 8224, 5120, 1280, 8, 1) == (OK, 2122111, 65 * 3, 195)     # C8 f16: 128 x 64 stream
     assert _plan(lib, 201728, 64, 64, 4, 0) == (OK, 112111, 3152, 3072)         # narrow fp32: 64 x 32
     assert _plan(lib, 201728, 64, 64, 4, 1) == (OK, 1121111, 3152, 3152)        # narrow f16: persistent 64 x 32
     assert _plan(lib, 201728, 64, 192, 4, 0)[1] == 112211                       # 48 output groups: 64 x 64
@@ -258,6 +261,10 @@ def test_forward_plan_tiles_and_tail_split(lib, monkeypatch):
     assert _plan(lib, 12608, 768, 768, 4, 0) == (OK, 111211, 394 * 3, 1182)
     monkeypatch.setenv("EQLIN_FWD_TILE", "212421")
     assert _plan(lib, 12608, 768, 768, 4, 0) == (OK, 212421, 99 * 2, 198)
+    monkeypatch.setenv("EQLIN_FWD_TILE", "122241")                                # weight DMA: never split
+    assert _plan(lib, 8224, 5120, 1280, 4, 0) == (OK, 122241, 129 * 3, 387)
+    monkeypatch.setenv("EQLIN_FWD_TILE", "112241")
+    assert _plan(lib, 8224, 5120, 1280, 4, 0) == (OK, 112241, 129 * 5, 645)
     monkeypatch.setenv("EQLIN_FWD_TILE", "123456")                                # not compiled: ignored
     assert _plan(lib, 12608, 768, 768, 4, 0)[1] == 112211
     assert _plan(lib, 12608, 770, 768, 4, 0)[0] == EINVAL
