@@ -77,7 +77,7 @@ def parse():
 
 
 # standalone diagnostic programs beside the library's sources (not in its kernels)
-_NOT_LIBRARY = ("ceilings.hip", "stage_trace.hip")
+_NOT_LIBRARY = ("ceilings.hip", "stage_trace.hip", "dma_check.hip")
 
 
 def kernel_source_sha256():

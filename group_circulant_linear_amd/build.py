@@ -17,9 +17,11 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libeqlin.so")
 SOURCES = ("eqlin_api.hip", "eqlin_kernels.hip", "eqlin_kernels_c8.hip", "eqlin_kernels_p4m.hip", "eqconv_kernels.hip")
 # standalone programs: the measured ceilings of the GPU (matrix-core rates, LDS
-# reads, HBM copy) and the stage timeline of the forward tile
+# reads, HBM copy), the stage timeline of the forward tile and the check of
+# the direct global-to-LDS load the f16 tiles use
 PROGRAMS = {"ceilings.hip": os.path.join(LIBDIR, "eqlin_ceilings"),
-            "stage_trace.hip": os.path.join(LIBDIR, "eqlin_stage_trace")}
+            "stage_trace.hip": os.path.join(LIBDIR, "eqlin_stage_trace"),
+            "dma_check.hip": os.path.join(LIBDIR, "eqlin_dma_check")}
 CEILINGS = PROGRAMS["ceilings.hip"]
 ARCH = "gfx950"
 

@@ -82,6 +82,7 @@ def test_kernel_source_sha_ignores_comment_lines(tmp_path, monkeypatch):
     (csrc / "k.hip").write_text("// a comment\nint f() {\n\n  return 1;   // one\n}\n")
     assert bench.kernel_source_sha256() == base
     (csrc / "stage_trace.hip").write_text("int main() { return 0; }\n")
+    (csrc / "dma_check.hip").write_text("int main() { return 0; }\n")
     assert bench.kernel_source_sha256() == base
     (csrc / "k.hip").write_text("int f() {\n  return 2;   // one\n}\n")
     assert bench.kernel_source_sha256() != base

@@ -725,3 +725,22 @@ def test_stage_trace_program_runs():
         assert sum(g["workgroups"] for g in l["groups"]) == l["workgroups"]
         for g in l["groups"]:
             assert 0 < g["stage_us"] < l["launch_us"] and g["end_us"][1] <= 2 * l["launch_us"]
+
+
+def test_dma_check_program_runs():
+    """The check of the direct global-to-LDS load that the f16 forward tiles
+    use for their weight operand (csrc/dma_check.hip, built beside the
+    library, calling the library's dma16): lane l's 16 bytes land at
+    16 l past the wave's LDS address, and lanes reading out of the buffer's
+    range write zeros."""
+    import json
+    import os
+    import subprocess
+    exe = os.path.join(os.path.dirname(eq.LIB), "eqlin_dma_check")
+    assert os.path.exists(exe), "DMA check program not built"
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    say(f"  {run.stdout.strip()}")
+    assert run.returncode == 0, run.stdout + run.stderr
+    res = json.loads([l for l in run.stdout.splitlines() if l.startswith("{")][-1])
+    assert res["mismatched"] == 0
+    assert res["out_of_range_words"] == 64 and res["out_of_range_zero"] == 64
