@@ -116,9 +116,12 @@ constexpr TileShape kC8F16Tiles[] = {
 // where the launch splits its tail (eqlin::fwd_full_tiles); minimise that
 // work divided by the tile's efficiency.  EQLIN_FWD_TILE overrides (any
 // compiled tile code).
-int choose_from_table(const TileShape* tiles, int ntiles, int64_t nrows, int mg, bool f32, bool split);
+// kg, ksplit: with a K-split workspace (eqlin_forward_ws), the tail of a
+// tile that takes the K split costs what fwd_ksplit_plan gives for kg input groups.
+int choose_from_table(const TileShape* tiles, int ntiles, int64_t nrows, int mg, bool f32, bool split, int kg = 0,
+                      bool ksplit = false);
 
-int choose_fwd_tile(int T, int dtype, int64_t nrows, int mg) {
+int choose_fwd_tile(int T, int dtype, int64_t nrows, int mg, int kg = 0, bool ksplit = false) {
   if (const char* env = getenv("EQLIN_FWD_TILE")) {
     const int t = atoi(env);
     if (EQLIN_BY_T(T, fwd_tile_known(t))) return t;
@@ -130,7 +133,7 @@ int choose_fwd_tile(int T, int dtype, int64_t nrows, int mg) {
                                    : int(sizeof(kP4F16Tiles) / sizeof(TileShape)))
                             : (f32 ? int(sizeof(kC8F32Tiles) / sizeof(TileShape))
                                    : int(sizeof(kC8F16Tiles) / sizeof(TileShape)));
-  return choose_from_table(tiles, ntiles, nrows, mg, f32, eqlin::fwd_tail_split_enabled());
+  return choose_from_table(tiles, ntiles, nrows, mg, f32, eqlin::fwd_tail_split_enabled(), kg, ksplit);
 }
 
 // The p4 convolution runs the p4 forward tiles (one workgroup per tile, with
@@ -147,14 +150,23 @@ int choose_conv_tile(int dtype, int64_t npix, int mg) {
              : choose_from_table(kConvF16Tiles, int(sizeof(kConvF16Tiles) / sizeof(TileShape)), npix, mg, false, split);
 }
 
-int choose_from_table(const TileShape* tiles, int ntiles, int64_t nrows, int mg, bool f32, bool split) {
+int choose_from_table(const TileShape* tiles, int ntiles, int64_t nrows, int mg, bool f32, bool split, int kg,
+                      bool ksplit) {
   int best = tiles[0].code;
   double best_cost = 1e300;
   for (int i = 0; i < ntiles; ++i) {
     const TileShape& t = tiles[i];
     const int64_t n = cdiv(nrows, t.bm) * cdiv(mg, t.bn);
-    const int64_t full = (split && eqlin::fwd_tail_split_fits_code(t.code, f32)) ? eqlin::fwd_full_tiles(n) : n;
-    const double rounds = full == n ? double(cdiv(n, eqlin::kNumCu)) : double(full / eqlin::kNumCu) + 0.5;
+    const bool halves = split && eqlin::fwd_tail_split_fits_code(t.code, f32);
+    const int64_t full = halves ? eqlin::fwd_full_tiles(n) : n;
+    double rounds = full == n ? double(cdiv(n, eqlin::kNumCu)) : double(full / eqlin::kNumCu) + 0.5;
+    if (split && ksplit && eqlin::fwd_ksplit_fits_code(t.code, f32, 4)) {
+      const int kst = (int)cdiv(kg, eqlin::stage_groups(f32 ? EQLIN_F32 : EQLIN_F16));
+      const eqlin::FwdKSplitPlan pl = eqlin::fwd_ksplit_plan(n, kst, halves);
+      if (pl.nparts > 0)
+        rounds = double(n / eqlin::kNumCu) +
+                 double(cdiv(pl.tail * pl.nparts, eqlin::kNumCu)) * double(cdiv(kst, pl.nparts)) / kst;
+    }
     const double cost = rounds * t.bm * t.bn / t.eff;
     if (cost < best_cost * 0.97) {  // keep the earlier (larger) tile unless clearly better
       best_cost = cost;
@@ -366,11 +378,35 @@ ConvWs conv_workspace(int64_t npix, int C, int D, int K, int dtype) {
   return w;
 }
 
+// eqlin_forward_ws's launch for a shape: its tile, K-split plan and
+// workspace bytes (0 where the plan has no K split).
+struct FwdWsPlan {
+  int tile;
+  eqlin::FwdKSplitPlan ks;
+  size_t bytes;
+};
+
+FwdWsPlan forward_ws_plan(int64_t N, int C, int D, int T, int dtype) {
+  const int O = eqlin::group_order(T);
+  const int kg = C / O, mg = D / O;
+  const bool f32 = dtype == EQLIN_F32;
+  FwdWsPlan p{choose_fwd_tile(T, dtype, N, mg, kg, O == 4), {0, 0}, 0};
+  if (N == 0 || !eqlin::fwd_tail_split_enabled() || !eqlin::fwd_ksplit_fits_code(p.tile, f32, O)) return p;
+  const int c = EQLIN_TILE_BASE(p.tile);
+  const int bm = 32 * (c / 100000) * ((c / 1000) % 10), bn = 32 * ((c / 10000) % 10) * ((c / 100) % 10);
+  p.ks = eqlin::fwd_ksplit_plan(cdiv(N, bm) * cdiv(mg, bn), (int)cdiv(kg, eqlin::stage_groups(dtype)),
+                                eqlin::fwd_tail_split_fits_code(p.tile, f32));
+  if (p.ks.nparts > 0)
+    p.bytes = eqlin::kFwdKSplitCounterBytes +
+              size_t(p.ks.tail) * size_t(p.ks.nparts) * eqlin::fwd_ksplit_slot_bytes(p.tile, O);
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
 
-int eqlin_version(void) { return 212; }
+int eqlin_version(void) { return 213; }
 
 const char* eqlin_status_str(int status) {
   switch (status) {
@@ -454,6 +490,37 @@ int eqlin_forward_residual(const void* X, int64_t N, int C, int D, int T, const 
   const int tile = choose_fwd_tile(T, dtype, N, D / O);
   return hip_status(EQLIN_BY_T(T, forward(dtype, tile, X, W_hat, Y, N, C / O, D / O, bias, act, R,
                                           static_cast<hipStream_t>(stream))));
+}
+
+size_t eqlin_forward_workspace_bytes(int64_t N, int C, int D, int T, int dtype, int* parts) {
+  if (parts) *parts = 0;
+  if (check_shape(N, C, D, T, dtype) != EQLIN_OK) return 0;
+  const int O = eqlin::group_order(T);
+  if (N > 0 && (!fwd_offsets_fit(C, O, dtype) || !out_rows_fit(D, dtype))) return 0;
+  const FwdWsPlan p = forward_ws_plan(N, C, D, T, dtype);
+  if (parts) *parts = p.ks.nparts;
+  return p.bytes;
+}
+
+int eqlin_forward_ws(const void* X, int64_t N, int C, int D, int T, const void* W_hat, const void* bias, int act,
+                     const void* R, void* Y, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  if (!workspace) return eqlin_forward_residual(X, N, C, D, T, W_hat, bias, act, R, Y, dtype, stream);
+  int st = check_shape(N, C, D, T, dtype);
+  if (st != EQLIN_OK) return st;
+  const int O = eqlin::group_order(T);
+  if (act != EQLIN_ACT_NONE && act != EQLIN_ACT_GELU) return EQLIN_EINVAL;
+  if (N == 0) return EQLIN_OK;
+  if (!X || !W_hat || !Y) return EQLIN_EINVAL;
+  if (!aligned16(X) || !aligned16(W_hat) || !aligned16(Y) || !aligned16(workspace)) return EQLIN_EALIGN;
+  if (R && !aligned16(R)) return EQLIN_EALIGN;
+  if (bias && (reinterpret_cast<uintptr_t>(bias) % elem_bytes(dtype)) != 0) return EQLIN_EALIGN;
+  if (!fwd_offsets_fit(C, O, dtype) || !out_rows_fit(D, dtype)) return EQLIN_ENOTSUP;
+  const FwdWsPlan p = forward_ws_plan(N, C, D, T, dtype);
+  if (workspace_bytes < p.bytes) return EQLIN_EWORKSPACE;
+  eqlin::FwdKSplit ks{};
+  if (p.ks.nparts > 0) ks = eqlin::FwdKSplit{workspace, p.ks.nparts};
+  return hip_status(EQLIN_BY_T(T, forward(dtype, p.tile, X, W_hat, Y, N, C / O, D / O, bias, act, R,
+                                          static_cast<hipStream_t>(stream), ks)));
 }
 
 size_t eqlin_backward_workspace_bytes(int64_t N, int C, int D, int T, int dtype) {

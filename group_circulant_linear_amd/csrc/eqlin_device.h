@@ -1138,6 +1138,107 @@ __device__ __forceinline__ void conv_diag(const u32x4 (&M)[4], bool centre, u32x
   }
 }
 
+// K split of a tail tile (float32): the tile's k stages are cut into
+// `nparts` consecutive ranges, each multiplied by its own workgroup (a
+// part).  Every part writes its accumulators to its slot of the workspace
+// and counts itself in the tile's arrival counter; the part that arrives
+// last adds the parts' sums in the fixed order 0, 1, .., nparts - 1 (so the
+// result does not depend on which part came last), runs the tile's epilogue
+// and returns the counter to zero for the next launch.  Nothing waits on
+// another workgroup: each part only counts and leaves, or, if last, reduces.
+struct KPiece {
+  float* ws;       // the tile's nparts slots of kpiece_slot_bytes
+  uint32_t* cnt;   // the tile's arrival counter (zero between launches)
+  int part, nparts, k0, kn;   // this part, the part count (<= kMaxKParts), its first stage and stage count
+};
+
+// Cache policy of a buffer access with device scope (the SC1 bit): the
+// access is coherent across the whole GPU, past the per-XCD L2 caches.
+constexpr int kScopeDevice = 16;
+
+// Bytes of one part's accumulators: every lane's T FM FN 32 x 32 fragments
+// as 16-byte pieces, lane-minor (each store instruction writes 1 KB).
+template <int T, int FM, int FN, int NT>
+constexpr uint32_t kpiece_slot_bytes() {
+  return (uint32_t)(NT / 64) * T * FM * FN * 4 * 64 * 16;
+}
+
+// Returns true in the part that arrived last, with acc holding the tile's
+// whole sums; false in every other part (which then has nothing left to do).
+// LDS must be free (after the stage loop's last barrier): one word of it
+// broadcasts the arrival count.
+template <int T, int FM, int FN, int NT>
+__device__ __forceinline__ bool kpiece_reduce(f32x16 (&acc)[T][FM][FN], char* lds, const KPiece& kp) {
+  constexpr int CH = T * FM * FN * 4;   // 16-byte pieces per lane
+  constexpr uint32_t kSlot = kpiece_slot_bytes<T, FM, FN, NT>();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const __amdgpu_buffer_rsrc_t slots = make_rsrc(kp.ws, (uint64_t)kp.nparts * kSlot);
+  const uint32_t base = (uint32_t)(wave * CH * 64 + lane) * 16u;
+  const uint32_t mine = (uint32_t)kp.part * kSlot + base;
+  // planes per round of reads: at most eight 16-byte pieces of every part
+  // in flight, few enough registers to keep the kernel's occupancy
+  constexpr int kPlanesPerRound = FM * FN == 1 ? 2 : 1;
+#pragma unroll
+  for (int p = 0; p < T; ++p)
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = ((p * FM + fm) * FN + fn) * 4 + j;
+          const f32x4 v = {acc[p][fm][fn][4 * j], acc[p][fm][fn][4 * j + 1], acc[p][fm][fn][4 * j + 2],
+                           acc[p][fm][fn][4 * j + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), slots, mine + (uint32_t)c * 1024u, 0,
+                                                 kScopeDevice);
+        }
+  // The sums are written and read with device scope (coherent across the
+  // XCDs' L2 caches, as the device-scope atomics are), so no cache-wide
+  // write-back or invalidation is needed, which an agent-scope fence would
+  // issue (and which costs every other workgroup on the XCD its cached
+  // operands).  Ordering: every lane's stores have completed (vmcnt 0)
+  // before the barrier that precedes the count, and the reads below are
+  // issued after the count has returned.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  uint32_t* flag = reinterpret_cast<uint32_t*>(lds);
+  if (threadIdx.x == 0) *flag = __hip_atomic_fetch_add(kp.cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (*flag != (uint32_t)(kp.nparts - 1)) return false;   // workgroup-uniform
+  if (threadIdx.x == 0) __hip_atomic_store(kp.cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // every part's sums, this one's included (its own stores are visible to
+  // it), read a round of planes at a time: all of a round's reads are issued
+  // before any is added, so that their latencies overlap
+  constexpr int kRounds = T / kPlanesPerRound, kRc = kPlanesPerRound * FM * FN * 4;   // pieces per round
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    f32x4 v[kRc][kMaxKParts];
+#pragma unroll
+    for (int c = 0; c < kRc; ++c) {
+      const uint32_t off = base + (uint32_t)(r * kRc + c) * 1024u;
+#pragma unroll
+      for (int i = 0; i < kMaxKParts; ++i)   // parts past nparts read as zeros (no memory access)
+        v[c][i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                slots, i < kp.nparts ? (uint32_t)i * kSlot + off : kOob, 0,
+                                                kScopeDevice));
+    }
+#pragma unroll
+    for (int c = 0; c < kRc; ++c) {
+      // ((v0 + v1) + v2) + v3: a fixed order; the zeros past nparts add exactly
+      f32x4 sum = v[c][0];
+#pragma unroll
+      for (int i = 1; i < kMaxKParts; ++i)
+        sum = f32x4{sum[0] + v[c][i][0], sum[1] + v[c][i][1], sum[2] + v[c][i][2], sum[3] + v[c][i][3]};
+      asm volatile("" : "+v"(sum));   // the sum is formed here, not sunk into the epilogue
+      const int cc = r * kRc + c, j = cc % 4, fn = (cc / 4) % FN, fm = (cc / (4 * FN)) % FM, p = cc / (4 * FN * FM);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[p][fm][fn][4 * j + e] = sum[e];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return true;
+}
+
 // One forward (or dX) tile: workgroup-level logical tile id `lid`.  NBUF = 2
 // double-buffers the LDS stages (one barrier per stage); NBUF = 1 halves the
 // LDS footprint (two barriers per stage) so that more workgroups fit a CU.
@@ -1148,12 +1249,15 @@ __device__ __forceinline__ void conv_diag(const u32x4 (&M)[4], bool centre, u32x
 // HALF: lid = 2 tile + h runs rows h BM/2 .. h BM/2 + BM/2 - 1 of the tile
 // (tail split): wave row wr multiplies k chunk wr of every stage for all of
 // those rows and the two rows' sums are added through LDS.
+// KS: one part of a K-split tail tile (see KPiece): stages kp.k0 ..
+// kp.k0 + kp.kn - 1 of tile lid, then kpiece_reduce before the epilogue.
 template <typename E, int G, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED, bool CONV = false,
-          bool HALF = false>
+          bool HALF = false, bool KS = false>
 __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __restrict__ in,
                                          const E* __restrict__ wp, E* __restrict__ out, int64_t nrows, int kg,
                                          int mg, int tiles_n, const E* __restrict__ bias, int act,
-                                         const E* __restrict__ res, const ConvGeom& geo = ConvGeom{}) {
+                                         const E* __restrict__ res, const ConvGeom& geo = ConvGeom{},
+                                         const KPiece& kp = KPiece{}) {
   constexpr int T = Grp<G>::kOrder;
   using U = Units<E, T>;
   constexpr int NT = 64 * WM * WN;
@@ -1177,12 +1281,19 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
                 "LDS size");
   static_assert(!HALF || fwd_tail_split_fits(sizeof(E) == 4, FM, FN, WM, WN, NBUF), "tail split");
   static_assert(!kDma || (PF == 1 && !HALF), "weight DMA: one register stage, whole tiles");
+  static_assert(!KS || (!kDma && !HALF && !CONV && fwd_ksplit_fits(sizeof(E) == 4, T, NBUF, 0)),
+                "K split: float32 p4 register-path tiles");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t tile = HALF ? lid >> 1 : lid;
   const int64_t row0 = (tile / tiles_n) * BM + (HALF ? (lid & 1) * (BM / 2) : 0);
   const int col0 = (int)(tile % tiles_n) * BN;
-  const int ksteps = (kg + SG - 1) / SG;
+  // kst: stages of the whole k range (the prepared rows' stride); a K-split
+  // part multiplies stages kb .. kb + ksteps - 1, whose groups end at kend
+  const int kst = (kg + SG - 1) / SG;
+  const int kb = KS ? kp.k0 : 0;
+  const int ksteps = KS ? kp.kn : kst;
+  const int kend = KS ? (kg < (kp.k0 + kp.kn) * SG ? kg : (kp.k0 + kp.kn) * SG) : kg;
   if (HALF && row0 >= nrows) return;   // second half of a last tile with no rows there (uniform)
   // this workgroup's rows end at row_end; the A range stops there, so the
   // unused rows of a half read zeros without memory traffic
@@ -1192,7 +1303,7 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
   const __amdgpu_buffer_rsrc_t a_src =
       CONV ? make_rsrc(in, geo.in_bytes) : make_rsrc(in + row0 * T * (int64_t)kg, (uint64_t)(row_end - row0) * row_bytes);
   const __amdgpu_buffer_rsrc_t b_src =
-      make_rsrc(wp + (int64_t)col0 * ksteps * SG * T, (uint64_t)(mg - col0) * (uint64_t)ksteps * BLOCK);
+      make_rsrc(wp + (int64_t)col0 * kst * SG * T, (uint64_t)(mg - col0) * (uint64_t)kst * BLOCK);
 
   const int q = tid & 3, rl = tid >> 2;
   // Weight DMA: a stage's T x BN plane rows are blocks of 16 rows (1 KB,
@@ -1205,12 +1316,12 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
   u32x4 b_words{};
   uint32_t dma_off[KD], dma_lds[KD];
   if constexpr (kDma) {
-    b_words = rsrc_words(wp + (int64_t)col0 * ksteps * SG * T, (uint64_t)(mg - col0) * (uint64_t)ksteps * BLOCK);
+    b_words = rsrc_words(wp + (int64_t)col0 * kst * SG * T, (uint64_t)(mg - col0) * (uint64_t)kst * BLOCK);
 #pragma unroll
     for (int i = 0; i < KD; ++i) {
       const int j = wave * KD + i, p = j / (BN / 16), blk = j % (BN / 16);
       const int m = blk * 16 + (lane >> 2), slot = (lane & 3) ^ ((lane >> 4) & 3);
-      dma_off[i] = (uint32_t)m * (uint32_t)ksteps * BLOCK + p * 64 + slot * 16;
+      dma_off[i] = (uint32_t)m * (uint32_t)kst * BLOCK + p * 64 + slot * 16;
       dma_lds[i] = __builtin_amdgcn_readfirstlane((uint32_t)(p * B_PLANE + blk * 16 * STRIDE));
     }
   }
@@ -1219,7 +1330,7 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
   // copy the weight block of stage ks into its buffer; `dep` orders the copy
   // after the input loads it follows (see step)
   auto dma_w = [&](int ks, uint32_t dep) {
-    const uint32_t soffb = __builtin_amdgcn_readfirstlane((uint32_t)(ks < ksteps ? ks : ksteps - 1) * (uint32_t)BLOCK);
+    const uint32_t soffb = __builtin_amdgcn_readfirstlane((uint32_t)(kb + (ks < ksteps ? ks : ksteps - 1)) * (uint32_t)BLOCK);
     const uint32_t base = lds_address(wbuf(ks));
 #pragma unroll
     for (int i = 0; i < KD; ++i) dma16(b_words, __builtin_amdgcn_readfirstlane(base + dma_lds[i]), dma_off[i], soffb, dep);
@@ -1263,8 +1374,8 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
     } else {
       // the stage advance is wave-uniform (scalar offset); a unit reads only
       // below the row's last group channel (lim <= 0 past the last stage)
-      const int lim = kg - ks * SG;
-      const uint32_t soff = (uint32_t)(ks * SG) * (uint32_t)(T * sizeof(E));
+      const int lim = kend - (kb + ks) * SG;
+      const uint32_t soff = (uint32_t)((kb + ks) * SG) * (uint32_t)(T * sizeof(E));
 #pragma unroll
       for (int ps = 0; ps < PA; ++ps) {
         const uint32_t r = (uint32_t)(ps * RPP + rl);
@@ -1282,13 +1393,13 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
     // weights: past the last stage the loads re-read it (the pipeline's idle
     // stage, never multiplied), so the scalar offset stays inside each row
     if constexpr (!kDma) {
-      const uint32_t soffb = (uint32_t)(ks < ksteps ? ks : ksteps - 1) * (uint32_t)BLOCK;
+      const uint32_t soffb = (uint32_t)(kb + (ks < ksteps ? ks : ksteps - 1)) * (uint32_t)BLOCK;
 #pragma unroll
       for (int ps = 0; ps < PB; ++ps) {
         const uint32_t m = (uint32_t)(ps * RPP + rl);
 #pragma unroll
         for (int p = 0; p < T; ++p)
-          rb[sl][ps][p] = bload16s(b_src, m * (uint32_t)ksteps * BLOCK + p * 64 + q * 16, soffb);
+          rb[sl][ps][p] = bload16s(b_src, m * (uint32_t)kst * BLOCK + p * 64 + q * 16, soffb);
       }
     }
   };
@@ -1417,6 +1528,9 @@ __device__ __forceinline__ void fwd_tile(char* lds, int64_t lid, const E* __rest
     }
   }
 
+  if constexpr (KS) {
+    if (!kpiece_reduce<T, FM, FN, NT>(acc, lds, kp)) return;
+  }
   if constexpr (HALF) {
     // after the last stage's barrier LDS is free: wave row 1 leaves its sums
     // there (16-byte pieces, lane-minor) and wave row 0 adds them
@@ -1621,20 +1735,53 @@ constexpr int fwd_waves_per_simd() {
 // PERSIST = 0: one workgroup per tile.  PERSIST = 1: a grid of resident
 // workgroups, each running every gridDim.x-th tile (fwd_stream); ntiles is the
 // tile count.
+// nparts >= 2 (K split of the tail, the tiles that fwd_ksplit_fits): the
+// grid holds nfull whole tiles and the parts of tiles nfull .. ntiles - 1,
+// nparts per tile, with their slots and arrival counters in ws / cnt (see
+// KPiece).
 template <typename E, int G, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED, int PERSIST>
 __global__ void __launch_bounds__(64 * WM * WN, (fwd_waves_per_simd<E, Grp<G>::kOrder, FM, FN, WN>()))
 fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ out,
            int64_t nrows, int kg, int mg, int tiles_n, const E* __restrict__ bias, int act,
-           const E* __restrict__ res, int64_t ntiles, int64_t nfull) {
+           const E* __restrict__ res, int64_t ntiles, int64_t nfull, float* __restrict__ ws,
+           uint32_t* __restrict__ cnt, int nparts) {
   __shared__ __attribute__((aligned(16))) char lds[fwd_lds_bytes<E, Grp<G>::kOrder, FM, FN, WM, WN, NBUF>()];
   if constexpr (PERSIST) {
     fwd_stream<E, G, FM, FN, WM, WN, NBUF, PF, SCHED>(lds, xcd_logical_id(blockIdx.x, gridDim.x), gridDim.x, ntiles,
                                                       in, wp, out, nrows, kg, mg, tiles_n, bias, act, res);
   } else {
+    int64_t bid = blockIdx.x;
+    if constexpr (fwd_ksplit_fits(sizeof(E) == 4, Grp<G>::kOrder, NBUF, PERSIST)) {
+      // Where every CU gets at most one part, the parts are dispatched
+      // first: the oldest waves of their CUs, they run their few stages
+      // ahead of the whole tiles instead of behind them (the instruction
+      // arbiter favours older waves), and the whole tiles end as on the CUs
+      // without a part plus the part's matrix-core work.  Measured at the
+      // ViT-B attention projection: 55.9 -> 52.9 us; with more parts than
+      // CUs (ViT-H fc2) dispatching them first delays the whole tiles
+      // instead (333 -> 428 us), so they go last there.
+      const int64_t nkp = (int64_t)gridDim.x - nfull;   // part workgroups
+      const bool first = nkp <= kNumCu;
+      const bool is_part = nparts > 1 && (first ? bid < nkp : bid >= nfull);
+      const int64_t pbid = first ? bid : bid - nfull;
+      if (nparts > 1 && first && !is_part) bid -= nkp;
+      if (is_part) {
+        // consecutive logical ids share an XCD: a tile's parts mostly meet in one L2
+        const int64_t lp = xcd_logical_id(pbid, nkp);
+        const int64_t t = lp / nparts;
+        const int part = (int)(lp - t * nparts);
+        const int kst = (kg + Traits<E>::kStageGroups - 1) / Traits<E>::kStageGroups;
+        const int k0 = part * kst / nparts, k1 = (part + 1) * kst / nparts;
+        constexpr uint32_t kSlot = kpiece_slot_bytes<Grp<G>::kOrder, FM, FN, 64 * WM * WN>();
+        const KPiece kp{ws + t * nparts * (int64_t)(kSlot / 4), cnt + t, part, nparts, k0, k1 - k0};
+        fwd_tile<E, G, FM, FN, WM, WN, NBUF, PF, SCHED, false, false, true>(
+            lds, nfull + t, in, wp, out, nrows, kg, mg, tiles_n, bias, act, res, ConvGeom{}, kp);
+        return;
+      }
+    }
     // workgroups 0 .. nfull - 1 run whole tiles; the rest, dispatched last
     // and so at most one per CU beyond the whole rounds, run the halves of
     // tiles nfull .. ntiles - 1 (tail split)
-    const int64_t bid = blockIdx.x;
     if constexpr (fwd_tail_split_fits(sizeof(E) == 4, FM, FN, WM, WN, NBUF)) {
       if (bid >= nfull) {
         fwd_tile<E, G, FM, FN, WM, WN, NBUF, PF, SCHED, false, true>(
@@ -2218,29 +2365,51 @@ int64_t resident_workgroups(K kernel, int threads) {
   return n;
 }
 
+// ks: the K split of the tail (fwd_ksplit_plan for this tile; ks.nparts == 0:
+// none, and then the tail split where it fits).  The caller has checked that
+// ks.ws holds the plan's counters and slots.
 template <typename E, int G, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED, int PERSIST>
 hipError_t launch_fwd_s(const void* in, const void* wp, void* out, int64_t nrows, int kg, int mg,
-                        const void* bias, int act, const void* res, hipStream_t s) {
+                        const void* bias, int act, const void* res, hipStream_t s, const FwdKSplit& ks = FwdKSplit{}) {
   constexpr int BM = 32 * FM * WM, BN = 32 * FN * WN;
   const int64_t tiles_m = cdiv(nrows, BM);
   const int tiles_n = (int)cdiv(mg, BN);
   const int64_t tiles = tiles_m * tiles_n;
   if (tiles <= 0) return hipSuccess;
   int64_t grid = tiles, nfull = tiles;
+  int nparts = 0;
+  float* slots = nullptr;
+  uint32_t* cnt = nullptr;
   auto kernel = fwd_kernel<E, G, FM, FN, WM, WN, NBUF, PF, SCHED, PERSIST>;
   if constexpr (PERSIST) {
     const int64_t resident = resident_workgroups(kernel, 64 * WM * WN);
     if (resident > 0 && resident < grid) grid = resident;
-  } else if constexpr (fwd_tail_split_fits(sizeof(E) == 4, FM, FN, WM, WN, NBUF)) {
-    if (fwd_tail_split_enabled()) {
-      nfull = fwd_full_tiles(tiles);
-      grid = nfull + 2 * (tiles - nfull);
+  } else {
+    bool ksplit = false;
+    if constexpr (fwd_ksplit_fits(sizeof(E) == 4, Grp<G>::kOrder, NBUF, PERSIST)) {
+      if (ks.nparts > 1 && ks.ws != nullptr) {
+        const FwdKSplitPlan pl = fwd_ksplit_plan(tiles, (int)cdiv(kg, Traits<E>::kStageGroups),
+                                                 fwd_tail_split_fits(sizeof(E) == 4, FM, FN, WM, WN, NBUF));
+        if (pl.nparts != ks.nparts) return hipErrorInvalidValue;   // the caller's plan is another shape's
+        ksplit = true;
+        nparts = pl.nparts;
+        nfull = tiles - pl.tail;
+        grid = nfull + pl.tail * nparts;
+        cnt = static_cast<uint32_t*>(ks.ws);
+        slots = reinterpret_cast<float*>(static_cast<char*>(ks.ws) + kFwdKSplitCounterBytes);
+      }
+    }
+    if constexpr (fwd_tail_split_fits(sizeof(E) == 4, FM, FN, WM, WN, NBUF)) {
+      if (!ksplit && fwd_tail_split_enabled()) {
+        nfull = fwd_full_tiles(tiles);
+        grid = nfull + 2 * (tiles - nfull);
+      }
     }
   }
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(64 * WM * WN), 0, s, static_cast<const E*>(in),
                      static_cast<const E*>(wp), static_cast<E*>(out), nrows, kg, mg, tiles_n,
-                     static_cast<const E*>(bias), act, static_cast<const E*>(res), tiles, nfull);
+                     static_cast<const E*>(bias), act, static_cast<const E*>(res), tiles, nfull, slots, cnt, nparts);
   return hipGetLastError();
 }
 

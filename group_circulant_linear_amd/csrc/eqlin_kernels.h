@@ -53,6 +53,59 @@ inline bool fwd_tail_split_enabled() {
   const char* e = getenv("EQLIN_FWD_SPLIT");
   return !(e && atoi(e) == 0);
 }
+
+// K split of the tail (float32 register-path tiles, one workgroup per tile):
+// with a caller's workspace, the tiles of the last, partial round can each
+// run as nparts workgroups over consecutive ranges of the k stages instead
+// (see KPiece in eqlin_device.h), which caps the busiest CU's extra work at
+// ceil(tail nparts / CUs) parts of ceil(stages / nparts) stages.  The plan
+// takes the part count (2 .. kMaxKParts) that minimises that work, where it
+// is at least 10% below what the tile's other choice costs (half a tile with
+// the tail split, else a whole tile): the parts' sums make a round trip
+// through memory.
+constexpr int kMaxKParts = 4;
+constexpr size_t kFwdKSplitCounterBytes = 1024;   // arrival counters of up to 256 tail tiles
+// The order-8 groups do not take it: their parts' slots are twice as large
+// and the fixup cost more than it saved (C8 ViT-B attention: 53.6 -> 68 us).
+constexpr bool fwd_ksplit_fits(bool f32, int T, int NBUF, int PERSIST) {
+  return f32 && T == 4 && NBUF < 3 && PERSIST == 0;
+}
+inline bool fwd_ksplit_fits_code(int code, bool f32, int T) {
+  const int c = EQLIN_TILE_BASE(code);
+  return fwd_ksplit_fits(f32, T, (c / 10) % 10, EQLIN_TILE_PERSIST(code));
+}
+struct FwdKSplitPlan {
+  int64_t tail;   // tiles run in parts (the last tail tiles)
+  int nparts;     // 0: no K split
+};
+inline FwdKSplitPlan fwd_ksplit_plan(int64_t tiles, int kst, bool halves_fit) {
+  const int64_t r = tiles % kNumCu;
+  FwdKSplitPlan best{0, 0};
+  if (r == 0 || kst < 2) return best;
+  double cost = (halves_fit && tiles > kNumCu && 2 * r <= kNumCu) ? 0.5 : 1.0;
+  const double bar = 0.9 * cost;
+  for (int sp = 2; sp <= kMaxKParts && sp <= kst; ++sp) {
+    const double c = double((r * sp + kNumCu - 1) / kNumCu) * ((kst + sp - 1) / sp) / kst;
+    if (c < bar && c < cost) {
+      cost = c;
+      best = {r, sp};
+    }
+  }
+  return best;
+}
+// Bytes of one part's accumulators for tile code `code` and group order T
+// (the tile's T planes of BM x BN float32 values).
+inline size_t fwd_ksplit_slot_bytes(int code, int T) {
+  const int c = EQLIN_TILE_BASE(code);
+  return size_t(4096) * (c / 100000) * ((c / 10000) % 10) * ((c / 1000) % 10) * ((c / 100) % 10) * T;
+}
+// The caller's K-split workspace for one launch: counters (zero before the
+// launch; the launch leaves them zero), then tail x nparts slots.
+struct FwdKSplit {
+  void* ws = nullptr;
+  int nparts = 0;
+};
+
 //
 // Group codes: 4 and 8 are the cyclic groups of that order (4: the p4
 // rotation group), kP4M the dihedral group p4m of order 8.
@@ -67,8 +120,10 @@ struct Launch {
   static bool fwd_tile_known(int tile);
   // bias: nullable, one storage-dtype value per output group; act: 0 none, 1 GELU (erf);
   // res: nullable, a residual laid out as out, added after the activation
+  // ks: the K split of the tail (FwdKSplit{}: none)
   static hipError_t forward(int dtype, int tile, const void* in, const void* wp, void* out, int64_t nrows, int kg,
-                            int mg, const void* bias, int act, const void* res, hipStream_t s);
+                            int mg, const void* bias, int act, const void* res, hipStream_t s,
+                            const FwdKSplit& ks = FwdKSplit{});
   // chunks (1, or a divisor of nrows with chunks x mg, chunks x ng <= 64): rows
   // read as rows of `chunks` consecutive rows (narrow layers), rows_per_split
   // counting those
@@ -86,7 +141,7 @@ struct Launch {
 #define EQLIN_DECLARE_LAUNCH(T)                                                                                     \
   template <> bool Launch<T>::fwd_tile_known(int tile);                                                             \
   template <> hipError_t Launch<T>::forward(int, int, const void*, const void*, void*, int64_t, int, int,          \
-                                            const void*, int, const void*, hipStream_t);                           \
+                                            const void*, int, const void*, hipStream_t, const FwdKSplit&);         \
   template <> hipError_t Launch<T>::dw(int, const void*, const void*, float*, float*, int64_t, int, int, int64_t,   \
                                        int, int, int, hipStream_t);                                                \
   template <> hipError_t Launch<T>::bwd_fused(int, const void*, const void*, const void*, void*, float*, float*,   \

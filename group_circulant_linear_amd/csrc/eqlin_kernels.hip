@@ -18,13 +18,14 @@ namespace {
 // double-buffered tiles (for comparisons).
 template <typename E, int FM, int FN, int WM, int WN, int NBUF, int PF, int P>
 hipError_t launch_fwd_p4(const void* in, const void* wp, void* out, int64_t nrows, int kg, int mg, const void* bias,
-                         int act, const void* res, hipStream_t s) {
+                         int act, const void* res, hipStream_t s, const FwdKSplit& ks) {
   static const int sched = [] {
     const char* e = getenv("EQLIN_SCHED");
     return e ? atoi(e) : 1;
   }();
-  return sched == 1 ? launch_fwd_s<E, 4, FM, FN, WM, WN, NBUF, PF, 1, P>(in, wp, out, nrows, kg, mg, bias, act, res, s)
-                    : launch_fwd_s<E, 4, FM, FN, WM, WN, NBUF, PF, 0, P>(in, wp, out, nrows, kg, mg, bias, act, res, s);
+  return sched == 1
+             ? launch_fwd_s<E, 4, FM, FN, WM, WN, NBUF, PF, 1, P>(in, wp, out, nrows, kg, mg, bias, act, res, s, ks)
+             : launch_fwd_s<E, 4, FM, FN, WM, WN, NBUF, PF, 0, P>(in, wp, out, nrows, kg, mg, bias, act, res, s, ks);
 }
 }  // namespace
 
@@ -41,14 +42,15 @@ bool Launch<4>::fwd_tile_known(int tile) {
 
 template <>
 hipError_t Launch<4>::forward(int dtype, int tile, const void* in, const void* wp, void* out, int64_t nrows, int kg,
-                              int mg, const void* bias, int act, const void* res, hipStream_t s) {
+                              int mg, const void* bias, int act, const void* res, hipStream_t s,
+                              const FwdKSplit& ks) {
 #define EQLIN_CASE(C)                                                                                       \
   case C:                                                                                                   \
     return dtype == 0                                                                                       \
                ? launch_fwd_p4<float, EQLIN_TILE_ARGS(C), EQLIN_TILE_PERSIST(C)>(in, wp, out, nrows, kg, mg, bias, \
-                                                                                 act, res, s)                   \
+                                                                                 act, res, s, ks)               \
                : launch_fwd_p4<_Float16, EQLIN_TILE_ARGS(C), EQLIN_TILE_PERSIST(C)>(in, wp, out, nrows, kg, mg,    \
-                                                                                    bias, act, res, s);
+                                                                                    bias, act, res, s, ks);
   switch (tile) {
     EQLIN_P4_TILES(EQLIN_CASE)
     default: return hipErrorInvalidValue;

@@ -103,7 +103,8 @@ void run(const char* name, int64_t N, int C, int D) {
   auto kernel = fwd_kernel<E, 4, FM, FN, WM, WN, NBUF, PF, 1, 0>;
   auto launch = [&] {
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(64 * WM * WN), 0, 0, x, w, o, N, kg, mg, tiles_n,
-                       (const E*)nullptr, 0, (const E*)nullptr, tiles, nfull);
+                       (const E*)nullptr, 0, (const E*)nullptr, tiles, nfull, (float*)nullptr,
+                       (uint32_t*)nullptr, 0);
   };
   CHECK(hipMemcpyToSymbol(HIP_SYMBOL(g_stage_trace), &none, sizeof(none)));
   for (int i = 0; i < 300; ++i) launch();   // settle the clocks

@@ -82,6 +82,9 @@ def load_library(path: str = LIB) -> ctypes.CDLL:
         "eqlin_forward_ex": (c_int, [c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_int, c_vp, c_int, c_vp]),
         "eqlin_forward_residual": (c_int, [c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_int, c_vp, c_vp, c_int,
                                            c_vp]),
+        "eqlin_forward_workspace_bytes": (c_sz, [c_i64, c_int, c_int, c_int, c_int, ctypes.POINTER(c_int)]),
+        "eqlin_forward_ws": (c_int, [c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_int, c_vp, c_vp, c_vp, c_sz,
+                                     c_int, c_vp]),
         "eqlin_backward_workspace_bytes": (c_sz, [c_i64, c_int, c_int, c_int, c_int]),
         "eqlin_backward": (c_int, [c_vp, c_vp, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_fp, c_vp, c_sz,
                                    c_int, c_vp]),
@@ -208,31 +211,62 @@ def eqlin_forward_plan(N: int, C: int, D: int, dtype: torch.dtype, T=T_P4) -> di
     return {"tile": tile.value, "tiles": tiles.value, "whole": whole.value}
 
 
-def eqlin_forward(X: torch.Tensor, W_hat: Prepared, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Y = X W^T for the group-circulant W, X [N][C] -> Y [N][D]."""
-    lib = load_library()
-    _need_cuda(X, "X")
-    dt = _dtype_code(X)
-    if X.dtype != W_hat.dtype:
-        raise TypeError("X and the prepared weights differ in dtype")
-    if X.dim() != 2 or X.shape[1] != W_hat.C:
-        raise ValueError(f"X must have shape [N, {W_hat.C}], got {tuple(X.shape)}")
-    N = X.shape[0]
-    if out is None:
-        out = torch.empty((N, W_hat.D), dtype=X.dtype, device=X.device)
-    _check_out(out, "out", (N, W_hat.D), X.dtype)
-    _check("eqlin_forward", lib.eqlin_forward(_ptr(X), N, W_hat.C, W_hat.D, W_hat.T, _ptr(W_hat.buf), _ptr(out),
-                                              dt, _stream(X)))
-    return out
+def eqlin_forward_workspace_bytes(N: int, C: int, D: int, dtype: torch.dtype, T=T_P4) -> tuple:
+    """(bytes, parts) of eqlin_forward_ws's K-split workspace for this shape ((0, 0): none needed)."""
+    parts = ctypes.c_int(0)
+    nbytes = load_library().eqlin_forward_workspace_bytes(N, C, D, group_code(T), _DTYPES[dtype], ctypes.byref(parts))
+    return int(nbytes), parts.value
+
+
+# The forward's K-split workspaces, one per (device, stream): allocated
+# zero-filled on that stream (its arrival counters must start at zero, and
+# every launch leaves them zero), grown when a larger layer needs more.
+# Launches on one stream run in order, so they can share one workspace.
+_FWD_WS: dict = {}
+
+
+def _forward_workspace(X: torch.Tensor, N: int, W_hat: Prepared) -> Optional[torch.Tensor]:
+    nbytes, _ = eqlin_forward_workspace_bytes(N, W_hat.C, W_hat.D, W_hat.dtype, W_hat.T)
+    if nbytes == 0:
+        return None
+    key = (X.device.index, _stream(X))
+    ws = _FWD_WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=X.device)
+        _FWD_WS[key] = ws
+    return ws
+
+
+def _check_workspace(ws: torch.Tensor, N: int, W_hat: Prepared) -> None:
+    _need_cuda(ws, "workspace")
+    if ws.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 tensor")
+    nbytes, _ = eqlin_forward_workspace_bytes(N, W_hat.C, W_hat.D, W_hat.dtype, W_hat.T)
+    if ws.numel() < nbytes:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, the layer needs {nbytes}")
+
+
+def eqlin_forward(X: torch.Tensor, W_hat: Prepared, out: Optional[torch.Tensor] = None,
+                  workspace="auto") -> torch.Tensor:
+    """Y = X W^T for the group-circulant W, X [N][C] -> Y [N][D].
+
+    workspace: "auto" (a zero-filled workspace kept per device and stream, so
+    that float32 layers can split the k axis of their last round of tiles:
+    eqlin_forward_ws), None (eqlin_forward: no K split), or a caller's uint8
+    tensor of at least eqlin_forward_workspace_bytes bytes, zero-filled before
+    its first use."""
+    return eqlin_forward_ex(X, W_hat, out=out, workspace=workspace)
 
 
 ACT = {"none": 0, "gelu": 1}
 
 
 def eqlin_forward_ex(X: torch.Tensor, W_hat: Prepared, bias: Optional[torch.Tensor] = None, act: str = "none",
-                     out: Optional[torch.Tensor] = None, residual: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     out: Optional[torch.Tensor] = None, residual: Optional[torch.Tensor] = None,
+                     workspace="auto") -> torch.Tensor:
     """Y = act(X W^T + b) (+ residual) in one kernel; bias [D/n] (group-invariant, storage dtype) or None;
-    residual [N][D] in X's dtype or None (it may be `out` itself: an in-place update)."""
+    residual [N][D] in X's dtype or None (it may be `out` itself: an in-place update); workspace as for
+    eqlin_forward."""
     lib = load_library()
     _need_cuda(X, "X")
     dt = _dtype_code(X)
@@ -254,7 +288,20 @@ def eqlin_forward_ex(X: torch.Tensor, W_hat: Prepared, bias: Optional[torch.Tens
     if out is None:
         out = torch.empty((N, W_hat.D), dtype=X.dtype, device=X.device)
     _check_out(out, "out", (N, W_hat.D), X.dtype)
-    if residual is None:
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a uint8 device tensor')
+        workspace = _forward_workspace(X, N, W_hat)
+    elif workspace is not None:
+        _check_workspace(workspace, N, W_hat)
+    if workspace is not None:
+        _check("eqlin_forward_ws",
+               lib.eqlin_forward_ws(_ptr(X), N, W_hat.C, W_hat.D, W_hat.T, _ptr(W_hat.buf), _ptr(bias), ACT[act],
+                                    _ptr(residual), _ptr(out), _ptr(workspace), workspace.numel(), dt, _stream(X)))
+    elif residual is None and bias is None and act == "none":
+        _check("eqlin_forward", lib.eqlin_forward(_ptr(X), N, W_hat.C, W_hat.D, W_hat.T, _ptr(W_hat.buf),
+                                                  _ptr(out), dt, _stream(X)))
+    elif residual is None:
         _check("eqlin_forward_ex", lib.eqlin_forward_ex(_ptr(X), N, W_hat.C, W_hat.D, W_hat.T, _ptr(W_hat.buf),
                                                         _ptr(bias), ACT[act], _ptr(out), dt, _stream(X)))
     else:

@@ -238,6 +238,42 @@ int eqlin_forward_ex(const void* X, int64_t N, int C, int D, int T, const void* 
 int eqlin_forward_residual(const void* X, int64_t N, int C, int D, int T, const void* W_hat,
                            const void* bias, int act, const void* R, void* Y, int dtype, void* stream);
 
+/*
+ * Workspace bytes eqlin_forward_ws needs for this shape, or 0 when its launch
+ * has no K split (then it needs none; also 0 for invalid arguments).  If
+ * parts is non-NULL it receives the part count of each split tile (0, or 2
+ * to 4).  Depends on the environment as eqlin_forward_plan does.
+ */
+size_t eqlin_forward_workspace_bytes(int64_t N, int C, int D, int T, int dtype, int* parts);
+
+/*
+ * a2-a4 with a workspace: eqlin_forward_residual (the same fused kernel,
+ * "Implementation" section, and the same arguments), where the float32 tiles
+ * of the last, partial round of workgroups may each run as 2 to 4
+ * workgroups over consecutive ranges of the k axis.  The summary's kernel
+ * design leaves the division of the work over the GPU open; this one keeps
+ * every CU within a third or a quarter of a tile of the others where the
+ * tail split of eqlin_forward leaves half a tile (ViT-B attention: 591
+ * tiles of 64 x 64 on 256 CUs).
+ *   workspace: NULL (then exactly eqlin_forward_residual), or a device
+ *     buffer, 16-byte aligned, of workspace_bytes >=
+ *     eqlin_forward_workspace_bytes (else EQLIN_EWORKSPACE).  Its first
+ *     1024 bytes are arrival counters: they must be zero before the first
+ *     call that uses the buffer (e.g. allocate it zero-filled), and every
+ *     call leaves them zero when its kernel completes.  The rest holds the
+ *     parts' partial sums (float32), written before they are read.  Calls
+ *     that overlap in time (other streams, other threads) must not share a
+ *     workspace.  The library does not retain it.
+ * Each split tile's parts are added in a fixed order by whichever part
+ * finishes last, so for given (N, C, D, T, dtype) the result is the same on
+ * every call; a row of a split tile can differ in the last bits from the
+ * same row computed by eqlin_forward (a different summation order).
+ * EQLIN_FWD_SPLIT=0 turns the K split off with the tail split.
+ */
+int eqlin_forward_ws(const void* X, int64_t N, int C, int D, int T, const void* W_hat,
+                     const void* bias, int act, const void* R, void* Y,
+                     void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
 /* Workspace bytes eqlin_backward / eqlin_backward_dw need for this shape. */
 size_t eqlin_backward_workspace_bytes(int64_t N, int C, int D, int T, int dtype);
 

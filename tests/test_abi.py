@@ -273,6 +273,53 @@ def test_forward_plan_tiles_and_tail_split(lib, monkeypatch):
     assert st == OK
 
 
+def _ws(lib, N, C, D, T, dt):
+    parts = ctypes.c_int(-1)
+    nbytes = lib.eqlin_forward_workspace_bytes(N, C, D, T, dt, ctypes.byref(parts))
+    return nbytes, parts.value
+
+
+def test_forward_k_split_plan(lib, monkeypatch):
+    # eqlin_forward_ws's K split of the last round (no device work): parts p
+    # minimise ceil(tail p / 256) ceil(stages / p) / stages, at least 10%
+    # below the other choice (half a tile with the tail split, else a whole
+    # tile); workspace = 1024 bytes of counters + tail x p slots of
+    # T x 64 x 64 float32 (the 64 x 64 tile) or T x 32 x 64 (32 x 64)
+    monkeypatch.delenv("EQLIN_FWD_TILE", raising=False)
+    monkeypatch.delenv("EQLIN_FWD_SPLIT", raising=False)
+    slot = 4 * 64 * 64 * 4
+    assert _ws(lib, 12608, 768, 768, 4, 0) == (1024 + 79 * 3 * slot, 3)        # ViT-B attention: 591 tiles, 12 stages
+    assert _ws(lib, 12608, 3072, 768, 4, 0) == (1024 + 79 * 3 * slot, 3)       # ViT-B fc2: 48 stages
+    assert _ws(lib, 12608, 768, 3072, 4, 0) == (1024 + 60 * 4 * slot, 4)       # ViT-B fc1: tail 60 of 2364
+    assert _ws(lib, 8224, 1280, 5120, 4, 0) == (1024 + 20 * 4 * slot, 4)       # ViT-H fc1: tail 20 of 2580
+    assert _ws(lib, 8224, 5120, 1280, 4, 0) == (1024 + 133 * 3 * slot, 3)      # ViT-H fc2: tail 133, no halves
+    assert _ws(lib, 12608, 768, 768, 8, 0) == (0, 0)                            # order 8: never
+    assert _ws(lib, 12608, 768, 768, 108, 0) == (0, 0)
+    assert _ws(lib, 2171, 768, 768, 4, 0) == (1024 + 204 * 2 * slot // 2, 2)   # 204 tiles of 32 x 64
+    assert _ws(lib, 12608, 768, 768, 4, 1) == (0, 0)                            # f16: never
+    assert _ws(lib, 201728, 64, 64, 4, 0) == (0, 0)                             # one k stage
+    assert _ws(lib, 16448, 768, 768, 4, 0) == (1024 + 3 * 4 * slot, 4)         # 771 tiles: tail 3
+    assert _ws(lib, 0, 768, 768, 4, 0) == (0, 0)
+    assert _ws(lib, 12608, 770, 768, 4, 0) == (0, 0)                            # invalid
+    assert lib.eqlin_forward_workspace_bytes(12608, 768, 768, 4, 0, None) == 1024 + 79 * 3 * slot
+    monkeypatch.setenv("EQLIN_FWD_SPLIT", "0")
+    assert _ws(lib, 12608, 768, 768, 4, 0) == (0, 0)
+
+
+def test_forward_ws_validation(lib):
+    X, W, Y = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000)
+    need = lib.eqlin_forward_workspace_bytes(12608, 768, 768, 4, 0, None)
+    ws = ctypes.c_void_p(0x10000)
+    f = lib.eqlin_forward_ws
+    assert f(X, 12608, 768, 768, 4, W, None, 0, None, Y, ws, need - 1, 0, None) == EWORKSPACE
+    assert f(X, 12608, 768, 768, 4, W, None, 0, None, Y, ctypes.c_void_p(0x10008), need, 0, None) == EALIGN
+    assert f(X, 12608, 768, 768, 4, W, None, 3, None, Y, ws, need, 0, None) == EINVAL
+    assert f(X, 12608, 770, 768, 4, W, None, 0, None, Y, ws, need, 0, None) == EINVAL
+    assert f(X, 12608, 768, 768, 5, W, None, 0, None, Y, ws, need, 0, None) == ENOTSUP
+    assert f(None, 12608, 768, 768, 4, W, None, 0, None, Y, ws, need, 0, None) == EINVAL
+    assert f(X, 0, 768, 768, 4, W, None, 0, None, Y, ws, 0, 0, None) == OK       # empty batch: nothing to do
+
+
 # ------------------------------------------------------------ refused launches
 
 EHIP = 5
@@ -349,10 +396,18 @@ def test_binding_rejects_wrong_outputs_before_any_launch(monkeypatch):
         with pytest.raises(ValueError):
             case()
         assert fake.calls == [], (i, fake.calls)
-    # correctly shaped outputs reach the library
+    # a caller's K-split workspace smaller than the layer's need (the stand-in
+    # library reports 1 byte) or of another dtype is refused the same way
+    for ws in (torch.zeros(0, dtype=torch.uint8), torch.zeros(4, dtype=torch.float32)):
+        with pytest.raises(ValueError):
+            eqlin.eqlin_forward(X, W, workspace=ws)
+        assert fake.calls == []
+    # correctly shaped outputs reach the library: the default forward through
+    # eqlin_forward_ws with the binding's workspace, without one eqlin_forward
     eqlin.eqlin_forward(X, W, out=torch.zeros(N, D))
+    eqlin.eqlin_forward(X, W, out=torch.zeros(N, D), workspace=None)
     eqlin.eqlin_backward(dY, X, W, dX_out=torch.zeros(N, C), dw_out=torch.zeros(D // 4, C // 4, 4))
-    assert fake.calls == ["eqlin_forward", "eqlin_backward"]
+    assert fake.calls == ["eqlin_forward_ws", "eqlin_forward", "eqlin_backward"]
 
 
 def test_noalloc_backward_refuses_layers_beyond_its_scratch(lib):

@@ -221,13 +221,16 @@ def test_forward_tail_split(g, tile, monkeypatch):
         X, w, _ = make_layer_inputs(N, C, D, dt, seed=15, T=T, with_dy=False)
         Wh = prep(w, g)
         ref = ref_forward(X, w, g)
+        # halves (no workspace: eqlin_forward), the K split (the binding's
+        # workspace: eqlin_forward_ws), every tile whole
         monkeypatch.setenv("EQLIN_FWD_SPLIT", "1")
-        Ys = host(eq.eqlin_forward(dev(X), Wh))
+        Ys = host(eq.eqlin_forward(dev(X), Wh, workspace=None))
+        Yk = host(eq.eqlin_forward(dev(X), Wh))
         monkeypatch.setenv("EQLIN_FWD_SPLIT", "0")
         Yw = host(eq.eqlin_forward(dev(X), Wh))
-        es, ew = rel_err(Ys, ref), rel_err(Yw, ref)
-        say(f"  split {es:.2e} whole {ew:.2e}")
-        assert es <= TOL[dt] and ew <= TOL[dt]
+        es, ek, ew = rel_err(Ys, ref), rel_err(Yk, ref), rel_err(Yw, ref)
+        say(f"  split {es:.2e} k split {ek:.2e} whole {ew:.2e}")
+        assert es <= TOL[dt] and ek <= TOL[dt] and ew <= TOL[dt]
     # bias and GELU in the halves' epilogue, and dX through the same launch
     monkeypatch.setenv("EQLIN_FWD_SPLIT", "1")
     N, mg = _split_shapes(tile)[1]
@@ -235,7 +238,7 @@ def test_forward_tail_split(g, tile, monkeypatch):
     X, w, dY = make_layer_inputs(N, C, D, dt, seed=16, T=T)
     b = np.random.default_rng(17).standard_normal(D // T).astype(X.dtype)
     Wh = prep(w, g)
-    Y = host(eq.eqlin_forward_ex(dev(X), Wh, dev(b), "gelu"))
+    Y = host(eq.eqlin_forward_ex(dev(X), Wh, dev(b), "gelu", workspace=None))
     Z = ref_forward(X, w, g) + np.repeat(b.astype(np.float64), T)[None, :]
     assert rel_err(Y, oracle.gelu_erf(Z)) <= TOL[dt]
     dX = host(eq.eqlin_backward_dx(dev(dY), Wh))
@@ -245,7 +248,9 @@ def test_forward_tail_split(g, tile, monkeypatch):
 def test_rows_and_batch_size(monkeypatch):
     # a row's output does not depend on the other rows of the call: bit for
     # bit with the tail split off, and for rows of whole tiles with it on;
-    # rows of split tiles (two partial sums over k) agree to the tolerance
+    # rows of split tiles (partial sums over k) agree to the tolerance.  With
+    # the K-split workspace a launch of fewer tiles than CUs splits every
+    # tile, so there the rows agree to the tolerance too.
     monkeypatch.setenv("EQLIN_FWD_TILE", "112211")
     N, C, D = 299 * 64 + 50, 4 * 42, 256          # 300 tiles: the last 44 run split
     X, w, _ = make_layer_inputs(N, C, D, "f32", seed=19, with_dy=False)
@@ -253,14 +258,70 @@ def test_rows_and_batch_size(monkeypatch):
     whole_rows = 256 * 64
     for split in ("0", "1"):
         monkeypatch.setenv("EQLIN_FWD_SPLIT", split)
-        Y = host(eq.eqlin_forward(dev(X), Wh))
-        Ya = host(eq.eqlin_forward(dev(X[:6400]), Wh))          # 100 tiles, never split
-        Yb = host(eq.eqlin_forward(dev(X[whole_rows:]), Wh))    # 44 tiles, never split
-        assert np.array_equal(Y[:6400], Ya)
-        if split == "0":
-            assert np.array_equal(Y[whole_rows:], Yb)
-        else:
-            assert rel_err(Y[whole_rows:], Yb) <= 1e-6
+        for ws in (None, "auto"):
+            Y = host(eq.eqlin_forward(dev(X), Wh, workspace=ws))
+            Ya = host(eq.eqlin_forward(dev(X[:6400]), Wh, workspace=ws))          # 100 tiles
+            Yb = host(eq.eqlin_forward(dev(X[whole_rows:]), Wh, workspace=ws))    # 44 tiles
+            if ws is None or split == "0":
+                assert np.array_equal(Y[:6400], Ya)
+            else:
+                assert rel_err(Y[:6400], Ya) <= 1e-6
+            if split == "0":
+                assert np.array_equal(Y[whole_rows:], Yb)
+            else:
+                assert rel_err(Y[whole_rows:], Yb) <= 1e-6
+
+
+# (N, C, D, group) -> parts of the K split (p4 only): the ViT-B attention
+# projection (591 tiles of 64 x 64, 79 in the last round: 3 parts, dispatched
+# before the whole tiles), the ViT-B fc1 shape with a ragged last row tile (4
+# parts), a launch of fewer tiles than CUs (204 tiles of 32 x 64 in 2 parts:
+# more parts than CUs, dispatched after the whole tiles), and the ViT-H fc2
+# shape (133 tail tiles in 3 parts of 27 stages, after the whole tiles)
+KSPLIT_CASES = [(12608, 768, 768, 4, 3), (12608 - 37, 768, 3072, 4, 4), (2176 - 5, 768, 768, 4, 2),
+                (8224, 5120, 1280, 4, 3)]
+
+
+@pytest.mark.parametrize("N,C,D,g,parts", KSPLIT_CASES)
+def test_forward_k_split(N, C, D, g, parts):
+    """The K split of the last round's tiles (eqlin_forward_ws): against the
+    oracle, against the launch without a workspace, the same bits on a
+    second call, the arrival counters back at zero, and the fused epilogue
+    (bias, GELU, residual) run by the part that finishes last."""
+    T = order(g)
+    nbytes, got_parts = eq.eqlin_forward_workspace_bytes(N, C, D, torch.float32, T=g)
+    assert got_parts == parts and nbytes > 0
+    say(f"k split group={g} N={N} C={C} D={D} parts={parts} workspace={nbytes}")
+    X, w, _ = make_layer_inputs(N, C, D, "f32", seed=31, T=T, with_dy=False)
+    Wh = prep(w, g)
+    tX = dev(X)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    Y1 = eq.eqlin_forward(tX, Wh, workspace=ws).clone()
+    Y2 = eq.eqlin_forward(tX, Wh, workspace=ws)
+    Y0 = eq.eqlin_forward(tX, Wh, workspace=None)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2)
+    assert torch.count_nonzero(ws[:1024]).item() == 0
+    ref = ref_forward(X, w, g)
+    e1, e0 = rel_err(host(Y1), ref), rel_err(host(Y0), ref)
+    say(f"  rel err k split {e1:.2e} without workspace {e0:.2e}")
+    assert e1 <= TOL["f32"] and e0 <= TOL["f32"]
+    # epilogue after the reduction
+    rng = np.random.default_rng(32)
+    b = rng.standard_normal(D // T).astype(np.float32)
+    R = rng.standard_normal((N, D)).astype(np.float32)
+    Yr = host(eq.eqlin_forward_ex(tX, Wh, dev(b), "gelu", residual=dev(R), workspace=ws))
+    Z = oracle.gelu_erf(ref + np.repeat(b.astype(np.float64), T)[None, :]) + R
+    assert rel_err(Yr, Z) <= TOL["f32"]
+    assert torch.count_nonzero(ws[:1024]).item() == 0
+    # a workspace one byte short is refused before any launch
+    with pytest.raises(ValueError):
+        eq.eqlin_forward(tX, Wh, workspace=ws[:nbytes - 1])
+
+
+def test_forward_k_split_not_for_order_8():
+    for g in (8, "p4m"):
+        assert eq.eqlin_forward_workspace_bytes(12608, 768, 768, torch.float32, T=g) == (0, 0)
 
 
 def _sample_rows(N, rng, k=96):
