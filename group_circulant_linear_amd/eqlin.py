@@ -213,8 +213,15 @@ def eqlin_forward_plan(N: int, C: int, D: int, dtype: torch.dtype, T=T_P4) -> di
 
 def eqlin_forward_workspace_bytes(N: int, C: int, D: int, dtype: torch.dtype, T=T_P4) -> tuple:
     """(bytes, parts) of eqlin_forward_ws's K-split workspace for this shape ((0, 0): none needed)."""
+    return _fwd_ws_bytes(N, C, D, group_code(T), _DTYPES[dtype], os.environ.get("EQLIN_FWD_TILE"),
+                         os.environ.get("EQLIN_FWD_SPLIT"))
+
+
+@functools.lru_cache(maxsize=256)
+def _fwd_ws_bytes(N: int, C: int, D: int, T: int, dt: int, tile_env, split_env) -> tuple:
+    # the plan depends on the shape and on the two environment overrides, which are part of the key
     parts = ctypes.c_int(0)
-    nbytes = load_library().eqlin_forward_workspace_bytes(N, C, D, group_code(T), _DTYPES[dtype], ctypes.byref(parts))
+    nbytes = load_library().eqlin_forward_workspace_bytes(N, C, D, T, dt, ctypes.byref(parts))
     return int(nbytes), parts.value
 
 

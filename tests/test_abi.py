@@ -2,6 +2,7 @@
 symbol, and rejects bad arguments before any kernel launch (no GPU needed:
 every call here fails validation, so nothing is enqueued)."""
 import ctypes
+import functools
 
 import pytest
 
@@ -373,6 +374,7 @@ def test_binding_rejects_wrong_outputs_before_any_launch(monkeypatch):
     torch = pytest.importorskip("torch")
     fake = _RecordingLib()
     monkeypatch.setattr(eqlin, "load_library", lambda path=None: fake)
+    monkeypatch.setattr(eqlin, "_fwd_ws_bytes", functools.lru_cache(maxsize=None)(eqlin._fwd_ws_bytes.__wrapped__))
     monkeypatch.setattr(eqlin, "_need_cuda", lambda t, name: None)
     monkeypatch.setattr(eqlin, "_stream", lambda t: 0)
     N, C, D = 16, 32, 48
