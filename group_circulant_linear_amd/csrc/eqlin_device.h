@@ -64,7 +64,7 @@ constexpr int kThreads = 256;
 // header; in the library the hook is empty.  Event ev of workgroup b: the
 // shader clock and the 100 MHz real-time counter, written by thread 0 to
 // g_stage_trace[(b * 64 + ev) * 2 + {0, 1}] (b < 8192; event 61 holds the
-// wave's hardware id).  Events: 0 start, 1 first stage in LDS, 2 first stage
+// wave's hardware id and its XCC id).  Events: 0 start, 1 first stage in LDS, 2 first stage
 // multiplied, 3 last stage multiplied, 62 output stores issued, 63 stores
 // completed.
 #ifdef EQLIN_STAGE_TRACE
@@ -75,9 +75,11 @@ __device__ __forceinline__ void stage_mark(int ev) {
     t[(blockIdx.x * 64 + ev) * 2] = __builtin_amdgcn_s_memtime();
     t[(blockIdx.x * 64 + ev) * 2 + 1] = __builtin_amdgcn_s_memrealtime();
     if (ev == 0) {
-      unsigned id;
+      unsigned id, xcc;
       asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(id));
+      asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
       t[(blockIdx.x * 64 + 61) * 2] = id;
+      t[(blockIdx.x * 64 + 61) * 2 + 1] = xcc & 0xf;
     }
   }
 }
@@ -1732,6 +1734,19 @@ constexpr int fwd_waves_per_simd() {
   return (T * FM * FN >= 16 || (T == 8 && sizeof(E) == 2)) ? 1 : (T == 4 && FM * FN == 1 && WN == 1) ? 3 : 2;
 }
 
+// The forward kernel's bound.  The library's fp32 p4 one-fragment,
+// single-buffered tiles fit three waves per SIMD (three workgroups per CU,
+// as their LDS allows) under the bound of two; the stage-timeline build's
+// timestamp stores would push them past it, so there the bound asks for
+// three, keeping the traced launch's occupancy that of the library.
+template <typename E, int T, int FM, int FN, int WN, int NBUF, int PF>
+constexpr int fwd_kernel_waves() {
+#ifdef EQLIN_STAGE_TRACE
+  if (sizeof(E) == 4 && T == 4 && FM * FN == 1 && NBUF == 1 && PF == 1) return 3;
+#endif
+  return fwd_waves_per_simd<E, T, FM, FN, WN>();
+}
+
 // PERSIST = 0: one workgroup per tile.  PERSIST = 1: a grid of resident
 // workgroups, each running every gridDim.x-th tile (fwd_stream); ntiles is the
 // tile count.
@@ -1740,7 +1755,7 @@ constexpr int fwd_waves_per_simd() {
 // nparts per tile, with their slots and arrival counters in ws / cnt (see
 // KPiece).
 template <typename E, int G, int FM, int FN, int WM, int WN, int NBUF, int PF, int SCHED, int PERSIST>
-__global__ void __launch_bounds__(64 * WM * WN, (fwd_waves_per_simd<E, Grp<G>::kOrder, FM, FN, WN>()))
+__global__ void __launch_bounds__(64 * WM * WN, (fwd_kernel_waves<E, Grp<G>::kOrder, FM, FN, WN, NBUF, PF>()))
 fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ out,
            int64_t nrows, int kg, int mg, int tiles_n, const E* __restrict__ bias, int act,
            const E* __restrict__ res, int64_t ntiles, int64_t nfull, float* __restrict__ ws,
@@ -1759,13 +1774,17 @@ fwd_kernel(const E* __restrict__ in, const E* __restrict__ wp, E* __restrict__ o
       // without a part plus the part's matrix-core work.  Measured at the
       // ViT-B attention projection: 55.9 -> 52.9 us; with more parts than
       // CUs (ViT-H fc2) dispatching them first delays the whole tiles
-      // instead (333 -> 428 us), so they go last there.
+      // instead (333 -> 428 us), so they go last there, at the highest wave
+      // priority so that they are not starved until the whole tiles end
+      // (ViT-H fc2 334 -> 326 us; their stages end at 96-204 us instead of
+      // 210-319 us).
       const int64_t nkp = (int64_t)gridDim.x - nfull;   // part workgroups
       const bool first = nkp <= kNumCu;
       const bool is_part = nparts > 1 && (first ? bid < nkp : bid >= nfull);
       const int64_t pbid = first ? bid : bid - nfull;
       if (nparts > 1 && first && !is_part) bid -= nkp;
       if (is_part) {
+        if (!first) __builtin_amdgcn_s_setprio(3);
         // consecutive logical ids share an XCD: a tile's parts mostly meet in one L2
         const int64_t lp = xcd_logical_id(pbid, nkp);
         const int64_t t = lp / nparts;

@@ -770,8 +770,8 @@ def test_f16_operand_range_forward_tiles(tile, monkeypatch):
 
 def test_stage_trace_program_runs():
     """The stage-timeline diagnostic (csrc/stage_trace.hip, built beside the
-    library) traces one launch of each of its four layer shapes: every line
-    has its rounds, each with a positive stage time, within the launch."""
+    library) traces one launch of each of its layer shapes: every line has
+    its rounds, each with a positive stage time, within the launch."""
     import json
     import os
     import subprocess
@@ -779,7 +779,13 @@ def test_stage_trace_program_runs():
     assert os.path.exists(exe), "stage trace program not built"
     out = subprocess.run([exe], capture_output=True, text=True, timeout=120, check=True).stdout
     lines = [json.loads(l) for l in out.splitlines() if l.startswith("{")]
-    assert [l["layer"] for l in lines] == ["vith_fc1", "vith_fc2", "vitb_fc2", "vitb_attn"]
+    assert [l["layer"] for l in lines] == ["vith_fc1", "vith_fc2", "vitb_fc2", "vitb_attn", "vitb_attn_ksplit",
+                                           "vith_fc2_f32_ksplit"]
+    # the K-split launches: three parts per tail tile, a group of their own,
+    # and the dispatcher's placement (XCC = workgroup id mod 8, every CU used)
+    for l in lines[4:]:
+        assert l["ksplit_parts"] == 3 and l["groups"][-1]["group"] == "k-split parts"
+        assert l["placement"]["cus"] == 256 and l["placement"]["xcc_is_workgroup_id_mod_8"]
     for l in lines:
         say(f"  {l['layer']} {l['dtype']}: {l['launch_us']} us, clock {l['shader_clock_ghz']} GHz")
         assert l["launch_us"] > 0 and l["groups"]
