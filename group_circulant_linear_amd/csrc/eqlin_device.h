@@ -1177,8 +1177,10 @@ __device__ __forceinline__ bool kpiece_reduce(f32x16 (&acc)[T][FM][FN], char* ld
   const __amdgpu_buffer_rsrc_t slots = make_rsrc(kp.ws, (uint64_t)kp.nparts * kSlot);
   const uint32_t base = (uint32_t)(wave * CH * 64 + lane) * 16u;
   const uint32_t mine = (uint32_t)kp.part * kSlot + base;
-  // planes per round of reads: at most eight 16-byte pieces of every part
-  // in flight, few enough registers to keep the kernel's occupancy
+  // planes per round of reads: eight 16-byte pieces of every part in
+  // flight for the tiles of one or two fragments per wave and plane (one
+  // plane, sixteen pieces, for four), few enough registers to keep the
+  // kernel's occupancy (the 64 x 64 tile: 166 registers, three waves per SIMD)
   constexpr int kPlanesPerRound = FM * FN == 1 ? 2 : 1;
 #pragma unroll
   for (int p = 0; p < T; ++p)
