@@ -314,6 +314,11 @@ def test_forward_k_split(N, C, D, g, parts):
     Z = oracle.gelu_erf(ref + np.repeat(b.astype(np.float64), T)[None, :]) + R
     assert rel_err(Yr, Z) <= TOL["f32"]
     assert torch.count_nonzero(ws[:1024]).item() == 0
+    # the residual updated in place (R is the output): only the part that
+    # arrives last reads R and writes Y
+    tR = dev(R)
+    eq.eqlin_forward_ex(tX, Wh, dev(b), "gelu", out=tR, residual=tR, workspace=ws)
+    assert rel_err(host(tR), Z) <= TOL["f32"]
     # a workspace one byte short is refused before any launch
     with pytest.raises(ValueError):
         eq.eqlin_forward(tX, Wh, workspace=ws[:nbytes - 1])
