@@ -307,6 +307,37 @@ def test_forward_k_split_plan(lib, monkeypatch):
     assert _ws(lib, 12608, 768, 768, 4, 0) == (0, 0)
 
 
+def test_forward_k_split_plan_rule(lib, monkeypatch):
+    # the plan against the rule the header and the launcher state, over a grid
+    # of shapes on the forced 64 x 64 tile: with t tiles (r = t mod 256 in the
+    # last round) of s k stages, parts p in 2..4 (p <= s) cost
+    # ceil(r p / 256) ceil(s / p) / s tiles on the busiest CU; the plan takes
+    # the cheapest p that is at least 10% below the other choice (half a tile
+    # where the tail split applies: more than 256 tiles and r <= 128; else a
+    # whole tile), and the workspace is 1024 bytes + r p slots of 64 KB
+    monkeypatch.setenv("EQLIN_FWD_TILE", "112211")
+    monkeypatch.delenv("EQLIN_FWD_SPLIT", raising=False)
+    checked = 0
+    for N in (64, 1000, 2176, 6400, 12608, 16448, 19000, 33000):
+        for C in (64, 192, 768, 1280, 3072):
+            for D in (256, 768, 1280):
+                tiles = -(-N // 64) * -(-(D // 4) // 64)
+                s = -(-(C // 4) // 16)
+                r = tiles % 256
+                want_p, cost = 0, (0.5 if tiles > 256 and 2 * r <= 256 else 1.0)
+                bar = 0.9 * cost
+                for p in range(2, 5):
+                    if p > s or r == 0:
+                        continue
+                    c = -(-r * p // 256) * -(-s // p) / s
+                    if c < bar and c < cost:
+                        want_p, cost = p, c
+                want = (1024 + r * want_p * 65536, want_p) if want_p else (0, 0)
+                assert _ws(lib, N, C, D, 4, 0) == want, (N, C, D)
+                checked += 1
+    assert checked == 120
+
+
 def test_forward_ws_validation(lib):
     X, W, Y = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000)
     need = lib.eqlin_forward_workspace_bytes(12608, 768, 768, 4, 0, None)
