@@ -8,6 +8,7 @@ if the library is not built, every call raises.
 """
 from __future__ import annotations
 
+import collections
 import ctypes
 import functools
 import os
@@ -228,8 +229,12 @@ def _fwd_ws_bytes(N: int, C: int, D: int, T: int, dt: int, tile_env, split_env) 
 # The forward's K-split workspaces, one per (device, stream): allocated
 # zero-filled on that stream (its arrival counters must start at zero, and
 # every launch leaves them zero), grown when a larger layer needs more.
-# Launches on one stream run in order, so they can share one workspace.
-_FWD_WS: dict = {}
+# Launches on one stream run in order, so they can share one workspace.  At
+# most _FWD_WS_MAX are kept (least recently used first out): a dropped one
+# was allocated and used on its own stream only, so torch's allocator reuses
+# its memory in that stream's order.
+_FWD_WS: "collections.OrderedDict" = collections.OrderedDict()
+_FWD_WS_MAX = 8
 
 
 def _forward_workspace(X: torch.Tensor, N: int, W_hat: Prepared) -> Optional[torch.Tensor]:
@@ -241,6 +246,9 @@ def _forward_workspace(X: torch.Tensor, N: int, W_hat: Prepared) -> Optional[tor
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(nbytes, dtype=torch.uint8, device=X.device)
         _FWD_WS[key] = ws
+    _FWD_WS.move_to_end(key)
+    while len(_FWD_WS) > _FWD_WS_MAX:
+        _FWD_WS.popitem(last=False)
     return ws
 
 

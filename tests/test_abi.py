@@ -454,3 +454,31 @@ def test_noalloc_backward_refuses_layers_beyond_its_scratch(lib):
     C = D = 4 * 1456
     assert 4 * (C // 4) * (D // 4) * 4 > scratch            # 33.9 MB: one split does not fit
     assert lib.eqlin_backward_noalloc(FAKE, FAKE, 64, C, D, 4, FAKE, None, FAKE, 0, None) == EWORKSPACE
+
+
+def test_binding_keeps_a_bounded_number_of_forward_workspaces(monkeypatch):
+    # one zero-filled workspace per (device, stream), the least recently used
+    # dropped past the cap; a stream's workspace is reused while it is large
+    # enough and replaced (zero-filled) when a layer needs more
+    torch = pytest.importorskip("torch")
+    monkeypatch.setattr(eqlin, "_FWD_WS", __import__("collections").OrderedDict())
+    streams = iter(range(1000, 2000))
+    current = {"s": 0}
+    monkeypatch.setattr(eqlin, "_stream", lambda t: current["s"])
+    need = {"n": 64}
+    monkeypatch.setattr(eqlin, "eqlin_forward_workspace_bytes", lambda *a, **k: (need["n"], 3))
+    W = eqlin.Prepared(torch.zeros(1, dtype=torch.uint8), 32, 32, torch.float32, 4)
+    X = torch.zeros(4, 32)
+    current["s"] = next(streams)
+    first = eqlin._forward_workspace(X, 4, W)
+    assert first.numel() == 64 and int(first.sum()) == 0
+    assert eqlin._forward_workspace(X, 4, W) is first
+    need["n"] = 128
+    bigger = eqlin._forward_workspace(X, 4, W)
+    assert bigger is not first and bigger.numel() == 128 and int(bigger.sum()) == 0
+    for _ in range(3 * eqlin._FWD_WS_MAX):
+        current["s"] = next(streams)
+        eqlin._forward_workspace(X, 4, W)
+    assert len(eqlin._FWD_WS) == eqlin._FWD_WS_MAX
+    need["n"] = 0
+    assert eqlin._forward_workspace(X, 4, W) is None
